@@ -1,0 +1,134 @@
+/*
+ * attn_varlen.h -- C ABI of libattn_varlen.so: document-masked (varlen)
+ * causal grouped-query attention, forward and backward, for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * What the library computes
+ * -------------------------
+ * A packed microbatch of T tokens is split into segments [cu[s], cu[s+1]).
+ * No token attends across its own segment boundary and attention is causal
+ * inside a segment (research.dws.rip/llm/kernels, section 01 "How it was
+ * measured").  Local layers add a sliding window, global layers use full
+ * causal context; query heads share key-value heads in groups (same page,
+ * Fig. 2 "Benchmark setup": 8 query / 2 key-value heads of width 128,
+ * 512-token window; section 02: the call is a varlen attention with sliding
+ * windows and grouped-query attention).  With G = Hq / Hkv, query head h
+ * reads key-value head floor(h / G), and for query i of segment [a, b):
+ *
+ *   visible keys  V(i) = { j : max(a, i - W + 1) <= j <= i }   (W <= 0: a <= j <= i)
+ *   S_ij  = scale * q_{i,h} . k_{j,g}
+ *   lse   = log sum_{j in V(i)} exp(S_ij)                       (natural log)
+ *   out   = sum_j exp(S_ij - lse) v_{j,g}
+ *
+ * and the backward pass returns the gradients of sum(dout * out) with
+ * respect to q, k and v (dk, dv summed over the G query heads of a group).
+ *
+ * Layouts (all row-major, head dim innermost, no strides):
+ *   q, out, dout, dq : bf16 [T, Hq, D]
+ *   k, v, dk, dv     : bf16 [T, Hkv, D]
+ *   lse              : fp32 [Hq, T]
+ *   cu_seqlens       : int32 [num_seqs + 1], on the device
+ * Tensor pointers are device pointers, 16-byte aligned.  The caller owns
+ * every buffer; the library never allocates, frees or keeps a pointer after
+ * a call returns.
+ *
+ * Conventions where the pages are silent
+ *   window <= 0      : full causal context inside each segment
+ *   window W >= 1    : W keys counting the query itself (i - W < j <= i)
+ *   cu_seqlens       : non-decreasing, cu[0] = 0, cu[num_seqs] = T; empty
+ *                      segments are allowed (padding to a fixed count) and
+ *                      change nothing, bit for bit
+ *                      (research.dws.rip/llm/kernels, section 06 "CUDA
+ *                      graphs work, with padding")
+ *   max_seqlen       : >= the longest segment (used to bound the schedule)
+ *   supported shapes : D == 128, Hq % Hkv == 0 and (Hq / Hkv) % 4 == 0
+ *
+ * Execution
+ *   Every call enqueues its kernels on `stream` and returns without waiting
+ *   and without reading device memory on the host, so calls can be captured
+ *   in a HIP graph.  The contents of cu_seqlens are not validated on the
+ *   host (that would need a device read).  Calls are deterministic: the same
+ *   inputs give bit-identical outputs (no floating-point atomics).
+ *
+ * Errors
+ *   Host-checkable problems return a negative attn_status before anything is
+ *   enqueued; outputs are then untouched.  ATTN_ELAUNCH reports a launch
+ *   failure from the HIP runtime.  Nothing is thrown across the ABI.
+ */
+#ifndef ATTN_VARLEN_H
+#define ATTN_VARLEN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_EINVAL = -1,       /* null/misaligned pointer, bad size, bad scale, ... */
+  ATTN_EUNSUPPORTED = -2, /* valid arguments this build does not implement (D != 128, group % 4) */
+  ATTN_EWORKSPACE = -3,   /* workspace null or smaller than attn_varlen_workspace_size() */
+  ATTN_EDEVICE = -4,      /* no usable gfx950 device / HIP runtime error before launch */
+  ATTN_ELAUNCH = -5       /* a kernel launch failed */
+} attn_status;
+
+/* opaque stream handle: a hipStream_t (0 = the legacy default stream) */
+typedef void* attn_stream_t;
+
+/*
+ * Bytes of device workspace one fwd or bwd call needs.  It holds the tile
+ * schedule (rebuilt on the device by every call) and, for the backward,
+ * the per-row D = rowsum(dout * out) in fp32.  Returns 0 for arguments
+ * the calls would reject.
+ *   total_tokens  T > 0
+ *   num_seqs_cap  the num_seqs the calls will pass (>= 1)
+ */
+size_t attn_varlen_workspace_size(int32_t total_tokens, int32_t num_seqs_cap,
+                                  int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_seqlen, int32_t window);
+
+/*
+ * Forward pass: out and lse from q, k, v.
+ *   q, k, v        bf16 inputs (layouts above), read only
+ *   cu_seqlens     int32 device array of num_seqs + 1 segment boundaries
+ *   scale          multiplies q.k before the softmax; finite and > 0
+ *   out            bf16 [T, Hq, D], written fully
+ *   lse            fp32 [Hq, T] natural-log normaliser, written fully
+ *   workspace      device memory of at least attn_varlen_workspace_size()
+ *                  bytes, 256-byte aligned; contents need not be initialised
+ */
+attn_status attn_varlen_fwd(const void* q, const void* k, const void* v,
+                            const int32_t* cu_seqlens, int32_t num_seqs,
+                            int32_t total_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t max_seqlen, int32_t window, float scale,
+                            void* out, float* lse,
+                            void* workspace, size_t workspace_bytes, attn_stream_t stream);
+
+/*
+ * Backward pass: dq, dk, dv from q, k, v, the forward's out and lse, and
+ * dout.  Same argument meanings as attn_varlen_fwd; out and lse must be the
+ * forward's results for the same inputs.  dq, dk, dv are written fully
+ * (rows of every segment; tokens outside all segments cannot exist since
+ * cu[num_seqs] = T).
+ */
+attn_status attn_varlen_bwd(const void* q, const void* k, const void* v,
+                            const void* out, const float* lse, const void* dout,
+                            const int32_t* cu_seqlens, int32_t num_seqs,
+                            int32_t total_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t max_seqlen, int32_t window, float scale,
+                            void* dq, void* dk, void* dv,
+                            void* workspace, size_t workspace_bytes, attn_stream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char* attn_varlen_strerror(attn_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t attn_varlen_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_VARLEN_H */

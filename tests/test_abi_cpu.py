@@ -1,0 +1,90 @@
+"""The C-ABI library loads, exports every symbol its header declares, and
+rejects bad arguments with the documented codes before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import varlen_sliding_window_amd as attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_varlen.h")
+
+EINVAL, EUNSUPPORTED, EWORKSPACE = -1, -2, -3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_varlen_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(attn.LIBRARY_PATH):
+        pytest.skip("library not built")
+    return attn.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"attn_varlen_fwd", "attn_varlen_bwd", "attn_varlen_workspace_size",
+            "attn_varlen_strerror"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in the header but not exported"
+
+
+def test_version_and_strerror(lib):
+    assert lib.attn_varlen_version() >= 100
+    for code in (0, -1, -2, -3, -4, -5, 7):
+        assert len(attn.strerror(code)) > 0
+
+
+def test_workspace_size(lib):
+    n = attn.workspace_size(16384, 64, 8, 2, 128, 4096, 512)
+    # at least D (fp32 [Hq, T]) plus both tile lists
+    assert n >= 8 * 16384 * 4 + 2 * 16 * (16384 // 32 + 64)
+    assert n % 256 == 0
+    assert attn.workspace_size(16384, 64, 8, 2, 64, 4096, 512) == 0     # head dim 64
+    assert attn.workspace_size(0, 1, 8, 2, 128, 1, 0) == 0               # T = 0
+    assert attn.workspace_size(100, 1, 8, 3, 128, 100, 0) == 0           # Hq % Hkv
+    assert attn.workspace_size(100, 1, 8, 2, 128, 101, 0) == 0           # max_seqlen > T
+
+
+FAKE = 1 << 20  # aligned, never dereferenced: every case below fails validation first
+
+
+def call_fwd(lib, **over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, nseq=1, T=64, hq=8, hkv=2, d=128, ms=64, w=0,
+                scale=0.088, out=FAKE, lse=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
+    args.update(over)
+    return lib.attn_varlen_fwd(args["q"], args["k"], args["v"], args["cu"], args["nseq"],
+                               args["T"], args["hq"], args["hkv"], args["d"], args["ms"],
+                               args["w"], args["scale"], args["out"], args["lse"], args["ws"],
+                               args["wsb"], args["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    ({"q": None}, EINVAL), ({"cu": None}, EINVAL), ({"out": None}, EINVAL),
+    ({"lse": None}, EINVAL), ({"q": FAKE + 8}, EINVAL), ({"T": 0}, EINVAL),
+    ({"nseq": 0}, EINVAL), ({"hkv": 3}, EINVAL), ({"hq": 0}, EINVAL), ({"ms": 0}, EINVAL),
+    ({"ms": 65}, EINVAL), ({"scale": 0.0}, EINVAL), ({"scale": -1.0}, EINVAL),
+    ({"scale": float("nan")}, EINVAL), ({"scale": float("inf")}, EINVAL),
+    ({"d": 64}, EUNSUPPORTED), ({"d": 256}, EUNSUPPORTED), ({"hq": 2, "hkv": 1}, EUNSUPPORTED),
+    ({"hq": 8, "hkv": 8}, EUNSUPPORTED), ({"ws": None}, EWORKSPACE), ({"wsb": 16}, EWORKSPACE),
+    ({"ws": FAKE + 16}, EWORKSPACE),
+])
+def test_fwd_rejects(lib, over, code):
+    assert call_fwd(lib, **over) == code
+
+
+def test_bwd_rejects(lib):
+    f = lib.attn_varlen_bwd
+    base = [FAKE] * 7 + [1, 64, 8, 2, 128, 64, 0, 0.088, FAKE, FAKE, FAKE, FAKE, 1 << 30, None]
+    for pos, val, code in ((4, None, EINVAL), (5, None, EINVAL), (15, None, EINVAL),
+                           (17, None, EINVAL), (11, 64, EUNSUPPORTED), (12, 65, EINVAL), (19, 8, EWORKSPACE),
+                           (14, 0.0, EINVAL)):
+        a = list(base)
+        a[pos] = val
+        assert f(*a) == code, (pos, val)

@@ -1,0 +1,12 @@
+"""Document-masked (varlen) causal grouped-query attention for MI355X (gfx950).
+
+``fwd``/``bwd`` call the C ABI of libattn_varlen.so (include/attn_varlen.h);
+the computation runs in hand-written HIP kernels.  ``flops`` holds the exact
+work counts used for throughput.
+"""
+from . import flops
+from ._binding import (LIBRARY_PATH, AttnError, bwd, fwd, load_library, new_workspace, strerror,
+                       workspace_size)
+
+__all__ = ["LIBRARY_PATH", "AttnError", "bwd", "flops", "fwd", "load_library", "new_workspace",
+           "strerror", "workspace_size"]

@@ -1,0 +1,156 @@
+"""ctypes binding of libattn_varlen.so (the C ABI in include/attn_varlen.h).
+
+Argument marshalling only: torch supplies device memory and the current
+stream, every step of the computation runs in the library's HIP kernels.
+There is no fallback: if the library is missing or the device is not a
+gfx950, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(_HERE, "libattn_varlen.so")
+
+ATTN_OK = 0
+STATUS_NAMES = {0: "ATTN_OK", -1: "ATTN_EINVAL", -2: "ATTN_EUNSUPPORTED",
+                -3: "ATTN_EWORKSPACE", -4: "ATTN_EDEVICE", -5: "ATTN_ELAUNCH"}
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {strerror(status)}")
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load (once) and type the shared library; raise if it was not built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIBRARY_PATH
+    if not os.path.exists(p):
+        raise FileNotFoundError(
+            f"{p} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(p)
+    i32, sz, vp = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
+    lib.attn_varlen_workspace_size.argtypes = [i32] * 7
+    lib.attn_varlen_workspace_size.restype = sz
+    lib.attn_varlen_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                    ctypes.c_float, vp, vp, vp, sz, vp]
+    lib.attn_varlen_fwd.restype = ctypes.c_int
+    lib.attn_varlen_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                    i32, ctypes.c_float, vp, vp, vp, vp, sz, vp]
+    lib.attn_varlen_bwd.restype = ctypes.c_int
+    lib.attn_varlen_strerror.argtypes = [ctypes.c_int]
+    lib.attn_varlen_strerror.restype = ctypes.c_char_p
+    lib.attn_varlen_version.argtypes = []
+    lib.attn_varlen_version.restype = i32
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def strerror(status: int) -> str:
+    return load_library().attn_varlen_strerror(int(status)).decode()
+
+
+def workspace_size(total_tokens: int, num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                   head_dim: int, max_seqlen: int, window: int) -> int:
+    return int(load_library().attn_varlen_workspace_size(
+        total_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, max_seqlen, window))
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _check_tensor(name, t, dtype, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+
+
+def _stream_handle(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def new_workspace(total_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, max_seqlen,
+                  window, device) -> torch.Tensor:
+    n = workspace_size(total_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                       max_seqlen, window)
+    if n == 0:
+        raise AttnError(-1, "attn_varlen_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def fwd(q, k, v, cu_seqlens, max_seqlen: int, window: int, scale: float | None = None,
+        out=None, lse=None, workspace=None):
+    """attn_varlen_fwd: returns (out [T,Hq,D] bf16, lse [Hq,T] fp32)."""
+    _check_tensor("q", q, torch.bfloat16, 3)
+    _check_tensor("k", k, torch.bfloat16, 3)
+    _check_tensor("v", v, torch.bfloat16, 3)
+    _check_tensor("cu_seqlens", cu_seqlens, torch.int32, 1)
+    t, hq, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != (t, hkv, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [T, Hkv, D] with q's T and D")
+    nseq = cu_seqlens.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((hq, t), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = new_workspace(t, nseq, hq, hkv, d, max_seqlen, window, q.device)
+    st = load_library().attn_varlen_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), nseq, t, hq, hkv, d, int(max_seqlen),
+        int(window), float(scale), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+        _stream_handle(q.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_varlen_fwd")
+    return out, lse
+
+
+def bwd(q, k, v, out, lse, dout, cu_seqlens, max_seqlen: int, window: int,
+        scale: float | None = None, dq=None, dk=None, dv=None, workspace=None):
+    """attn_varlen_bwd: returns (dq, dk, dv), bf16, shaped like q, k, v."""
+    for name, t_ in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _check_tensor(name, t_, torch.bfloat16, 3)
+    _check_tensor("lse", lse, torch.float32, 2)
+    _check_tensor("cu_seqlens", cu_seqlens, torch.int32, 1)
+    t, hq, d = q.shape
+    hkv = k.shape[1]
+    if out.shape != q.shape or dout.shape != q.shape or lse.shape != (hq, t):
+        raise ValueError("out/dout must match q and lse must be [Hq, T]")
+    if k.shape != (t, hkv, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [T, Hkv, D] with q's T and D")
+    nseq = cu_seqlens.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        workspace = new_workspace(t, nseq, hq, hkv, d, max_seqlen, window, q.device)
+    st = load_library().attn_varlen_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(cu_seqlens), nseq,
+        t, hq, hkv, d, int(max_seqlen), int(window), float(scale), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(workspace), workspace.numel(), _stream_handle(q.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_varlen_bwd")
+    return dq, dk, dv

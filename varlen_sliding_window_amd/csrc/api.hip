@@ -1,0 +1,154 @@
+// C ABI of libattn_varlen.so (declared in include/attn_varlen.h).
+//
+// Host side only: argument checks that need no device read, the workspace
+// layout, and kernel launches on the caller's stream.  Nothing here waits
+// on the device or allocates memory.
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "../../include/attn_varlen.h"
+#include "common.h"
+#include "launch.h"
+
+namespace {
+
+using attn::Problem;
+using attn::WorkspaceLayout;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+
+attn_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ATTN_EDEVICE;
+  if (dev >= kMaxDevices) return ATTN_EDEVICE;
+  int state = g_device_ok[dev].load(std::memory_order_relaxed);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_EDEVICE;
+    state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_device_ok[dev].store(state, std::memory_order_relaxed);
+  }
+  return state == 1 ? ATTN_OK : ATTN_EDEVICE;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape and scalar checks shared by every entry point.
+attn_status check_shape(int32_t total_tokens, int32_t num_seqs, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t max_seqlen) {
+  if (total_tokens <= 0 || num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0)
+    return ATTN_EINVAL;
+  if (num_q_heads % num_kv_heads != 0) return ATTN_EINVAL;
+  if (max_seqlen <= 0 || max_seqlen > total_tokens) return ATTN_EINVAL;
+  if (head_dim != attn::HEAD_DIM) return ATTN_EUNSUPPORTED;
+  if ((num_q_heads / num_kv_heads) % 4 != 0) return ATTN_EUNSUPPORTED;
+  // grid sizes must fit in 32 bits
+  const size_t cap = attn::tile_capacity(total_tokens, num_seqs);
+  if (cap * (size_t)num_q_heads >= (size_t)1 << 31) return ATTN_EUNSUPPORTED;
+  return ATTN_OK;
+}
+
+attn_status check_common(const void* q, const void* k, const void* v, const int32_t* cu,
+                         int32_t total_tokens, int32_t num_seqs, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t max_seqlen, float scale,
+                         void* workspace, size_t workspace_bytes, WorkspaceLayout* w) {
+  attn_status s = check_shape(total_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                              max_seqlen);
+  if (s != ATTN_OK) return s;
+  if (!q || !k || !v || !cu) return ATTN_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(cu, 4))
+    return ATTN_EINVAL;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_EINVAL;
+  *w = attn::workspace_layout(total_tokens, num_seqs, num_q_heads);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < w->total) return ATTN_EWORKSPACE;
+  return ATTN_OK;
+}
+
+// A window of T or more keys can exclude nothing inside a segment, so it is
+// the global (full causal) case; mapping it to 0 keeps index arithmetic far
+// from int overflow.
+int32_t effective_window(int32_t window, int32_t total_tokens) {
+  return (window <= 0 || window >= total_tokens) ? 0 : window;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_varlen_workspace_size(int32_t total_tokens, int32_t num_seqs_cap,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_seqlen, int32_t window) {
+  (void)window;
+  if (check_shape(total_tokens, num_seqs_cap, num_q_heads, num_kv_heads, head_dim,
+                  max_seqlen) != ATTN_OK)
+    return 0;
+  return attn::workspace_layout(total_tokens, num_seqs_cap, num_q_heads).total;
+}
+
+attn_status attn_varlen_fwd(const void* q, const void* k, const void* v,
+                            const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t max_seqlen, int32_t window, float scale, void* out,
+                            float* lse, void* workspace, size_t workspace_bytes,
+                            attn_stream_t stream) {
+  WorkspaceLayout w;
+  attn_status s = check_common(q, k, v, cu_seqlens, total_tokens, num_seqs, num_q_heads,
+                               num_kv_heads, head_dim, max_seqlen, scale, workspace,
+                               workspace_bytes, &w);
+  if (s != ATTN_OK) return s;
+  if (!out || !lse || !aligned(out, 16) || !aligned(lse, 4)) return ATTN_EINVAL;
+  s = check_device();
+  if (s != ATTN_OK) return s;
+  const Problem p{total_tokens, num_seqs, num_q_heads, num_kv_heads,
+                  effective_window(window, total_tokens), scale};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (attn::launch_schedule(cu_seqlens, p, workspace, w, st) != hipSuccess) return ATTN_ELAUNCH;
+  if (attn::launch_forward(q, k, v, p, out, lse, workspace, w, st) != hipSuccess)
+    return ATTN_ELAUNCH;
+  return ATTN_OK;
+}
+
+attn_status attn_varlen_bwd(const void* q, const void* k, const void* v, const void* out,
+                            const float* lse, const void* dout, const int32_t* cu_seqlens,
+                            int32_t num_seqs, int32_t total_tokens, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t max_seqlen,
+                            int32_t window, float scale, void* dq, void* dk, void* dv,
+                            void* workspace, size_t workspace_bytes, attn_stream_t stream) {
+  WorkspaceLayout w;
+  attn_status s = check_common(q, k, v, cu_seqlens, total_tokens, num_seqs, num_q_heads,
+                               num_kv_heads, head_dim, max_seqlen, scale, workspace,
+                               workspace_bytes, &w);
+  if (s != ATTN_OK) return s;
+  if (!out || !lse || !dout || !dq || !dk || !dv) return ATTN_EINVAL;
+  if (!aligned(out, 16) || !aligned(dout, 16) || !aligned(lse, 4) || !aligned(dq, 16) ||
+      !aligned(dk, 16) || !aligned(dv, 16))
+    return ATTN_EINVAL;
+  s = check_device();
+  if (s != ATTN_OK) return s;
+  const Problem p{total_tokens, num_seqs, num_q_heads, num_kv_heads,
+                  effective_window(window, total_tokens), scale};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (attn::launch_schedule(cu_seqlens, p, workspace, w, st) != hipSuccess) return ATTN_ELAUNCH;
+  if (attn::launch_backward(q, k, v, out, lse, dout, p, dq, dk, dv, workspace, w, st) !=
+      hipSuccess)
+    return ATTN_ELAUNCH;
+  return ATTN_OK;
+}
+
+const char* attn_varlen_strerror(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "success";
+    case ATTN_EINVAL: return "invalid argument (null or misaligned pointer, bad size or scale)";
+    case ATTN_EUNSUPPORTED: return "unsupported shape (head_dim must be 128 and Hq/Hkv a multiple of 4)";
+    case ATTN_EWORKSPACE: return "workspace missing, misaligned (256 B) or too small";
+    case ATTN_EDEVICE: return "no usable gfx950 device";
+    case ATTN_ELAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t attn_varlen_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,342 @@
+// Backward kernels: dQ (which also produces D) and dK/dV.
+//
+// The gradients follow from out = softmax(scale q k^T) v per segment:
+//   P = exp(S - lse), dP = dO V^T, D = rowsum(dO * O), dS = P (dP - D),
+//   dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO,
+// with dK and dV summed over the query heads that share a key-value head
+// (research.dws.rip/llm/kernels, Fig. 2 "Benchmark setup": 8 query heads
+// over 2 key-value heads).  P is rebuilt from the forward's lse, so no
+// score matrix is ever stored.
+//
+// dQ kernel: one work-group per (q-tile, group of 4 query heads), one head
+//   per wave, exactly like the forward: S^T and dP^T are computed with the
+//   query in the lane, so per-row lse and D are one register each, and
+//   dQ^T = K^T dS^T takes dS^T straight from registers.  Each wave also
+//   forms D = rowsum(dO * O) for its rows (fp32) and writes it to the
+//   workspace for the dK/dV kernel, which runs next on the same stream.
+// dK/dV kernel: one work-group per (k-tile of 32 keys, key-value head); its
+//   4 waves take the group's query heads (wave w: heads w, w + 4, ...).  K
+//   and V stay in registers; each wave streams its head's Q/dO rows through
+//   its own LDS slice in QBLK = 32-row steps and keeps dK/dV partial sums in
+//   fp32 registers.  The 4 partials are added in a fixed order through LDS
+//   at the end, so the head-group reduction needs no atomics and is
+//   bit-for-bit reproducible.
+#include "device.h"
+#include "launch.h"
+
+namespace attn {
+namespace {
+
+constexpr int BWD_THREADS = 256;
+
+__global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ out, const bf16* __restrict__ dout, const float* __restrict__ lse,
+    const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
+    int window, float scale_log2, float scale, bf16* __restrict__ dq, float* __restrict__ dbuf) {
+  __shared__ __attribute__((aligned(16))) bf16 Ks[KBLK * LDS_PITCH];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[KBLK * LDS_PITCH];
+
+  const int chunks = Hq >> 2;
+  const int item = blockIdx.x / chunks;
+  const int hc = blockIdx.x - item * chunks;
+  if (item >= header[0]) return;
+  const Tile tl = tiles[item];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, lh = lane >> 5, lq = lane & 31;
+  const int head = hc * 4 + wave;
+  const int g = (hc * 4) / (Hq / Hkv);
+  const int q0 = tl.t0, q1 = tl.t1, a = tl.seg_a;
+  const int klo = first_visible_key(q0, a, window);
+  const int nblk = (q1 - klo + KBLK - 1) / KBLK;
+  const int qrow = q0 + lq;
+  const size_t qstride = (size_t)Hq * HEAD_DIM;
+  const size_t kstride = (size_t)Hkv * HEAD_DIM;
+
+  // Q^T and dO^T as B operands; D from dO and O at the same positions
+  bf16x8 qf[8], df[8];
+  float dpart = 0.f;
+  {
+    const size_t off = (size_t)qrow * qstride + (size_t)head * HEAD_DIM + lh * 8;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (qrow < T) {
+        qf[ks] = as_bf16x8(ldg16(q + off + ks * 16));
+        df[ks] = as_bf16x8(ldg16(dout + off + ks * 16));
+        const bf16x8 ov = as_bf16x8(ldg16(out + off + ks * 16));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dpart += (float)df[ks][e] * (float)ov[e];
+      } else {
+        qf[ks] = zero_bf16x8();
+        df[ks] = zero_bf16x8();
+      }
+    }
+  }
+  const float Dv = dpart + __shfl_xor(dpart, 32);
+  const float lse2 = qrow < T ? lse[(size_t)head * T + qrow] * LOG2E : 0.f;
+  if (qrow < q1 && lh == 0) dbuf[(size_t)head * T + qrow] = Dv;
+
+  const int srow = tid >> 4, scol = (tid & 15) * 8;
+  uint4 kr[4], vr[4];
+  auto gload = [&](int kb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = kb + srow + 16 * i;
+      if (key >= 0) {
+        const size_t off = (size_t)key * kstride + (size_t)g * HEAD_DIM + scol;
+        kr[i] = ldg16(k + off);
+        vr[i] = ldg16(v + off);
+      } else {
+        kr[i] = make_uint4(0u, 0u, 0u, 0u);
+        vr[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  };
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) acc[db] = zero_f32x16();
+  const int full_lo = first_visible_key(q0 + TILE - 1, a, window);
+  const int my_lo = first_visible_key(qrow, a, window);
+
+  gload(q1 - KBLK);
+  for (int n = 0; n < nblk; ++n) {
+    const int kb = q1 - KBLK * (n + 1);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<uint4*>(Ks + (srow + 16 * i) * LDS_PITCH + scol) = kr[i];
+      *reinterpret_cast<uint4*>(Vs + (srow + 16 * i) * LDS_PITCH + scol) = vr[i];
+    }
+    __syncthreads();
+    if (n + 1 < nblk) gload(kb - KBLK);
+
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      s[h2] = zero_f32x16();
+      dp[h2] = zero_f32x16();
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        s[h2] = mfma32(lds_frag_cols(Ks + h2 * 32 * LDS_PITCH, ks, lane), qf[ks], s[h2]);
+        dp[h2] = mfma32(lds_frag_cols(Vs + h2 * 32 * LDS_PITCH, ks, lane), df[ks], dp[h2]);
+      }
+    }
+    const bool full = (kb + KBLK - 1 <= q0) && (kb >= full_lo);
+    bf16x8 dsf[4];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb + h2 * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
+        const bool vis = full || (key >= my_lo && key <= qrow);
+        const float p = vis ? exp2_fast(s[h2][r] * scale_log2 - lse2) : 0.f;
+        dsf[h2 * 2 + (r >> 3)][r & 7] = (bf16)(p * (dp[h2][r] - Dv));
+      }
+    // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q]
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        acc[db] = mfma32(lds_frag_rows(Ks + db * 32, t, lane), dsf[t], acc[db]);
+  }
+
+  if (qrow < q1) {
+    bf16* op = dq + (size_t)qrow * qstride + (size_t)head * HEAD_DIM + lh * 4;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        store_bf16x4(op + db * 32 + j * 8, acc[db][4 * j] * scale, acc[db][4 * j + 1] * scale,
+                     acc[db][4 * j + 2] * scale, acc[db][4 * j + 3] * scale);
+  }
+}
+
+constexpr int DKDV_WAVES = 4;
+constexpr int RED_PITCH = HEAD_DIM + 4;   // fp32 pitch of the reduction buffer
+constexpr size_t DKDV_TILE_BYTES = (size_t)QBLK * LDS_PITCH * sizeof(bf16);
+constexpr size_t DKDV_LDS_BYTES =
+    2 * DKDV_WAVES * DKDV_TILE_BYTES + 2 * DKDV_WAVES * QBLK * sizeof(float);
+static_assert((size_t)DKDV_WAVES * TILE * RED_PITCH * sizeof(float) <=
+                  2 * DKDV_WAVES * DKDV_TILE_BYTES,
+              "reduction buffer must fit in the staging buffers");
+
+__global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dbuf,
+    const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
+    int window, float scale_log2, float scale, bf16* __restrict__ dk, bf16* __restrict__ dv) {
+  __shared__ __attribute__((aligned(16))) char smem[DKDV_LDS_BYTES];
+
+  const int item = blockIdx.x / Hkv;
+  const int g = blockIdx.x - item * Hkv;
+  if (item >= header[0]) return;
+  const Tile tl = tiles[item];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, lh = lane >> 5, lq = lane & 31;
+  const int G = Hq / Hkv;
+  const int k0 = tl.t0, k1 = tl.t1, b = tl.seg_b;
+  const int qhi = window > 0 ? min(b, k1 - 1 + window) : b;
+  const int nqb = (qhi - k0 + QBLK - 1) / QBLK;
+  const size_t qstride = (size_t)Hq * HEAD_DIM;
+  const size_t kstride = (size_t)Hkv * HEAD_DIM;
+
+  bf16* Qs = reinterpret_cast<bf16*>(smem) + (size_t)wave * QBLK * LDS_PITCH;
+  bf16* Ds = reinterpret_cast<bf16*>(smem + DKDV_WAVES * DKDV_TILE_BYTES) +
+             (size_t)wave * QBLK * LDS_PITCH;
+  float* Ls = reinterpret_cast<float*>(smem + 2 * DKDV_WAVES * DKDV_TILE_BYTES) + wave * QBLK;
+  float* Dd = Ls + DKDV_WAVES * QBLK;
+
+  // K^T and V^T as B operands: lane holds k[k0 + lq][16 ks + 8 lh + 0..7]
+  const int krow = k0 + lq;
+  bf16x8 kf[8], vf[8];
+  {
+    const size_t off = (size_t)krow * kstride + (size_t)g * HEAD_DIM + lh * 8;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      kf[ks] = krow < T ? as_bf16x8(ldg16(k + off + ks * 16)) : zero_bf16x8();
+      vf[ks] = krow < T ? as_bf16x8(ldg16(v + off + ks * 16)) : zero_bf16x8();
+    }
+  }
+
+  f32x16 dka[4], dva[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    dka[db] = zero_f32x16();
+    dva[db] = zero_f32x16();
+  }
+
+  // rows handled by this lane when staging: (lane >> 4) + 4 j, columns (lane & 15) * 8
+  const int srow = lane >> 4, scol = (lane & 15) * 8;
+  const bool keys_full = (k1 - k0) == TILE;
+
+  for (int hh = wave; hh < G; hh += DKDV_WAVES) {
+    const int head = g * G + hh;
+    for (int i = 0; i < nqb; ++i) {
+      const int qb = k0 + i * QBLK;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int row = srow + 4 * j;
+        const int qi = qb + row;
+        uint4 qv = make_uint4(0u, 0u, 0u, 0u), dv4 = make_uint4(0u, 0u, 0u, 0u);
+        if (qi < T) {
+          const size_t off = (size_t)qi * qstride + (size_t)head * HEAD_DIM + scol;
+          qv = ldg16(q + off);
+          dv4 = ldg16(dout + off);
+        }
+        *reinterpret_cast<uint4*>(Qs + row * LDS_PITCH + scol) = qv;
+        *reinterpret_cast<uint4*>(Ds + row * LDS_PITCH + scol) = dv4;
+      }
+      if (lane < QBLK) {
+        const int qi = qb + lane;
+        Ls[lane] = qi < T ? lse[(size_t)head * T + qi] * LOG2E : 0.f;
+        Dd[lane] = qi < T ? dbuf[(size_t)head * T + qi] : 0.f;
+      }
+      __syncthreads();
+
+      // S[q][key] = Q K^T and dP = dO V^T: s[r] holds query qb + 8(r/4) + 4 lh + r%4, key k0 + lq
+      f32x16 s = zero_f32x16(), dp = zero_f32x16();
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        s = mfma32(lds_frag_cols(Qs, ks, lane), kf[ks], s);
+        dp = mfma32(lds_frag_cols(Ds, ks, lane), vf[ks], dp);
+      }
+      const bool full = keys_full && (qb + QBLK - 1 < b) && (qb >= k0 + TILE - 1) &&
+                        (window <= 0 || qb + QBLK - 1 < k0 + window);
+      bf16x8 pf[2], dsf[2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 l4 = *reinterpret_cast<const float4*>(Ls + 8 * j + 4 * lh);
+        const float4 d4 = *reinterpret_cast<const float4*>(Dd + 8 * j + 4 * lh);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * j + e;
+          const int qi = qb + 8 * j + 4 * lh + e;
+          const bool vis = full || (krow < k1 && qi < b && krow <= qi &&
+                                    (window <= 0 || krow > qi - window));
+          const float p = vis ? exp2_fast(s[r] * scale_log2 - lv[e]) : 0.f;
+          pf[r >> 3][r & 7] = (bf16)p;
+          dsf[r >> 3][r & 7] = (bf16)(p * (dp[r] - dd[e]));
+        }
+      }
+      // dV[key][d] += P^T dO ; dK[key][d] += dS^T Q  (scale applied at the end)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          dva[db] = mfma32(pf[t], lds_frag_rows(Ds + db * 32, t, lane), dva[db]);
+          dka[db] = mfma32(dsf[t], lds_frag_rows(Qs + db * 32, t, lane), dka[db]);
+        }
+    }
+  }
+
+  // Head-group reduction in a fixed order (wave 0 + 1 + 2 + 3), then store.
+  float* red = reinterpret_cast<float*>(smem);
+  const int okey = tid >> 3, od = (tid & 7) * 16;
+  for (int pass = 0; pass < 2; ++pass) {
+    __syncthreads();
+    float* mine = red + (size_t)wave * TILE * RED_PITCH;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = (r >> 2) * 8 + lh * 4 + (r & 3);
+        mine[key * RED_PITCH + db * 32 + lq] = pass == 0 ? dka[db][r] : dva[db][r];
+      }
+    __syncthreads();
+    if (k0 + okey < k1) {
+      const float mul = pass == 0 ? scale : 1.f;
+      bf16* dst = (pass == 0 ? dk : dv) + (size_t)(k0 + okey) * kstride +
+                  (size_t)g * HEAD_DIM + od;
+#pragma unroll
+      for (int e = 0; e < 16; e += 4) {
+        float acc4[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          float sum = 0.f;
+#pragma unroll
+          for (int w = 0; w < DKDV_WAVES; ++w)
+            sum += red[(size_t)w * TILE * RED_PITCH + okey * RED_PITCH + od + e + x];
+          acc4[x] = sum * mul;
+        }
+        store_bf16x4(dst + e, acc4[0], acc4[1], acc4[2], acc4[3]);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_backward(const void* q, const void* k, const void* v, const void* out,
+                           const float* lse, const void* dout, const Problem& p, void* dq,
+                           void* dk, void* dv, void* workspace, const WorkspaceLayout& w,
+                           hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  float* dbuf = reinterpret_cast<float*>(ws + w.dbuf);
+  const int* header = reinterpret_cast<const int*>(ws + w.header);
+  const unsigned grid_q = (unsigned)(w.tile_cap * (size_t)(p.num_q_heads / 4));
+  hipLaunchKernelGGL(dq_kernel, dim3(grid_q), dim3(BWD_THREADS), 0, stream,
+                     static_cast<const bf16*>(q), static_cast<const bf16*>(k),
+                     static_cast<const bf16*>(v), static_cast<const bf16*>(out),
+                     static_cast<const bf16*>(dout), lse, header,
+                     reinterpret_cast<const Tile*>(ws + w.tiles_fwd), p.total_tokens,
+                     p.num_q_heads, p.num_kv_heads, p.window, p.scale * LOG2E, p.scale,
+                     static_cast<bf16*>(dq), dbuf);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned grid_k = (unsigned)(w.tile_cap * (size_t)p.num_kv_heads);
+  hipLaunchKernelGGL(dkdv_kernel, dim3(grid_k), dim3(BWD_THREADS), 0, stream,
+                     static_cast<const bf16*>(q), static_cast<const bf16*>(k),
+                     static_cast<const bf16*>(v), static_cast<const bf16*>(dout), lse, dbuf,
+                     header, reinterpret_cast<const Tile*>(ws + w.tiles_bwd), p.total_tokens,
+                     p.num_q_heads, p.num_kv_heads, p.window, p.scale * LOG2E, p.scale,
+                     static_cast<bf16*>(dk), static_cast<bf16*>(dv));
+  return hipGetLastError();
+}
+
+}  // namespace attn

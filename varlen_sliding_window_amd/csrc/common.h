@@ -1,0 +1,72 @@
+// Shared definitions of the gfx950 attention kernels: fragment types, tile
+// geometry, the schedule's tile record and the workspace layout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int HEAD_DIM = 128;
+// Rows of one tile: a q-tile (forward, dQ) or a k-tile (dK/dV) is at most
+// TILE consecutive tokens of one segment, starting at the segment start.
+constexpr int TILE = 32;
+// Keys per inner step of the forward and dQ kernels.
+constexpr int KBLK = 64;
+// Queries per inner step of the dK/dV kernel.
+constexpr int QBLK = 32;
+// LDS row pitch in bf16 elements: 128 + 16 pad (288 bytes).  The pad keeps
+// both the 16-byte row reads and the transposing 8-byte reads spread over
+// the banks.
+constexpr int LDS_PITCH = HEAD_DIM + 16;
+// Cost buckets of the longest-first sort.
+constexpr int SORT_BINS = 1024;
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+// One tile of one segment: tokens [t0, t1) of segment [seg_a, seg_b).
+struct __attribute__((aligned(16))) Tile {
+  int t0, t1, seg_a, seg_b;
+};
+
+// Workspace: [header | forward-order tiles | backward-order tiles |
+//             per-segment tile offsets | D (fp32 [Hq, T])]
+struct WorkspaceLayout {
+  size_t header, tiles_fwd, tiles_bwd, seg_offsets, dbuf, total;
+  size_t tile_cap;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline size_t tile_capacity(int64_t total_tokens, int64_t num_seqs) {
+  // sum over segments of ceil(L / TILE) <= T / TILE + num_seqs
+  return (size_t)((total_tokens + TILE - 1) / TILE) + (size_t)num_seqs;
+}
+
+inline WorkspaceLayout workspace_layout(int64_t total_tokens, int64_t num_seqs,
+                                        int64_t num_q_heads) {
+  WorkspaceLayout w;
+  w.tile_cap = tile_capacity(total_tokens, num_seqs);
+  w.header = 0;
+  w.tiles_fwd = 256;
+  w.tiles_bwd = w.tiles_fwd + align256(w.tile_cap * sizeof(Tile));
+  w.seg_offsets = w.tiles_bwd + align256(w.tile_cap * sizeof(Tile));
+  w.dbuf = w.seg_offsets + align256((size_t)(num_seqs + 1) * sizeof(int));
+  w.total = w.dbuf + align256((size_t)num_q_heads * (size_t)total_tokens * sizeof(float));
+  return w;
+}
+
+// Visible key range of query i in segment starting at a (inclusive bounds).
+__device__ __forceinline__ int first_visible_key(int i, int a, int window) {
+  return window > 0 ? max(a, i - window + 1) : a;
+}
+
+}  // namespace attn

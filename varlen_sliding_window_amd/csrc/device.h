@@ -1,0 +1,82 @@
+// Device helpers shared by the forward and backward kernels.
+//
+// MFMA fragment layouts used throughout (v_mfma_f32_32x32x16_bf16, one wave
+// of 64 lanes, l = lane, h = l / 32, c = l % 32):
+//   A (32 x 16): lane l holds A[c][8h + i], i = 0..7
+//   B (16 x 32): lane l holds B[8h + i][c]
+//   D (32 x 32): lane l, register r holds D[8(r/4) + 4h + (r%4)][c]
+// A result's row index lives in registers and its column in the lane, so a
+// result can feed the next product's reduction (k) index directly when the
+// k order is permuted to match: for 16-wide step t of a 32-row result,
+// element i of lane half h is row 16t + 8(i/4) + 4h + (i%4), i.e. register
+// r = 8t + i.  The other operand is read in the same permuted order with two
+// transposing LDS reads of 4 consecutive rows each (rows 16t + 4h + 0..3 and
+// 16t + 8 + 4h + 0..3).
+#pragma once
+
+#include "common.h"
+
+namespace attn {
+
+__device__ __forceinline__ uint4 ldg16(const bf16* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  return __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u));
+}
+
+__device__ __forceinline__ f32x16 zero_f32x16() {
+  f32x16 z;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) z[r] = 0.f;
+  return z;
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each block of 16 lanes,
+// source lane 4i + a points at row i, columns 4a..4a+3 of a 4 x 16 bf16
+// sub-matrix; destination lane 4a + b receives column 4a + b, rows 0..3.
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+// A or B fragment whose lane index runs over the columns of a row-major LDS
+// tile and whose 8 register elements run over rows 16t + 8(i/4) + 4h + i%4:
+// `tile` points at row 0, column 0 of the 32 columns this fragment covers.
+__device__ __forceinline__ bf16x8 lds_frag_rows(const bf16* tile, int t, int lane) {
+  const int h = lane >> 5;
+  const bf16* p = tile + (16 * t + 4 * h + ((lane & 15) >> 2)) * LDS_PITCH + (lane & 16) +
+                  4 * (lane & 3);
+  const bf16x4 lo = lds_read_tr(p);
+  const bf16x4 hi = lds_read_tr(p + 8 * LDS_PITCH);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// A or B fragment whose lane index runs over rows (c = lane % 32) and whose
+// register elements are 8 consecutive columns 16 ks + 8h + 0..7.
+__device__ __forceinline__ bf16x8 lds_frag_cols(const bf16* tile, int ks, int lane) {
+  return *reinterpret_cast<const bf16x8*>(tile + (lane & 31) * LDS_PITCH + ks * 16 +
+                                          (lane >> 5) * 8);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ void store_bf16x4(bf16* p, float a, float b, float c, float d) {
+  bf16x4 v;
+  v[0] = (bf16)a;
+  v[1] = (bf16)b;
+  v[2] = (bf16)c;
+  v[3] = (bf16)d;
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+
+}  // namespace attn

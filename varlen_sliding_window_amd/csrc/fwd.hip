@@ -1,0 +1,181 @@
+// Forward kernel: out and lse of document-masked causal GQA attention.
+//
+// One work-group (4 waves) takes one q-tile of TILE = 32 rows and the 4
+// query heads of one key-value head group (research.dws.rip/llm/kernels,
+// Fig. 2 "Benchmark setup": 8 query heads share 2 key-value heads, so 4 query
+// heads read the same K/V).  Each wave owns one head: its 32 q rows stay in
+// registers as MFMA operands, while the work-group streams the visible keys
+// through LDS in KBLK = 64-key blocks shared by the 4 heads.
+//
+// The wave computes S^T = K Q^T (keys x queries), so each lane holds one
+// query's scores in registers: the row max needs one cross-half exchange,
+// the row sum is kept per lane and combined once at the end, and P^T feeds
+// the O^T = V^T P^T product straight from registers (V^T read from the
+// natural-layout V tile with transposing LDS reads).  Softmax runs in the
+// exp2 domain with scale * log2(e) folded into one multiply.  Key blocks are
+// aligned to the tile end and walked from the diagonal backwards, so only
+// the diagonal block and the blocks at the segment start or window edge
+// need the mask.
+#include "device.h"
+#include "launch.h"
+
+namespace attn {
+namespace {
+
+constexpr int FWD_THREADS = 256;
+
+__global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
+    int window, float scale_log2, bf16* __restrict__ out, float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(16))) bf16 Ks[KBLK * LDS_PITCH];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[KBLK * LDS_PITCH];
+
+  const int chunks = Hq >> 2;
+  const int item = blockIdx.x / chunks;
+  const int hc = blockIdx.x - item * chunks;
+  if (item >= header[0]) return;
+  const Tile tl = tiles[item];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, lh = lane >> 5, lq = lane & 31;
+  const int head = hc * 4 + wave;
+  const int g = (hc * 4) / (Hq / Hkv);
+  const int q0 = tl.t0, q1 = tl.t1, a = tl.seg_a;
+  const int klo = first_visible_key(q0, a, window);
+  const int nblk = (q1 - klo + KBLK - 1) / KBLK;
+  const int qrow = q0 + lq;
+  const size_t qstride = (size_t)Hq * HEAD_DIM;
+  const size_t kstride = (size_t)Hkv * HEAD_DIM;
+
+  // Q^T as the B operand: lane holds q[qrow][16 ks + 8 lh + 0..7]
+  bf16x8 qf[8];
+  {
+    const bf16* qp = q + (size_t)qrow * qstride + (size_t)head * HEAD_DIM + lh * 8;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = qrow < T ? as_bf16x8(ldg16(qp + ks * 16)) : zero_bf16x8();
+  }
+
+  // K/V staging: thread copies rows srow + 16 i (i = 0..3), 8 columns at scol
+  const int srow = tid >> 4, scol = (tid & 15) * 8;
+  uint4 kr[4], vr[4];
+  auto gload = [&](int kb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = kb + srow + 16 * i;   // key <= q1 - 1 < T always
+      if (key >= 0) {
+        const size_t off = (size_t)key * kstride + (size_t)g * HEAD_DIM + scol;
+        kr[i] = ldg16(k + off);
+        vr[i] = ldg16(v + off);
+      } else {
+        kr[i] = make_uint4(0u, 0u, 0u, 0u);
+        vr[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  };
+
+  f32x16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = zero_f32x16();
+  float m = -INFINITY, lsum = 0.f;
+  const int full_lo = first_visible_key(q0 + TILE - 1, a, window);
+  const int my_lo = first_visible_key(qrow, a, window);
+
+  gload(q1 - KBLK);
+  for (int n = 0; n < nblk; ++n) {
+    const int kb = q1 - KBLK * (n + 1);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<uint4*>(Ks + (srow + 16 * i) * LDS_PITCH + scol) = kr[i];
+      *reinterpret_cast<uint4*>(Vs + (srow + 16 * i) * LDS_PITCH + scol) = vr[i];
+    }
+    __syncthreads();
+    if (n + 1 < nblk) gload(kb - KBLK);
+
+    // S^T for keys kb + 32 h2 + [0, 32): s[h2][r] = q[qrow] . k[kb + 32 h2 + 8(r/4) + 4 lh + r%4]
+    f32x16 s[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      s[h2] = zero_f32x16();
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        s[h2] = mfma32(lds_frag_cols(Ks + h2 * 32 * LDS_PITCH, ks, lane), qf[ks], s[h2]);
+    }
+    const bool full = (kb + KBLK - 1 <= q0) && (kb >= full_lo);
+    if (!full) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb + h2 * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
+          if (key < my_lo || key > qrow) s[h2][r] = -INFINITY;
+        }
+    }
+
+    // online softmax (log2 domain) for this lane's query
+    float mx = -INFINITY;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[h2][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(m, mx * scale_log2);
+    const float mref = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = exp2_fast(m - mref);
+    bf16x8 pf[4];
+    float rs = 0.f;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2_fast(s[h2][r] * scale_log2 - mref);
+        rs += p;
+        pf[h2 * 2 + (r >> 3)][r & 7] = (bf16)p;
+      }
+    lsum = lsum * alpha + rs;
+    m = mnew;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+
+    // O^T[d][q] += sum_key V^T[d][key] P^T[key][q]
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        o[db] = mfma32(lds_frag_rows(Vs + db * 32, t, lane), pf[t], o[db]);
+  }
+
+  const float lt = lsum + __shfl_xor(lsum, 32);
+  if (qrow < q1) {
+    const float inv = 1.f / lt;
+    bf16* op = out + (size_t)qrow * qstride + (size_t)head * HEAD_DIM + lh * 4;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        store_bf16x4(op + db * 32 + j * 8, o[db][4 * j] * inv, o[db][4 * j + 1] * inv,
+                     o[db][4 * j + 2] * inv, o[db][4 * j + 3] * inv);
+    if (lh == 0) lse[(size_t)head * T + qrow] = (m + log2_fast(lt)) * LN2;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_forward(const void* q, const void* k, const void* v, const Problem& p,
+                          void* out, float* lse, void* workspace, const WorkspaceLayout& w,
+                          hipStream_t stream) {
+  const char* ws = static_cast<const char*>(workspace);
+  const unsigned grid = (unsigned)(w.tile_cap * (size_t)(p.num_q_heads / 4));
+  hipLaunchKernelGGL(fwd_kernel, dim3(grid), dim3(FWD_THREADS), 0, stream,
+                     static_cast<const bf16*>(q), static_cast<const bf16*>(k),
+                     static_cast<const bf16*>(v), reinterpret_cast<const int*>(ws + w.header),
+                     reinterpret_cast<const Tile*>(ws + w.tiles_fwd), p.total_tokens,
+                     p.num_q_heads, p.num_kv_heads, p.window, p.scale * LOG2E,
+                     static_cast<bf16*>(out), lse);
+  return hipGetLastError();
+}
+
+}  // namespace attn

@@ -1,0 +1,26 @@
+// Internal launchers, one per kernel family (defined next to their kernels).
+#pragma once
+
+#include "common.h"
+
+namespace attn {
+
+struct Problem {
+  int total_tokens, num_seqs, num_q_heads, num_kv_heads, window;
+  float scale;
+};
+
+// Builds both sorted tile lists in the workspace from cu_seqlens.
+hipError_t launch_schedule(const int32_t* cu_seqlens, const Problem& p, void* workspace,
+                           const WorkspaceLayout& w, hipStream_t stream);
+
+hipError_t launch_forward(const void* q, const void* k, const void* v, const Problem& p,
+                          void* out, float* lse, void* workspace, const WorkspaceLayout& w,
+                          hipStream_t stream);
+
+hipError_t launch_backward(const void* q, const void* k, const void* v, const void* out,
+                           const float* lse, const void* dout, const Problem& p, void* dq,
+                           void* dk, void* dv, void* workspace, const WorkspaceLayout& w,
+                           hipStream_t stream);
+
+}  // namespace attn

@@ -1,0 +1,156 @@
+// Tile scheduler: turns cu_seqlens into the two work lists of one call.
+//
+// Segments are cut into tiles of TILE tokens starting at each segment start
+// (the last tile of a segment may be short).  Because no token attends
+// across its own document boundary (research.dws.rip/llm/kernels, section
+// 01 "How it was measured"), a tile only ever meets keys (forward, dQ) or
+// queries (dK/dV) of its own segment, so fully masked tiles are never
+// emitted.  The same tiles are sorted twice, longest first:
+//   forward / dQ order : by the number of KBLK-key steps over the visible
+//                        keys [max(a, t0 - W + 1), t1)
+//   dK / dV order      : by the number of QBLK-query steps over the queries
+//                        that see the tile, [t0, min(b, t1 - 1 + W))
+// Work-groups are dispatched in list order, so the hardware's in-order
+// dispatch gives a greedy longest-processing-time-first assignment.
+//
+// Everything runs on the device (one work-group), so nothing waits for the
+// host and a call can be captured in a graph; the work lists live in the
+// caller's workspace.  Segment bounds are clamped into [0, T] so that even
+// malformed cu_seqlens cannot send a kernel outside its buffers.
+#include "common.h"
+#include "launch.h"
+
+namespace attn {
+namespace {
+
+constexpr int SCHED_THREADS = 1024;
+static_assert(SORT_BINS == SCHED_THREADS, "one sort bin per thread");
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return min(max(x, lo), hi); }
+
+// Inclusive block-wide scan; *total receives the sum over the block.
+__device__ int block_scan(int v, int* buf, int* total) {
+  const int tid = threadIdx.x;
+  buf[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < SCHED_THREADS; off <<= 1) {
+    const int add = tid >= off ? buf[tid - off] : 0;
+    __syncthreads();
+    buf[tid] += add;
+    __syncthreads();
+  }
+  const int r = buf[tid];
+  *total = buf[SCHED_THREADS - 1];
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ Tile tile_at(int i, const int* __restrict__ seg_off,
+                                        const int32_t* __restrict__ cu, int nseq, int T) {
+  // largest s < nseq with seg_off[s] <= i (empty segments share an offset with the next)
+  int lo = 0, hi = nseq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (seg_off[mid] <= i) lo = mid; else hi = mid - 1;
+  }
+  const int a = clampi(cu[lo], 0, T);
+  const int b = clampi(cu[lo + 1], a, T);
+  // With valid boundaries t0 lies in [a, b).  Malformed ones (offsets that
+  // overflowed) give an empty tile at b, which every kernel skips safely.
+  long long t0 = (long long)a + ((long long)i - seg_off[lo]) * TILE;
+  if (t0 < a || t0 > b) t0 = b;
+  Tile t;
+  t.t0 = (int)t0;
+  t.t1 = (int)min(t0 + TILE, (long long)b);
+  t.seg_a = a;
+  t.seg_b = b;
+  return t;
+}
+
+__device__ __forceinline__ int fwd_bin(const Tile& t, int window) {
+  const int klo = first_visible_key(t.t0, t.seg_a, window);
+  return min((t.t1 - klo + KBLK - 1) / KBLK, SORT_BINS - 1);
+}
+
+__device__ __forceinline__ int bwd_bin(const Tile& t, int window) {
+  const int qhi = window > 0 ? min(t.seg_b, t.t1 - 1 + window) : t.seg_b;
+  return min((qhi - t.t0 + QBLK - 1) / QBLK, SORT_BINS - 1);
+}
+
+__global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
+    const int32_t* __restrict__ cu, int nseq, int T, int window, int tile_cap,
+    int* __restrict__ header,
+    Tile* __restrict__ fwd_list, Tile* __restrict__ bwd_list, int* __restrict__ seg_off) {
+  __shared__ int buf[SCHED_THREADS];
+  __shared__ int hist_f[SORT_BINS];
+  __shared__ int hist_b[SORT_BINS];
+  const int tid = threadIdx.x;
+
+  // 1. tiles per segment -> exclusive offsets
+  int carry = 0;
+  for (int base = 0; base < nseq; base += SCHED_THREADS) {
+    const int s = base + tid;
+    int n = 0;
+    if (s < nseq) {
+      const int a = clampi(cu[s], 0, T);
+      const int b = clampi(cu[s + 1], a, T);
+      n = (b - a + TILE - 1) / TILE;
+    }
+    int total;
+    const int incl = block_scan(n, buf, &total);
+    if (s < nseq) seg_off[s] = carry + incl - n;
+    carry += total;
+  }
+  // Valid boundaries give at most tile_cap tiles; malformed (overlapping) ones
+  // are cut there so the lists never overflow the workspace.
+  const int ntiles = min(carry, tile_cap);
+  hist_f[tid] = 0;
+  hist_b[tid] = 0;
+  if (tid == 0) seg_off[nseq] = ntiles;
+  __syncthreads();
+
+  // 2. histogram of costs
+  for (int i = tid; i < ntiles; i += SCHED_THREADS) {
+    const Tile t = tile_at(i, seg_off, cu, nseq, T);
+    atomicAdd(&hist_f[fwd_bin(t, window)], 1);
+    atomicAdd(&hist_b[bwd_bin(t, window)], 1);
+  }
+  __syncthreads();
+
+  // 3. bucket start offsets, most expensive bucket first
+  {
+    const int c = SORT_BINS - 1 - tid;
+    const int vf = hist_f[c];
+    const int vb = hist_b[c];
+    int total;
+    const int incf = block_scan(vf, buf, &total);
+    const int incb = block_scan(vb, buf, &total);
+    hist_f[c] = incf - vf;
+    hist_b[c] = incb - vb;
+  }
+  __syncthreads();
+
+  // 4. scatter (order inside a bucket is arbitrary; results do not depend on it)
+  for (int i = tid; i < ntiles; i += SCHED_THREADS) {
+    const Tile t = tile_at(i, seg_off, cu, nseq, T);
+    fwd_list[atomicAdd(&hist_f[fwd_bin(t, window)], 1)] = t;
+    bwd_list[atomicAdd(&hist_b[bwd_bin(t, window)], 1)] = t;
+  }
+  if (tid == 0) header[0] = ntiles;
+}
+
+}  // namespace
+
+hipError_t launch_schedule(const int32_t* cu_seqlens, const Problem& p, void* workspace,
+                           const WorkspaceLayout& w, hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(SCHED_THREADS), 0, stream, cu_seqlens,
+                     p.num_seqs, p.total_tokens, p.window, (int)w.tile_cap,
+                     reinterpret_cast<int*>(ws + w.header),
+                     reinterpret_cast<Tile*>(ws + w.tiles_fwd),
+                     reinterpret_cast<Tile*>(ws + w.tiles_bwd),
+                     reinterpret_cast<int*>(ws + w.seg_offsets));
+  return hipGetLastError();
+}
+
+}  // namespace attn
