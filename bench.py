@@ -1,0 +1,290 @@
+#!/usr/bin/env python3
+"""Throughput of document-masked causal GQA attention, forward + backward, on MI355X.
+
+One step is one pass of the whole hot path over one seeded 16,384-token
+microbatch packed at context 4,096 (8 query / 2 key-value heads of 128): a
+local layer with a 512-token window, then a global layer, each forward +
+backward through the C ABI (schedule, forward, dQ + D, dK/dV kernels).  The
+two layers share the microbatch's cu_seqlens and draw their own q/k/v/dout.
+This is the workload the kernel benchmarks page times in its Figs. 3 and 4
+(research.dws.rip/llm/kernels), with synthetic documents standing in for the
+page's real token shards.
+
+Throughput counts 4*d flops per unmasked (query, key) pair per query head
+forward and 10*d backward, pairs counted exactly from cu_seqlens and the
+window.  Prints one JSON line.
+
+    python bench.py [--steps 20] [--warmup 5] [--workload ctx4096_w512+global]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+
+WORKLOADS = {
+    # name: (list of (layer label, config name)), shared cu_seqlens from the first config
+    "ctx4096_w512+global": [("window512", "ctx4096_w512"), ("global", "ctx4096_global")],
+    "ctx512_w512": [("window512", "ctx512_w512")],
+    "ctx4096_w512": [("window512", "ctx4096_w512")],
+    "ctx4096_global": [("global", "ctx4096_global")],
+    "ctx1024_global": [("global", "ctx1024_global")],
+    "ctx2048_global": [("global", "ctx2048_global")],
+    "stack_ctx4096": [("window512", "ctx4096_w512")] * 15 + [("global", "ctx4096_global")] * 5,
+    "stack_ctx4096_h16": [("window512", "ctx4096_w512_h16")] * 15
+    + [("global", "ctx4096_global_h16")] * 5,
+}
+
+# Flops each kernel must execute per unmasked pair per query head, in units of d
+# (each product of a d-long row pair is 2d flops): forward S and PV; dQ kernel
+# recomputes S and dP, then dQ; dK/dV kernel recomputes S and dP, then dV and dK.
+KERNEL_FLOPS_PER_PAIR_D = {"forward": 4, "dq": 6, "dkdv": 8}
+
+
+def cpu_info():
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model
+
+
+def build_layers(workload: str, seed: int, device):
+    import torch
+    from synthetic import CONFIGS, make_cu_seqlens, make_layer
+    from varlen_sliding_window_amd.flops import attention_flops
+    import varlen_sliding_window_amd as attn
+
+    spec = WORKLOADS[workload]
+    cu, _ = make_cu_seqlens(CONFIGS[spec[0][1]], seed)
+    layers = []
+    for idx, (label, cname) in enumerate(spec):
+        cfg = CONFIGS[cname]
+        mb = make_layer(cfg, seed, idx, cu)
+
+        def dev(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+                torch.bfloat16).to(device)
+
+        q, k, v, do = dev(mb.q_bits), dev(mb.k_bits), dev(mb.v_bits), dev(mb.dout_bits)
+        t, hq, d = q.shape
+        lay = {
+            "label": label, "cfg": cfg, "mb": mb, "q": q, "k": k, "v": v, "do": do,
+            "cu": torch.from_numpy(cu.astype(np.int32)).to(device),
+            "max_seqlen": mb.max_seqlen, "window": cfg.window, "scale": cfg.scale,
+            "out": torch.empty_like(q), "lse": torch.empty((hq, t), dtype=torch.float32,
+                                                           device=device),
+            "dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+            "ws": attn.new_workspace(t, len(cu) - 1, hq, k.shape[1], d, mb.max_seqlen,
+                                     cfg.window, device),
+            "flops": attention_flops(cu, cfg.window, hq, d),
+        }
+        layers.append(lay)
+    return cu, layers
+
+
+def run_layer(attn, L):
+    attn.fwd(L["q"], L["k"], L["v"], L["cu"], L["max_seqlen"], L["window"], L["scale"],
+             out=L["out"], lse=L["lse"], workspace=L["ws"])
+    attn.bwd(L["q"], L["k"], L["v"], L["out"], L["lse"], L["do"], L["cu"], L["max_seqlen"],
+             L["window"], L["scale"], dq=L["dq"], dk=L["dk"], dv=L["dv"], workspace=L["ws"])
+
+
+def cpu_baseline(layer, seed):
+    """The CPU oracle, as it stands, on one layer of the same workload."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle import attention_backward
+
+    cores = len(os.sched_getaffinity(0))
+    mb = layer["mb"]
+    with threadpool_limits(limits=cores):
+        used = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        t0 = time.perf_counter()
+        attention_backward(mb.f32("q"), mb.f32("k"), mb.f32("v"), mb.f32("dout"),
+                           mb.cu_seqlens, layer["window"], layer["scale"])
+        secs = time.perf_counter() - t0
+    fl = layer["flops"]["fwd_bwd"]
+    return {"value": fl / secs / 1e12, "unit": "TFLOP/s", "cores": int(used), "kind": "oracle",
+            "seconds": secs, "cpu": cpu_info(),
+            "sample": (f"one {layer['label']} layer forward+backward of the seed-{seed} "
+                       f"microbatch ({mb.num_seqs} segments, all {mb.cfg.num_q_heads} query "
+                       f"heads, {layer['flops']['pairs']} pairs/head), fp64 NumPy")}
+
+
+def load_traffic(kernel: str, workload_label: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
+    were taken on the current kernel sources (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "varlen_sliding_window_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    if data.get("sources_sha256") != h.hexdigest():
+        return None
+    entry = data.get("kernels", {}).get(f"{workload_label}/{kernel}")
+    return None if entry is None else entry.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--workload", default="ctx4096_w512+global", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip timing the CPU oracle (profiling runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import varlen_sliding_window_amd as attn
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    attn.load_library()
+    device = torch.device("cuda", 0)
+    cu, layers = build_layers(args.workload, args.seed, device)
+    print(f"[bench] workload {args.workload}: {len(layers)} layer(s), {len(cu) - 1} segments, "
+          f"max_seqlen {layers[0]['max_seqlen']}", file=sys.stderr, flush=True)
+
+    def step(events=None):
+        for i, L in enumerate(layers):
+            if events is not None:
+                events[i][0].record()
+            run_layer(attn, L)
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in layers] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    step_flops = sum(L["flops"]["fwd_bwd"] for L in layers)
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    per_label = {}
+    for i, L in enumerate(layers):
+        times = [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
+        d = per_label.setdefault(L["label"], {"times": [], "flops": 0, "count": 0})
+        d["times"].extend(times)
+        d["flops"] += L["flops"]["fwd_bwd"]
+        d["count"] += 1
+    layer_report = {}
+    for label, d in per_label.items():
+        med = statistics.median(d["times"])
+        fl = d["flops"] / d["count"]
+        layer_report[label] = {"ms_fwd_bwd_median": med,
+                               "ms_p10": float(np.percentile(d["times"], 10)),
+                               "ms_p90": float(np.percentile(d["times"], 90)),
+                               "gflop": fl / 1e9, "tflops": fl / (med * 1e-3) / 1e12}
+
+    # per-kernel durations: HIP events around each launch, one pass per layer label
+    kernels = {}
+    for label in per_label:
+        attn.profile_start()
+        for _ in range(args.steps):
+            for L in layers:
+                if L["label"] == label:
+                    run_layer(attn, L)
+        torch.cuda.synchronize()
+        stats = attn.profile_stop()
+        lay = next(L for L in layers if L["label"] == label)
+        for kname, st in stats.items():
+            entry = dict(st)
+            per_d = KERNEL_FLOPS_PER_PAIR_D.get(kname)
+            if per_d is not None:
+                fl = per_d * lay["cfg"].head_dim * lay["flops"]["pairs"] * lay["cfg"].num_q_heads
+                entry["flops_per_launch"] = fl
+                entry["tflops"] = fl / (st["avg_ms"] * 1e-3) / 1e12
+            kernels[f"{label}/{kname}"] = entry
+
+    dom_key = max(kernels, key=lambda k: kernels[k]["total_ms"] / max(
+        1, sum(1 for L in layers if L["label"] == k.split("/")[0])))
+    dom = kernels[dom_key]
+    achieved = dom.get("tflops", 0.0)
+    roofline = {"bound": "mfma", "kernel": dom_key, "achieved": achieved,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "avg_ms": dom["avg_ms"], "flops_per_launch": dom.get("flops_per_launch"),
+                "traffic": load_traffic(dom_key.split("/")[1], dom_key.split("/")[0])}
+
+    result = {
+        "metric": "fwd+bwd TFLOPS per 16,384-token microbatch (window-512 and global layers, "
+                  "context 4,096)",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded lognormal document packing, N(0,1) bf16 tensors)",
+        "config": {
+            "workload": args.workload,
+            "total_tokens": int(cu[-1]),
+            "ctx": layers[0]["cfg"].ctx,
+            "num_q_heads": layers[0]["cfg"].num_q_heads,
+            "num_kv_heads": layers[0]["cfg"].num_kv_heads,
+            "head_dim": layers[0]["cfg"].head_dim,
+            "layers": [L["label"] for L in layers],
+            "seed": args.seed,
+            "num_seqs": len(cu) - 1,
+            "max_seqlen": layers[0]["max_seqlen"],
+            "gflop_per_step": step_flops / 1e9,
+        },
+        "layers": layer_report,
+        "kernels": kernels,
+        "roofline": roofline,
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on one layer", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(layers[0], args.seed)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

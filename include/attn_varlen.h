@@ -127,6 +127,29 @@ const char* attn_varlen_strerror(attn_status s);
 /* Library version as major*10000 + minor*100 + patch. */
 int32_t attn_varlen_version(void);
 
+/*
+ * Kernel timing, a measurement aid (off by default; no cost when off).
+ * attn_varlen_profile_start() clears earlier records and makes every later
+ * fwd/bwd call bracket each of its kernel launches with a pair of HIP
+ * events recorded on the call's stream.  attn_varlen_profile_stop() turns
+ * recording off, waits for the recorded events, and writes up to `cap`
+ * per-kernel summaries (kernels in launch-pipeline order: "schedule",
+ * "forward", "dq", "dkdv"; only kernels that ran).  It returns the number of
+ * kernels that ran (which may exceed cap), or a negative attn_status.  The
+ * events add a few microseconds per launch, so time whole calls with
+ * recording off.  Not for use while another thread is issuing calls.
+ */
+typedef struct {
+  char name[32];
+  int32_t launches;
+  double total_ms;   /* sum of event-to-event durations */
+  double min_ms;
+  double max_ms;
+} attn_kernel_stats;
+
+attn_status attn_varlen_profile_start(void);
+int32_t attn_varlen_profile_stop(attn_kernel_stats* stats, int32_t cap);
+
 #ifdef __cplusplus
 }
 #endif

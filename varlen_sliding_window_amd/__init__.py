@@ -5,8 +5,8 @@ the computation runs in hand-written HIP kernels.  ``flops`` holds the exact
 work counts used for throughput.
 """
 from . import flops
-from ._binding import (LIBRARY_PATH, AttnError, bwd, fwd, load_library, new_workspace, strerror,
-                       workspace_size)
+from ._binding import (LIBRARY_PATH, AttnError, bwd, fwd, load_library, new_workspace,
+                       profile_start, profile_stop, strerror, workspace_size)
 
 __all__ = ["LIBRARY_PATH", "AttnError", "bwd", "flops", "fwd", "load_library", "new_workspace",
-           "strerror", "workspace_size"]
+           "profile_start", "profile_stop", "strerror", "workspace_size"]

@@ -23,6 +23,12 @@ STATUS_NAMES = {0: "ATTN_OK", -1: "ATTN_EINVAL", -2: "ATTN_EUNSUPPORTED",
 _lib = None
 
 
+class KernelStats(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int32),
+                ("total_ms", ctypes.c_double), ("min_ms", ctypes.c_double),
+                ("max_ms", ctypes.c_double)]
+
+
 class AttnError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -52,6 +58,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_varlen_strerror.restype = ctypes.c_char_p
     lib.attn_varlen_version.argtypes = []
     lib.attn_varlen_version.restype = i32
+    lib.attn_varlen_profile_start.argtypes = []
+    lib.attn_varlen_profile_start.restype = ctypes.c_int
+    lib.attn_varlen_profile_stop.argtypes = [ctypes.POINTER(KernelStats), i32]
+    lib.attn_varlen_profile_stop.restype = i32
     if path is None:
         _lib = lib
     return lib
@@ -154,3 +164,24 @@ def bwd(q, k, v, out, lse, dout, cu_seqlens, max_seqlen: int, window: int,
     if st != ATTN_OK:
         raise AttnError(st, "attn_varlen_bwd")
     return dq, dk, dv
+
+
+def profile_start() -> None:
+    """Bracket every following kernel launch with HIP events on its stream."""
+    st = load_library().attn_varlen_profile_start()
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_varlen_profile_start")
+
+
+def profile_stop() -> dict:
+    """Stop recording; {kernel: {launches, total_ms, avg_ms, min_ms, max_ms}}."""
+    buf = (KernelStats * 16)()
+    n = load_library().attn_varlen_profile_stop(buf, 16)
+    if n < 0:
+        raise AttnError(n, "attn_varlen_profile_stop")
+    res = {}
+    for s_ in buf[:min(n, 16)]:
+        res[s_.name.decode()] = {"launches": s_.launches, "total_ms": s_.total_ms,
+                                 "avg_ms": s_.total_ms / max(s_.launches, 1),
+                                 "min_ms": s_.min_ms, "max_ms": s_.max_ms}
+    return res

@@ -5,7 +5,10 @@
 // on the device or allocates memory.
 #include <atomic>
 #include <cmath>
+#include <cstdio>
 #include <cstring>
+#include <mutex>
+#include <vector>
 
 #include "../../include/attn_varlen.h"
 #include "common.h"
@@ -66,6 +69,35 @@ attn_status check_common(const void* q, const void* k, const void* v, const int3
   return ATTN_OK;
 }
 
+// ---- optional kernel timing (attn_varlen_profile_start / _stop) ----------
+enum KernelId { K_SCHEDULE = 0, K_FORWARD, K_DQ, K_DKDV, K_COUNT };
+const char* const kKernelNames[K_COUNT] = {"schedule", "forward", "dq", "dkdv"};
+
+struct ProfileRecord {
+  int kernel;
+  hipEvent_t start, stop;
+};
+
+std::mutex g_prof_mu;
+std::atomic<bool> g_prof_on{false};
+std::vector<ProfileRecord> g_prof;
+
+// Launch f() on stream st; when profiling is on, bracket it with two events
+// recorded on the same stream.
+template <class F>
+hipError_t timed_launch(int kernel, hipStream_t st, F&& f) {
+  if (!g_prof_on.load(std::memory_order_relaxed)) return f();
+  ProfileRecord r{kernel, nullptr, nullptr};
+  if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess)
+    return f();
+  (void)hipEventRecord(r.start, st);
+  const hipError_t e = f();
+  (void)hipEventRecord(r.stop, st);
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  g_prof.push_back(r);
+  return e;
+}
+
 // A window of T or more keys can exclude nothing inside a segment, so it is
 // the global (full causal) case; mapping it to 0 keeps index arithmetic far
 // from int overflow.
@@ -104,8 +136,13 @@ attn_status attn_varlen_fwd(const void* q, const void* k, const void* v,
   const Problem p{total_tokens, num_seqs, num_q_heads, num_kv_heads,
                   effective_window(window, total_tokens), scale};
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (attn::launch_schedule(cu_seqlens, p, workspace, w, st) != hipSuccess) return ATTN_ELAUNCH;
-  if (attn::launch_forward(q, k, v, p, out, lse, workspace, w, st) != hipSuccess)
+  if (timed_launch(K_SCHEDULE, st, [&] {
+        return attn::launch_schedule(cu_seqlens, p, workspace, w, st);
+      }) != hipSuccess)
+    return ATTN_ELAUNCH;
+  if (timed_launch(K_FORWARD, st, [&] {
+        return attn::launch_forward(q, k, v, p, out, lse, workspace, w, st);
+      }) != hipSuccess)
     return ATTN_ELAUNCH;
   return ATTN_OK;
 }
@@ -130,9 +167,17 @@ attn_status attn_varlen_bwd(const void* q, const void* k, const void* v, const v
   const Problem p{total_tokens, num_seqs, num_q_heads, num_kv_heads,
                   effective_window(window, total_tokens), scale};
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (attn::launch_schedule(cu_seqlens, p, workspace, w, st) != hipSuccess) return ATTN_ELAUNCH;
-  if (attn::launch_backward(q, k, v, out, lse, dout, p, dq, dk, dv, workspace, w, st) !=
-      hipSuccess)
+  if (timed_launch(K_SCHEDULE, st, [&] {
+        return attn::launch_schedule(cu_seqlens, p, workspace, w, st);
+      }) != hipSuccess)
+    return ATTN_ELAUNCH;
+  if (timed_launch(K_DQ, st, [&] {
+        return attn::launch_dq(q, k, v, out, lse, dout, p, dq, workspace, w, st);
+      }) != hipSuccess)
+    return ATTN_ELAUNCH;
+  if (timed_launch(K_DKDV, st, [&] {
+        return attn::launch_dkdv(q, k, v, lse, dout, p, dk, dv, workspace, w, st);
+      }) != hipSuccess)
     return ATTN_ELAUNCH;
   return ATTN_OK;
 }
@@ -150,5 +195,49 @@ const char* attn_varlen_strerror(attn_status s) {
 }
 
 int32_t attn_varlen_version(void) { return 100; }
+
+attn_status attn_varlen_profile_start(void) {
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  for (ProfileRecord& r : g_prof) {
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  g_prof.clear();
+  g_prof_on.store(true);
+  return ATTN_OK;
+}
+
+int32_t attn_varlen_profile_stop(attn_kernel_stats* stats, int32_t cap) {
+  g_prof_on.store(false);
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  attn_kernel_stats acc[K_COUNT];
+  std::memset(acc, 0, sizeof(acc));
+  attn_status status = ATTN_OK;
+  for (ProfileRecord& r : g_prof) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.stop) != hipSuccess ||
+        hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess)
+      status = ATTN_EDEVICE;
+    attn_kernel_stats& a = acc[r.kernel];
+    if (a.launches == 0 || ms < a.min_ms) a.min_ms = ms;
+    if (ms > a.max_ms) a.max_ms = ms;
+    a.total_ms += ms;
+    a.launches += 1;
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  g_prof.clear();
+  if (status != ATTN_OK) return status;
+  int32_t n = 0;
+  for (int k = 0; k < K_COUNT; ++k) {
+    if (acc[k].launches == 0) continue;
+    if (stats && n < cap) {
+      stats[n] = acc[k];
+      std::snprintf(stats[n].name, sizeof(stats[n].name), "%s", kKernelNames[k]);
+    }
+    ++n;
+  }
+  return n;
+}
 
 }  // extern "C"

@@ -312,28 +312,32 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
 
 }  // namespace
 
-hipError_t launch_backward(const void* q, const void* k, const void* v, const void* out,
-                           const float* lse, const void* dout, const Problem& p, void* dq,
-                           void* dk, void* dv, void* workspace, const WorkspaceLayout& w,
-                           hipStream_t stream) {
+hipError_t launch_dq(const void* q, const void* k, const void* v, const void* out,
+                     const float* lse, const void* dout, const Problem& p, void* dq,
+                     void* workspace, const WorkspaceLayout& w, hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
-  float* dbuf = reinterpret_cast<float*>(ws + w.dbuf);
-  const int* header = reinterpret_cast<const int*>(ws + w.header);
-  const unsigned grid_q = (unsigned)(w.tile_cap * (size_t)(p.num_q_heads / 4));
-  hipLaunchKernelGGL(dq_kernel, dim3(grid_q), dim3(BWD_THREADS), 0, stream,
+  const unsigned grid = (unsigned)(w.tile_cap * (size_t)(p.num_q_heads / 4));
+  hipLaunchKernelGGL(dq_kernel, dim3(grid), dim3(BWD_THREADS), 0, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                      static_cast<const bf16*>(v), static_cast<const bf16*>(out),
-                     static_cast<const bf16*>(dout), lse, header,
+                     static_cast<const bf16*>(dout), lse, reinterpret_cast<const int*>(ws + w.header),
                      reinterpret_cast<const Tile*>(ws + w.tiles_fwd), p.total_tokens,
                      p.num_q_heads, p.num_kv_heads, p.window, p.scale * LOG2E, p.scale,
-                     static_cast<bf16*>(dq), dbuf);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const unsigned grid_k = (unsigned)(w.tile_cap * (size_t)p.num_kv_heads);
-  hipLaunchKernelGGL(dkdv_kernel, dim3(grid_k), dim3(BWD_THREADS), 0, stream,
+                     static_cast<bf16*>(dq), reinterpret_cast<float*>(ws + w.dbuf));
+  return hipGetLastError();
+}
+
+hipError_t launch_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                       const void* dout, const Problem& p, void* dk, void* dv, void* workspace,
+                       const WorkspaceLayout& w, hipStream_t stream) {
+  const char* ws = static_cast<const char*>(workspace);
+  const unsigned grid = (unsigned)(w.tile_cap * (size_t)p.num_kv_heads);
+  hipLaunchKernelGGL(dkdv_kernel, dim3(grid), dim3(BWD_THREADS), 0, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),
-                     static_cast<const bf16*>(v), static_cast<const bf16*>(dout), lse, dbuf,
-                     header, reinterpret_cast<const Tile*>(ws + w.tiles_bwd), p.total_tokens,
+                     static_cast<const bf16*>(v), static_cast<const bf16*>(dout), lse,
+                     reinterpret_cast<const float*>(ws + w.dbuf),
+                     reinterpret_cast<const int*>(ws + w.header),
+                     reinterpret_cast<const Tile*>(ws + w.tiles_bwd), p.total_tokens,
                      p.num_q_heads, p.num_kv_heads, p.window, p.scale * LOG2E, p.scale,
                      static_cast<bf16*>(dk), static_cast<bf16*>(dv));
   return hipGetLastError();

@@ -18,9 +18,13 @@ hipError_t launch_forward(const void* q, const void* k, const void* v, const Pro
                           void* out, float* lse, void* workspace, const WorkspaceLayout& w,
                           hipStream_t stream);
 
-hipError_t launch_backward(const void* q, const void* k, const void* v, const void* out,
-                           const float* lse, const void* dout, const Problem& p, void* dq,
-                           void* dk, void* dv, void* workspace, const WorkspaceLayout& w,
-                           hipStream_t stream);
+// dQ, and D = rowsum(dout * out) into the workspace; must precede launch_dkdv.
+hipError_t launch_dq(const void* q, const void* k, const void* v, const void* out,
+                     const float* lse, const void* dout, const Problem& p, void* dq,
+                     void* workspace, const WorkspaceLayout& w, hipStream_t stream);
+
+hipError_t launch_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                       const void* dout, const Problem& p, void* dk, void* dv, void* workspace,
+                       const WorkspaceLayout& w, hipStream_t stream);
 
 }  // namespace attn
