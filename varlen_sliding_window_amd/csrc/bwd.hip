@@ -33,7 +33,8 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ out, const bf16* __restrict__ dout, const float* __restrict__ lse,
     const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
-    int window, float scale_log2, float scale, bf16* __restrict__ dq, float* __restrict__ dbuf) {
+    int window, float scale_log2, float scale, int tile_cap, bf16* __restrict__ dq,
+    RowStats* __restrict__ rowstats) {
   __shared__ __attribute__((aligned(16))) bf16 Ks[KBLK * LDS_PITCH];
   __shared__ __attribute__((aligned(16))) bf16 Vs[KBLK * LDS_PITCH];
 
@@ -75,7 +76,12 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(
   }
   const float Dv = dpart + __shfl_xor(dpart, 32);
   const float lse2 = qrow < T ? lse[(size_t)head * T + qrow] * LOG2E : 0.f;
-  if (qrow < q1 && lh == 0) dbuf[(size_t)head * T + qrow] = Dv;
+  if (qrow < q1 && lh == 0) {
+    RowStats rs;
+    rs.lse2 = lse2;
+    rs.d = Dv;
+    rowstats[((size_t)head * tile_cap + tl.idx) * TILE + lq] = rs;
+  }
 
   const int srow = tid >> 4, scol = (tid & 15) * 8;
   uint4 kr[4], vr[4];
@@ -155,16 +161,18 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(
 
 constexpr int DKDV_WAVES = 4;
 constexpr int RED_PITCH = HEAD_DIM + 4;   // fp32 pitch of the reduction buffer
-constexpr size_t DKDV_TILE_BYTES = (size_t)QBLK * LDS_PITCH * sizeof(bf16);
-constexpr size_t DKDV_LDS_BYTES =
-    2 * DKDV_WAVES * DKDV_TILE_BYTES + 2 * DKDV_WAVES * QBLK * sizeof(float);
-static_assert((size_t)DKDV_WAVES * TILE * RED_PITCH * sizeof(float) <=
-                  2 * DKDV_WAVES * DKDV_TILE_BYTES,
+// Per wave and buffer: Q tile, dO tile (32 x 128 bf16 each, swizzled), then
+// the 32 rows' RowStats.
+static_assert(QBLK == TILE, "a dK/dV q-block is exactly one q-tile");
+constexpr int DKDV_TILE_ELEMS = QBLK * HEAD_DIM;
+constexpr size_t DKDV_BUF_BYTES = 2 * DKDV_TILE_ELEMS * sizeof(bf16) + QBLK * sizeof(RowStats);
+constexpr size_t DKDV_LDS_BYTES = (size_t)DKDV_WAVES * 2 * DKDV_BUF_BYTES;
+static_assert((size_t)DKDV_WAVES * TILE * RED_PITCH * sizeof(float) <= DKDV_LDS_BYTES,
               "reduction buffer must fit in the staging buffers");
 
 __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dbuf,
+    const bf16* __restrict__ dout, const RowStats* __restrict__ rowstats, int tile_cap,
     const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
     int window, float scale_log2, float scale, bf16* __restrict__ dk, bf16* __restrict__ dv) {
   __shared__ __attribute__((aligned(16))) char smem[DKDV_LDS_BYTES];
@@ -180,24 +188,44 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
   const int k0 = tl.t0, k1 = tl.t1, b = tl.seg_b;
   const int qhi = window > 0 ? min(b, k1 - 1 + window) : b;
   const int nqb = (qhi - k0 + QBLK - 1) / QBLK;
+  const int steps = (G / DKDV_WAVES) * nqb;   // (head, q-block) pairs of this wave
   const size_t qstride = (size_t)Hq * HEAD_DIM;
   const size_t kstride = (size_t)Hkv * HEAD_DIM;
 
-  bf16* Qs = reinterpret_cast<bf16*>(smem) + (size_t)wave * QBLK * LDS_PITCH;
-  bf16* Ds = reinterpret_cast<bf16*>(smem + DKDV_WAVES * DKDV_TILE_BYTES) +
-             (size_t)wave * QBLK * LDS_PITCH;
-  float* Ls = reinterpret_cast<float*>(smem + 2 * DKDV_WAVES * DKDV_TILE_BYTES) + wave * QBLK;
-  float* Dd = Ls + DKDV_WAVES * QBLK;
+  char* wbase = smem + (size_t)wave * 2 * DKDV_BUF_BYTES;
+  auto q_tile = [&](int buf) { return reinterpret_cast<bf16*>(wbase + buf * DKDV_BUF_BYTES); };
+  auto do_tile = [&](int buf) { return q_tile(buf) + DKDV_TILE_ELEMS; };
+  auto ld_vals = [&](int buf) {
+    return reinterpret_cast<float*>(wbase + buf * DKDV_BUF_BYTES +
+                                    2 * DKDV_TILE_ELEMS * sizeof(bf16));
+  };
+
+  // Prefetch of step `it` into buffer `buf`: Q and dO rows of q-block i (the
+  // q-tile idx + i of this segment), then that tile's 32 RowStats (lanes 0-15,
+  // 16 bytes each).  Rows past the segment hold stale values; they are
+  // masked with selects, so even NaNs there cannot leak.
+  auto issue = [&](int it, int buf) {
+    const int head = g * G + wave + DKDV_WAVES * (it / nqb);
+    const int i = it % nqb;
+    const int qb = k0 + i * QBLK;
+    swz_tile32_load_async(q_tile(buf), q + (size_t)head * HEAD_DIM, qstride, qb, T, lane);
+    swz_tile32_load_async(do_tile(buf), dout + (size_t)head * HEAD_DIM, qstride, qb, T, lane);
+    if (lane < 16) {
+      const RowStats* src = rowstats + ((size_t)head * tile_cap + tl.idx + i) * TILE + 2 * lane;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)ld_vals(buf), 16, 0, 0);
+    }
+  };
+  if (steps > 0) issue(0, 0);
 
   // K^T and V^T as B operands: lane holds k[k0 + lq][16 ks + 8 lh + 0..7]
   const int krow = k0 + lq;
   bf16x8 kf[8], vf[8];
   {
-    const size_t off = (size_t)krow * kstride + (size_t)g * HEAD_DIM + lh * 8;
+    const size_t off = (size_t)min(krow, T - 1) * kstride + (size_t)g * HEAD_DIM + lh * 8;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      kf[ks] = krow < T ? as_bf16x8(ldg16(k + off + ks * 16)) : zero_bf16x8();
-      vf[ks] = krow < T ? as_bf16x8(ldg16(v + off + ks * 16)) : zero_bf16x8();
+      kf[ks] = as_bf16x8(ldg16(k + off + ks * 16));
+      vf[ks] = as_bf16x8(ldg16(v + off + ks * 16));
     }
   }
 
@@ -207,72 +235,62 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
     dka[db] = zero_f32x16();
     dva[db] = zero_f32x16();
   }
-
-  // rows handled by this lane when staging: (lane >> 4) + 4 j, columns (lane & 15) * 8
-  const int srow = lane >> 4, scol = (lane & 15) * 8;
   const bool keys_full = (k1 - k0) == TILE;
 
-  for (int hh = wave; hh < G; hh += DKDV_WAVES) {
-    const int head = g * G + hh;
-    for (int i = 0; i < nqb; ++i) {
-      const int qb = k0 + i * QBLK;
-      __syncthreads();
+  for (int it = 0; it < steps; ++it) {
+    const int buf = it & 1;
+    // The only loads in flight are this step's; wait for them, take this
+    // step's row statistics into registers, then start the next step's
+    // loads so they overlap this step's math.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const float* LD = ld_vals(buf);   // (lse2, D) pairs of rows qb + 0..31
+    float lv[16], dd[16];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int row = srow + 4 * j;
-        const int qi = qb + row;
-        uint4 qv = make_uint4(0u, 0u, 0u, 0u), dv4 = make_uint4(0u, 0u, 0u, 0u);
-        if (qi < T) {
-          const size_t off = (size_t)qi * qstride + (size_t)head * HEAD_DIM + scol;
-          qv = ldg16(q + off);
-          dv4 = ldg16(dout + off);
-        }
-        *reinterpret_cast<uint4*>(Qs + row * LDS_PITCH + scol) = qv;
-        *reinterpret_cast<uint4*>(Ds + row * LDS_PITCH + scol) = dv4;
-      }
-      if (lane < QBLK) {
-        const int qi = qb + lane;
-        Ls[lane] = qi < T ? lse[(size_t)head * T + qi] * LOG2E : 0.f;
-        Dd[lane] = qi < T ? dbuf[(size_t)head * T + qi] : 0.f;
-      }
-      __syncthreads();
-
-      // S[q][key] = Q K^T and dP = dO V^T: s[r] holds query qb + 8(r/4) + 4 lh + r%4, key k0 + lq
-      f32x16 s = zero_f32x16(), dp = zero_f32x16();
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        s = mfma32(lds_frag_cols(Qs, ks, lane), kf[ks], s);
-        dp = mfma32(lds_frag_cols(Ds, ks, lane), vf[ks], dp);
-      }
-      const bool full = keys_full && (qb + QBLK - 1 < b) && (qb >= k0 + TILE - 1) &&
-                        (window <= 0 || qb + QBLK - 1 < k0 + window);
-      bf16x8 pf[2], dsf[2];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 l4 = *reinterpret_cast<const float4*>(Ls + 8 * j + 4 * lh);
-        const float4 d4 = *reinterpret_cast<const float4*>(Dd + 8 * j + 4 * lh);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * j + e;
-          const int qi = qb + 8 * j + 4 * lh + e;
-          const bool vis = full || (krow < k1 && qi < b && krow <= qi &&
-                                    (window <= 0 || krow > qi - window));
-          const float p = vis ? exp2_fast(s[r] * scale_log2 - lv[e]) : 0.f;
-          pf[r >> 3][r & 7] = (bf16)p;
-          dsf[r >> 3][r & 7] = (bf16)(p * (dp[r] - dd[e]));
-        }
-      }
-      // dV[key][d] += P^T dO ; dK[key][d] += dS^T Q  (scale applied at the end)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          dva[db] = mfma32(pf[t], lds_frag_rows(Ds + db * 32, t, lane), dva[db]);
-          dka[db] = mfma32(dsf[t], lds_frag_rows(Qs + db * 32, t, lane), dka[db]);
-        }
+    for (int j = 0; j < 4; ++j) {
+      const float4 a4 = *reinterpret_cast<const float4*>(LD + 2 * (8 * j + 4 * lh));
+      const float4 b4 = *reinterpret_cast<const float4*>(LD + 2 * (8 * j + 4 * lh) + 4);
+      lv[4 * j + 0] = a4.x; dd[4 * j + 0] = a4.y;
+      lv[4 * j + 1] = a4.z; dd[4 * j + 1] = a4.w;
+      lv[4 * j + 2] = b4.x; dd[4 * j + 2] = b4.y;
+      lv[4 * j + 3] = b4.z; dd[4 * j + 3] = b4.w;
     }
+    if (it + 1 < steps) issue(it + 1, buf ^ 1);
+    const int qb = k0 + (it % nqb) * QBLK;
+    const bf16* Qs = q_tile(buf);
+    const bf16* Ds = do_tile(buf);
+
+    // S[q][key] = Q K^T and dP = dO V^T: s[r] holds query qb + 8(r/4) + 4 lh + r%4, key k0 + lq
+    f32x16 s = zero_f32x16(), dp = zero_f32x16();
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      s = mfma32(swz_frag_cols(Qs, ks, lane), kf[ks], s);
+      dp = mfma32(swz_frag_cols(Ds, ks, lane), vf[ks], dp);
+    }
+    const bool full = keys_full && (qb + QBLK - 1 < b) && (qb >= k0 + TILE - 1) &&
+                      (window <= 0 || qb + QBLK - 1 < k0 + window);
+    bf16x8 pf[2], dsf[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * j + e;
+        const int qi = qb + 8 * j + 4 * lh + e;
+        const bool vis = full || (krow < k1 && qi < b && krow <= qi &&
+                                  (window <= 0 || krow > qi - window));
+        const float p = vis ? exp2_fast(s[r] * scale_log2 - lv[r]) : 0.f;
+        const float ds = vis ? p * (dp[r] - dd[r]) : 0.f;
+        pf[r >> 3][r & 7] = (bf16)p;
+        dsf[r >> 3][r & 7] = (bf16)ds;
+      }
+    }
+    // dV[key][d] += P^T dO ; dK[key][d] += dS^T Q  (scale applied at the end)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        dva[db] = mfma32(pf[t], swz_frag_rows(Ds, db * 32, t, lane), dva[db]);
+        dka[db] = mfma32(dsf[t], swz_frag_rows(Qs, db * 32, t, lane), dka[db]);
+      }
   }
 
   // Head-group reduction in a fixed order (wave 0 + 1 + 2 + 3), then store.
@@ -323,7 +341,8 @@ hipError_t launch_dq(const void* q, const void* k, const void* v, const void* ou
                      static_cast<const bf16*>(dout), lse, reinterpret_cast<const int*>(ws + w.header),
                      reinterpret_cast<const Tile*>(ws + w.tiles_fwd), p.total_tokens,
                      p.num_q_heads, p.num_kv_heads, p.window, p.scale * LOG2E, p.scale,
-                     static_cast<bf16*>(dq), reinterpret_cast<float*>(ws + w.dbuf));
+                     (int)w.tile_cap, static_cast<bf16*>(dq),
+                     reinterpret_cast<RowStats*>(ws + w.rowstats));
   return hipGetLastError();
 }
 
@@ -334,8 +353,8 @@ hipError_t launch_dkdv(const void* q, const void* k, const void* v, const float*
   const unsigned grid = (unsigned)(w.tile_cap * (size_t)p.num_kv_heads);
   hipLaunchKernelGGL(dkdv_kernel, dim3(grid), dim3(BWD_THREADS), 0, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),
-                     static_cast<const bf16*>(v), static_cast<const bf16*>(dout), lse,
-                     reinterpret_cast<const float*>(ws + w.dbuf),
+                     static_cast<const bf16*>(v), static_cast<const bf16*>(dout),
+                     reinterpret_cast<const RowStats*>(ws + w.rowstats), (int)w.tile_cap,
                      reinterpret_cast<const int*>(ws + w.header),
                      reinterpret_cast<const Tile*>(ws + w.tiles_bwd), p.total_tokens,
                      p.num_q_heads, p.num_kv_heads, p.window, p.scale * LOG2E, p.scale,

@@ -33,14 +33,24 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
 // One tile of one segment: tokens [t0, t1) of segment [seg_a, seg_b).
+// idx numbers the tiles in token order; the tiles of one segment have
+// consecutive indices, so tile idx + i starts TILE * i tokens later.
 struct __attribute__((aligned(16))) Tile {
   int t0, t1, seg_a, seg_b;
+  int idx, pad0, pad1, pad2;
+};
+
+// Per-row values the backward passes from the dQ kernel to the dK/dV kernel:
+// lse * log2(e) and D = rowsum(dout * out), stored per (query head, tile) as
+// TILE consecutive pairs (256 bytes, 256-byte aligned).
+struct RowStats {
+  float lse2, d;
 };
 
 // Workspace: [header | forward-order tiles | backward-order tiles |
-//             per-segment tile offsets | D (fp32 [Hq, T])]
+//             per-segment tile offsets | RowStats [Hq][tile_cap][TILE]]
 struct WorkspaceLayout {
-  size_t header, tiles_fwd, tiles_bwd, seg_offsets, dbuf, total;
+  size_t header, tiles_fwd, tiles_bwd, seg_offsets, rowstats, total;
   size_t tile_cap;
 };
 
@@ -59,8 +69,8 @@ inline WorkspaceLayout workspace_layout(int64_t total_tokens, int64_t num_seqs,
   w.tiles_fwd = 256;
   w.tiles_bwd = w.tiles_fwd + align256(w.tile_cap * sizeof(Tile));
   w.seg_offsets = w.tiles_bwd + align256(w.tile_cap * sizeof(Tile));
-  w.dbuf = w.seg_offsets + align256((size_t)(num_seqs + 1) * sizeof(int));
-  w.total = w.dbuf + align256((size_t)num_q_heads * (size_t)total_tokens * sizeof(float));
+  w.rowstats = w.seg_offsets + align256((size_t)(num_seqs + 1) * sizeof(int));
+  w.total = w.rowstats + align256((size_t)num_q_heads * w.tile_cap * TILE * sizeof(RowStats));
   return w;
 }
 

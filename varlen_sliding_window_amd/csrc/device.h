@@ -67,6 +67,52 @@ __device__ __forceinline__ bf16x8 lds_frag_cols(const bf16* tile, int ks, int la
                                           (lane >> 5) * 8);
 }
 
+// ---- swizzled, unpadded LDS tiles --------------------------------------------
+// A tile holds rows of HEAD_DIM bf16 (256 bytes) with no padding; 16-byte
+// chunk c of row r is stored at chunk c ^ swz(r).  The swizzle is a
+// bijection per row, and makes both the 16-byte row reads (16 lanes on 16
+// rows, same chunk) and the transposing 8-byte reads (16 lanes on 4 rows x
+// 2 chunks) hit distinct banks.  Unpadded rows let one wave fill 4 whole rows
+// (1 KB) with a single direct global-to-LDS load.
+__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
+// Like lds_frag_cols, on a swizzled tile.
+__device__ __forceinline__ bf16x8 swz_frag_cols(const bf16* tile, int ks, int lane) {
+  const int r = lane & 31;
+  const int c = 2 * ks + (lane >> 5);
+  return *reinterpret_cast<const bf16x8*>(tile + r * HEAD_DIM + ((c ^ swz(r)) << 3));
+}
+
+// Like lds_frag_rows, on a swizzled tile; col0 is the first of 32 columns.
+__device__ __forceinline__ bf16x8 swz_frag_rows(const bf16* tile, int col0, int t, int lane) {
+  const int r0 = 16 * t + 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int r1 = r0 + 8;
+  const int col = col0 + (lane & 16) + 4 * (lane & 3);
+  const int c = col >> 3, off = col & 7;
+  const bf16x4 lo = lds_read_tr(tile + r0 * HEAD_DIM + ((c ^ swz(r0)) << 3) + off);
+  const bf16x4 hi = lds_read_tr(tile + r1 * HEAD_DIM + ((c ^ swz(r1)) << 3) + off);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Asynchronous copy (one wave) of 32 rows x 128 bf16 into a swizzled tile:
+// rows row0 .. row0 + 31 of a row-major matrix whose row r starts at
+// g + r * stride.  Rows at or past T are clamped to T - 1 (their values
+// are masked by the caller).  8 direct global-to-LDS loads per lane; the
+// caller waits with s_waitcnt vmcnt before reading the tile.
+__device__ __forceinline__ void swz_tile32_load_async(bf16* tile, const bf16* g, size_t stride,
+                                                      int row0, int T, int lane) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 4 * i + (lane >> 4);
+    const int c = (lane & 15) ^ swz(r);
+    const int row = min(row0 + r, T - 1);
+    __builtin_amdgcn_global_load_lds(g + (size_t)row * stride + c * 8,
+                                     (lds_void*)(tile + i * 512), 16, 0, 0);
+  }
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 

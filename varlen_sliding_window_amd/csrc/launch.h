@@ -18,7 +18,8 @@ hipError_t launch_forward(const void* q, const void* k, const void* v, const Pro
                           void* out, float* lse, void* workspace, const WorkspaceLayout& w,
                           hipStream_t stream);
 
-// dQ, and D = rowsum(dout * out) into the workspace; must precede launch_dkdv.
+// dQ, and each row's lse * log2(e) and D = rowsum(dout * out) into the
+// workspace; must precede launch_dkdv.
 hipError_t launch_dq(const void* q, const void* k, const void* v, const void* out,
                      const float* lse, const void* dout, const Problem& p, void* dq,
                      void* workspace, const WorkspaceLayout& w, hipStream_t stream);

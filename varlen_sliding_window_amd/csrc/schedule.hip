@@ -64,6 +64,8 @@ __device__ __forceinline__ Tile tile_at(int i, const int* __restrict__ seg_off,
   t.t1 = (int)min(t0 + TILE, (long long)b);
   t.seg_a = a;
   t.seg_b = b;
+  t.idx = i;
+  t.pad0 = t.pad1 = t.pad2 = 0;
   return t;
 }
 
