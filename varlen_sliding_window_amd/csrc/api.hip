@@ -10,7 +10,7 @@
 #include <mutex>
 #include <vector>
 
-#include "../../include/attn_varlen.h"
+#include "attn_varlen.h"
 #include "common.h"
 #include "launch.h"
 
@@ -137,7 +137,7 @@ attn_status attn_varlen_fwd(const void* q, const void* k, const void* v,
                   effective_window(window, total_tokens), scale};
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (timed_launch(K_SCHEDULE, st, [&] {
-        return attn::launch_schedule(cu_seqlens, p, workspace, w, st);
+        return attn::launch_schedule(cu_seqlens, p, false, workspace, w, st);
       }) != hipSuccess)
     return ATTN_ELAUNCH;
   if (timed_launch(K_FORWARD, st, [&] {
@@ -168,7 +168,7 @@ attn_status attn_varlen_bwd(const void* q, const void* k, const void* v, const v
                   effective_window(window, total_tokens), scale};
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (timed_launch(K_SCHEDULE, st, [&] {
-        return attn::launch_schedule(cu_seqlens, p, workspace, w, st);
+        return attn::launch_schedule(cu_seqlens, p, true, workspace, w, st);
       }) != hipSuccess)
     return ATTN_ELAUNCH;
   if (timed_launch(K_DQ, st, [&] {

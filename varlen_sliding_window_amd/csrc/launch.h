@@ -10,9 +10,10 @@ struct Problem {
   float scale;
 };
 
-// Builds both sorted tile lists in the workspace from cu_seqlens.
-hipError_t launch_schedule(const int32_t* cu_seqlens, const Problem& p, void* workspace,
-                           const WorkspaceLayout& w, hipStream_t stream);
+// Builds the sorted tile lists in the workspace from cu_seqlens: the
+// forward-order list always, the backward-order list only when need_bwd.
+hipError_t launch_schedule(const int32_t* cu_seqlens, const Problem& p, bool need_bwd,
+                           void* workspace, const WorkspaceLayout& w, hipStream_t stream);
 
 hipError_t launch_forward(const void* q, const void* k, const void* v, const Problem& p,
                           void* out, float* lse, void* workspace, const WorkspaceLayout& w,

@@ -28,19 +28,29 @@ static_assert(SORT_BINS == SCHED_THREADS, "one sort bin per thread");
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return min(max(x, lo), hi); }
 
-// Inclusive block-wide scan; *total receives the sum over the block.
-__device__ int block_scan(int v, int* buf, int* total) {
-  const int tid = threadIdx.x;
-  buf[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < SCHED_THREADS; off <<= 1) {
-    const int add = tid >= off ? buf[tid - off] : 0;
-    __syncthreads();
-    buf[tid] += add;
-    __syncthreads();
+// Inclusive block-wide scan (1024 threads = 16 waves): shuffles inside each
+// wave, one wave scans the 16 wave totals.  *total receives the block sum.
+__device__ int block_scan(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(v, off);
+    if (lane >= off) v += t;
   }
-  const int r = buf[tid];
-  *total = buf[SCHED_THREADS - 1];
+  if (lane == 63) wsum[w] = v;
+  __syncthreads();
+  if (w == 0) {
+    int x = lane < 16 ? wsum[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int t = __shfl_up(x, off);
+      if (lane >= off) x += t;
+    }
+    if (lane < 16) wsum[lane] = x;
+  }
+  __syncthreads();
+  const int r = v + (w > 0 ? wsum[w - 1] : 0);
+  *total = wsum[15];
   __syncthreads();
   return r;
 }
@@ -79,14 +89,28 @@ __device__ __forceinline__ int bwd_bin(const Tile& t, int window) {
   return min((qhi - t.t0 + QBLK - 1) / QBLK, SORT_BINS - 1);
 }
 
+// Segments whose boundaries and offsets fit here are scheduled from LDS;
+// larger counts fall back to the workspace copy in global memory.
+constexpr int SCHED_LDS_SEGS = 4096;
+
 __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
-    const int32_t* __restrict__ cu, int nseq, int T, int window, int tile_cap,
-    int* __restrict__ header,
-    Tile* __restrict__ fwd_list, Tile* __restrict__ bwd_list, int* __restrict__ seg_off) {
-  __shared__ int buf[SCHED_THREADS];
+    const int32_t* __restrict__ cu_g, int nseq, int T, int window, int tile_cap, int need_bwd,
+    int* __restrict__ header, Tile* __restrict__ fwd_list, Tile* __restrict__ bwd_list,
+    int* __restrict__ seg_off_g) {
+  __shared__ int buf[SCHED_THREADS / 64];
   __shared__ int hist_f[SORT_BINS];
   __shared__ int hist_b[SORT_BINS];
+  __shared__ int lds_cu[SCHED_LDS_SEGS + 1];
+  __shared__ int lds_off[SCHED_LDS_SEGS + 1];
   const int tid = threadIdx.x;
+  const int32_t* cu = cu_g;
+  int* seg_off = seg_off_g;
+  if (nseq <= SCHED_LDS_SEGS) {
+    for (int i = tid; i <= nseq; i += SCHED_THREADS) lds_cu[i] = cu_g[i];
+    cu = lds_cu;
+    seg_off = lds_off;
+    __syncthreads();
+  }
 
   // 1. tiles per segment -> exclusive offsets
   int carry = 0;
@@ -115,7 +139,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
   for (int i = tid; i < ntiles; i += SCHED_THREADS) {
     const Tile t = tile_at(i, seg_off, cu, nseq, T);
     atomicAdd(&hist_f[fwd_bin(t, window)], 1);
-    atomicAdd(&hist_b[bwd_bin(t, window)], 1);
+    if (need_bwd) atomicAdd(&hist_b[bwd_bin(t, window)], 1);
   }
   __syncthreads();
 
@@ -136,18 +160,18 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
   for (int i = tid; i < ntiles; i += SCHED_THREADS) {
     const Tile t = tile_at(i, seg_off, cu, nseq, T);
     fwd_list[atomicAdd(&hist_f[fwd_bin(t, window)], 1)] = t;
-    bwd_list[atomicAdd(&hist_b[bwd_bin(t, window)], 1)] = t;
+    if (need_bwd) bwd_list[atomicAdd(&hist_b[bwd_bin(t, window)], 1)] = t;
   }
   if (tid == 0) header[0] = ntiles;
 }
 
 }  // namespace
 
-hipError_t launch_schedule(const int32_t* cu_seqlens, const Problem& p, void* workspace,
-                           const WorkspaceLayout& w, hipStream_t stream) {
+hipError_t launch_schedule(const int32_t* cu_seqlens, const Problem& p, bool need_bwd,
+                           void* workspace, const WorkspaceLayout& w, hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(SCHED_THREADS), 0, stream, cu_seqlens,
-                     p.num_seqs, p.total_tokens, p.window, (int)w.tile_cap,
+                     p.num_seqs, p.total_tokens, p.window, (int)w.tile_cap, need_bwd ? 1 : 0,
                      reinterpret_cast<int*>(ws + w.header),
                      reinterpret_cast<Tile*>(ws + w.tiles_fwd),
                      reinterpret_cast<Tile*>(ws + w.tiles_bwd),
