@@ -108,45 +108,76 @@ def run_layer(attn, L):
              L["window"], L["scale"], dq=L["dq"], dk=L["dk"], dv=L["dv"], workspace=L["ws"])
 
 
-def cpu_baseline(layer, seed):
-    """The CPU oracle, as it stands, on one layer of the same workload."""
+def cpu_baseline(layers, seed, min_seconds=10.0, max_reps=4):
+    """The CPU oracle, as it stands, on the step's layers (fwd+bwd each),
+    repeated until at least min_seconds of CPU work (bounded by max_reps)."""
     from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import attention_backward
 
     cores = len(os.sched_getaffinity(0))
-    mb = layer["mb"]
+    reps = 0
+    flops = 0
+    t0 = time.perf_counter()
     with threadpool_limits(limits=cores):
         used = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-        t0 = time.perf_counter()
-        attention_backward(mb.f32("q"), mb.f32("k"), mb.f32("v"), mb.f32("dout"),
-                           mb.cu_seqlens, layer["window"], layer["scale"])
-        secs = time.perf_counter() - t0
-    fl = layer["flops"]["fwd_bwd"]
-    return {"value": fl / secs / 1e12, "unit": "TFLOP/s", "cores": int(used), "kind": "oracle",
+        while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < min_seconds):
+            for L in layers:
+                mb = L["mb"]
+                attention_backward(mb.f32("q"), mb.f32("k"), mb.f32("v"), mb.f32("dout"),
+                                   mb.cu_seqlens, L["window"], L["scale"])
+                flops += L["flops"]["fwd_bwd"]
+            reps += 1
+    secs = time.perf_counter() - t0
+    labels = "+".join(L["label"] for L in layers)
+    mb = layers[0]["mb"]
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(used), "kind": "oracle",
             "seconds": secs, "cpu": cpu_info(),
-            "sample": (f"one {layer['label']} layer forward+backward of the seed-{seed} "
-                       f"microbatch ({mb.num_seqs} segments, all {mb.cfg.num_q_heads} query "
-                       f"heads, {layer['flops']['pairs']} pairs/head), fp64 NumPy")}
+            "sample": (f"{reps} x one step ({labels}, forward+backward) of the seed-{seed} "
+                       f"microbatch, {mb.num_seqs} segments, all {mb.cfg.num_q_heads} query heads; "
+                       f"fp64 NumPy oracle; counted flops / wall seconds")}
 
 
-def load_traffic(kernel: str, workload_label: str):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
-    were taken on the current kernel sources (else None)."""
+def sources_sha256() -> str:
     import hashlib
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        data = json.load(f)
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "varlen_sliding_window_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
-    if data.get("sources_sha256") != h.hexdigest():
+    return h.hexdigest()
+
+
+def load_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (profiles/*.md, a 'traffic-json:' line), provided the counters
+    were taken on the current kernel sources; else None."""
+    pdir = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(pdir):
         return None
-    entry = data.get("kernels", {}).get(f"{workload_label}/{kernel}")
-    return None if entry is None else entry.get("bytes_per_launch")
+    sha = sources_sha256()
+    for name in sorted(os.listdir(pdir)):
+        if not name.endswith(".md"):
+            continue
+        with open(os.path.join(pdir, name)) as f:
+            for line in f:
+                if line.startswith("traffic-json:"):
+                    data = json.loads(line.split(":", 1)[1])
+                    if data.get("sources_sha256") == sha and data.get("kernel") == kernel:
+                        return data.get("bytes_per_launch")
+    return None
+
+
+def copy_calibration(device, mib: int = 256, reps: int = 3):
+    """Plain device copies of a known size, for scaling the FETCH_SIZE and
+    WRITE_SIZE counters (each copy reads and writes exactly mib MiB)."""
+    import torch
+    src = torch.ones(mib * 1024 * 1024 // 4, dtype=torch.float32, device=device)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_copy": src.numel() * 4, "copies": reps}))
 
 
 def main():
@@ -156,9 +187,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--workload", default="ctx4096_w512+global", choices=sorted(WORKLOADS))
+    ap.add_argument("--print-sources-sha", action="store_true",
+                    help="print the kernel-source hash the traffic summary is keyed on")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the CPU oracle (profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain copies of a known size (counter calibration)")
     args = ap.parse_args()
+    if args.print_sources_sha:
+        print(sources_sha256())
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -173,6 +211,9 @@ def main():
         sys.exit(1)
     attn.load_library()
     device = torch.device("cuda", 0)
+    if args.copy_calibration:
+        copy_calibration(device)
+        return
     cu, layers = build_layers(args.workload, args.seed, device)
     print(f"[bench] workload {args.workload}: {len(layers)} layer(s), {len(cu) - 1} segments, "
           f"max_seqlen {layers[0]['max_seqlen']}", file=sys.stderr, flush=True)
@@ -239,14 +280,28 @@ def main():
                 entry["tflops"] = fl / (st["avg_ms"] * 1e-3) / 1e12
             kernels[f"{label}/{kname}"] = entry
 
-    dom_key = max(kernels, key=lambda k: kernels[k]["total_ms"] / max(
-        1, sum(1 for L in layers if L["label"] == k.split("/")[0])))
-    dom = kernels[dom_key]
-    achieved = dom.get("tflops", 0.0)
-    roofline = {"bound": "mfma", "kernel": dom_key, "achieved": achieved,
+    # Dominant kernel over the whole step (every launch of it, all layers):
+    # achieved = its algorithmic flops / its summed event durations.  A
+    # rocprofv3 --stats run of the same command averages the same launches.
+    by_kernel = {}
+    for key, entry in kernels.items():
+        kname = key.split("/")[1]
+        agg = by_kernel.setdefault(kname, {"ms": 0.0, "flops": 0.0, "launches": 0.0})
+        # a label's profile pass ran every layer of that label once per step
+        per_step = entry["launches"] / args.steps
+        agg["ms"] += entry["total_ms"] / args.steps
+        agg["flops"] += entry.get("flops_per_launch", 0.0) * per_step
+        agg["launches"] += per_step
+    dom_name = max(by_kernel, key=lambda k: by_kernel[k]["ms"])
+    dom = by_kernel[dom_name]
+    achieved = dom["flops"] / (dom["ms"] * 1e-3) / 1e12 if dom["ms"] > 0 else 0.0
+    traffic = load_traffic(dom_name)
+    roofline = {"bound": "mfma", "kernel": dom_name, "achieved": achieved,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "avg_ms": dom["avg_ms"], "flops_per_launch": dom.get("flops_per_launch"),
-                "traffic": load_traffic(dom_key.split("/")[1], dom_key.split("/")[0])}
+                "traffic": traffic,
+                "avg_ms": dom["ms"] / dom["launches"], "launches_per_step": dom["launches"],
+                "flops_per_launch": dom["flops"] / dom["launches"],
+                "share_of_step": dom["ms"] / ms_per_step}
 
     result = {
         "metric": "fwd+bwd TFLOPS per 16,384-token microbatch (window-512 and global layers, "
@@ -281,8 +336,8 @@ def main():
         "gpu": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on one layer", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(layers[0], args.seed)
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(layers, args.seed)
     print(json.dumps(result), flush=True)
 
 
