@@ -12,15 +12,18 @@
 //   per wave, exactly like the forward: S^T and dP^T are computed with the
 //   query in the lane, so per-row lse and D are one register each, and
 //   dQ^T = K^T dS^T takes dS^T straight from registers.  Each wave also
-//   forms D = rowsum(dO * O) for its rows (fp32) and writes it to the
-//   workspace for the dK/dV kernel, which runs next on the same stream.
+//   forms D = rowsum(dO * O) for its rows (fp32) and writes -lse/scale and
+//   -D per row to the workspace for the dK/dV kernel, which runs next on the
+//   same stream and seeds its S and dP accumulators with them.
 // dK/dV kernel: one work-group per (k-tile of 32 keys, key-value head); its
 //   4 waves take the group's query heads (wave w: heads w, w + 4, ...).  K
 //   and V stay in registers; each wave streams its head's Q/dO rows through
-//   its own LDS slice in QBLK = 32-row steps and keeps dK/dV partial sums in
-//   fp32 registers.  The 4 partials are added in a fixed order through LDS
-//   at the end, so the head-group reduction needs no atomics and is
-//   bit-for-bit reproducible.
+//   its own double-buffered LDS slice in QBLK = 32-row steps (direct
+//   global-to-LDS loads one step ahead) and keeps dK/dV partial sums in fp32
+//   registers.  The loop is software-pipelined: the softmax of one step runs
+//   between the S/dP products of the next.  The 4 partials are added in a
+//   fixed order through LDS at the end, so the head-group reduction needs no
+//   atomics and is bit-for-bit reproducible.
 #include "device.h"
 #include "launch.h"
 
@@ -34,7 +37,7 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(
     const bf16* __restrict__ out, const bf16* __restrict__ dout, const float* __restrict__ lse,
     const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
     int window, float scale_log2, float scale, int tile_cap, bf16* __restrict__ dq,
-    RowStats* __restrict__ rowstats) {
+    TileStats* __restrict__ stats) {
   __shared__ __attribute__((aligned(16))) bf16 Ks[KBLK * LDS_PITCH];
   __shared__ __attribute__((aligned(16))) bf16 Vs[KBLK * LDS_PITCH];
 
@@ -75,12 +78,14 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(
     }
   }
   const float Dv = dpart + __shfl_xor(dpart, 32);
-  const float lse2 = qrow < T ? lse[(size_t)head * T + qrow] * LOG2E : 0.f;
-  if (qrow < q1 && lh == 0) {
-    RowStats rs;
-    rs.lse2 = lse2;
-    rs.d = Dv;
-    rowstats[((size_t)head * tile_cap + tl.idx) * TILE + lq] = rs;
+  const float lsev = qrow < T ? lse[(size_t)head * T + qrow] : 0.f;
+  const float lse2 = lsev * LOG2E;
+  if (lh == 0) {
+    // Rows past the tile get seeds that make them vanish (P = 0, dP - D = 0),
+    // so every value the dK/dV kernel reads is finite.
+    TileStats* ts = stats + (size_t)head * tile_cap + tl.idx;
+    ts->s0[lq] = qrow < q1 ? -lsev / scale : -INFINITY;
+    ts->dp0[lq] = qrow < q1 ? -Dv : 0.f;
   }
 
   const int srow = tid >> 4, scol = (tid & 15) * 8;
@@ -162,17 +167,17 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(
 constexpr int DKDV_WAVES = 4;
 constexpr int RED_PITCH = HEAD_DIM + 4;   // fp32 pitch of the reduction buffer
 // Per wave and buffer: Q tile, dO tile (32 x 128 bf16 each, swizzled), then
-// the 32 rows' RowStats.
+// the q-tile's TileStats.
 static_assert(QBLK == TILE, "a dK/dV q-block is exactly one q-tile");
-constexpr int DKDV_TILE_ELEMS = QBLK * HEAD_DIM;
-constexpr size_t DKDV_BUF_BYTES = 2 * DKDV_TILE_ELEMS * sizeof(bf16) + QBLK * sizeof(RowStats);
+constexpr int DKDV_TILE_BYTES = QBLK * HEAD_DIM * (int)sizeof(bf16);
+constexpr int DKDV_BUF_BYTES = 2 * DKDV_TILE_BYTES + (int)sizeof(TileStats);
 constexpr size_t DKDV_LDS_BYTES = (size_t)DKDV_WAVES * 2 * DKDV_BUF_BYTES;
 static_assert((size_t)DKDV_WAVES * TILE * RED_PITCH * sizeof(float) <= DKDV_LDS_BYTES,
               "reduction buffer must fit in the staging buffers");
 
 __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const bf16* __restrict__ dout, const RowStats* __restrict__ rowstats, int tile_cap,
+    const bf16* __restrict__ dout, const TileStats* __restrict__ stats, int tile_cap,
     const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
     int window, float scale_log2, float scale, bf16* __restrict__ dk, bf16* __restrict__ dv) {
   __shared__ __attribute__((aligned(16))) char smem[DKDV_LDS_BYTES];
@@ -183,7 +188,8 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
   const Tile tl = tiles[item];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, lh = lane >> 5, lq = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lh = lane >> 5, lq = lane & 31;
   const int G = Hq / Hkv;
   const int k0 = tl.t0, k1 = tl.t1, b = tl.seg_b;
   const int qhi = window > 0 ? min(b, k1 - 1 + window) : b;
@@ -193,29 +199,71 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
   const size_t kstride = (size_t)Hkv * HEAD_DIM;
 
   char* wbase = smem + (size_t)wave * 2 * DKDV_BUF_BYTES;
-  auto q_tile = [&](int buf) { return reinterpret_cast<bf16*>(wbase + buf * DKDV_BUF_BYTES); };
-  auto do_tile = [&](int buf) { return q_tile(buf) + DKDV_TILE_ELEMS; };
-  auto ld_vals = [&](int buf) {
-    return reinterpret_cast<float*>(wbase + buf * DKDV_BUF_BYTES +
-                                    2 * DKDV_TILE_ELEMS * sizeof(bf16));
+  auto q_tile = [&](int buf) {
+    return reinterpret_cast<const bf16*>(wbase + buf * DKDV_BUF_BYTES);
   };
+  auto do_tile = [&](int buf) {
+    return reinterpret_cast<const bf16*>(wbase + buf * DKDV_BUF_BYTES + DKDV_TILE_BYTES);
+  };
+  auto st_tile = [&](int buf) {
+    return reinterpret_cast<const float*>(wbase + buf * DKDV_BUF_BYTES + 2 * DKDV_TILE_BYTES);
+  };
+  const uint32_t lds_wave = lds_address(wbase);
 
-  // Prefetch of step `it` into buffer `buf`: Q and dO rows of q-block i (the
-  // q-tile idx + i of this segment), then that tile's 32 RowStats (lanes 0-15,
-  // 16 bytes each).  Rows past the segment hold stale values; they are
-  // masked with selects, so even NaNs there cannot leak.
-  auto issue = [&](int it, int buf) {
-    const int head = g * G + wave + DKDV_WAVES * (it / nqb);
-    const int i = it % nqb;
+  // Lane part of the tile loads: load j (1 KB) fills rows 4j + lane / 16 of
+  // the swizzled tile; the lane fetches the 16-byte chunk that lands at
+  // physical chunk lane % 16 of its row.
+  const uint32_t rstride = (uint32_t)(qstride * sizeof(bf16));
+  uint32_t dma_off[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = 4 * j + (lane >> 4);
+    dma_off[j] = (uint32_t)r * rstride + (uint32_t)(((lane & 15) ^ swz(r)) << 4);
+  }
+
+  // Loads of one step into buffer `buf`: Q and dO rows of q-block i (the
+  // q-tile idx + i of this segment) of query head `head`, then that tile's
+  // TileStats (lanes 0-15, 16 bytes each).  Rows past T re-read row T - 1;
+  // rows past the segment hold other values.  Both are masked with selects,
+  // so even NaNs there cannot leak.
+  auto issue = [&](int head, int i, int buf) {
     const int qb = k0 + i * QBLK;
-    swz_tile32_load_async(q_tile(buf), q + (size_t)head * HEAD_DIM, qstride, qb, T, lane);
-    swz_tile32_load_async(do_tile(buf), dout + (size_t)head * HEAD_DIM, qstride, qb, T, lane);
-    if (lane < 16) {
-      const RowStats* src = rowstats + ((size_t)head * tile_cap + tl.idx + i) * TILE + 2 * lane;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)ld_vals(buf), 16, 0, 0);
+    const size_t hoff = (size_t)qb * qstride + (size_t)head * HEAD_DIM;
+    const bf16* qsrc = q + hoff;
+    const bf16* dsrc = dout + hoff;
+    const uint32_t l = lds_wave + (uint32_t)(buf * DKDV_BUF_BYTES);
+    const int rmax = T - 1 - qb;
+    if (rmax >= QBLK - 1) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        dma16(qsrc, dma_off[j], l + j * 1024);
+        dma16(dsrc, dma_off[j], l + DKDV_TILE_BYTES + j * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = 4 * j + (lane >> 4);
+        const uint32_t off = (uint32_t)min(r, rmax) * rstride +
+                             (uint32_t)(((lane & 15) ^ swz(r)) << 4);
+        dma16(qsrc, off, l + j * 1024);
+        dma16(dsrc, off, l + DKDV_TILE_BYTES + j * 1024);
+      }
+    }
+    if (lane < 16)
+      dma16(stats + (size_t)head * tile_cap + tl.idx + i, (uint32_t)lane * 16,
+            l + 2 * DKDV_TILE_BYTES);
+  };
+  // Steps run over (head, q-block) pairs: heads wave, wave + 4, ..., and for
+  // each head q-blocks 0 .. nqb - 1.  (ld_head, ld_i) is the next step to load.
+  int ld_head = g * G + wave, ld_i = 0;
+  auto issue_next = [&](int buf) {
+    issue(ld_head, ld_i, buf);
+    if (++ld_i == nqb) {
+      ld_i = 0;
+      ld_head += DKDV_WAVES;
     }
   };
-  if (steps > 0) issue(0, 0);
+  if (steps > 0) issue_next(0);
 
   // K^T and V^T as B operands: lane holds k[k0 + lq][16 ks + 8 lh + 0..7]
   const int krow = k0 + lq;
@@ -227,6 +275,10 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
       kf[ks] = as_bf16x8(ldg16(k + off + ks * 16));
       vf[ks] = as_bf16x8(ldg16(v + off + ks * 16));
     }
+    // Make the compiler wait for these loads here: a wait inside the loop
+    // would also wait for the step's own prefetch.
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(kf[ks]), "v"(vf[ks]));
   }
 
   f32x16 dka[4], dva[4];
@@ -235,63 +287,120 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
     dka[db] = zero_f32x16();
     dva[db] = zero_f32x16();
   }
-  const bool keys_full = (k1 - k0) == TILE;
 
-  for (int it = 0; it < steps; ++it) {
-    const int buf = it & 1;
-    // The only loads in flight are this step's; wait for them, take this
-    // step's row statistics into registers, then start the next step's
-    // loads so they overlap this step's math.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    const float* LD = ld_vals(buf);   // (lse2, D) pairs of rows qb + 0..31
-    float lv[16], dd[16];
+  // Visibility of element r of a step at q-block qb: its query
+  // qi = qb + 4 lh + 8(r/4) + r%4 sees this lane's key iff
+  // 0 <= qi - krow <= vis_hi - krow.  Keys past the tile see nothing: their
+  // offset is pushed far below zero.
+  const bool kvalid = krow < k1;
+  const int vis_hi = window > 0 ? min(b - 1, krow + window - 1) : b - 1;
+  const int mbias = (kvalid ? 0 : -(1 << 30)) + 4 * lh - krow;
+  const uint32_t mspan = kvalid ? (uint32_t)(vis_hi - krow) : 0u;
+
+  // S = Q K^T and dP = dO V^T of the step held in buffer `buf` (two
+  // independent chains), seeded with -lse/scale and -D: s[r] = S - lse/scale
+  // and dp[r] = dP - D of query qb + 8(r/4) + 4 lh + r%4 and key k0 + lq.
+  // Also reads the step's transposed dO and Q fragments (B operands of dV
+  // and dK), so that the buffer is done with once this returns.
+  auto s_dp = [&](int buf, f32x16& s, f32x16& dp, bf16x8* dof, bf16x8* qtf) {
+    const float* st = st_tile(buf);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float4 a4 = *reinterpret_cast<const float4*>(LD + 2 * (8 * j + 4 * lh));
-      const float4 b4 = *reinterpret_cast<const float4*>(LD + 2 * (8 * j + 4 * lh) + 4);
-      lv[4 * j + 0] = a4.x; dd[4 * j + 0] = a4.y;
-      lv[4 * j + 1] = a4.z; dd[4 * j + 1] = a4.w;
-      lv[4 * j + 2] = b4.x; dd[4 * j + 2] = b4.y;
-      lv[4 * j + 3] = b4.z; dd[4 * j + 3] = b4.w;
+      const float4 a4 = *reinterpret_cast<const float4*>(st + 8 * j + 4 * lh);
+      const float4 b4 = *reinterpret_cast<const float4*>(st + TILE + 8 * j + 4 * lh);
+      s[4 * j + 0] = a4.x; s[4 * j + 1] = a4.y; s[4 * j + 2] = a4.z; s[4 * j + 3] = a4.w;
+      dp[4 * j + 0] = b4.x; dp[4 * j + 1] = b4.y; dp[4 * j + 2] = b4.z; dp[4 * j + 3] = b4.w;
     }
-    if (it + 1 < steps) issue(it + 1, buf ^ 1);
-    const int qb = k0 + (it % nqb) * QBLK;
     const bf16* Qs = q_tile(buf);
     const bf16* Ds = do_tile(buf);
-
-    // S[q][key] = Q K^T and dP = dO V^T: s[r] holds query qb + 8(r/4) + 4 lh + r%4, key k0 + lq
-    f32x16 s = zero_f32x16(), dp = zero_f32x16();
+    bf16x8 qa[8], da[8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      s = mfma32(swz_frag_cols(Qs, ks, lane), kf[ks], s);
-      dp = mfma32(swz_frag_cols(Ds, ks, lane), vf[ks], dp);
+      qa[ks] = swz_frag_cols(Qs, ks, lane);
+      da[ks] = swz_frag_cols(Ds, ks, lane);
     }
-    const bool full = keys_full && (qb + QBLK - 1 < b) && (qb >= k0 + TILE - 1) &&
-                      (window <= 0 || qb + QBLK - 1 < k0 + window);
-    bf16x8 pf[2], dsf[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * j + e;
-        const int qi = qb + 8 * j + 4 * lh + e;
-        const bool vis = full || (krow < k1 && qi < b && krow <= qi &&
-                                  (window <= 0 || krow > qi - window));
-        const float p = vis ? exp2_fast(s[r] * scale_log2 - lv[r]) : 0.f;
-        const float ds = vis ? p * (dp[r] - dd[r]) : 0.f;
-        pf[r >> 3][r & 7] = (bf16)p;
-        dsf[r >> 3][r & 7] = (bf16)ds;
-      }
+    for (int ks = 0; ks < 8; ++ks) {
+      s = mfma32(qa[ks], kf[ks], s);
+      dp = mfma32(da[ks], vf[ks], dp);
     }
-    // dV[key][d] += P^T dO ; dK[key][d] += dS^T Q  (scale applied at the end)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int x = 0; x < 8; ++x) {
+      dof[x] = swz_frag_rows(Ds, (x & 3) * 32, x >> 2, lane);
+      qtf[x] = swz_frag_rows(Qs, (x & 3) * 32, x >> 2, lane);
+    }
+  };
+  // Half t of P and dS (queries 16t .. 16t + 15 of the step at qb) as bf16
+  // A fragments (rows = keys, k = queries); invisible elements become 0.
+  auto p_ds = [&](const f32x16& s, const f32x16& dp, int qb, int t, bf16x8& pf, bf16x8& dsf) {
+    const int x = qb + mbias;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        dva[db] = mfma32(pf[t], swz_frag_rows(Ds, db * 32, t, lane), dva[db]);
-        dka[db] = mfma32(dsf[t], swz_frag_rows(Qs, db * 32, t, lane), dka[db]);
-      }
+    for (int e = 0; e < 8; ++e) {
+      const int r = 8 * t + e;
+      float p = exp2_fast(s[r] * scale_log2);
+      p = (uint32_t)(x + 8 * (r >> 2) + (r & 3)) <= mspan ? p : 0.f;
+      pf[e] = (bf16)p;
+      dsf[e] = (bf16)(p * dp[r]);
+    }
+  };
+  // Half t of dV[key][d] += P^T dO and dK[key][d] += dS^T Q (scale applied
+  // at the end).
+  auto dv_dk = [&](int t, const bf16x8& pf, const bf16x8& dsf, const bf16x8* dof,
+                   const bf16x8* qtf) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      dva[db] = mfma32(pf, dof[t * 4 + db], dva[db]);
+      dka[db] = mfma32(dsf, qtf[t * 4 + db], dka[db]);
+    }
+  };
+
+  // Software pipeline over the steps.  Iteration `it` finishes step it (its
+  // S/dP products were computed one iteration earlier) while computing the
+  // S/dP products of step it + 1: the softmax of step it runs between the
+  // matrix products of step it + 1, then the dV/dK products of step it run.
+  // Buffer it % 2 holds step it; every read of it happens in iteration
+  // it - 1, so at the top of iteration it the loads of step it + 2 can go
+  // there, with a whole iteration to land.  On the last iteration the S/dP
+  // products of the step after are computed from stale data and discarded.
+  auto body = [&](int it, int qb, f32x16& s_c, f32x16& dp_c, bf16x8* dof_c, bf16x8* qtf_c,
+                  f32x16& s_n, f32x16& dp_n, bf16x8* dof_n, bf16x8* qtf_n) {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    if (it + 2 < steps) issue_next(it & 1);
+    s_dp((it + 1) & 1, s_n, dp_n, dof_n, qtf_n);
+    bf16x8 pf0, ds0, pf1, ds1;
+    p_ds(s_c, dp_c, qb, 0, pf0, ds0);
+    p_ds(s_c, dp_c, qb, 1, pf1, ds1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);    // 8 LDS reads
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // 3 LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // 7 VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    dv_dk(0, pf0, ds0, dof_c, qtf_c);
+    dv_dk(1, pf1, ds1, dof_c, qtf_c);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  f32x16 sA, dpA, sB, dpB;
+  bf16x8 dofA[8], qtfA[8], dofB[8], qtfB[8];
+  if (steps > 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (steps > 1) issue_next(1);
+    s_dp(0, sA, dpA, dofA, qtfA);
   }
+  int qb = k0;
+  auto next_qb = [&](int x) { return x + QBLK < k0 + nqb * QBLK ? x + QBLK : k0; };
+  int it = 0;
+  for (; it + 1 < steps; it += 2) {
+    body(it, qb, sA, dpA, dofA, qtfA, sB, dpB, dofB, qtfB);
+    qb = next_qb(qb);
+    body(it + 1, qb, sB, dpB, dofB, qtfB, sA, dpA, dofA, qtfA);
+    qb = next_qb(qb);
+  }
+  if (it < steps) body(it, qb, sA, dpA, dofA, qtfA, sB, dpB, dofB, qtfB);
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 
   // Head-group reduction in a fixed order (wave 0 + 1 + 2 + 3), then store.
   float* red = reinterpret_cast<float*>(smem);
@@ -342,7 +451,7 @@ hipError_t launch_dq(const void* q, const void* k, const void* v, const void* ou
                      reinterpret_cast<const Tile*>(ws + w.tiles_fwd), p.total_tokens,
                      p.num_q_heads, p.num_kv_heads, p.window, p.scale * LOG2E, p.scale,
                      (int)w.tile_cap, static_cast<bf16*>(dq),
-                     reinterpret_cast<RowStats*>(ws + w.rowstats));
+                     reinterpret_cast<TileStats*>(ws + w.rowstats));
   return hipGetLastError();
 }
 
@@ -354,7 +463,7 @@ hipError_t launch_dkdv(const void* q, const void* k, const void* v, const float*
   hipLaunchKernelGGL(dkdv_kernel, dim3(grid), dim3(BWD_THREADS), 0, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                      static_cast<const bf16*>(v), static_cast<const bf16*>(dout),
-                     reinterpret_cast<const RowStats*>(ws + w.rowstats), (int)w.tile_cap,
+                     reinterpret_cast<const TileStats*>(ws + w.rowstats), (int)w.tile_cap,
                      reinterpret_cast<const int*>(ws + w.header),
                      reinterpret_cast<const Tile*>(ws + w.tiles_bwd), p.total_tokens,
                      p.num_q_heads, p.num_kv_heads, p.window, p.scale * LOG2E, p.scale,

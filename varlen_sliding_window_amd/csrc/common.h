@@ -40,15 +40,18 @@ struct __attribute__((aligned(16))) Tile {
   int idx, pad0, pad1, pad2;
 };
 
-// Per-row values the backward passes from the dQ kernel to the dK/dV kernel:
-// lse * log2(e) and D = rowsum(dout * out), stored per (query head, tile) as
-// TILE consecutive pairs (256 bytes, 256-byte aligned).
-struct RowStats {
-  float lse2, d;
+// Per-row values the backward passes from the dQ kernel to the dK/dV kernel,
+// stored per (query head, q-tile): the starting values of the S and dP
+// accumulators of each row, -lse / scale and -D with D = rowsum(dout * out).
+// Seeded with them, the dK/dV kernel's products give P = exp2(scale log2(e)
+// acc_S) and dP - D = acc_dP directly.  256 bytes per tile.
+struct TileStats {
+  float s0[TILE];
+  float dp0[TILE];
 };
 
 // Workspace: [header | forward-order tiles | backward-order tiles |
-//             per-segment tile offsets | RowStats [Hq][tile_cap][TILE]]
+//             per-segment tile offsets | TileStats [Hq][tile_cap]]
 struct WorkspaceLayout {
   size_t header, tiles_fwd, tiles_bwd, seg_offsets, rowstats, total;
   size_t tile_cap;
@@ -70,7 +73,7 @@ inline WorkspaceLayout workspace_layout(int64_t total_tokens, int64_t num_seqs,
   w.tiles_bwd = w.tiles_fwd + align256(w.tile_cap * sizeof(Tile));
   w.seg_offsets = w.tiles_bwd + align256(w.tile_cap * sizeof(Tile));
   w.rowstats = w.seg_offsets + align256((size_t)(num_seqs + 1) * sizeof(int));
-  w.total = w.rowstats + align256((size_t)num_q_heads * w.tile_cap * TILE * sizeof(RowStats));
+  w.total = w.rowstats + align256((size_t)num_q_heads * w.tile_cap * sizeof(TileStats));
   return w;
 }
 

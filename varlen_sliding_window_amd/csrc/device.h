@@ -113,6 +113,32 @@ __device__ __forceinline__ void swz_tile32_load_async(bf16* tile, const bf16* g,
   }
 }
 
+// Direct global-to-LDS load by one wave: the 16 bytes at base + off of each
+// active lane land at LDS byte address lds + 16 * lane.  It is issued as
+// inline assembly so that the compiler does not make later LDS reads wait
+// for it: callers wait themselves (s_waitcnt vmcnt) before reading the
+// destination, and never read a destination with a load still in flight.
+// M0 carries the LDS address (one wait state between its write and the load)
+// and is restored afterwards, since the compiler owns it.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(lds)
+      : "memory");
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  typedef __attribute__((address_space(3))) const char lds_cchar;
+  return (uint32_t)(uintptr_t)(lds_cchar*)p;
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
