@@ -32,14 +32,17 @@ namespace {
 
 constexpr int BWD_THREADS = 256;
 
+constexpr int DQ_TILE_BYTES = KBLK * HEAD_DIM * (int)sizeof(bf16);   // 16 KB
+constexpr int DQ_BUF_BYTES = 2 * DQ_TILE_BYTES;                     // K and V
+static_assert(KBLK == 16 * 4, "each wave loads 16 rows of a block");
+
 __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ out, const bf16* __restrict__ dout, const float* __restrict__ lse,
     const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
     int window, float scale_log2, float scale, int tile_cap, bf16* __restrict__ dq,
     TileStats* __restrict__ stats) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[KBLK * LDS_PITCH];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[KBLK * LDS_PITCH];
+  __shared__ __attribute__((aligned(16))) char smem[2 * DQ_BUF_BYTES];
 
   const int chunks = Hq >> 2;
   const int item = blockIdx.x / chunks;
@@ -48,7 +51,8 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(
   const Tile tl = tiles[item];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, lh = lane >> 5, lq = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lh = lane >> 5, lq = lane & 31;
   const int head = hc * 4 + wave;
   const int g = (hc * 4) / (Hq / Hkv);
   const int q0 = tl.t0, q1 = tl.t1, a = tl.seg_a;
@@ -56,7 +60,28 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(
   const int nblk = (q1 - klo + KBLK - 1) / KBLK;
   const int qrow = q0 + lq;
   const size_t qstride = (size_t)Hq * HEAD_DIM;
-  const size_t kstride = (size_t)Hkv * HEAD_DIM;
+  const uint32_t kstride_b = (uint32_t)(Hkv * HEAD_DIM * sizeof(bf16));
+
+  // Block loads, as in the forward: wave w fills rows 16w .. 16w + 15 of the
+  // swizzled K and V tiles; keys before 0 re-read key 0 (always masked).
+  const bf16* kbase = k + (size_t)g * HEAD_DIM;
+  const bf16* vbase = v + (size_t)g * HEAD_DIM;
+  const uint32_t lds0 = lds_address(smem) + (uint32_t)(wave * 16 * HEAD_DIM * sizeof(bf16));
+  uint32_t coff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) coff[j] = (uint32_t)(((lane & 15) ^ swz(4 * j + (lane >> 4))) << 4);
+  auto issue = [&](int n, int buf) {
+    const int kb = q1 - KBLK * (n + 1);
+    const uint32_t l = lds0 + (uint32_t)(buf * DQ_BUF_BYTES);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = max(kb + 16 * wave + 4 * j + (lane >> 4), 0);
+      const uint32_t off = (uint32_t)key * kstride_b + coff[j];
+      dma16(kbase, off, l + j * 1024);
+      dma16(vbase, off, l + DQ_TILE_BYTES + j * 1024);
+    }
+  };
+  issue(0, 0);
 
   // Q^T and dO^T as B operands; D from dO and O at the same positions
   bf16x8 qf[8], df[8];
@@ -76,6 +101,10 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(
         df[ks] = zero_bf16x8();
       }
     }
+    // Make the compiler wait for these loads here, not inside the loop where
+    // the wait would also cover the block loads in flight.
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qf[ks]), "v"(df[ks]));
   }
   const float Dv = dpart + __shfl_xor(dpart, 32);
   const float lsev = qrow < T ? lse[(size_t)head * T + qrow] : 0.f;
@@ -88,40 +117,23 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(
     ts->dp0[lq] = qrow < q1 ? -Dv : 0.f;
   }
 
-  const int srow = tid >> 4, scol = (tid & 15) * 8;
-  uint4 kr[4], vr[4];
-  auto gload = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kb + srow + 16 * i;
-      if (key >= 0) {
-        const size_t off = (size_t)key * kstride + (size_t)g * HEAD_DIM + scol;
-        kr[i] = ldg16(k + off);
-        vr[i] = ldg16(v + off);
-      } else {
-        kr[i] = make_uint4(0u, 0u, 0u, 0u);
-        vr[i] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-  };
-
   f32x16 acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) acc[db] = zero_f32x16();
   const int full_lo = first_visible_key(q0 + TILE - 1, a, window);
   const int my_lo = first_visible_key(qrow, a, window);
 
-  gload(q1 - KBLK);
   for (int n = 0; n < nblk; ++n) {
     const int kb = q1 - KBLK * (n + 1);
+    const int buf = n & 1;
+    // This wave's loads of block n have landed; after the barrier so have
+    // everyone's, and every wave is done with block n - 1, whose buffer the
+    // loads of block n + 1 now overwrite.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<uint4*>(Ks + (srow + 16 * i) * LDS_PITCH + scol) = kr[i];
-      *reinterpret_cast<uint4*>(Vs + (srow + 16 * i) * LDS_PITCH + scol) = vr[i];
-    }
-    __syncthreads();
-    if (n + 1 < nblk) gload(kb - KBLK);
+    if (n + 1 < nblk) issue(n + 1, buf ^ 1);
+    const bf16* Ks = reinterpret_cast<const bf16*>(smem + buf * DQ_BUF_BYTES);
+    const bf16* Vs = Ks + KBLK * HEAD_DIM;
 
     f32x16 s[2], dp[2];
 #pragma unroll
@@ -130,8 +142,8 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(
       dp[h2] = zero_f32x16();
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        s[h2] = mfma32(lds_frag_cols(Ks + h2 * 32 * LDS_PITCH, ks, lane), qf[ks], s[h2]);
-        dp[h2] = mfma32(lds_frag_cols(Vs + h2 * 32 * LDS_PITCH, ks, lane), df[ks], dp[h2]);
+        s[h2] = mfma32(swz_frag_cols(Ks + h2 * 32 * HEAD_DIM, ks, lane), qf[ks], s[h2]);
+        dp[h2] = mfma32(swz_frag_cols(Vs + h2 * 32 * HEAD_DIM, ks, lane), df[ks], dp[h2]);
       }
     }
     const bool full = (kb + KBLK - 1 <= q0) && (kb >= full_lo);
@@ -141,17 +153,18 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kb + h2 * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
-        const bool vis = full || (key >= my_lo && key <= qrow);
-        const float p = vis ? exp2_fast(s[h2][r] * scale_log2 - lse2) : 0.f;
-        dsf[h2 * 2 + (r >> 3)][r & 7] = (bf16)(p * (dp[h2][r] - Dv));
+        const bool vis = full | ((key >= my_lo) & (key <= qrow));
+        const float p = exp2_fast(s[h2][r] * scale_log2 - lse2);
+        dsf[h2 * 2 + (r >> 3)][r & 7] = (bf16)(vis ? p * (dp[h2][r] - Dv) : 0.f);
       }
     // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q]
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int db = 0; db < 4; ++db)
-        acc[db] = mfma32(lds_frag_rows(Ks + db * 32, t, lane), dsf[t], acc[db]);
+        acc[db] = mfma32(swz_frag_rows(Ks, db * 32, t, lane), dsf[t], acc[db]);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   if (qrow < q1) {
     bf16* op = dq + (size_t)qrow * qstride + (size_t)head * HEAD_DIM + lh * 4;

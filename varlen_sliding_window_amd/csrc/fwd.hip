@@ -5,17 +5,23 @@
 // Fig. 2 "Benchmark setup": 8 query heads share 2 key-value heads, so 4 query
 // heads read the same K/V).  Each wave owns one head: its 32 q rows stay in
 // registers as MFMA operands, while the work-group streams the visible keys
-// through LDS in KBLK = 64-key blocks shared by the 4 heads.
+// through LDS in KBLK = 64-key blocks shared by the 4 heads.  The blocks
+// arrive by direct global-to-LDS loads, double-buffered: the loads of the
+// next block go out as soon as every wave is done with the buffer they
+// overwrite, one barrier per block.
 //
 // The wave computes S^T = K Q^T (keys x queries), so each lane holds one
 // query's scores in registers: the row max needs one cross-half exchange,
 // the row sum is kept per lane and combined once at the end, and P^T feeds
 // the O^T = V^T P^T product straight from registers (V^T read from the
 // natural-layout V tile with transposing LDS reads).  Softmax runs in the
-// exp2 domain with scale * log2(e) folded into one multiply.  Key blocks are
-// aligned to the tile end and walked from the diagonal backwards, so only
-// the diagonal block and the blocks at the segment start or window edge
-// need the mask.
+// exp2 domain with scale * log2(e) folded into one multiply, and the
+// running maximum is only moved (and O rescaled) when a block raises it by
+// more than RESCALE_LOG2: in between, probabilities may exceed 1 by up to
+// 2^RESCALE_LOG2, which bf16 and the fp32 sums carry exactly as well.  Key
+// blocks are aligned to the tile end and walked from the diagonal backwards,
+// so the first block sets a good maximum and only the diagonal block and the
+// blocks at the segment start or window edge need the mask.
 #include "device.h"
 #include "launch.h"
 
@@ -23,13 +29,17 @@ namespace attn {
 namespace {
 
 constexpr int FWD_THREADS = 256;
+constexpr int FWD_WAVES = 4;
+constexpr int FWD_TILE_BYTES = KBLK * HEAD_DIM * (int)sizeof(bf16);   // 16 KB
+constexpr int FWD_BUF_BYTES = 2 * FWD_TILE_BYTES;                     // K and V
+constexpr float RESCALE_LOG2 = 8.f;
+static_assert(KBLK == 16 * FWD_WAVES, "each wave loads 16 rows of a block");
 
 __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
     int window, float scale_log2, bf16* __restrict__ out, float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[KBLK * LDS_PITCH];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[KBLK * LDS_PITCH];
+  __shared__ __attribute__((aligned(16))) char smem[2 * FWD_BUF_BYTES];
 
   const int chunks = Hq >> 2;
   const int item = blockIdx.x / chunks;
@@ -38,7 +48,8 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(
   const Tile tl = tiles[item];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, lh = lane >> 5, lq = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lh = lane >> 5, lq = lane & 31;
   const int head = hc * 4 + wave;
   const int g = (hc * 4) / (Hq / Hkv);
   const int q0 = tl.t0, q1 = tl.t1, a = tl.seg_a;
@@ -46,7 +57,30 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(
   const int nblk = (q1 - klo + KBLK - 1) / KBLK;
   const int qrow = q0 + lq;
   const size_t qstride = (size_t)Hq * HEAD_DIM;
-  const size_t kstride = (size_t)Hkv * HEAD_DIM;
+  const uint32_t kstride_b = (uint32_t)(Hkv * HEAD_DIM * sizeof(bf16));
+
+  // Block loads: wave w fills rows 16w .. 16w + 15 of the K and V tiles,
+  // 4 rows (1 KB) per load; the lane fetches the 16-byte chunk that lands at
+  // physical chunk lane % 16 of its swizzled row.  Keys before 0 re-read key
+  // 0; they are always masked.
+  const bf16* kbase = k + (size_t)g * HEAD_DIM;
+  const bf16* vbase = v + (size_t)g * HEAD_DIM;
+  const uint32_t lds0 = lds_address(smem) + (uint32_t)(wave * 16 * HEAD_DIM * sizeof(bf16));
+  uint32_t coff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) coff[j] = (uint32_t)(((lane & 15) ^ swz(4 * j + (lane >> 4))) << 4);
+  auto issue = [&](int n, int buf) {
+    const int kb = q1 - KBLK * (n + 1);
+    const uint32_t l = lds0 + (uint32_t)(buf * FWD_BUF_BYTES);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = max(kb + 16 * wave + 4 * j + (lane >> 4), 0);
+      const uint32_t off = (uint32_t)key * kstride_b + coff[j];
+      dma16(kbase, off, l + j * 1024);
+      dma16(vbase, off, l + FWD_TILE_BYTES + j * 1024);
+    }
+  };
+  issue(0, 0);
 
   // Q^T as the B operand: lane holds q[qrow][16 ks + 8 lh + 0..7]
   bf16x8 qf[8];
@@ -54,25 +88,11 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(
     const bf16* qp = q + (size_t)qrow * qstride + (size_t)head * HEAD_DIM + lh * 8;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[ks] = qrow < T ? as_bf16x8(ldg16(qp + ks * 16)) : zero_bf16x8();
-  }
-
-  // K/V staging: thread copies rows srow + 16 i (i = 0..3), 8 columns at scol
-  const int srow = tid >> 4, scol = (tid & 15) * 8;
-  uint4 kr[4], vr[4];
-  auto gload = [&](int kb) {
+    // Make the compiler wait for these loads here, not inside the loop where
+    // the wait would also cover the block loads in flight.
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kb + srow + 16 * i;   // key <= q1 - 1 < T always
-      if (key >= 0) {
-        const size_t off = (size_t)key * kstride + (size_t)g * HEAD_DIM + scol;
-        kr[i] = ldg16(k + off);
-        vr[i] = ldg16(v + off);
-      } else {
-        kr[i] = make_uint4(0u, 0u, 0u, 0u);
-        vr[i] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-  };
+    for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qf[ks]));
+  }
 
   f32x16 o[4];
 #pragma unroll
@@ -81,26 +101,29 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(
   const int full_lo = first_visible_key(q0 + TILE - 1, a, window);
   const int my_lo = first_visible_key(qrow, a, window);
 
-  gload(q1 - KBLK);
   for (int n = 0; n < nblk; ++n) {
     const int kb = q1 - KBLK * (n + 1);
+    const int buf = n & 1;
+    // This wave's loads of block n have landed; after the barrier so have
+    // everyone's, and every wave is done with block n - 1, whose buffer the
+    // loads of block n + 1 now overwrite.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<uint4*>(Ks + (srow + 16 * i) * LDS_PITCH + scol) = kr[i];
-      *reinterpret_cast<uint4*>(Vs + (srow + 16 * i) * LDS_PITCH + scol) = vr[i];
-    }
-    __syncthreads();
-    if (n + 1 < nblk) gload(kb - KBLK);
+    if (n + 1 < nblk) issue(n + 1, buf ^ 1);
+    const bf16* Ks = reinterpret_cast<const bf16*>(smem + buf * FWD_BUF_BYTES);
+    const bf16* Vs = Ks + KBLK * HEAD_DIM;
 
     // S^T for keys kb + 32 h2 + [0, 32): s[h2][r] = q[qrow] . k[kb + 32 h2 + 8(r/4) + 4 lh + r%4]
+    bf16x8 kfr[16];
+#pragma unroll
+    for (int x = 0; x < 16; ++x) kfr[x] = swz_frag_cols(Ks + (x >> 3) * 32 * HEAD_DIM, x & 7, lane);
     f32x16 s[2];
+    s[0] = zero_f32x16();
+    s[1] = zero_f32x16();
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      s[h2] = zero_f32x16();
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        s[h2] = mfma32(lds_frag_cols(Ks + h2 * 32 * LDS_PITCH, ks, lane), qf[ks], s[h2]);
+    for (int ks = 0; ks < 8; ++ks) {
+      s[0] = mfma32(kfr[ks], qf[ks], s[0]);
+      s[1] = mfma32(kfr[8 + ks], qf[ks], s[1]);
     }
     const bool full = (kb + KBLK - 1 <= q0) && (kb >= full_lo);
     if (!full) {
@@ -113,16 +136,24 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(
         }
     }
 
-    // online softmax (log2 domain) for this lane's query
+    // online softmax (log2 domain) for this lane's query, lazy rescaling
     float mx = -INFINITY;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[h2][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m, mx * scale_log2);
-    const float mref = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = exp2_fast(m - mref);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mx > m + RESCALE_LOG2)) {
+      const float mnew = fmaxf(m, mx);
+      const float alpha = mnew == -INFINITY ? 1.f : exp2_fast(m - mnew);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      lsum *= alpha;
+      m = mnew;
+    }
+    const float mref = m == -INFINITY ? 0.f : m;
     bf16x8 pf[4];
     float rs = 0.f;
 #pragma unroll
@@ -133,20 +164,16 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(
         rs += p;
         pf[h2 * 2 + (r >> 3)][r & 7] = (bf16)p;
       }
-    lsum = lsum * alpha + rs;
-    m = mnew;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    lsum += rs;
 
     // O^T[d][q] += sum_key V^T[d][key] P^T[key][q]
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int db = 0; db < 4; ++db)
-        o[db] = mfma32(lds_frag_rows(Vs + db * 32, t, lane), pf[t], o[db]);
+        o[db] = mfma32(swz_frag_rows(Vs, db * 32, t, lane), pf[t], o[db]);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   const float lt = lsum + __shfl_xor(lsum, 32);
   if (qrow < q1) {
