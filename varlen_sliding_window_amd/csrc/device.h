@@ -68,13 +68,18 @@ __device__ __forceinline__ bf16x8 lds_frag_cols(const bf16* tile, int ks, int la
 }
 
 // ---- swizzled, unpadded LDS tiles --------------------------------------------
-// A tile holds rows of HEAD_DIM bf16 (256 bytes) with no padding; 16-byte
-// chunk c of row r is stored at chunk c ^ swz(r).  The swizzle is a
-// bijection per row, and makes both the 16-byte row reads (16 lanes on 16
-// rows, same chunk) and the transposing 8-byte reads (16 lanes on 4 rows x
-// 2 chunks) hit distinct banks.  Unpadded rows let one wave fill 4 whole rows
-// (1 KB) with a single direct global-to-LDS load.
-__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+// A tile holds rows of HEAD_DIM bf16 (256 bytes, all 64 banks) with no
+// padding; 16-byte chunk c of row r is stored at chunk c ^ swz(r), where
+// swz rotates the low four bits of r by two.  The swizzle is a bijection per
+// row and keeps both read patterns free of bank conflicts:
+//   16-byte row reads: 16 lanes on 16 consecutive rows, same chunk ->
+//     swz takes 16 distinct values;
+//   transposing 8-byte reads: 32 lanes on 4 consecutive rows x 4 consecutive
+//     chunks (an aligned group of 4) -> the 4 rows' swz values differ in
+//     bits 2-3, so each row lands in its own group of 4 chunks.
+// Unpadded rows let one wave fill 4 whole rows (1 KB) with a single direct
+// global-to-LDS load.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 // Like lds_frag_cols, on a swizzled tile.
 __device__ __forceinline__ bf16x8 swz_frag_cols(const bf16* tile, int ks, int lane) {
