@@ -192,11 +192,23 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const TileStats* __restrict__ stats, int tile_cap,
     const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
-    int window, float scale_log2, float scale, bf16* __restrict__ dk, bf16* __restrict__ dv) {
+    int window, float scale_log2, float scale, int run_len, bf16* __restrict__ dk,
+    bf16* __restrict__ dv) {
   __shared__ __attribute__((aligned(16))) char smem[DKDV_LDS_BYTES];
 
-  const int item = blockIdx.x / Hkv;
-  const int g = blockIdx.x - item * Hkv;
+  // Work-groups go to the 8 XCDs round-robin (work-group b to XCD b % 8).
+  // XCD x takes runs of R consecutive entries of the sorted list with one
+  // key-value head, so that the work-groups running together on an XCD are
+  // mostly neighbouring key tiles whose Q/dO rows meet in that XCD's L2.
+  // Rounds of 8 runs go to the XCDs in alternating directions, so that no
+  // XCD always gets the most expensive run of a round.
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int round = slot / run_len;
+  const int rx = (round & 1) ? 7 - xcd : xcd;
+  const int pos = (round * 8 + rx) * run_len + (slot - round * run_len);
+  const int run = pos / (run_len * Hkv), within = pos - run * run_len * Hkv;
+  const int g = within / run_len;
+  const int item = run * run_len + (within - g * run_len);
   if (item >= header[0]) return;
   const Tile tl = tiles[item];
 
@@ -472,14 +484,22 @@ hipError_t launch_dkdv(const void* q, const void* k, const void* v, const float*
                        const void* dout, const Problem& p, void* dk, void* dv, void* workspace,
                        const WorkspaceLayout& w, hipStream_t stream) {
   const char* ws = static_cast<const char*>(workspace);
-  const unsigned grid = (unsigned)(w.tile_cap * (size_t)p.num_kv_heads);
+  // Runs of R list entries per key-value head, dealt to the XCDs in rounds
+  // of 8 runs (see the kernel); the grid covers every (tile, head) pair.
+  // Local layers, where most tiles cost the same, take long runs (more L2
+  // reuse); global layers, where costs fall along each document, take short
+  // ones (better balance).
+  const int run_len = p.window > 0 ? 32 : 8;
+  const size_t items = (size_t)p.num_kv_heads * (w.tile_cap + run_len - 1);
+  const size_t round = 8 * (size_t)run_len;
+  const unsigned grid = (unsigned)((items + round - 1) / round * round);
   hipLaunchKernelGGL(dkdv_kernel, dim3(grid), dim3(BWD_THREADS), 0, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                      static_cast<const bf16*>(v), static_cast<const bf16*>(dout),
                      reinterpret_cast<const TileStats*>(ws + w.rowstats), (int)w.tile_cap,
                      reinterpret_cast<const int*>(ws + w.header),
                      reinterpret_cast<const Tile*>(ws + w.tiles_bwd), p.total_tokens,
-                     p.num_q_heads, p.num_kv_heads, p.window, p.scale * LOG2E, p.scale,
+                     p.num_q_heads, p.num_kv_heads, p.window, p.scale * LOG2E, p.scale, run_len,
                      static_cast<bf16*>(dk), static_cast<bf16*>(dv));
   return hipGetLastError();
 }

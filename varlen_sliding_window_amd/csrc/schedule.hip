@@ -89,6 +89,28 @@ __device__ __forceinline__ int bwd_bin(const Tile& t, int window) {
   return min((qhi - t.t0 + QBLK - 1) / QBLK, SORT_BINS - 1);
 }
 
+// Slot of this lane's tile in bucket `bin` (hist holds the next free slot of
+// every bucket).  Called by whole waves; lanes with valid == false take none.
+// Lanes sharing the bucket of the lowest unplaced lane get consecutive
+// slots in lane order, for up to four buckets per wave.
+__device__ int ordered_slot(int* hist, int bin, bool valid) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long active = __ballot(valid);
+  int slot = 0;
+  for (int round = 0; round < 4 && active != 0ull; ++round) {
+    const int leader = __ffsll((long long)active) - 1;
+    const int b = __builtin_amdgcn_readlane(bin, leader);
+    const unsigned long long m = __ballot(valid && bin == b) & active;
+    int base = 0;
+    if (lane == leader) base = atomicAdd(&hist[b], __popcll(m));
+    base = __builtin_amdgcn_readlane(base, leader);
+    if ((m >> lane) & 1ull) slot = base + __popcll(m & ((1ull << lane) - 1ull));
+    active &= ~m;
+  }
+  if ((active >> lane) & 1ull) slot = atomicAdd(&hist[bin], 1);
+  return slot;
+}
+
 // Segments whose boundaries and offsets fit here are scheduled from LDS;
 // larger counts fall back to the workspace copy in global memory.
 constexpr int SCHED_LDS_SEGS = 4096;
@@ -156,11 +178,27 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
   }
   __syncthreads();
 
-  // 4. scatter (order inside a bucket is arbitrary; results do not depend on it)
-  for (int i = tid; i < ntiles; i += SCHED_THREADS) {
-    const Tile t = tile_at(i, seg_off, cu, nseq, T);
-    fwd_list[atomicAdd(&hist_f[fwd_bin(t, window)], 1)] = t;
-    if (need_bwd) bwd_list[atomicAdd(&hist_b[bwd_bin(t, window)], 1)] = t;
+  // 4. scatter (results do not depend on the order inside a bucket).  In the
+  // backward list each wave places its 64 consecutive tiles so that tiles of
+  // one bucket from one wave keep their token order (a few ballot rounds,
+  // then single atomics for what is left): runs of equal cost stay runs of
+  // neighbouring tiles, which the dK/dV kernel maps onto one XCD, whose L2
+  // then serves the rows that neighbouring tiles share.
+  for (int i0 = 0; i0 < ntiles; i0 += SCHED_THREADS) {
+    const int i = i0 + tid;
+    const bool valid = i < ntiles;
+    Tile t;
+    int bf = 0, bb = 0;
+    if (valid) {
+      t = tile_at(i, seg_off, cu, nseq, T);
+      bf = fwd_bin(t, window);
+      bb = bwd_bin(t, window);
+    }
+    if (valid) fwd_list[atomicAdd(&hist_f[bf], 1)] = t;
+    if (need_bwd) {
+      const int pb = ordered_slot(hist_b, bb, valid);
+      if (valid) bwd_list[pb] = t;
+    }
   }
   if (tid == 0) header[0] = ntiles;
 }
