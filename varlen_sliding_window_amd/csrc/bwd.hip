@@ -146,17 +146,27 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(
         dp[h2] = mfma32(swz_frag_cols(Vs + h2 * 32 * HEAD_DIM, ks, lane), df[ks], dp[h2]);
       }
     }
+    // dS^T = P^T (dP^T - D), computed for every element; blocks that cross
+    // the diagonal, the window edge or the segment start then zero the
+    // invisible elements with selects (so values there, even NaNs, drop out).
     const bool full = (kb + KBLK - 1 <= q0) && (kb >= full_lo);
+    float dsv[32];
+#pragma unroll
+    for (int x = 0; x < 32; ++x) {
+      const float p = exp2_fast(s[x >> 4][x & 15] * scale_log2 - lse2);
+      dsv[x] = p * (dp[x >> 4][x & 15] - Dv);
+    }
+    if (!full) {
+#pragma unroll
+      for (int x = 0; x < 32; ++x) {
+        const int r = x & 15;
+        const int key = kb + (x >> 4) * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
+        dsv[x] = (key >= my_lo) & (key <= qrow) ? dsv[x] : 0.f;
+      }
+    }
     bf16x8 dsf[4];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kb + h2 * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
-        const bool vis = full | ((key >= my_lo) & (key <= qrow));
-        const float p = exp2_fast(s[h2][r] * scale_log2 - lse2);
-        dsf[h2 * 2 + (r >> 3)][r & 7] = (bf16)(vis ? p * (dp[h2][r] - Dv) : 0.f);
-      }
+    for (int x = 0; x < 32; ++x) dsf[x >> 3][x & 7] = (bf16)dsv[x];
     // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q]
 #pragma unroll
     for (int t = 0; t < 4; ++t)
