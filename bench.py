@@ -303,6 +303,30 @@ def main():
                 "flops_per_launch": dom["flops"] / dom["launches"],
                 "share_of_step": dom["ms"] / ms_per_step}
 
+    # The same step captured once as a HIP graph and replayed (the library
+    # allocates nothing and never waits on the host, so the whole step is
+    # capturable); replays remove the per-launch gaps between kernels.
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(max(args.warmup, 1)):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    graph_report = {"ms_per_step": graph_ms, "tflops": step_flops / (graph_ms * 1e-3) / 1e12,
+                    "speedup_vs_eager": ms_per_step / graph_ms, "steps": args.steps}
+    del graph
+
     result = {
         "metric": "fwd+bwd TFLOPS per 16,384-token microbatch (window-512 and global layers, "
                   "context 4,096)",
@@ -333,6 +357,7 @@ def main():
         "layers": layer_report,
         "kernels": kernels,
         "roofline": roofline,
+        "graph_replay": graph_report,
         "gpu": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:
