@@ -161,7 +161,7 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(
       for (int x = 0; x < 32; ++x) {
         const int r = x & 15;
         const int key = kb + (x >> 4) * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
-        dsv[x] = (key >= my_lo) & (key <= qrow) ? dsv[x] : 0.f;
+        dsv[x] = ((key >= my_lo) & (key <= qrow)) ? dsv[x] : 0.f;
       }
     }
     bf16x8 dsf[4];
