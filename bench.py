@@ -191,6 +191,8 @@ def main():
                     help="print the kernel-source hash the traffic summary is keyed on")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the CPU oracle (profiling runs)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the graph-replay timing (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain copies of a known size (counter calibration)")
     args = ap.parse_args()
@@ -306,26 +308,28 @@ def main():
     # The same step captured once as a HIP graph and replayed (the library
     # allocates nothing and never waits on the host, so the whole step is
     # capturable); replays remove the per-launch gaps between kernels.
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        step()
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step()
-    for _ in range(max(args.warmup, 1)):
-        graph.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        graph.replay()
-    torch.cuda.synchronize()
-    graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    graph_report = {"ms_per_step": graph_ms, "tflops": step_flops / (graph_ms * 1e-3) / 1e12,
-                    "speedup_vs_eager": ms_per_step / graph_ms, "steps": args.steps}
-    del graph
+    graph_report = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(max(args.warmup, 1)):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        graph_report = {"ms_per_step": graph_ms, "tflops": step_flops / (graph_ms * 1e-3) / 1e12,
+                        "speedup_vs_eager": ms_per_step / graph_ms, "steps": args.steps}
+        del graph
 
     result = {
         "metric": "fwd+bwd TFLOPS per 16,384-token microbatch (window-512 and global layers, "
