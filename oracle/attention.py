@@ -34,6 +34,19 @@ query itself (i - W < j <= i); window <= 0 means full causal context; query
 head h reads key-value head floor(h / G); the scale multiplies q.k before
 the softmax; LSE is the natural log, laid out [Hq, T].
 
+Logit soft-cap (optional, softcap = c > 0).  The performance reference page
+(dewml.dev/reference/performance, section "Head dimension 256 through
+tokamax's Triton flash attention") lists Gemma 2's attention-logit soft-cap
+as a feature a training kernel needs in its forward and its backward.  The
+cap bounds each scaled logit smoothly to (-c, c) before the softmax:
+
+    S'_ij  = c * tanh(S_ij / c)        (replaces S_ij above; no bias term)
+    dS_ij  = P_ij (dP_ij - D_hi) * (1 - tanh(S_ij / c)^2)
+
+i.e. the softmax gradient taken with respect to S' and carried back through
+the cap by the chain rule.  The page gives no value for c; softcap <= 0
+means no cap.
+
 Implementation: one dense [L, L] block per (segment, query head) with a
 boolean mask, all in float64.  Inputs are taken as float arrays (the exact
 bf16 values the GPU reads, widened); nothing is rounded on the way.
@@ -73,19 +86,30 @@ def _check(q, k, v):
     return hq // hkv
 
 
-def _segment_head_forward(qs, ks, vs, mask, scale):
-    """Softmax attention of one segment and one query head (fp64)."""
+def _capped_logits(qs, ks, scale, softcap):
+    """Scaled logits of one segment and head, soft-capped when softcap > 0.
+
+    Also returns d S' / d S (all ones without a cap)."""
     s = scale * (qs @ ks.T)
+    if softcap > 0:
+        t = np.tanh(s / softcap)
+        return softcap * t, 1.0 - t * t
+    return s, np.ones_like(s)
+
+
+def _segment_head_forward(qs, ks, vs, mask, scale, softcap=0.0):
+    """Softmax attention of one segment and one query head (fp64)."""
+    s, dcap = _capped_logits(qs, ks, scale, softcap)
     s = np.where(mask, s, -np.inf)
     m = s.max(axis=1, keepdims=True)          # every row sees at least itself
     e = np.exp(s - m)
     z = e.sum(axis=1, keepdims=True)
     lse = (m + np.log(z))[:, 0]
     p = e / z
-    return p @ vs, lse, p
+    return p @ vs, lse, p, dcap
 
 
-def attention_forward(q, k, v, cu_seqlens, window: int, scale: float):
+def attention_forward(q, k, v, cu_seqlens, window: int, scale: float, softcap: float = 0.0):
     """out [T, Hq, d] and lse [Hq, T], float64.  Rows outside every segment are 0 / -inf."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -98,13 +122,15 @@ def attention_forward(q, k, v, cu_seqlens, window: int, scale: float):
         mask = visible_mask(b - a, window)
         for h in range(hq):
             g = h // group
-            o, l, _ = _segment_head_forward(q[a:b, h], k[a:b, g], v[a:b, g], mask, scale)
+            o, l, _, _ = _segment_head_forward(q[a:b, h], k[a:b, g], v[a:b, g], mask, scale,
+                                               softcap)
             out[a:b, h] = o
             lse[h, a:b] = l
     return out, lse
 
 
-def attention_backward(q, k, v, dout, cu_seqlens, window: int, scale: float):
+def attention_backward(q, k, v, dout, cu_seqlens, window: int, scale: float,
+                       softcap: float = 0.0):
     """Analytic gradients of sum(dout * out): dq, dk, dv (float64), plus out, lse, D."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -123,12 +149,12 @@ def attention_backward(q, k, v, dout, cu_seqlens, window: int, scale: float):
         for h in range(hq):
             g = h // group
             qs, ks, vs, dos = q[a:b, h], k[a:b, g], v[a:b, g], do[a:b, h]
-            o, l, p = _segment_head_forward(qs, ks, vs, mask, scale)
+            o, l, p, dcap = _segment_head_forward(qs, ks, vs, mask, scale, softcap)
             out[a:b, h] = o
             lse[h, a:b] = l
             dp = dos @ vs.T
             dd = (p * dp).sum(axis=1, keepdims=True)
-            ds = p * (dp - dd)
+            ds = p * (dp - dd) * dcap
             dsum[h, a:b] = dd[:, 0]
             dq[a:b, h] = scale * (ds @ ks)
             dk[a:b, g] += scale * (ds.T @ qs)
@@ -136,7 +162,8 @@ def attention_backward(q, k, v, dout, cu_seqlens, window: int, scale: float):
     return dq, dk, dv, out, lse, dsum
 
 
-def attention_row(q, k, v, dout, cu_seqlens, window: int, scale: float, h: int, i: int):
+def attention_row(q, k, v, dout, cu_seqlens, window: int, scale: float, h: int, i: int,
+                  softcap: float = 0.0):
     """One query row, computed alone: (out_ih [d], lse_hi, dq_ih [d]).
 
     Used to check single sampled outputs of large problems without running
@@ -153,11 +180,16 @@ def attention_row(q, k, v, dout, cu_seqlens, window: int, scale: float, h: int, 
     qi = np.asarray(q[i, h], dtype=np.float64)
     doi = np.asarray(dout[i, h], dtype=np.float64)
     s = scale * (ks @ qi)
+    dcap = np.ones_like(s)
+    if softcap > 0:
+        t = np.tanh(s / softcap)
+        s = softcap * t
+        dcap = 1.0 - t * t
     m = s.max()
     e = np.exp(s - m)
     z = e.sum()
     p = e / z
     o = p @ vs
     dp = vs @ doi
-    ds = p * (dp - p @ dp)
+    ds = p * (dp - p @ dp) * dcap
     return o, m + np.log(z), scale * (ds @ ks)

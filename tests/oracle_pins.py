@@ -278,6 +278,149 @@ def pin_row_function(o):
             _close(rdq, dq[i, h], 1e-12, "row dq")
 
 
+# --------------------------------------------------------------------------
+# Logit soft-cap: S' = c tanh(S / c) before the softmax
+# --------------------------------------------------------------------------
+def pin_softcap_two_keys(o):
+    """Hand-derived two-key case.  One document [t0, t1], d = 2, scale 1,
+    q1 = (2, 0), k0 = (1, 0), k1 = (-1, 0): S_1 = (2, -2) and, with cap
+    c = 2, S'_1 = (2 tanh 1, -2 tanh 1).  Row 1 is a two-way softmax:
+    p0 = 1 / (1 + exp(-4 tanh 1)), p1 = 1 - p0, LSE = log(2 cosh(2 tanh 1)),
+    and dS_10 = -dS_11 = sech^2(1) p0 p1 (dP_10 - dP_11).  Row 0 sees only
+    key 0: O_0 = v0, LSE_0 = c tanh(S_00 / c), dS_00 = 0."""
+    c = 2.0
+    q = np.array([[[0.5, 1.0]], [[2.0, 0.0]]])
+    k = np.array([[[1.0, 0.0]], [[-1.0, 0.0]]])
+    v = np.array([[[3.0, -1.0]], [[0.5, 2.0]]])
+    do = np.array([[[1.0, 2.0]], [[-1.5, 0.25]]])
+    dq, dk, dv, out, lse, _ = o.attention_backward(q, k, v, do, [0, 2], 0, 1.0, c)
+    th = math.tanh(1.0)
+    p0 = 1.0 / (1.0 + math.exp(-4.0 * th))
+    p1 = 1.0 - p0
+    sech2 = 1.0 - th * th
+    dp0 = do[1, 0] @ v[0, 0]
+    dp1 = do[1, 0] @ v[1, 0]
+    ds10 = sech2 * p0 * p1 * (dp0 - dp1)
+    _close(out[0, 0], v[0, 0], 1e-14, "cap 2-key O_0")
+    _close(lse[0, 0], c * math.tanh(0.5 / c), 1e-14, "cap 2-key LSE_0")
+    _close(out[1, 0], p0 * v[0, 0] + p1 * v[1, 0], 1e-14, "cap 2-key O_1")
+    _close(lse[0, 1], math.log(2.0 * math.cosh(2.0 * th)), 1e-14, "cap 2-key LSE_1")
+    _close(dq[0, 0], np.zeros(2), 1e-14, "cap 2-key dq_0")
+    _close(dq[1, 0], ds10 * (k[0, 0] - k[1, 0]), 1e-14, "cap 2-key dq_1")
+    _close(dk[0, 0], ds10 * q[1, 0], 1e-14, "cap 2-key dk_0")
+    _close(dk[1, 0], -ds10 * q[1, 0], 1e-14, "cap 2-key dk_1")
+    _close(dv[0, 0], do[0, 0] + p0 * do[1, 0], 1e-14, "cap 2-key dv_0")
+    _close(dv[1, 0], p1 * do[1, 0], 1e-14, "cap 2-key dv_1")
+
+
+def pin_softcap_large_is_uncapped(o):
+    """c tanh(S / c) = S - S^3 / (3 c^2) + ...: a cap of 1e6 on logits of
+    size ~10 changes nothing beyond ~1e-10 relative."""
+    q, k, v, do = rand_inputs(14, CU_MIXED, 4, 2, 8, 2.0)
+    for w in (0, 3):
+        ref = o.attention_backward(q, k, v, do, CU_MIXED, w, 0.6)
+        got = o.attention_backward(q, k, v, do, CU_MIXED, w, 0.6, 1e6)
+        for x, y, name in zip(got, ref, ("dq", "dk", "dv", "out", "lse", "D")):
+            assert _rel(x, y) <= 1e-9, f"cap 1e6 vs none: {name} differs"
+
+
+def pin_softcap_bounds(o):
+    """Every capped logit lies in [-c, c] (tanh reaches +-1 in fp64 once
+    saturated), so each row's LSE lies within [log n - c, log n + c] for its
+    n visible keys, and rows still sum to one."""
+    q, k, v, _ = rand_inputs(15, CU_MIXED, 4, 2, 8, 10.0)
+    c = 0.75
+    v1 = np.ones_like(v)
+    for w in (0, 4):
+        out, lse = o.attention_forward(q, k, v1, CU_MIXED, w, 1.0, c)
+        _close(out, np.ones_like(out), 1e-12, f"cap rows sum to 1 (W={w})")
+        for a, b in zip(CU_MIXED[:-1], CU_MIXED[1:]):
+            for i in range(a, b):
+                lo = a if w <= 0 else max(a, i - w + 1)
+                n = i - lo + 1
+                assert np.all(np.abs(lse[:, i] - math.log(n)) <= c + 1e-12), "cap LSE bound"
+
+
+def pin_softcap_torch_autograd(o):
+    """torch (fp64, CPU): scores, tanh cap, masked softmax over a block-
+    diagonal causal/window mask, and autograd for the gradients."""
+    import torch
+    cu = [0, 7, 7, 19, 20, 33]
+    hq, hkv, d = 4, 2, 8
+    q, k, v, do = rand_inputs(16, cu, hq, hkv, d, 3.0)
+    t = cu[-1]
+    scale, c = 0.5, 2.5
+    for w in (0, 5):
+        dq, dk, dv, out, lse, _ = o.attention_backward(q, k, v, do, cu, w, scale, c)
+        tq = torch.tensor(q.transpose(1, 0, 2), requires_grad=True)
+        tk = torch.tensor(k.transpose(1, 0, 2), requires_grad=True)
+        tv = torch.tensor(v.transpose(1, 0, 2), requires_grad=True)
+        kr = tk.repeat_interleave(hq // hkv, dim=0)
+        vr = tv.repeat_interleave(hq // hkv, dim=0)
+        seg = torch.zeros(t, dtype=torch.long)
+        for sidx, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
+            seg[a:b] = sidx
+        i = torch.arange(t)[:, None]
+        j = torch.arange(t)[None, :]
+        allowed = (seg[:, None] == seg[None, :]) & (j <= i)
+        if w > 0:
+            allowed &= j > i - w
+        sc = scale * torch.matmul(tq, kr.transpose(1, 2))
+        sc = c * torch.tanh(sc / c)
+        sc = sc.masked_fill(~allowed, float("-inf"))
+        ref_lse = torch.logsumexp(sc, dim=-1)
+        ref = torch.matmul(torch.softmax(sc, dim=-1), vr)
+        ref.backward(torch.tensor(do.transpose(1, 0, 2)))
+        _close(out, ref.detach().numpy().transpose(1, 0, 2), 1e-10, f"cap torch out (W={w})")
+        _close(lse, ref_lse.detach().numpy(), 1e-10, f"cap torch lse (W={w})")
+        _close(dq, tq.grad.numpy().transpose(1, 0, 2), 1e-10, f"cap torch dq (W={w})")
+        _close(dk, tk.grad.numpy().transpose(1, 0, 2), 1e-10, f"cap torch dk (W={w})")
+        _close(dv, tv.grad.numpy().transpose(1, 0, 2), 1e-10, f"cap torch dv (W={w})")
+
+
+def pin_softcap_finite_differences(o):
+    """Central differences of sum(dO * O) through the cap (c = 1.5, logits
+    of size ~5, so tanh is far from linear)."""
+    cu = [0, 1, 6, 13]
+    q, k, v, do = rand_inputs(17, cu, 2, 1, 4, 2.0)
+    h = 1e-6
+    c, scale = 1.5, 0.8
+    for w in (0, 3):
+        dq, dk, dv, *_ = o.attention_backward(q, k, v, do, cu, w, scale, c)
+
+        def loss(qq, kk, vv):
+            out, _ = o.attention_forward(qq, kk, vv, cu, w, scale, c)
+            return float((out * do).sum())
+
+        for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            num = np.zeros_like(x)
+            it = np.nditer(x, flags=["multi_index"])
+            for _ in it:
+                idx = it.multi_index
+                args_p = {"q": q, "k": k, "v": v}
+                args_m = dict(args_p)
+                args_p[name] = x.copy()
+                args_m[name] = x.copy()
+                args_p[name][idx] += h
+                args_m[name][idx] -= h
+                num[idx] = (loss(args_p["q"], args_p["k"], args_p["v"]) -
+                            loss(args_m["q"], args_m["k"], args_m["v"])) / (2 * h)
+            r = _rel(grad, num)
+            assert r <= 1e-6, f"cap finite differences d{name} (W={w}): rel err {r:.2e}"
+
+
+def pin_softcap_row_function(o):
+    """The single-row function equals the full oracle's row, with a cap."""
+    q, k, v, do = rand_inputs(18, CU_MIXED, 4, 2, 8, 2.0)
+    for w in (0, 3):
+        dq, _, _, out, lse, _ = o.attention_backward(q, k, v, do, CU_MIXED, w, 0.3, 1.25)
+        for h, i in ((0, 0), (3, 5), (1, 13), (2, 28), (3, 36)):
+            ro, rl, rdq = o.attention_row(q, k, v, do, CU_MIXED, w, 0.3, h, i, 1.25)
+            _close(ro, out[i, h], 1e-12, "cap row out")
+            _close(rl, lse[h, i], 1e-12, "cap row lse")
+            _close(rdq, dq[i, h], 1e-12, "cap row dq")
+
+
 ALL_PINS = [
     pin_golden,
     pin_rows_sum_to_one,
@@ -293,4 +436,10 @@ ALL_PINS = [
     pin_row_function,
     pin_torch_sdpa,
     pin_finite_differences,
+    pin_softcap_two_keys,
+    pin_softcap_large_is_uncapped,
+    pin_softcap_bounds,
+    pin_softcap_row_function,
+    pin_softcap_torch_autograd,
+    pin_softcap_finite_differences,
 ]

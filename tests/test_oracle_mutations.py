@@ -36,6 +36,15 @@ MUTATIONS = [
     ("row window off by one", "lo = max(a, i - window + 1) if window > 0 else a",
      "lo = max(a, i - window) if window > 0 else a"),
     ("row dq drops D", "ds = p * (dp - p @ dp)", "ds = p * dp"),
+    ("cap derivative dropped", "ds = p * (dp - dd) * dcap", "ds = p * (dp - dd)"),
+    ("cap derivative 1 - t", "return softcap * t, 1.0 - t * t", "return softcap * t, 1.0 - t"),
+    ("cap on unscaled logits", "t = np.tanh(s / softcap)\n        return softcap * t",
+     "t = np.tanh(s / scale / softcap)\n        return scale * softcap * t"),
+    ("cap as hard clip", "t = np.tanh(s / softcap)\n        return softcap * t",
+     "t = np.clip(s / softcap, -1.0, 1.0)\n        return softcap * t"),
+    ("row cap derivative dropped", "ds = p * (dp - p @ dp) * dcap", "ds = p * (dp - p @ dp)"),
+    ("row cap ignored", "    if softcap > 0:\n        t = np.tanh(s / softcap)\n        s = softcap * t",
+     "    if softcap > 1e300:\n        t = np.tanh(s / softcap)\n        s = softcap * t"),
 ]
 
 
