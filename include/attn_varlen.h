@@ -121,6 +121,34 @@ attn_status attn_varlen_bwd(const void* q, const void* k, const void* v,
                             void* dq, void* dk, void* dv,
                             void* workspace, size_t workspace_bytes, attn_stream_t stream);
 
+/*
+ * Forward and backward with an optional logit soft-cap.  With softcap = c > 0
+ * every scaled logit S = scale * q.k is replaced by c * tanh(S / c) before
+ * the softmax (Gemma 2's attention soft-cap, which the performance reference
+ * page dewml.dev/reference/performance lists, in its section on head
+ * dimension 256 through tokamax's Triton flash attention, as a feature the
+ * backward must support too), lse is taken over the capped logits, and the
+ * backward carries the cap's derivative 1 - tanh^2(S / c) into dq and dk.
+ * softcap = 0 is exactly attn_varlen_fwd / attn_varlen_bwd.  Other
+ * arguments as there; the backward must get the same softcap as the forward
+ * that produced out and lse.
+ *   softcap   finite and >= 0; negative, NaN or infinite -> ATTN_EINVAL
+ */
+attn_status attn_varlen_fwd_ex(const void* q, const void* k, const void* v,
+                               const int32_t* cu_seqlens, int32_t num_seqs,
+                               int32_t total_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t max_seqlen, int32_t window, float scale,
+                               float softcap, void* out, float* lse,
+                               void* workspace, size_t workspace_bytes, attn_stream_t stream);
+
+attn_status attn_varlen_bwd_ex(const void* q, const void* k, const void* v,
+                               const void* out, const float* lse, const void* dout,
+                               const int32_t* cu_seqlens, int32_t num_seqs,
+                               int32_t total_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t max_seqlen, int32_t window, float scale,
+                               float softcap, void* dq, void* dk, void* dv,
+                               void* workspace, size_t workspace_bytes, attn_stream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char* attn_varlen_strerror(attn_status s);
 

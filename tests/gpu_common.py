@@ -31,29 +31,25 @@ def device_inputs(mb: Microbatch, device="cuda"):
     return q, k, v, do, cu
 
 
-def run_hip(mb: Microbatch, window: int, max_seqlen: int | None = None, cu=None):
-    """Forward then backward through the C ABI; returns float64 numpy arrays."""
+def raw_outputs(mb: Microbatch, window: int, cu=None, max_seqlen=None, softcap: float = 0.0,
+                scale: float | None = None):
+    """Forward then backward through the C ABI; the raw torch tensors."""
     q, k, v, do, cu_dev = device_inputs(mb)
     if cu is not None:
         cu_dev = torch.as_tensor(np.asarray(cu, dtype=np.int32)).cuda()
     ms = mb.max_seqlen if max_seqlen is None else max_seqlen
-    out, lse = attn.fwd(q, k, v, cu_dev, ms, window, mb.cfg.scale)
-    dq, dk, dv = attn.bwd(q, k, v, out, lse, do, cu_dev, ms, window, mb.cfg.scale)
-    torch.cuda.synchronize()
-    return {name: t.float().cpu().numpy().astype(np.float64)
-            for name, t in (("out", out), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv))}
-
-
-def raw_outputs(mb: Microbatch, window: int, cu=None, max_seqlen=None):
-    """Same as run_hip but returns the raw torch tensors (for bitwise checks)."""
-    q, k, v, do, cu_dev = device_inputs(mb)
-    if cu is not None:
-        cu_dev = torch.as_tensor(np.asarray(cu, dtype=np.int32)).cuda()
-    ms = mb.max_seqlen if max_seqlen is None else max_seqlen
-    out, lse = attn.fwd(q, k, v, cu_dev, ms, window, mb.cfg.scale)
-    dq, dk, dv = attn.bwd(q, k, v, out, lse, do, cu_dev, ms, window, mb.cfg.scale)
+    sc = mb.cfg.scale if scale is None else scale
+    out, lse = attn.fwd(q, k, v, cu_dev, ms, window, sc, softcap=softcap)
+    dq, dk, dv = attn.bwd(q, k, v, out, lse, do, cu_dev, ms, window, sc, softcap=softcap)
     torch.cuda.synchronize()
     return {"out": out, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+
+
+def run_hip(mb: Microbatch, window: int, max_seqlen: int | None = None, cu=None,
+            softcap: float = 0.0, scale: float | None = None):
+    """Same as raw_outputs, as float64 numpy arrays."""
+    r = raw_outputs(mb, window, cu=cu, max_seqlen=max_seqlen, softcap=softcap, scale=scale)
+    return {name: t.float().cpu().numpy().astype(np.float64) for name, t in r.items()}
 
 
 def rel_errors(x: np.ndarray, y: np.ndarray) -> tuple[float, float]:

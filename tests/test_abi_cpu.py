@@ -79,6 +79,15 @@ def test_fwd_rejects(lib, over, code):
     assert call_fwd(lib, **over) == code
 
 
+@pytest.mark.parametrize("cap", [-1.0, -1e-30, float("nan"), float("inf"), float("-inf")])
+def test_softcap_rejects(lib, cap):
+    args = [FAKE] * 4 + [1, 64, 8, 2, 128, 64, 0, 0.088, cap, FAKE, FAKE, FAKE, 1 << 30, None]
+    assert lib.attn_varlen_fwd_ex(*args) == EINVAL
+    bargs = [FAKE] * 7 + [1, 64, 8, 2, 128, 64, 0, 0.088, cap, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                          None]
+    assert lib.attn_varlen_bwd_ex(*bargs) == EINVAL
+
+
 def test_bwd_rejects(lib):
     f = lib.attn_varlen_bwd
     base = [FAKE] * 7 + [1, 64, 8, 2, 128, 64, 0, 0.088, FAKE, FAKE, FAKE, FAKE, 1 << 30, None]

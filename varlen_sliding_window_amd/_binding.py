@@ -54,6 +54,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_varlen_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                     i32, ctypes.c_float, vp, vp, vp, vp, sz, vp]
     lib.attn_varlen_bwd.restype = ctypes.c_int
+    lib.attn_varlen_fwd_ex.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                       ctypes.c_float, ctypes.c_float, vp, vp, vp, sz, vp]
+    lib.attn_varlen_fwd_ex.restype = ctypes.c_int
+    lib.attn_varlen_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                       i32, i32, ctypes.c_float, ctypes.c_float, vp, vp, vp, vp,
+                                       sz, vp]
+    lib.attn_varlen_bwd_ex.restype = ctypes.c_int
     lib.attn_varlen_strerror.argtypes = [ctypes.c_int]
     lib.attn_varlen_strerror.restype = ctypes.c_char_p
     lib.attn_varlen_version.argtypes = []
@@ -108,8 +115,11 @@ def new_workspace(total_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, m
 
 
 def fwd(q, k, v, cu_seqlens, max_seqlen: int, window: int, scale: float | None = None,
-        out=None, lse=None, workspace=None):
-    """attn_varlen_fwd: returns (out [T,Hq,D] bf16, lse [Hq,T] fp32)."""
+        out=None, lse=None, workspace=None, softcap: float = 0.0):
+    """attn_varlen_fwd (attn_varlen_fwd_ex when softcap > 0): returns
+    (out [T,Hq,D] bf16, lse [Hq,T] fp32).
+
+    softcap > 0 caps every logit to softcap * tanh(logit / softcap)."""
     _check_tensor("q", q, torch.bfloat16, 3)
     _check_tensor("k", k, torch.bfloat16, 3)
     _check_tensor("v", v, torch.bfloat16, 3)
@@ -127,18 +137,24 @@ def fwd(q, k, v, cu_seqlens, max_seqlen: int, window: int, scale: float | None =
         lse = torch.empty((hq, t), dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = new_workspace(t, nseq, hq, hkv, d, max_seqlen, window, q.device)
-    st = load_library().attn_varlen_fwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), nseq, t, hq, hkv, d, int(max_seqlen),
-        int(window), float(scale), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
-        _stream_handle(q.device))
+    lib = load_library()
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), nseq, t, hq, hkv, d, int(max_seqlen),
+            int(window), float(scale))
+    tail = (_ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream_handle(q.device))
+    if softcap:
+        st, where = lib.attn_varlen_fwd_ex(*head, float(softcap), *tail), "attn_varlen_fwd_ex"
+    else:
+        st, where = lib.attn_varlen_fwd(*head, *tail), "attn_varlen_fwd"
     if st != ATTN_OK:
-        raise AttnError(st, "attn_varlen_fwd")
+        raise AttnError(st, where)
     return out, lse
 
 
 def bwd(q, k, v, out, lse, dout, cu_seqlens, max_seqlen: int, window: int,
-        scale: float | None = None, dq=None, dk=None, dv=None, workspace=None):
-    """attn_varlen_bwd: returns (dq, dk, dv), bf16, shaped like q, k, v."""
+        scale: float | None = None, dq=None, dk=None, dv=None, workspace=None,
+        softcap: float = 0.0):
+    """attn_varlen_bwd (attn_varlen_bwd_ex when softcap > 0): returns
+    (dq, dk, dv), bf16, shaped like q, k, v.  softcap must be the forward's."""
     for name, t_ in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
         _check_tensor(name, t_, torch.bfloat16, 3)
     _check_tensor("lse", lse, torch.float32, 2)
@@ -157,12 +173,17 @@ def bwd(q, k, v, out, lse, dout, cu_seqlens, max_seqlen: int, window: int,
     dv = torch.empty_like(v) if dv is None else dv
     if workspace is None:
         workspace = new_workspace(t, nseq, hq, hkv, d, max_seqlen, window, q.device)
-    st = load_library().attn_varlen_bwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(cu_seqlens), nseq,
-        t, hq, hkv, d, int(max_seqlen), int(window), float(scale), _ptr(dq), _ptr(dk), _ptr(dv),
-        _ptr(workspace), workspace.numel(), _stream_handle(q.device))
+    lib = load_library()
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(cu_seqlens), nseq,
+            t, hq, hkv, d, int(max_seqlen), int(window), float(scale))
+    tail = (_ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+            _stream_handle(q.device))
+    if softcap:
+        st, where = lib.attn_varlen_bwd_ex(*head, float(softcap), *tail), "attn_varlen_bwd_ex"
+    else:
+        st, where = lib.attn_varlen_bwd(*head, *tail), "attn_varlen_bwd"
     if st != ATTN_OK:
-        raise AttnError(st, "attn_varlen_bwd")
+        raise AttnError(st, where)
     return dq, dk, dv
 
 

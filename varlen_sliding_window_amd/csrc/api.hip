@@ -119,22 +119,23 @@ size_t attn_varlen_workspace_size(int32_t total_tokens, int32_t num_seqs_cap,
   return attn::workspace_layout(total_tokens, num_seqs_cap, num_q_heads).total;
 }
 
-attn_status attn_varlen_fwd(const void* q, const void* k, const void* v,
-                            const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
-                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                            int32_t max_seqlen, int32_t window, float scale, void* out,
-                            float* lse, void* workspace, size_t workspace_bytes,
-                            attn_stream_t stream) {
+attn_status attn_varlen_fwd_ex(const void* q, const void* k, const void* v,
+                               const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t max_seqlen, int32_t window, float scale, float softcap,
+                               void* out, float* lse, void* workspace, size_t workspace_bytes,
+                               attn_stream_t stream) {
   WorkspaceLayout w;
   attn_status s = check_common(q, k, v, cu_seqlens, total_tokens, num_seqs, num_q_heads,
                                num_kv_heads, head_dim, max_seqlen, scale, workspace,
                                workspace_bytes, &w);
   if (s != ATTN_OK) return s;
   if (!out || !lse || !aligned(out, 16) || !aligned(lse, 4)) return ATTN_EINVAL;
+  if (!std::isfinite(softcap) || softcap < 0.f) return ATTN_EINVAL;
   s = check_device();
   if (s != ATTN_OK) return s;
   const Problem p{total_tokens, num_seqs, num_q_heads, num_kv_heads,
-                  effective_window(window, total_tokens), scale};
+                  effective_window(window, total_tokens), scale, softcap};
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (timed_launch(K_SCHEDULE, st, [&] {
         return attn::launch_schedule(cu_seqlens, p, false, workspace, w, st);
@@ -147,12 +148,24 @@ attn_status attn_varlen_fwd(const void* q, const void* k, const void* v,
   return ATTN_OK;
 }
 
-attn_status attn_varlen_bwd(const void* q, const void* k, const void* v, const void* out,
-                            const float* lse, const void* dout, const int32_t* cu_seqlens,
-                            int32_t num_seqs, int32_t total_tokens, int32_t num_q_heads,
-                            int32_t num_kv_heads, int32_t head_dim, int32_t max_seqlen,
-                            int32_t window, float scale, void* dq, void* dk, void* dv,
-                            void* workspace, size_t workspace_bytes, attn_stream_t stream) {
+attn_status attn_varlen_fwd(const void* q, const void* k, const void* v,
+                            const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t max_seqlen, int32_t window, float scale, void* out,
+                            float* lse, void* workspace, size_t workspace_bytes,
+                            attn_stream_t stream) {
+  return attn_varlen_fwd_ex(q, k, v, cu_seqlens, num_seqs, total_tokens, num_q_heads,
+                            num_kv_heads, head_dim, max_seqlen, window, scale, 0.f, out, lse,
+                            workspace, workspace_bytes, stream);
+}
+
+attn_status attn_varlen_bwd_ex(const void* q, const void* k, const void* v, const void* out,
+                               const float* lse, const void* dout, const int32_t* cu_seqlens,
+                               int32_t num_seqs, int32_t total_tokens, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t max_seqlen,
+                               int32_t window, float scale, float softcap, void* dq, void* dk,
+                               void* dv, void* workspace, size_t workspace_bytes,
+                               attn_stream_t stream) {
   WorkspaceLayout w;
   attn_status s = check_common(q, k, v, cu_seqlens, total_tokens, num_seqs, num_q_heads,
                                num_kv_heads, head_dim, max_seqlen, scale, workspace,
@@ -162,10 +175,11 @@ attn_status attn_varlen_bwd(const void* q, const void* k, const void* v, const v
   if (!aligned(out, 16) || !aligned(dout, 16) || !aligned(lse, 4) || !aligned(dq, 16) ||
       !aligned(dk, 16) || !aligned(dv, 16))
     return ATTN_EINVAL;
+  if (!std::isfinite(softcap) || softcap < 0.f) return ATTN_EINVAL;
   s = check_device();
   if (s != ATTN_OK) return s;
   const Problem p{total_tokens, num_seqs, num_q_heads, num_kv_heads,
-                  effective_window(window, total_tokens), scale};
+                  effective_window(window, total_tokens), scale, softcap};
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (timed_launch(K_SCHEDULE, st, [&] {
         return attn::launch_schedule(cu_seqlens, p, true, workspace, w, st);
@@ -182,6 +196,17 @@ attn_status attn_varlen_bwd(const void* q, const void* k, const void* v, const v
   return ATTN_OK;
 }
 
+attn_status attn_varlen_bwd(const void* q, const void* k, const void* v, const void* out,
+                            const float* lse, const void* dout, const int32_t* cu_seqlens,
+                            int32_t num_seqs, int32_t total_tokens, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t max_seqlen,
+                            int32_t window, float scale, void* dq, void* dk, void* dv,
+                            void* workspace, size_t workspace_bytes, attn_stream_t stream) {
+  return attn_varlen_bwd_ex(q, k, v, out, lse, dout, cu_seqlens, num_seqs, total_tokens,
+                            num_q_heads, num_kv_heads, head_dim, max_seqlen, window, scale, 0.f,
+                            dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
 const char* attn_varlen_strerror(attn_status s) {
   switch (s) {
     case ATTN_OK: return "success";
@@ -194,7 +219,7 @@ const char* attn_varlen_strerror(attn_status s) {
   return "unknown status";
 }
 
-int32_t attn_varlen_version(void) { return 100; }
+int32_t attn_varlen_version(void) { return 200; }
 
 attn_status attn_varlen_profile_start(void) {
   std::lock_guard<std::mutex> lock(g_prof_mu);

@@ -24,6 +24,12 @@
 //   between the S/dP products of the next.  The 4 partials are added in a
 //   fixed order through LDS at the end, so the head-group reduction needs no
 //   atomics and is bit-for-bit reproducible.
+//
+// Logit soft-cap (the CAP instantiations): with t = tanh(scale qk / c) the
+// softmax sees c t, so P = exp2(c log2(e) t - lse log2(e)), and dS picks up
+// the cap's derivative, dS = P (dP - D)(1 - t^2), before the products that
+// carry it to dQ and dK.  The tanh cannot take the lse seed inside, so the
+// dK/dV kernel then starts S at zero and keeps -lse log2(e) per row beside it.
 #include "device.h"
 #include "launch.h"
 
@@ -36,12 +42,13 @@ constexpr int DQ_TILE_BYTES = KBLK * HEAD_DIM * (int)sizeof(bf16);   // 16 KB
 constexpr int DQ_BUF_BYTES = 2 * DQ_TILE_BYTES;                     // K and V
 static_assert(KBLK == 16 * 4, "each wave loads 16 rows of a block");
 
+template <bool CAP>
 __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ out, const bf16* __restrict__ dout, const float* __restrict__ lse,
     const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
-    int window, float scale_log2, float scale, int tile_cap, bf16* __restrict__ dq,
-    TileStats* __restrict__ stats) {
+    int window, float scale_log2, float scale, float cap_a, float cap_c2, int tile_cap,
+    bf16* __restrict__ dq, TileStats* __restrict__ stats) {
   __shared__ __attribute__((aligned(16))) char smem[2 * DQ_BUF_BYTES];
 
   const int chunks = Hq >> 2;
@@ -113,7 +120,7 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(
     // Rows past the tile get seeds that make them vanish (P = 0, dP - D = 0),
     // so every value the dK/dV kernel reads is finite.
     TileStats* ts = stats + (size_t)head * tile_cap + tl.idx;
-    ts->s0[lq] = qrow < q1 ? -lsev / scale : -INFINITY;
+    ts->s0[lq] = qrow < q1 ? (CAP ? -lse2 : -lsev / scale) : -INFINITY;
     ts->dp0[lq] = qrow < q1 ? -Dv : 0.f;
   }
 
@@ -153,8 +160,14 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(
     float dsv[32];
 #pragma unroll
     for (int x = 0; x < 32; ++x) {
-      const float p = exp2_fast(s[x >> 4][x & 15] * scale_log2 - lse2);
-      dsv[x] = p * (dp[x >> 4][x & 15] - Dv);
+      if constexpr (CAP) {
+        const float t = tanh_fast(cap_a * s[x >> 4][x & 15]);
+        const float p = exp2_fast(cap_c2 * t - lse2);
+        dsv[x] = p * (dp[x >> 4][x & 15] - Dv) * (1.f - t * t);
+      } else {
+        const float p = exp2_fast(s[x >> 4][x & 15] * scale_log2 - lse2);
+        dsv[x] = p * (dp[x >> 4][x & 15] - Dv);
+      }
     }
     if (!full) {
 #pragma unroll
@@ -198,12 +211,13 @@ constexpr size_t DKDV_LDS_BYTES = (size_t)DKDV_WAVES * 2 * DKDV_BUF_BYTES;
 static_assert((size_t)DKDV_WAVES * TILE * RED_PITCH * sizeof(float) <= DKDV_LDS_BYTES,
               "reduction buffer must fit in the staging buffers");
 
+template <bool CAP>
 __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const TileStats* __restrict__ stats, int tile_cap,
     const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
-    int window, float scale_log2, float scale, int run_len, bf16* __restrict__ dk,
-    bf16* __restrict__ dv) {
+    int window, float scale_log2, float scale, float cap_a, float cap_c2, int run_len,
+    bf16* __restrict__ dk, bf16* __restrict__ dv) {
   __shared__ __attribute__((aligned(16))) char smem[DKDV_LDS_BYTES];
 
   // Work-groups go to the 8 XCDs round-robin (work-group b to XCD b % 8).
@@ -335,17 +349,23 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
   // S = Q K^T and dP = dO V^T of the step held in buffer `buf` (two
   // independent chains), seeded with -lse/scale and -D: s[r] = S - lse/scale
   // and dp[r] = dP - D of query qb + 8(r/4) + 4 lh + r%4 and key k0 + lq.
+  // With a cap, S starts at zero and ls[r] = -lse log2(e) of the same query.
   // Also reads the step's transposed dO and Q fragments (B operands of dV
   // and dK), so that the buffer is done with once this returns.
-  auto s_dp = [&](int buf, f32x16& s, f32x16& dp, bf16x8* dof, bf16x8* qtf) {
+  auto s_dp = [&](int buf, f32x16& s, f32x16& dp, bf16x8* dof, bf16x8* qtf, f32x16& ls) {
     const float* st = st_tile(buf);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float4 a4 = *reinterpret_cast<const float4*>(st + 8 * j + 4 * lh);
       const float4 b4 = *reinterpret_cast<const float4*>(st + TILE + 8 * j + 4 * lh);
-      s[4 * j + 0] = a4.x; s[4 * j + 1] = a4.y; s[4 * j + 2] = a4.z; s[4 * j + 3] = a4.w;
+      if constexpr (CAP) {
+        ls[4 * j + 0] = a4.x; ls[4 * j + 1] = a4.y; ls[4 * j + 2] = a4.z; ls[4 * j + 3] = a4.w;
+      } else {
+        s[4 * j + 0] = a4.x; s[4 * j + 1] = a4.y; s[4 * j + 2] = a4.z; s[4 * j + 3] = a4.w;
+      }
       dp[4 * j + 0] = b4.x; dp[4 * j + 1] = b4.y; dp[4 * j + 2] = b4.z; dp[4 * j + 3] = b4.w;
     }
+    if constexpr (CAP) s = zero_f32x16();
     const bf16* Qs = q_tile(buf);
     const bf16* Ds = do_tile(buf);
     bf16x8 qa[8], da[8];
@@ -367,15 +387,24 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
   };
   // Half t of P and dS (queries 16t .. 16t + 15 of the step at qb) as bf16
   // A fragments (rows = keys, k = queries); invisible elements become 0.
-  auto p_ds = [&](const f32x16& s, const f32x16& dp, int qb, int t, bf16x8& pf, bf16x8& dsf) {
+  auto p_ds = [&](const f32x16& s, const f32x16& dp, const f32x16& ls, int qb, int t,
+                  bf16x8& pf, bf16x8& dsf) {
     const int x = qb + mbias;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int r = 8 * t + e;
-      float p = exp2_fast(s[r] * scale_log2);
-      p = (uint32_t)(x + 8 * (r >> 2) + (r & 3)) <= mspan ? p : 0.f;
-      pf[e] = (bf16)p;
-      dsf[e] = (bf16)(p * dp[r]);
+      if constexpr (CAP) {
+        const float th = tanh_fast(cap_a * s[r]);
+        float p = exp2_fast(cap_c2 * th + ls[r]);
+        p = (uint32_t)(x + 8 * (r >> 2) + (r & 3)) <= mspan ? p : 0.f;
+        pf[e] = (bf16)p;
+        dsf[e] = (bf16)(p * dp[r] * (1.f - th * th));
+      } else {
+        float p = exp2_fast(s[r] * scale_log2);
+        p = (uint32_t)(x + 8 * (r >> 2) + (r & 3)) <= mspan ? p : 0.f;
+        pf[e] = (bf16)p;
+        dsf[e] = (bf16)(p * dp[r]);
+      }
     }
   };
   // Half t of dV[key][d] += P^T dO and dK[key][d] += dS^T Q (scale applied
@@ -398,13 +427,14 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
   // there, with a whole iteration to land.  On the last iteration the S/dP
   // products of the step after are computed from stale data and discarded.
   auto body = [&](int it, int qb, f32x16& s_c, f32x16& dp_c, bf16x8* dof_c, bf16x8* qtf_c,
-                  f32x16& s_n, f32x16& dp_n, bf16x8* dof_n, bf16x8* qtf_n) {
+                  f32x16& ls_c, f32x16& s_n, f32x16& dp_n, bf16x8* dof_n, bf16x8* qtf_n,
+                  f32x16& ls_n) {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     if (it + 2 < steps) issue_next(it & 1);
-    s_dp((it + 1) & 1, s_n, dp_n, dof_n, qtf_n);
+    s_dp((it + 1) & 1, s_n, dp_n, dof_n, qtf_n, ls_n);
     bf16x8 pf0, ds0, pf1, ds1;
-    p_ds(s_c, dp_c, qb, 0, pf0, ds0);
-    p_ds(s_c, dp_c, qb, 1, pf1, ds1);
+    p_ds(s_c, dp_c, ls_c, qb, 0, pf0, ds0);
+    p_ds(s_c, dp_c, ls_c, qb, 1, pf1, ds1);
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);    // 8 LDS reads
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
@@ -418,23 +448,23 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  f32x16 sA, dpA, sB, dpB;
+  f32x16 sA, dpA, sB, dpB, lsA, lsB;   // lsA, lsB: only with a cap
   bf16x8 dofA[8], qtfA[8], dofB[8], qtfB[8];
   if (steps > 0) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (steps > 1) issue_next(1);
-    s_dp(0, sA, dpA, dofA, qtfA);
+    s_dp(0, sA, dpA, dofA, qtfA, lsA);
   }
   int qb = k0;
   auto next_qb = [&](int x) { return x + QBLK < k0 + nqb * QBLK ? x + QBLK : k0; };
   int it = 0;
   for (; it + 1 < steps; it += 2) {
-    body(it, qb, sA, dpA, dofA, qtfA, sB, dpB, dofB, qtfB);
+    body(it, qb, sA, dpA, dofA, qtfA, lsA, sB, dpB, dofB, qtfB, lsB);
     qb = next_qb(qb);
-    body(it + 1, qb, sB, dpB, dofB, qtfB, sA, dpA, dofA, qtfA);
+    body(it + 1, qb, sB, dpB, dofB, qtfB, lsB, sA, dpA, dofA, qtfA, lsA);
     qb = next_qb(qb);
   }
-  if (it < steps) body(it, qb, sA, dpA, dofA, qtfA, sB, dpB, dofB, qtfB);
+  if (it < steps) body(it, qb, sA, dpA, dofA, qtfA, lsA, sB, dpB, dofB, qtfB, lsB);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 
   // Head-group reduction in a fixed order (wave 0 + 1 + 2 + 3), then store.
@@ -479,13 +509,15 @@ hipError_t launch_dq(const void* q, const void* k, const void* v, const void* ou
                      void* workspace, const WorkspaceLayout& w, hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
   const unsigned grid = (unsigned)(w.tile_cap * (size_t)(p.num_q_heads / 4));
-  hipLaunchKernelGGL(dq_kernel, dim3(grid), dim3(BWD_THREADS), 0, stream,
-                     static_cast<const bf16*>(q), static_cast<const bf16*>(k),
-                     static_cast<const bf16*>(v), static_cast<const bf16*>(out),
-                     static_cast<const bf16*>(dout), lse, reinterpret_cast<const int*>(ws + w.header),
+  const CapConstants cc = cap_constants(p);
+  hipLaunchKernelGGL(p.softcap > 0.f ? dq_kernel<true> : dq_kernel<false>, dim3(grid),
+                     dim3(BWD_THREADS), 0, stream, static_cast<const bf16*>(q),
+                     static_cast<const bf16*>(k), static_cast<const bf16*>(v),
+                     static_cast<const bf16*>(out), static_cast<const bf16*>(dout), lse,
+                     reinterpret_cast<const int*>(ws + w.header),
                      reinterpret_cast<const Tile*>(ws + w.tiles_fwd), p.total_tokens,
                      p.num_q_heads, p.num_kv_heads, p.window, p.scale * LOG2E, p.scale,
-                     (int)w.tile_cap, static_cast<bf16*>(dq),
+                     cc.cap_a, cc.cap_c2, (int)w.tile_cap, static_cast<bf16*>(dq),
                      reinterpret_cast<TileStats*>(ws + w.rowstats));
   return hipGetLastError();
 }
@@ -503,14 +535,17 @@ hipError_t launch_dkdv(const void* q, const void* k, const void* v, const float*
   const size_t items = (size_t)p.num_kv_heads * (w.tile_cap + run_len - 1);
   const size_t round = 8 * (size_t)run_len;
   const unsigned grid = (unsigned)((items + round - 1) / round * round);
-  hipLaunchKernelGGL(dkdv_kernel, dim3(grid), dim3(BWD_THREADS), 0, stream,
-                     static_cast<const bf16*>(q), static_cast<const bf16*>(k),
-                     static_cast<const bf16*>(v), static_cast<const bf16*>(dout),
+  const CapConstants cc = cap_constants(p);
+  hipLaunchKernelGGL(p.softcap > 0.f ? dkdv_kernel<true> : dkdv_kernel<false>, dim3(grid),
+                     dim3(BWD_THREADS), 0, stream, static_cast<const bf16*>(q),
+                     static_cast<const bf16*>(k), static_cast<const bf16*>(v),
+                     static_cast<const bf16*>(dout),
                      reinterpret_cast<const TileStats*>(ws + w.rowstats), (int)w.tile_cap,
                      reinterpret_cast<const int*>(ws + w.header),
                      reinterpret_cast<const Tile*>(ws + w.tiles_bwd), p.total_tokens,
-                     p.num_q_heads, p.num_kv_heads, p.window, p.scale * LOG2E, p.scale, run_len,
-                     static_cast<bf16*>(dk), static_cast<bf16*>(dv));
+                     p.num_q_heads, p.num_kv_heads, p.window, p.scale * LOG2E, p.scale,
+                     cc.cap_a, cc.cap_c2, run_len, static_cast<bf16*>(dk),
+                     static_cast<bf16*>(dv));
   return hipGetLastError();
 }
 

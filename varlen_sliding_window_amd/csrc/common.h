@@ -44,7 +44,8 @@ struct __attribute__((aligned(16))) Tile {
 // stored per (query head, q-tile): the starting values of the S and dP
 // accumulators of each row, -lse / scale and -D with D = rowsum(dout * out).
 // Seeded with them, the dK/dV kernel's products give P = exp2(scale log2(e)
-// acc_S) and dP - D = acc_dP directly.  256 bytes per tile.
+// acc_S) and dP - D = acc_dP directly.  With a logit soft-cap, s0 holds
+// -lse log2(e) instead (added after the cap).  256 bytes per tile.
 struct TileStats {
   float s0[TILE];
   float dp0[TILE];

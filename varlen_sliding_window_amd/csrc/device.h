@@ -147,6 +147,26 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
+// tanh in fp32 with a relative error of about 2e-7 everywhere.
+//   |x| >= 0.55: 1 - 2 / (exp(2x) + 1) from the hardware exp2 and reciprocal;
+//     a large x makes the exponential +inf and the quotient 0 (tanh = 1), a
+//     very negative one makes it 0 (tanh = -1).
+//   |x| <  0.55: x + x^3 g(x^2), where the quartic g was fitted by weighted
+//     least squares to (tanh(x) - x) / x^3 on that interval; the exponential
+//     form would lose all relative accuracy as x -> 0 (a cap far above the
+//     logits then still reproduces them).
+__device__ __forceinline__ float tanh_fast(float x) {
+  const float wide = 1.f - 2.f * __builtin_amdgcn_rcpf(exp2_fast(x * (2.f * LOG2E)) + 1.f);
+  const float y = x * x;
+  float g = -0.00636491494f;
+  g = fmaf(g, y, 0.0211331641f);
+  g = fmaf(g, y, -0.0538665094f);
+  g = fmaf(g, y, 0.133327132f);
+  g = fmaf(g, y, -0.33333321f);
+  const float narrow = fmaf(x * y, g, x);
+  return fabsf(x) < 0.55f ? narrow : wide;
+}
+
 __device__ __forceinline__ void store_bf16x4(bf16* p, float a, float b, float c, float d) {
   bf16x4 v;
   v[0] = (bf16)a;

@@ -22,6 +22,10 @@
 // blocks are aligned to the tile end and walked from the diagonal backwards,
 // so the first block sets a good maximum and only the diagonal block and the
 // blocks at the segment start or window edge need the mask.
+//
+// With a logit soft-cap (the CAP instantiation) each score becomes
+// softcap * tanh(scale * qk / softcap) right after its product, already in
+// log2 units, and the rest of the kernel runs unchanged with a unit scale.
 #include "device.h"
 #include "launch.h"
 
@@ -35,10 +39,12 @@ constexpr int FWD_BUF_BYTES = 2 * FWD_TILE_BYTES;                     // K and V
 constexpr float RESCALE_LOG2 = 8.f;
 static_assert(KBLK == 16 * FWD_WAVES, "each wave loads 16 rows of a block");
 
+template <bool CAP>
 __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
-    int window, float scale_log2, bf16* __restrict__ out, float* __restrict__ lse) {
+    int window, float scale_log2, float cap_a, float cap_c2, bf16* __restrict__ out,
+    float* __restrict__ lse) {
   __shared__ __attribute__((aligned(16))) char smem[2 * FWD_BUF_BYTES];
 
   const int chunks = Hq >> 2;
@@ -125,6 +131,12 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(
       s[0] = mfma32(kfr[ks], qf[ks], s[0]);
       s[1] = mfma32(kfr[8 + ks], qf[ks], s[1]);
     }
+    if constexpr (CAP) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[h2][r] = cap_c2 * tanh_fast(cap_a * s[h2][r]);
+    }
     const bool full = (kb + KBLK - 1 <= q0) && (kb >= full_lo);
     if (!full) {
 #pragma unroll
@@ -196,12 +208,15 @@ hipError_t launch_forward(const void* q, const void* k, const void* v, const Pro
                           hipStream_t stream) {
   const char* ws = static_cast<const char*>(workspace);
   const unsigned grid = (unsigned)(w.tile_cap * (size_t)(p.num_q_heads / 4));
-  hipLaunchKernelGGL(fwd_kernel, dim3(grid), dim3(FWD_THREADS), 0, stream,
-                     static_cast<const bf16*>(q), static_cast<const bf16*>(k),
+  const CapConstants cc = cap_constants(p);
+  const bool cap = p.softcap > 0.f;
+  // capped scores arrive in log2 units already: unit scale
+  hipLaunchKernelGGL(cap ? fwd_kernel<true> : fwd_kernel<false>, dim3(grid), dim3(FWD_THREADS),
+                     0, stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                      static_cast<const bf16*>(v), reinterpret_cast<const int*>(ws + w.header),
                      reinterpret_cast<const Tile*>(ws + w.tiles_fwd), p.total_tokens,
-                     p.num_q_heads, p.num_kv_heads, p.window, p.scale * LOG2E,
-                     static_cast<bf16*>(out), lse);
+                     p.num_q_heads, p.num_kv_heads, p.window, cap ? 1.f : p.scale * LOG2E,
+                     cc.cap_a, cc.cap_c2, static_cast<bf16*>(out), lse);
   return hipGetLastError();
 }
 

@@ -8,7 +8,18 @@ namespace attn {
 struct Problem {
   int total_tokens, num_seqs, num_q_heads, num_kv_heads, window;
   float scale;
+  float softcap;   // > 0: logits become softcap * tanh(logit / softcap); 0: no cap
 };
+
+// Constants of the capped logit in the exp2 domain:
+//   log2(e) * softcap * tanh(scale * qk / softcap) = cap_c2 * tanh(cap_a * qk).
+struct CapConstants {
+  float cap_a, cap_c2;
+};
+inline CapConstants cap_constants(const Problem& p) {
+  return p.softcap > 0.f ? CapConstants{p.scale / p.softcap, p.softcap * LOG2E}
+                         : CapConstants{0.f, 0.f};
+}
 
 // Builds the sorted tile lists in the workspace from cu_seqlens: the
 // forward-order list always, the backward-order list only when need_bwd.
