@@ -46,7 +46,8 @@ def test_workspace_size(lib):
     # at least D (fp32 [Hq, T]) plus both tile lists
     assert n >= 8 * 16384 * 4 + 2 * 16 * (16384 // 32 + 64)
     assert n % 256 == 0
-    assert attn.workspace_size(16384, 64, 8, 2, 64, 4096, 512) == 0     # head dim 64
+    assert attn.workspace_size(16384, 64, 8, 2, 64, 4096, 512) == n     # head dim 64
+    assert attn.workspace_size(16384, 64, 8, 2, 96, 4096, 512) == 0     # head dim 96
     assert attn.workspace_size(0, 1, 8, 2, 128, 1, 0) == 0               # T = 0
     assert attn.workspace_size(100, 1, 8, 3, 128, 100, 0) == 0           # Hq % Hkv
     assert attn.workspace_size(100, 1, 8, 2, 128, 101, 0) == 0           # max_seqlen > T
@@ -71,7 +72,8 @@ def call_fwd(lib, **over):
     ({"nseq": 0}, EINVAL), ({"hkv": 3}, EINVAL), ({"hq": 0}, EINVAL), ({"ms": 0}, EINVAL),
     ({"ms": 65}, EINVAL), ({"scale": 0.0}, EINVAL), ({"scale": -1.0}, EINVAL),
     ({"scale": float("nan")}, EINVAL), ({"scale": float("inf")}, EINVAL),
-    ({"d": 64}, EUNSUPPORTED), ({"d": 256}, EUNSUPPORTED), ({"hq": 2, "hkv": 1}, EUNSUPPORTED),
+    ({"d": 96}, EUNSUPPORTED), ({"d": 32}, EUNSUPPORTED), ({"d": 512}, EUNSUPPORTED),
+    ({"d": 0}, EUNSUPPORTED), ({"hq": 2, "hkv": 1}, EUNSUPPORTED),
     ({"hq": 8, "hkv": 8}, EUNSUPPORTED), ({"ws": None}, EWORKSPACE), ({"wsb": 16}, EWORKSPACE),
     ({"ws": FAKE + 16}, EWORKSPACE),
 ])
@@ -92,7 +94,7 @@ def test_bwd_rejects(lib):
     f = lib.attn_varlen_bwd
     base = [FAKE] * 7 + [1, 64, 8, 2, 128, 64, 0, 0.088, FAKE, FAKE, FAKE, FAKE, 1 << 30, None]
     for pos, val, code in ((4, None, EINVAL), (5, None, EINVAL), (15, None, EINVAL),
-                           (17, None, EINVAL), (11, 64, EUNSUPPORTED), (12, 65, EINVAL), (19, 8, EWORKSPACE),
+                           (17, None, EINVAL), (11, 96, EUNSUPPORTED), (12, 65, EINVAL), (19, 8, EWORKSPACE),
                            (14, 0.0, EINVAL)):
         a = list(base)
         a[pos] = val

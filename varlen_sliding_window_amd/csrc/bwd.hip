@@ -38,18 +38,16 @@ namespace {
 
 constexpr int BWD_THREADS = 256;
 
-constexpr int DQ_TILE_BYTES = KBLK * HEAD_DIM * (int)sizeof(bf16);   // 16 KB
-constexpr int DQ_BUF_BYTES = 2 * DQ_TILE_BYTES;                     // K and V
-static_assert(KBLK == 16 * 4, "each wave loads 16 rows of a block");
-
-template <bool CAP>
-__global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(
+template <int D, bool CAP>
+__global__ __launch_bounds__(BWD_THREADS, BlockGeom<D>::MIN_WG) void dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ out, const bf16* __restrict__ dout, const float* __restrict__ lse,
     const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
     int window, float scale_log2, float scale, float cap_a, float cap_c2, int tile_cap,
     bf16* __restrict__ dq, TileStats* __restrict__ stats) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * DQ_BUF_BYTES];
+  using Geo = BlockGeom<D>;
+  constexpr int KB = Geo::KB, H2 = Geo::H2, KS = Geo::KS, DB = Geo::DB;
+  __shared__ __attribute__((aligned(16))) char smem[2 * Geo::BUF_BYTES];
 
   const int chunks = Hq >> 2;
   const int item = blockIdx.x / chunks;
@@ -64,39 +62,44 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(
   const int g = (hc * 4) / (Hq / Hkv);
   const int q0 = tl.t0, q1 = tl.t1, a = tl.seg_a;
   const int klo = first_visible_key(q0, a, window);
-  const int nblk = (q1 - klo + KBLK - 1) / KBLK;
+  const int nblk = (q1 - klo + KB - 1) / KB;
   const int qrow = q0 + lq;
-  const size_t qstride = (size_t)Hq * HEAD_DIM;
-  const uint32_t kstride_b = (uint32_t)(Hkv * HEAD_DIM * sizeof(bf16));
+  const size_t qstride = (size_t)Hq * D;
+  const uint32_t kstride_b = (uint32_t)(Hkv * D * sizeof(bf16));
 
-  // Block loads, as in the forward: wave w fills rows 16w .. 16w + 15 of the
-  // swizzled K and V tiles; keys before 0 re-read key 0 (always masked).
-  const bf16* kbase = k + (size_t)g * HEAD_DIM;
-  const bf16* vbase = v + (size_t)g * HEAD_DIM;
-  const uint32_t lds0 = lds_address(smem) + (uint32_t)(wave * 16 * HEAD_DIM * sizeof(bf16));
-  uint32_t coff[4];
+  // Block loads, as in the forward: wave w fills rows ROWS_PER_WAVE * w + [0,
+  // ROWS_PER_WAVE) of the swizzled K and V tiles; keys before 0 re-read key 0
+  // (always masked).
+  const bf16* kbase = k + (size_t)g * D;
+  const bf16* vbase = v + (size_t)g * D;
+  const uint32_t lds0 = lds_address(smem) + (uint32_t)(wave * Geo::ROWS_PER_WAVE * D * sizeof(bf16));
+  uint32_t coff[Geo::LOADS];
+  int lrow[Geo::LOADS];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) coff[j] = (uint32_t)(((lane & 15) ^ swz(4 * j + (lane >> 4))) << 4);
+  for (int j = 0; j < Geo::LOADS; ++j) {
+    lrow[j] = Geo::ROWS_PER_WAVE * wave + TileLoad<D>::RPD * j + lane / TileLoad<D>::CPR;
+    coff[j] = TileLoad<D>::chunk_offset(lane, lrow[j]);
+  }
   auto issue = [&](int n, int buf) {
-    const int kb = q1 - KBLK * (n + 1);
-    const uint32_t l = lds0 + (uint32_t)(buf * DQ_BUF_BYTES);
+    const int kb = q1 - KB * (n + 1);
+    const uint32_t l = lds0 + (uint32_t)(buf * Geo::BUF_BYTES);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = max(kb + 16 * wave + 4 * j + (lane >> 4), 0);
+    for (int j = 0; j < Geo::LOADS; ++j) {
+      const int key = max(kb + lrow[j], 0);
       const uint32_t off = (uint32_t)key * kstride_b + coff[j];
       dma16(kbase, off, l + j * 1024);
-      dma16(vbase, off, l + DQ_TILE_BYTES + j * 1024);
+      dma16(vbase, off, l + Geo::TILE_BYTES + j * 1024);
     }
   };
   issue(0, 0);
 
   // Q^T and dO^T as B operands; D from dO and O at the same positions
-  bf16x8 qf[8], df[8];
+  bf16x8 qf[KS], df[KS];
   float dpart = 0.f;
   {
-    const size_t off = (size_t)qrow * qstride + (size_t)head * HEAD_DIM + lh * 8;
+    const size_t off = (size_t)qrow * qstride + (size_t)head * D + lh * 8;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       if (qrow < T) {
         qf[ks] = as_bf16x8(ldg16(q + off + ks * 16));
         df[ks] = as_bf16x8(ldg16(dout + off + ks * 16));
@@ -111,7 +114,7 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(
     // Make the compiler wait for these loads here, not inside the loop where
     // the wait would also cover the block loads in flight.
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qf[ks]), "v"(df[ks]));
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]), "v"(df[ks]));
   }
   const float Dv = dpart + __shfl_xor(dpart, 32);
   const float lsev = qrow < T ? lse[(size_t)head * T + qrow] : 0.f;
@@ -124,14 +127,14 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(
     ts->dp0[lq] = qrow < q1 ? -Dv : 0.f;
   }
 
-  f32x16 acc[4];
+  f32x16 acc[DB];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) acc[db] = zero_f32x16();
+  for (int db = 0; db < DB; ++db) acc[db] = zero_f32x16();
   const int full_lo = first_visible_key(q0 + TILE - 1, a, window);
   const int my_lo = first_visible_key(qrow, a, window);
 
   for (int n = 0; n < nblk; ++n) {
-    const int kb = q1 - KBLK * (n + 1);
+    const int kb = q1 - KB * (n + 1);
     const int buf = n & 1;
     // This wave's loads of block n have landed; after the barrier so have
     // everyone's, and every wave is done with block n - 1, whose buffer the
@@ -139,27 +142,27 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (n + 1 < nblk) issue(n + 1, buf ^ 1);
-    const bf16* Ks = reinterpret_cast<const bf16*>(smem + buf * DQ_BUF_BYTES);
-    const bf16* Vs = Ks + KBLK * HEAD_DIM;
+    const bf16* Ks = reinterpret_cast<const bf16*>(smem + buf * Geo::BUF_BYTES);
+    const bf16* Vs = Ks + KB * D;
 
-    f32x16 s[2], dp[2];
+    f32x16 s[H2], dp[H2];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
+    for (int h2 = 0; h2 < H2; ++h2) {
       s[h2] = zero_f32x16();
       dp[h2] = zero_f32x16();
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        s[h2] = mfma32(swz_frag_cols(Ks + h2 * 32 * HEAD_DIM, ks, lane), qf[ks], s[h2]);
-        dp[h2] = mfma32(swz_frag_cols(Vs + h2 * 32 * HEAD_DIM, ks, lane), df[ks], dp[h2]);
+      for (int ks = 0; ks < KS; ++ks) {
+        s[h2] = mfma32(swz_frag_cols<D>(Ks + h2 * 32 * D, ks, lane), qf[ks], s[h2]);
+        dp[h2] = mfma32(swz_frag_cols<D>(Vs + h2 * 32 * D, ks, lane), df[ks], dp[h2]);
       }
     }
     // dS^T = P^T (dP^T - D), computed for every element; blocks that cross
     // the diagonal, the window edge or the segment start then zero the
     // invisible elements with selects (so values there, even NaNs, drop out).
-    const bool full = (kb + KBLK - 1 <= q0) && (kb >= full_lo);
-    float dsv[32];
+    const bool full = (kb + KB - 1 <= q0) && (kb >= full_lo);
+    float dsv[H2 * 16];
 #pragma unroll
-    for (int x = 0; x < 32; ++x) {
+    for (int x = 0; x < H2 * 16; ++x) {
       if constexpr (CAP) {
         const float t = tanh_fast(cap_a * s[x >> 4][x & 15]);
         const float p = exp2_fast(cap_c2 * t - lse2);
@@ -171,28 +174,28 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(
     }
     if (!full) {
 #pragma unroll
-      for (int x = 0; x < 32; ++x) {
+      for (int x = 0; x < H2 * 16; ++x) {
         const int r = x & 15;
         const int key = kb + (x >> 4) * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
         dsv[x] = ((key >= my_lo) & (key <= qrow)) ? dsv[x] : 0.f;
       }
     }
-    bf16x8 dsf[4];
+    bf16x8 dsf[2 * H2];
 #pragma unroll
-    for (int x = 0; x < 32; ++x) dsf[x >> 3][x & 7] = (bf16)dsv[x];
+    for (int x = 0; x < H2 * 16; ++x) dsf[x >> 3][x & 7] = (bf16)dsv[x];
     // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q]
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 2 * H2; ++t)
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-        acc[db] = mfma32(swz_frag_rows(Ks, db * 32, t, lane), dsf[t], acc[db]);
+      for (int db = 0; db < DB; ++db)
+        acc[db] = mfma32(swz_frag_rows<D>(Ks, db * 32, t, lane), dsf[t], acc[db]);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   if (qrow < q1) {
-    bf16* op = dq + (size_t)qrow * qstride + (size_t)head * HEAD_DIM + lh * 4;
+    bf16* op = dq + (size_t)qrow * qstride + (size_t)head * D + lh * 4;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         store_bf16x4(op + db * 32 + j * 8, acc[db][4 * j] * scale, acc[db][4 * j + 1] * scale,
@@ -201,24 +204,35 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(
 }
 
 constexpr int DKDV_WAVES = 4;
-constexpr int RED_PITCH = HEAD_DIM + 4;   // fp32 pitch of the reduction buffer
-// Per wave and buffer: Q tile, dO tile (32 x 128 bf16 each, swizzled), then
-// the q-tile's TileStats.
 static_assert(QBLK == TILE, "a dK/dV q-block is exactly one q-tile");
-constexpr int DKDV_TILE_BYTES = QBLK * HEAD_DIM * (int)sizeof(bf16);
-constexpr int DKDV_BUF_BYTES = 2 * DKDV_TILE_BYTES + (int)sizeof(TileStats);
-constexpr size_t DKDV_LDS_BYTES = (size_t)DKDV_WAVES * 2 * DKDV_BUF_BYTES;
-static_assert((size_t)DKDV_WAVES * TILE * RED_PITCH * sizeof(float) <= DKDV_LDS_BYTES,
-              "reduction buffer must fit in the staging buffers");
 
-template <bool CAP>
+// Per-head-dim geometry of the dK/dV kernel.  Per wave and buffer: Q tile,
+// dO tile (32 x D bf16 each, swizzled), then the q-tile's TileStats.
+template <int D>
+struct DkdvGeom {
+  static constexpr int KS = D / 16;                     // k-steps of a D-long product
+  static constexpr int DB = D / 32;                     // 32-column blocks of D
+  static constexpr int RED_PITCH = D + 4;               // fp32 pitch of the reduction buffer
+  static constexpr int TILE_BYTES = QBLK * D * (int)sizeof(bf16);
+  static constexpr int BUF_BYTES = 2 * TILE_BYTES + (int)sizeof(TileStats);
+  static constexpr size_t LDS_BYTES = (size_t)DKDV_WAVES * 2 * BUF_BYTES;
+  static constexpr int LOADS = QBLK / TileLoad<D>::RPD;   // 1 KB loads per tile
+  static_assert(LDS_BYTES <= 160 * 1024, "staging buffers must fit in LDS");
+  static_assert((size_t)DKDV_WAVES * TILE * RED_PITCH * sizeof(float) <= LDS_BYTES,
+                "reduction buffer must fit in the staging buffers");
+};
+
+template <int D, bool CAP>
 __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const TileStats* __restrict__ stats, int tile_cap,
     const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
     int window, float scale_log2, float scale, float cap_a, float cap_c2, int run_len,
     bf16* __restrict__ dk, bf16* __restrict__ dv) {
-  __shared__ __attribute__((aligned(16))) char smem[DKDV_LDS_BYTES];
+  using Geo = DkdvGeom<D>;
+  constexpr int KS = Geo::KS, DB = Geo::DB, RED_PITCH = Geo::RED_PITCH;
+  constexpr int DKDV_TILE_BYTES = Geo::TILE_BYTES, DKDV_BUF_BYTES = Geo::BUF_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[Geo::LDS_BYTES];
 
   // Work-groups go to the 8 XCDs round-robin (work-group b to XCD b % 8).
   // XCD x takes runs of R consecutive entries of the sorted list with one
@@ -244,8 +258,8 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
   const int qhi = window > 0 ? min(b, k1 - 1 + window) : b;
   const int nqb = (qhi - k0 + QBLK - 1) / QBLK;
   const int steps = (G / DKDV_WAVES) * nqb;   // (head, q-block) pairs of this wave
-  const size_t qstride = (size_t)Hq * HEAD_DIM;
-  const size_t kstride = (size_t)Hkv * HEAD_DIM;
+  const size_t qstride = (size_t)Hq * D;
+  const size_t kstride = (size_t)Hkv * D;
 
   char* wbase = smem + (size_t)wave * 2 * DKDV_BUF_BYTES;
   auto q_tile = [&](int buf) {
@@ -259,15 +273,15 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
   };
   const uint32_t lds_wave = lds_address(wbase);
 
-  // Lane part of the tile loads: load j (1 KB) fills rows 4j + lane / 16 of
-  // the swizzled tile; the lane fetches the 16-byte chunk that lands at
-  // physical chunk lane % 16 of its row.
+  // Lane part of the tile loads: load j (1 KB) fills rows RPD j + lane / CPR
+  // of the swizzled tile; the lane fetches the 16-byte chunk that lands at
+  // physical chunk lane % CPR of its row.
   const uint32_t rstride = (uint32_t)(qstride * sizeof(bf16));
-  uint32_t dma_off[8];
+  uint32_t dma_off[Geo::LOADS];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 4 * j + (lane >> 4);
-    dma_off[j] = (uint32_t)r * rstride + (uint32_t)(((lane & 15) ^ swz(r)) << 4);
+  for (int j = 0; j < Geo::LOADS; ++j) {
+    const int r = TileLoad<D>::RPD * j + lane / TileLoad<D>::CPR;
+    dma_off[j] = (uint32_t)r * rstride + TileLoad<D>::chunk_offset(lane, r);
   }
 
   // Loads of one step into buffer `buf`: Q and dO rows of q-block i (the
@@ -277,23 +291,22 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
   // so even NaNs there cannot leak.
   auto issue = [&](int head, int i, int buf) {
     const int qb = k0 + i * QBLK;
-    const size_t hoff = (size_t)qb * qstride + (size_t)head * HEAD_DIM;
+    const size_t hoff = (size_t)qb * qstride + (size_t)head * D;
     const bf16* qsrc = q + hoff;
     const bf16* dsrc = dout + hoff;
     const uint32_t l = lds_wave + (uint32_t)(buf * DKDV_BUF_BYTES);
     const int rmax = T - 1 - qb;
     if (rmax >= QBLK - 1) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < Geo::LOADS; ++j) {
         dma16(qsrc, dma_off[j], l + j * 1024);
         dma16(dsrc, dma_off[j], l + DKDV_TILE_BYTES + j * 1024);
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int r = 4 * j + (lane >> 4);
-        const uint32_t off = (uint32_t)min(r, rmax) * rstride +
-                             (uint32_t)(((lane & 15) ^ swz(r)) << 4);
+      for (int j = 0; j < Geo::LOADS; ++j) {
+        const int r = TileLoad<D>::RPD * j + lane / TileLoad<D>::CPR;
+        const uint32_t off = (uint32_t)min(r, rmax) * rstride + TileLoad<D>::chunk_offset(lane, r);
         dma16(qsrc, off, l + j * 1024);
         dma16(dsrc, off, l + DKDV_TILE_BYTES + j * 1024);
       }
@@ -316,23 +329,23 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
 
   // K^T and V^T as B operands: lane holds k[k0 + lq][16 ks + 8 lh + 0..7]
   const int krow = k0 + lq;
-  bf16x8 kf[8], vf[8];
+  bf16x8 kf[KS], vf[KS];
   {
-    const size_t off = (size_t)min(krow, T - 1) * kstride + (size_t)g * HEAD_DIM + lh * 8;
+    const size_t off = (size_t)min(krow, T - 1) * kstride + (size_t)g * D + lh * 8;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       kf[ks] = as_bf16x8(ldg16(k + off + ks * 16));
       vf[ks] = as_bf16x8(ldg16(v + off + ks * 16));
     }
     // Make the compiler wait for these loads here: a wait inside the loop
     // would also wait for the step's own prefetch.
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(kf[ks]), "v"(vf[ks]));
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(kf[ks]), "v"(vf[ks]));
   }
 
-  f32x16 dka[4], dva[4];
+  f32x16 dka[DB], dva[DB];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
+  for (int db = 0; db < DB; ++db) {
     dka[db] = zero_f32x16();
     dva[db] = zero_f32x16();
   }
@@ -368,21 +381,21 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
     if constexpr (CAP) s = zero_f32x16();
     const bf16* Qs = q_tile(buf);
     const bf16* Ds = do_tile(buf);
-    bf16x8 qa[8], da[8];
+    bf16x8 qa[KS], da[KS];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      qa[ks] = swz_frag_cols(Qs, ks, lane);
-      da[ks] = swz_frag_cols(Ds, ks, lane);
+    for (int ks = 0; ks < KS; ++ks) {
+      qa[ks] = swz_frag_cols<D>(Qs, ks, lane);
+      da[ks] = swz_frag_cols<D>(Ds, ks, lane);
     }
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       s = mfma32(qa[ks], kf[ks], s);
       dp = mfma32(da[ks], vf[ks], dp);
     }
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      dof[x] = swz_frag_rows(Ds, (x & 3) * 32, x >> 2, lane);
-      qtf[x] = swz_frag_rows(Qs, (x & 3) * 32, x >> 2, lane);
+    for (int x = 0; x < 2 * DB; ++x) {
+      dof[x] = swz_frag_rows<D>(Ds, (x % DB) * 32, x / DB, lane);
+      qtf[x] = swz_frag_rows<D>(Qs, (x % DB) * 32, x / DB, lane);
     }
   };
   // Half t of P and dS (queries 16t .. 16t + 15 of the step at qb) as bf16
@@ -412,9 +425,9 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
   auto dv_dk = [&](int t, const bf16x8& pf, const bf16x8& dsf, const bf16x8* dof,
                    const bf16x8* qtf) {
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      dva[db] = mfma32(pf, dof[t * 4 + db], dva[db]);
-      dka[db] = mfma32(dsf, qtf[t * 4 + db], dka[db]);
+    for (int db = 0; db < DB; ++db) {
+      dva[db] = mfma32(pf, dof[t * DB + db], dva[db]);
+      dka[db] = mfma32(dsf, qtf[t * DB + db], dka[db]);
     }
   };
 
@@ -435,12 +448,15 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
     bf16x8 pf0, ds0, pf1, ds1;
     p_ds(s_c, dp_c, ls_c, qb, 0, pf0, ds0);
     p_ds(s_c, dp_c, ls_c, qb, 1, pf1, ds1);
+    // The S/dP products (2 KS of them) interleaved with the step's LDS reads
+    // (8 row-stat reads, 2 KS row reads, 8 DB transposing reads: 3 per
+    // product after the first 8) and the softmax arithmetic (about 112 VALU).
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);    // 8 LDS reads
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
+    for (int x = 0; x < 2 * KS; ++x) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // 3 LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // 7 VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 112 / (2 * KS), 0);  // VALU
     }
     __builtin_amdgcn_sched_barrier(0);
     dv_dk(0, pf0, ds0, dof_c, qtf_c);
@@ -449,7 +465,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
   };
 
   f32x16 sA, dpA, sB, dpB, lsA, lsB;   // lsA, lsB: only with a cap
-  bf16x8 dofA[8], qtfA[8], dofB[8], qtfB[8];
+  bf16x8 dofA[2 * DB], qtfA[2 * DB], dofB[2 * DB], qtfB[2 * DB];
   if (steps > 0) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (steps > 1) issue_next(1);
@@ -469,12 +485,13 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
 
   // Head-group reduction in a fixed order (wave 0 + 1 + 2 + 3), then store.
   float* red = reinterpret_cast<float*>(smem);
-  const int okey = tid >> 3, od = (tid & 7) * 16;
+  constexpr int OCOLS = D / 8;   // output columns per thread (32 keys x 8 threads)
+  const int okey = tid >> 3, od = (tid & 7) * OCOLS;
   for (int pass = 0; pass < 2; ++pass) {
     __syncthreads();
     float* mine = red + (size_t)wave * TILE * RED_PITCH;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = (r >> 2) * 8 + lh * 4 + (r & 3);
@@ -483,10 +500,9 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
     __syncthreads();
     if (k0 + okey < k1) {
       const float mul = pass == 0 ? scale : 1.f;
-      bf16* dst = (pass == 0 ? dk : dv) + (size_t)(k0 + okey) * kstride +
-                  (size_t)g * HEAD_DIM + od;
+      bf16* dst = (pass == 0 ? dk : dv) + (size_t)(k0 + okey) * kstride + (size_t)g * D + od;
 #pragma unroll
-      for (int e = 0; e < 16; e += 4) {
+      for (int e = 0; e < OCOLS; e += 4) {
         float acc4[4];
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
@@ -502,30 +518,27 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
   }
 }
 
-}  // namespace
-
-hipError_t launch_dq(const void* q, const void* k, const void* v, const void* out,
-                     const float* lse, const void* dout, const Problem& p, void* dq,
-                     void* workspace, const WorkspaceLayout& w, hipStream_t stream) {
-  char* ws = static_cast<char*>(workspace);
+template <int D, bool CAP>
+void launch_dq_kernel(const void* q, const void* k, const void* v, const void* out,
+                      const float* lse, const void* dout, const Problem& p, void* dq, char* ws,
+                      const WorkspaceLayout& w, hipStream_t stream) {
   const unsigned grid = (unsigned)(w.tile_cap * (size_t)(p.num_q_heads / 4));
   const CapConstants cc = cap_constants(p);
-  hipLaunchKernelGGL(p.softcap > 0.f ? dq_kernel<true> : dq_kernel<false>, dim3(grid),
-                     dim3(BWD_THREADS), 0, stream, static_cast<const bf16*>(q),
-                     static_cast<const bf16*>(k), static_cast<const bf16*>(v),
-                     static_cast<const bf16*>(out), static_cast<const bf16*>(dout), lse,
+  hipLaunchKernelGGL((dq_kernel<D, CAP>), dim3(grid), dim3(BWD_THREADS), 0, stream,
+                     static_cast<const bf16*>(q), static_cast<const bf16*>(k),
+                     static_cast<const bf16*>(v), static_cast<const bf16*>(out),
+                     static_cast<const bf16*>(dout), lse,
                      reinterpret_cast<const int*>(ws + w.header),
                      reinterpret_cast<const Tile*>(ws + w.tiles_fwd), p.total_tokens,
                      p.num_q_heads, p.num_kv_heads, p.window, p.scale * LOG2E, p.scale,
                      cc.cap_a, cc.cap_c2, (int)w.tile_cap, static_cast<bf16*>(dq),
                      reinterpret_cast<TileStats*>(ws + w.rowstats));
-  return hipGetLastError();
 }
 
-hipError_t launch_dkdv(const void* q, const void* k, const void* v, const float* lse,
-                       const void* dout, const Problem& p, void* dk, void* dv, void* workspace,
-                       const WorkspaceLayout& w, hipStream_t stream) {
-  const char* ws = static_cast<const char*>(workspace);
+template <int D, bool CAP>
+void launch_dkdv_kernel(const void* q, const void* k, const void* v, const void* dout,
+                        const Problem& p, void* dk, void* dv, const char* ws,
+                        const WorkspaceLayout& w, hipStream_t stream) {
   // Runs of R list entries per key-value head, dealt to the XCDs in rounds
   // of 8 runs (see the kernel); the grid covers every (tile, head) pair.
   // Local layers, where most tiles cost the same, take long runs (more L2
@@ -536,16 +549,51 @@ hipError_t launch_dkdv(const void* q, const void* k, const void* v, const float*
   const size_t round = 8 * (size_t)run_len;
   const unsigned grid = (unsigned)((items + round - 1) / round * round);
   const CapConstants cc = cap_constants(p);
-  hipLaunchKernelGGL(p.softcap > 0.f ? dkdv_kernel<true> : dkdv_kernel<false>, dim3(grid),
-                     dim3(BWD_THREADS), 0, stream, static_cast<const bf16*>(q),
-                     static_cast<const bf16*>(k), static_cast<const bf16*>(v),
-                     static_cast<const bf16*>(dout),
+  hipLaunchKernelGGL((dkdv_kernel<D, CAP>), dim3(grid), dim3(BWD_THREADS), 0, stream,
+                     static_cast<const bf16*>(q), static_cast<const bf16*>(k),
+                     static_cast<const bf16*>(v), static_cast<const bf16*>(dout),
                      reinterpret_cast<const TileStats*>(ws + w.rowstats), (int)w.tile_cap,
                      reinterpret_cast<const int*>(ws + w.header),
                      reinterpret_cast<const Tile*>(ws + w.tiles_bwd), p.total_tokens,
                      p.num_q_heads, p.num_kv_heads, p.window, p.scale * LOG2E, p.scale,
                      cc.cap_a, cc.cap_c2, run_len, static_cast<bf16*>(dk),
                      static_cast<bf16*>(dv));
+}
+
+}  // namespace
+
+hipError_t launch_dq(const void* q, const void* k, const void* v, const void* out,
+                     const float* lse, const void* dout, const Problem& p, void* dq,
+                     void* workspace, const WorkspaceLayout& w, hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  const bool cap = p.softcap > 0.f;
+#define ATTN_DQ(D)                                                                    \
+  (cap ? launch_dq_kernel<D, true>(q, k, v, out, lse, dout, p, dq, ws, w, stream)     \
+       : launch_dq_kernel<D, false>(q, k, v, out, lse, dout, p, dq, ws, w, stream))
+  switch (p.head_dim) {
+    case 64: ATTN_DQ(64); break;
+    case 128: ATTN_DQ(128); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef ATTN_DQ
+  return hipGetLastError();
+}
+
+hipError_t launch_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                       const void* dout, const Problem& p, void* dk, void* dv, void* workspace,
+                       const WorkspaceLayout& w, hipStream_t stream) {
+  (void)lse;
+  const char* ws = static_cast<const char*>(workspace);
+  const bool cap = p.softcap > 0.f;
+#define ATTN_DKDV(D)                                                                \
+  (cap ? launch_dkdv_kernel<D, true>(q, k, v, dout, p, dk, dv, ws, w, stream)       \
+       : launch_dkdv_kernel<D, false>(q, k, v, dout, p, dk, dv, ws, w, stream))
+  switch (p.head_dim) {
+    case 64: ATTN_DKDV(64); break;
+    case 128: ATTN_DKDV(128); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef ATTN_DKDV
   return hipGetLastError();
 }
 

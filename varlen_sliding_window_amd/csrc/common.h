@@ -14,18 +14,14 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int HEAD_DIM = 128;
 // Rows of one tile: a q-tile (forward, dQ) or a k-tile (dK/dV) is at most
 // TILE consecutive tokens of one segment, starting at the segment start.
 constexpr int TILE = 32;
-// Keys per inner step of the forward and dQ kernels.
+// Keys per inner step of the forward and dQ kernels (the unit of the
+// schedule's cost sort; head dim 256 runs 32-key steps, which sort the same).
 constexpr int KBLK = 64;
 // Queries per inner step of the dK/dV kernel.
 constexpr int QBLK = 32;
-// LDS row pitch in bf16 elements: 128 + 16 pad (288 bytes).  The pad keeps
-// both the 16-byte row reads and the transposing 8-byte reads spread over
-// the banks.
-constexpr int LDS_PITCH = HEAD_DIM + 16;
 // Cost buckets of the longest-first sort.
 constexpr int SORT_BINS = 1024;
 

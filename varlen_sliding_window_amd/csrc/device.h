@@ -48,75 +48,88 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
   return __builtin_bit_cast(bf16x4, r);
 }
 
-// A or B fragment whose lane index runs over the columns of a row-major LDS
-// tile and whose 8 register elements run over rows 16t + 8(i/4) + 4h + i%4:
-// `tile` points at row 0, column 0 of the 32 columns this fragment covers.
-__device__ __forceinline__ bf16x8 lds_frag_rows(const bf16* tile, int t, int lane) {
-  const int h = lane >> 5;
-  const bf16* p = tile + (16 * t + 4 * h + ((lane & 15) >> 2)) * LDS_PITCH + (lane & 16) +
-                  4 * (lane & 3);
-  const bf16x4 lo = lds_read_tr(p);
-  const bf16x4 hi = lds_read_tr(p + 8 * LDS_PITCH);
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+// ---- swizzled, unpadded LDS tiles --------------------------------------------
+// A tile holds rows of D bf16 (D = 64, 128 or 256: 128, 256 or 512 bytes)
+// with no padding; 16-byte chunk c of row r is stored at chunk c ^ swz<D>(r).
+// The swizzle is a bijection per row (it only flips the low bits of c) and
+// keeps both read patterns free of LDS bank conflicts (64 banks of 4 bytes,
+// so one 256-byte line of banks):
+//   16-byte row reads (16 lanes on 16 consecutive rows, same chunk): the 16
+//     addresses must fall in 16 different 16-byte bank groups;
+//   transposing 8-byte reads (32 lanes on 4 consecutive rows x an aligned
+//     group of 4 chunks): the 4 rows must land in 4 different groups of 4.
+// D = 128 (a row is one bank line): swz rotates the low four bits of r by two,
+//   a bijection on 16 rows whose bits 2-3 differ within any 4 aligned rows.
+// D = 256 (two bank lines per row): the same swz on the chunk's low four bits.
+// D = 64 (two rows per bank line, parity picks the half): within each parity
+//   class the row's bits 1-3 are rotated by one, again a bijection on the 8
+//   rows of that class, and rows 4k and 4k + 2 differ in the group bit.
+// Unpadded rows let one wave fill 1 KB of whole rows with a single direct
+// global-to-LDS load.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(D == 64 || D == 128 || D == 256, "head dims 64, 128, 256");
+  if constexpr (D == 64)
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  else
+    return ((r & 3) << 2) | ((r >> 2) & 3);
 }
 
 // A or B fragment whose lane index runs over rows (c = lane % 32) and whose
-// register elements are 8 consecutive columns 16 ks + 8h + 0..7.
-__device__ __forceinline__ bf16x8 lds_frag_cols(const bf16* tile, int ks, int lane) {
-  return *reinterpret_cast<const bf16x8*>(tile + (lane & 31) * LDS_PITCH + ks * 16 +
-                                          (lane >> 5) * 8);
-}
-
-// ---- swizzled, unpadded LDS tiles --------------------------------------------
-// A tile holds rows of HEAD_DIM bf16 (256 bytes, all 64 banks) with no
-// padding; 16-byte chunk c of row r is stored at chunk c ^ swz(r), where
-// swz rotates the low four bits of r by two.  The swizzle is a bijection per
-// row and keeps both read patterns free of bank conflicts:
-//   16-byte row reads: 16 lanes on 16 consecutive rows, same chunk ->
-//     swz takes 16 distinct values;
-//   transposing 8-byte reads: 32 lanes on 4 consecutive rows x 4 consecutive
-//     chunks (an aligned group of 4) -> the 4 rows' swz values differ in
-//     bits 2-3, so each row lands in its own group of 4 chunks.
-// Unpadded rows let one wave fill 4 whole rows (1 KB) with a single direct
-// global-to-LDS load.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-
-// Like lds_frag_cols, on a swizzled tile.
+// register elements are 8 consecutive columns 16 ks + 8h + 0..7 of a
+// swizzled tile (rows 32-aligned relative to the tile start).
+template <int D>
 __device__ __forceinline__ bf16x8 swz_frag_cols(const bf16* tile, int ks, int lane) {
   const int r = lane & 31;
   const int c = 2 * ks + (lane >> 5);
-  return *reinterpret_cast<const bf16x8*>(tile + r * HEAD_DIM + ((c ^ swz(r)) << 3));
+  return *reinterpret_cast<const bf16x8*>(tile + r * D + ((c ^ swz<D>(r)) << 3));
 }
 
-// Like lds_frag_rows, on a swizzled tile; col0 is the first of 32 columns.
+// A or B fragment whose lane index runs over 32 columns of a swizzled tile
+// (starting at column col0, a multiple of 32) and whose 8 register elements
+// run over rows 16t + 8(i/4) + 4h + i%4, read with two transposing reads.
+template <int D>
 __device__ __forceinline__ bf16x8 swz_frag_rows(const bf16* tile, int col0, int t, int lane) {
   const int r0 = 16 * t + 4 * (lane >> 5) + ((lane & 15) >> 2);
   const int r1 = r0 + 8;
   const int col = col0 + (lane & 16) + 4 * (lane & 3);
   const int c = col >> 3, off = col & 7;
-  const bf16x4 lo = lds_read_tr(tile + r0 * HEAD_DIM + ((c ^ swz(r0)) << 3) + off);
-  const bf16x4 hi = lds_read_tr(tile + r1 * HEAD_DIM + ((c ^ swz(r1)) << 3) + off);
+  const bf16x4 lo = lds_read_tr(tile + r0 * D + ((c ^ swz<D>(r0)) << 3) + off);
+  const bf16x4 hi = lds_read_tr(tile + r1 * D + ((c ^ swz<D>(r1)) << 3) + off);
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Asynchronous copy (one wave) of 32 rows x 128 bf16 into a swizzled tile:
-// rows row0 .. row0 + 31 of a row-major matrix whose row r starts at
-// g + r * stride.  Rows at or past T are clamped to T - 1 (their values
-// are masked by the caller).  8 direct global-to-LDS loads per lane; the
-// caller waits with s_waitcnt vmcnt before reading the tile.
-__device__ __forceinline__ void swz_tile32_load_async(bf16* tile, const bf16* g, size_t stride,
-                                                      int row0, int T, int lane) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = 4 * i + (lane >> 4);
-    const int c = (lane & 15) ^ swz(r);
-    const int row = min(row0 + r, T - 1);
-    __builtin_amdgcn_global_load_lds(g + (size_t)row * stride + c * 8,
-                                     (lds_void*)(tile + i * 512), 16, 0, 0);
+// Geometry of one wave's 1 KB direct loads into a swizzled tile of rows of D
+// bf16: lane l moves 16 bytes into physical chunk l % CPR of row l / CPR of
+// the load's RPD rows, so it fetches the logical chunk that lands there.
+template <int D>
+struct TileLoad {
+  static constexpr int CPR = D / 8;     // 16-byte chunks per row
+  static constexpr int RPD = 64 / CPR;  // rows per 1 KB load
+  // Byte offset within a row of the chunk that lane `lane` fetches, when the
+  // lane lands in tile row r.
+  __device__ static uint32_t chunk_offset(int lane, int r) {
+    return (uint32_t)(((lane % CPR) ^ swz<D>(r)) << 4);
   }
-}
+};
+
+// Per-head-dim geometry of the kernels that stream key-value blocks (the
+// forward and dQ): 4 waves share each double-buffered K/V block in LDS.
+template <int D>
+struct BlockGeom {
+  static constexpr int KB = D <= 128 ? 64 : 32;          // keys per block
+  static constexpr int H2 = KB / 32;                     // 32-key halves of a block
+  static constexpr int KS = D / 16;                      // k-steps of a D-long product
+  static constexpr int DB = D / 32;                      // 32-column blocks of D
+  static constexpr int TILE_BYTES = KB * D * (int)sizeof(bf16);
+  static constexpr int BUF_BYTES = 2 * TILE_BYTES;       // K and V
+  static constexpr int ROWS_PER_WAVE = KB / 4;           // rows each wave loads
+  static constexpr int LOADS = ROWS_PER_WAVE / TileLoad<D>::RPD;   // 1 KB loads per tensor
+  // work-groups per CU: 2 up to D = 128; at D = 256 a wave's operands and
+  // accumulators need a whole SIMD's registers
+  static constexpr int MIN_WG = D <= 128 ? 2 : 1;
+  static_assert(LOADS >= 1 && ROWS_PER_WAVE % TileLoad<D>::RPD == 0, "whole loads per wave");
+};
 
 // Direct global-to-LDS load by one wave: the 16 bytes at base + off of each
 // active lane land at LDS byte address lds + 16 * lane.  It is issued as

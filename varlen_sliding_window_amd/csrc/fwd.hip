@@ -5,7 +5,8 @@
 // Fig. 2 "Benchmark setup": 8 query heads share 2 key-value heads, so 4 query
 // heads read the same K/V).  Each wave owns one head: its 32 q rows stay in
 // registers as MFMA operands, while the work-group streams the visible keys
-// through LDS in KBLK = 64-key blocks shared by the 4 heads.  The blocks
+// through LDS in blocks shared by the 4 heads (64 keys for head dims 64 and
+// 128, 32 for 256, so that two double-buffered K/V blocks stay at 64 KB).  The blocks
 // arrive by direct global-to-LDS loads, double-buffered: the loads of the
 // next block go out as soon as every wave is done with the buffer they
 // overwrite, one barrier per block.
@@ -33,19 +34,17 @@ namespace attn {
 namespace {
 
 constexpr int FWD_THREADS = 256;
-constexpr int FWD_WAVES = 4;
-constexpr int FWD_TILE_BYTES = KBLK * HEAD_DIM * (int)sizeof(bf16);   // 16 KB
-constexpr int FWD_BUF_BYTES = 2 * FWD_TILE_BYTES;                     // K and V
 constexpr float RESCALE_LOG2 = 8.f;
-static_assert(KBLK == 16 * FWD_WAVES, "each wave loads 16 rows of a block");
 
-template <bool CAP>
-__global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(
+template <int D, bool CAP>
+__global__ __launch_bounds__(FWD_THREADS, BlockGeom<D>::MIN_WG) void fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
     int window, float scale_log2, float cap_a, float cap_c2, bf16* __restrict__ out,
     float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * FWD_BUF_BYTES];
+  using Geo = BlockGeom<D>;
+  constexpr int KB = Geo::KB, H2 = Geo::H2, KS = Geo::KS, DB = Geo::DB;
+  __shared__ __attribute__((aligned(16))) char smem[2 * Geo::BUF_BYTES];
 
   const int chunks = Hq >> 2;
   const int item = blockIdx.x / chunks;
@@ -60,55 +59,58 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(
   const int g = (hc * 4) / (Hq / Hkv);
   const int q0 = tl.t0, q1 = tl.t1, a = tl.seg_a;
   const int klo = first_visible_key(q0, a, window);
-  const int nblk = (q1 - klo + KBLK - 1) / KBLK;
+  const int nblk = (q1 - klo + KB - 1) / KB;
   const int qrow = q0 + lq;
-  const size_t qstride = (size_t)Hq * HEAD_DIM;
-  const uint32_t kstride_b = (uint32_t)(Hkv * HEAD_DIM * sizeof(bf16));
+  const size_t qstride = (size_t)Hq * D;
+  const uint32_t kstride_b = (uint32_t)(Hkv * D * sizeof(bf16));
 
-  // Block loads: wave w fills rows 16w .. 16w + 15 of the K and V tiles,
-  // 4 rows (1 KB) per load; the lane fetches the 16-byte chunk that lands at
-  // physical chunk lane % 16 of its swizzled row.  Keys before 0 re-read key
+  // Block loads: wave w fills rows ROWS_PER_WAVE * w + [0, ROWS_PER_WAVE) of
+  // the K and V tiles, RPD rows (1 KB) per load.  Keys before 0 re-read key
   // 0; they are always masked.
-  const bf16* kbase = k + (size_t)g * HEAD_DIM;
-  const bf16* vbase = v + (size_t)g * HEAD_DIM;
-  const uint32_t lds0 = lds_address(smem) + (uint32_t)(wave * 16 * HEAD_DIM * sizeof(bf16));
-  uint32_t coff[4];
+  const bf16* kbase = k + (size_t)g * D;
+  const bf16* vbase = v + (size_t)g * D;
+  const uint32_t lds0 = lds_address(smem) + (uint32_t)(wave * Geo::ROWS_PER_WAVE * D * sizeof(bf16));
+  uint32_t coff[Geo::LOADS];
+  int lrow[Geo::LOADS];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) coff[j] = (uint32_t)(((lane & 15) ^ swz(4 * j + (lane >> 4))) << 4);
+  for (int j = 0; j < Geo::LOADS; ++j) {
+    lrow[j] = Geo::ROWS_PER_WAVE * wave + TileLoad<D>::RPD * j + lane / TileLoad<D>::CPR;
+    coff[j] = TileLoad<D>::chunk_offset(lane, lrow[j]);
+  }
   auto issue = [&](int n, int buf) {
-    const int kb = q1 - KBLK * (n + 1);
-    const uint32_t l = lds0 + (uint32_t)(buf * FWD_BUF_BYTES);
+    const int kb = q1 - KB * (n + 1);
+    const uint32_t l = lds0 + (uint32_t)(buf * Geo::BUF_BYTES);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = max(kb + 16 * wave + 4 * j + (lane >> 4), 0);
+    for (int j = 0; j < Geo::LOADS; ++j) {
+      const int key = max(kb + lrow[j], 0);
       const uint32_t off = (uint32_t)key * kstride_b + coff[j];
       dma16(kbase, off, l + j * 1024);
-      dma16(vbase, off, l + FWD_TILE_BYTES + j * 1024);
+      dma16(vbase, off, l + Geo::TILE_BYTES + j * 1024);
     }
   };
   issue(0, 0);
 
   // Q^T as the B operand: lane holds q[qrow][16 ks + 8 lh + 0..7]
-  bf16x8 qf[8];
+  bf16x8 qf[KS];
   {
-    const bf16* qp = q + (size_t)qrow * qstride + (size_t)head * HEAD_DIM + lh * 8;
+    const bf16* qp = q + (size_t)qrow * qstride + (size_t)head * D + lh * 8;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = qrow < T ? as_bf16x8(ldg16(qp + ks * 16)) : zero_bf16x8();
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = qrow < T ? as_bf16x8(ldg16(qp + ks * 16)) : zero_bf16x8();
     // Make the compiler wait for these loads here, not inside the loop where
     // the wait would also cover the block loads in flight.
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qf[ks]));
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
 
-  f32x16 o[4];
+  f32x16 o[DB];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) o[db] = zero_f32x16();
+  for (int db = 0; db < DB; ++db) o[db] = zero_f32x16();
   float m = -INFINITY, lsum = 0.f;
   const int full_lo = first_visible_key(q0 + TILE - 1, a, window);
   const int my_lo = first_visible_key(qrow, a, window);
 
   for (int n = 0; n < nblk; ++n) {
-    const int kb = q1 - KBLK * (n + 1);
+    const int kb = q1 - KB * (n + 1);
     const int buf = n & 1;
     // This wave's loads of block n have landed; after the barrier so have
     // everyone's, and every wave is done with block n - 1, whose buffer the
@@ -116,31 +118,30 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (n + 1 < nblk) issue(n + 1, buf ^ 1);
-    const bf16* Ks = reinterpret_cast<const bf16*>(smem + buf * FWD_BUF_BYTES);
-    const bf16* Vs = Ks + KBLK * HEAD_DIM;
+    const bf16* Ks = reinterpret_cast<const bf16*>(smem + buf * Geo::BUF_BYTES);
+    const bf16* Vs = Ks + KB * D;
 
     // S^T for keys kb + 32 h2 + [0, 32): s[h2][r] = q[qrow] . k[kb + 32 h2 + 8(r/4) + 4 lh + r%4]
-    bf16x8 kfr[16];
+    bf16x8 kfr[H2 * KS];
 #pragma unroll
-    for (int x = 0; x < 16; ++x) kfr[x] = swz_frag_cols(Ks + (x >> 3) * 32 * HEAD_DIM, x & 7, lane);
-    f32x16 s[2];
-    s[0] = zero_f32x16();
-    s[1] = zero_f32x16();
+    for (int x = 0; x < H2 * KS; ++x) kfr[x] = swz_frag_cols<D>(Ks + (x / KS) * 32 * D, x % KS, lane);
+    f32x16 s[H2];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      s[0] = mfma32(kfr[ks], qf[ks], s[0]);
-      s[1] = mfma32(kfr[8 + ks], qf[ks], s[1]);
-    }
+    for (int h2 = 0; h2 < H2; ++h2) s[h2] = zero_f32x16();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int h2 = 0; h2 < H2; ++h2) s[h2] = mfma32(kfr[h2 * KS + ks], qf[ks], s[h2]);
     if constexpr (CAP) {
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
+      for (int h2 = 0; h2 < H2; ++h2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[h2][r] = cap_c2 * tanh_fast(cap_a * s[h2][r]);
     }
-    const bool full = (kb + KBLK - 1 <= q0) && (kb >= full_lo);
+    const bool full = (kb + KB - 1 <= q0) && (kb >= full_lo);
     if (!full) {
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
+      for (int h2 = 0; h2 < H2; ++h2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kb + h2 * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(
     // online softmax (log2 domain) for this lane's query, lazy rescaling
     float mx = -INFINITY;
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+    for (int h2 = 0; h2 < H2; ++h2)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[h2][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
@@ -159,17 +160,17 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(
       const float mnew = fmaxf(m, mx);
       const float alpha = mnew == -INFINITY ? 1.f : exp2_fast(m - mnew);
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       lsum *= alpha;
       m = mnew;
     }
     const float mref = m == -INFINITY ? 0.f : m;
-    bf16x8 pf[4];
+    bf16x8 pf[2 * H2];
     float rs = 0.f;
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+    for (int h2 = 0; h2 < H2; ++h2)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = exp2_fast(s[h2][r] * scale_log2 - mref);
@@ -180,25 +181,49 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(
 
     // O^T[d][q] += sum_key V^T[d][key] P^T[key][q]
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 2 * H2; ++t)
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-        o[db] = mfma32(swz_frag_rows(Vs, db * 32, t, lane), pf[t], o[db]);
+      for (int db = 0; db < DB; ++db)
+        o[db] = mfma32(swz_frag_rows<D>(Vs, db * 32, t, lane), pf[t], o[db]);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   const float lt = lsum + __shfl_xor(lsum, 32);
   if (qrow < q1) {
     const float inv = 1.f / lt;
-    bf16* op = out + (size_t)qrow * qstride + (size_t)head * HEAD_DIM + lh * 4;
+    bf16* op = out + (size_t)qrow * qstride + (size_t)head * D + lh * 4;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         store_bf16x4(op + db * 32 + j * 8, o[db][4 * j] * inv, o[db][4 * j + 1] * inv,
                      o[db][4 * j + 2] * inv, o[db][4 * j + 3] * inv);
     if (lh == 0) lse[(size_t)head * T + qrow] = (m + log2_fast(lt)) * LN2;
   }
+}
+
+template <int D, bool CAP>
+void launch_fwd_kernel(unsigned grid, hipStream_t stream, const void* q, const void* k,
+                       const void* v, const char* ws, const WorkspaceLayout& w, const Problem& p,
+                       void* out, float* lse) {
+  const CapConstants cc = cap_constants(p);
+  // capped scores arrive in log2 units already: unit scale
+  hipLaunchKernelGGL((fwd_kernel<D, CAP>), dim3(grid), dim3(FWD_THREADS), 0, stream,
+                     static_cast<const bf16*>(q), static_cast<const bf16*>(k),
+                     static_cast<const bf16*>(v), reinterpret_cast<const int*>(ws + w.header),
+                     reinterpret_cast<const Tile*>(ws + w.tiles_fwd), p.total_tokens,
+                     p.num_q_heads, p.num_kv_heads, p.window, CAP ? 1.f : p.scale * LOG2E,
+                     cc.cap_a, cc.cap_c2, static_cast<bf16*>(out), lse);
+}
+
+template <int D>
+void launch_fwd_dim(unsigned grid, hipStream_t stream, const void* q, const void* k,
+                    const void* v, const char* ws, const WorkspaceLayout& w, const Problem& p,
+                    void* out, float* lse) {
+  if (p.softcap > 0.f)
+    launch_fwd_kernel<D, true>(grid, stream, q, k, v, ws, w, p, out, lse);
+  else
+    launch_fwd_kernel<D, false>(grid, stream, q, k, v, ws, w, p, out, lse);
 }
 
 }  // namespace
@@ -208,15 +233,12 @@ hipError_t launch_forward(const void* q, const void* k, const void* v, const Pro
                           hipStream_t stream) {
   const char* ws = static_cast<const char*>(workspace);
   const unsigned grid = (unsigned)(w.tile_cap * (size_t)(p.num_q_heads / 4));
-  const CapConstants cc = cap_constants(p);
-  const bool cap = p.softcap > 0.f;
-  // capped scores arrive in log2 units already: unit scale
-  hipLaunchKernelGGL(cap ? fwd_kernel<true> : fwd_kernel<false>, dim3(grid), dim3(FWD_THREADS),
-                     0, stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
-                     static_cast<const bf16*>(v), reinterpret_cast<const int*>(ws + w.header),
-                     reinterpret_cast<const Tile*>(ws + w.tiles_fwd), p.total_tokens,
-                     p.num_q_heads, p.num_kv_heads, p.window, cap ? 1.f : p.scale * LOG2E,
-                     cc.cap_a, cc.cap_c2, static_cast<bf16*>(out), lse);
+  switch (p.head_dim) {
+    case 64: launch_fwd_dim<64>(grid, stream, q, k, v, ws, w, p, out, lse); break;
+    case 128: launch_fwd_dim<128>(grid, stream, q, k, v, ws, w, p, out, lse); break;
+    case 256: launch_fwd_dim<256>(grid, stream, q, k, v, ws, w, p, out, lse); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -6,7 +6,7 @@
 namespace attn {
 
 struct Problem {
-  int total_tokens, num_seqs, num_q_heads, num_kv_heads, window;
+  int total_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, window;
   float scale;
   float softcap;   // > 0: logits become softcap * tanh(logit / softcap); 0: no cap
 };
