@@ -47,6 +47,7 @@ def test_workspace_size(lib):
     assert n >= 8 * 16384 * 4 + 2 * 16 * (16384 // 32 + 64)
     assert n % 256 == 0
     assert attn.workspace_size(16384, 64, 8, 2, 64, 4096, 512) == n     # head dim 64
+    assert attn.workspace_size(16384, 64, 8, 2, 256, 4096, 512) == n    # head dim 256
     assert attn.workspace_size(16384, 64, 8, 2, 96, 4096, 512) == 0     # head dim 96
     assert attn.workspace_size(0, 1, 8, 2, 128, 1, 0) == 0               # T = 0
     assert attn.workspace_size(100, 1, 8, 3, 128, 100, 0) == 0           # Hq % Hkv

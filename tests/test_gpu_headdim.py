@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 if torch.cuda.is_available():
     from gpu_common import assert_parity, run_hip  # noqa: E402
 
-HEAD_DIMS = [64]
+HEAD_DIMS = [64, 256]
 
 
 def oracle(mb, window, softcap=0.0):

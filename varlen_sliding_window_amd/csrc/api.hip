@@ -45,7 +45,7 @@ attn_status check_shape(int32_t total_tokens, int32_t num_seqs, int32_t num_q_he
     return ATTN_EINVAL;
   if (num_q_heads % num_kv_heads != 0) return ATTN_EINVAL;
   if (max_seqlen <= 0 || max_seqlen > total_tokens) return ATTN_EINVAL;
-  if (head_dim != 64 && head_dim != 128) return ATTN_EUNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return ATTN_EUNSUPPORTED;
   if ((num_q_heads / num_kv_heads) % 4 != 0) return ATTN_EUNSUPPORTED;
   // grid sizes must fit in 32 bits
   const size_t cap = attn::tile_capacity(total_tokens, num_seqs);
@@ -211,7 +211,7 @@ const char* attn_varlen_strerror(attn_status s) {
   switch (s) {
     case ATTN_OK: return "success";
     case ATTN_EINVAL: return "invalid argument (null or misaligned pointer, bad size or scale)";
-    case ATTN_EUNSUPPORTED: return "unsupported shape (head_dim must be 64 or 128 and Hq/Hkv a multiple of 4)";
+    case ATTN_EUNSUPPORTED: return "unsupported shape (head_dim must be 64, 128 or 256 and Hq/Hkv a multiple of 4)";
     case ATTN_EWORKSPACE: return "workspace missing, misaligned (256 B) or too small";
     case ATTN_EDEVICE: return "no usable gfx950 device";
     case ATTN_ELAUNCH: return "kernel launch failed";

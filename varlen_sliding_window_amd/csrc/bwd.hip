@@ -518,6 +518,246 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
   }
 }
 
+// dK/dV at head dim 256.  At D = 256 one wave's share of the kernel above
+// would not fit (the dK/dV accumulators of 32 keys alone fill a SIMD's
+// registers, and double-buffered 256-wide Q/dO rows fill the LDS twice
+// over), so each (key tile, query head) goes to a pair of waves that split
+// the head dim: wave w takes columns 128 (w & 1) + [0, 128) of Q, dO, K, V,
+// dK and dV, and query heads w / 2, w / 2 + 2, ... of the group.  Each wave
+// forms its half of the S and dP contractions; the pair adds the two halves
+// through LDS, after which both hold the step's whole S and dP and go on
+// exactly as above on their own 128 columns.  One step at a time (no
+// software pipeline), with the next step's Q/dO loads in flight; two
+// barriers per step order the exchange.
+template <bool CAP>
+__global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_split_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const TileStats* __restrict__ stats, int tile_cap,
+    const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
+    int window, float scale_log2, float scale, float cap_a, float cap_c2, int run_len,
+    bf16* __restrict__ dk, bf16* __restrict__ dv) {
+  constexpr int D = 256, DH = 128;      // head dim, columns per wave
+  using Geo = DkdvGeom<DH>;             // staging of 128-wide half rows
+  constexpr int KS = Geo::KS, DB = Geo::DB, RED_PITCH = Geo::RED_PITCH;
+  constexpr int TILE_BYTES = Geo::TILE_BYTES, BUF_BYTES = Geo::BUF_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[Geo::LDS_BYTES];
+
+  // work-group -> (key tile, key-value head): as in dkdv_kernel
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int round = slot / run_len;
+  const int rx = (round & 1) ? 7 - xcd : xcd;
+  const int pos = (round * 8 + rx) * run_len + (slot - round * run_len);
+  const int run = pos / (run_len * Hkv), within = pos - run * run_len * Hkv;
+  const int g = within / run_len;
+  const int item = run * run_len + (within - g * run_len);
+  if (item >= header[0]) return;
+  const Tile tl = tiles[item];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lh = lane >> 5, lq = lane & 31;
+  const int half = wave & 1, pair = wave >> 1;
+  const int G = Hq / Hkv;
+  const int k0 = tl.t0, k1 = tl.t1, b = tl.seg_b;
+  const int qhi = window > 0 ? min(b, k1 - 1 + window) : b;
+  const int nqb = (qhi - k0 + QBLK - 1) / QBLK;
+  const int steps = (G / 2) * nqb;   // (head, q-block) pairs of this wave
+  const size_t qstride = (size_t)Hq * D;
+  const size_t kstride = (size_t)Hkv * D;
+
+  char* wbase = smem + (size_t)wave * 2 * BUF_BYTES;
+  const uint32_t lds_wave = lds_address(wbase);
+  const uint32_t rstride = (uint32_t)(qstride * sizeof(bf16));
+  uint32_t dma_off[Geo::LOADS];
+#pragma unroll
+  for (int j = 0; j < Geo::LOADS; ++j) {
+    const int r = TileLoad<DH>::RPD * j + lane / TileLoad<DH>::CPR;
+    dma_off[j] = (uint32_t)r * rstride + TileLoad<DH>::chunk_offset(lane, r);
+  }
+  // Loads of one step into buffer `buf`: this wave's 128 columns of the Q
+  // and dO rows of q-block i of query head `head`, then the q-tile's
+  // TileStats.  Rows past T re-read row T - 1 (masked later).
+  auto issue = [&](int head, int i, int buf) {
+    const int qb = k0 + i * QBLK;
+    const size_t hoff = (size_t)qb * qstride + (size_t)head * D + (size_t)half * DH;
+    const bf16* qsrc = q + hoff;
+    const bf16* dsrc = dout + hoff;
+    const uint32_t l = lds_wave + (uint32_t)(buf * BUF_BYTES);
+    const int rmax = T - 1 - qb;
+#pragma unroll
+    for (int j = 0; j < Geo::LOADS; ++j) {
+      const int r = TileLoad<DH>::RPD * j + lane / TileLoad<DH>::CPR;
+      const uint32_t off = rmax >= QBLK - 1
+                               ? dma_off[j]
+                               : (uint32_t)min(r, rmax) * rstride + TileLoad<DH>::chunk_offset(lane, r);
+      dma16(qsrc, off, l + j * 1024);
+      dma16(dsrc, off, l + TILE_BYTES + j * 1024);
+    }
+    if (lane < 16)
+      dma16(stats + (size_t)head * tile_cap + tl.idx + i, (uint32_t)lane * 16, l + 2 * TILE_BYTES);
+  };
+  int ld_head = g * G + pair, ld_i = 0;
+  auto issue_next = [&](int buf) {
+    issue(ld_head, ld_i, buf);
+    if (++ld_i == nqb) {
+      ld_i = 0;
+      ld_head += 2;
+    }
+  };
+  if (steps > 0) issue_next(0);
+
+  // this wave's 128 columns of K^T and V^T as B operands
+  const int krow = k0 + lq;
+  bf16x8 kf[KS], vf[KS];
+  {
+    const size_t off = (size_t)min(krow, T - 1) * kstride + (size_t)g * D + (size_t)half * DH + lh * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[ks] = as_bf16x8(ldg16(k + off + ks * 16));
+      vf[ks] = as_bf16x8(ldg16(v + off + ks * 16));
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(kf[ks]), "v"(vf[ks]));
+  }
+
+  f32x16 dka[DB], dva[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dka[db] = zero_f32x16();
+    dva[db] = zero_f32x16();
+  }
+  const bool kvalid = krow < k1;
+  const int vis_hi = window > 0 ? min(b - 1, krow + window - 1) : b - 1;
+  const int mbias = (kvalid ? 0 : -(1 << 30)) + 4 * lh - krow;
+  const uint32_t mspan = kvalid ? (uint32_t)(vis_hi - krow) : 0u;
+
+  int qb = k0;
+  for (int it = 0; it < steps; ++it) {
+    const int buf = it & 1;
+    // This wave's loads of step it have landed; after the barrier the partner
+    // is done reading this wave's other buffer (last step's exchange), which
+    // the loads of step it + 1 now overwrite.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (it + 1 < steps) issue_next(buf ^ 1);
+    char* bb = wbase + buf * BUF_BYTES;
+    const bf16* Qs = reinterpret_cast<const bf16*>(bb);
+    const bf16* Ds = reinterpret_cast<const bf16*>(bb + TILE_BYTES);
+    const float* st = reinterpret_cast<const float*>(bb + 2 * TILE_BYTES);
+
+    // Half contractions, seeded (-lse/scale, -D) in the half-0 wave only.
+    f32x16 s, dp, ls;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 a4 = *reinterpret_cast<const float4*>(st + 8 * j + 4 * lh);
+      const float4 b4 = *reinterpret_cast<const float4*>(st + TILE + 8 * j + 4 * lh);
+      const float sa[4] = {a4.x, a4.y, a4.z, a4.w}, sb[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (CAP) {
+          ls[4 * j + e] = sa[e];
+          s[4 * j + e] = 0.f;
+        } else {
+          s[4 * j + e] = half == 0 ? sa[e] : 0.f;
+        }
+        dp[4 * j + e] = half == 0 ? sb[e] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = mfma32(swz_frag_cols<DH>(Qs, ks, lane), kf[ks], s);
+      dp = mfma32(swz_frag_cols<DH>(Ds, ks, lane), vf[ks], dp);
+    }
+    bf16x8 dof[2 * DB], qtf[2 * DB];
+#pragma unroll
+    for (int x = 0; x < 2 * DB; ++x) {
+      dof[x] = swz_frag_rows<DH>(Ds, (x % DB) * 32, x / DB, lane);
+      qtf[x] = swz_frag_rows<DH>(Qs, (x % DB) * 32, x / DB, lane);
+    }
+    // Exchange: every read of this buffer has returned, so its Q region
+    // takes this wave's halves (lane-contiguous float4s); after the barrier
+    // each wave adds its partner's.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    float4* xs = reinterpret_cast<float4*>(bb);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      xs[j * 64 + lane] = make_float4(s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]);
+      xs[(4 + j) * 64 + lane] = make_float4(dp[4 * j], dp[4 * j + 1], dp[4 * j + 2], dp[4 * j + 3]);
+    }
+    __syncthreads();
+    const float4* px = reinterpret_cast<const float4*>(smem + (size_t)(wave ^ 1) * 2 * BUF_BYTES +
+                                                       buf * BUF_BYTES);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 ps = px[j * 64 + lane];
+      const float4 pd = px[(4 + j) * 64 + lane];
+      s[4 * j] += ps.x; s[4 * j + 1] += ps.y; s[4 * j + 2] += ps.z; s[4 * j + 3] += ps.w;
+      dp[4 * j] += pd.x; dp[4 * j + 1] += pd.y; dp[4 * j + 2] += pd.z; dp[4 * j + 3] += pd.w;
+    }
+
+    // P and dS (rows = this lane's key, k = the step's queries), then this
+    // wave's 128 columns of dV += P^T dO and dK += dS^T Q.
+    const int x0 = qb + mbias;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      bf16x8 pf, dsf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * t + e;
+        const bool vis = (uint32_t)(x0 + 8 * (r >> 2) + (r & 3)) <= mspan;
+        if constexpr (CAP) {
+          const float th = tanh_fast(cap_a * s[r]);
+          float p = exp2_fast(cap_c2 * th + ls[r]);
+          p = vis ? p : 0.f;
+          pf[e] = (bf16)p;
+          dsf[e] = (bf16)(p * dp[r] * (1.f - th * th));
+        } else {
+          float p = exp2_fast(s[r] * scale_log2);
+          p = vis ? p : 0.f;
+          pf[e] = (bf16)p;
+          dsf[e] = (bf16)(p * dp[r]);
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dva[db] = mfma32(pf, dof[t * DB + db], dva[db]);
+        dka[db] = mfma32(dsf, qtf[t * DB + db], dka[db]);
+      }
+    }
+    qb = qb + QBLK < k0 + nqb * QBLK ? qb + QBLK : k0;
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+
+  // Reduction over the two head sets in a fixed order (column half h is
+  // wave h + wave h + 2), then store.
+  float* red = reinterpret_cast<float*>(smem);
+  constexpr int OCOLS = D / 8;   // output columns per thread (32 keys x 8 threads)
+  const int okey = tid >> 3, od = (tid & 7) * OCOLS;
+  const int oh = od / DH, oc = od - oh * DH;
+  for (int pass = 0; pass < 2; ++pass) {
+    __syncthreads();
+    float* mine = red + (size_t)wave * TILE * RED_PITCH;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = (r >> 2) * 8 + lh * 4 + (r & 3);
+        mine[key * RED_PITCH + db * 32 + lq] = pass == 0 ? dka[db][r] : dva[db][r];
+      }
+    __syncthreads();
+    if (k0 + okey < k1) {
+      const float mul = pass == 0 ? scale : 1.f;
+      bf16* dst = (pass == 0 ? dk : dv) + (size_t)(k0 + okey) * kstride + (size_t)g * D + od;
+      const float* r0 = red + (size_t)oh * TILE * RED_PITCH + okey * RED_PITCH + oc;
+      const float* r1 = red + (size_t)(oh + 2) * TILE * RED_PITCH + okey * RED_PITCH + oc;
+#pragma unroll
+      for (int e = 0; e < OCOLS; e += 4)
+        store_bf16x4(dst + e, (r0[e] + r1[e]) * mul, (r0[e + 1] + r1[e + 1]) * mul,
+                     (r0[e + 2] + r1[e + 2]) * mul, (r0[e + 3] + r1[e + 3]) * mul);
+    }
+  }
+}
+
 template <int D, bool CAP>
 void launch_dq_kernel(const void* q, const void* k, const void* v, const void* out,
                       const float* lse, const void* dout, const Problem& p, void* dq, char* ws,
@@ -549,7 +789,8 @@ void launch_dkdv_kernel(const void* q, const void* k, const void* v, const void*
   const size_t round = 8 * (size_t)run_len;
   const unsigned grid = (unsigned)((items + round - 1) / round * round);
   const CapConstants cc = cap_constants(p);
-  hipLaunchKernelGGL((dkdv_kernel<D, CAP>), dim3(grid), dim3(BWD_THREADS), 0, stream,
+  auto kernel = D == 256 ? dkdv_split_kernel<CAP> : dkdv_kernel<D == 256 ? 128 : D, CAP>;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(BWD_THREADS), 0, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                      static_cast<const bf16*>(v), static_cast<const bf16*>(dout),
                      reinterpret_cast<const TileStats*>(ws + w.rowstats), (int)w.tile_cap,
@@ -573,6 +814,7 @@ hipError_t launch_dq(const void* q, const void* k, const void* v, const void* ou
   switch (p.head_dim) {
     case 64: ATTN_DQ(64); break;
     case 128: ATTN_DQ(128); break;
+    case 256: ATTN_DQ(256); break;
     default: return hipErrorInvalidValue;
   }
 #undef ATTN_DQ
@@ -591,6 +833,7 @@ hipError_t launch_dkdv(const void* q, const void* k, const void* v, const float*
   switch (p.head_dim) {
     case 64: ATTN_DKDV(64); break;
     case 128: ATTN_DKDV(128); break;
+    case 256: ATTN_DKDV(256); break;
     default: return hipErrorInvalidValue;
   }
 #undef ATTN_DKDV
