@@ -15,6 +15,12 @@ forward and 10*d backward, pairs counted exactly from cu_seqlens and the
 window.  Prints one JSON line.
 
     python bench.py [--steps 20] [--warmup 5] [--workload ctx4096_w512+global]
+                    [--softcap C] [--head-dim D]
+
+--softcap C times the same step with every logit soft-capped to
+C tanh(logit / C) (attn_varlen_fwd_ex / attn_varlen_bwd_ex); the counted
+flops are the same.  --head-dim D (64, 128 or 256) runs the workload with
+that head width (scale 1 / sqrt(D)); flops scale with D.
 """
 from __future__ import annotations
 
@@ -38,6 +44,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 WORKLOADS = {
     # name: (list of (layer label, config name)), shared cu_seqlens from the first config
     "ctx4096_w512+global": [("window512", "ctx4096_w512"), ("global", "ctx4096_global")],
+    "ctx4096_w512+global_h16": [("window512", "ctx4096_w512_h16"),
+                                ("global", "ctx4096_global_h16")],
     "ctx512_w512": [("window512", "ctx512_w512")],
     "ctx4096_w512": [("window512", "ctx4096_w512")],
     "ctx4096_global": [("global", "ctx4096_global")],
@@ -67,7 +75,8 @@ def cpu_info():
     return model
 
 
-def build_layers(workload: str, seed: int, device):
+def build_layers(workload: str, seed: int, device, softcap: float = 0.0, head_dim: int = 0):
+    import dataclasses
     import torch
     from synthetic import CONFIGS, make_cu_seqlens, make_layer
     from varlen_sliding_window_amd.flops import attention_flops
@@ -78,6 +87,8 @@ def build_layers(workload: str, seed: int, device):
     layers = []
     for idx, (label, cname) in enumerate(spec):
         cfg = CONFIGS[cname]
+        if head_dim:
+            cfg = dataclasses.replace(cfg, head_dim=head_dim)
         mb = make_layer(cfg, seed, idx, cu)
 
         def dev(bits):
@@ -96,6 +107,7 @@ def build_layers(workload: str, seed: int, device):
             "ws": attn.new_workspace(t, len(cu) - 1, hq, k.shape[1], d, mb.max_seqlen,
                                      cfg.window, device),
             "flops": attention_flops(cu, cfg.window, hq, d),
+            "softcap": softcap,
         }
         layers.append(lay)
     return cu, layers
@@ -103,9 +115,10 @@ def build_layers(workload: str, seed: int, device):
 
 def run_layer(attn, L):
     attn.fwd(L["q"], L["k"], L["v"], L["cu"], L["max_seqlen"], L["window"], L["scale"],
-             out=L["out"], lse=L["lse"], workspace=L["ws"])
+             out=L["out"], lse=L["lse"], workspace=L["ws"], softcap=L["softcap"])
     attn.bwd(L["q"], L["k"], L["v"], L["out"], L["lse"], L["do"], L["cu"], L["max_seqlen"],
-             L["window"], L["scale"], dq=L["dq"], dk=L["dk"], dv=L["dv"], workspace=L["ws"])
+             L["window"], L["scale"], dq=L["dq"], dk=L["dk"], dv=L["dv"], workspace=L["ws"],
+             softcap=L["softcap"])
 
 
 def cpu_baseline(layers, seed, min_seconds=10.0, max_reps=4):
@@ -124,7 +137,7 @@ def cpu_baseline(layers, seed, min_seconds=10.0, max_reps=4):
             for L in layers:
                 mb = L["mb"]
                 attention_backward(mb.f32("q"), mb.f32("k"), mb.f32("v"), mb.f32("dout"),
-                                   mb.cu_seqlens, L["window"], L["scale"])
+                                   mb.cu_seqlens, L["window"], L["scale"], L["softcap"])
                 flops += L["flops"]["fwd_bwd"]
             reps += 1
     secs = time.perf_counter() - t0
@@ -187,6 +200,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--workload", default="ctx4096_w512+global", choices=sorted(WORKLOADS))
+    ap.add_argument("--softcap", type=float, default=0.0,
+                    help="logit soft-cap C > 0 (every logit becomes C tanh(logit / C))")
+    ap.add_argument("--head-dim", type=int, default=0, choices=[0, 64, 128, 256],
+                    help="head width (default: the workload's, 128)")
     ap.add_argument("--print-sources-sha", action="store_true",
                     help="print the kernel-source hash the traffic summary is keyed on")
     ap.add_argument("--no-cpu-baseline", action="store_true",
@@ -216,7 +233,7 @@ def main():
     if args.copy_calibration:
         copy_calibration(device)
         return
-    cu, layers = build_layers(args.workload, args.seed, device)
+    cu, layers = build_layers(args.workload, args.seed, device, args.softcap, args.head_dim)
     print(f"[bench] workload {args.workload}: {len(layers)} layer(s), {len(cu) - 1} segments, "
           f"max_seqlen {layers[0]['max_seqlen']}", file=sys.stderr, flush=True)
 
@@ -357,6 +374,7 @@ def main():
             "num_seqs": len(cu) - 1,
             "max_seqlen": layers[0]["max_seqlen"],
             "gflop_per_step": step_flops / 1e9,
+            "softcap": args.softcap if args.softcap > 0 else None,
         },
         "layers": layer_report,
         "kernels": kernels,
