@@ -161,10 +161,15 @@ __global__ __launch_bounds__(BWD_THREADS, BlockGeom<D>::MIN_WG) void dq_kernel(
     // invisible elements with selects (so values there, even NaNs, drop out).
     const bool full = (kb + KB - 1 <= q0) && (kb >= full_lo);
     float dsv[H2 * 16];
+    if constexpr (CAP) {
+      // one 32-key half at a time (both at once would exceed 256 registers)
+#pragma unroll
+      for (int h2 = 0; h2 < H2; ++h2) tanh_fragments<1>(&s[h2], cap_a, TANH_NARROW / cap_a);
+    }
 #pragma unroll
     for (int x = 0; x < H2 * 16; ++x) {
       if constexpr (CAP) {
-        const float t = tanh_fast(cap_a * s[x >> 4][x & 15]);
+        const float t = s[x >> 4][x & 15];
         const float p = exp2_fast(cap_c2 * t - lse2);
         dsv[x] = p * (dp[x >> 4][x & 15] - Dv) * (1.f - t * t);
       } else {
@@ -400,6 +405,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
   };
   // Half t of P and dS (queries 16t .. 16t + 15 of the step at qb) as bf16
   // A fragments (rows = keys, k = queries); invisible elements become 0.
+  // With a cap, s already holds tanh(scale qk / c).
   auto p_ds = [&](const f32x16& s, const f32x16& dp, const f32x16& ls, int qb, int t,
                   bf16x8& pf, bf16x8& dsf) {
     const int x = qb + mbias;
@@ -407,7 +413,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
     for (int e = 0; e < 8; ++e) {
       const int r = 8 * t + e;
       if constexpr (CAP) {
-        const float th = tanh_fast(cap_a * s[r]);
+        const float th = s[r];   // tanh(scale qk / c), see body
         float p = exp2_fast(cap_c2 * th + ls[r]);
         p = (uint32_t)(x + 8 * (r >> 2) + (r & 3)) <= mspan ? p : 0.f;
         pf[e] = (bf16)p;
@@ -445,6 +451,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     if (it + 2 < steps) issue_next(it & 1);
     s_dp((it + 1) & 1, s_n, dp_n, dof_n, qtf_n, ls_n);
+    if constexpr (CAP) tanh_fragments<1>(&s_c, cap_a, TANH_NARROW / cap_a);
     bf16x8 pf0, ds0, pf1, ds1;
     p_ds(s_c, dp_c, ls_c, qb, 0, pf0, ds0);
     p_ds(s_c, dp_c, ls_c, qb, 1, pf1, ds1);
@@ -697,6 +704,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_split_kernel(
 
     // P and dS (rows = this lane's key, k = the step's queries), then this
     // wave's 128 columns of dV += P^T dO and dK += dS^T Q.
+    if constexpr (CAP) tanh_fragments<1>(&s, cap_a, TANH_NARROW / cap_a);
     const int x0 = qb + mbias;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -706,7 +714,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_split_kernel(
         const int r = 8 * t + e;
         const bool vis = (uint32_t)(x0 + 8 * (r >> 2) + (r & 3)) <= mspan;
         if constexpr (CAP) {
-          const float th = tanh_fast(cap_a * s[r]);
+          const float th = s[r];
           float p = exp2_fast(cap_c2 * th + ls[r]);
           p = vis ? p : 0.f;
           pf[e] = (bf16)p;

@@ -168,16 +168,45 @@ __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_lo
 //     least squares to (tanh(x) - x) / x^3 on that interval; the exponential
 //     form would lose all relative accuracy as x -> 0 (a cap far above the
 //     logits then still reproduces them).
-__device__ __forceinline__ float tanh_fast(float x) {
-  const float wide = 1.f - 2.f * __builtin_amdgcn_rcpf(exp2_fast(x * (2.f * LOG2E)) + 1.f);
+constexpr float TANH_NARROW = 0.55f;   // |x| below this takes the polynomial
+
+__device__ __forceinline__ float tanh_narrow(float x) {
   const float y = x * x;
   float g = -0.00636491494f;
   g = fmaf(g, y, 0.0211331641f);
   g = fmaf(g, y, -0.0538665094f);
   g = fmaf(g, y, 0.133327132f);
   g = fmaf(g, y, -0.33333321f);
-  const float narrow = fmaf(x * y, g, x);
-  return fabsf(x) < 0.55f ? narrow : wide;
+  return fmaf(x * y, g, x);
+}
+
+__device__ __forceinline__ float tanh_fast(float x) {
+  const float wide = 1.f - 2.f * __builtin_amdgcn_rcpf(exp2_fast(x * (2.f * LOG2E)) + 1.f);
+  return fabsf(x) < TANH_NARROW ? tanh_narrow(x) : wide;
+}
+
+// Soft-capped logits of M accumulator fragments, in place: x <- tanh(a x).
+// When no lane of the wave holds an argument outside the polynomial's range
+// (the usual case for a cap well above the logits) the exponential form is
+// not evaluated at all.  `thr` = TANH_NARROW / a.
+template <int M>
+__device__ __forceinline__ void tanh_fragments(f32x16* x, float a, float thr) {
+  float big = 0.f;
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) big = fmaxf(big, fabsf(x[m][i]));
+  if (__builtin_amdgcn_ballot_w64(!(big < thr))) {   // NaN takes the general path
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[m][i] = tanh_fast(a * x[m][i]);
+  } else {
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[m][i] = tanh_narrow(a * x[m][i]);
+  }
 }
 
 __device__ __forceinline__ void store_bf16x4(bf16* p, float a, float b, float c, float d) {

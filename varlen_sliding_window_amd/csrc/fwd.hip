@@ -133,10 +133,11 @@ __global__ __launch_bounds__(FWD_THREADS, BlockGeom<D>::MIN_WG) void fwd_kernel(
 #pragma unroll
       for (int h2 = 0; h2 < H2; ++h2) s[h2] = mfma32(kfr[h2 * KS + ks], qf[ks], s[h2]);
     if constexpr (CAP) {
+      tanh_fragments<H2>(s, cap_a, TANH_NARROW / cap_a);
 #pragma unroll
       for (int h2 = 0; h2 < H2; ++h2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[h2][r] = cap_c2 * tanh_fast(cap_a * s[h2][r]);
+        for (int r = 0; r < 16; ++r) s[h2][r] *= cap_c2;
     }
     const bool full = (kb + KB - 1 <= q0) && (kb >= full_lo);
     if (!full) {
