@@ -116,9 +116,10 @@ def build_layers(workload: str, seed: int, device, softcap: float = 0.0, head_di
 def run_layer(attn, L):
     attn.fwd(L["q"], L["k"], L["v"], L["cu"], L["max_seqlen"], L["window"], L["scale"],
              out=L["out"], lse=L["lse"], workspace=L["ws"], softcap=L["softcap"])
+    # the backward of a layer reuses the tile schedule its forward just built
     attn.bwd(L["q"], L["k"], L["v"], L["out"], L["lse"], L["do"], L["cu"], L["max_seqlen"],
              L["window"], L["scale"], dq=L["dq"], dk=L["dk"], dv=L["dv"], workspace=L["ws"],
-             softcap=L["softcap"])
+             softcap=L["softcap"], reuse_schedule=True)
 
 
 def cpu_baseline(layers, seed, min_seconds=10.0, max_reps=4):

@@ -133,7 +133,20 @@ attn_status attn_varlen_bwd(const void* q, const void* k, const void* v,
  * arguments as there; the backward must get the same softcap as the forward
  * that produced out and lse.
  *   softcap   finite and >= 0; negative, NaN or infinite -> ATTN_EINVAL
+ *   flags     (backward) 0 or ATTN_BWD_REUSE_SCHEDULE; other bits -> ATTN_EINVAL
+ *
+ * ATTN_BWD_REUSE_SCHEDULE: every forward call leaves in its workspace the
+ * tile schedule of both passes (it depends only on cu_seqlens, the sizes and
+ * the window).  A backward call that passes this flag with the same
+ * workspace, after a forward call on the same stream with the same
+ * cu_seqlens contents, num_seqs, total_tokens, num_q_heads and window (the
+ * pair of calls of one layer in a training step), skips rebuilding it.  The
+ * caller vouches for the cu_seqlens contents; the kernels check the rest on
+ * the device and do nothing (outputs unwritten) if the schedule in the
+ * workspace was built for another total_tokens, num_seqs or window.
  */
+enum { ATTN_BWD_REUSE_SCHEDULE = 1 };
+
 attn_status attn_varlen_fwd_ex(const void* q, const void* k, const void* v,
                                const int32_t* cu_seqlens, int32_t num_seqs,
                                int32_t total_tokens, int32_t num_q_heads, int32_t num_kv_heads,
@@ -146,7 +159,7 @@ attn_status attn_varlen_bwd_ex(const void* q, const void* k, const void* v,
                                const int32_t* cu_seqlens, int32_t num_seqs,
                                int32_t total_tokens, int32_t num_q_heads, int32_t num_kv_heads,
                                int32_t head_dim, int32_t max_seqlen, int32_t window, float scale,
-                               float softcap, void* dq, void* dk, void* dv,
+                               float softcap, uint32_t flags, void* dq, void* dk, void* dv,
                                void* workspace, size_t workspace_bytes, attn_stream_t stream);
 
 /* Static description of a status code (never NULL). */

@@ -86,8 +86,15 @@ def test_fwd_rejects(lib, over, code):
 def test_softcap_rejects(lib, cap):
     args = [FAKE] * 4 + [1, 64, 8, 2, 128, 64, 0, 0.088, cap, FAKE, FAKE, FAKE, 1 << 30, None]
     assert lib.attn_varlen_fwd_ex(*args) == EINVAL
-    bargs = [FAKE] * 7 + [1, 64, 8, 2, 128, 64, 0, 0.088, cap, FAKE, FAKE, FAKE, FAKE, 1 << 30,
-                          None]
+    bargs = [FAKE] * 7 + [1, 64, 8, 2, 128, 64, 0, 0.088, cap, 0, FAKE, FAKE, FAKE, FAKE,
+                          1 << 30, None]
+    assert lib.attn_varlen_bwd_ex(*bargs) == EINVAL
+
+
+@pytest.mark.parametrize("flags", [2, 4, 0x80000000, 3])
+def test_bwd_ex_rejects_unknown_flags(lib, flags):
+    bargs = [FAKE] * 7 + [1, 64, 8, 2, 128, 64, 0, 0.088, 0.0, flags, FAKE, FAKE, FAKE, FAKE,
+                          1 << 30, None]
     assert lib.attn_varlen_bwd_ex(*bargs) == EINVAL
 
 

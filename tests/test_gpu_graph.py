@@ -36,8 +36,8 @@ def padded_boundaries(cfg_name: str, seed: int, capacity: int = CAPACITY) -> np.
     return out
 
 
-@pytest.mark.parametrize("window", [512, 0])
-def test_graph_replay_matches_eager(window):
+@pytest.mark.parametrize("window,reuse", [(512, False), (0, False), (512, True)])
+def test_graph_replay_matches_eager(window, reuse):
     cfg = CONFIGS["ctx4096_w512"]
     T, hq, hkv, d = cfg.total_tokens, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
     # tensors from one seed; boundaries from several (all pad to CAPACITY)
@@ -54,7 +54,8 @@ def test_graph_replay_matches_eager(window):
 
     def step():
         attn.fwd(q, k, v, cu, T, window, scale, out=out, lse=lse, workspace=ws)
-        attn.bwd(q, k, v, out, lse, do, cu, T, window, scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+        attn.bwd(q, k, v, out, lse, do, cu, T, window, scale, dq=dq, dk=dk, dv=dv, workspace=ws,
+                 reuse_schedule=reuse)
 
     def set_boundaries(b: np.ndarray):
         cu.copy_(torch.from_numpy(b))

@@ -17,6 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY_PATH = os.path.join(_HERE, "libattn_varlen.so")
 
 ATTN_OK = 0
+ATTN_BWD_REUSE_SCHEDULE = 1
 STATUS_NAMES = {0: "ATTN_OK", -1: "ATTN_EINVAL", -2: "ATTN_EUNSUPPORTED",
                 -3: "ATTN_EWORKSPACE", -4: "ATTN_EDEVICE", -5: "ATTN_ELAUNCH"}
 
@@ -58,8 +59,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                        ctypes.c_float, ctypes.c_float, vp, vp, vp, sz, vp]
     lib.attn_varlen_fwd_ex.restype = ctypes.c_int
     lib.attn_varlen_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
-                                       i32, i32, ctypes.c_float, ctypes.c_float, vp, vp, vp, vp,
-                                       sz, vp]
+                                       i32, i32, ctypes.c_float, ctypes.c_float, ctypes.c_uint32,
+                                       vp, vp, vp, vp, sz, vp]
     lib.attn_varlen_bwd_ex.restype = ctypes.c_int
     lib.attn_varlen_strerror.argtypes = [ctypes.c_int]
     lib.attn_varlen_strerror.restype = ctypes.c_char_p
@@ -152,9 +153,12 @@ def fwd(q, k, v, cu_seqlens, max_seqlen: int, window: int, scale: float | None =
 
 def bwd(q, k, v, out, lse, dout, cu_seqlens, max_seqlen: int, window: int,
         scale: float | None = None, dq=None, dk=None, dv=None, workspace=None,
-        softcap: float = 0.0):
-    """attn_varlen_bwd (attn_varlen_bwd_ex when softcap > 0): returns
-    (dq, dk, dv), bf16, shaped like q, k, v.  softcap must be the forward's."""
+        softcap: float = 0.0, reuse_schedule: bool = False):
+    """attn_varlen_bwd (attn_varlen_bwd_ex with a soft-cap or reuse_schedule):
+    returns (dq, dk, dv), bf16, shaped like q, k, v.  softcap must be the
+    forward's.  reuse_schedule: `workspace` was just used by the forward call
+    of the same layer (same cu_seqlens and window), whose tile schedule the
+    backward then uses instead of rebuilding it."""
     for name, t_ in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
         _check_tensor(name, t_, torch.bfloat16, 3)
     _check_tensor("lse", lse, torch.float32, 2)
@@ -171,6 +175,7 @@ def bwd(q, k, v, out, lse, dout, cu_seqlens, max_seqlen: int, window: int,
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    workspace_arg_missing = workspace is None
     if workspace is None:
         workspace = new_workspace(t, nseq, hq, hkv, d, max_seqlen, window, q.device)
     lib = load_library()
@@ -178,8 +183,12 @@ def bwd(q, k, v, out, lse, dout, cu_seqlens, max_seqlen: int, window: int,
             t, hq, hkv, d, int(max_seqlen), int(window), float(scale))
     tail = (_ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
             _stream_handle(q.device))
-    if softcap:
-        st, where = lib.attn_varlen_bwd_ex(*head, float(softcap), *tail), "attn_varlen_bwd_ex"
+    if reuse_schedule and workspace_arg_missing:
+        raise ValueError("reuse_schedule needs the forward call's workspace")
+    if softcap or reuse_schedule:
+        flags = ATTN_BWD_REUSE_SCHEDULE if reuse_schedule else 0
+        st, where = (lib.attn_varlen_bwd_ex(*head, float(softcap), flags, *tail),
+                     "attn_varlen_bwd_ex")
     else:
         st, where = lib.attn_varlen_bwd(*head, *tail), "attn_varlen_bwd"
     if st != ATTN_OK:

@@ -137,8 +137,9 @@ attn_status attn_varlen_fwd_ex(const void* q, const void* k, const void* v,
   const Problem p{total_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim,
                   effective_window(window, total_tokens), scale, softcap};
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // both lists, so that the matching backward call may reuse them
   if (timed_launch(K_SCHEDULE, st, [&] {
-        return attn::launch_schedule(cu_seqlens, p, false, workspace, w, st);
+        return attn::launch_schedule(cu_seqlens, p, true, workspace, w, st);
       }) != hipSuccess)
     return ATTN_ELAUNCH;
   if (timed_launch(K_FORWARD, st, [&] {
@@ -163,9 +164,9 @@ attn_status attn_varlen_bwd_ex(const void* q, const void* k, const void* v, cons
                                const float* lse, const void* dout, const int32_t* cu_seqlens,
                                int32_t num_seqs, int32_t total_tokens, int32_t num_q_heads,
                                int32_t num_kv_heads, int32_t head_dim, int32_t max_seqlen,
-                               int32_t window, float scale, float softcap, void* dq, void* dk,
-                               void* dv, void* workspace, size_t workspace_bytes,
-                               attn_stream_t stream) {
+                               int32_t window, float scale, float softcap, uint32_t flags,
+                               void* dq, void* dk, void* dv, void* workspace,
+                               size_t workspace_bytes, attn_stream_t stream) {
   WorkspaceLayout w;
   attn_status s = check_common(q, k, v, cu_seqlens, total_tokens, num_seqs, num_q_heads,
                                num_kv_heads, head_dim, max_seqlen, scale, workspace,
@@ -176,12 +177,14 @@ attn_status attn_varlen_bwd_ex(const void* q, const void* k, const void* v, cons
       !aligned(dk, 16) || !aligned(dv, 16))
     return ATTN_EINVAL;
   if (!std::isfinite(softcap) || softcap < 0.f) return ATTN_EINVAL;
+  if (flags & ~(uint32_t)ATTN_BWD_REUSE_SCHEDULE) return ATTN_EINVAL;
   s = check_device();
   if (s != ATTN_OK) return s;
   const Problem p{total_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim,
                   effective_window(window, total_tokens), scale, softcap};
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (timed_launch(K_SCHEDULE, st, [&] {
+  if (!(flags & ATTN_BWD_REUSE_SCHEDULE) &&
+      timed_launch(K_SCHEDULE, st, [&] {
         return attn::launch_schedule(cu_seqlens, p, true, workspace, w, st);
       }) != hipSuccess)
     return ATTN_ELAUNCH;
@@ -204,7 +207,7 @@ attn_status attn_varlen_bwd(const void* q, const void* k, const void* v, const v
                             void* workspace, size_t workspace_bytes, attn_stream_t stream) {
   return attn_varlen_bwd_ex(q, k, v, out, lse, dout, cu_seqlens, num_seqs, total_tokens,
                             num_q_heads, num_kv_heads, head_dim, max_seqlen, window, scale, 0.f,
-                            dq, dk, dv, workspace, workspace_bytes, stream);
+                            0u, dq, dk, dv, workspace, workspace_bytes, stream);
 }
 
 const char* attn_varlen_strerror(attn_status s) {

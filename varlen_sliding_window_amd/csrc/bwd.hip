@@ -52,7 +52,7 @@ __global__ __launch_bounds__(BWD_THREADS, BlockGeom<D>::MIN_WG) void dq_kernel(
   const int chunks = Hq >> 2;
   const int item = blockIdx.x / chunks;
   const int hc = blockIdx.x - item * chunks;
-  if (item >= header[0]) return;
+  if (item >= header[0] || !schedule_matches(header, T, tile_cap, window)) return;
   const Tile tl = tiles[item];
 
   const int tid = threadIdx.x;
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
   const int run = pos / (run_len * Hkv), within = pos - run * run_len * Hkv;
   const int g = within / run_len;
   const int item = run * run_len + (within - g * run_len);
-  if (item >= header[0]) return;
+  if (item >= header[0] || !schedule_matches(header, T, tile_cap, window)) return;
   const Tile tl = tiles[item];
 
   const int tid = threadIdx.x;
@@ -557,7 +557,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_split_kernel(
   const int run = pos / (run_len * Hkv), within = pos - run * run_len * Hkv;
   const int g = within / run_len;
   const int item = run * run_len + (within - g * run_len);
-  if (item >= header[0]) return;
+  if (item >= header[0] || !schedule_matches(header, T, tile_cap, window)) return;
   const Tile tl = tiles[item];
 
   const int tid = threadIdx.x;

@@ -74,6 +74,15 @@ inline WorkspaceLayout workspace_layout(int64_t total_tokens, int64_t num_seqs,
   return w;
 }
 
+// Workspace header: [0] number of tiles, then the total tokens, tile capacity
+// and window the schedule was built for.  A backward call that reuses the
+// forward's schedule runs only if they match its own, so a stale schedule
+// can give wrong results but never addresses outside the call's buffers.
+__device__ __forceinline__ bool schedule_matches(const int* header, int T, int tile_cap,
+                                                 int window) {
+  return header[1] == T && header[2] == tile_cap && header[3] == window;
+}
+
 // Visible key range of query i in segment starting at a (inclusive bounds).
 __device__ __forceinline__ int first_visible_key(int i, int a, int window) {
   return window > 0 ? max(a, i - window + 1) : a;

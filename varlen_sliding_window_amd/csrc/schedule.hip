@@ -200,7 +200,12 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
       if (valid) bwd_list[pb] = t;
     }
   }
-  if (tid == 0) header[0] = ntiles;
+  if (tid == 0) {
+    header[0] = ntiles;
+    header[1] = T;
+    header[2] = tile_cap;
+    header[3] = window;
+  }
 }
 
 }  // namespace
