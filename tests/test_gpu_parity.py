@@ -66,6 +66,24 @@ def test_edge_segments(window):
     assert_parity(got, oracle(mb, window), f"edge/W{window}")
 
 
+@pytest.mark.parametrize("window", [0, 100])
+def test_more_tiles_than_scheduler_threads(window):
+    """Over 1,024 tiles: the scheduler's multi-pass path (one thread per tile
+    no longer suffices), on 40,000 tokens of documents of 1 to 700 tokens."""
+    rng = np.random.default_rng(77)
+    lens = []
+    while sum(lens) < 40000:
+        lens.append(int(rng.integers(1, 701)))
+    lens[-1] -= sum(lens) - 40000
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    tiles = int(np.sum((np.diff(cu) + 31) // 32))
+    assert tiles > 1024
+    mb = make_custom(cu, 4, 1, seed=78 + window)
+    print(f"[case] {tiles} tiles, {len(lens)} segments, W={window}", flush=True)
+    got = run_hip(mb, window)
+    assert_parity(got, oracle(mb, window), f"{tiles} tiles/W{window}")
+
+
 def test_single_token_microbatch():
     mb = make_custom([0, 1], 4, 1, seed=5)
     got = run_hip(mb, 0)

@@ -157,47 +157,80 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
   if (tid == 0) seg_off[nseq] = ntiles;
   __syncthreads();
 
-  // 2. histogram of costs
-  for (int i = tid; i < ntiles; i += SCHED_THREADS) {
-    const Tile t = tile_at(i, seg_off, cu, nseq, T);
-    atomicAdd(&hist_f[fwd_bin(t, window)], 1);
-    if (need_bwd) atomicAdd(&hist_b[bwd_bin(t, window)], 1);
+  // 2. histogram of costs.  When every tile has a thread of its own (the
+  // usual case: T / TILE + nseq <= 1024) it is built once and kept in
+  // registers for the scatter; lanes of a wave that share a bucket add to
+  // it with one atomic.
+  const bool one_pass = ntiles <= SCHED_THREADS;
+  Tile mine;
+  int my_bf = 0, my_bb = 0;
+  const bool my_valid = one_pass && tid < ntiles;
+  if (my_valid) {
+    mine = tile_at(tid, seg_off, cu, nseq, T);
+    my_bf = fwd_bin(mine, window);
+    my_bb = bwd_bin(mine, window);
+  }
+  if (one_pass) {
+    (void)ordered_slot(hist_f, my_bf, my_valid);
+    if (need_bwd) (void)ordered_slot(hist_b, my_bb, my_valid);
+  } else {
+    for (int i = tid; i < ntiles; i += SCHED_THREADS) {
+      const Tile t = tile_at(i, seg_off, cu, nseq, T);
+      atomicAdd(&hist_f[fwd_bin(t, window)], 1);
+      if (need_bwd) atomicAdd(&hist_b[bwd_bin(t, window)], 1);
+    }
   }
   __syncthreads();
 
-  // 3. bucket start offsets, most expensive bucket first
+  // 3. bucket start offsets, most expensive bucket first (both lists in one
+  // scan, 16 bits each, while the counts fit)
   {
     const int c = SORT_BINS - 1 - tid;
     const int vf = hist_f[c];
     const int vb = hist_b[c];
     int total;
-    const int incf = block_scan(vf, buf, &total);
-    const int incb = block_scan(vb, buf, &total);
-    hist_f[c] = incf - vf;
-    hist_b[c] = incb - vb;
+    if (ntiles < (1 << 15)) {
+      const int inc = block_scan(vf | (vb << 16), buf, &total);
+      hist_f[c] = (inc & 0xffff) - vf;
+      hist_b[c] = (inc >> 16) - vb;
+    } else {
+      const int incf = block_scan(vf, buf, &total);
+      const int incb = block_scan(vb, buf, &total);
+      hist_f[c] = incf - vf;
+      hist_b[c] = incb - vb;
+    }
   }
   __syncthreads();
 
-  // 4. scatter (results do not depend on the order inside a bucket).  In the
-  // backward list each wave places its 64 consecutive tiles so that tiles of
+  // 4. scatter.  Each wave places its 64 consecutive tiles so that tiles of
   // one bucket from one wave keep their token order (a few ballot rounds,
   // then single atomics for what is left): runs of equal cost stay runs of
   // neighbouring tiles, which the dK/dV kernel maps onto one XCD, whose L2
   // then serves the rows that neighbouring tiles share.
-  for (int i0 = 0; i0 < ntiles; i0 += SCHED_THREADS) {
-    const int i = i0 + tid;
-    const bool valid = i < ntiles;
-    Tile t;
-    int bf = 0, bb = 0;
-    if (valid) {
-      t = tile_at(i, seg_off, cu, nseq, T);
-      bf = fwd_bin(t, window);
-      bb = bwd_bin(t, window);
-    }
-    if (valid) fwd_list[atomicAdd(&hist_f[bf], 1)] = t;
+  if (one_pass) {
+    const int pf = ordered_slot(hist_f, my_bf, my_valid);
+    if (my_valid) fwd_list[pf] = mine;
     if (need_bwd) {
-      const int pb = ordered_slot(hist_b, bb, valid);
-      if (valid) bwd_list[pb] = t;
+      const int pb = ordered_slot(hist_b, my_bb, my_valid);
+      if (my_valid) bwd_list[pb] = mine;
+    }
+  } else {
+    for (int i0 = 0; i0 < ntiles; i0 += SCHED_THREADS) {
+      const int i = i0 + tid;
+      const bool valid = i < ntiles;
+      Tile t;
+      int bf = 0, bb = 0;
+      if (valid) {
+        t = tile_at(i, seg_off, cu, nseq, T);
+        bf = fwd_bin(t, window);
+        bb = bwd_bin(t, window);
+      }
+      const int pf = ordered_slot(hist_f, bf, valid);
+      if (valid) fwd_list[pf] = t;
+      if (need_bwd) {
+        const int pb = ordered_slot(hist_b, bb, valid);
+        if (valid) bwd_list[pb] = t;
+      }
     }
   }
   if (tid == 0) {
