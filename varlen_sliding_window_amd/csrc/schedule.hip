@@ -159,8 +159,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
 
   // 2. histogram of costs.  When every tile has a thread of its own (the
   // usual case: T / TILE + nseq <= 1024) it is built once and kept in
-  // registers for the scatter; lanes of a wave that share a bucket add to
-  // it with one atomic.
+  // registers for the scatter.
   const bool one_pass = ntiles <= SCHED_THREADS;
   Tile mine;
   int my_bf = 0, my_bb = 0;
@@ -171,8 +170,10 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
     my_bb = bwd_bin(mine, window);
   }
   if (one_pass) {
-    (void)ordered_slot(hist_f, my_bf, my_valid);
-    if (need_bwd) (void)ordered_slot(hist_b, my_bb, my_valid);
+    if (my_valid) {
+      atomicAdd(&hist_f[my_bf], 1);
+      if (need_bwd) atomicAdd(&hist_b[my_bb], 1);
+    }
   } else {
     for (int i = tid; i < ntiles; i += SCHED_THREADS) {
       const Tile t = tile_at(i, seg_off, cu, nseq, T);
@@ -202,14 +203,14 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
   }
   __syncthreads();
 
-  // 4. scatter.  Each wave places its 64 consecutive tiles so that tiles of
+  // 4. scatter (results do not depend on the order inside a bucket).  In the
+  // backward list each wave places its 64 consecutive tiles so that tiles of
   // one bucket from one wave keep their token order (a few ballot rounds,
   // then single atomics for what is left): runs of equal cost stay runs of
   // neighbouring tiles, which the dK/dV kernel maps onto one XCD, whose L2
   // then serves the rows that neighbouring tiles share.
   if (one_pass) {
-    const int pf = ordered_slot(hist_f, my_bf, my_valid);
-    if (my_valid) fwd_list[pf] = mine;
+    if (my_valid) fwd_list[atomicAdd(&hist_f[my_bf], 1)] = mine;
     if (need_bwd) {
       const int pb = ordered_slot(hist_b, my_bb, my_valid);
       if (my_valid) bwd_list[pb] = mine;
@@ -225,8 +226,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
         bf = fwd_bin(t, window);
         bb = bwd_bin(t, window);
       }
-      const int pf = ordered_slot(hist_f, bf, valid);
-      if (valid) fwd_list[pf] = t;
+      if (valid) fwd_list[atomicAdd(&hist_f[bf], 1)] = t;
       if (need_bwd) {
         const int pb = ordered_slot(hist_b, bb, valid);
         if (valid) bwd_list[pb] = t;
