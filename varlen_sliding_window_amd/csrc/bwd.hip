@@ -227,8 +227,10 @@ struct DkdvGeom {
                 "reduction buffer must fit in the staging buffers");
 };
 
+// At D = 64 the uncapped kernel fits 256 registers, so two work-groups
+// share a CU and each hides the other's start-up and load latency.
 template <int D, bool CAP>
-__global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(
+__global__ __launch_bounds__(BWD_THREADS, (D == 64 && !CAP) ? 2 : 1) void dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const TileStats* __restrict__ stats, int tile_cap,
     const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
