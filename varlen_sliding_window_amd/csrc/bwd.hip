@@ -768,6 +768,207 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_split_kernel(
   }
 }
 
+// dK/dV at head dim 128 without a cap, with two waves per SIMD: 8 waves
+// per work-group, wave w taking query head w % 4 (+ 4 j) and the q-blocks of
+// parity w / 4.  The kernel above needs 447 registers per wave for its
+// software pipeline; this one fits 256 by giving that up: K stays in
+// registers, V is staged once per work-group in LDS and shared by the 8
+// waves, and each wave's Q/dO block has a single LDS buffer, so while one
+// wave waits for its next block the other wave on its SIMD computes.  The 8
+// partial sums are added in a fixed order at the end.
+constexpr int OCC_WAVES = 8;
+constexpr int OCC_THREADS = 64 * OCC_WAVES;
+
+__global__ __launch_bounds__(OCC_THREADS, 1) void dkdv_occ_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const TileStats* __restrict__ stats, int tile_cap,
+    const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
+    int window, float scale_log2, float scale, float cap_a, float cap_c2, int run_len,
+    bf16* __restrict__ dk, bf16* __restrict__ dv) {
+  (void)cap_a;
+  (void)cap_c2;
+  constexpr int D = 128;
+  using Geo = DkdvGeom<D>;
+  constexpr int KS = Geo::KS, DB = Geo::DB, RED_PITCH = Geo::RED_PITCH;
+  constexpr int TILE_BYTES = Geo::TILE_BYTES, BUF_BYTES = Geo::BUF_BYTES;
+  constexpr int VT_BYTES = TILE * D * (int)sizeof(bf16);
+  constexpr size_t LDS_BYTES = (size_t)VT_BYTES + (size_t)OCC_WAVES * BUF_BYTES;
+  static_assert(LDS_BYTES <= 160 * 1024, "staging must fit in LDS");
+  static_assert((size_t)OCC_WAVES * TILE * RED_PITCH * sizeof(float) <= LDS_BYTES,
+                "reduction buffer must fit in the staging buffers");
+  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int round = slot / run_len;
+  const int rx = (round & 1) ? 7 - xcd : xcd;
+  const int pos = (round * 8 + rx) * run_len + (slot - round * run_len);
+  const int run = pos / (run_len * Hkv), within = pos - run * run_len * Hkv;
+  const int g = within / run_len;
+  const int item = run * run_len + (within - g * run_len);
+  if (item >= header[0] || !schedule_matches(header, T, tile_cap, window)) return;
+  const Tile tl = tiles[item];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lh = lane >> 5, lq = lane & 31;
+  const int hs = wave & 3, par = wave >> 2;
+  const int G = Hq / Hkv;
+  const int k0 = tl.t0, k1 = tl.t1, b = tl.seg_b;
+  const int qhi = window > 0 ? min(b, k1 - 1 + window) : b;
+  const int nqb = (qhi - k0 + QBLK - 1) / QBLK;
+  const int nmine = (nqb - par + 1) / 2;       // q-blocks of this parity
+  const int steps = (G / 4) * nmine;
+  const size_t qstride = (size_t)Hq * D;
+  const size_t kstride = (size_t)Hkv * D;
+
+  const bf16* Vt = reinterpret_cast<const bf16*>(smem);
+  char* wb = smem + VT_BYTES + (size_t)wave * BUF_BYTES;
+  const bf16* Qs = reinterpret_cast<const bf16*>(wb);
+  const bf16* Ds = reinterpret_cast<const bf16*>(wb + TILE_BYTES);
+  const float* st = reinterpret_cast<const float*>(wb + 2 * TILE_BYTES);
+  const uint32_t lds_wb = lds_address(wb);
+
+  // V rows of the key tile: wave w loads rows 4w .. 4w + 3 (1 KB)
+  {
+    const int r = TileLoad<D>::RPD * wave + lane / TileLoad<D>::CPR;
+    const uint32_t off = (uint32_t)min(k0 + r, T - 1) * (uint32_t)(kstride * sizeof(bf16)) +
+                         TileLoad<D>::chunk_offset(lane, r);
+    dma16(v + (size_t)g * D, off, lds_address(smem) + (uint32_t)(wave * 1024));
+  }
+
+  const uint32_t rstride = (uint32_t)(qstride * sizeof(bf16));
+  auto issue = [&](int head, int i) {
+    const int qb = k0 + i * QBLK;
+    const size_t hoff = (size_t)qb * qstride + (size_t)head * D;
+    const bf16* qsrc = q + hoff;
+    const bf16* dsrc = dout + hoff;
+    const int rmax = T - 1 - qb;
+#pragma unroll
+    for (int j = 0; j < Geo::LOADS; ++j) {
+      const int r = TileLoad<D>::RPD * j + lane / TileLoad<D>::CPR;
+      const uint32_t off = (uint32_t)min(r, rmax) * rstride + TileLoad<D>::chunk_offset(lane, r);
+      dma16(qsrc, off, lds_wb + j * 1024);
+      dma16(dsrc, off, lds_wb + TILE_BYTES + j * 1024);
+    }
+    if (lane < 16)
+      dma16(stats + (size_t)head * tile_cap + tl.idx + i, (uint32_t)lane * 16,
+            lds_wb + 2 * TILE_BYTES);
+  };
+  int ld_head = g * G + hs, ld_i = par;
+  auto issue_next = [&]() {
+    issue(ld_head, ld_i);
+    ld_i += 2;
+    if (ld_i >= nqb) {
+      ld_i = par;
+      ld_head += 4;
+    }
+  };
+  if (steps > 0) issue_next();
+
+  // K^T as the B operand of S: lane holds k[k0 + lq][16 ks + 8 lh + 0..7]
+  const int krow = k0 + lq;
+  bf16x8 kf[KS];
+  {
+    const size_t off = (size_t)min(krow, T - 1) * kstride + (size_t)g * D + lh * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = as_bf16x8(ldg16(k + off + ks * 16));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(kf[ks]));
+  }
+  f32x16 dka[DB], dva[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dka[db] = zero_f32x16();
+    dva[db] = zero_f32x16();
+  }
+  const bool kvalid = krow < k1;
+  const int vis_hi = window > 0 ? min(b - 1, krow + window - 1) : b - 1;
+  const int mbias = (kvalid ? 0 : -(1 << 30)) + 4 * lh - krow;
+  const uint32_t mspan = kvalid ? (uint32_t)(vis_hi - krow) : 0u;
+  // the V tile (every wave's rows) is in LDS after the barrier
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  int ci = par;   // q-block of the current step
+  for (int it = 0; it < steps; ++it) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // S and dP seeded with -lse/scale and -D of the step's rows
+    f32x16 s, dp;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 a4 = *reinterpret_cast<const float4*>(st + 8 * j + 4 * lh);
+      const float4 b4 = *reinterpret_cast<const float4*>(st + TILE + 8 * j + 4 * lh);
+      s[4 * j + 0] = a4.x; s[4 * j + 1] = a4.y; s[4 * j + 2] = a4.z; s[4 * j + 3] = a4.w;
+      dp[4 * j + 0] = b4.x; dp[4 * j + 1] = b4.y; dp[4 * j + 2] = b4.z; dp[4 * j + 3] = b4.w;
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = mfma32(swz_frag_cols<D>(Qs, ks, lane), kf[ks], s);
+      dp = mfma32(swz_frag_cols<D>(Ds, ks, lane), swz_frag_cols<D>(Vt, ks, lane), dp);
+    }
+    const int x0 = k0 + ci * QBLK + mbias;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      bf16x8 pf, dsf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * t + e;
+        const bool vis = (uint32_t)(x0 + 8 * (r >> 2) + (r & 3)) <= mspan;
+        float p = exp2_fast(s[r] * scale_log2);
+        p = vis ? p : 0.f;
+        pf[e] = (bf16)p;
+        dsf[e] = (bf16)(p * dp[r]);
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dva[db] = mfma32(pf, swz_frag_rows<D>(Ds, db * 32, t, lane), dva[db]);
+        dka[db] = mfma32(dsf, swz_frag_rows<D>(Qs, db * 32, t, lane), dka[db]);
+      }
+    }
+    // every read of this wave's buffer has returned (the products above
+    // consumed them), so the next step's loads may overwrite it
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (it + 1 < steps) issue_next();
+    ci += 2;
+    if (ci >= nqb) ci = par;
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+
+  // Reduction over the 8 waves in a fixed order, then store.
+  float* red = reinterpret_cast<float*>(smem);
+  constexpr int OCOLS = D / 16;   // output columns per thread (32 keys x 16 threads)
+  const int okey = tid >> 4, od = (tid & 15) * OCOLS;
+  for (int pass = 0; pass < 2; ++pass) {
+    __syncthreads();
+    float* mine = red + (size_t)wave * TILE * RED_PITCH;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = (r >> 2) * 8 + lh * 4 + (r & 3);
+        mine[key * RED_PITCH + db * 32 + lq] = pass == 0 ? dka[db][r] : dva[db][r];
+      }
+    __syncthreads();
+    if (k0 + okey < k1) {
+      const float mul = pass == 0 ? scale : 1.f;
+      bf16* dst = (pass == 0 ? dk : dv) + (size_t)(k0 + okey) * kstride + (size_t)g * D + od;
+#pragma unroll
+      for (int e = 0; e < OCOLS; e += 4) {
+        float acc4[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          float sum = 0.f;
+#pragma unroll
+          for (int w = 0; w < OCC_WAVES; ++w)
+            sum += red[(size_t)w * TILE * RED_PITCH + okey * RED_PITCH + od + e + x];
+          acc4[x] = sum * mul;
+        }
+        store_bf16x4(dst + e, acc4[0], acc4[1], acc4[2], acc4[3]);
+      }
+    }
+  }
+}
+
 template <int D, bool CAP>
 void launch_dq_kernel(const void* q, const void* k, const void* v, const void* out,
                       const float* lse, const void* dout, const Problem& p, void* dq, char* ws,
@@ -799,8 +1000,13 @@ void launch_dkdv_kernel(const void* q, const void* k, const void* v, const void*
   const size_t round = 8 * (size_t)run_len;
   const unsigned grid = (unsigned)((items + round - 1) / round * round);
   const CapConstants cc = cap_constants(p);
-  auto kernel = D == 256 ? dkdv_split_kernel<CAP> : dkdv_kernel<D == 256 ? 128 : D, CAP>;
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(BWD_THREADS), 0, stream,
+  // head dim 256: pairs of waves split the head dim; 128 uncapped: two waves
+  // per SIMD; otherwise the software-pipelined kernel
+  constexpr bool occ = D == 128 && !CAP;
+  auto kernel = D == 256 ? dkdv_split_kernel<CAP>
+                : occ    ? dkdv_occ_kernel
+                         : dkdv_kernel<D == 256 ? 128 : D, CAP>;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(occ ? OCC_THREADS : BWD_THREADS), 0, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                      static_cast<const bf16*>(v), static_cast<const bf16*>(dout),
                      reinterpret_cast<const TileStats*>(ws + w.rowstats), (int)w.tile_cap,
