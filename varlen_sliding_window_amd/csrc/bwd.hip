@@ -771,11 +771,14 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_split_kernel(
 // dK/dV at head dim 128 without a cap, with two waves per SIMD: 8 waves
 // per work-group, wave w taking query head w % 4 (+ 4 j) and the q-blocks of
 // parity w / 4.  The kernel above needs 447 registers per wave for its
-// software pipeline; this one fits 256 by giving that up: K stays in
-// registers, V is staged once per work-group in LDS and shared by the 8
+// software pipeline; this one fits 256 by giving that up: the key tile's K
+// and V rows are staged once per work-group in LDS and shared by the 8
 // waves, and each wave's Q/dO block has a single LDS buffer, so while one
-// wave waits for its next block the other wave on its SIMD computes.  The 8
-// partial sums are added in a fixed order at the end.
+// wave waits for its next block the other wave on its SIMD computes.  Inside
+// a step the LDS operand reads run ahead of the products in small register
+// rings (two k-steps for S/dP, four products for dV/dK), fenced so that the
+// compiler keeps that distance.  The 8 partial sums are added in a fixed
+// order at the end.
 constexpr int OCC_WAVES = 8;
 constexpr int OCC_THREADS = 64 * OCC_WAVES;
 
@@ -791,7 +794,7 @@ __global__ __launch_bounds__(OCC_THREADS, 1) void dkdv_occ_kernel(
   using Geo = DkdvGeom<D>;
   constexpr int KS = Geo::KS, DB = Geo::DB, RED_PITCH = Geo::RED_PITCH;
   constexpr int TILE_BYTES = Geo::TILE_BYTES, BUF_BYTES = Geo::BUF_BYTES;
-  constexpr int VT_BYTES = TILE * D * (int)sizeof(bf16);
+  constexpr int VT_BYTES = 2 * TILE * D * (int)sizeof(bf16);   // K and V tiles
   constexpr size_t LDS_BYTES = (size_t)VT_BYTES + (size_t)OCC_WAVES * BUF_BYTES;
   static_assert(LDS_BYTES <= 160 * 1024, "staging must fit in LDS");
   static_assert((size_t)OCC_WAVES * TILE * RED_PITCH * sizeof(float) <= LDS_BYTES,
@@ -821,19 +824,21 @@ __global__ __launch_bounds__(OCC_THREADS, 1) void dkdv_occ_kernel(
   const size_t qstride = (size_t)Hq * D;
   const size_t kstride = (size_t)Hkv * D;
 
-  const bf16* Vt = reinterpret_cast<const bf16*>(smem);
+  const bf16* Kt = reinterpret_cast<const bf16*>(smem);
+  const bf16* Vt = Kt + TILE * D;
   char* wb = smem + VT_BYTES + (size_t)wave * BUF_BYTES;
   const bf16* Qs = reinterpret_cast<const bf16*>(wb);
   const bf16* Ds = reinterpret_cast<const bf16*>(wb + TILE_BYTES);
   const float* st = reinterpret_cast<const float*>(wb + 2 * TILE_BYTES);
   const uint32_t lds_wb = lds_address(wb);
 
-  // V rows of the key tile: wave w loads rows 4w .. 4w + 3 (1 KB)
+  // K and V rows of the key tile: wave w loads rows 4w .. 4w + 3 (1 KB each)
   {
     const int r = TileLoad<D>::RPD * wave + lane / TileLoad<D>::CPR;
     const uint32_t off = (uint32_t)min(k0 + r, T - 1) * (uint32_t)(kstride * sizeof(bf16)) +
                          TileLoad<D>::chunk_offset(lane, r);
-    dma16(v + (size_t)g * D, off, lds_address(smem) + (uint32_t)(wave * 1024));
+    dma16(k + (size_t)g * D, off, lds_address(smem) + (uint32_t)(wave * 1024));
+    dma16(v + (size_t)g * D, off, lds_address(smem) + (uint32_t)(TILE * D * sizeof(bf16) + wave * 1024));
   }
 
   const uint32_t rstride = (uint32_t)(qstride * sizeof(bf16));
@@ -867,14 +872,6 @@ __global__ __launch_bounds__(OCC_THREADS, 1) void dkdv_occ_kernel(
 
   // K^T as the B operand of S: lane holds k[k0 + lq][16 ks + 8 lh + 0..7]
   const int krow = k0 + lq;
-  bf16x8 kf[KS];
-  {
-    const size_t off = (size_t)min(krow, T - 1) * kstride + (size_t)g * D + lh * 8;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kf[ks] = as_bf16x8(ldg16(k + off + ks * 16));
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(kf[ks]));
-  }
   f32x16 dka[DB], dva[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
@@ -885,7 +882,7 @@ __global__ __launch_bounds__(OCC_THREADS, 1) void dkdv_occ_kernel(
   const int vis_hi = window > 0 ? min(b - 1, krow + window - 1) : b - 1;
   const int mbias = (kvalid ? 0 : -(1 << 30)) + 4 * lh - krow;
   const uint32_t mspan = kvalid ? (uint32_t)(vis_hi - krow) : 0u;
-  // the V tile (every wave's rows) is in LDS after the barrier
+  // the K and V tiles (every wave's rows) are in LDS after the barrier
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
@@ -901,28 +898,60 @@ __global__ __launch_bounds__(OCC_THREADS, 1) void dkdv_occ_kernel(
       s[4 * j + 0] = a4.x; s[4 * j + 1] = a4.y; s[4 * j + 2] = a4.z; s[4 * j + 3] = a4.w;
       dp[4 * j + 0] = b4.x; dp[4 * j + 1] = b4.y; dp[4 * j + 2] = b4.z; dp[4 * j + 3] = b4.w;
     }
+    {
+      // operand reads run two k-steps ahead of the products (ring of 3)
+      bf16x8 ring[3][4];
+      auto load = [&](int ks, bf16x8* r) {
+        r[0] = swz_frag_cols<D>(Qs, ks, lane);
+        r[1] = swz_frag_cols<D>(Kt, ks, lane);
+        r[2] = swz_frag_cols<D>(Ds, ks, lane);
+        r[3] = swz_frag_cols<D>(Vt, ks, lane);
+      };
+      load(0, ring[0]);
+      load(1, ring[1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s = mfma32(swz_frag_cols<D>(Qs, ks, lane), kf[ks], s);
-      dp = mfma32(swz_frag_cols<D>(Ds, ks, lane), swz_frag_cols<D>(Vt, ks, lane), dp);
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 2 < KS) load(ks + 2, ring[(ks + 2) % 3]);
+        s = mfma32(ring[ks % 3][0], ring[ks % 3][1], s);
+        dp = mfma32(ring[ks % 3][2], ring[ks % 3][3], dp);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     const int x0 = k0 + ci * QBLK + mbias;
+    bf16x8 pf[2], dsf[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      bf16x8 pf, dsf;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int r = 8 * t + e;
         const bool vis = (uint32_t)(x0 + 8 * (r >> 2) + (r & 3)) <= mspan;
         float p = exp2_fast(s[r] * scale_log2);
         p = vis ? p : 0.f;
-        pf[e] = (bf16)p;
-        dsf[e] = (bf16)(p * dp[r]);
+        pf[t][e] = (bf16)p;
+        dsf[t][e] = (bf16)(p * dp[r]);
       }
+    {
+      // the 16 dV/dK products, their transposing reads four products ahead
+      constexpr int NP = 4 * DB;   // products: (t, db, dV or dK)
+      constexpr int AHEAD = 4;
+      bf16x8 ring[AHEAD + 1];
+      auto load = [&](int m) {
+        const int t = m / (2 * DB), db = (m >> 1) % DB;
+        return swz_frag_rows<D>((m & 1) ? Qs : Ds, db * 32, t, lane);
+      };
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        dva[db] = mfma32(pf, swz_frag_rows<D>(Ds, db * 32, t, lane), dva[db]);
-        dka[db] = mfma32(dsf, swz_frag_rows<D>(Qs, db * 32, t, lane), dka[db]);
+      for (int m = 0; m < AHEAD; ++m) ring[m] = load(m);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int m = 0; m < NP; ++m) {
+        if (m + AHEAD < NP) ring[(m + AHEAD) % (AHEAD + 1)] = load(m + AHEAD);
+        const int t = m / (2 * DB), db = (m >> 1) % DB;
+        if (m & 1)
+          dka[db] = mfma32(dsf[t], ring[m % (AHEAD + 1)], dka[db]);
+        else
+          dva[db] = mfma32(pf[t], ring[m % (AHEAD + 1)], dva[db]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // every read of this wave's buffer has returned (the products above
