@@ -150,10 +150,28 @@ __global__ __launch_bounds__(BWD_THREADS, BlockGeom<D>::MIN_WG) void dq_kernel(
     for (int h2 = 0; h2 < H2; ++h2) {
       s[h2] = zero_f32x16();
       dp[h2] = zero_f32x16();
+    }
+    {
+      // K / V fragment reads run AHEAD products ahead of the products that
+      // use them (a register ring; the fences keep the compiler from sinking them)
+      constexpr int NP = 2 * H2 * KS, AHEAD = 2;
+      bf16x8 ring[AHEAD + 1];
+      auto load = [&](int m) {
+        const int h2 = m / (2 * KS), ks = (m >> 1) % KS;
+        return swz_frag_cols<D>(((m & 1) ? Vs : Ks) + h2 * 32 * D, ks, lane);
+      };
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s[h2] = mfma32(swz_frag_cols<D>(Ks + h2 * 32 * D, ks, lane), qf[ks], s[h2]);
-        dp[h2] = mfma32(swz_frag_cols<D>(Vs + h2 * 32 * D, ks, lane), df[ks], dp[h2]);
+      for (int m = 0; m < AHEAD; ++m) ring[m] = load(m);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int m = 0; m < NP; ++m) {
+        if (m + AHEAD < NP) ring[(m + AHEAD) % (AHEAD + 1)] = load(m + AHEAD);
+        const int h2 = m / (2 * KS), ks = (m >> 1) % KS;
+        if (m & 1)
+          dp[h2] = mfma32(ring[m % (AHEAD + 1)], df[ks], dp[h2]);
+        else
+          s[h2] = mfma32(ring[m % (AHEAD + 1)], qf[ks], s[h2]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // dS^T = P^T (dP^T - D), computed for every element; blocks that cross
@@ -189,11 +207,20 @@ __global__ __launch_bounds__(BWD_THREADS, BlockGeom<D>::MIN_WG) void dq_kernel(
 #pragma unroll
     for (int x = 0; x < H2 * 16; ++x) dsf[x >> 3][x & 7] = (bf16)dsv[x];
     // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q]
+    {
+      constexpr int NP = 2 * H2 * DB, AHEAD = 2;
+      bf16x8 ring[AHEAD + 1];
+      auto load = [&](int m) { return swz_frag_rows<D>(Ks, (m % DB) * 32, m / DB, lane); };
 #pragma unroll
-    for (int t = 0; t < 2 * H2; ++t)
+      for (int m = 0; m < AHEAD; ++m) ring[m] = load(m);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        acc[db] = mfma32(swz_frag_rows<D>(Ks, db * 32, t, lane), dsf[t], acc[db]);
+      for (int m = 0; m < NP; ++m) {
+        if (m + AHEAD < NP) ring[(m + AHEAD) % (AHEAD + 1)] = load(m + AHEAD);
+        acc[m % DB] = mfma32(ring[m % (AHEAD + 1)], dsf[m / DB], acc[m % DB]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 

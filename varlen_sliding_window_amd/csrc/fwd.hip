@@ -122,16 +122,29 @@ __global__ __launch_bounds__(FWD_THREADS, BlockGeom<D>::MIN_WG) void fwd_kernel(
     const bf16* Vs = Ks + KB * D;
 
     // S^T for keys kb + 32 h2 + [0, 32): s[h2][r] = q[qrow] . k[kb + 32 h2 + 8(r/4) + 4 lh + r%4]
-    bf16x8 kfr[H2 * KS];
-#pragma unroll
-    for (int x = 0; x < H2 * KS; ++x) kfr[x] = swz_frag_cols<D>(Ks + (x / KS) * 32 * D, x % KS, lane);
     f32x16 s[H2];
 #pragma unroll
     for (int h2 = 0; h2 < H2; ++h2) s[h2] = zero_f32x16();
+    {
+      // K fragment reads run AHEAD products ahead of the products that use
+      // them (a register ring; the fences keep the compiler from sinking them)
+      constexpr int NP = H2 * KS, AHEAD = 6;
+      bf16x8 ring[AHEAD + 1];
+      auto load = [&](int m) {
+        const int ks = m / H2, h2 = m % H2;
+        return swz_frag_cols<D>(Ks + h2 * 32 * D, ks, lane);
+      };
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+      for (int m = 0; m < AHEAD; ++m) ring[m] = load(m);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int h2 = 0; h2 < H2; ++h2) s[h2] = mfma32(kfr[h2 * KS + ks], qf[ks], s[h2]);
+      for (int m = 0; m < NP; ++m) {
+        if (m + AHEAD < NP) ring[(m + AHEAD) % (AHEAD + 1)] = load(m + AHEAD);
+        const int ks = m / H2, h2 = m % H2;
+        s[h2] = mfma32(ring[m % (AHEAD + 1)], qf[ks], s[h2]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
     if constexpr (CAP) {
       tanh_fragments<H2>(s, cap_a, TANH_NARROW / cap_a);
 #pragma unroll
