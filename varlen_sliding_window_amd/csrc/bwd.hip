@@ -15,15 +15,19 @@
 //   forms D = rowsum(dO * O) for its rows (fp32) and writes -lse/scale and
 //   -D per row to the workspace for the dK/dV kernel, which runs next on the
 //   same stream and seeds its S and dP accumulators with them.
-// dK/dV kernel: one work-group per (k-tile of 32 keys, key-value head); its
-//   4 waves take the group's query heads (wave w: heads w, w + 4, ...).  K
-//   and V stay in registers; each wave streams its head's Q/dO rows through
-//   its own double-buffered LDS slice in QBLK = 32-row steps (direct
-//   global-to-LDS loads one step ahead) and keeps dK/dV partial sums in fp32
-//   registers.  The loop is software-pipelined: the softmax of one step runs
-//   between the S/dP products of the next.  The 4 partials are added in a
-//   fixed order through LDS at the end, so the head-group reduction needs no
-//   atomics and is bit-for-bit reproducible.
+// dK/dV kernels: one work-group per (k-tile of 32 keys, key-value head); its
+//   waves take the group's query heads and stream each head's Q/dO rows
+//   through LDS in QBLK = 32-row steps (direct global-to-LDS loads), keeping
+//   dK/dV partial sums in fp32 registers; the partials are added in a fixed
+//   order through LDS at the end, so the head-group reduction needs no
+//   atomics and is bit-for-bit reproducible.  Three variants by head dim:
+//   D = 64, dkdv_kernel: 4 waves (wave w: heads w, w + 4, ...), K and V in
+//     registers, each wave's Q/dO double-buffered and loaded one step ahead,
+//     software-pipelined (the softmax of one step runs between the S/dP
+//     products of the next);
+//   D = 128, dkdv_occ_kernel: 8 waves, two per SIMD (a wave per head and
+//     q-block parity), K and V shared in LDS, one Q/dO buffer per wave;
+//   D = 256, dkdv_split_kernel: pairs of waves split the head dim.
 //
 // Logit soft-cap (the CAP instantiations): with t = tanh(scale qk / c) the
 // softmax sees c t, so P = exp2(c log2(e) t - lse log2(e)), and dS picks up
@@ -254,8 +258,10 @@ struct DkdvGeom {
                 "reduction buffer must fit in the staging buffers");
 };
 
-// At D = 64 the uncapped kernel fits 256 registers, so two work-groups
-// share a CU and each hides the other's start-up and load latency.
+// Used at D = 64 (at D = 128 its software pipeline needs 447 registers per
+// wave, one wave per SIMD; dkdv_occ_kernel below runs two).  At D = 64 the
+// uncapped kernel fits 256 registers, so two work-groups share a CU and each
+// hides the other's start-up and load latency.
 template <int D, bool CAP>
 __global__ __launch_bounds__(BWD_THREADS, (D == 64 && !CAP) ? 2 : 1) void dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -795,10 +801,10 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_split_kernel(
   }
 }
 
-// dK/dV at head dim 128 without a cap, with two waves per SIMD: 8 waves
-// per work-group, wave w taking query head w % 4 (+ 4 j) and the q-blocks of
-// parity w / 4.  The kernel above needs 447 registers per wave for its
-// software pipeline; this one fits 256 by giving that up: the key tile's K
+// dK/dV at head dim 128 with two waves per SIMD: 8 waves per work-group,
+// wave w taking query head w % 4 (+ 4 j) and the q-blocks of parity w / 4.
+// The kernel above would need 447 registers per wave at this head dim for
+// its software pipeline; this one fits 256 by giving that up: the key tile's K
 // and V rows are staged once per work-group in LDS and shared by the 8
 // waves, and each wave's Q/dO block has a single LDS buffer, so while one
 // wave waits for its next block the other wave on its SIMD computes.  Inside
@@ -809,14 +815,13 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_split_kernel(
 constexpr int OCC_WAVES = 8;
 constexpr int OCC_THREADS = 64 * OCC_WAVES;
 
+template <bool CAP>
 __global__ __launch_bounds__(OCC_THREADS, 1) void dkdv_occ_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const TileStats* __restrict__ stats, int tile_cap,
     const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
     int window, float scale_log2, float scale, float cap_a, float cap_c2, int run_len,
     bf16* __restrict__ dk, bf16* __restrict__ dv) {
-  (void)cap_a;
-  (void)cap_c2;
   constexpr int D = 128;
   using Geo = DkdvGeom<D>;
   constexpr int KS = Geo::KS, DB = Geo::DB, RED_PITCH = Geo::RED_PITCH;
@@ -916,13 +921,18 @@ __global__ __launch_bounds__(OCC_THREADS, 1) void dkdv_occ_kernel(
   int ci = par;   // q-block of the current step
   for (int it = 0; it < steps; ++it) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    // S and dP seeded with -lse/scale and -D of the step's rows
+    // S and dP seeded with -lse/scale and -D of the step's rows (with a cap,
+    // S starts at zero and -lse log2(e) is read back from LDS for P below)
     f32x16 s, dp;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float4 a4 = *reinterpret_cast<const float4*>(st + 8 * j + 4 * lh);
       const float4 b4 = *reinterpret_cast<const float4*>(st + TILE + 8 * j + 4 * lh);
-      s[4 * j + 0] = a4.x; s[4 * j + 1] = a4.y; s[4 * j + 2] = a4.z; s[4 * j + 3] = a4.w;
+      if constexpr (CAP) {
+        s[4 * j + 0] = 0.f; s[4 * j + 1] = 0.f; s[4 * j + 2] = 0.f; s[4 * j + 3] = 0.f;
+      } else {
+        const float4 a4 = *reinterpret_cast<const float4*>(st + 8 * j + 4 * lh);
+        s[4 * j + 0] = a4.x; s[4 * j + 1] = a4.y; s[4 * j + 2] = a4.z; s[4 * j + 3] = a4.w;
+      }
       dp[4 * j + 0] = b4.x; dp[4 * j + 1] = b4.y; dp[4 * j + 2] = b4.z; dp[4 * j + 3] = b4.w;
     }
     {
@@ -945,6 +955,7 @@ __global__ __launch_bounds__(OCC_THREADS, 1) void dkdv_occ_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    if constexpr (CAP) tanh_fragments<1>(&s, cap_a, TANH_NARROW / cap_a);
     const int x0 = k0 + ci * QBLK + mbias;
     bf16x8 pf[2], dsf[2];
 #pragma unroll
@@ -953,10 +964,19 @@ __global__ __launch_bounds__(OCC_THREADS, 1) void dkdv_occ_kernel(
       for (int e = 0; e < 8; ++e) {
         const int r = 8 * t + e;
         const bool vis = (uint32_t)(x0 + 8 * (r >> 2) + (r & 3)) <= mspan;
-        float p = exp2_fast(s[r] * scale_log2);
-        p = vis ? p : 0.f;
-        pf[t][e] = (bf16)p;
-        dsf[t][e] = (bf16)(p * dp[r]);
+        if constexpr (CAP) {
+          const float th = s[r];
+          const float ls = st[8 * (r >> 2) + 4 * lh + (r & 3)];   // -lse log2(e)
+          float p = exp2_fast(cap_c2 * th + ls);
+          p = vis ? p : 0.f;
+          pf[t][e] = (bf16)p;
+          dsf[t][e] = (bf16)(p * dp[r] * (1.f - th * th));
+        } else {
+          float p = exp2_fast(s[r] * scale_log2);
+          p = vis ? p : 0.f;
+          pf[t][e] = (bf16)p;
+          dsf[t][e] = (bf16)(p * dp[r]);
+        }
       }
     {
       // the 16 dV/dK products, their transposing reads four products ahead
@@ -1056,12 +1076,18 @@ void launch_dkdv_kernel(const void* q, const void* k, const void* v, const void*
   const size_t round = 8 * (size_t)run_len;
   const unsigned grid = (unsigned)((items + round - 1) / round * round);
   const CapConstants cc = cap_constants(p);
-  // head dim 256: pairs of waves split the head dim; 128 uncapped: two waves
-  // per SIMD; otherwise the software-pipelined kernel
-  constexpr bool occ = D == 128 && !CAP;
-  auto kernel = D == 256 ? dkdv_split_kernel<CAP>
-                : occ    ? dkdv_occ_kernel
-                         : dkdv_kernel<D == 256 ? 128 : D, CAP>;
+  // head dim 256: pairs of waves split the head dim; 128: two waves per
+  // SIMD; 64: the software-pipelined kernel
+  constexpr bool occ = D == 128;
+  void (*kernel)(const bf16*, const bf16*, const bf16*, const bf16*, const TileStats*, int,
+                 const int*, const Tile*, int, int, int, int, float, float, float, float, int,
+                 bf16*, bf16*);
+  if constexpr (D == 256)
+    kernel = dkdv_split_kernel<CAP>;
+  else if constexpr (D == 128)
+    kernel = dkdv_occ_kernel<CAP>;
+  else
+    kernel = dkdv_kernel<D, CAP>;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(occ ? OCC_THREADS : BWD_THREADS), 0, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                      static_cast<const bf16*>(v), static_cast<const bf16*>(dout),
