@@ -149,80 +149,74 @@ __global__ __launch_bounds__(BWD_THREADS, BlockGeom<D>::MIN_WG) void dq_kernel(
     const bf16* Ks = reinterpret_cast<const bf16*>(smem + buf * Geo::BUF_BYTES);
     const bf16* Vs = Ks + KB * D;
 
-    f32x16 s[H2], dp[H2];
+    // One 32-key half of the block at a time: its S/dP products, dS, then its
+    // share of dQ (fewer live registers, so the operand reads can run
+    // further ahead of the products).
+    const bool full = (kb + KB - 1 <= q0) && (kb >= full_lo);
 #pragma unroll
     for (int h2 = 0; h2 < H2; ++h2) {
-      s[h2] = zero_f32x16();
-      dp[h2] = zero_f32x16();
-    }
-    {
-      // K / V fragment reads run AHEAD products ahead of the products that
-      // use them (a register ring; the fences keep the compiler from sinking them)
-      constexpr int NP = 2 * H2 * KS, AHEAD = 2;
-      bf16x8 ring[AHEAD + 1];
-      auto load = [&](int m) {
-        const int h2 = m / (2 * KS), ks = (m >> 1) % KS;
-        return swz_frag_cols<D>(((m & 1) ? Vs : Ks) + h2 * 32 * D, ks, lane);
-      };
+      f32x16 s = zero_f32x16(), dp = zero_f32x16();
+      {
+        constexpr int NP = 2 * KS, AHEAD = 4;
+        bf16x8 ring[AHEAD + 1];
+        auto load = [&](int m) {
+          return swz_frag_cols<D>(((m & 1) ? Vs : Ks) + h2 * 32 * D, m >> 1, lane);
+        };
 #pragma unroll
-      for (int m = 0; m < AHEAD; ++m) ring[m] = load(m);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int m = 0; m < NP; ++m) {
-        if (m + AHEAD < NP) ring[(m + AHEAD) % (AHEAD + 1)] = load(m + AHEAD);
-        const int h2 = m / (2 * KS), ks = (m >> 1) % KS;
-        if (m & 1)
-          dp[h2] = mfma32(ring[m % (AHEAD + 1)], df[ks], dp[h2]);
-        else
-          s[h2] = mfma32(ring[m % (AHEAD + 1)], qf[ks], s[h2]);
+        for (int m = 0; m < AHEAD; ++m) ring[m] = load(m);
         __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < NP; ++m) {
+          if (m + AHEAD < NP) ring[(m + AHEAD) % (AHEAD + 1)] = load(m + AHEAD);
+          if (m & 1)
+            dp = mfma32(ring[m % (AHEAD + 1)], df[m >> 1], dp);
+          else
+            s = mfma32(ring[m % (AHEAD + 1)], qf[m >> 1], s);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-    }
-    // dS^T = P^T (dP^T - D), computed for every element; blocks that cross
-    // the diagonal, the window edge or the segment start then zero the
-    // invisible elements with selects (so values there, even NaNs, drop out).
-    const bool full = (kb + KB - 1 <= q0) && (kb >= full_lo);
-    float dsv[H2 * 16];
-    if constexpr (CAP) {
-      // one 32-key half at a time (both at once would exceed 256 registers)
+      // dS^T = P^T (dP^T - D) for every element; on blocks that cross the
+      // diagonal, the window edge or the segment start, selects zero the
+      // invisible elements (so values there, even NaNs, drop out).
+      if constexpr (CAP) tanh_fragments<1>(&s, cap_a, TANH_NARROW / cap_a);
+      float dsv[16];
 #pragma unroll
-      for (int h2 = 0; h2 < H2; ++h2) tanh_fragments<1>(&s[h2], cap_a, TANH_NARROW / cap_a);
-    }
-#pragma unroll
-    for (int x = 0; x < H2 * 16; ++x) {
-      if constexpr (CAP) {
-        const float t = s[x >> 4][x & 15];
-        const float p = exp2_fast(cap_c2 * t - lse2);
-        dsv[x] = p * (dp[x >> 4][x & 15] - Dv) * (1.f - t * t);
-      } else {
-        const float p = exp2_fast(s[x >> 4][x & 15] * scale_log2 - lse2);
-        dsv[x] = p * (dp[x >> 4][x & 15] - Dv);
+      for (int r = 0; r < 16; ++r) {
+        if constexpr (CAP) {
+          const float t = s[r];
+          const float p = exp2_fast(cap_c2 * t - lse2);
+          dsv[r] = p * (dp[r] - Dv) * (1.f - t * t);
+        } else {
+          const float p = exp2_fast(s[r] * scale_log2 - lse2);
+          dsv[r] = p * (dp[r] - Dv);
+        }
       }
-    }
-    if (!full) {
+      if (!full) {
 #pragma unroll
-      for (int x = 0; x < H2 * 16; ++x) {
-        const int r = x & 15;
-        const int key = kb + (x >> 4) * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
-        dsv[x] = ((key >= my_lo) & (key <= qrow)) ? dsv[x] : 0.f;
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb + h2 * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
+          dsv[r] = ((key >= my_lo) & (key <= qrow)) ? dsv[r] : 0.f;
+        }
       }
-    }
-    bf16x8 dsf[2 * H2];
+      bf16x8 dsf[2];
 #pragma unroll
-    for (int x = 0; x < H2 * 16; ++x) dsf[x >> 3][x & 7] = (bf16)dsv[x];
-    // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q]
-    {
-      constexpr int NP = 2 * H2 * DB, AHEAD = 2;
-      bf16x8 ring[AHEAD + 1];
-      auto load = [&](int m) { return swz_frag_rows<D>(Ks, (m % DB) * 32, m / DB, lane); };
+      for (int r = 0; r < 16; ++r) dsf[r >> 3][r & 7] = (bf16)dsv[r];
+      // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q] over this half's keys
+      {
+        constexpr int NP = 2 * DB, AHEAD = 4;
+        bf16x8 ring[AHEAD + 1];
+        auto load = [&](int m) {
+          return swz_frag_rows<D>(Ks, (m % DB) * 32, 2 * h2 + m / DB, lane);
+        };
 #pragma unroll
-      for (int m = 0; m < AHEAD; ++m) ring[m] = load(m);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int m = 0; m < NP; ++m) {
-        if (m + AHEAD < NP) ring[(m + AHEAD) % (AHEAD + 1)] = load(m + AHEAD);
-        acc[m % DB] = mfma32(ring[m % (AHEAD + 1)], dsf[m / DB], acc[m % DB]);
+        for (int m = 0; m < AHEAD; ++m) ring[m] = load(m);
         __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < NP; ++m) {
+          if (m + AHEAD < NP) ring[(m + AHEAD) % (AHEAD + 1)] = load(m + AHEAD);
+          acc[m % DB] = mfma32(ring[m % (AHEAD + 1)], dsf[m / DB], acc[m % DB]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
   }
