@@ -41,7 +41,8 @@
  *                      (research.dws.rip/llm/kernels, section 06 "CUDA
  *                      graphs work, with padding")
  *   max_seqlen       : >= the longest segment (used to bound the schedule)
- *   supported shapes : D == 128, Hq % Hkv == 0 and (Hq / Hkv) % 4 == 0
+ *   supported shapes : D in {64, 128, 256}, Hq % Hkv == 0, (Hq / Hkv) % 4 == 0,
+ *                      and k (T x Hkv x D bf16) under 4 GiB
  *
  * Execution
  *   Every call enqueues its kernels on `stream` and returns without waiting
@@ -68,7 +69,7 @@ extern "C" {
 typedef enum {
   ATTN_OK = 0,
   ATTN_EINVAL = -1,       /* null/misaligned pointer, bad size, bad scale, ... */
-  ATTN_EUNSUPPORTED = -2, /* valid arguments this build does not implement (D != 128, group % 4) */
+  ATTN_EUNSUPPORTED = -2, /* valid arguments this build does not implement (D, group % 4, k >= 4 GiB) */
   ATTN_EWORKSPACE = -3,   /* workspace null or smaller than attn_varlen_workspace_size() */
   ATTN_EDEVICE = -4,      /* no usable gfx950 device / HIP runtime error before launch */
   ATTN_ELAUNCH = -5       /* a kernel launch failed */

@@ -52,6 +52,10 @@ def test_workspace_size(lib):
     assert attn.workspace_size(0, 1, 8, 2, 128, 1, 0) == 0               # T = 0
     assert attn.workspace_size(100, 1, 8, 3, 128, 100, 0) == 0           # Hq % Hkv
     assert attn.workspace_size(100, 1, 8, 2, 128, 101, 0) == 0           # max_seqlen > T
+    # k of T x Hkv x D bf16 must stay under 4 GiB (32-bit row offsets)
+    assert attn.workspace_size((1 << 23) - 1, 1, 16, 2, 128, 4096, 0) > 0   # 4 GiB - 512 B
+    assert attn.workspace_size(1 << 23, 1, 16, 2, 128, 4096, 0) == 0         # 4 GiB
+    assert attn.workspace_size(1 << 22, 1, 32, 8, 256, 4096, 0) == 0     # 16 GiB
 
 
 FAKE = 1 << 20  # aligned, never dereferenced: every case below fails validation first

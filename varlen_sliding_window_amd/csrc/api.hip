@@ -50,6 +50,10 @@ attn_status check_shape(int32_t total_tokens, int32_t num_seqs, int32_t num_q_he
   // grid sizes must fit in 32 bits
   const size_t cap = attn::tile_capacity(total_tokens, num_seqs);
   if (cap * (size_t)num_q_heads >= (size_t)1 << 31) return ATTN_EUNSUPPORTED;
+  // the kernels address k and v rows with 32-bit byte offsets from a
+  // key-value head's first row
+  if ((size_t)total_tokens * (size_t)num_kv_heads * (size_t)head_dim * 2 > (size_t)UINT32_MAX)
+    return ATTN_EUNSUPPORTED;
   return ATTN_OK;
 }
 
