@@ -3,8 +3,8 @@
 Test infrastructure: only tests/, the smoke check and the bench's CPU
 baseline may import it.  The product path never does.
 """
-from .attention import (attention_backward, attention_forward, attention_row, segments,
-                        visible_mask)
+from .attention import (attention_backward, attention_forward, attention_key, attention_row,
+                        segments, visible_mask)
 
-__all__ = ["attention_backward", "attention_forward", "attention_row", "segments",
-           "visible_mask"]
+__all__ = ["attention_backward", "attention_forward", "attention_key", "attention_row",
+           "segments", "visible_mask"]

@@ -193,3 +193,47 @@ def attention_row(q, k, v, dout, cu_seqlens, window: int, scale: float, h: int, 
     dp = vs @ doi
     ds = p * (dp - p @ dp) * dcap
     return o, m + np.log(z), scale * (ds @ ks)
+
+
+def attention_key(q, k, v, dout, cu_seqlens, window: int, scale: float, g: int, j: int,
+                  softcap: float = 0.0):
+    """One key's gradients, computed alone: (dk_jg [d], dv_jg [d]).
+
+    The column counterpart of attention_row: the same definitions restricted
+    to the queries i that see key j (j in V(i)), each with its whole row
+    softmax, summed over the query heads of key-value head g.  Used to check
+    sampled dK/dV entries of problems too large for the whole oracle.
+    """
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    s_idx = int(np.searchsorted(cu, j, side="right")) - 1
+    a, b = int(cu[s_idx]), int(cu[s_idx + 1])
+    hi = min(b - 1, j + window - 1) if window > 0 else b - 1
+    rows = np.arange(j, hi + 1)                     # queries that see key j
+    lo = np.maximum(a, rows - window + 1) if window > 0 else np.full_like(rows, a)
+    keys = np.arange(int(lo.min()), hi + 1)
+    mask = (keys[None, :] >= lo[:, None]) & (keys[None, :] <= rows[:, None])
+    group = q.shape[1] // k.shape[1]
+    kk = np.asarray(k[keys, g], dtype=np.float64)
+    vv = np.asarray(v[keys, g], dtype=np.float64)
+    col = j - int(keys[0])
+    dk = np.zeros(k.shape[2])
+    dv = np.zeros(k.shape[2])
+    for h in range(g * group, (g + 1) * group):
+        qs = np.asarray(q[rows, h], dtype=np.float64)
+        dos = np.asarray(dout[rows, h], dtype=np.float64)
+        s = scale * (qs @ kk.T)
+        dcap = np.ones_like(s)
+        if softcap > 0:
+            t = np.tanh(s / softcap)
+            s = softcap * t
+            dcap = 1.0 - t * t
+        s = np.where(mask, s, -np.inf)
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        p = e / e.sum(axis=1, keepdims=True)
+        dp = dos @ vv.T
+        dd = (p * dp).sum(axis=1, keepdims=True)
+        ds = p * (dp - dd) * dcap
+        dk += scale * (ds[:, col] @ qs)
+        dv += p[:, col] @ dos
+    return dk, dv

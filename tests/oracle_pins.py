@@ -421,6 +421,18 @@ def pin_softcap_row_function(o):
             _close(rdq, dq[i, h], 1e-12, "cap row dq")
 
 
+def pin_key_function(o):
+    """The single-key function equals the full oracle's dk, dv rows (with and
+    without a window and a cap), for keys at segment starts, ends and inside."""
+    q, k, v, do = rand_inputs(19, CU_MIXED, 4, 2, 8, 1.5)
+    for w, cap in ((0, 0.0), (3, 0.0), (4, 1.25)):
+        _, dk, dv, *_ = o.attention_backward(q, k, v, do, CU_MIXED, w, 0.3, cap)
+        for g, j in ((0, 0), (1, 5), (0, 6), (1, 12), (0, 13), (1, 14), (0, 28), (1, 36)):
+            rk, rv = o.attention_key(q, k, v, do, CU_MIXED, w, 0.3, g, j, cap)
+            _close(rk, dk[j, g], 1e-12, f"key dk (W={w}, cap={cap}, j={j})")
+            _close(rv, dv[j, g], 1e-12, f"key dv (W={w}, cap={cap}, j={j})")
+
+
 ALL_PINS = [
     pin_golden,
     pin_rows_sum_to_one,
@@ -434,6 +446,7 @@ ALL_PINS = [
     pin_key_shift,
     pin_d_identity,
     pin_row_function,
+    pin_key_function,
     pin_torch_sdpa,
     pin_finite_differences,
     pin_softcap_two_keys,

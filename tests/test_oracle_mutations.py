@@ -19,8 +19,9 @@ MUTATIONS = [
     ("no window", "if window > 0:\n        m &=", "if window > 10**9:\n        m &="),
     ("scale missing in dq", "dq[a:b, h] = scale * (ds @ ks)", "dq[a:b, h] = ds @ ks"),
     ("scale missing in dk", "dk[a:b, g] += scale * (ds.T @ qs)", "dk[a:b, g] += ds.T @ qs"),
-    ("dS drops D", "ds = p * (dp - dd)", "ds = p * dp"),
-    ("dS wrong sign", "ds = p * (dp - dd)", "ds = p * (dd - dp)"),
+    ("dS drops D", "ds = p * (dp - dd) * dcap\n            dsum", "ds = p * dp * dcap\n            dsum"),
+    ("dS wrong sign", "ds = p * (dp - dd) * dcap\n            dsum",
+     "ds = p * (dd - dp) * dcap\n            dsum"),
     ("dk not summed over group", "dk[a:b, g] += scale", "dk[a:b, g] = scale"),
     ("dv not summed over group", "dv[a:b, g] += p.T @ dos", "dv[a:b, g] = p.T @ dos"),
     ("dv transposed P", "dv[a:b, g] += p.T @ dos", "dv[a:b, g] += p @ dos"),
@@ -36,13 +37,18 @@ MUTATIONS = [
     ("row window off by one", "lo = max(a, i - window + 1) if window > 0 else a",
      "lo = max(a, i - window) if window > 0 else a"),
     ("row dq drops D", "ds = p * (dp - p @ dp)", "ds = p * dp"),
-    ("cap derivative dropped", "ds = p * (dp - dd) * dcap", "ds = p * (dp - dd)"),
+    ("cap derivative dropped", "ds = p * (dp - dd) * dcap\n            dsum",
+     "ds = p * (dp - dd)\n            dsum"),
     ("cap derivative 1 - t", "return softcap * t, 1.0 - t * t", "return softcap * t, 1.0 - t"),
     ("cap on unscaled logits", "t = np.tanh(s / softcap)\n        return softcap * t",
      "t = np.tanh(s / scale / softcap)\n        return scale * softcap * t"),
     ("cap as hard clip", "t = np.tanh(s / softcap)\n        return softcap * t",
      "t = np.clip(s / softcap, -1.0, 1.0)\n        return softcap * t"),
     ("row cap derivative dropped", "ds = p * (dp - p @ dp) * dcap", "ds = p * (dp - p @ dp)"),
+    ("key window one too short", "hi = min(b - 1, j + window - 1) if window > 0 else b - 1",
+     "hi = min(b - 1, j + window - 2) if window > 0 else b - 1"),
+    ("key dS drops D", "ds = p * (dp - dd) * dcap\n        dk += scale", "ds = p * dp * dcap\n        dk += scale"),
+    ("key sums one head only", "for h in range(g * group, (g + 1) * group):", "for h in range(g * group, g * group + 1):"),
     ("row cap ignored", "    if softcap > 0:\n        t = np.tanh(s / softcap)\n        s = softcap * t",
      "    if softcap > 1e300:\n        t = np.tanh(s / softcap)\n        s = softcap * t"),
 ]
