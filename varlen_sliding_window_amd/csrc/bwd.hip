@@ -95,13 +95,44 @@ __global__ __launch_bounds__(BWD_THREADS, BlockGeom<D>::MIN_WG) void dq_kernel(
       dma16(vbase, off, l + Geo::TILE_BYTES + j * 1024);
     }
   };
+  // Q^T and dO^T as B operands; D from dO and O at the same positions.  Up
+  // to D = 128 a wave's 32 rows of Q fit in its quarter of the second K/V
+  // buffer: Q arrives there as whole-row direct loads (with the first
+  // block's and the lanes' loads of O) and is read out as fragments, then dO
+  // takes its place the same way.  The second round trip costs less than
+  // lanes loading dO row by row.  At D = 256 lanes load all three.
+  constexpr bool STAGE = RowTile<D>::BYTES * 4 <= Geo::BUF_BYTES;
+  auto wave_tile = [&](int b) {
+    return reinterpret_cast<bf16*>(smem + b * Geo::BUF_BYTES + wave * RowTile<D>::BYTES);
+  };
+  const size_t tile_off = (size_t)q0 * qstride + (size_t)head * D;
+  const uint32_t row_bytes = (uint32_t)(qstride * sizeof(bf16));
+  const int rows = min(TILE, T - q0);
+  if constexpr (STAGE) dma_tile_rows<D>(q + tile_off, row_bytes, rows, lds_address(wave_tile(1)), lane);
   issue(0, 0);
-
-  // Q^T and dO^T as B operands; D from dO and O at the same positions
   bf16x8 qf[KS], df[KS];
   float dpart = 0.f;
-  {
-    const size_t off = (size_t)qrow * qstride + (size_t)head * D + lh * 8;
+  const size_t off = (size_t)qrow * qstride + (size_t)head * D + lh * 8;
+  if constexpr (STAGE) {
+    bf16x8 ov[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) ov[ks] = qrow < T ? as_bf16x8(ldg16(out + off + ks * 16)) : zero_bf16x8();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = swz_frag_cols<D>(wave_tile(1), ks, lane);
+    // the Q reads are done before dO overwrites the tile
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    dma_tile_rows<D>(dout + tile_off, row_bytes, rows, lds_address(wave_tile(1)), lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      df[ks] = swz_frag_cols<D>(wave_tile(1), ks, lane);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dpart += (float)df[ks][e] * (float)ov[ks][e];
+    }
+  } else {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (qrow < T) {
@@ -115,11 +146,11 @@ __global__ __launch_bounds__(BWD_THREADS, BlockGeom<D>::MIN_WG) void dq_kernel(
         df[ks] = zero_bf16x8();
       }
     }
-    // Make the compiler wait for these loads here, not inside the loop where
-    // the wait would also cover the block loads in flight.
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]), "v"(df[ks]));
   }
+  // Make the compiler wait for these loads here, not inside the loop where
+  // the wait would also cover the block loads in flight.
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]), "v"(df[ks]));
   const float Dv = dpart + __shfl_xor(dpart, 32);
   const float lsev = qrow < T ? lse[(size_t)head * T + qrow] : 0.f;
   const float lse2 = lsev * LOG2E;
@@ -153,76 +184,91 @@ __global__ __launch_bounds__(BWD_THREADS, BlockGeom<D>::MIN_WG) void dq_kernel(
     // share of dQ (fewer live registers, so the operand reads can run
     // further ahead of the products).
     const bool full = (kb + KB - 1 <= q0) && (kb >= full_lo);
+    // S^T and dP^T of half h2
+    auto sdp = [&](int h2, f32x16& s, f32x16& dp) {
+      constexpr int NP = 2 * KS, AHEAD = 4;
+      bf16x8 ring[AHEAD + 1];
+      auto load = [&](int m) {
+        return swz_frag_cols<D>(((m & 1) ? Vs : Ks) + h2 * 32 * D, m >> 1, lane);
+      };
 #pragma unroll
-    for (int h2 = 0; h2 < H2; ++h2) {
-      f32x16 s = zero_f32x16(), dp = zero_f32x16();
-      {
-        constexpr int NP = 2 * KS, AHEAD = 4;
-        bf16x8 ring[AHEAD + 1];
-        auto load = [&](int m) {
-          return swz_frag_cols<D>(((m & 1) ? Vs : Ks) + h2 * 32 * D, m >> 1, lane);
-        };
+      for (int m = 0; m < AHEAD; ++m) ring[m] = load(m);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int m = 0; m < AHEAD; ++m) ring[m] = load(m);
+      for (int m = 0; m < NP; ++m) {
+        if (m + AHEAD < NP) ring[(m + AHEAD) % (AHEAD + 1)] = load(m + AHEAD);
+        if (m & 1)
+          dp = mfma32(ring[m % (AHEAD + 1)], df[m >> 1], dp);
+        else
+          s = mfma32(ring[m % (AHEAD + 1)], qf[m >> 1], s);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int m = 0; m < NP; ++m) {
-          if (m + AHEAD < NP) ring[(m + AHEAD) % (AHEAD + 1)] = load(m + AHEAD);
-          if (m & 1)
-            dp = mfma32(ring[m % (AHEAD + 1)], df[m >> 1], dp);
-          else
-            s = mfma32(ring[m % (AHEAD + 1)], qf[m >> 1], s);
-          __builtin_amdgcn_sched_barrier(0);
-        }
       }
-      // dS^T = P^T (dP^T - D) for every element; on blocks that cross the
-      // diagonal, the window edge or the segment start, selects zero the
-      // invisible elements (so values there, even NaNs, drop out).
+      // With a cap, s becomes tanh(S / c).  On blocks that cross the
+      // diagonal, the window edge or the segment start, invisible elements
+      // get dP = D and a logit whose P is finite (-inf without a cap, t = 0
+      // with one), so their dS below is exactly zero.
       if constexpr (CAP) tanh_fragments<1>(&s, cap_a, TANH_NARROW / cap_a);
-      float dsv[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if constexpr (CAP) {
-          const float t = s[r];
-          const float p = exp2_fast(cap_c2 * t - lse2);
-          dsv[r] = p * (dp[r] - Dv) * (1.f - t * t);
-        } else {
-          const float p = exp2_fast(s[r] * scale_log2 - lse2);
-          dsv[r] = p * (dp[r] - Dv);
-        }
-      }
       if (!full) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kb + h2 * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
-          dsv[r] = ((key >= my_lo) & (key <= qrow)) ? dsv[r] : 0.f;
+          const bool vis = (key >= my_lo) & (key <= qrow);
+          s[r] = vis ? s[r] : (CAP ? 0.f : -INFINITY);
+          dp[r] = vis ? dp[r] : Dv;
         }
       }
+    };
+    // dS^T = P^T (dP^T - D), elements r and r + 1
+    auto ds_pair = [&](int r, const f32x16& s, const f32x16& dp, bf16x8* dsf) {
+      float v[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        if constexpr (CAP) {
+          const float t = s[r + e];
+          const float p = exp2_fast(cap_c2 * t - lse2);
+          v[e] = p * (dp[r + e] - Dv) * (1.f - t * t);
+        } else {
+          const float p = exp2_fast(s[r + e] * scale_log2 - lse2);
+          v[e] = p * (dp[r + e] - Dv);
+        }
+      }
+      dsf[r >> 3][r & 7] = (bf16)v[0];
+      dsf[r >> 3][(r & 7) + 1] = (bf16)v[1];
+    };
+    // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q] over half h2's keys
+    auto dqp = [&](int h2, const bf16x8* dsf) {
+      constexpr int NP = 2 * DB, AHEAD = 3;
+      bf16x8 ring[AHEAD + 1];
+      auto load = [&](int m) { return swz_frag_rows<D>(Ks, (m % DB) * 32, 2 * h2 + m / DB, lane); };
+#pragma unroll
+      for (int m = 0; m < AHEAD; ++m) ring[m] = load(m);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int m = 0; m < NP; ++m) {
+        if (m + AHEAD < NP) ring[(m + AHEAD) % (AHEAD + 1)] = load(m + AHEAD);
+        acc[m % DB] = mfma32(ring[m % (AHEAD + 1)], dsf[m / DB], acc[m % DB]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+#pragma unroll
+    for (int h2 = 0; h2 < H2; ++h2) {
+      f32x16 s = zero_f32x16(), dp = zero_f32x16();
+      sdp(h2, s, dp);
       bf16x8 dsf[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dsf[r >> 3][r & 7] = (bf16)dsv[r];
-      // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q] over this half's keys
-      {
-        constexpr int NP = 2 * DB, AHEAD = 4;
-        bf16x8 ring[AHEAD + 1];
-        auto load = [&](int m) {
-          return swz_frag_rows<D>(Ks, (m % DB) * 32, 2 * h2 + m / DB, lane);
-        };
-#pragma unroll
-        for (int m = 0; m < AHEAD; ++m) ring[m] = load(m);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int m = 0; m < NP; ++m) {
-          if (m + AHEAD < NP) ring[(m + AHEAD) % (AHEAD + 1)] = load(m + AHEAD);
-          acc[m % DB] = mfma32(ring[m % (AHEAD + 1)], dsf[m / DB], acc[m % DB]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+      for (int r = 0; r < 16; r += 2) ds_pair(r, s, dp, dsf);
+      dqp(h2, dsf);
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  if (qrow < q1) {
+  if constexpr (STAGE) {
+    // Through the K/V buffer the last block did not use (idle since the
+    // last barrier): whole-row stores.
+    bf16* ot = wave_tile(nblk & 1);
+    stage_acc_rows<D>(ot, acc, scale, lane);
+    store_tile_rows<D>(dq + (size_t)q0 * qstride + (size_t)head * D, qstride, q1 - q0, ot, lane);
+  } else if (qrow < q1) {
     bf16* op = dq + (size_t)qrow * qstride + (size_t)head * D + lh * 4;
 #pragma unroll
     for (int db = 0; db < DB; ++db)

@@ -157,6 +157,65 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return (uint32_t)(uintptr_t)(lds_cchar*)p;
 }
 
+// One wave's tile of 32 rows of D bf16 (a q-tile of one head) moved between
+// global memory and a swizzled LDS tile with whole-row accesses: a 1 KB
+// direct load or a 1 KB store per instruction, instead of 32 rows touched by
+// every instruction when the rows go straight to or from MFMA fragments.
+template <int D>
+struct RowTile {
+  static constexpr int ROWS = 32;
+  static constexpr int BYTES = ROWS * D * (int)sizeof(bf16);
+  static constexpr int MOVES = ROWS / TileLoad<D>::RPD;   // 1 KB moves per tile
+};
+
+// Direct loads of tile rows [0, nrows) (1 <= nrows; rows past nrows repeat row
+// nrows - 1): tile row r is the global row at byte offset r * stride_b from
+// base.  The caller waits (s_waitcnt vmcnt) before reading the tile.
+template <int D>
+__device__ __forceinline__ void dma_tile_rows(const bf16* base, uint32_t stride_b, int nrows,
+                                              uint32_t lds, int lane) {
+#pragma unroll
+  for (int j = 0; j < RowTile<D>::MOVES; ++j) {
+    const int r = TileLoad<D>::RPD * j + lane / TileLoad<D>::CPR;
+    const uint32_t off = (uint32_t)min(r, nrows - 1) * stride_b + TileLoad<D>::chunk_offset(lane, r);
+    dma16(base, off, lds + j * 1024);
+  }
+}
+
+// Writes the wave's accumulator fragments acc[db] (lane l: row l % 32,
+// columns 32 db + 8(i/4) + 4(l/32) + i%4, see the D layout above), times
+// `scale`, as bf16 into a swizzled 32 x D LDS tile.
+template <int D>
+__device__ __forceinline__ void stage_acc_rows(bf16* tile, const f32x16* acc, float scale,
+                                               int lane) {
+  const int row = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = 4 * db + j;
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (bf16)(acc[db][4 * j + e] * scale);
+      *reinterpret_cast<bf16x4*>(tile + row * D + ((c ^ swz<D>(row)) << 3) + 4 * half) = v;
+    }
+}
+
+// Stores tile rows [0, nrows) of a swizzled 32 x D LDS tile to global rows
+// `stride` elements apart starting at base, 16 bytes per lane.  The tile is
+// the wave's own (LDS operations of one wave complete in order).
+template <int D>
+__device__ __forceinline__ void store_tile_rows(bf16* base, size_t stride, int nrows,
+                                                const bf16* tile, int lane) {
+#pragma unroll
+  for (int j = 0; j < RowTile<D>::MOVES; ++j) {
+    const int r = TileLoad<D>::RPD * j + lane / TileLoad<D>::CPR;
+    const int c = lane % TileLoad<D>::CPR;
+    const uint4 v = *reinterpret_cast<const uint4*>(tile + r * D + ((c ^ swz<D>(r)) << 3));
+    if (r < nrows) *reinterpret_cast<uint4*>(base + (size_t)r * stride + c * 8) = v;
+  }
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 

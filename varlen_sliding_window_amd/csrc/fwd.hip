@@ -88,11 +88,25 @@ __global__ __launch_bounds__(FWD_THREADS, BlockGeom<D>::MIN_WG) void fwd_kernel(
       dma16(vbase, off, l + Geo::TILE_BYTES + j * 1024);
     }
   };
-  issue(0, 0);
-
-  // Q^T as the B operand: lane holds q[qrow][16 ks + 8 lh + 0..7]
+  // Q^T as the B operand: lane holds q[qrow][16 ks + 8 lh + 0..7].  Up to
+  // D = 128 a wave's 32 q rows fit in its quarter of the second K/V buffer,
+  // so they arrive there as whole-row direct loads (ahead of the first
+  // block's) and are read out as fragments; at D = 256 lanes load them.
+  constexpr bool STAGE = RowTile<D>::BYTES * 4 <= Geo::BUF_BYTES;
+  auto wave_tile = [&](int b) {
+    return reinterpret_cast<bf16*>(smem + b * Geo::BUF_BYTES + wave * RowTile<D>::BYTES);
+  };
   bf16x8 qf[KS];
-  {
+  if constexpr (STAGE) {
+    dma_tile_rows<D>(q + (size_t)q0 * qstride + (size_t)head * D, (uint32_t)(qstride * sizeof(bf16)),
+                     min(TILE, T - q0), lds_address(wave_tile(1)), lane);
+    issue(0, 0);
+    // the Q rows have landed (the block's 2 * LOADS loads may still be in flight)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * Geo::LOADS) : "memory");
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = swz_frag_cols<D>(wave_tile(1), ks, lane);
+  } else {
+    issue(0, 0);
     const bf16* qp = q + (size_t)qrow * qstride + (size_t)head * D + lh * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = qrow < T ? as_bf16x8(ldg16(qp + ks * 16)) : zero_bf16x8();
@@ -203,8 +217,14 @@ __global__ __launch_bounds__(FWD_THREADS, BlockGeom<D>::MIN_WG) void fwd_kernel(
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   const float lt = lsum + __shfl_xor(lsum, 32);
-  if (qrow < q1) {
-    const float inv = 1.f / lt;
+  const float inv = 1.f / lt;
+  if constexpr (STAGE) {
+    // Through the K/V buffer the last block did not use (idle since the
+    // last barrier): whole-row stores.
+    bf16* ot = wave_tile(nblk & 1);
+    stage_acc_rows<D>(ot, o, inv, lane);
+    store_tile_rows<D>(out + (size_t)q0 * qstride + (size_t)head * D, qstride, q1 - q0, ot, lane);
+  } else if (qrow < q1) {
     bf16* op = out + (size_t)qrow * qstride + (size_t)head * D + lh * 4;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -212,8 +232,8 @@ __global__ __launch_bounds__(FWD_THREADS, BlockGeom<D>::MIN_WG) void fwd_kernel(
       for (int j = 0; j < 4; ++j)
         store_bf16x4(op + db * 32 + j * 8, o[db][4 * j] * inv, o[db][4 * j + 1] * inv,
                      o[db][4 * j + 2] * inv, o[db][4 * j + 3] * inv);
-    if (lh == 0) lse[(size_t)head * T + qrow] = (m + log2_fast(lt)) * LN2;
   }
+  if (lh == 0 && qrow < q1) lse[(size_t)head * T + qrow] = (m + log2_fast(lt)) * LN2;
 }
 
 template <int D, bool CAP>
