@@ -456,3 +456,62 @@ ALL_PINS = [
     pin_softcap_torch_autograd,
     pin_softcap_finite_differences,
 ]
+
+
+# --------------------------------------------------------------------------
+# Band-block formulation (oracle/band.py): pinned against the dense oracle
+# (itself pinned above) and against closed forms of its own.
+# --------------------------------------------------------------------------
+BAND_CASES = [(CU_MIXED, 1), (CU_MIXED, 3), (CU_MIXED, 8), ([0, 40, 70], 7),
+              ([0, 5, 64], 16), ([0, 3, 3, 19, 52], 5), (CU_MIXED, 40)]
+
+
+def pin_band_equals_dense(ob):
+    """Band-block results equal the dense definition (windows of 1 key up to
+    longer than the microbatch, blocks crossing document boundaries)."""
+    from oracle import attention as dense
+    for n, (cu, w) in enumerate(BAND_CASES):
+        q, k, v, do = rand_inputs(40 + n, cu, 4, 2, 8, 1.2)
+        out, lse, dq, dk, dv = ob.band_attention(q, k, v, do, cu, w, 0.35)
+        rdq, rdk, rdv, rout, rlse, _ = dense.attention_backward(q, k, v, do, cu, w, 0.35)
+        for name, x, y in (("out", out, rout), ("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+            _close(x, y, 1e-11, f"band {name} (W={w}, cu={cu})")
+        fin = np.isfinite(rlse)
+        assert np.array_equal(np.isfinite(lse), fin), f"band lse support (W={w})"
+        _close(lse[fin], rlse[fin], 1e-11, f"band lse (W={w})")
+
+
+def pin_band_bias_counts(ob):
+    """Row i of a band sees exactly min(i - a + 1, W) keys (a its segment
+    start), all inside the band's [(b - 1) W, (b + 1) W) columns."""
+    cu = [0, 3, 3, 19, 52]
+    for w in (1, 4, 7, 20, 60):
+        t = cu[-1]
+        for b in range((t + w - 1) // w):
+            q0, q1, lo, hi, bias = ob.band_bias(cu, t, w, b)
+            assert (q0, q1, lo, hi) == (b * w, min(t, (b + 1) * w), max(0, (b - 1) * w), min(t, (b + 1) * w))
+            assert bias.shape == (q1 - q0, hi - lo)
+            for r, i in enumerate(range(q0, q1)):
+                a = cu[int(np.searchsorted(cu, i, side="right")) - 1]   # start of i's segment
+                want = min(i - a + 1, w)
+                got = int(np.isfinite(bias[r]).sum())
+                assert got == want, f"band row {i} (W={w}): {got} visible keys, want {want}"
+
+
+def pin_band_q_zero(ob):
+    """q = 0 makes every visible key equally likely: lse = log(min(i - a + 1, W))
+    and out = the mean of the visible values (closed form)."""
+    cu = [0, 9, 30]
+    w = 6
+    _, k, v, do = rand_inputs(47, cu, 4, 2, 8)
+    q = np.zeros((cu[-1], 4, 8))
+    out, lse, *_ = ob.band_attention(q, k, v, do, cu, w, 0.5)
+    for a, b in ((0, 9), (9, 30)):
+        for i in range(a, b):
+            lo = max(a, i - w + 1)
+            for h in range(4):
+                assert abs(lse[h, i] - math.log(i - lo + 1)) <= 1e-12, f"band lse row {i}"
+                _close(out[i, h], v[lo:i + 1, h // 2].mean(axis=0), 1e-12, f"band out row {i}")
+
+
+BAND_PINS = [pin_band_equals_dense, pin_band_bias_counts, pin_band_q_zero]
