@@ -15,12 +15,16 @@ forward and 10*d backward, pairs counted exactly from cu_seqlens and the
 window.  Prints one JSON line.
 
     python bench.py [--steps 20] [--warmup 50] [--workload ctx4096_w512+global]
-                    [--softcap C] [--head-dim D]
+                    [--softcap C] [--head-dim D] [--band]
 
 --softcap C times the same step with every logit soft-capped to
 C tanh(logit / C) (attn_varlen_fwd_ex / attn_varlen_bwd_ex); the counted
 flops are the same.  --head-dim D (64, 128 or 256) runs the workload with
-that head width (scale 1 / sqrt(D)); flops scale with D.
+that head width (scale 1 / sqrt(D)); flops scale with D.  --band runs the
+windowed layers through the band-block calls (attn_varlen_band_fwd /
+attn_varlen_band_bwd: each W-token query block against the keys of its own
+block and the one before, results equal to the plain calls); the counted
+flops stay those of the visible pairs.
 """
 from __future__ import annotations
 
@@ -75,7 +79,8 @@ def cpu_info():
     return model
 
 
-def build_layers(workload: str, seed: int, device, softcap: float = 0.0, head_dim: int = 0):
+def build_layers(workload: str, seed: int, device, softcap: float = 0.0, head_dim: int = 0,
+                 band: bool = False):
     import dataclasses
     import torch
     from synthetic import CONFIGS, make_cu_seqlens, make_layer
@@ -108,6 +113,7 @@ def build_layers(workload: str, seed: int, device, softcap: float = 0.0, head_di
                                      cfg.window, device),
             "flops": attention_flops(cu, cfg.window, hq, d),
             "softcap": softcap,
+            "band": band and cfg.window > 0,
         }
         layers.append(lay)
     return cu, layers
@@ -115,11 +121,12 @@ def build_layers(workload: str, seed: int, device, softcap: float = 0.0, head_di
 
 def run_layer(attn, L):
     attn.fwd(L["q"], L["k"], L["v"], L["cu"], L["max_seqlen"], L["window"], L["scale"],
-             out=L["out"], lse=L["lse"], workspace=L["ws"], softcap=L["softcap"])
+             out=L["out"], lse=L["lse"], workspace=L["ws"], softcap=L["softcap"], band=L["band"])
     # the backward of a layer reuses the tile schedule its forward just built
+    # (the band-block backward always rebuilds its own)
     attn.bwd(L["q"], L["k"], L["v"], L["out"], L["lse"], L["do"], L["cu"], L["max_seqlen"],
              L["window"], L["scale"], dq=L["dq"], dk=L["dk"], dv=L["dv"], workspace=L["ws"],
-             softcap=L["softcap"], reuse_schedule=True)
+             softcap=L["softcap"], reuse_schedule=not L["band"], band=L["band"])
 
 
 def cpu_baseline(layers, seed, min_seconds=10.0, max_reps=4):
@@ -206,6 +213,8 @@ def main():
                     help="logit soft-cap C > 0 (every logit becomes C tanh(logit / C))")
     ap.add_argument("--head-dim", type=int, default=0, choices=[0, 64, 128, 256],
                     help="head width (default: the workload's, 128)")
+    ap.add_argument("--band", action="store_true",
+                    help="windowed layers through the band-block calls")
     ap.add_argument("--print-sources-sha", action="store_true",
                     help="print the kernel-source hash the traffic summary is keyed on")
     ap.add_argument("--no-cpu-baseline", action="store_true",
@@ -235,7 +244,8 @@ def main():
     if args.copy_calibration:
         copy_calibration(device)
         return
-    cu, layers = build_layers(args.workload, args.seed, device, args.softcap, args.head_dim)
+    cu, layers = build_layers(args.workload, args.seed, device, args.softcap, args.head_dim,
+                              args.band)
     print(f"[bench] workload {args.workload}: {len(layers)} layer(s), {len(cu) - 1} segments, "
           f"max_seqlen {layers[0]['max_seqlen']}", file=sys.stderr, flush=True)
 
@@ -383,6 +393,7 @@ def main():
             "max_seqlen": layers[0]["max_seqlen"],
             "gflop_per_step": step_flops / 1e9,
             "softcap": args.softcap if args.softcap > 0 else None,
+            "band": True if args.band else None,
         },
         "layers": layer_report,
         "kernels": kernels,

@@ -163,6 +163,36 @@ attn_status attn_varlen_bwd_ex(const void* q, const void* k, const void* v,
                                float softcap, uint32_t flags, void* dq, void* dk, void* dv,
                                void* workspace, size_t workspace_bytes, attn_stream_t stream);
 
+/*
+ * Band-block formulation of the windowed calls (the performance reference
+ * page dewml.dev/reference/performance, section "Packed sliding-window
+ * attention on GPU: local_attention": queries in blocks of W, each block
+ * against a [W, 2W] band of keys, its own block and the one before it, with
+ * the window, causal and document mask inside the band).  Blocks are aligned
+ * to token 0 of the microbatch.  Same arguments, layouts, ownership and
+ * errors as attn_varlen_fwd / attn_varlen_bwd, plus: window must be >= 1
+ * (ATTN_EINVAL otherwise; a window >= total_tokens makes one band hold
+ * everything, the global case).  Each q-tile loops over every key block of
+ * its rows' bands (and each k-tile over every query block whose band holds
+ * its keys) within the segment, with the same per-row mask, so the results
+ * equal the plain calls' bit for bit while the kernels process the band's
+ * masked blocks too: a cross-check of the window ranges and a measure of
+ * the band's cost.  The backward always rebuilds its schedule.
+ */
+attn_status attn_varlen_band_fwd(const void* q, const void* k, const void* v,
+                                 const int32_t* cu_seqlens, int32_t num_seqs,
+                                 int32_t total_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_seqlen, int32_t window,
+                                 float scale, void* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, attn_stream_t stream);
+
+attn_status attn_varlen_band_bwd(const void* q, const void* k, const void* v, const void* out,
+                                 const float* lse, const void* dout, const int32_t* cu_seqlens,
+                                 int32_t num_seqs, int32_t total_tokens, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t max_seqlen,
+                                 int32_t window, float scale, void* dq, void* dk, void* dv,
+                                 void* workspace, size_t workspace_bytes, attn_stream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char* attn_varlen_strerror(attn_status s);
 

@@ -111,3 +111,20 @@ def test_bwd_rejects(lib):
         a = list(base)
         a[pos] = val
         assert f(*a) == code, (pos, val)
+
+
+@pytest.mark.parametrize("window", [0, -1, -512])
+def test_band_calls_need_a_window(lib, window):
+    args = [FAKE] * 4 + [1, 64, 8, 2, 128, 64, window, 0.088, FAKE, FAKE, FAKE, 1 << 30, None]
+    assert lib.attn_varlen_band_fwd(*args) == EINVAL
+    bargs = [FAKE] * 7 + [1, 64, 8, 2, 128, 64, window, 0.088, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                          None]
+    assert lib.attn_varlen_band_bwd(*bargs) == EINVAL
+
+
+def test_band_calls_check_like_the_plain_ones(lib):
+    # a null q or an unsupported head dim fail the same way with and without the band
+    args = [None] + [FAKE] * 3 + [1, 64, 8, 2, 128, 64, 16, 0.088, FAKE, FAKE, FAKE, 1 << 30, None]
+    assert lib.attn_varlen_band_fwd(*args) == EINVAL
+    args = [FAKE] * 4 + [1, 64, 8, 2, 96, 64, 16, 0.088, FAKE, FAKE, FAKE, 1 << 30, None]
+    assert lib.attn_varlen_band_fwd(*args) == EUNSUPPORTED

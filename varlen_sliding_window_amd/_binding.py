@@ -62,6 +62,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                        i32, i32, ctypes.c_float, ctypes.c_float, ctypes.c_uint32,
                                        vp, vp, vp, vp, sz, vp]
     lib.attn_varlen_bwd_ex.restype = ctypes.c_int
+    lib.attn_varlen_band_fwd.argtypes = lib.attn_varlen_fwd.argtypes
+    lib.attn_varlen_band_fwd.restype = ctypes.c_int
+    lib.attn_varlen_band_bwd.argtypes = lib.attn_varlen_bwd.argtypes
+    lib.attn_varlen_band_bwd.restype = ctypes.c_int
     lib.attn_varlen_strerror.argtypes = [ctypes.c_int]
     lib.attn_varlen_strerror.restype = ctypes.c_char_p
     lib.attn_varlen_version.argtypes = []
@@ -116,11 +120,12 @@ def new_workspace(total_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, m
 
 
 def fwd(q, k, v, cu_seqlens, max_seqlen: int, window: int, scale: float | None = None,
-        out=None, lse=None, workspace=None, softcap: float = 0.0):
-    """attn_varlen_fwd (attn_varlen_fwd_ex when softcap > 0): returns
-    (out [T,Hq,D] bf16, lse [Hq,T] fp32).
+        out=None, lse=None, workspace=None, softcap: float = 0.0, band: bool = False):
+    """attn_varlen_fwd (attn_varlen_fwd_ex when softcap > 0, attn_varlen_band_fwd
+    when band): returns (out [T,Hq,D] bf16, lse [Hq,T] fp32).
 
-    softcap > 0 caps every logit to softcap * tanh(logit / softcap)."""
+    softcap > 0 caps every logit to softcap * tanh(logit / softcap); band runs
+    the band-block formulation (window >= 1, no soft-cap)."""
     _check_tensor("q", q, torch.bfloat16, 3)
     _check_tensor("k", k, torch.bfloat16, 3)
     _check_tensor("v", v, torch.bfloat16, 3)
@@ -142,7 +147,11 @@ def fwd(q, k, v, cu_seqlens, max_seqlen: int, window: int, scale: float | None =
     head = (_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), nseq, t, hq, hkv, d, int(max_seqlen),
             int(window), float(scale))
     tail = (_ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream_handle(q.device))
-    if softcap:
+    if band:
+        if softcap:
+            raise ValueError("the band-block calls take no soft-cap")
+        st, where = lib.attn_varlen_band_fwd(*head, *tail), "attn_varlen_band_fwd"
+    elif softcap:
         st, where = lib.attn_varlen_fwd_ex(*head, float(softcap), *tail), "attn_varlen_fwd_ex"
     else:
         st, where = lib.attn_varlen_fwd(*head, *tail), "attn_varlen_fwd"
@@ -153,12 +162,14 @@ def fwd(q, k, v, cu_seqlens, max_seqlen: int, window: int, scale: float | None =
 
 def bwd(q, k, v, out, lse, dout, cu_seqlens, max_seqlen: int, window: int,
         scale: float | None = None, dq=None, dk=None, dv=None, workspace=None,
-        softcap: float = 0.0, reuse_schedule: bool = False):
-    """attn_varlen_bwd (attn_varlen_bwd_ex with a soft-cap or reuse_schedule):
-    returns (dq, dk, dv), bf16, shaped like q, k, v.  softcap must be the
-    forward's.  reuse_schedule: `workspace` was just used by the forward call
-    of the same layer (same cu_seqlens and window), whose tile schedule the
-    backward then uses instead of rebuilding it."""
+        softcap: float = 0.0, reuse_schedule: bool = False, band: bool = False):
+    """attn_varlen_bwd (attn_varlen_bwd_ex with a soft-cap or reuse_schedule,
+    attn_varlen_band_bwd when band): returns (dq, dk, dv), bf16, shaped like
+    q, k, v.  softcap must be the forward's.  reuse_schedule: `workspace` was
+    just used by the forward call of the same layer (same cu_seqlens and
+    window), whose tile schedule the backward then uses instead of rebuilding
+    it.  band: the band-block formulation (window >= 1, no soft-cap, always
+    rebuilds its schedule)."""
     for name, t_ in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
         _check_tensor(name, t_, torch.bfloat16, 3)
     _check_tensor("lse", lse, torch.float32, 2)
@@ -185,7 +196,11 @@ def bwd(q, k, v, out, lse, dout, cu_seqlens, max_seqlen: int, window: int,
             _stream_handle(q.device))
     if reuse_schedule and workspace_arg_missing:
         raise ValueError("reuse_schedule needs the forward call's workspace")
-    if softcap or reuse_schedule:
+    if band:
+        if softcap or reuse_schedule:
+            raise ValueError("the band-block calls take no soft-cap and no flags")
+        st, where = lib.attn_varlen_band_bwd(*head, *tail), "attn_varlen_band_bwd"
+    elif softcap or reuse_schedule:
         flags = ATTN_BWD_REUSE_SCHEDULE if reuse_schedule else 0
         st, where = (lib.attn_varlen_bwd_ex(*head, float(softcap), flags, *tail),
                      "attn_varlen_bwd_ex")

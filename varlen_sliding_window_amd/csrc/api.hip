@@ -111,6 +111,81 @@ int32_t effective_window(int32_t window, int32_t total_tokens) {
 
 }  // namespace
 
+namespace {
+
+attn_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                     int32_t num_seqs, int32_t total_tokens, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t max_seqlen, int32_t window,
+                     float scale, float softcap, bool band, void* out, float* lse,
+                     void* workspace, size_t workspace_bytes, attn_stream_t stream) {
+  WorkspaceLayout w;
+  attn_status s = check_common(q, k, v, cu_seqlens, total_tokens, num_seqs, num_q_heads,
+                               num_kv_heads, head_dim, max_seqlen, scale, workspace,
+                               workspace_bytes, &w);
+  if (s != ATTN_OK) return s;
+  if (!out || !lse || !aligned(out, 16) || !aligned(lse, 4)) return ATTN_EINVAL;
+  if (!std::isfinite(softcap) || softcap < 0.f) return ATTN_EINVAL;
+  if (band && window <= 0) return ATTN_EINVAL;
+  s = check_device();
+  if (s != ATTN_OK) return s;
+  const int32_t wnd = effective_window(window, total_tokens);
+  const Problem p{total_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, wnd, scale,
+                  softcap, band && wnd > 0 ? 1 : 0};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // both lists, so that the matching backward call may reuse them
+  if (timed_launch(K_SCHEDULE, st, [&] {
+        return attn::launch_schedule(cu_seqlens, p, true, workspace, w, st);
+      }) != hipSuccess)
+    return ATTN_ELAUNCH;
+  if (timed_launch(K_FORWARD, st, [&] {
+        return attn::launch_forward(q, k, v, p, out, lse, workspace, w, st);
+      }) != hipSuccess)
+    return ATTN_ELAUNCH;
+  return ATTN_OK;
+}
+
+attn_status bwd_impl(const void* q, const void* k, const void* v, const void* out,
+                     const float* lse, const void* dout, const int32_t* cu_seqlens,
+                     int32_t num_seqs, int32_t total_tokens, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t max_seqlen, int32_t window,
+                     float scale, float softcap, uint32_t flags, bool band, void* dq, void* dk,
+                     void* dv, void* workspace, size_t workspace_bytes, attn_stream_t stream) {
+  WorkspaceLayout w;
+  attn_status s = check_common(q, k, v, cu_seqlens, total_tokens, num_seqs, num_q_heads,
+                               num_kv_heads, head_dim, max_seqlen, scale, workspace,
+                               workspace_bytes, &w);
+  if (s != ATTN_OK) return s;
+  if (!out || !lse || !dout || !dq || !dk || !dv) return ATTN_EINVAL;
+  if (!aligned(out, 16) || !aligned(dout, 16) || !aligned(lse, 4) || !aligned(dq, 16) ||
+      !aligned(dk, 16) || !aligned(dv, 16))
+    return ATTN_EINVAL;
+  if (!std::isfinite(softcap) || softcap < 0.f) return ATTN_EINVAL;
+  if (flags & ~(uint32_t)ATTN_BWD_REUSE_SCHEDULE) return ATTN_EINVAL;
+  if (band && window <= 0) return ATTN_EINVAL;
+  s = check_device();
+  if (s != ATTN_OK) return s;
+  const int32_t wnd = effective_window(window, total_tokens);
+  const Problem p{total_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, wnd, scale,
+                  softcap, band && wnd > 0 ? 1 : 0};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!(flags & ATTN_BWD_REUSE_SCHEDULE) &&
+      timed_launch(K_SCHEDULE, st, [&] {
+        return attn::launch_schedule(cu_seqlens, p, true, workspace, w, st);
+      }) != hipSuccess)
+    return ATTN_ELAUNCH;
+  if (timed_launch(K_DQ, st, [&] {
+        return attn::launch_dq(q, k, v, out, lse, dout, p, dq, workspace, w, st);
+      }) != hipSuccess)
+    return ATTN_ELAUNCH;
+  if (timed_launch(K_DKDV, st, [&] {
+        return attn::launch_dkdv(q, k, v, lse, dout, p, dk, dv, workspace, w, st);
+      }) != hipSuccess)
+    return ATTN_ELAUNCH;
+  return ATTN_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t attn_varlen_workspace_size(int32_t total_tokens, int32_t num_seqs_cap,
@@ -129,28 +204,9 @@ attn_status attn_varlen_fwd_ex(const void* q, const void* k, const void* v,
                                int32_t max_seqlen, int32_t window, float scale, float softcap,
                                void* out, float* lse, void* workspace, size_t workspace_bytes,
                                attn_stream_t stream) {
-  WorkspaceLayout w;
-  attn_status s = check_common(q, k, v, cu_seqlens, total_tokens, num_seqs, num_q_heads,
-                               num_kv_heads, head_dim, max_seqlen, scale, workspace,
-                               workspace_bytes, &w);
-  if (s != ATTN_OK) return s;
-  if (!out || !lse || !aligned(out, 16) || !aligned(lse, 4)) return ATTN_EINVAL;
-  if (!std::isfinite(softcap) || softcap < 0.f) return ATTN_EINVAL;
-  s = check_device();
-  if (s != ATTN_OK) return s;
-  const Problem p{total_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                  effective_window(window, total_tokens), scale, softcap};
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  // both lists, so that the matching backward call may reuse them
-  if (timed_launch(K_SCHEDULE, st, [&] {
-        return attn::launch_schedule(cu_seqlens, p, true, workspace, w, st);
-      }) != hipSuccess)
-    return ATTN_ELAUNCH;
-  if (timed_launch(K_FORWARD, st, [&] {
-        return attn::launch_forward(q, k, v, p, out, lse, workspace, w, st);
-      }) != hipSuccess)
-    return ATTN_ELAUNCH;
-  return ATTN_OK;
+  return fwd_impl(q, k, v, cu_seqlens, num_seqs, total_tokens, num_q_heads, num_kv_heads,
+                  head_dim, max_seqlen, window, scale, softcap, false, out, lse, workspace,
+                  workspace_bytes, stream);
 }
 
 attn_status attn_varlen_fwd(const void* q, const void* k, const void* v,
@@ -171,36 +227,9 @@ attn_status attn_varlen_bwd_ex(const void* q, const void* k, const void* v, cons
                                int32_t window, float scale, float softcap, uint32_t flags,
                                void* dq, void* dk, void* dv, void* workspace,
                                size_t workspace_bytes, attn_stream_t stream) {
-  WorkspaceLayout w;
-  attn_status s = check_common(q, k, v, cu_seqlens, total_tokens, num_seqs, num_q_heads,
-                               num_kv_heads, head_dim, max_seqlen, scale, workspace,
-                               workspace_bytes, &w);
-  if (s != ATTN_OK) return s;
-  if (!out || !lse || !dout || !dq || !dk || !dv) return ATTN_EINVAL;
-  if (!aligned(out, 16) || !aligned(dout, 16) || !aligned(lse, 4) || !aligned(dq, 16) ||
-      !aligned(dk, 16) || !aligned(dv, 16))
-    return ATTN_EINVAL;
-  if (!std::isfinite(softcap) || softcap < 0.f) return ATTN_EINVAL;
-  if (flags & ~(uint32_t)ATTN_BWD_REUSE_SCHEDULE) return ATTN_EINVAL;
-  s = check_device();
-  if (s != ATTN_OK) return s;
-  const Problem p{total_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                  effective_window(window, total_tokens), scale, softcap};
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (!(flags & ATTN_BWD_REUSE_SCHEDULE) &&
-      timed_launch(K_SCHEDULE, st, [&] {
-        return attn::launch_schedule(cu_seqlens, p, true, workspace, w, st);
-      }) != hipSuccess)
-    return ATTN_ELAUNCH;
-  if (timed_launch(K_DQ, st, [&] {
-        return attn::launch_dq(q, k, v, out, lse, dout, p, dq, workspace, w, st);
-      }) != hipSuccess)
-    return ATTN_ELAUNCH;
-  if (timed_launch(K_DKDV, st, [&] {
-        return attn::launch_dkdv(q, k, v, lse, dout, p, dk, dv, workspace, w, st);
-      }) != hipSuccess)
-    return ATTN_ELAUNCH;
-  return ATTN_OK;
+  return bwd_impl(q, k, v, out, lse, dout, cu_seqlens, num_seqs, total_tokens, num_q_heads,
+                  num_kv_heads, head_dim, max_seqlen, window, scale, softcap, flags, false, dq,
+                  dk, dv, workspace, workspace_bytes, stream);
 }
 
 attn_status attn_varlen_bwd(const void* q, const void* k, const void* v, const void* out,
@@ -212,6 +241,28 @@ attn_status attn_varlen_bwd(const void* q, const void* k, const void* v, const v
   return attn_varlen_bwd_ex(q, k, v, out, lse, dout, cu_seqlens, num_seqs, total_tokens,
                             num_q_heads, num_kv_heads, head_dim, max_seqlen, window, scale, 0.f,
                             0u, dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_varlen_band_fwd(const void* q, const void* k, const void* v,
+                                 const int32_t* cu_seqlens, int32_t num_seqs,
+                                 int32_t total_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_seqlen, int32_t window,
+                                 float scale, void* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, attn_stream_t stream) {
+  return fwd_impl(q, k, v, cu_seqlens, num_seqs, total_tokens, num_q_heads, num_kv_heads,
+                  head_dim, max_seqlen, window, scale, 0.f, true, out, lse, workspace,
+                  workspace_bytes, stream);
+}
+
+attn_status attn_varlen_band_bwd(const void* q, const void* k, const void* v, const void* out,
+                                 const float* lse, const void* dout, const int32_t* cu_seqlens,
+                                 int32_t num_seqs, int32_t total_tokens, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t max_seqlen,
+                                 int32_t window, float scale, void* dq, void* dk, void* dv,
+                                 void* workspace, size_t workspace_bytes, attn_stream_t stream) {
+  return bwd_impl(q, k, v, out, lse, dout, cu_seqlens, num_seqs, total_tokens, num_q_heads,
+                  num_kv_heads, head_dim, max_seqlen, window, scale, 0.f, 0u, true, dq, dk, dv,
+                  workspace, workspace_bytes, stream);
 }
 
 const char* attn_varlen_strerror(attn_status s) {
@@ -226,7 +277,7 @@ const char* attn_varlen_strerror(attn_status s) {
   return "unknown status";
 }
 
-int32_t attn_varlen_version(void) { return 200; }
+int32_t attn_varlen_version(void) { return 210; }
 
 attn_status attn_varlen_profile_start(void) {
   std::lock_guard<std::mutex> lock(g_prof_mu);

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(BWD_THREADS, BlockGeom<D>::MIN_WG) void dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ out, const bf16* __restrict__ dout, const float* __restrict__ lse,
     const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
-    int window, float scale_log2, float scale, float cap_a, float cap_c2, int tile_cap,
+    int window, int band, float scale_log2, float scale, float cap_a, float cap_c2, int tile_cap,
     bf16* __restrict__ dq, TileStats* __restrict__ stats) {
   using Geo = BlockGeom<D>;
   constexpr int KB = Geo::KB, H2 = Geo::H2, KS = Geo::KS, DB = Geo::DB;
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(BWD_THREADS, BlockGeom<D>::MIN_WG) void dq_kernel(
   const int head = hc * 4 + wave;
   const int g = (hc * 4) / (Hq / Hkv);
   const int q0 = tl.t0, q1 = tl.t1, a = tl.seg_a;
-  const int klo = first_visible_key(q0, a, window);
+  const int klo = tile_key_lo(q0, a, window, band);
   const int nblk = (q1 - klo + KB - 1) / KB;
   const int qrow = q0 + lq;
   const size_t qstride = (size_t)Hq * D;
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(BWD_THREADS, (D == 64 && !CAP) ? 2 : 1) void dkdv_k
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const TileStats* __restrict__ stats, int tile_cap,
     const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
-    int window, float scale_log2, float scale, float cap_a, float cap_c2, int run_len,
+    int window, int band, float scale_log2, float scale, float cap_a, float cap_c2, int run_len,
     bf16* __restrict__ dk, bf16* __restrict__ dv) {
   using Geo = DkdvGeom<D>;
   constexpr int KS = Geo::KS, DB = Geo::DB, RED_PITCH = Geo::RED_PITCH;
@@ -335,7 +335,7 @@ __global__ __launch_bounds__(BWD_THREADS, (D == 64 && !CAP) ? 2 : 1) void dkdv_k
   const int lane = tid & 63, lh = lane >> 5, lq = lane & 31;
   const int G = Hq / Hkv;
   const int k0 = tl.t0, k1 = tl.t1, b = tl.seg_b;
-  const int qhi = window > 0 ? min(b, k1 - 1 + window) : b;
+  const int qhi = tile_query_hi(k1, b, window, band);
   const int nqb = (qhi - k0 + QBLK - 1) / QBLK;
   const int steps = (G / DKDV_WAVES) * nqb;   // (head, q-block) pairs of this wave
   const size_t qstride = (size_t)Hq * D;
@@ -616,7 +616,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_split_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const TileStats* __restrict__ stats, int tile_cap,
     const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
-    int window, float scale_log2, float scale, float cap_a, float cap_c2, int run_len,
+    int window, int band, float scale_log2, float scale, float cap_a, float cap_c2, int run_len,
     bf16* __restrict__ dk, bf16* __restrict__ dv) {
   constexpr int D = 256, DH = 128;      // head dim, columns per wave
   using Geo = DkdvGeom<DH>;             // staging of 128-wide half rows
@@ -641,7 +641,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_split_kernel(
   const int half = wave & 1, pair = wave >> 1;
   const int G = Hq / Hkv;
   const int k0 = tl.t0, k1 = tl.t1, b = tl.seg_b;
-  const int qhi = window > 0 ? min(b, k1 - 1 + window) : b;
+  const int qhi = tile_query_hi(k1, b, window, band);
   const int nqb = (qhi - k0 + QBLK - 1) / QBLK;
   const int steps = (G / 2) * nqb;   // (head, q-block) pairs of this wave
   const size_t qstride = (size_t)Hq * D;
@@ -860,7 +860,7 @@ __global__ __launch_bounds__(OCC_THREADS, 1) void dkdv_occ_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const TileStats* __restrict__ stats, int tile_cap,
     const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
-    int window, float scale_log2, float scale, float cap_a, float cap_c2, int run_len,
+    int window, int band, float scale_log2, float scale, float cap_a, float cap_c2, int run_len,
     bf16* __restrict__ dk, bf16* __restrict__ dv) {
   constexpr int D = 128;
   using Geo = DkdvGeom<D>;
@@ -889,7 +889,7 @@ __global__ __launch_bounds__(OCC_THREADS, 1) void dkdv_occ_kernel(
   const int hs = wave & 3, par = wave >> 2;
   const int G = Hq / Hkv;
   const int k0 = tl.t0, k1 = tl.t1, b = tl.seg_b;
-  const int qhi = window > 0 ? min(b, k1 - 1 + window) : b;
+  const int qhi = tile_query_hi(k1, b, window, band);
   const int nqb = (qhi - k0 + QBLK - 1) / QBLK;
   const int nmine = (nqb - par + 1) / 2;       // q-blocks of this parity
   const int steps = (G / 4) * nmine;
@@ -1097,7 +1097,7 @@ void launch_dq_kernel(const void* q, const void* k, const void* v, const void* o
                      static_cast<const bf16*>(dout), lse,
                      reinterpret_cast<const int*>(ws + w.header),
                      reinterpret_cast<const Tile*>(ws + w.tiles_fwd), p.total_tokens,
-                     p.num_q_heads, p.num_kv_heads, p.window, p.scale * LOG2E, p.scale,
+                     p.num_q_heads, p.num_kv_heads, p.window, p.band, p.scale * LOG2E, p.scale,
                      cc.cap_a, cc.cap_c2, (int)w.tile_cap, static_cast<bf16*>(dq),
                      reinterpret_cast<TileStats*>(ws + w.rowstats));
 }
@@ -1120,8 +1120,8 @@ void launch_dkdv_kernel(const void* q, const void* k, const void* v, const void*
   // SIMD; 64: the software-pipelined kernel
   constexpr bool occ = D == 128;
   void (*kernel)(const bf16*, const bf16*, const bf16*, const bf16*, const TileStats*, int,
-                 const int*, const Tile*, int, int, int, int, float, float, float, float, int,
-                 bf16*, bf16*);
+                 const int*, const Tile*, int, int, int, int, int, float, float, float, float,
+                 int, bf16*, bf16*);
   if constexpr (D == 256)
     kernel = dkdv_split_kernel<CAP>;
   else if constexpr (D == 128)
@@ -1134,7 +1134,7 @@ void launch_dkdv_kernel(const void* q, const void* k, const void* v, const void*
                      reinterpret_cast<const TileStats*>(ws + w.rowstats), (int)w.tile_cap,
                      reinterpret_cast<const int*>(ws + w.header),
                      reinterpret_cast<const Tile*>(ws + w.tiles_bwd), p.total_tokens,
-                     p.num_q_heads, p.num_kv_heads, p.window, p.scale * LOG2E, p.scale,
+                     p.num_q_heads, p.num_kv_heads, p.window, p.band, p.scale * LOG2E, p.scale,
                      cc.cap_a, cc.cap_c2, run_len, static_cast<bf16*>(dk),
                      static_cast<bf16*>(dv));
 }

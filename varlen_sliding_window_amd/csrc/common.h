@@ -88,4 +88,22 @@ __device__ __forceinline__ int first_visible_key(int i, int a, int window) {
   return window > 0 ? max(a, i - window + 1) : a;
 }
 
+// Key range a q-tile [q0, ...) of segment [a, ...) loops over: from its
+// first visible key or, in the band-block formulation (the performance
+// reference page, section "Packed sliding-window attention on GPU:
+// local_attention"), from the start of the W-token block before the block
+// of q0 (blocks aligned to token 0), cut to the segment.  The per-row mask is
+// the same either way, so the band only adds fully masked key blocks.
+__device__ __forceinline__ int tile_key_lo(int q0, int a, int window, int band) {
+  return band ? max(a, (q0 / window - 1) * window) : first_visible_key(q0, a, window);
+}
+
+// Query range end (exclusive) that a k-tile [.., k1) of segment [.., b) meets:
+// the queries that see its last key or, in the band-block formulation, every
+// query of the W-token block after the block of key k1 - 1.
+__device__ __forceinline__ int tile_query_hi(int k1, int b, int window, int band) {
+  if (window <= 0) return b;
+  return band ? min(b, ((k1 - 1) / window + 2) * window) : min(b, k1 - 1 + window);
+}
+
 }  // namespace attn

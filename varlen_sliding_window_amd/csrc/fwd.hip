@@ -40,7 +40,7 @@ template <int D, bool CAP>
 __global__ __launch_bounds__(FWD_THREADS, BlockGeom<D>::MIN_WG) void fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
-    int window, float scale_log2, float cap_a, float cap_c2, bf16* __restrict__ out,
+    int window, int band, float scale_log2, float cap_a, float cap_c2, bf16* __restrict__ out,
     float* __restrict__ lse) {
   using Geo = BlockGeom<D>;
   constexpr int KB = Geo::KB, H2 = Geo::H2, KS = Geo::KS, DB = Geo::DB;
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(FWD_THREADS, BlockGeom<D>::MIN_WG) void fwd_kernel(
   const int head = hc * 4 + wave;
   const int g = (hc * 4) / (Hq / Hkv);
   const int q0 = tl.t0, q1 = tl.t1, a = tl.seg_a;
-  const int klo = first_visible_key(q0, a, window);
+  const int klo = tile_key_lo(q0, a, window, band);
   const int nblk = (q1 - klo + KB - 1) / KB;
   const int qrow = q0 + lq;
   const size_t qstride = (size_t)Hq * D;
@@ -246,7 +246,7 @@ void launch_fwd_kernel(unsigned grid, hipStream_t stream, const void* q, const v
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                      static_cast<const bf16*>(v), reinterpret_cast<const int*>(ws + w.header),
                      reinterpret_cast<const Tile*>(ws + w.tiles_fwd), p.total_tokens,
-                     p.num_q_heads, p.num_kv_heads, p.window, CAP ? 1.f : p.scale * LOG2E,
+                     p.num_q_heads, p.num_kv_heads, p.window, p.band, CAP ? 1.f : p.scale * LOG2E,
                      cc.cap_a, cc.cap_c2, static_cast<bf16*>(out), lse);
 }
 

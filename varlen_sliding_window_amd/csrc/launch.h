@@ -9,6 +9,7 @@ struct Problem {
   int total_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, window;
   float scale;
   float softcap;   // > 0: logits become softcap * tanh(logit / softcap); 0: no cap
+  int band;        // 1: band-block key/query ranges (window > 0 only); 0: tight ranges
 };
 
 // Constants of the capped logit in the exp2 domain:

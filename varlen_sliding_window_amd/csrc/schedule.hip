@@ -79,13 +79,13 @@ __device__ __forceinline__ Tile tile_at(int i, const int* __restrict__ seg_off,
   return t;
 }
 
-__device__ __forceinline__ int fwd_bin(const Tile& t, int window) {
-  const int klo = first_visible_key(t.t0, t.seg_a, window);
+__device__ __forceinline__ int fwd_bin(const Tile& t, int window, int band) {
+  const int klo = tile_key_lo(t.t0, t.seg_a, window, band);
   return min((t.t1 - klo + KBLK - 1) / KBLK, SORT_BINS - 1);
 }
 
-__device__ __forceinline__ int bwd_bin(const Tile& t, int window) {
-  const int qhi = window > 0 ? min(t.seg_b, t.t1 - 1 + window) : t.seg_b;
+__device__ __forceinline__ int bwd_bin(const Tile& t, int window, int band) {
+  const int qhi = tile_query_hi(t.t1, t.seg_b, window, band);
   return min((qhi - t.t0 + QBLK - 1) / QBLK, SORT_BINS - 1);
 }
 
@@ -116,8 +116,8 @@ __device__ int ordered_slot(int* hist, int bin, bool valid) {
 constexpr int SCHED_LDS_SEGS = 4096;
 
 __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
-    const int32_t* __restrict__ cu_g, int nseq, int T, int window, int tile_cap, int need_bwd,
-    int* __restrict__ header, Tile* __restrict__ fwd_list, Tile* __restrict__ bwd_list,
+    const int32_t* __restrict__ cu_g, int nseq, int T, int window, int band, int tile_cap,
+    int need_bwd, int* __restrict__ header, Tile* __restrict__ fwd_list, Tile* __restrict__ bwd_list,
     int* __restrict__ seg_off_g) {
   __shared__ int buf[SCHED_THREADS / 64];
   __shared__ int hist_f[SORT_BINS];
@@ -166,8 +166,8 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
   const bool my_valid = one_pass && tid < ntiles;
   if (my_valid) {
     mine = tile_at(tid, seg_off, cu, nseq, T);
-    my_bf = fwd_bin(mine, window);
-    my_bb = bwd_bin(mine, window);
+    my_bf = fwd_bin(mine, window, band);
+    my_bb = bwd_bin(mine, window, band);
   }
   if (one_pass) {
     if (my_valid) {
@@ -177,8 +177,8 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
   } else {
     for (int i = tid; i < ntiles; i += SCHED_THREADS) {
       const Tile t = tile_at(i, seg_off, cu, nseq, T);
-      atomicAdd(&hist_f[fwd_bin(t, window)], 1);
-      if (need_bwd) atomicAdd(&hist_b[bwd_bin(t, window)], 1);
+      atomicAdd(&hist_f[fwd_bin(t, window, band)], 1);
+      if (need_bwd) atomicAdd(&hist_b[bwd_bin(t, window, band)], 1);
     }
   }
   __syncthreads();
@@ -223,8 +223,8 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
       int bf = 0, bb = 0;
       if (valid) {
         t = tile_at(i, seg_off, cu, nseq, T);
-        bf = fwd_bin(t, window);
-        bb = bwd_bin(t, window);
+        bf = fwd_bin(t, window, band);
+        bb = bwd_bin(t, window, band);
       }
       if (valid) fwd_list[atomicAdd(&hist_f[bf], 1)] = t;
       if (need_bwd) {
@@ -247,7 +247,8 @@ hipError_t launch_schedule(const int32_t* cu_seqlens, const Problem& p, bool nee
                            void* workspace, const WorkspaceLayout& w, hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(SCHED_THREADS), 0, stream, cu_seqlens,
-                     p.num_seqs, p.total_tokens, p.window, (int)w.tile_cap, need_bwd ? 1 : 0,
+                     p.num_seqs, p.total_tokens, p.window, p.band, (int)w.tile_cap,
+                     need_bwd ? 1 : 0,
                      reinterpret_cast<int*>(ws + w.header),
                      reinterpret_cast<Tile*>(ws + w.tiles_fwd),
                      reinterpret_cast<Tile*>(ws + w.tiles_bwd),
