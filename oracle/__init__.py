@@ -1,4 +1,6 @@
-"""CPU oracle for document-masked causal grouped-query attention (fp64).
+"""CPU oracles (fp64): document-masked causal grouped-query attention
+(attention.py), its band-block formulation (band.py) and gated delta-rule
+linear attention (delta.py).
 
 Test infrastructure: only tests/, the smoke check and the bench's CPU
 baseline may import it.  The product path never does.
