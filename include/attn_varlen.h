@@ -193,6 +193,36 @@ attn_status attn_varlen_band_bwd(const void* q, const void* k, const void* v, co
                                  int32_t window, float scale, void* dq, void* dk, void* dv,
                                  void* workspace, size_t workspace_bytes, attn_stream_t stream);
 
+/*
+ * Gated delta-rule linear attention (Gated DeltaNet), forward: the competing
+ * local layer of the kernel benchmarks page (research.dws.rip/llm/kernels,
+ * section 03 "What linear attention costs", Figs. 1 and 5), per the gated
+ * delta rule it names.  Per head h and document of cu_seqlens (the state
+ * starts at zero at every document start), with a d_v x d_k state S:
+ *   S_t = exp(g_t) S_{t-1} + beta_t (v_t - exp(g_t) S_{t-1} k_t) k_t^T,
+ *   out_t = scale S_t q_t.
+ *   q, k, v     bf16 [T, H, D] (head dim D = d_k = d_v), contiguous, 16-byte aligned
+ *   g           fp32 [T, H], log decay (<= 0 in use; not checked)
+ *   beta        fp32 [T, H], write strength (in (0, 1) in use; not checked)
+ *   out         bf16 [T, H, D], written fully for tokens inside documents
+ *   scale       finite and > 0
+ *   supported   D == 128 (ATTN_EUNSUPPORTED otherwise); any H >= 1
+ *   workspace   >= attn_delta_workspace_size(T, num_seqs, H, D) bytes, 256-byte
+ *               aligned: per (64-token chunk, head) fp32 records of the chunk's
+ *               triangular-solve results, about 82 KB each
+ * Enqueues three kernels on `stream` (chunk plan, per-chunk preparation,
+ * per-document scan); same ownership and error conventions as the
+ * attention calls.  No backward yet.
+ */
+size_t attn_delta_workspace_size(int32_t total_tokens, int32_t num_seqs_cap, int32_t num_heads,
+                                 int32_t head_dim);
+
+attn_status attn_delta_fwd(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                           int32_t total_tokens, int32_t num_heads, int32_t head_dim, float scale,
+                           void* out, void* workspace, size_t workspace_bytes,
+                           attn_stream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char* attn_varlen_strerror(attn_status s);
 

@@ -128,3 +128,19 @@ def test_band_calls_check_like_the_plain_ones(lib):
     assert lib.attn_varlen_band_fwd(*args) == EINVAL
     args = [FAKE] * 4 + [1, 64, 8, 2, 96, 64, 16, 0.088, FAKE, FAKE, FAKE, 1 << 30, None]
     assert lib.attn_varlen_band_fwd(*args) == EUNSUPPORTED
+
+
+def test_delta_rejects(lib):
+    f = lib.attn_delta_fwd
+    base = [FAKE] * 6 + [1, 64, 2, 128, 0.088, FAKE, FAKE, 1 << 30, None]
+    assert f(*base[:9], 96, *base[10:]) == EUNSUPPORTED          # head dim
+    for pos, val, code in ((0, None, EINVAL), (3, None, EINVAL), (4, FAKE + 2, EINVAL),
+                           (7, 0, EINVAL), (8, 0, EINVAL), (10, 0.0, EINVAL),
+                           (10, float("nan"), EINVAL), (12, None, EWORKSPACE),
+                           (13, 16, EWORKSPACE)):
+        args = list(base)
+        args[pos] = val
+        assert f(*args) == code, (pos, val)
+    assert lib.attn_delta_workspace_size(64, 1, 2, 128) > 0
+    assert lib.attn_delta_workspace_size(64, 1, 2, 64) == 0
+    assert lib.attn_delta_workspace_size(0, 1, 2, 128) == 0

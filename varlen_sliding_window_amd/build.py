@@ -13,7 +13,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["schedule.hip", "fwd.hip", "bwd.hip", "api.hip"]
+SOURCES = ["schedule.hip", "fwd.hip", "bwd.hip", "delta.hip", "api.hip"]
 OUTPUT = os.path.join(HERE, "libattn_varlen.so")
 
 

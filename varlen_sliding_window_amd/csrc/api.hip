@@ -74,8 +74,8 @@ attn_status check_common(const void* q, const void* k, const void* v, const int3
 }
 
 // ---- optional kernel timing (attn_varlen_profile_start / _stop) ----------
-enum KernelId { K_SCHEDULE = 0, K_FORWARD, K_DQ, K_DKDV, K_COUNT };
-const char* const kKernelNames[K_COUNT] = {"schedule", "forward", "dq", "dkdv"};
+enum KernelId { K_SCHEDULE = 0, K_FORWARD, K_DQ, K_DKDV, K_DELTA, K_COUNT };
+const char* const kKernelNames[K_COUNT] = {"schedule", "forward", "dq", "dkdv", "delta_fwd"};
 
 struct ProfileRecord {
   int kernel;
@@ -263,6 +263,43 @@ attn_status attn_varlen_band_bwd(const void* q, const void* k, const void* v, co
   return bwd_impl(q, k, v, out, lse, dout, cu_seqlens, num_seqs, total_tokens, num_q_heads,
                   num_kv_heads, head_dim, max_seqlen, window, scale, 0.f, 0u, true, dq, dk, dv,
                   workspace, workspace_bytes, stream);
+}
+
+size_t attn_delta_workspace_size(int32_t total_tokens, int32_t num_seqs_cap, int32_t num_heads,
+                                 int32_t head_dim) {
+  if (total_tokens <= 0 || num_seqs_cap <= 0 || num_heads <= 0 || head_dim != attn::DELTA_DIM)
+    return 0;
+  const attn::DeltaLayout w = attn::delta_layout(total_tokens, num_seqs_cap, num_heads);
+  if (w.chunk_cap * (size_t)num_heads >= ((size_t)1 << 31)) return 0;
+  return w.total;
+}
+
+attn_status attn_delta_fwd(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                           int32_t total_tokens, int32_t num_heads, int32_t head_dim, float scale,
+                           void* out, void* workspace, size_t workspace_bytes,
+                           attn_stream_t stream) {
+  if (total_tokens <= 0 || num_seqs <= 0 || num_heads <= 0) return ATTN_EINVAL;
+  if (head_dim != attn::DELTA_DIM) return ATTN_EUNSUPPORTED;
+  if (!q || !k || !v || !g || !beta || !cu_seqlens || !out) return ATTN_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(g, 4) || !aligned(beta, 4) || !aligned(cu_seqlens, 4))
+    return ATTN_EINVAL;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_EINVAL;
+  const attn::DeltaLayout w = attn::delta_layout(total_tokens, num_seqs, num_heads);
+  if (w.chunk_cap * (size_t)num_heads >= ((size_t)1 << 31) ||
+      (size_t)num_seqs * num_heads * attn::DELTA_DIM >= ((size_t)1 << 31))
+    return ATTN_EUNSUPPORTED;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < w.total) return ATTN_EWORKSPACE;
+  attn_status s = check_device();
+  if (s != ATTN_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (timed_launch(K_DELTA, st, [&] {
+        return attn::launch_delta_fwd(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens,
+                                      num_heads, scale, out, workspace, w, st);
+      }) != hipSuccess)
+    return ATTN_ELAUNCH;
+  return ATTN_OK;
 }
 
 const char* attn_varlen_strerror(attn_status s) {

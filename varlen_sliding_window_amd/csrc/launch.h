@@ -41,4 +41,30 @@ hipError_t launch_dkdv(const void* q, const void* k, const void* v, const float*
                        const void* dout, const Problem& p, void* dk, void* dv, void* workspace,
                        const WorkspaceLayout& w, hipStream_t stream);
 
+// Gated delta-rule forward (delta.hip): chunks of DELTA_CHUNK tokens, head
+// dim DELTA_DIM for keys and values.  Workspace: [header | per-segment chunk
+// offsets | one fp32 record per (chunk, head)].
+constexpr int DELTA_CHUNK = 64;
+constexpr int DELTA_DIM = 128;
+struct DeltaLayout {
+  size_t header, seg_off, records, total;
+  size_t chunk_cap, record_bytes;
+};
+inline DeltaLayout delta_layout(int64_t total_tokens, int64_t num_seqs, int64_t num_heads) {
+  DeltaLayout w;
+  w.chunk_cap = (size_t)((total_tokens + DELTA_CHUNK - 1) / DELTA_CHUNK) + (size_t)num_seqs;
+  w.record_bytes = ((size_t)2 * DELTA_CHUNK * DELTA_DIM + (size_t)DELTA_CHUNK * DELTA_CHUNK +
+                    2 * (size_t)DELTA_CHUNK) * sizeof(float);
+  w.header = 0;
+  w.seg_off = 256;
+  w.records = w.seg_off + align256((size_t)(num_seqs + 1) * sizeof(int));
+  w.total = w.records + w.chunk_cap * (size_t)num_heads * w.record_bytes;
+  return w;
+}
+
+hipError_t launch_delta_fwd(const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, const int32_t* cu_seqlens, int num_seqs,
+                            int total_tokens, int num_heads, float scale, void* out,
+                            void* workspace, const DeltaLayout& w, hipStream_t stream);
+
 }  // namespace attn
