@@ -31,7 +31,7 @@ constexpr int DC = DELTA_CHUNK;       // tokens per chunk
 constexpr int DD = DELTA_DIM;         // d_k = d_v
 constexpr int PLAN_THREADS = 1024;
 constexpr int PREP_THREADS = 256;
-constexpr int SCAN_THREADS = 256;
+constexpr int SCAN_THREADS = 512;
 constexpr int SLICE = 16;             // d_v columns per scan work-group
 constexpr int LP = DD + 1;            // LDS pitch of DD-wide fp32 rows
 
@@ -92,10 +92,11 @@ __global__ __launch_bounds__(PREP_THREADS) void delta_prep_kernel(
     const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
     int nseq, int T, int H, const int* __restrict__ header, const int* __restrict__ seg_off,
     float* __restrict__ records) {
-  __shared__ float Ks[DC * LP];   // K, then the W right-hand side, then W
-  __shared__ float Vs[DC * LP];   // V, then the U0 right-hand side, then U0
-  __shared__ float Qs[DC * LP];
-  __shared__ float As[DC * (DC + 1)];
+  constexpr int BP = DD + 8;   // bf16 row pitch (16 bytes of padding)
+  __shared__ __attribute__((aligned(16))) bf16 Ks[DC * BP];
+  __shared__ __attribute__((aligned(16))) bf16 Qs[DC * BP];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[DC * BP];
+  __shared__ float As[DC * (DC + 1)];   // A, then T = (I + A)^-1 in place
   __shared__ float Gs[DC], Bs[DC];
   const int chunk = blockIdx.x / H, h = blockIdx.x - chunk * H;
   if (chunk >= header[0]) return;
@@ -112,13 +113,15 @@ __global__ __launch_bounds__(PREP_THREADS) void delta_prep_kernel(
   const int tid = threadIdx.x;
   const size_t rs = (size_t)H * DD;   // token stride of q, k, v
 
-  for (int e = tid; e < DC * DD; e += PREP_THREADS) {
-    const int i = e / DD, d = e - i * DD;
-    const bool in = i < n;
-    const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + d;
-    Ks[i * LP + d] = in ? bf(k[off]) : 0.f;
-    Vs[i * LP + d] = in ? bf(v[off]) : 0.f;
-    Qs[i * LP + d] = in ? bf(q[off]) : 0.f;
+  // q and k rows, 16 bytes per lane (rows past the chunk are zero)
+#pragma unroll
+  for (int r = 0; r < DC * DD / 8 / PREP_THREADS; ++r) {
+    const int f = tid + PREP_THREADS * r, i = f / (DD / 8), ch = f % (DD / 8);
+    const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + ch * 8;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(Ks + i * BP + ch * 8) = i < n ? *reinterpret_cast<const uint4*>(k + off) : z;
+    *reinterpret_cast<uint4*>(Qs + i * BP + ch * 8) = i < n ? *reinterpret_cast<const uint4*>(q + off) : z;
+    *reinterpret_cast<uint4*>(Vs + i * BP + ch * 8) = i < n ? *reinterpret_cast<const uint4*>(v + off) : z;
   }
   if (tid < DC) {
     const bool in = tid < n;
@@ -140,21 +143,23 @@ __global__ __launch_bounds__(PREP_THREADS) void delta_prep_kernel(
   {
     const int i0 = (tid / 16) * 4, j0 = (tid % 16) * 4;
     float kk[4][4] = {}, qk[4][4] = {};
-    for (int d = 0; d < DD; ++d) {
-      float ki[4], qi[4], kj[4];
+    for (int d = 0; d < DD; d += 8) {
+      bf16x8 ki[4], qi[4], kj[4];
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        ki[x] = Ks[(i0 + x) * LP + d];
-        qi[x] = Qs[(i0 + x) * LP + d];
-        kj[x] = Ks[(j0 + x) * LP + d];
+        ki[x] = *reinterpret_cast<const bf16x8*>(Ks + (i0 + x) * BP + d);
+        qi[x] = *reinterpret_cast<const bf16x8*>(Qs + (i0 + x) * BP + d);
+        kj[x] = *reinterpret_cast<const bf16x8*>(Ks + (j0 + x) * BP + d);
       }
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
+      for (int e = 0; e < 8; ++e)
 #pragma unroll
-        for (int y = 0; y < 4; ++y) {
-          kk[x][y] += ki[x] * kj[y];
-          qk[x][y] += qi[x] * kj[y];
-        }
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+          for (int y = 0; y < 4; ++y) {
+            kk[x][y] += (float)ki[x][e] * (float)kj[y][e];
+            qk[x][y] += (float)qi[x][e] * (float)kj[y][e];
+          }
     }
 #pragma unroll
     for (int x = 0; x < 4; ++x)
@@ -172,20 +177,59 @@ __global__ __launch_bounds__(PREP_THREADS) void delta_prep_kernel(
     rec[DeltaRecord::END + tid] = tid < n ? __expf(Gs[last] - Gs[tid]) : 0.f;
   }
   __syncthreads();
-  // Right-hand sides, then forward substitution down each column: thread t
-  // owns column t of [W | U0] and reads only rows of its own column.
-  {
-    float* Y = tid < DD ? Ks : Vs;
-    const int col = tid < DD ? tid : tid - DD;
-    const bool wcol = tid < DD;
-    for (int i = 0; i < DC; ++i) {
-      const float scale_i = wcol ? Bs[i] * __expf(Gs[i]) : Bs[i];
-      float y = Y[i * LP + col] * scale_i;
-      for (int j = 0; j < i; ++j) y -= As[i * (DC + 1) + j] * Y[j * LP + col];
-      Y[i * LP + col] = y;
+  // T = (I + A)^-1, unit lower triangular, row by row in place of A: for
+  // c < i, T_ic = -A_ic - sum_{c < j < i} A_ij T_jc (thread c).  Row i reads
+  // its own A entries and the finished rows j < i, and is written only after
+  // every thread of the row has read it.
+  for (int i = 1; i < DC; ++i) {
+    float acc = 0.f;
+    if (tid < i) {
+      const int c = tid;
+      // four interleaved partial sums shorten the dependent chain
+      float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+      int j = c + 1;
+      for (; j + 3 < i; j += 4) {
+        p0 += As[i * (DC + 1) + j] * As[j * (DC + 1) + c];
+        p1 += As[i * (DC + 1) + j + 1] * As[(j + 1) * (DC + 1) + c];
+        p2 += As[i * (DC + 1) + j + 2] * As[(j + 2) * (DC + 1) + c];
+        p3 += As[i * (DC + 1) + j + 3] * As[(j + 3) * (DC + 1) + c];
+      }
+      for (; j < i; ++j) p0 += As[i * (DC + 1) + j] * As[j * (DC + 1) + c];
+      acc = -As[i * (DC + 1) + c] - ((p0 + p1) + (p2 + p3));
     }
-    float* dst = rec + (wcol ? DeltaRecord::W : DeltaRecord::U0);
-    for (int i = 0; i < DC; ++i) dst[i * DD + col] = Y[i * LP + col];
+    __syncthreads();
+    if (tid < i) As[i * (DC + 1) + tid] = acc;
+    __syncthreads();
+  }
+  // W = T diag(beta gamma) K and U0 = T diag(beta) V: thread (4 rows, 8
+  // columns) of each, T's diagonal being 1.
+  {
+    const int i0 = (tid / 16) * 4, d8 = (tid % 16) * 8;
+    float w[4][8] = {}, u[4][8] = {};
+    for (int j = 0; j < DC; ++j) {
+      const float sw = Bs[j] * __expf(Gs[j]), su = Bs[j];
+      const bf16x8 kv = *reinterpret_cast<const bf16x8*>(Ks + j * BP + d8);
+      const bf16x8 vv = *reinterpret_cast<const bf16x8*>(Vs + j * BP + d8);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int i = i0 + x;
+        const float t = j < i ? As[i * (DC + 1) + j] : (j == i ? 1.f : 0.f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          w[x][e] += t * sw * (float)kv[e];
+          u[x][e] += t * su * (float)vv[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      float4* dw = reinterpret_cast<float4*>(rec + DeltaRecord::W + (i0 + x) * DD + d8);
+      float4* du = reinterpret_cast<float4*>(rec + DeltaRecord::U0 + (i0 + x) * DD + d8);
+      dw[0] = make_float4(w[x][0], w[x][1], w[x][2], w[x][3]);
+      dw[1] = make_float4(w[x][4], w[x][5], w[x][6], w[x][7]);
+      du[0] = make_float4(u[x][0], u[x][1], u[x][2], u[x][3]);
+      du[1] = make_float4(u[x][4], u[x][5], u[x][6], u[x][7]);
+    }
   }
 }
 
@@ -222,10 +266,12 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
   const size_t rs = (size_t)H * DD;
   for (int e = tid; e < SLICE * LP; e += SCAN_THREADS) Ss[e] = 0.f;
 
-  // register staging of one chunk: W (8 float4), q and k (4 x 8 bf16 each),
-  // P (4 float4), the slice of U0 (1 float4), gamma / end decay (1 float)
-  float4 wr[8], pr[4], ur;
-  uint4 qr[4], kr[4];
+  // register staging of one chunk: W, P, q and k rows, the slice of U0 and
+  // gamma / end decay, spread over the work-group's threads
+  constexpr int NT = SCAN_THREADS;
+  constexpr int WR = DC * DD / 4 / NT, PR = DC * DC / 4 / NT, QR = DC * DD / 8 / NT;
+  float4 wr[WR], pr[PR], ur = make_float4(0.f, 0.f, 0.f, 0.f);
+  uint4 qr[QR], kr[QR];
   float gr = 0.f;
   auto fetch = [&](int ci) {
     const int c0 = a + ci * DC;
@@ -233,16 +279,18 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
     const float* rec = records + ((size_t)(first + ci) * H + h) * DeltaRecord::FLOATS;
     const float4* r4 = reinterpret_cast<const float4*>(rec);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) wr[r] = r4[DeltaRecord::W / 4 + tid + 256 * r];
+    for (int r = 0; r < WR; ++r) wr[r] = r4[DeltaRecord::W / 4 + tid + NT * r];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pr[r] = r4[DeltaRecord::P / 4 + tid + 256 * r];
-      const int f = tid + 256 * r, i = f / 16, ch = f % 16;
+    for (int r = 0; r < PR; ++r) pr[r] = r4[DeltaRecord::P / 4 + tid + NT * r];
+#pragma unroll
+    for (int r = 0; r < QR; ++r) {
+      const int f = tid + NT * r, i = f / (DD / 8), ch = f % (DD / 8);
       const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + ch * 8;
       qr[r] = i < n ? *reinterpret_cast<const uint4*>(q + off) : make_uint4(0, 0, 0, 0);
       kr[r] = i < n ? *reinterpret_cast<const uint4*>(k + off) : make_uint4(0, 0, 0, 0);
     }
-    ur = r4[(DeltaRecord::U0 + (size_t)(tid / 4) * DD + cbase) / 4 + (tid % 4)];
+    if (tid < DC * SLICE / 4)
+      ur = r4[(DeltaRecord::U0 + (size_t)(tid / (SLICE / 4)) * DD + cbase) / 4 + (tid % (SLICE / 4))];
     gr = tid < DC ? rec[DeltaRecord::GAM + tid] : (tid < 2 * DC ? rec[DeltaRecord::END + tid - DC] : 0.f);
   };
   if (count > 0) fetch(0);
@@ -252,26 +300,29 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
     const int n = min(DC, b - c0);
     __syncthreads();   // every read of the previous chunk's LDS data is done
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int f = tid + 256 * r, i = f / 32, c4 = (f % 32) * 4;
+    for (int r = 0; r < WR; ++r) {
+      const int f = tid + NT * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
       Ws[i * LP + c4] = wr[r].x;
       Ws[i * LP + c4 + 1] = wr[r].y;
       Ws[i * LP + c4 + 2] = wr[r].z;
       Ws[i * LP + c4 + 3] = wr[r].w;
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int f = tid + 256 * r;
-      const int pi = f / 16, pj = (f % 16) * 4;
+    for (int r = 0; r < PR; ++r) {
+      const int f = tid + NT * r, pi = f / (DC / 4), pj = (f % (DC / 4)) * 4;
       Ps[pi * (DC + 1) + pj] = pr[r].x;
       Ps[pi * (DC + 1) + pj + 1] = pr[r].y;
       Ps[pi * (DC + 1) + pj + 2] = pr[r].z;
       Ps[pi * (DC + 1) + pj + 3] = pr[r].w;
-      *reinterpret_cast<uint4*>(Qs + pi * BP + (f % 16) * 8) = qr[r];
-      *reinterpret_cast<uint4*>(Ks + pi * BP + (f % 16) * 8) = kr[r];
     }
-    {
-      const int i = tid / 4, c4 = (tid % 4) * 4;
+#pragma unroll
+    for (int r = 0; r < QR; ++r) {
+      const int f = tid + NT * r, i = f / (DD / 8), ch = f % (DD / 8);
+      *reinterpret_cast<uint4*>(Qs + i * BP + ch * 8) = qr[r];
+      *reinterpret_cast<uint4*>(Ks + i * BP + ch * 8) = kr[r];
+    }
+    if (tid < DC * SLICE / 4) {
+      const int i = tid / (SLICE / 4), c4 = (tid % (SLICE / 4)) * 4;
       U0s[i * (SLICE + 1) + c4] = ur.x;
       U0s[i * (SLICE + 1) + c4 + 1] = ur.y;
       U0s[i * (SLICE + 1) + c4 + 2] = ur.z;
@@ -282,57 +333,57 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
     __syncthreads();
     if (ci + 1 < count) fetch(ci + 1);
 
-    // U = U0 - W S^T and Q S^T: thread (row i, 4 slice columns)
-    const int i = tid / 4, c4 = (tid % 4) * 4;
+    // U = U0 - W S^T and Q S^T: thread (row i, CPT slice columns)
+    constexpr int CPT = DC * SLICE / NT;          // columns per thread
+    const int i = tid / (SLICE / CPT), cc = (tid % (SLICE / CPT)) * CPT;
     {
-      float ws[4] = {0.f, 0.f, 0.f, 0.f}, qs[4] = {0.f, 0.f, 0.f, 0.f};
+      float ws[CPT] = {}, qs[CPT] = {};
       for (int d = 0; d < DD; ++d) {
         const float w = Ws[i * LP + d];
         const float qv = (float)Qs[i * BP + d];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const float sv = Ss[(c4 + x) * LP + d];
+        for (int x = 0; x < CPT; ++x) {
+          const float sv = Ss[(cc + x) * LP + d];
           ws[x] += w * sv;
           qs[x] += qv * sv;
         }
       }
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        Us[i * (SLICE + 1) + c4 + x] = U0s[i * (SLICE + 1) + c4 + x] - ws[x];
-        QSs[i * (SLICE + 1) + c4 + x] = qs[x];
+      for (int x = 0; x < CPT; ++x) {
+        Us[i * (SLICE + 1) + cc + x] = U0s[i * (SLICE + 1) + cc + x] - ws[x];
+        QSs[i * (SLICE + 1) + cc + x] = qs[x];
       }
     }
     __syncthreads();
     // O = scale (gamma Q S^T + P U) for the chunk's rows inside the document
     if (i < n) {
-      float acc[4];
+      float acc[CPT];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) acc[x] = Gm[i] * QSs[i * (SLICE + 1) + c4 + x];
+      for (int x = 0; x < CPT; ++x) acc[x] = Gm[i] * QSs[i * (SLICE + 1) + cc + x];
       for (int j = 0; j <= i; ++j) {
         const float p = Ps[i * (DC + 1) + j];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) acc[x] += p * Us[j * (SLICE + 1) + c4 + x];
+        for (int x = 0; x < CPT; ++x) acc[x] += p * Us[j * (SLICE + 1) + cc + x];
       }
-      bf16x4 o4;
+      bf16* op = out + (size_t)(c0 + i) * rs + (size_t)h * DD + cbase + cc;
 #pragma unroll
-      for (int x = 0; x < 4; ++x) o4[x] = (bf16)(scale * acc[x]);
-      *reinterpret_cast<bf16x4*>(out + (size_t)(c0 + i) * rs + (size_t)h * DD + cbase + c4) = o4;
+      for (int x = 0; x < CPT; ++x) op[x] = (bf16)(scale * acc[x]);
     }
-    // S_C = gamma_C S + U^T diag(end decay) K: thread (row c, 8 columns of d)
+    // S_C = gamma_C S + U^T diag(end decay) K: thread (row c, DPT columns of d)
     {
-      const int c = tid / 16, d8 = (tid % 16) * 8;
-      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      constexpr int DPT = SLICE * DD / NT;
+      const int c = tid / (DD / DPT), d0 = (tid % (DD / DPT)) * DPT;
+      float acc[DPT] = {};
       for (int j = 0; j < n; ++j) {
         const float u = Us[j * (SLICE + 1) + c] * En[j];
-        const bf16x8 kv = *reinterpret_cast<const bf16x8*>(Ks + j * BP + d8);
 #pragma unroll
-        for (int y = 0; y < 8; ++y) acc[y] += u * (float)kv[y];
+        for (int y = 0; y < DPT; ++y) acc[y] += u * (float)Ks[j * BP + d0 + y];
       }
       const float gc = Gm[n - 1];
       // each thread updates only its own entries of S, and every read of S
       // in this chunk came before the last barrier
 #pragma unroll
-      for (int y = 0; y < 8; ++y) Ss[c * LP + d8 + y] = gc * Ss[c * LP + d8 + y] + acc[y];
+      for (int y = 0; y < DPT; ++y) Ss[c * LP + d0 + y] = gc * Ss[c * LP + d0 + y] + acc[y];
     }
   }
 }
