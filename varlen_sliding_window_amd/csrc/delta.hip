@@ -32,7 +32,7 @@ constexpr int DD = DELTA_DIM;         // d_k = d_v
 constexpr int PLAN_THREADS = 1024;
 constexpr int PREP_THREADS = 256;
 constexpr int SCAN_THREADS = 512;
-constexpr int SLICE = 16;             // d_v columns per scan work-group
+constexpr int SLICE = 32;             // d_v columns per scan work-group
 constexpr int LP = DD + 1;            // LDS pitch of DD-wide fp32 rows
 
 __device__ __forceinline__ float bf(const bf16 x) { return (float)x; }
