@@ -209,10 +209,10 @@ attn_status attn_varlen_band_bwd(const void* q, const void* k, const void* v, co
  *   supported   D == 128 (ATTN_EUNSUPPORTED otherwise); any H >= 1
  *   workspace   >= attn_delta_workspace_size(T, num_seqs, H, D) bytes, 256-byte
  *               aligned: per (64-token chunk, head) fp32 records of the chunk's
- *               triangular-solve results, about 82 KB each
+ *               triangular-solve results, about 100 KB each
  * Enqueues three kernels on `stream` (chunk plan, per-chunk preparation,
  * per-document scan); same ownership and error conventions as the
- * attention calls.  No backward yet.
+ * attention calls.
  */
 size_t attn_delta_workspace_size(int32_t total_tokens, int32_t num_seqs_cap, int32_t num_heads,
                                  int32_t head_dim);
@@ -221,6 +221,31 @@ attn_status attn_delta_fwd(const void* q, const void* k, const void* v, const fl
                            const float* beta, const int32_t* cu_seqlens, int32_t num_seqs,
                            int32_t total_tokens, int32_t num_heads, int32_t head_dim, float scale,
                            void* out, void* workspace, size_t workspace_bytes,
+                           attn_stream_t stream);
+
+/*
+ * Gated delta-rule backward: the gradients of sum(dout * out) for the
+ * forward above, with the same inputs and checks.
+ *   dout        bf16 [T, H, D]
+ *   dq, dk, dv  bf16 [T, H, D], written for tokens inside documents
+ *   dg, dbeta   fp32 [T, H], written for tokens inside documents
+ *   workspace   >= attn_delta_bwd_workspace_size(T, num_seqs, H, D) bytes,
+ *               256-byte aligned: the forward's records (recomputed, with the
+ *               triangular inverse kept), each chunk's start state and
+ *               end-state gradient (fp32 D x D) and its dU, about 264 KB per
+ *               (64-token chunk, head)
+ * Recomputes the forward (no saved tensors cross the boundary) and runs a
+ * reverse per-document scan and two per-chunk gradient kernels: six kernels
+ * on `stream`, nothing allocated.
+ */
+size_t attn_delta_bwd_workspace_size(int32_t total_tokens, int32_t num_seqs_cap,
+                                     int32_t num_heads, int32_t head_dim);
+
+attn_status attn_delta_bwd(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const void* dout, const int32_t* cu_seqlens,
+                           int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                           int32_t head_dim, float scale, void* dq, void* dk, void* dv, float* dg,
+                           float* dbeta, void* workspace, size_t workspace_bytes,
                            attn_stream_t stream);
 
 /* Static description of a status code (never NULL). */
@@ -236,7 +261,7 @@ int32_t attn_varlen_version(void);
  * events recorded on the call's stream.  attn_varlen_profile_stop() turns
  * recording off, waits for the recorded events, and writes up to `cap`
  * per-kernel summaries (kernels in launch-pipeline order: "schedule",
- * "forward", "dq", "dkdv"; only kernels that ran).  It returns the number of
+ * "forward", "dq", "dkdv", "delta_fwd", "delta_bwd"; only kernels that ran).  It returns the number of
  * kernels that ran (which may exceed cap), or a negative attn_status.  The
  * events add a few microseconds per launch, so time whole calls with
  * recording off.  Not for use while another thread is issuing calls.

@@ -10,6 +10,8 @@ the projections): with the microbatch's cu_seqlens and one
   v     standard_normal [T, H, D] rounded to bf16;
   g     log of uniform(0.85, 0.999) [T, H] (per-token decay), fp32;
   beta  uniform(0.05, 0.95) [T, H] (write strength), fp32.
+The output gradient of the backward (``make_delta_dout``) is standard_normal
+[T, H, D] from its own ``default_rng(seed)``, rounded to bf16.
 The bf16 values come back as raw bit patterns (what the GPU reads) and as the
 equal float32 arrays (what the oracle reads).
 """
@@ -51,3 +53,10 @@ def make_delta_inputs(cu_seqlens, num_heads: int, head_dim: int, seed: int) -> D
     beta = rng.uniform(0.05, 0.95, size=(t, num_heads)).astype(np.float32)
     return DeltaInputs(cu, f32_to_bf16_bits(q.astype(np.float32)), f32_to_bf16_bits(k.astype(np.float32)),
                        f32_to_bf16_bits(v), g, beta)
+
+
+def make_delta_dout(num_tokens: int, num_heads: int, head_dim: int, seed: int) -> np.ndarray:
+    """bf16 bit pattern [T, H, D] of a standard-normal output gradient."""
+    rng = np.random.default_rng(seed)
+    return f32_to_bf16_bits(rng.standard_normal((num_tokens, num_heads, head_dim),
+                                                dtype=np.float32))

@@ -17,7 +17,7 @@ EINVAL, EUNSUPPORTED, EWORKSPACE = -1, -2, -3
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_varlen_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(attn_(?:varlen|delta)_\w+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -30,7 +30,8 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert {"attn_varlen_fwd", "attn_varlen_bwd", "attn_varlen_workspace_size",
-            "attn_varlen_strerror"} <= set(names)
+            "attn_varlen_strerror", "attn_delta_fwd", "attn_delta_bwd",
+            "attn_delta_bwd_workspace_size"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
 
@@ -144,3 +145,26 @@ def test_delta_rejects(lib):
     assert lib.attn_delta_workspace_size(64, 1, 2, 128) > 0
     assert lib.attn_delta_workspace_size(64, 1, 2, 64) == 0
     assert lib.attn_delta_workspace_size(0, 1, 2, 128) == 0
+
+
+def test_delta_bwd_rejects(lib):
+    f = lib.attn_delta_bwd
+    base = [FAKE] * 7 + [1, 64, 2, 128, 0.088] + [FAKE] * 6 + [1 << 31, None]
+    for pos, val, code in ((0, None, EINVAL), (5, None, EINVAL), (5, FAKE + 8, EINVAL),
+                           (12, None, EINVAL), (15, None, EINVAL), (16, FAKE + 2, EINVAL),
+                           (10, 64, EUNSUPPORTED), (11, -1.0, EINVAL), (9, 0, EINVAL),
+                           (17, None, EWORKSPACE), (17, FAKE + 16, EWORKSPACE),
+                           (18, 1024, EWORKSPACE)):
+        args = list(base)
+        args[pos] = val
+        assert f(*args) == code, (pos, val)
+
+
+def test_delta_bwd_workspace_size(lib):
+    fwd = lib.attn_delta_workspace_size(16384, 64, 8, 128)
+    bwd = lib.attn_delta_bwd_workspace_size(16384, 64, 8, 128)
+    chunks = 16384 // 64 + 64
+    # per (chunk, head): the record, two fp32 128 x 128 states and a 64 x 128 dU
+    assert bwd - fwd == chunks * 8 * (2 * 128 * 128 + 64 * 128) * 4
+    assert lib.attn_delta_bwd_workspace_size(64, 1, 2, 96) == 0
+    assert lib.attn_delta_bwd_workspace_size(0, 1, 2, 128) == 0

@@ -5,10 +5,12 @@ the computation runs in hand-written HIP kernels.  ``flops`` holds the exact
 work counts used for throughput.
 """
 from . import flops
-from ._binding import (LIBRARY_PATH, AttnError, bwd, delta_fwd, delta_workspace_size, fwd,
+from ._binding import (LIBRARY_PATH, AttnError, bwd, delta_bwd, delta_bwd_workspace_size, delta_fwd,
+                       delta_workspace_size, fwd,
                        load_library, new_workspace, profile_start, profile_stop, strerror,
                        workspace_size)
 
-__all__ = ["LIBRARY_PATH", "AttnError", "bwd", "delta_fwd", "delta_workspace_size", "flops", "fwd",
+__all__ = ["LIBRARY_PATH", "AttnError", "bwd", "delta_bwd", "delta_bwd_workspace_size", "delta_fwd",
+           "delta_workspace_size", "flops", "fwd",
            "load_library", "new_workspace", "profile_start", "profile_stop", "strerror",
            "workspace_size"]

@@ -74,8 +74,9 @@ attn_status check_common(const void* q, const void* k, const void* v, const int3
 }
 
 // ---- optional kernel timing (attn_varlen_profile_start / _stop) ----------
-enum KernelId { K_SCHEDULE = 0, K_FORWARD, K_DQ, K_DKDV, K_DELTA, K_COUNT };
-const char* const kKernelNames[K_COUNT] = {"schedule", "forward", "dq", "dkdv", "delta_fwd"};
+enum KernelId { K_SCHEDULE = 0, K_FORWARD, K_DQ, K_DKDV, K_DELTA, K_DELTA_BWD, K_COUNT };
+const char* const kKernelNames[K_COUNT] = {"schedule", "forward", "dq",
+                                           "dkdv",     "delta_fwd", "delta_bwd"};
 
 struct ProfileRecord {
   int kernel;
@@ -265,13 +266,44 @@ attn_status attn_varlen_band_bwd(const void* q, const void* k, const void* v, co
                   workspace, workspace_bytes, stream);
 }
 
-size_t attn_delta_workspace_size(int32_t total_tokens, int32_t num_seqs_cap, int32_t num_heads,
-                                 int32_t head_dim) {
+namespace {
+// Shape and pointer checks shared by the delta-rule calls.
+attn_status check_delta(const void* q, const void* k, const void* v, const float* g,
+                        const float* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                        int32_t total_tokens, int32_t num_heads, int32_t head_dim, float scale) {
+  if (total_tokens <= 0 || num_seqs <= 0 || num_heads <= 0) return ATTN_EINVAL;
+  if (head_dim != attn::DELTA_DIM) return ATTN_EUNSUPPORTED;
+  if (!q || !k || !v || !g || !beta || !cu_seqlens) return ATTN_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, 4) ||
+      !aligned(beta, 4) || !aligned(cu_seqlens, 4))
+    return ATTN_EINVAL;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_EINVAL;
+  const attn::DeltaLayout w = attn::delta_layout(total_tokens, num_seqs, num_heads);
+  if (w.chunk_cap * (size_t)num_heads >= ((size_t)1 << 31) ||
+      (size_t)num_seqs * num_heads * attn::DELTA_DIM >= ((size_t)1 << 31))
+    return ATTN_EUNSUPPORTED;
+  return ATTN_OK;
+}
+
+size_t delta_workspace(int32_t total_tokens, int32_t num_seqs_cap, int32_t num_heads,
+                       int32_t head_dim, bool backward) {
   if (total_tokens <= 0 || num_seqs_cap <= 0 || num_heads <= 0 || head_dim != attn::DELTA_DIM)
     return 0;
-  const attn::DeltaLayout w = attn::delta_layout(total_tokens, num_seqs_cap, num_heads);
+  const attn::DeltaLayout w =
+      attn::delta_layout(total_tokens, num_seqs_cap, num_heads, backward);
   if (w.chunk_cap * (size_t)num_heads >= ((size_t)1 << 31)) return 0;
   return w.total;
+}
+}  // namespace
+
+size_t attn_delta_workspace_size(int32_t total_tokens, int32_t num_seqs_cap, int32_t num_heads,
+                                 int32_t head_dim) {
+  return delta_workspace(total_tokens, num_seqs_cap, num_heads, head_dim, false);
+}
+
+size_t attn_delta_bwd_workspace_size(int32_t total_tokens, int32_t num_seqs_cap,
+                                     int32_t num_heads, int32_t head_dim) {
+  return delta_workspace(total_tokens, num_seqs_cap, num_heads, head_dim, true);
 }
 
 attn_status attn_delta_fwd(const void* q, const void* k, const void* v, const float* g,
@@ -279,24 +311,44 @@ attn_status attn_delta_fwd(const void* q, const void* k, const void* v, const fl
                            int32_t total_tokens, int32_t num_heads, int32_t head_dim, float scale,
                            void* out, void* workspace, size_t workspace_bytes,
                            attn_stream_t stream) {
-  if (total_tokens <= 0 || num_seqs <= 0 || num_heads <= 0) return ATTN_EINVAL;
-  if (head_dim != attn::DELTA_DIM) return ATTN_EUNSUPPORTED;
-  if (!q || !k || !v || !g || !beta || !cu_seqlens || !out) return ATTN_EINVAL;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
-      !aligned(g, 4) || !aligned(beta, 4) || !aligned(cu_seqlens, 4))
-    return ATTN_EINVAL;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_EINVAL;
+  attn_status s = check_delta(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
+                              head_dim, scale);
+  if (s != ATTN_OK) return s;
+  if (!out || !aligned(out, 16)) return ATTN_EINVAL;
   const attn::DeltaLayout w = attn::delta_layout(total_tokens, num_seqs, num_heads);
-  if (w.chunk_cap * (size_t)num_heads >= ((size_t)1 << 31) ||
-      (size_t)num_seqs * num_heads * attn::DELTA_DIM >= ((size_t)1 << 31))
-    return ATTN_EUNSUPPORTED;
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < w.total) return ATTN_EWORKSPACE;
-  attn_status s = check_device();
+  s = check_device();
   if (s != ATTN_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (timed_launch(K_DELTA, st, [&] {
         return attn::launch_delta_fwd(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens,
                                       num_heads, scale, out, workspace, w, st);
+      }) != hipSuccess)
+    return ATTN_ELAUNCH;
+  return ATTN_OK;
+}
+
+attn_status attn_delta_bwd(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const void* dout, const int32_t* cu_seqlens,
+                           int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                           int32_t head_dim, float scale, void* dq, void* dk, void* dv, float* dg,
+                           float* dbeta, void* workspace, size_t workspace_bytes,
+                           attn_stream_t stream) {
+  attn_status s = check_delta(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
+                              head_dim, scale);
+  if (s != ATTN_OK) return s;
+  if (!dout || !dq || !dk || !dv || !dg || !dbeta) return ATTN_EINVAL;
+  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(dg, 4) || !aligned(dbeta, 4))
+    return ATTN_EINVAL;
+  const attn::DeltaLayout w = attn::delta_layout(total_tokens, num_seqs, num_heads, true);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < w.total) return ATTN_EWORKSPACE;
+  s = check_device();
+  if (s != ATTN_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (timed_launch(K_DELTA_BWD, st, [&] {
+        return attn::launch_delta_bwd(q, k, v, g, beta, dout, cu_seqlens, num_seqs, total_tokens,
+                                      num_heads, scale, dq, dk, dv, dg, dbeta, workspace, w, st);
       }) != hipSuccess)
     return ATTN_ELAUNCH;
   return ATTN_OK;
@@ -314,7 +366,7 @@ const char* attn_varlen_strerror(attn_status s) {
   return "unknown status";
 }
 
-int32_t attn_varlen_version(void) { return 210; }
+int32_t attn_varlen_version(void) { return 220; }
 
 attn_status attn_varlen_profile_start(void) {
   std::lock_guard<std::mutex> lock(g_prof_mu);

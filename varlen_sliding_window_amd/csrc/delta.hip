@@ -76,22 +76,30 @@ __global__ __launch_bounds__(PLAN_THREADS) void delta_plan_kernel(const int32_t*
   }
 }
 
-// One record per (chunk, head): W [DC][DD], U0 [DC][DD], P [DC][DC], gamma
-// [DC], decay to the chunk end [DC], fp32.
+// One record per (chunk, head), fp32: W [DC][DD] (the backward overwrites it
+// with dW), U0 [DC][DD] (U after a saving scan), P [DC][DC], gamma [DC],
+// decay to the chunk end [DC], T = (I + A)^-1 [DC][DC] (backward only), and
+// side values of the backward: the output term's decay gradient [DC], the
+// end-decay gradients [DC] and the end-state decay gradient [1].
 struct DeltaRecord {
   static constexpr size_t W = 0;
   static constexpr size_t U0 = W + (size_t)DC * DD;
   static constexpr size_t P = U0 + (size_t)DC * DD;
   static constexpr size_t GAM = P + (size_t)DC * DC;
   static constexpr size_t END = GAM + DC;
-  static constexpr size_t FLOATS = END + DC;
+  static constexpr size_t TI = END + DC;
+  static constexpr size_t SIDE = TI + (size_t)DC * DC;
+  static constexpr size_t FLOATS = SIDE + 4 * DC;
 };
+static_assert(DeltaRecord::FLOATS == delta_record_floats(), "record layout");
+static_assert(DeltaRecord::FLOATS % 4 == 0 && DeltaRecord::U0 % 4 == 0 && DeltaRecord::P % 4 == 0,
+              "records and their fields stay 16-byte aligned");
 
 __global__ __launch_bounds__(PREP_THREADS) void delta_prep_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
     int nseq, int T, int H, const int* __restrict__ header, const int* __restrict__ seg_off,
-    float* __restrict__ records) {
+    float* __restrict__ records, int keep_inverse) {
   constexpr int BP = DD + 8;   // bf16 row pitch (16 bytes of padding)
   __shared__ __attribute__((aligned(16))) bf16 Ks[DC * BP];
   __shared__ __attribute__((aligned(16))) bf16 Qs[DC * BP];
@@ -201,6 +209,11 @@ __global__ __launch_bounds__(PREP_THREADS) void delta_prep_kernel(
     if (tid < i) As[i * (DC + 1) + tid] = acc;
     __syncthreads();
   }
+  if (keep_inverse)   // T with its unit diagonal, zero above it
+    for (int f = tid; f < DC * DC; f += PREP_THREADS) {
+      const int i = f / DC, j = f % DC;
+      rec[DeltaRecord::TI + f] = j < i ? As[i * (DC + 1) + j] : (j == i ? 1.f : 0.f);
+    }
   // W = T diag(beta gamma) K and U0 = T diag(beta) V: thread (4 rows, 8
   // columns) of each, T's diagonal being 1.
   {
@@ -235,11 +248,14 @@ __global__ __launch_bounds__(PREP_THREADS) void delta_prep_kernel(
 
 // Walks a document's chunks in order for one head and a slice of SLICE d_v
 // columns, carrying those rows of S in LDS.  The next chunk's record and q/k
-// rows are loaded into registers while the current chunk computes.
+// rows are loaded into registers while the current chunk computes.  With
+// `states`, it also stores each chunk's start state there and the chunk's U
+// over the record's U0 (each work-group owns its slice of both); with a null
+// `out`, it writes no output.
 __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const int32_t* __restrict__ cu,
     int nseq, int T, int H, float scale, const int* __restrict__ seg_off,
-    const float* __restrict__ records, bf16* __restrict__ out) {
+    float* __restrict__ records, bf16* __restrict__ out, float* __restrict__ states) {
   constexpr int SL = DD / SLICE;       // slices per head
   constexpr int BP = DD + 8;           // bf16 row pitch (16 bytes of padding)
   __shared__ float Ss[SLICE * LP];     // S rows c0 .. c0 + SLICE - 1, all d_k
@@ -332,6 +348,16 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
     else if (tid < 2 * DC) En[tid - DC] = gr;
     __syncthreads();
     if (ci + 1 < count) fetch(ci + 1);
+    const size_t unit = (size_t)(first + ci) * H + h;
+    if (states) {   // this slice's rows of the chunk's start state
+      float* st = states + unit * DD * DD + (size_t)cbase * DD;
+#pragma unroll
+      for (int r = 0; r < SLICE * DD / 4 / NT; ++r) {
+        const int e4 = tid + NT * r, row = e4 / (DD / 4), c4 = (e4 % (DD / 4)) * 4;
+        const float* src = Ss + row * LP + c4;
+        *reinterpret_cast<float4*>(st + row * DD + c4) = make_float4(src[0], src[1], src[2], src[3]);
+      }
+    }
 
     // U = U0 - W S^T and Q S^T: thread (row i, CPT slice columns)
     constexpr int CPT = DC * SLICE / NT;          // columns per thread
@@ -353,10 +379,15 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
         Us[i * (SLICE + 1) + cc + x] = U0s[i * (SLICE + 1) + cc + x] - ws[x];
         QSs[i * (SLICE + 1) + cc + x] = qs[x];
       }
+      if (states) {
+        float* urec = records + unit * DeltaRecord::FLOATS + DeltaRecord::U0 + (size_t)i * DD + cbase + cc;
+#pragma unroll
+        for (int x = 0; x < CPT; ++x) urec[x] = U0s[i * (SLICE + 1) + cc + x] - ws[x];
+      }
     }
     __syncthreads();
     // O = scale (gamma Q S^T + P U) for the chunk's rows inside the document
-    if (i < n) {
+    if (out && i < n) {
       float acc[CPT];
 #pragma unroll
       for (int x = 0; x < CPT; ++x) acc[x] = Gm[i] * QSs[i * (SLICE + 1) + cc + x];
@@ -388,6 +419,674 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
   }
 }
 
+
+// Reverse of the scan: walks a document's chunks from the last for one head
+// and a slice of SLICE d_v rows of dS (the gradient of the state), starting
+// from zero after the document's last token.  Per chunk it stores dS (the
+// end-state gradient) and dU, then steps dS back to the chunk's start.
+__global__ __launch_bounds__(SCAN_THREADS) void delta_rscan_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ dout,
+    const int32_t* __restrict__ cu, int nseq, int T, int H, float scale,
+    const int* __restrict__ seg_off, const float* __restrict__ records,
+    float* __restrict__ dstates, float* __restrict__ dubuf) {
+  constexpr int SL = DD / SLICE;
+  constexpr int BP = DD + 8;
+  constexpr int OP = SLICE + 1;
+  __shared__ float dSs[SLICE * LP];    // dS rows c0 .. c0 + SLICE - 1, all d_k
+  __shared__ float Ws[DC * LP];
+  __shared__ __attribute__((aligned(16))) bf16 Qs[DC * BP];
+  __shared__ __attribute__((aligned(16))) bf16 Ks[DC * BP];
+  __shared__ float Ps[DC * (DC + 1)];
+  __shared__ float dOs[DC * OP];
+  __shared__ float dUs[DC * OP];
+  __shared__ float Gm[DC], En[DC];
+  const int sl = blockIdx.x % SL;
+  const int h = (blockIdx.x / SL) % H;
+  const int s = blockIdx.x / (SL * H);
+  if (s >= nseq) return;
+  const int a = min(max(cu[s], 0), T);
+  const int b = min(max(cu[s + 1], a), T);
+  const int total = seg_off[nseq];
+  const int first = min(seg_off[s], total);
+  const int count = max(0, min(seg_off[s + 1], total) - first);
+  const int tid = threadIdx.x;
+  const int cbase = sl * SLICE;
+  const size_t rs = (size_t)H * DD;
+  for (int e = tid; e < SLICE * LP; e += SCAN_THREADS) dSs[e] = 0.f;
+
+  constexpr int NT = SCAN_THREADS;
+  constexpr int WR = DC * DD / 4 / NT, PR = DC * DC / 4 / NT, QR = DC * DD / 8 / NT;
+  constexpr int OR = DC * SLICE / 8;   // threads loading 8 dO values each
+  float4 wr[WR], pr[PR];
+  uint4 qr[QR], kr[QR], dor = make_uint4(0, 0, 0, 0);
+  float gr = 0.f;
+  auto fetch = [&](int ci) {
+    const int c0 = a + ci * DC;
+    const int n = min(DC, b - c0);
+    const float* rec = records + ((size_t)(first + ci) * H + h) * DeltaRecord::FLOATS;
+    const float4* r4 = reinterpret_cast<const float4*>(rec);
+#pragma unroll
+    for (int r = 0; r < WR; ++r) wr[r] = r4[DeltaRecord::W / 4 + tid + NT * r];
+#pragma unroll
+    for (int r = 0; r < PR; ++r) pr[r] = r4[DeltaRecord::P / 4 + tid + NT * r];
+#pragma unroll
+    for (int r = 0; r < QR; ++r) {
+      const int f = tid + NT * r, i = f / (DD / 8), ch = f % (DD / 8);
+      const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + ch * 8;
+      qr[r] = i < n ? *reinterpret_cast<const uint4*>(q + off) : make_uint4(0, 0, 0, 0);
+      kr[r] = i < n ? *reinterpret_cast<const uint4*>(k + off) : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < OR) {
+      const int i = tid / (SLICE / 8), ch = tid % (SLICE / 8);
+      const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + cbase + ch * 8;
+      dor = i < n ? *reinterpret_cast<const uint4*>(dout + off) : make_uint4(0, 0, 0, 0);
+    }
+    gr = tid < DC ? rec[DeltaRecord::GAM + tid] : (tid < 2 * DC ? rec[DeltaRecord::END + tid - DC] : 0.f);
+  };
+  if (count > 0) fetch(count - 1);
+
+  for (int ci = count - 1; ci >= 0; --ci) {
+    const int n = min(DC, b - (a + ci * DC));
+    __syncthreads();   // every read of the previous chunk's LDS data is done
+#pragma unroll
+    for (int r = 0; r < WR; ++r) {
+      const int f = tid + NT * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
+      Ws[i * LP + c4] = wr[r].x;
+      Ws[i * LP + c4 + 1] = wr[r].y;
+      Ws[i * LP + c4 + 2] = wr[r].z;
+      Ws[i * LP + c4 + 3] = wr[r].w;
+    }
+#pragma unroll
+    for (int r = 0; r < PR; ++r) {
+      const int f = tid + NT * r, pi = f / (DC / 4), pj = (f % (DC / 4)) * 4;
+      Ps[pi * (DC + 1) + pj] = pr[r].x;
+      Ps[pi * (DC + 1) + pj + 1] = pr[r].y;
+      Ps[pi * (DC + 1) + pj + 2] = pr[r].z;
+      Ps[pi * (DC + 1) + pj + 3] = pr[r].w;
+    }
+#pragma unroll
+    for (int r = 0; r < QR; ++r) {
+      const int f = tid + NT * r, i = f / (DD / 8), ch = f % (DD / 8);
+      *reinterpret_cast<uint4*>(Qs + i * BP + ch * 8) = qr[r];
+      *reinterpret_cast<uint4*>(Ks + i * BP + ch * 8) = kr[r];
+    }
+    if (tid < OR) {
+      const int i = tid / (SLICE / 8), ch = tid % (SLICE / 8);
+      bf16x8 ov;
+      __builtin_memcpy(&ov, &dor, sizeof(ov));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dOs[i * OP + ch * 8 + e] = (float)ov[e];
+    }
+    if (tid < DC) Gm[tid] = gr;
+    else if (tid < 2 * DC) En[tid - DC] = gr;
+    __syncthreads();
+    if (ci > 0) fetch(ci - 1);
+    const size_t unit = (size_t)(first + ci) * H + h;
+    {   // the end-state gradient of this chunk, this slice's rows
+      float* st = dstates + unit * DD * DD + (size_t)cbase * DD;
+#pragma unroll
+      for (int r = 0; r < SLICE * DD / 4 / NT; ++r) {
+        const int e4 = tid + NT * r, row = e4 / (DD / 4), c4 = (e4 % (DD / 4)) * 4;
+        const float* src = dSs + row * LP + c4;
+        *reinterpret_cast<float4*>(st + row * DD + c4) = make_float4(src[0], src[1], src[2], src[3]);
+      }
+    }
+    // dU = scale P^T dO + diag(end decay) K dS^T: thread (row j, CPT columns)
+    constexpr int CPT = DC * SLICE / NT;
+    {
+      const int j = tid / (SLICE / CPT), cc = (tid % (SLICE / CPT)) * CPT;
+      float kd[CPT] = {}, pd[CPT] = {};
+      for (int d = 0; d < DD; ++d) {
+        const float kv = (float)Ks[j * BP + d];
+#pragma unroll
+        for (int x = 0; x < CPT; ++x) kd[x] += kv * dSs[(cc + x) * LP + d];
+      }
+      for (int i = j; i < n; ++i) {
+        const float p = Ps[i * (DC + 1) + j];
+#pragma unroll
+        for (int x = 0; x < CPT; ++x) pd[x] += p * dOs[i * OP + cc + x];
+      }
+      float* du = dubuf + unit * DC * DD + (size_t)j * DD + cbase + cc;
+#pragma unroll
+      for (int x = 0; x < CPT; ++x) {
+        const float v = En[j] * kd[x] + scale * pd[x];
+        dUs[j * OP + cc + x] = v;
+        du[x] = v;
+      }
+    }
+    __syncthreads();
+    // dS_0 = gamma_C dS + sum_i (scale gamma_i dO_i q_i^T - dU_i w_i^T):
+    // thread (row c, DPT columns of d)
+    {
+      constexpr int DPT = SLICE * DD / NT;
+      const int c = tid / (DD / DPT), d0 = (tid % (DD / DPT)) * DPT;
+      float acc[DPT] = {};
+      for (int i = 0; i < n; ++i) {
+        const float a1 = scale * Gm[i] * dOs[i * OP + c];
+        const float a2 = dUs[i * OP + c];
+#pragma unroll
+        for (int y = 0; y < DPT; ++y)
+          acc[y] += a1 * (float)Qs[i * BP + d0 + y] - a2 * Ws[i * LP + d0 + y];
+      }
+      const float gc = Gm[n - 1];
+#pragma unroll
+      for (int y = 0; y < DPT; ++y) dSs[c * LP + d0 + y] = gc * dSs[c * LP + d0 + y] + acc[y];
+    }
+  }
+}
+
+// Segment and first token of chunk `chunk` (seg_off holds each segment's
+// first chunk): the largest s with seg_off[s] <= chunk.
+__device__ __forceinline__ void delta_chunk_span(const int32_t* __restrict__ cu,
+                                                 const int* __restrict__ seg_off, int nseq, int T,
+                                                 int chunk, int& c0, int& n) {
+  int lo = 0, hi = nseq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (seg_off[mid] <= chunk) lo = mid; else hi = mid - 1;
+  }
+  const int a = min(max(cu[lo], 0), T);
+  const int b = min(max(cu[lo + 1], a), T);
+  c0 = a + (chunk - seg_off[lo]) * DC;
+  n = max(0, min(DC, b - c0));
+}
+
+constexpr int GRAD_THREADS = 256;
+
+// Products with the chunk's start state S_0 and end-state gradient dS_C, per
+// (chunk, head): dQ_state = scale diag(gamma) dO S_0, dW = -dU S_0,
+// dK_state = diag(e) U dS_C, and the decay gradients they imply.  S_0 and
+// dS_C stream through LDS 16 rows at a time; thread (4 rows, 8 columns).
+// dQ_state and dK_state go over this unit's dS_C once it has been read, dW
+// over the record's W.
+__global__ __launch_bounds__(GRAD_THREADS) void delta_gstate_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ dout,
+    const int32_t* __restrict__ cu, int nseq, int T, int H, float scale,
+    const int* __restrict__ header, const int* __restrict__ seg_off, float* __restrict__ records,
+    const float* __restrict__ states, float* __restrict__ dstates,
+    const float* __restrict__ dubuf) {
+  constexpr int BP = DD + 8;
+  constexpr int RB = 16;   // state rows per staging step
+  __shared__ __attribute__((aligned(16))) bf16 dOs[DC * BP];
+  __shared__ float Us[DC * LP];
+  __shared__ float dUs[DC * LP];
+  __shared__ __attribute__((aligned(16))) float S0b[RB * DD];
+  __shared__ __attribute__((aligned(16))) float dSb[RB * DD];
+  __shared__ float red[GRAD_THREADS / 64];
+  const int chunk = blockIdx.x / H, h = blockIdx.x - chunk * H;
+  if (chunk >= header[0]) return;
+  int c0, n;
+  delta_chunk_span(cu, seg_off, nseq, T, chunk, c0, n);
+  const int tid = threadIdx.x;
+  const size_t rs = (size_t)H * DD;
+  const size_t unit = blockIdx.x;
+  float* rec = records + unit * DeltaRecord::FLOATS;
+  const float* S0 = states + unit * DD * DD;
+  float* dS = dstates + unit * DD * DD;
+  const float* dU = dubuf + unit * DC * DD;
+#pragma unroll
+  for (int r = 0; r < DC * DD / 8 / GRAD_THREADS; ++r) {
+    const int f = tid + GRAD_THREADS * r, i = f / (DD / 8), ch = f % (DD / 8);
+    const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + ch * 8;
+    *reinterpret_cast<uint4*>(dOs + i * BP + ch * 8) =
+        i < n ? *reinterpret_cast<const uint4*>(dout + off) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < DC * DD / 4 / GRAD_THREADS; ++r) {
+    const int f = tid + GRAD_THREADS * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
+    const float4 u = reinterpret_cast<const float4*>(rec + DeltaRecord::U0)[f];
+    const float4 du = reinterpret_cast<const float4*>(dU)[f];
+    Us[i * LP + c4] = u.x; Us[i * LP + c4 + 1] = u.y; Us[i * LP + c4 + 2] = u.z; Us[i * LP + c4 + 3] = u.w;
+    dUs[i * LP + c4] = du.x; dUs[i * LP + c4 + 1] = du.y; dUs[i * LP + c4 + 2] = du.z; dUs[i * LP + c4 + 3] = du.w;
+  }
+  const int i0 = (tid / 16) * 4, d8 = (tid % 16) * 8;
+  float aq[4][8] = {}, aw[4][8] = {}, ak[4][8] = {};
+  float dgc = 0.f;   // <dS_C, S_0>, this thread's share
+  for (int cb = 0; cb < DD; cb += RB) {
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < RB * DD / 4 / GRAD_THREADS; ++r) {
+      const int f = tid + GRAD_THREADS * r;
+      const float4 s4 = reinterpret_cast<const float4*>(S0 + (size_t)cb * DD)[f];
+      const float4 d4 = reinterpret_cast<const float4*>(dS + (size_t)cb * DD)[f];
+      reinterpret_cast<float4*>(S0b)[f] = s4;
+      reinterpret_cast<float4*>(dSb)[f] = d4;
+      dgc += s4.x * d4.x + s4.y * d4.y + s4.z * d4.z + s4.w * d4.w;
+    }
+    __syncthreads();
+    for (int c = 0; c < RB; ++c) {
+      const float4 sa = *reinterpret_cast<const float4*>(S0b + c * DD + d8);
+      const float4 sb = *reinterpret_cast<const float4*>(S0b + c * DD + d8 + 4);
+      const float4 ta = *reinterpret_cast<const float4*>(dSb + c * DD + d8);
+      const float4 tb = *reinterpret_cast<const float4*>(dSb + c * DD + d8 + 4);
+      const float s0[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+      const float ds[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const float o = (float)dOs[(i0 + x) * BP + cb + c];
+        const float du = dUs[(i0 + x) * LP + cb + c];
+        const float u = Us[(i0 + x) * LP + cb + c];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          aq[x][e] += o * s0[e];
+          aw[x][e] += du * s0[e];
+          ak[x][e] += u * ds[e];
+        }
+      }
+    }
+  }
+  __syncthreads();   // every read of this unit's dS_C is done before it is overwritten
+  // row dots q_i . (dO S_0)_i and k_i . (U dS_C)_i, summed over the 16 lanes of a row group
+  float qsd[4], kd[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int i = i0 + x;
+    qsd[x] = 0.f;
+    kd[x] = 0.f;
+    if (i < n) {
+      const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + d8;
+      const bf16x8 qv = *reinterpret_cast<const bf16x8*>(q + off);
+      const bf16x8 kv = *reinterpret_cast<const bf16x8*>(k + off);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qsd[x] += (float)qv[e] * aq[x][e];
+        kd[x] += (float)kv[e] * ak[x][e];
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      qsd[x] += __shfl_xor(qsd[x], off);
+      kd[x] += __shfl_xor(kd[x], off);
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) dgc += __shfl_xor(dgc, off);
+  if ((tid & 63) == 0) red[tid >> 6] = dgc;
+  __syncthreads();
+  const float* gam = rec + DeltaRecord::GAM;
+  const float* en = rec + DeltaRecord::END;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int i = i0 + x;
+    const float gq = scale * gam[i], ek = en[i];
+    float4* pq = reinterpret_cast<float4*>(dS + (size_t)i * DD + d8);
+    float4* pk = reinterpret_cast<float4*>(dS + (size_t)DC * DD + (size_t)i * DD + d8);
+    float4* pw = reinterpret_cast<float4*>(rec + DeltaRecord::W + (size_t)i * DD + d8);
+    pq[0] = make_float4(gq * aq[x][0], gq * aq[x][1], gq * aq[x][2], gq * aq[x][3]);
+    pq[1] = make_float4(gq * aq[x][4], gq * aq[x][5], gq * aq[x][6], gq * aq[x][7]);
+    pk[0] = make_float4(ek * ak[x][0], ek * ak[x][1], ek * ak[x][2], ek * ak[x][3]);
+    pk[1] = make_float4(ek * ak[x][4], ek * ak[x][5], ek * ak[x][6], ek * ak[x][7]);
+    pw[0] = make_float4(-aw[x][0], -aw[x][1], -aw[x][2], -aw[x][3]);
+    pw[1] = make_float4(-aw[x][4], -aw[x][5], -aw[x][6], -aw[x][7]);
+    if ((tid & 15) == 0) {
+      rec[DeltaRecord::SIDE + i] = gq * qsd[x];          // gamma_i d(gamma_i), output term
+      rec[DeltaRecord::SIDE + DC + i] = ek * kd[x];      // e_i d(e_i)
+    }
+  }
+  if (tid == 0)   // gamma_C d(gamma_C) of the end state
+    rec[DeltaRecord::SIDE + 2 * DC] = gam[max(n - 1, 0)] * ((red[0] + red[1]) + (red[2] + red[3]));
+}
+
+// The rest of the chunk's gradients, per (chunk, head), all in LDS: the
+// masked scores (dP = scale dO U^T), the triangular solve (dX = T^T dW,
+// dY = T^T dU, dT = dW X^T + dU Y^T, dA = -T^T dT T^T below the diagonal,
+// X = diag(beta gamma) K, Y = diag(beta) V) and the log-decay gradients,
+// summed back onto g inside the chunk.
+__global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, const bf16* __restrict__ dout,
+    const int32_t* __restrict__ cu, int nseq, int T, int H, float scale,
+    const int* __restrict__ header, const int* __restrict__ seg_off,
+    const float* __restrict__ records, const float* __restrict__ dstates,
+    const float* __restrict__ dubuf, bf16* __restrict__ dq, bf16* __restrict__ dk,
+    bf16* __restrict__ dv, float* __restrict__ dg, float* __restrict__ dbeta) {
+  constexpr int BP = DD + 8, CP = DC + 1;
+  __shared__ __attribute__((aligned(16))) bf16 Kb[DC * BP];
+  __shared__ __attribute__((aligned(16))) bf16 Qb[DC * BP];
+  __shared__ __attribute__((aligned(16))) float Vr[DC * BP / 2];   // V (bf16), then a C x C matrix
+  __shared__ __attribute__((aligned(16))) float F1[DC * LP];       // U, then dW
+  __shared__ __attribute__((aligned(16))) float F2[DC * LP];       // dO (bf16), then dU
+  __shared__ float M1[DC * CP], M2[DC * CP];
+  __shared__ float Gs[DC], Bs[DC], gm[DC], dGs[DC], dBs[DC];
+  static_assert(DC * CP <= DC * BP / 2, "a C x C matrix fits where V was");
+  const int chunk = blockIdx.x / H, h = blockIdx.x - chunk * H;
+  if (chunk >= header[0]) return;
+  int c0, n;
+  delta_chunk_span(cu, seg_off, nseq, T, chunk, c0, n);
+  const int tid = threadIdx.x;
+  const size_t rs = (size_t)H * DD;
+  const size_t unit = blockIdx.x;
+  const float* rec = records + unit * DeltaRecord::FLOATS;
+  bf16* Vb = reinterpret_cast<bf16*>(Vr);
+  bf16* dOb = reinterpret_cast<bf16*>(F2);
+  float* M3 = Vr;
+#pragma unroll
+  for (int r = 0; r < DC * DD / 8 / GRAD_THREADS; ++r) {
+    const int f = tid + GRAD_THREADS * r, i = f / (DD / 8), ch = f % (DD / 8);
+    const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + ch * 8;
+    const bool in = i < n;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(Kb + i * BP + ch * 8) = in ? *reinterpret_cast<const uint4*>(k + off) : z;
+    *reinterpret_cast<uint4*>(Qb + i * BP + ch * 8) = in ? *reinterpret_cast<const uint4*>(q + off) : z;
+    *reinterpret_cast<uint4*>(Vb + i * BP + ch * 8) = in ? *reinterpret_cast<const uint4*>(v + off) : z;
+    *reinterpret_cast<uint4*>(dOb + i * BP + ch * 8) = in ? *reinterpret_cast<const uint4*>(dout + off) : z;
+  }
+#pragma unroll
+  for (int r = 0; r < DC * DD / 4 / GRAD_THREADS; ++r) {
+    const int f = tid + GRAD_THREADS * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
+    const float4 u = reinterpret_cast<const float4*>(rec + DeltaRecord::U0)[f];
+    F1[i * LP + c4] = u.x; F1[i * LP + c4 + 1] = u.y; F1[i * LP + c4 + 2] = u.z; F1[i * LP + c4 + 3] = u.w;
+  }
+  if (tid < DC) {
+    const bool in = tid < n;
+    Gs[tid] = in ? g[(size_t)(c0 + tid) * H + h] : 0.f;
+    Bs[tid] = in ? beta[(size_t)(c0 + tid) * H + h] : 0.f;
+    gm[tid] = rec[DeltaRecord::GAM + tid];
+    dGs[tid] = 0.f;
+    dBs[tid] = 0.f;
+  }
+  __syncthreads();
+  if (tid == 0) {   // in-chunk cumulative log decay, summed as the preparation does
+    float acc = 0.f;
+    for (int i = 0; i < DC; ++i) {
+      acc += Gs[i];
+      Gs[i] = acc;
+    }
+  }
+  __syncthreads();
+  const int r0 = (tid / 16) * 4, s0 = (tid % 16) * 4;   // C x C tile: rows r0.., columns s0..
+  const int i0 = r0, d8 = (tid % 16) * 8;               // C x D tile: rows i0.., columns d8..
+
+  // dP = scale dO U^T; the decay gradient of the scores P (x) dP; the masked
+  // decayed dP into M1
+  {
+    float dp[4][4] = {};
+    for (int d = 0; d < DD; ++d) {
+      float o[4], u[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        o[x] = (float)dOb[(r0 + x) * BP + d];
+        u[x] = F1[(s0 + x) * LP + d];
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) dp[x][y] += o[x] * u[y];
+    }
+    float row[4] = {}, col[4] = {};
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        const int i = r0 + x, j = s0 + y;
+        const float dpv = scale * dp[x][y];
+        const float pd = rec[DeltaRecord::P + i * DC + j] * dpv;
+        row[x] += pd;
+        col[y] += pd;
+        M1[i * CP + j] = j <= i ? __expf(Gs[i] - Gs[j]) * dpv : 0.f;
+      }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      atomicAdd(&dGs[r0 + x], row[x]);
+      atomicAdd(&dGs[s0 + x], -col[x]);
+    }
+  }
+  __syncthreads();
+  // dQ = dQ_state + dPm K (written); dK = dK_state + dPm^T Q (kept)
+  const float* gst = dstates + unit * DD * DD;   // dQ_state [C][D], then dK_state [C][D]
+  float dkr[4][8];
+  {
+    float dqr[4][8];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const float4* pq = reinterpret_cast<const float4*>(gst + (size_t)(i0 + x) * DD + d8);
+      const float4* pk = reinterpret_cast<const float4*>(gst + (size_t)DC * DD + (size_t)(i0 + x) * DD + d8);
+      const float4 qa = pq[0], qb = pq[1], ka = pk[0], kb = pk[1];
+      dqr[x][0] = qa.x; dqr[x][1] = qa.y; dqr[x][2] = qa.z; dqr[x][3] = qa.w;
+      dqr[x][4] = qb.x; dqr[x][5] = qb.y; dqr[x][6] = qb.z; dqr[x][7] = qb.w;
+      dkr[x][0] = ka.x; dkr[x][1] = ka.y; dkr[x][2] = ka.z; dkr[x][3] = ka.w;
+      dkr[x][4] = kb.x; dkr[x][5] = kb.y; dkr[x][6] = kb.z; dkr[x][7] = kb.w;
+    }
+    for (int j = 0; j < DC; ++j) {
+      const bf16x8 kv = *reinterpret_cast<const bf16x8*>(Kb + j * BP + d8);
+      const bf16x8 qv = *reinterpret_cast<const bf16x8*>(Qb + j * BP + d8);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const float pa = M1[(i0 + x) * CP + j], pb = M1[j * CP + i0 + x];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          dqr[x][e] += pa * (float)kv[e];
+          dkr[x][e] += pb * (float)qv[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+      if (i0 + x < n) {
+        bf16x8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = (bf16)dqr[x][e];
+        *reinterpret_cast<bf16x8*>(dq + (size_t)(c0 + i0 + x) * rs + (size_t)h * DD + d8) = o;
+      }
+  }
+  __syncthreads();   // U, dO and dPm are no longer read
+#pragma unroll
+  for (int r = 0; r < DC * DD / 4 / GRAD_THREADS; ++r) {
+    const int f = tid + GRAD_THREADS * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
+    const float4 w = reinterpret_cast<const float4*>(rec + DeltaRecord::W)[f];
+    const float4 du = reinterpret_cast<const float4*>(dubuf + unit * DC * DD)[f];
+    F1[i * LP + c4] = w.x; F1[i * LP + c4 + 1] = w.y; F1[i * LP + c4 + 2] = w.z; F1[i * LP + c4 + 3] = w.w;
+    F2[i * LP + c4] = du.x; F2[i * LP + c4 + 1] = du.y; F2[i * LP + c4 + 2] = du.z; F2[i * LP + c4 + 3] = du.w;
+  }
+  for (int f = tid; f < DC * DC; f += GRAD_THREADS) M1[(f / DC) * CP + f % DC] = rec[DeltaRecord::TI + f];
+  __syncthreads();
+  // dX = T^T dW, dY = T^T dU (T_ji = 0 for j < i); dV = diag(beta) dY;
+  // dK += diag(beta gamma) dX; the beta and decay gradients through X and Y
+  {
+    float dx[4][8] = {}, dy[4][8] = {};
+    for (int j = i0; j < DC; ++j) {
+      float w[8], u[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        w[e] = F1[j * LP + d8 + e];
+        u[e] = F2[j * LP + d8 + e];
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const float t = M1[j * CP + i0 + x];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          dx[x][e] += t * w[e];
+          dy[x][e] += t * u[e];
+        }
+      }
+    }
+    float kdx[4], vdy[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int i = i0 + x;
+      const bf16x8 kv = *reinterpret_cast<const bf16x8*>(Kb + i * BP + d8);
+      const bf16x8 vv = *reinterpret_cast<const bf16x8*>(Vb + i * BP + d8);
+      const float bgi = Bs[i] * gm[i];
+      kdx[x] = 0.f;
+      vdy[x] = 0.f;
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        kdx[x] += (float)kv[e] * dx[x][e];
+        vdy[x] += (float)vv[e] * dy[x][e];
+        dkr[x][e] += bgi * dx[x][e];
+        o[e] = (bf16)(Bs[i] * dy[x][e]);
+      }
+      if (i < n) *reinterpret_cast<bf16x8*>(dv + (size_t)(c0 + i) * rs + (size_t)h * DD + d8) = o;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) {
+        kdx[x] += __shfl_xor(kdx[x], off);
+        vdy[x] += __shfl_xor(vdy[x], off);
+      }
+    }
+    if ((tid & 15) == 0)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int i = i0 + x;
+        atomicAdd(&dBs[i], gm[i] * kdx[x] + vdy[x]);
+        atomicAdd(&dGs[i], gm[i] * Bs[i] * kdx[x]);
+      }
+  }
+  // dT = dW diag(beta gamma) K^T + dU diag(beta) V^T into M2
+  {
+    float tk[4][4] = {}, tv[4][4] = {};
+    for (int d = 0; d < DD; d += 8) {
+      bf16x8 kj[4], vj[4];
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        kj[y] = *reinterpret_cast<const bf16x8*>(Kb + (s0 + y) * BP + d);
+        vj[y] = *reinterpret_cast<const bf16x8*>(Vb + (s0 + y) * BP + d);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float w[4], u[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          w[x] = F1[(r0 + x) * LP + d + e];
+          u[x] = F2[(r0 + x) * LP + d + e];
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+          for (int y = 0; y < 4; ++y) {
+            tk[x][y] += w[x] * (float)kj[y][e];
+            tv[x][y] += u[x] * (float)vj[y][e];
+          }
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        const int j = s0 + y;
+        M2[(r0 + x) * CP + j] = Bs[j] * (gm[j] * tk[x][y] + tv[x][y]);
+      }
+  }
+  __syncthreads();   // V is no longer read: its space holds dT T^T next
+  {
+    float m[4][4] = {};
+    for (int c = 0; c < DC; ++c) {
+      float a_[4], t_[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        a_[x] = M2[(r0 + x) * CP + c];
+        t_[x] = M1[(s0 + x) * CP + c];
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) m[x][y] += a_[x] * t_[y];
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) M3[(r0 + x) * CP + s0 + y] = m[x][y];
+  }
+  __syncthreads();
+  // dA = -(T^T (dT T^T)) below the diagonal; with KK = K K^T and
+  // A_ij = beta_i exp(G_i - G_j) KK_ij, the beta and decay gradients through
+  // A, and Bm = dA (x) beta_i exp(G_i - G_j) into M2 (dT is no longer read)
+  {
+    float da[4][4] = {}, kk[4][4] = {};
+    for (int c = 0; c < DC; ++c) {
+      float t_[4], m_[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        t_[x] = M1[c * CP + r0 + x];
+        m_[x] = M3[c * CP + s0 + x];
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) da[x][y] -= t_[x] * m_[y];
+    }
+    for (int d = 0; d < DD; d += 8) {
+      bf16x8 ki[4], kj[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        ki[x] = *reinterpret_cast<const bf16x8*>(Kb + (r0 + x) * BP + d);
+        kj[x] = *reinterpret_cast<const bf16x8*>(Kb + (s0 + x) * BP + d);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+          for (int y = 0; y < 4; ++y) kk[x][y] += (float)ki[x][e] * (float)kj[y][e];
+    }
+    float row[4] = {}, col[4] = {}, db[4] = {};
+    float bm[4][4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        const int i = r0 + x, j = s0 + y;
+        bm[x][y] = 0.f;
+        if (j < i) {
+          const float dec = __expf(Gs[i] - Gs[j]);
+          const float dkk = da[x][y] * dec * kk[x][y];
+          db[x] += dkk;
+          const float ada = Bs[i] * dkk;   // A_ij dA_ij
+          row[x] += ada;
+          col[y] += ada;
+          bm[x][y] = da[x][y] * Bs[i] * dec;
+        }
+      }
+    __syncthreads();   // every read of dT is done before Bm replaces it
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+#pragma unroll
+      for (int y = 0; y < 4; ++y) M2[(r0 + x) * CP + s0 + y] = bm[x][y];
+      atomicAdd(&dBs[r0 + x], db[x]);
+      atomicAdd(&dGs[r0 + x], row[x]);
+      atomicAdd(&dGs[s0 + x], -col[x]);
+    }
+  }
+  __syncthreads();
+  // dK += Bm K + Bm^T K (written)
+  for (int j = 0; j < DC; ++j) {
+    const bf16x8 kv = *reinterpret_cast<const bf16x8*>(Kb + j * BP + d8);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const float w = M2[(i0 + x) * CP + j] + M2[j * CP + i0 + x];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dkr[x][e] += w * (float)kv[e];
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+    if (i0 + x < n) {
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (bf16)dkr[x][e];
+      *reinterpret_cast<bf16x8*>(dk + (size_t)(c0 + i0 + x) * rs + (size_t)h * DD + d8) = o;
+    }
+  // the log-decay gradient of every token: the side values of the state
+  // products (output term; end decays, whose sum lands on the last token, as
+  // does the end-state term), then the reverse cumulative sum inside the chunk
+  if (tid < DC) {
+    const float* side = rec + DeltaRecord::SIDE;
+    float sde = 0.f;
+    for (int j = 0; j < n; ++j) sde += side[DC + j];
+    float add = side[tid] - side[DC + tid];
+    if (tid == n - 1) add += side[2 * DC] + sde;
+    dGs[tid] += add;
+  }
+  __syncthreads();
+  if (tid < n) {
+    float run = 0.f;
+    for (int i = n - 1; i >= tid; --i) run += dGs[i];
+    dg[(size_t)(c0 + tid) * H + h] = run;
+    dbeta[(size_t)(c0 + tid) * H + h] = dBs[tid];
+  }
+}
+
 }  // namespace
 
 hipError_t launch_delta_fwd(const void* q, const void* k, const void* v, const float* g,
@@ -403,12 +1102,50 @@ hipError_t launch_delta_fwd(const void* q, const void* k, const void* v, const f
   hipLaunchKernelGGL(delta_prep_kernel, dim3((unsigned)(w.chunk_cap * (size_t)num_heads)),
                      dim3(PREP_THREADS), 0, stream, static_cast<const bf16*>(q),
                      static_cast<const bf16*>(k), static_cast<const bf16*>(v), g, beta,
-                     cu_seqlens, num_seqs, total_tokens, num_heads, header, seg_off, records);
+                     cu_seqlens, num_seqs, total_tokens, num_heads, header, seg_off, records, 0);
   hipLaunchKernelGGL(delta_scan_kernel,
                      dim3((unsigned)((size_t)num_seqs * num_heads * (DD / SLICE))),
                      dim3(SCAN_THREADS), 0, stream, static_cast<const bf16*>(q),
                      static_cast<const bf16*>(k), cu_seqlens, num_seqs, total_tokens, num_heads,
-                     scale, seg_off, records, static_cast<bf16*>(out));
+                     scale, seg_off, records, static_cast<bf16*>(out), nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_delta_bwd(const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, const void* dout, const int32_t* cu_seqlens,
+                            int num_seqs, int total_tokens, int num_heads, float scale, void* dq,
+                            void* dk, void* dv, float* dg, float* dbeta, void* workspace,
+                            const DeltaLayout& w, hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  int* header = reinterpret_cast<int*>(ws + w.header);
+  int* seg_off = reinterpret_cast<int*>(ws + w.seg_off);
+  float* records = reinterpret_cast<float*>(ws + w.records);
+  float* states = reinterpret_cast<float*>(ws + w.states);
+  float* dstates = reinterpret_cast<float*>(ws + w.dstates);
+  float* dubuf = reinterpret_cast<float*>(ws + w.dubuf);
+  const bf16* qb = static_cast<const bf16*>(q);
+  const bf16* kb = static_cast<const bf16*>(k);
+  const bf16* vb = static_cast<const bf16*>(v);
+  const bf16* ob = static_cast<const bf16*>(dout);
+  const dim3 units((unsigned)(w.chunk_cap * (size_t)num_heads));
+  const dim3 scans((unsigned)((size_t)num_seqs * num_heads * (DD / SLICE)));
+  hipLaunchKernelGGL(delta_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, cu_seqlens,
+                     num_seqs, total_tokens, (int)w.chunk_cap, header, seg_off);
+  hipLaunchKernelGGL(delta_prep_kernel, units, dim3(PREP_THREADS), 0, stream, qb, kb, vb, g, beta,
+                     cu_seqlens, num_seqs, total_tokens, num_heads, header, seg_off, records, 1);
+  hipLaunchKernelGGL(delta_scan_kernel, scans, dim3(SCAN_THREADS), 0, stream, qb, kb, cu_seqlens,
+                     num_seqs, total_tokens, num_heads, scale, seg_off, records,
+                     static_cast<bf16*>(nullptr), states);
+  hipLaunchKernelGGL(delta_rscan_kernel, scans, dim3(SCAN_THREADS), 0, stream, qb, kb, ob,
+                     cu_seqlens, num_seqs, total_tokens, num_heads, scale, seg_off, records,
+                     dstates, dubuf);
+  hipLaunchKernelGGL(delta_gstate_kernel, units, dim3(GRAD_THREADS), 0, stream, qb, kb, ob,
+                     cu_seqlens, num_seqs, total_tokens, num_heads, scale, header, seg_off,
+                     records, states, dstates, dubuf);
+  hipLaunchKernelGGL(delta_glocal_kernel, units, dim3(GRAD_THREADS), 0, stream, qb, kb, vb, g,
+                     beta, ob, cu_seqlens, num_seqs, total_tokens, num_heads, scale, header,
+                     seg_off, records, dstates, dubuf, static_cast<bf16*>(dq),
+                     static_cast<bf16*>(dk), static_cast<bf16*>(dv), dg, dbeta);
   return hipGetLastError();
 }
 

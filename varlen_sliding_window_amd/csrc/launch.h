@@ -41,24 +41,41 @@ hipError_t launch_dkdv(const void* q, const void* k, const void* v, const float*
                        const void* dout, const Problem& p, void* dk, void* dv, void* workspace,
                        const WorkspaceLayout& w, hipStream_t stream);
 
-// Gated delta-rule forward (delta.hip): chunks of DELTA_CHUNK tokens, head
-// dim DELTA_DIM for keys and values.  Workspace: [header | per-segment chunk
-// offsets | one fp32 record per (chunk, head)].
+// Gated delta-rule linear attention (delta.hip): chunks of DELTA_CHUNK
+// tokens, head dim DELTA_DIM for keys and values.  Workspace: [header |
+// per-segment chunk offsets | one fp32 record per (chunk, head)], and for the
+// backward also [chunk-start states | end-state gradients | dU], one per
+// (chunk, head).
 constexpr int DELTA_CHUNK = 64;
 constexpr int DELTA_DIM = 128;
+// record: W, U0 [C][D]; P, T [C][C]; gamma, end decay and 4 C side values
+constexpr size_t delta_record_floats() {
+  return (size_t)2 * DELTA_CHUNK * DELTA_DIM + (size_t)2 * DELTA_CHUNK * DELTA_CHUNK +
+         (size_t)6 * DELTA_CHUNK;
+}
 struct DeltaLayout {
-  size_t header, seg_off, records, total;
+  size_t header, seg_off, records, states, dstates, dubuf, total;
   size_t chunk_cap, record_bytes;
 };
-inline DeltaLayout delta_layout(int64_t total_tokens, int64_t num_seqs, int64_t num_heads) {
+inline DeltaLayout delta_layout(int64_t total_tokens, int64_t num_seqs, int64_t num_heads,
+                                bool backward = false) {
   DeltaLayout w;
   w.chunk_cap = (size_t)((total_tokens + DELTA_CHUNK - 1) / DELTA_CHUNK) + (size_t)num_seqs;
-  w.record_bytes = ((size_t)2 * DELTA_CHUNK * DELTA_DIM + (size_t)DELTA_CHUNK * DELTA_CHUNK +
-                    2 * (size_t)DELTA_CHUNK) * sizeof(float);
+  w.record_bytes = delta_record_floats() * sizeof(float);
+  const size_t units = w.chunk_cap * (size_t)num_heads;
   w.header = 0;
   w.seg_off = 256;
   w.records = w.seg_off + align256((size_t)(num_seqs + 1) * sizeof(int));
-  w.total = w.records + w.chunk_cap * (size_t)num_heads * w.record_bytes;
+  w.states = w.records + units * w.record_bytes;
+  w.dstates = w.states;
+  w.dubuf = w.states;
+  w.total = w.states;
+  if (backward) {
+    const size_t state_bytes = (size_t)DELTA_DIM * DELTA_DIM * sizeof(float);
+    w.dstates = w.states + units * state_bytes;
+    w.dubuf = w.dstates + units * state_bytes;
+    w.total = w.dubuf + units * (size_t)DELTA_CHUNK * DELTA_DIM * sizeof(float);
+  }
   return w;
 }
 
@@ -66,5 +83,14 @@ hipError_t launch_delta_fwd(const void* q, const void* k, const void* v, const f
                             const float* beta, const int32_t* cu_seqlens, int num_seqs,
                             int total_tokens, int num_heads, float scale, void* out,
                             void* workspace, const DeltaLayout& w, hipStream_t stream);
+
+// Gradients of sum(dout * out) for the gated delta rule: dq, dk, dv bf16
+// [T, H, D]; dg, dbeta fp32 [T, H].  Recomputes the forward's records and
+// states in the workspace (laid out with backward = true).
+hipError_t launch_delta_bwd(const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, const void* dout, const int32_t* cu_seqlens,
+                            int num_seqs, int total_tokens, int num_heads, float scale, void* dq,
+                            void* dk, void* dv, float* dg, float* dbeta, void* workspace,
+                            const DeltaLayout& w, hipStream_t stream);
 
 }  // namespace attn
