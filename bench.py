@@ -189,56 +189,71 @@ def load_traffic(kernel: str):
 
 
 def delta_bench(args, device):
-    """Gated delta-rule forward on the workload microbatch (one layer, H = 8
-    heads of 128, the documents of the attention workload's cu_seqlens).
-    Counts 6 d^2 flops per token and head (the recurrence's S k, update and
-    S q); prints one JSON line."""
+    """Gated delta-rule layer step on the workload microbatch (one layer, H = 8
+    heads of 128, the documents of the attention workload's cu_seqlens): the
+    forward, then the backward (which recomputes the forward's records), as a
+    training step runs them.  Also times each alone; prints one JSON line."""
     import torch
     import varlen_sliding_window_amd as attn
-    from synthetic import CONFIGS, make_cu_seqlens, make_delta_inputs
+    from synthetic import CONFIGS, make_cu_seqlens, make_delta_dout, make_delta_inputs
 
     cu, _ = make_cu_seqlens(CONFIGS["ctx4096_w512"], args.seed)
     heads, d = 8, 128
     inp = make_delta_inputs(cu, heads, d, args.seed)
+    t = int(cu[-1])
 
     def dev_bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
 
     q, k, v = dev_bf16(inp.q_bits), dev_bf16(inp.k_bits), dev_bf16(inp.v_bits)
+    dout = dev_bf16(make_delta_dout(t, heads, d, args.seed + 1))
     g = torch.from_numpy(inp.g).to(device)
     beta = torch.from_numpy(inp.beta).to(device)
     cu_dev = torch.from_numpy(cu.astype(np.int32)).to(device)
-    t = int(cu[-1])
-    ws = torch.empty(attn.delta_workspace_size(t, len(cu) - 1, heads, d), dtype=torch.uint8,
+    nseq = len(cu) - 1
+    ws = torch.empty(attn.delta_bwd_workspace_size(t, nseq, heads, d), dtype=torch.uint8,
                      device=device)
     out = torch.zeros_like(q)
 
-    def step():
+    def fwd():
         attn.delta_fwd(q, k, v, g, beta, cu_dev, d ** -0.5, out=out, workspace=ws)
+
+    def bwd():
+        attn.delta_bwd(q, k, v, g, beta, dout, cu_dev, d ** -0.5, workspace=ws)
+
+    def step():
+        fwd()
+        bwd()
+
+    def timed(fn, steps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    flops = 6.0 * d * d * t * heads
+    ms = timed(step, args.steps)
+    ms_fwd = timed(fwd, args.steps)
+    ms_bwd = timed(bwd, args.steps)
     attn.profile_start()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     kern = attn.profile_stop()
     print(json.dumps({
-        "metric": "gated delta-rule forward TFLOP/s per 16,384-token microbatch (8 heads of 128)",
-        "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": "gated delta-rule layer step (forward + backward) per 16,384-token microbatch, 8 heads of 128",
+        "value": ms, "unit": "ms", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
-        "higher_is_better": True, "dtype": "bf16 in, fp32 arithmetic",
-        "data": "synthetic (seeded lognormal document packing; unit q, k; N(0,1) v)",
+        "higher_is_better": False, "dtype": "bf16 in, fp32 arithmetic",
+        "data": "synthetic (seeded lognormal document packing; unit q, k; N(0,1) v and dout)",
+        "vs_baseline": None,
         "config": {"workload": "delta_ctx4096", "total_tokens": t, "num_heads": heads,
-                   "head_dim": d, "num_seqs": len(cu) - 1, "seed": args.seed,
-                   "gflop_per_step": flops / 1e9},
+                   "head_dim": d, "num_seqs": nseq, "seed": args.seed},
+        "forward_ms": ms_fwd, "backward_ms": ms_bwd,
+        "forward_tflops": 6.0 * d * d * t * heads / (ms_fwd * 1e-3) / 1e12,
         "kernels": {kk: {"avg_ms": vv["avg_ms"]} for kk, vv in kern.items()},
     }))
 

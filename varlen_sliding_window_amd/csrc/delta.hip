@@ -433,7 +433,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_rscan_kernel(
   constexpr int BP = DD + 8;
   constexpr int OP = SLICE + 1;
   __shared__ float dSs[SLICE * LP];    // dS rows c0 .. c0 + SLICE - 1, all d_k
-  __shared__ float Ws[DC * LP];
+  __shared__ __attribute__((aligned(16))) float Ws[DC * DD];   // read a row at a time
   __shared__ __attribute__((aligned(16))) bf16 Qs[DC * BP];
   __shared__ __attribute__((aligned(16))) bf16 Ks[DC * BP];
   __shared__ float Ps[DC * (DC + 1)];
@@ -489,13 +489,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_rscan_kernel(
     const int n = min(DC, b - (a + ci * DC));
     __syncthreads();   // every read of the previous chunk's LDS data is done
 #pragma unroll
-    for (int r = 0; r < WR; ++r) {
-      const int f = tid + NT * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
-      Ws[i * LP + c4] = wr[r].x;
-      Ws[i * LP + c4 + 1] = wr[r].y;
-      Ws[i * LP + c4 + 2] = wr[r].z;
-      Ws[i * LP + c4 + 3] = wr[r].w;
-    }
+    for (int r = 0; r < WR; ++r) reinterpret_cast<float4*>(Ws)[tid + NT * r] = wr[r];
 #pragma unroll
     for (int r = 0; r < PR; ++r) {
       const int f = tid + NT * r, pi = f / (DC / 4), pj = (f % (DC / 4)) * 4;
@@ -557,20 +551,31 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_rscan_kernel(
     __syncthreads();
     // dS_0 = gamma_C dS + sum_i (scale gamma_i dO_i q_i^T - dU_i w_i^T):
     // thread (row c, DPT columns of d)
-    {
-      constexpr int DPT = SLICE * DD / NT;
-      const int c = tid / (DD / DPT), d0 = (tid % (DD / DPT)) * DPT;
-      float acc[DPT] = {};
+    {   // thread (row c, two groups of 4 columns 64 apart): a wave's lanes read adjacent 16 bytes
+      static_assert(SLICE * DD / NT == 8 && DD == 128, "8 columns per thread");
+      const int c = tid / 16, l4 = (tid % 16) * 4;
+      float acc[8] = {};
       for (int i = 0; i < n; ++i) {
         const float a1 = scale * Gm[i] * dOs[i * OP + c];
         const float a2 = dUs[i * OP + c];
 #pragma unroll
-        for (int y = 0; y < DPT; ++y)
-          acc[y] += a1 * (float)Qs[i * BP + d0 + y] - a2 * Ws[i * LP + d0 + y];
+        for (int y = 0; y < 2; ++y) {
+          const float4 w = *reinterpret_cast<const float4*>(Ws + i * DD + l4 + 64 * y);
+          const bf16x4 qv = *reinterpret_cast<const bf16x4*>(Qs + i * BP + l4 + 64 * y);
+          acc[4 * y] += a1 * (float)qv[0] - a2 * w.x;
+          acc[4 * y + 1] += a1 * (float)qv[1] - a2 * w.y;
+          acc[4 * y + 2] += a1 * (float)qv[2] - a2 * w.z;
+          acc[4 * y + 3] += a1 * (float)qv[3] - a2 * w.w;
+        }
       }
       const float gc = Gm[n - 1];
 #pragma unroll
-      for (int y = 0; y < DPT; ++y) dSs[c * LP + d0 + y] = gc * dSs[c * LP + d0 + y] + acc[y];
+      for (int y = 0; y < 2; ++y)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float* p = dSs + c * LP + l4 + 64 * y + e;
+          *p = gc * *p + acc[4 * y + e];
+        }
     }
   }
 }
