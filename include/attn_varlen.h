@@ -230,14 +230,29 @@ attn_status attn_delta_fwd(const void* q, const void* k, const void* v, const fl
  *   dq, dk, dv  bf16 [T, H, D], written for tokens inside documents
  *   dg, dbeta   fp32 [T, H], written for tokens inside documents
  *   workspace   >= attn_delta_bwd_workspace_size(T, num_seqs, H, D) bytes,
- *               256-byte aligned: the forward's records (recomputed, with the
- *               triangular inverse kept), each chunk's start state and
- *               end-state gradient (fp32 D x D) and its dU, about 264 KB per
+ *               256-byte aligned: the forward's records (with the triangular
+ *               inverse kept), each chunk's start state and end-state
+ *               gradient (fp32 D x D), its dU and dW, about 297 KB per
  *               (64-token chunk, head)
- * Recomputes the forward (no saved tensors cross the boundary) and runs a
- * reverse per-document scan and two per-chunk gradient kernels: six kernels
- * on `stream`, nothing allocated.
+ * Recomputes the forward's records and chunk states (three kernels), then
+ * runs a reverse per-document scan and two per-chunk gradient kernels, all
+ * on `stream`; nothing allocated.
+ *
+ * The _ex forms take flags (other bits -> ATTN_EINVAL):
+ * ATTN_DELTA_FWD_SAVE (forward): the forward also keeps, in a workspace of
+ * attn_delta_bwd_workspace_size bytes, everything its backward needs (the
+ * records with the inverse, each chunk's start state and U).
+ * ATTN_DELTA_BWD_REUSE (backward): skips recomputing them, taking those of
+ * the last saving forward call in the same workspace on the same stream.
+ * The caller vouches that it had the same q, k, v, g, beta and cu_seqlens
+ * contents (the pair of calls of one layer in a training step); the kernels
+ * check on the device that it was a saving forward with the same
+ * total_tokens, heads and num_seqs, and otherwise do nothing (outputs
+ * unwritten).  A reusing backward leaves the saved data intact, so it may
+ * run more than once.
  */
+enum { ATTN_DELTA_FWD_SAVE = 1, ATTN_DELTA_BWD_REUSE = 1 };
+
 size_t attn_delta_bwd_workspace_size(int32_t total_tokens, int32_t num_seqs_cap,
                                      int32_t num_heads, int32_t head_dim);
 
@@ -247,6 +262,19 @@ attn_status attn_delta_bwd(const void* q, const void* k, const void* v, const fl
                            int32_t head_dim, float scale, void* dq, void* dk, void* dv, float* dg,
                            float* dbeta, void* workspace, size_t workspace_bytes,
                            attn_stream_t stream);
+
+attn_status attn_delta_fwd_ex(const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                              int32_t total_tokens, int32_t num_heads, int32_t head_dim,
+                              float scale, uint32_t flags, void* out, void* workspace,
+                              size_t workspace_bytes, attn_stream_t stream);
+
+attn_status attn_delta_bwd_ex(const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, const void* dout, const int32_t* cu_seqlens,
+                              int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                              int32_t head_dim, float scale, uint32_t flags, void* dq, void* dk,
+                              void* dv, float* dg, float* dbeta, void* workspace,
+                              size_t workspace_bytes, attn_stream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char* attn_varlen_strerror(attn_status s);

@@ -164,7 +164,21 @@ def test_delta_bwd_workspace_size(lib):
     fwd = lib.attn_delta_workspace_size(16384, 64, 8, 128)
     bwd = lib.attn_delta_bwd_workspace_size(16384, 64, 8, 128)
     chunks = 16384 // 64 + 64
-    # per (chunk, head): the record, two fp32 128 x 128 states and a 64 x 128 dU
-    assert bwd - fwd == chunks * 8 * (2 * 128 * 128 + 64 * 128) * 4
+    # per (chunk, head): two fp32 128 x 128 states, a 64 x 128 dU and dW
+    assert bwd - fwd == chunks * 8 * (2 * 128 * 128 + 2 * 64 * 128) * 4
     assert lib.attn_delta_bwd_workspace_size(64, 1, 2, 96) == 0
     assert lib.attn_delta_bwd_workspace_size(0, 1, 2, 128) == 0
+
+
+@pytest.mark.parametrize("flags", [2, 3, 0x80000000])
+def test_delta_ex_rejects_unknown_flags(lib, flags):
+    fargs = [FAKE] * 6 + [1, 64, 2, 128, 0.088, flags, FAKE, FAKE, 1 << 31, None]
+    assert lib.attn_delta_fwd_ex(*fargs) == EINVAL
+    bargs = [FAKE] * 7 + [1, 64, 2, 128, 0.088, flags] + [FAKE] * 6 + [1 << 31, None]
+    assert lib.attn_delta_bwd_ex(*bargs) == EINVAL
+
+
+def test_delta_saving_forward_needs_the_backward_workspace(lib):
+    fwd_n = lib.attn_delta_workspace_size(64, 1, 2, 128)
+    args = [FAKE] * 6 + [1, 64, 2, 128, 0.088, 1, FAKE, FAKE, fwd_n, None]
+    assert lib.attn_delta_fwd_ex(*args) == EWORKSPACE

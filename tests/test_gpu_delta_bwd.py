@@ -106,3 +106,54 @@ def test_delta_bwd_repeatable_and_scale():
     for name, x, y in zip(NAMES[:3], a[:3], b[:3]):   # no atomics on these paths
         assert np.array_equal(x, y), name
     compare(a, reference(inp, dout, 0.3), "scale 0.3")
+
+
+def _device(inp, dout_bits):
+    q, k, v = (bits_to_torch(getattr(inp, n + "_bits")) for n in ("q", "k", "v"))
+    g = torch.from_numpy(inp.g).cuda()
+    beta = torch.from_numpy(inp.beta).cuda()
+    cu = torch.from_numpy(inp.cu_seqlens.astype(np.int32)).cuda()
+    return q, k, v, g, beta, bits_to_torch(dout_bits), cu
+
+
+def test_delta_bwd_reusing_a_saving_forward():
+    cu = np.array([0, 130, 131, 400], dtype=np.int32)
+    inp = make_delta_inputs(cu, 3, 128, seed=27)
+    q, k, v, g, beta, do, cu_d = _device(inp, make_delta_dout(400, 3, 128, seed=28))
+    plain = attn.delta_fwd(q, k, v, g, beta, cu_d)
+    ref = attn.delta_bwd(q, k, v, g, beta, do, cu_d)
+    ws = torch.empty(attn.delta_bwd_workspace_size(400, 3, 3, 128), dtype=torch.uint8,
+                     device="cuda")
+    saved = attn.delta_fwd(q, k, v, g, beta, cu_d, workspace=ws, save=True)
+    assert torch.equal(saved, plain), "saving changes the forward's output"
+    for rep in range(2):   # a reusing backward leaves the saved data as it was
+        got = attn.delta_bwd(q, k, v, g, beta, do, cu_d, workspace=ws, reuse=True)
+        torch.cuda.synchronize()
+        for name, x, y in zip(NAMES, got, ref):
+            if name in ("dq", "dk", "dv"):
+                assert torch.equal(x, y), (rep, name)
+            else:   # LDS float atomics may add in another order
+                torch.testing.assert_close(x, y, rtol=1e-5, atol=1e-6)
+
+
+def test_delta_bwd_reuse_is_refused_without_a_matching_save():
+    cu = np.array([0, 70, 200], dtype=np.int32)
+    inp = make_delta_inputs(cu, 2, 128, seed=29)
+    q, k, v, g, beta, do, cu_d = _device(inp, make_delta_dout(200, 2, 128, seed=30))
+    ws = torch.empty(attn.delta_bwd_workspace_size(200, 2, 2, 128), dtype=torch.uint8,
+                     device="cuda")
+    attn.delta_fwd(q, k, v, g, beta, cu_d, workspace=ws, save=True)
+    attn.delta_fwd(q, k, v, g, beta, cu_d, workspace=ws)           # a forward that saves nothing
+    got = attn.delta_bwd(q, k, v, g, beta, do, cu_d, workspace=ws, reuse=True)
+    torch.cuda.synchronize()
+    assert all(torch.count_nonzero(x) == 0 for x in got), "ran on a workspace not saved for it"
+    # saved for another segment count (same tokens and heads): refused too
+    one = torch.tensor([0, 200], dtype=torch.int32, device="cuda")
+    attn.delta_fwd(q, k, v, g, beta, one, workspace=ws, save=True)
+    got = attn.delta_bwd(q, k, v, g, beta, do, cu_d, workspace=ws, reuse=True)
+    torch.cuda.synchronize()
+    assert all(torch.count_nonzero(x) == 0 for x in got)
+    # without the flag the backward recomputes and fills them
+    got = attn.delta_bwd(q, k, v, g, beta, do, cu_d, workspace=ws)
+    torch.cuda.synchronize()
+    assert all(torch.count_nonzero(x) > 0 for x in got)

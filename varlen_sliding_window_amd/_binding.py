@@ -76,6 +76,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_delta_bwd.argtypes = [vp] * 7 + [i32, i32, i32, i32, ctypes.c_float] + [vp] * 6 + [
         sz, vp]
     lib.attn_delta_bwd.restype = ctypes.c_int
+    lib.attn_delta_fwd_ex.argtypes = [vp] * 6 + [i32, i32, i32, i32, ctypes.c_float,
+                                                 ctypes.c_uint32, vp, vp, sz, vp]
+    lib.attn_delta_fwd_ex.restype = ctypes.c_int
+    lib.attn_delta_bwd_ex.argtypes = [vp] * 7 + [i32, i32, i32, i32, ctypes.c_float,
+                                                 ctypes.c_uint32] + [vp] * 6 + [sz, vp]
+    lib.attn_delta_bwd_ex.restype = ctypes.c_int
     lib.attn_varlen_strerror.argtypes = [ctypes.c_int]
     lib.attn_varlen_strerror.restype = ctypes.c_char_p
     lib.attn_varlen_version.argtypes = []
@@ -226,9 +232,11 @@ def delta_workspace_size(total_tokens: int, num_seqs: int, num_heads: int, head_
 
 
 def delta_fwd(q, k, v, g, beta, cu_seqlens, scale: float | None = None, out=None,
-              workspace=None):
-    """attn_delta_fwd: gated delta-rule linear attention forward.  q, k, v bf16
-    [T, H, D]; g, beta fp32 [T, H]; returns out bf16 [T, H, D]."""
+              workspace=None, save: bool = False):
+    """attn_delta_fwd(_ex): gated delta-rule linear attention forward.  q, k, v
+    bf16 [T, H, D]; g, beta fp32 [T, H]; returns out bf16 [T, H, D].  With
+    save=True the workspace (of delta_bwd_workspace_size bytes) keeps what a
+    delta_bwd(..., reuse=True) with the same inputs and workspace needs."""
     for name, t_ in (("q", q), ("k", k), ("v", v)):
         _check_tensor(name, t_, torch.bfloat16, 3)
     _check_tensor("g", g, torch.float32, 2)
@@ -243,16 +251,16 @@ def delta_fwd(q, k, v, g, beta, cu_seqlens, scale: float | None = None, out=None
     if out is None:
         out = torch.zeros_like(q)
     if workspace is None:
-        n = delta_workspace_size(t, nseq, h, d)
+        n = (delta_bwd_workspace_size if save else delta_workspace_size)(t, nseq, h, d)
         if n == 0:
             raise AttnError(-1, "attn_delta_workspace_size")
         workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
-    st = load_library().attn_delta_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                       _ptr(cu_seqlens), nseq, t, h, d, float(scale), _ptr(out),
-                                       _ptr(workspace), workspace.numel(),
-                                       _stream_handle(q.device))
+    st = load_library().attn_delta_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                          _ptr(cu_seqlens), nseq, t, h, d, float(scale),
+                                          1 if save else 0, _ptr(out), _ptr(workspace),
+                                          workspace.numel(), _stream_handle(q.device))
     if st != ATTN_OK:
-        raise AttnError(st, "attn_delta_fwd")
+        raise AttnError(st, "attn_delta_fwd_ex")
     return out
 
 
@@ -262,9 +270,14 @@ def delta_bwd_workspace_size(total_tokens: int, num_seqs: int, num_heads: int,
                                                              head_dim))
 
 
-def delta_bwd(q, k, v, g, beta, dout, cu_seqlens, scale: float | None = None, workspace=None):
-    """attn_delta_bwd: gradients of sum(dout * out) of the gated delta-rule
-    forward.  Returns dq, dk, dv (bf16 [T, H, D]) and dg, dbeta (fp32 [T, H])."""
+def delta_bwd(q, k, v, g, beta, dout, cu_seqlens, scale: float | None = None, workspace=None,
+              reuse: bool = False):
+    """attn_delta_bwd(_ex): gradients of sum(dout * out) of the gated
+    delta-rule forward.  Returns dq, dk, dv (bf16 [T, H, D]) and dg, dbeta
+    (fp32 [T, H]), zero-filled first.  reuse=True takes the records and states
+    a delta_fwd(..., save=True) with the same inputs left in `workspace`."""
+    if reuse and workspace is None:
+        raise ValueError("reuse needs the workspace of a saving forward")
     for name, t_ in (("q", q), ("k", k), ("v", v), ("dout", dout)):
         _check_tensor(name, t_, torch.bfloat16, 3)
     _check_tensor("g", g, torch.float32, 2)
@@ -284,13 +297,13 @@ def delta_bwd(q, k, v, g, beta, dout, cu_seqlens, scale: float | None = None, wo
         if n == 0:
             raise AttnError(-1, "attn_delta_bwd_workspace_size")
         workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
-    st = load_library().attn_delta_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                       _ptr(dout), _ptr(cu_seqlens), nseq, t, h, d, float(scale),
-                                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta),
-                                       _ptr(workspace), workspace.numel(),
-                                       _stream_handle(q.device))
+    st = load_library().attn_delta_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                          _ptr(dout), _ptr(cu_seqlens), nseq, t, h, d,
+                                          float(scale), 1 if reuse else 0, _ptr(dq), _ptr(dk),
+                                          _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(workspace),
+                                          workspace.numel(), _stream_handle(q.device))
     if st != ATTN_OK:
-        raise AttnError(st, "attn_delta_bwd")
+        raise AttnError(st, "attn_delta_bwd_ex")
     return dq, dk, dv, dg, dbeta
 
 

@@ -306,34 +306,46 @@ size_t attn_delta_bwd_workspace_size(int32_t total_tokens, int32_t num_seqs_cap,
   return delta_workspace(total_tokens, num_seqs_cap, num_heads, head_dim, true);
 }
 
-attn_status attn_delta_fwd(const void* q, const void* k, const void* v, const float* g,
-                           const float* beta, const int32_t* cu_seqlens, int32_t num_seqs,
-                           int32_t total_tokens, int32_t num_heads, int32_t head_dim, float scale,
-                           void* out, void* workspace, size_t workspace_bytes,
-                           attn_stream_t stream) {
+attn_status attn_delta_fwd_ex(const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                              int32_t total_tokens, int32_t num_heads, int32_t head_dim,
+                              float scale, uint32_t flags, void* out, void* workspace,
+                              size_t workspace_bytes, attn_stream_t stream) {
+  if (flags & ~(uint32_t)ATTN_DELTA_FWD_SAVE) return ATTN_EINVAL;
+  const bool save = flags & ATTN_DELTA_FWD_SAVE;
   attn_status s = check_delta(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
                               head_dim, scale);
   if (s != ATTN_OK) return s;
   if (!out || !aligned(out, 16)) return ATTN_EINVAL;
-  const attn::DeltaLayout w = attn::delta_layout(total_tokens, num_seqs, num_heads);
+  const attn::DeltaLayout w = attn::delta_layout(total_tokens, num_seqs, num_heads, save);
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < w.total) return ATTN_EWORKSPACE;
   s = check_device();
   if (s != ATTN_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (timed_launch(K_DELTA, st, [&] {
         return attn::launch_delta_fwd(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens,
-                                      num_heads, scale, out, workspace, w, st);
+                                      num_heads, scale, out, workspace, w, save, st);
       }) != hipSuccess)
     return ATTN_ELAUNCH;
   return ATTN_OK;
 }
 
-attn_status attn_delta_bwd(const void* q, const void* k, const void* v, const float* g,
-                           const float* beta, const void* dout, const int32_t* cu_seqlens,
-                           int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
-                           int32_t head_dim, float scale, void* dq, void* dk, void* dv, float* dg,
-                           float* dbeta, void* workspace, size_t workspace_bytes,
+attn_status attn_delta_fwd(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                           int32_t total_tokens, int32_t num_heads, int32_t head_dim, float scale,
+                           void* out, void* workspace, size_t workspace_bytes,
                            attn_stream_t stream) {
+  return attn_delta_fwd_ex(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
+                           head_dim, scale, 0u, out, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_delta_bwd_ex(const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, const void* dout, const int32_t* cu_seqlens,
+                              int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                              int32_t head_dim, float scale, uint32_t flags, void* dq, void* dk,
+                              void* dv, float* dg, float* dbeta, void* workspace,
+                              size_t workspace_bytes, attn_stream_t stream) {
+  if (flags & ~(uint32_t)ATTN_DELTA_BWD_REUSE) return ATTN_EINVAL;
   attn_status s = check_delta(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
                               head_dim, scale);
   if (s != ATTN_OK) return s;
@@ -348,10 +360,22 @@ attn_status attn_delta_bwd(const void* q, const void* k, const void* v, const fl
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (timed_launch(K_DELTA_BWD, st, [&] {
         return attn::launch_delta_bwd(q, k, v, g, beta, dout, cu_seqlens, num_seqs, total_tokens,
-                                      num_heads, scale, dq, dk, dv, dg, dbeta, workspace, w, st);
+                                      num_heads, scale, dq, dk, dv, dg, dbeta, workspace, w,
+                                      flags & ATTN_DELTA_BWD_REUSE, st);
       }) != hipSuccess)
     return ATTN_ELAUNCH;
   return ATTN_OK;
+}
+
+attn_status attn_delta_bwd(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const void* dout, const int32_t* cu_seqlens,
+                           int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                           int32_t head_dim, float scale, void* dq, void* dk, void* dv, float* dg,
+                           float* dbeta, void* workspace, size_t workspace_bytes,
+                           attn_stream_t stream) {
+  return attn_delta_bwd_ex(q, k, v, g, beta, dout, cu_seqlens, num_seqs, total_tokens, num_heads,
+                           head_dim, scale, 0u, dq, dk, dv, dg, dbeta, workspace, workspace_bytes,
+                           stream);
 }
 
 const char* attn_varlen_strerror(attn_status s) {

@@ -37,9 +37,12 @@ constexpr int LP = DD + 1;            // LDS pitch of DD-wide fp32 rows
 
 __device__ __forceinline__ float bf(const bf16 x) { return (float)x; }
 
-// Chunks per segment -> exclusive offsets; header[0] = chunk count.
+// Chunks per segment -> exclusive offsets.  Header: [0] chunk count, [1]
+// total tokens, [2] heads, [3] the chunk capacity when the call saves the
+// chunk states for a backward (-1 otherwise).
 __global__ __launch_bounds__(PLAN_THREADS) void delta_plan_kernel(const int32_t* __restrict__ cu,
                                                                    int nseq, int T, int chunk_cap,
+                                                                   int H, int saves,
                                                                    int* __restrict__ header,
                                                                    int* __restrict__ seg_off) {
   __shared__ int part[PLAN_THREADS];
@@ -73,11 +76,21 @@ __global__ __launch_bounds__(PLAN_THREADS) void delta_plan_kernel(const int32_t*
     seg_off[nseq] = total;
     header[0] = total;
     header[1] = T;
+    header[2] = H;
+    header[3] = saves ? chunk_cap : -1;
   }
 }
 
-// One record per (chunk, head), fp32: W [DC][DD] (the backward overwrites it
-// with dW), U0 [DC][DD] (U after a saving scan), P [DC][DC], gamma [DC],
+// A backward that reuses a forward's saved records and states runs only if
+// that forward saved them for the same total tokens, heads and chunk
+// capacity (hence the same number of segments), so a stale workspace can
+// give wrong results but never addresses outside the call's buffers.
+__device__ __forceinline__ bool delta_saved_for(const int* header, int T, int H, int chunk_cap) {
+  return header[1] == T && header[2] == H && header[3] == chunk_cap;
+}
+
+// One record per (chunk, head), fp32: W [DC][DD], U0 [DC][DD] (U after a
+// saving scan), P [DC][DC], gamma [DC],
 // decay to the chunk end [DC], T = (I + A)^-1 [DC][DC] (backward only), and
 // side values of the backward: the output term's decay gradient [DC], the
 // end-decay gradients [DC] and the end-state decay gradient [1].
@@ -426,9 +439,9 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
 // end-state gradient) and dU, then steps dS back to the chunk's start.
 __global__ __launch_bounds__(SCAN_THREADS) void delta_rscan_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ dout,
-    const int32_t* __restrict__ cu, int nseq, int T, int H, float scale,
-    const int* __restrict__ seg_off, const float* __restrict__ records,
-    float* __restrict__ dstates, float* __restrict__ dubuf) {
+    const int32_t* __restrict__ cu, int nseq, int T, int H, float scale, int chunk_cap,
+    const int* __restrict__ header, const int* __restrict__ seg_off,
+    const float* __restrict__ records, float* __restrict__ dstates, float* __restrict__ dubuf) {
   constexpr int SL = DD / SLICE;
   constexpr int BP = DD + 8;
   constexpr int OP = SLICE + 1;
@@ -443,7 +456,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_rscan_kernel(
   const int sl = blockIdx.x % SL;
   const int h = (blockIdx.x / SL) % H;
   const int s = blockIdx.x / (SL * H);
-  if (s >= nseq) return;
+  if (s >= nseq || !delta_saved_for(header, T, H, chunk_cap)) return;
   const int a = min(max(cu[s], 0), T);
   const int b = min(max(cu[s + 1], a), T);
   const int total = seg_off[nseq];
@@ -603,13 +616,13 @@ constexpr int GRAD_THREADS = 256;
 // dK_state = diag(e) U dS_C, and the decay gradients they imply.  S_0 and
 // dS_C stream through LDS 16 rows at a time; thread (4 rows, 8 columns).
 // dQ_state and dK_state go over this unit's dS_C once it has been read, dW
-// over the record's W.
+// to its own buffer (the saved records stay as the forward left them).
 __global__ __launch_bounds__(GRAD_THREADS) void delta_gstate_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ dout,
-    const int32_t* __restrict__ cu, int nseq, int T, int H, float scale,
+    const int32_t* __restrict__ cu, int nseq, int T, int H, float scale, int chunk_cap,
     const int* __restrict__ header, const int* __restrict__ seg_off, float* __restrict__ records,
     const float* __restrict__ states, float* __restrict__ dstates,
-    const float* __restrict__ dubuf) {
+    const float* __restrict__ dubuf, float* __restrict__ dwbuf) {
   constexpr int BP = DD + 8;
   constexpr int RB = 16;   // state rows per staging step
   __shared__ __attribute__((aligned(16))) bf16 dOs[DC * BP];
@@ -619,7 +632,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_gstate_kernel(
   __shared__ __attribute__((aligned(16))) float dSb[RB * DD];
   __shared__ float red[GRAD_THREADS / 64];
   const int chunk = blockIdx.x / H, h = blockIdx.x - chunk * H;
-  if (chunk >= header[0]) return;
+  if (chunk >= header[0] || !delta_saved_for(header, T, H, chunk_cap)) return;
   int c0, n;
   delta_chunk_span(cu, seg_off, nseq, T, chunk, c0, n);
   const int tid = threadIdx.x;
@@ -716,7 +729,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_gstate_kernel(
     const float gq = scale * gam[i], ek = en[i];
     float4* pq = reinterpret_cast<float4*>(dS + (size_t)i * DD + d8);
     float4* pk = reinterpret_cast<float4*>(dS + (size_t)DC * DD + (size_t)i * DD + d8);
-    float4* pw = reinterpret_cast<float4*>(rec + DeltaRecord::W + (size_t)i * DD + d8);
+    float4* pw = reinterpret_cast<float4*>(dwbuf + unit * DC * DD + (size_t)i * DD + d8);
     pq[0] = make_float4(gq * aq[x][0], gq * aq[x][1], gq * aq[x][2], gq * aq[x][3]);
     pq[1] = make_float4(gq * aq[x][4], gq * aq[x][5], gq * aq[x][6], gq * aq[x][7]);
     pk[0] = make_float4(ek * ak[x][0], ek * ak[x][1], ek * ak[x][2], ek * ak[x][3]);
@@ -740,10 +753,11 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_gstate_kernel(
 __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const bf16* __restrict__ dout,
-    const int32_t* __restrict__ cu, int nseq, int T, int H, float scale,
+    const int32_t* __restrict__ cu, int nseq, int T, int H, float scale, int chunk_cap,
     const int* __restrict__ header, const int* __restrict__ seg_off,
     const float* __restrict__ records, const float* __restrict__ dstates,
-    const float* __restrict__ dubuf, bf16* __restrict__ dq, bf16* __restrict__ dk,
+    const float* __restrict__ dubuf, const float* __restrict__ dwbuf, bf16* __restrict__ dq,
+    bf16* __restrict__ dk,
     bf16* __restrict__ dv, float* __restrict__ dg, float* __restrict__ dbeta) {
   constexpr int BP = DD + 8, CP = DC + 1;
   __shared__ __attribute__((aligned(16))) bf16 Kb[DC * BP];
@@ -755,7 +769,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
   __shared__ float Gs[DC], Bs[DC], gm[DC], dGs[DC], dBs[DC];
   static_assert(DC * CP <= DC * BP / 2, "a C x C matrix fits where V was");
   const int chunk = blockIdx.x / H, h = blockIdx.x - chunk * H;
-  if (chunk >= header[0]) return;
+  if (chunk >= header[0] || !delta_saved_for(header, T, H, chunk_cap)) return;
   int c0, n;
   delta_chunk_span(cu, seg_off, nseq, T, chunk, c0, n);
   const int tid = threadIdx.x;
@@ -878,7 +892,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
 #pragma unroll
   for (int r = 0; r < DC * DD / 4 / GRAD_THREADS; ++r) {
     const int f = tid + GRAD_THREADS * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
-    const float4 w = reinterpret_cast<const float4*>(rec + DeltaRecord::W)[f];
+    const float4 w = reinterpret_cast<const float4*>(dwbuf + unit * DC * DD)[f];
     const float4 du = reinterpret_cast<const float4*>(dubuf + unit * DC * DD)[f];
     F1[i * LP + c4] = w.x; F1[i * LP + c4 + 1] = w.y; F1[i * LP + c4 + 2] = w.z; F1[i * LP + c4 + 3] = w.w;
     F2[i * LP + c4] = du.x; F2[i * LP + c4 + 1] = du.y; F2[i * LP + c4 + 2] = du.z; F2[i * LP + c4 + 3] = du.w;
@@ -1097,22 +1111,26 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
 hipError_t launch_delta_fwd(const void* q, const void* k, const void* v, const float* g,
                             const float* beta, const int32_t* cu_seqlens, int num_seqs,
                             int total_tokens, int num_heads, float scale, void* out,
-                            void* workspace, const DeltaLayout& w, hipStream_t stream) {
+                            void* workspace, const DeltaLayout& w, bool save,
+                            hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
   int* header = reinterpret_cast<int*>(ws + w.header);
   int* seg_off = reinterpret_cast<int*>(ws + w.seg_off);
   float* records = reinterpret_cast<float*>(ws + w.records);
+  const bf16* qb = static_cast<const bf16*>(q);
+  const bf16* kb = static_cast<const bf16*>(k);
   hipLaunchKernelGGL(delta_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, cu_seqlens,
-                     num_seqs, total_tokens, (int)w.chunk_cap, header, seg_off);
+                     num_seqs, total_tokens, (int)w.chunk_cap, num_heads, save ? 1 : 0, header,
+                     seg_off);
   hipLaunchKernelGGL(delta_prep_kernel, dim3((unsigned)(w.chunk_cap * (size_t)num_heads)),
-                     dim3(PREP_THREADS), 0, stream, static_cast<const bf16*>(q),
-                     static_cast<const bf16*>(k), static_cast<const bf16*>(v), g, beta,
-                     cu_seqlens, num_seqs, total_tokens, num_heads, header, seg_off, records, 0);
+                     dim3(PREP_THREADS), 0, stream, qb, kb, static_cast<const bf16*>(v), g, beta,
+                     cu_seqlens, num_seqs, total_tokens, num_heads, header, seg_off, records,
+                     save ? 1 : 0);
   hipLaunchKernelGGL(delta_scan_kernel,
                      dim3((unsigned)((size_t)num_seqs * num_heads * (DD / SLICE))),
-                     dim3(SCAN_THREADS), 0, stream, static_cast<const bf16*>(q),
-                     static_cast<const bf16*>(k), cu_seqlens, num_seqs, total_tokens, num_heads,
-                     scale, seg_off, records, static_cast<bf16*>(out), nullptr);
+                     dim3(SCAN_THREADS), 0, stream, qb, kb, cu_seqlens, num_seqs, total_tokens,
+                     num_heads, scale, seg_off, records, static_cast<bf16*>(out),
+                     save ? reinterpret_cast<float*>(ws + w.states) : nullptr);
   return hipGetLastError();
 }
 
@@ -1120,36 +1138,36 @@ hipError_t launch_delta_bwd(const void* q, const void* k, const void* v, const f
                             const float* beta, const void* dout, const int32_t* cu_seqlens,
                             int num_seqs, int total_tokens, int num_heads, float scale, void* dq,
                             void* dk, void* dv, float* dg, float* dbeta, void* workspace,
-                            const DeltaLayout& w, hipStream_t stream) {
+                            const DeltaLayout& w, bool reuse, hipStream_t stream) {
+  if (!reuse) {   // the forward's records and states, saved
+    const hipError_t e = launch_delta_fwd(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens,
+                                          num_heads, scale, nullptr, workspace, w, true, stream);
+    if (e != hipSuccess) return e;
+  }
   char* ws = static_cast<char*>(workspace);
-  int* header = reinterpret_cast<int*>(ws + w.header);
-  int* seg_off = reinterpret_cast<int*>(ws + w.seg_off);
+  const int* header = reinterpret_cast<const int*>(ws + w.header);
+  const int* seg_off = reinterpret_cast<const int*>(ws + w.seg_off);
   float* records = reinterpret_cast<float*>(ws + w.records);
-  float* states = reinterpret_cast<float*>(ws + w.states);
+  const float* states = reinterpret_cast<const float*>(ws + w.states);
   float* dstates = reinterpret_cast<float*>(ws + w.dstates);
   float* dubuf = reinterpret_cast<float*>(ws + w.dubuf);
+  float* dwbuf = reinterpret_cast<float*>(ws + w.dwbuf);
   const bf16* qb = static_cast<const bf16*>(q);
   const bf16* kb = static_cast<const bf16*>(k);
   const bf16* vb = static_cast<const bf16*>(v);
   const bf16* ob = static_cast<const bf16*>(dout);
+  const int cap = (int)w.chunk_cap;
   const dim3 units((unsigned)(w.chunk_cap * (size_t)num_heads));
   const dim3 scans((unsigned)((size_t)num_seqs * num_heads * (DD / SLICE)));
-  hipLaunchKernelGGL(delta_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, cu_seqlens,
-                     num_seqs, total_tokens, (int)w.chunk_cap, header, seg_off);
-  hipLaunchKernelGGL(delta_prep_kernel, units, dim3(PREP_THREADS), 0, stream, qb, kb, vb, g, beta,
-                     cu_seqlens, num_seqs, total_tokens, num_heads, header, seg_off, records, 1);
-  hipLaunchKernelGGL(delta_scan_kernel, scans, dim3(SCAN_THREADS), 0, stream, qb, kb, cu_seqlens,
-                     num_seqs, total_tokens, num_heads, scale, seg_off, records,
-                     static_cast<bf16*>(nullptr), states);
   hipLaunchKernelGGL(delta_rscan_kernel, scans, dim3(SCAN_THREADS), 0, stream, qb, kb, ob,
-                     cu_seqlens, num_seqs, total_tokens, num_heads, scale, seg_off, records,
-                     dstates, dubuf);
+                     cu_seqlens, num_seqs, total_tokens, num_heads, scale, cap, header, seg_off,
+                     records, dstates, dubuf);
   hipLaunchKernelGGL(delta_gstate_kernel, units, dim3(GRAD_THREADS), 0, stream, qb, kb, ob,
-                     cu_seqlens, num_seqs, total_tokens, num_heads, scale, header, seg_off,
-                     records, states, dstates, dubuf);
+                     cu_seqlens, num_seqs, total_tokens, num_heads, scale, cap, header, seg_off,
+                     records, states, dstates, dubuf, dwbuf);
   hipLaunchKernelGGL(delta_glocal_kernel, units, dim3(GRAD_THREADS), 0, stream, qb, kb, vb, g,
-                     beta, ob, cu_seqlens, num_seqs, total_tokens, num_heads, scale, header,
-                     seg_off, records, dstates, dubuf, static_cast<bf16*>(dq),
+                     beta, ob, cu_seqlens, num_seqs, total_tokens, num_heads, scale, cap, header,
+                     seg_off, records, dstates, dubuf, dwbuf, static_cast<bf16*>(dq),
                      static_cast<bf16*>(dk), static_cast<bf16*>(dv), dg, dbeta);
   return hipGetLastError();
 }

@@ -54,7 +54,7 @@ constexpr size_t delta_record_floats() {
          (size_t)6 * DELTA_CHUNK;
 }
 struct DeltaLayout {
-  size_t header, seg_off, records, states, dstates, dubuf, total;
+  size_t header, seg_off, records, states, dstates, dubuf, dwbuf, total;
   size_t chunk_cap, record_bytes;
 };
 inline DeltaLayout delta_layout(int64_t total_tokens, int64_t num_seqs, int64_t num_heads,
@@ -69,12 +69,15 @@ inline DeltaLayout delta_layout(int64_t total_tokens, int64_t num_seqs, int64_t 
   w.states = w.records + units * w.record_bytes;
   w.dstates = w.states;
   w.dubuf = w.states;
+  w.dwbuf = w.states;
   w.total = w.states;
   if (backward) {
     const size_t state_bytes = (size_t)DELTA_DIM * DELTA_DIM * sizeof(float);
+    const size_t chunk_bytes = (size_t)DELTA_CHUNK * DELTA_DIM * sizeof(float);
     w.dstates = w.states + units * state_bytes;
     w.dubuf = w.dstates + units * state_bytes;
-    w.total = w.dubuf + units * (size_t)DELTA_CHUNK * DELTA_DIM * sizeof(float);
+    w.dwbuf = w.dubuf + units * chunk_bytes;
+    w.total = w.dwbuf + units * chunk_bytes;
   }
   return w;
 }
@@ -82,15 +85,17 @@ inline DeltaLayout delta_layout(int64_t total_tokens, int64_t num_seqs, int64_t 
 hipError_t launch_delta_fwd(const void* q, const void* k, const void* v, const float* g,
                             const float* beta, const int32_t* cu_seqlens, int num_seqs,
                             int total_tokens, int num_heads, float scale, void* out,
-                            void* workspace, const DeltaLayout& w, hipStream_t stream);
+                            void* workspace, const DeltaLayout& w, bool save,
+                            hipStream_t stream);
 
 // Gradients of sum(dout * out) for the gated delta rule: dq, dk, dv bf16
 // [T, H, D]; dg, dbeta fp32 [T, H].  Recomputes the forward's records and
-// states in the workspace (laid out with backward = true).
+// states in the workspace (laid out with backward = true), or with `reuse`
+// takes those a saving forward left there.
 hipError_t launch_delta_bwd(const void* q, const void* k, const void* v, const float* g,
                             const float* beta, const void* dout, const int32_t* cu_seqlens,
                             int num_seqs, int total_tokens, int num_heads, float scale, void* dq,
                             void* dk, void* dv, float* dg, float* dbeta, void* workspace,
-                            const DeltaLayout& w, hipStream_t stream);
+                            const DeltaLayout& w, bool reuse, hipStream_t stream);
 
 }  // namespace attn
