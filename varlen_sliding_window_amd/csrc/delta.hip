@@ -609,7 +609,8 @@ __device__ __forceinline__ void delta_chunk_span(const int32_t* __restrict__ cu,
   n = max(0, min(DC, b - c0));
 }
 
-constexpr int GRAD_THREADS = 256;
+constexpr int GRAD_THREADS = 512;
+constexpr int GR = DC / (GRAD_THREADS / 16);   // rows per thread of the per-chunk tiles (16 threads a row group)
 
 // Products with the chunk's start state S_0 and end-state gradient dS_C, per
 // (chunk, head): dQ_state = scale diag(gamma) dO S_0, dW = -dU S_0,
@@ -657,8 +658,8 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_gstate_kernel(
     Us[i * LP + c4] = u.x; Us[i * LP + c4 + 1] = u.y; Us[i * LP + c4 + 2] = u.z; Us[i * LP + c4 + 3] = u.w;
     dUs[i * LP + c4] = du.x; dUs[i * LP + c4 + 1] = du.y; dUs[i * LP + c4 + 2] = du.z; dUs[i * LP + c4 + 3] = du.w;
   }
-  const int i0 = (tid / 16) * 4, d8 = (tid % 16) * 8;
-  float aq[4][8] = {}, aw[4][8] = {}, ak[4][8] = {};
+  const int i0 = (tid / 16) * GR, d8 = (tid % 16) * 8;
+  float aq[GR][8] = {}, aw[GR][8] = {}, ak[GR][8] = {};
   float dgc = 0.f;   // <dS_C, S_0>, this thread's share
   for (int cb = 0; cb < DD; cb += RB) {
     __syncthreads();
@@ -680,7 +681,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_gstate_kernel(
       const float s0[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
       const float ds[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
+      for (int x = 0; x < GR; ++x) {
         const float o = (float)dOs[(i0 + x) * BP + cb + c];
         const float du = dUs[(i0 + x) * LP + cb + c];
         const float u = Us[(i0 + x) * LP + cb + c];
@@ -695,9 +696,9 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_gstate_kernel(
   }
   __syncthreads();   // every read of this unit's dS_C is done before it is overwritten
   // row dots q_i . (dO S_0)_i and k_i . (U dS_C)_i, summed over the 16 lanes of a row group
-  float qsd[4], kd[4];
+  float qsd[GR], kd[GR];
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
+  for (int x = 0; x < GR; ++x) {
     const int i = i0 + x;
     qsd[x] = 0.f;
     kd[x] = 0.f;
@@ -724,7 +725,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_gstate_kernel(
   const float* gam = rec + DeltaRecord::GAM;
   const float* en = rec + DeltaRecord::END;
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
+  for (int x = 0; x < GR; ++x) {
     const int i = i0 + x;
     const float gq = scale * gam[i], ek = en[i];
     float4* pq = reinterpret_cast<float4*>(dS + (size_t)i * DD + d8);
@@ -741,8 +742,12 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_gstate_kernel(
       rec[DeltaRecord::SIDE + DC + i] = ek * kd[x];      // e_i d(e_i)
     }
   }
-  if (tid == 0)   // gamma_C d(gamma_C) of the end state
-    rec[DeltaRecord::SIDE + 2 * DC] = gam[max(n - 1, 0)] * ((red[0] + red[1]) + (red[2] + red[3]));
+  if (tid == 0) {   // gamma_C d(gamma_C) of the end state
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < GRAD_THREADS / 64; ++w) tot += red[w];
+    rec[DeltaRecord::SIDE + 2 * DC] = gam[max(n - 1, 0)] * tot;
+  }
 }
 
 // The rest of the chunk's gradients, per (chunk, head), all in LDS: the
@@ -813,28 +818,27 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
     }
   }
   __syncthreads();
-  const int r0 = (tid / 16) * 4, s0 = (tid % 16) * 4;   // C x C tile: rows r0.., columns s0..
+  const int r0 = (tid / 16) * GR, s0 = (tid % 16) * 4;  // C x C tile: rows r0.., columns s0..
   const int i0 = r0, d8 = (tid % 16) * 8;               // C x D tile: rows i0.., columns d8..
 
   // dP = scale dO U^T; the decay gradient of the scores P (x) dP; the masked
   // decayed dP into M1
   {
-    float dp[4][4] = {};
+    float dp[GR][4] = {};
     for (int d = 0; d < DD; ++d) {
-      float o[4], u[4];
+      float o[GR], u[4];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        o[x] = (float)dOb[(r0 + x) * BP + d];
-        u[x] = F1[(s0 + x) * LP + d];
-      }
+      for (int x = 0; x < GR; ++x) o[x] = (float)dOb[(r0 + x) * BP + d];
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
+      for (int y = 0; y < 4; ++y) u[y] = F1[(s0 + y) * LP + d];
+#pragma unroll
+      for (int x = 0; x < GR; ++x)
 #pragma unroll
         for (int y = 0; y < 4; ++y) dp[x][y] += o[x] * u[y];
     }
-    float row[4] = {}, col[4] = {};
+    float row[GR] = {}, col[4] = {};
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int x = 0; x < GR; ++x)
 #pragma unroll
       for (int y = 0; y < 4; ++y) {
         const int i = r0 + x, j = s0 + y;
@@ -845,19 +849,18 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
         M1[i * CP + j] = j <= i ? __expf(Gs[i] - Gs[j]) * dpv : 0.f;
       }
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      atomicAdd(&dGs[r0 + x], row[x]);
-      atomicAdd(&dGs[s0 + x], -col[x]);
-    }
+    for (int x = 0; x < GR; ++x) atomicAdd(&dGs[r0 + x], row[x]);
+#pragma unroll
+    for (int y = 0; y < 4; ++y) atomicAdd(&dGs[s0 + y], -col[y]);
   }
   __syncthreads();
   // dQ = dQ_state + dPm K (written); dK = dK_state + dPm^T Q (kept)
   const float* gst = dstates + unit * DD * DD;   // dQ_state [C][D], then dK_state [C][D]
-  float dkr[4][8];
+  float dkr[GR][8];
   {
-    float dqr[4][8];
+    float dqr[GR][8];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
+    for (int x = 0; x < GR; ++x) {
       const float4* pq = reinterpret_cast<const float4*>(gst + (size_t)(i0 + x) * DD + d8);
       const float4* pk = reinterpret_cast<const float4*>(gst + (size_t)DC * DD + (size_t)(i0 + x) * DD + d8);
       const float4 qa = pq[0], qb = pq[1], ka = pk[0], kb = pk[1];
@@ -870,7 +873,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
       const bf16x8 kv = *reinterpret_cast<const bf16x8*>(Kb + j * BP + d8);
       const bf16x8 qv = *reinterpret_cast<const bf16x8*>(Qb + j * BP + d8);
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
+      for (int x = 0; x < GR; ++x) {
         const float pa = M1[(i0 + x) * CP + j], pb = M1[j * CP + i0 + x];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -880,7 +883,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
       }
     }
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int x = 0; x < GR; ++x)
       if (i0 + x < n) {
         bf16x8 o;
 #pragma unroll
@@ -902,7 +905,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
   // dX = T^T dW, dY = T^T dU (T_ji = 0 for j < i); dV = diag(beta) dY;
   // dK += diag(beta gamma) dX; the beta and decay gradients through X and Y
   {
-    float dx[4][8] = {}, dy[4][8] = {};
+    float dx[GR][8] = {}, dy[GR][8] = {};
     for (int j = i0; j < DC; ++j) {
       float w[8], u[8];
 #pragma unroll
@@ -911,7 +914,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
         u[e] = F2[j * LP + d8 + e];
       }
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
+      for (int x = 0; x < GR; ++x) {
         const float t = M1[j * CP + i0 + x];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -920,9 +923,9 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
         }
       }
     }
-    float kdx[4], vdy[4];
+    float kdx[GR], vdy[GR];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
+    for (int x = 0; x < GR; ++x) {
       const int i = i0 + x;
       const bf16x8 kv = *reinterpret_cast<const bf16x8*>(Kb + i * BP + d8);
       const bf16x8 vv = *reinterpret_cast<const bf16x8*>(Vb + i * BP + d8);
@@ -946,7 +949,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
     }
     if ((tid & 15) == 0)
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
+      for (int x = 0; x < GR; ++x) {
         const int i = i0 + x;
         atomicAdd(&dBs[i], gm[i] * kdx[x] + vdy[x]);
         atomicAdd(&dGs[i], gm[i] * Bs[i] * kdx[x]);
@@ -954,7 +957,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
   }
   // dT = dW diag(beta gamma) K^T + dU diag(beta) V^T into M2
   {
-    float tk[4][4] = {}, tv[4][4] = {};
+    float tk[GR][4] = {}, tv[GR][4] = {};
     for (int d = 0; d < DD; d += 8) {
       bf16x8 kj[4], vj[4];
 #pragma unroll
@@ -964,14 +967,14 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float w[4], u[4];
+        float w[GR], u[GR];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
+        for (int x = 0; x < GR; ++x) {
           w[x] = F1[(r0 + x) * LP + d + e];
           u[x] = F2[(r0 + x) * LP + d + e];
         }
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
+        for (int x = 0; x < GR; ++x)
 #pragma unroll
           for (int y = 0; y < 4; ++y) {
             tk[x][y] += w[x] * (float)kj[y][e];
@@ -980,7 +983,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
       }
     }
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int x = 0; x < GR; ++x)
 #pragma unroll
       for (int y = 0; y < 4; ++y) {
         const int j = s0 + y;
@@ -989,21 +992,20 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
   }
   __syncthreads();   // V is no longer read: its space holds dT T^T next
   {
-    float m[4][4] = {};
+    float m[GR][4] = {};
     for (int c = 0; c < DC; ++c) {
-      float a_[4], t_[4];
+      float a_[GR], t_[4];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        a_[x] = M2[(r0 + x) * CP + c];
-        t_[x] = M1[(s0 + x) * CP + c];
-      }
+      for (int x = 0; x < GR; ++x) a_[x] = M2[(r0 + x) * CP + c];
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
+      for (int y = 0; y < 4; ++y) t_[y] = M1[(s0 + y) * CP + c];
+#pragma unroll
+      for (int x = 0; x < GR; ++x)
 #pragma unroll
         for (int y = 0; y < 4; ++y) m[x][y] += a_[x] * t_[y];
     }
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int x = 0; x < GR; ++x)
 #pragma unroll
       for (int y = 0; y < 4; ++y) M3[(r0 + x) * CP + s0 + y] = m[x][y];
   }
@@ -1012,37 +1014,35 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
   // A_ij = beta_i exp(G_i - G_j) KK_ij, the beta and decay gradients through
   // A, and Bm = dA (x) beta_i exp(G_i - G_j) into M2 (dT is no longer read)
   {
-    float da[4][4] = {}, kk[4][4] = {};
+    float da[GR][4] = {}, kk[GR][4] = {};
     for (int c = 0; c < DC; ++c) {
-      float t_[4], m_[4];
+      float t_[GR], m_[4];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        t_[x] = M1[c * CP + r0 + x];
-        m_[x] = M3[c * CP + s0 + x];
-      }
+      for (int x = 0; x < GR; ++x) t_[x] = M1[c * CP + r0 + x];
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
+      for (int y = 0; y < 4; ++y) m_[y] = M3[c * CP + s0 + y];
+#pragma unroll
+      for (int x = 0; x < GR; ++x)
 #pragma unroll
         for (int y = 0; y < 4; ++y) da[x][y] -= t_[x] * m_[y];
     }
     for (int d = 0; d < DD; d += 8) {
-      bf16x8 ki[4], kj[4];
+      bf16x8 ki[GR], kj[4];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        ki[x] = *reinterpret_cast<const bf16x8*>(Kb + (r0 + x) * BP + d);
-        kj[x] = *reinterpret_cast<const bf16x8*>(Kb + (s0 + x) * BP + d);
-      }
+      for (int x = 0; x < GR; ++x) ki[x] = *reinterpret_cast<const bf16x8*>(Kb + (r0 + x) * BP + d);
+#pragma unroll
+      for (int y = 0; y < 4; ++y) kj[y] = *reinterpret_cast<const bf16x8*>(Kb + (s0 + y) * BP + d);
 #pragma unroll
       for (int e = 0; e < 8; ++e)
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
+        for (int x = 0; x < GR; ++x)
 #pragma unroll
           for (int y = 0; y < 4; ++y) kk[x][y] += (float)ki[x][e] * (float)kj[y][e];
     }
-    float row[4] = {}, col[4] = {}, db[4] = {};
-    float bm[4][4];
+    float row[GR] = {}, col[4] = {}, db[GR] = {};
+    float bm[GR][4];
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int x = 0; x < GR; ++x)
 #pragma unroll
       for (int y = 0; y < 4; ++y) {
         const int i = r0 + x, j = s0 + y;
@@ -1059,27 +1059,28 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
       }
     __syncthreads();   // every read of dT is done before Bm replaces it
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
+    for (int x = 0; x < GR; ++x) {
 #pragma unroll
       for (int y = 0; y < 4; ++y) M2[(r0 + x) * CP + s0 + y] = bm[x][y];
       atomicAdd(&dBs[r0 + x], db[x]);
       atomicAdd(&dGs[r0 + x], row[x]);
-      atomicAdd(&dGs[s0 + x], -col[x]);
     }
+#pragma unroll
+    for (int y = 0; y < 4; ++y) atomicAdd(&dGs[s0 + y], -col[y]);
   }
   __syncthreads();
   // dK += Bm K + Bm^T K (written)
   for (int j = 0; j < DC; ++j) {
     const bf16x8 kv = *reinterpret_cast<const bf16x8*>(Kb + j * BP + d8);
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
+    for (int x = 0; x < GR; ++x) {
       const float w = M2[(i0 + x) * CP + j] + M2[j * CP + i0 + x];
 #pragma unroll
       for (int e = 0; e < 8; ++e) dkr[x][e] += w * (float)kv[e];
     }
   }
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+  for (int x = 0; x < GR; ++x)
     if (i0 + x < n) {
       bf16x8 o;
 #pragma unroll
