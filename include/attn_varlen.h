@@ -276,6 +276,34 @@ attn_status attn_delta_bwd_ex(const void* q, const void* k, const void* v, const
                               void* dv, float* dg, float* dbeta, void* workspace,
                               size_t workspace_bytes, attn_stream_t stream);
 
+/*
+ * Kimi Delta Attention forward: the gated delta rule with one decay per key
+ * channel, the second linear layer the kernel benchmarks page
+ * (research.dws.rip/llm/kernels, section 03, Figs. 1 and 5) times, per the
+ * published recurrence.  Per head and document (state reset to zero at
+ * every document start), with alpha_t = exp(g_t) a vector over d_k:
+ *   S'_t = S_{t-1} Diag(alpha_t),
+ *   S_t = S'_t + beta_t (v_t - S'_t k_t) k_t^T,  out_t = scale S_t q_t.
+ *   q, k, v, out  as attn_delta_fwd
+ *   g             fp32 [T, H, D], per-channel log decay, 16-byte aligned
+ *   beta          fp32 [T, H]
+ *   workspace     >= attn_kda_workspace_size(T, num_seqs, H, D) bytes,
+ *                 256-byte aligned: per (64-token chunk, head) an fp32 record
+ *                 of about 148 KB
+ * Enqueues three kernels (chunk plan, per-chunk preparation, per-document
+ * scan) on `stream`; conventions as attn_delta_fwd.  The factors it forms
+ * are decays over at most one chunk or, in the in-chunk products, over at
+ * most three tokens, so any g <= 0 is safe.  No backward yet.
+ */
+size_t attn_kda_workspace_size(int32_t total_tokens, int32_t num_seqs_cap, int32_t num_heads,
+                               int32_t head_dim);
+
+attn_status attn_kda_fwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                         int32_t total_tokens, int32_t num_heads, int32_t head_dim, float scale,
+                         void* out, void* workspace, size_t workspace_bytes,
+                         attn_stream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char* attn_varlen_strerror(attn_status s);
 
@@ -289,7 +317,7 @@ int32_t attn_varlen_version(void);
  * events recorded on the call's stream.  attn_varlen_profile_stop() turns
  * recording off, waits for the recorded events, and writes up to `cap`
  * per-kernel summaries (kernels in launch-pipeline order: "schedule",
- * "forward", "dq", "dkdv", "delta_fwd", "delta_bwd"; only kernels that ran).  It returns the number of
+ * "forward", "dq", "dkdv", "delta_fwd", "delta_bwd", "kda_fwd"; only kernels that ran).  It returns the number of
  * kernels that ran (which may exceed cap), or a negative attn_status.  The
  * events add a few microseconds per launch, so time whole calls with
  * recording off.  Not for use while another thread is issuing calls.

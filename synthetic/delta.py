@@ -10,6 +10,8 @@ the projections): with the microbatch's cu_seqlens and one
   v     standard_normal [T, H, D] rounded to bf16;
   g     log of uniform(0.85, 0.999) [T, H] (per-token decay), fp32;
   beta  uniform(0.05, 0.95) [T, H] (write strength), fp32.
+Kimi Delta inputs (``make_kda_inputs``) draw the same way, except that g is
+log of uniform(0.85, 0.999) per key channel, [T, H, D].
 The output gradient of the backward (``make_delta_dout``) is standard_normal
 [T, H, D] from its own ``default_rng(seed)``, rounded to bf16.
 The bf16 values come back as raw bit patterns (what the GPU reads) and as the
@@ -50,6 +52,25 @@ def make_delta_inputs(cu_seqlens, num_heads: int, head_dim: int, seed: int) -> D
     k = unit(rng.standard_normal((t, num_heads, head_dim), dtype=np.float32))
     v = rng.standard_normal((t, num_heads, head_dim), dtype=np.float32)
     g = np.log(rng.uniform(0.85, 0.999, size=(t, num_heads))).astype(np.float32)
+    beta = rng.uniform(0.05, 0.95, size=(t, num_heads)).astype(np.float32)
+    return DeltaInputs(cu, f32_to_bf16_bits(q.astype(np.float32)), f32_to_bf16_bits(k.astype(np.float32)),
+                       f32_to_bf16_bits(v), g, beta)
+
+
+def make_kda_inputs(cu_seqlens, num_heads: int, head_dim: int, seed: int) -> DeltaInputs:
+    """As make_delta_inputs, with a per-channel gate g [T, H, D]."""
+    cu = np.asarray(cu_seqlens, dtype=np.int32)
+    t = int(cu[-1])
+    rng = np.random.default_rng(seed)
+
+    def unit(x):
+        n = np.linalg.norm(x, axis=-1, keepdims=True)
+        return x / np.where(n > 0, n, 1.0)
+
+    q = unit(rng.standard_normal((t, num_heads, head_dim), dtype=np.float32))
+    k = unit(rng.standard_normal((t, num_heads, head_dim), dtype=np.float32))
+    v = rng.standard_normal((t, num_heads, head_dim), dtype=np.float32)
+    g = np.log(rng.uniform(0.85, 0.999, size=(t, num_heads, head_dim))).astype(np.float32)
     beta = rng.uniform(0.05, 0.95, size=(t, num_heads)).astype(np.float32)
     return DeltaInputs(cu, f32_to_bf16_bits(q.astype(np.float32)), f32_to_bf16_bits(k.astype(np.float32)),
                        f32_to_bf16_bits(v), g, beta)

@@ -17,7 +17,7 @@ EINVAL, EUNSUPPORTED, EWORKSPACE = -1, -2, -3
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_(?:varlen|delta)_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(attn_(?:varlen|delta|kda)_\w+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert {"attn_varlen_fwd", "attn_varlen_bwd", "attn_varlen_workspace_size",
             "attn_varlen_strerror", "attn_delta_fwd", "attn_delta_bwd",
-            "attn_delta_bwd_workspace_size"} <= set(names)
+            "attn_delta_bwd_workspace_size", "attn_kda_fwd", "attn_kda_workspace_size"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
 
@@ -182,3 +182,18 @@ def test_delta_saving_forward_needs_the_backward_workspace(lib):
     fwd_n = lib.attn_delta_workspace_size(64, 1, 2, 128)
     args = [FAKE] * 6 + [1, 64, 2, 128, 0.088, 1, FAKE, FAKE, fwd_n, None]
     assert lib.attn_delta_fwd_ex(*args) == EWORKSPACE
+
+
+def test_kda_rejects(lib):
+    f = lib.attn_kda_fwd
+    base = [FAKE] * 6 + [1, 64, 2, 128, 0.088, FAKE, FAKE, 1 << 30, None]
+    for pos, val, code in ((0, None, EINVAL), (3, None, EINVAL), (3, FAKE + 4, EINVAL),
+                           (9, 64, EUNSUPPORTED), (10, 0.0, EINVAL), (11, None, EINVAL),
+                           (12, None, EWORKSPACE), (13, 16, EWORKSPACE)):
+        args = list(base)
+        args[pos] = val
+        assert f(*args) == code, (pos, val)
+    n = lib.attn_kda_workspace_size(16384, 64, 8, 128)
+    # per (chunk, head) record: four 64 x 128 and one 64 x 64 fp32 matrices and 128 decays
+    assert n >= (16384 // 64 + 64) * 8 * (4 * 64 * 128 + 64 * 64 + 128) * 4
+    assert lib.attn_kda_workspace_size(16384, 64, 8, 64) == 0

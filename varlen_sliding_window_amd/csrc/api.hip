@@ -74,9 +74,9 @@ attn_status check_common(const void* q, const void* k, const void* v, const int3
 }
 
 // ---- optional kernel timing (attn_varlen_profile_start / _stop) ----------
-enum KernelId { K_SCHEDULE = 0, K_FORWARD, K_DQ, K_DKDV, K_DELTA, K_DELTA_BWD, K_COUNT };
-const char* const kKernelNames[K_COUNT] = {"schedule", "forward", "dq",
-                                           "dkdv",     "delta_fwd", "delta_bwd"};
+enum KernelId { K_SCHEDULE = 0, K_FORWARD, K_DQ, K_DKDV, K_DELTA, K_DELTA_BWD, K_KDA, K_COUNT };
+const char* const kKernelNames[K_COUNT] = {"schedule",  "forward",   "dq",     "dkdv",
+                                           "delta_fwd", "delta_bwd", "kda_fwd"};
 
 struct ProfileRecord {
   int kernel;
@@ -337,6 +337,36 @@ attn_status attn_delta_fwd(const void* q, const void* k, const void* v, const fl
                            attn_stream_t stream) {
   return attn_delta_fwd_ex(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
                            head_dim, scale, 0u, out, workspace, workspace_bytes, stream);
+}
+
+size_t attn_kda_workspace_size(int32_t total_tokens, int32_t num_seqs_cap, int32_t num_heads,
+                               int32_t head_dim) {
+  if (delta_workspace(total_tokens, num_seqs_cap, num_heads, head_dim, false) == 0) return 0;
+  return attn::delta_layout(total_tokens, num_seqs_cap, num_heads, false, attn::kda_record_floats())
+      .total;
+}
+
+attn_status attn_kda_fwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                         int32_t total_tokens, int32_t num_heads, int32_t head_dim, float scale,
+                         void* out, void* workspace, size_t workspace_bytes,
+                         attn_stream_t stream) {
+  attn_status s = check_delta(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
+                              head_dim, scale);
+  if (s != ATTN_OK) return s;
+  if (!out || !aligned(out, 16) || !aligned(g, 16)) return ATTN_EINVAL;
+  const attn::DeltaLayout w = attn::delta_layout(total_tokens, num_seqs, num_heads, false,
+                                                 attn::kda_record_floats());
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < w.total) return ATTN_EWORKSPACE;
+  s = check_device();
+  if (s != ATTN_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (timed_launch(K_KDA, st, [&] {
+        return attn::launch_kda_fwd(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens,
+                                    num_heads, scale, out, workspace, w, st);
+      }) != hipSuccess)
+    return ATTN_ELAUNCH;
+  return ATTN_OK;
 }
 
 attn_status attn_delta_bwd_ex(const void* q, const void* k, const void* v, const float* g,

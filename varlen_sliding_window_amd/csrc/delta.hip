@@ -1,4 +1,5 @@
-// Gated delta-rule linear attention (Gated DeltaNet), forward, chunked.
+// Gated delta-rule linear attention, chunked: Gated DeltaNet (scalar gate)
+// forward and backward, Kimi Delta Attention (per-channel gate) forward.
 //
 // The kernel benchmarks page (research.dws.rip/llm/kernels, section 03 "What
 // linear attention costs") times Gated DeltaNet as the competing local
@@ -1107,6 +1108,338 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
   }
 }
 
+
+// ---- Kimi Delta Attention (a log decay per key channel) -------------------
+//
+// Per chunk, with G_i the in-chunk cumulative log decay of every channel
+// (a d_k vector) and gamma_i = exp(G_i):
+//   S_i = S_0 Diag(gamma_i) + sum_{j <= i} u_j (k_j o exp(G_i - G_j))^T,
+//   (I + A) U = diag(beta) V - diag(beta) (K o Gamma) S_0^T,
+//   A_ij = beta_i sum_d k_id k_jd exp(G_id - G_jd)  (j < i),
+// so U = U0 - W S_0^T with W = T diag(beta) (K o Gamma), U0 = T diag(beta) V,
+//   O = scale ((Q o Gamma) S_0^T + P U),  P_ij = sum_d q_id k_jd exp(G_id - G_jd),
+//   S_C = S_0 Diag(gamma_C) + U^T (K o exp(G_C - G)).
+// Every factor the kernels form is a decay over at most the chunk (<= 1) or,
+// in the Gram products, over at most three tokens, so no exponential
+// overflows whatever the gate.
+
+struct KdaRecord {
+  static constexpr size_t W = 0;
+  static constexpr size_t U0 = W + (size_t)DC * DD;
+  static constexpr size_t QH = U0 + (size_t)DC * DD;   // q_i o gamma_i
+  static constexpr size_t KH = QH + (size_t)DC * DD;   // k_j o exp(G_C - G_j)
+  static constexpr size_t P = KH + (size_t)DC * DD;
+  static constexpr size_t GC = P + (size_t)DC * DC;    // gamma_C, per channel
+  static constexpr size_t FLOATS = GC + DD;
+};
+static_assert(KdaRecord::FLOATS == kda_record_floats(), "record layout");
+static_assert(KdaRecord::FLOATS % 4 == 0 && KdaRecord::GC % 4 == 0, "16-byte aligned fields");
+
+__global__ __launch_bounds__(PREP_THREADS) void kda_prep_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
+    int nseq, int T, int H, const int* __restrict__ header, const int* __restrict__ seg_off,
+    float* __restrict__ records) {
+  constexpr int BP = DD + 8;
+  __shared__ __attribute__((aligned(16))) bf16 Ks[DC * BP];
+  __shared__ __attribute__((aligned(16))) bf16 Qs[DC * BP];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[DC * BP];
+  __shared__ float Gl[DC * LP];          // cumulative log decays, then X = beta gamma k
+  __shared__ float As[DC * (DC + 1)];    // A, then T = (I + A)^-1 in place
+  __shared__ float Bs[DC];
+  const int chunk = blockIdx.x / H, h = blockIdx.x - chunk * H;
+  if (chunk >= header[0]) return;
+  int c0, n;
+  delta_chunk_span(cu, seg_off, nseq, T, chunk, c0, n);
+  const int tid = threadIdx.x;
+  const size_t rs = (size_t)H * DD;
+#pragma unroll
+  for (int r = 0; r < DC * DD / 8 / PREP_THREADS; ++r) {
+    const int f = tid + PREP_THREADS * r, i = f / (DD / 8), ch = f % (DD / 8);
+    const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + ch * 8;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(Ks + i * BP + ch * 8) = i < n ? *reinterpret_cast<const uint4*>(k + off) : z;
+    *reinterpret_cast<uint4*>(Qs + i * BP + ch * 8) = i < n ? *reinterpret_cast<const uint4*>(q + off) : z;
+    *reinterpret_cast<uint4*>(Vs + i * BP + ch * 8) = i < n ? *reinterpret_cast<const uint4*>(v + off) : z;
+  }
+#pragma unroll
+  for (int r = 0; r < DC * DD / 4 / PREP_THREADS; ++r) {
+    const int f = tid + PREP_THREADS * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
+    const float4 gv = i < n ? *reinterpret_cast<const float4*>(g + (size_t)(c0 + i) * rs + (size_t)h * DD + c4)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    Gl[i * LP + c4] = gv.x; Gl[i * LP + c4 + 1] = gv.y; Gl[i * LP + c4 + 2] = gv.z; Gl[i * LP + c4 + 3] = gv.w;
+  }
+  if (tid < DC) Bs[tid] = tid < n ? beta[(size_t)(c0 + tid) * H + h] : 0.f;
+  __syncthreads();
+  if (tid < DD) {   // in-chunk cumulative log decay of channel tid
+    float acc = 0.f;
+    for (int i = 0; i < DC; ++i) {
+      acc += Gl[i * LP + tid];
+      Gl[i * LP + tid] = acc;
+    }
+  }
+  __syncthreads();
+  float* rec = records + (size_t)blockIdx.x * KdaRecord::FLOATS;
+  // Gram products with the per-channel decays, a 4 x 4 block of (row, column)
+  // pairs per thread; exp(G_i - G_j) = exp(G_i - G_j0) exp(G_j0 - G_j) about
+  // the block's first column j0, both factors bounded (rows i >= j0)
+  {
+    const int i0 = (tid / 16) * 4, j0 = (tid % 16) * 4;
+    float kk[4][4] = {}, qk[4][4] = {};
+    if (j0 <= i0) {   // blocks above the diagonal stay zero
+      for (int d = 0; d < DD; d += 8) {
+        bf16x8 ki[4], qi[4], kj[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          ki[x] = *reinterpret_cast<const bf16x8*>(Ks + (i0 + x) * BP + d);
+          qi[x] = *reinterpret_cast<const bf16x8*>(Qs + (i0 + x) * BP + d);
+          kj[x] = *reinterpret_cast<const bf16x8*>(Ks + (j0 + x) * BP + d);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float ref = Gl[j0 * LP + d + e];
+          float ka[4], qa[4], kb[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const float a = __expf(Gl[(i0 + x) * LP + d + e] - ref);
+            ka[x] = (float)ki[x][e] * a;
+            qa[x] = (float)qi[x][e] * a;
+            kb[x] = (float)kj[x][e] * __expf(ref - Gl[(j0 + x) * LP + d + e]);
+          }
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+              kk[x][y] += ka[x] * kb[y];
+              qk[x][y] += qa[x] * kb[y];
+            }
+        }
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        const int i = i0 + x, j = j0 + y;
+        As[i * (DC + 1) + j] = j < i ? Bs[i] * kk[x][y] : 0.f;
+        rec[KdaRecord::P + i * DC + j] = j <= i ? qk[x][y] : 0.f;
+      }
+  }
+  // the chunk's total decay, q o gamma and k o exp(G_C - G)
+  const int last = max(n - 1, 0);
+  if (tid < DD) rec[KdaRecord::GC + tid] = __expf(Gl[last * LP + tid]);
+  for (int f = tid; f < DC * DD; f += PREP_THREADS) {
+    const int i = f / DD, d = f % DD;
+    const float G = Gl[i * LP + d];
+    rec[KdaRecord::QH + f] = (float)Qs[i * BP + d] * __expf(G);
+    rec[KdaRecord::KH + f] = i < n ? (float)Ks[i * BP + d] * __expf(Gl[last * LP + d] - G) : 0.f;
+  }
+  __syncthreads();
+  // T = (I + A)^-1 row by row in place of A, as for the scalar gate
+  for (int i = 1; i < DC; ++i) {
+    float acc = 0.f;
+    if (tid < i) {
+      const int c = tid;
+      float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+      int j = c + 1;
+      for (; j + 3 < i; j += 4) {
+        p0 += As[i * (DC + 1) + j] * As[j * (DC + 1) + c];
+        p1 += As[i * (DC + 1) + j + 1] * As[(j + 1) * (DC + 1) + c];
+        p2 += As[i * (DC + 1) + j + 2] * As[(j + 2) * (DC + 1) + c];
+        p3 += As[i * (DC + 1) + j + 3] * As[(j + 3) * (DC + 1) + c];
+      }
+      for (; j < i; ++j) p0 += As[i * (DC + 1) + j] * As[j * (DC + 1) + c];
+      acc = -As[i * (DC + 1) + c] - ((p0 + p1) + (p2 + p3));
+    }
+    __syncthreads();
+    if (tid < i) As[i * (DC + 1) + tid] = acc;
+    __syncthreads();
+  }
+  // X = diag(beta) (K o Gamma) over the log decays (each thread its own entries)
+  for (int f = tid; f < DC * DD; f += PREP_THREADS) {
+    const int i = f / DD, d = f % DD;
+    Gl[i * LP + d] = Bs[i] * (float)Ks[i * BP + d] * __expf(Gl[i * LP + d]);
+  }
+  __syncthreads();
+  // W = T X, U0 = T diag(beta) V: thread (4 rows, 8 columns)
+  {
+    const int i0 = (tid / 16) * 4, d8 = (tid % 16) * 8;
+    float w[4][8] = {}, u[4][8] = {};
+    for (int j = 0; j < DC; ++j) {
+      const float su = Bs[j];
+      const bf16x8 vv = *reinterpret_cast<const bf16x8*>(Vs + j * BP + d8);
+      float xv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xv[e] = Gl[j * LP + d8 + e];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int i = i0 + x;
+        const float t = j < i ? As[i * (DC + 1) + j] : (j == i ? 1.f : 0.f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          w[x][e] += t * xv[e];
+          u[x][e] += t * su * (float)vv[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      float4* dw = reinterpret_cast<float4*>(rec + KdaRecord::W + (i0 + x) * DD + d8);
+      float4* du = reinterpret_cast<float4*>(rec + KdaRecord::U0 + (i0 + x) * DD + d8);
+      dw[0] = make_float4(w[x][0], w[x][1], w[x][2], w[x][3]);
+      dw[1] = make_float4(w[x][4], w[x][5], w[x][6], w[x][7]);
+      du[0] = make_float4(u[x][0], u[x][1], u[x][2], u[x][3]);
+      du[1] = make_float4(u[x][4], u[x][5], u[x][6], u[x][7]);
+    }
+  }
+}
+
+// Walks a document's chunks for one head and a slice of SLICE d_v rows of S,
+// as delta_scan_kernel does, with the decays folded into the record:
+// U = U0 - W S^T, O = scale (Q_hat S^T + P U), S <- S Diag(gamma_C) + U^T K_hat.
+__global__ __launch_bounds__(SCAN_THREADS) void kda_scan_kernel(
+    const int32_t* __restrict__ cu, int nseq, int T, int H, float scale,
+    const int* __restrict__ seg_off, const float* __restrict__ records, bf16* __restrict__ out) {
+  constexpr int SL = DD / SLICE;
+  constexpr int OP = SLICE + 1;
+  __shared__ float Ss[SLICE * LP];
+  __shared__ float Ws[DC * LP];
+  __shared__ float QHs[DC * LP];
+  __shared__ __attribute__((aligned(16))) float KHs[DC * DD];   // read a row at a time
+  __shared__ float Ps[DC * (DC + 1)];
+  __shared__ float U0s[DC * OP];
+  __shared__ float Us[DC * OP];
+  __shared__ float QSs[DC * OP];
+  __shared__ __attribute__((aligned(16))) float GCs[DD];
+  const int sl = blockIdx.x % SL;
+  const int h = (blockIdx.x / SL) % H;
+  const int s = blockIdx.x / (SL * H);
+  if (s >= nseq) return;
+  const int a = min(max(cu[s], 0), T);
+  const int b = min(max(cu[s + 1], a), T);
+  const int total = seg_off[nseq];
+  const int first = min(seg_off[s], total);
+  const int count = max(0, min(seg_off[s + 1], total) - first);
+  const int tid = threadIdx.x;
+  const int cbase = sl * SLICE;
+  const size_t rs = (size_t)H * DD;
+  for (int e = tid; e < SLICE * LP; e += SCAN_THREADS) Ss[e] = 0.f;
+
+  constexpr int NT = SCAN_THREADS;
+  constexpr int WR = DC * DD / 4 / NT, PR = DC * DC / 4 / NT;
+  float4 wr[WR], qr[WR], kr[WR], pr[PR];
+  float4 ur = make_float4(0.f, 0.f, 0.f, 0.f), gr = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto fetch = [&](int ci) {
+    const float4* r4 = reinterpret_cast<const float4*>(
+        records + ((size_t)(first + ci) * H + h) * KdaRecord::FLOATS);
+#pragma unroll
+    for (int r = 0; r < WR; ++r) {
+      wr[r] = r4[KdaRecord::W / 4 + tid + NT * r];
+      qr[r] = r4[KdaRecord::QH / 4 + tid + NT * r];
+      kr[r] = r4[KdaRecord::KH / 4 + tid + NT * r];
+    }
+#pragma unroll
+    for (int r = 0; r < PR; ++r) pr[r] = r4[KdaRecord::P / 4 + tid + NT * r];
+    if (tid < DC * SLICE / 4)
+      ur = r4[(KdaRecord::U0 + (size_t)(tid / (SLICE / 4)) * DD + cbase) / 4 + (tid % (SLICE / 4))];
+    if (tid < DD / 4) gr = r4[KdaRecord::GC / 4 + tid];
+  };
+  if (count > 0) fetch(0);
+
+  for (int ci = 0; ci < count; ++ci) {
+    const int c0 = a + ci * DC;
+    const int n = min(DC, b - c0);
+    __syncthreads();   // every read of the previous chunk's LDS data is done
+#pragma unroll
+    for (int r = 0; r < WR; ++r) {
+      const int f = tid + NT * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
+      Ws[i * LP + c4] = wr[r].x; Ws[i * LP + c4 + 1] = wr[r].y;
+      Ws[i * LP + c4 + 2] = wr[r].z; Ws[i * LP + c4 + 3] = wr[r].w;
+      QHs[i * LP + c4] = qr[r].x; QHs[i * LP + c4 + 1] = qr[r].y;
+      QHs[i * LP + c4 + 2] = qr[r].z; QHs[i * LP + c4 + 3] = qr[r].w;
+      reinterpret_cast<float4*>(KHs)[f] = kr[r];
+    }
+#pragma unroll
+    for (int r = 0; r < PR; ++r) {
+      const int f = tid + NT * r, pi = f / (DC / 4), pj = (f % (DC / 4)) * 4;
+      Ps[pi * (DC + 1) + pj] = pr[r].x;
+      Ps[pi * (DC + 1) + pj + 1] = pr[r].y;
+      Ps[pi * (DC + 1) + pj + 2] = pr[r].z;
+      Ps[pi * (DC + 1) + pj + 3] = pr[r].w;
+    }
+    if (tid < DC * SLICE / 4) {
+      const int i = tid / (SLICE / 4), c4 = (tid % (SLICE / 4)) * 4;
+      U0s[i * OP + c4] = ur.x; U0s[i * OP + c4 + 1] = ur.y;
+      U0s[i * OP + c4 + 2] = ur.z; U0s[i * OP + c4 + 3] = ur.w;
+    }
+    if (tid < DD / 4) reinterpret_cast<float4*>(GCs)[tid] = gr;
+    __syncthreads();
+    if (ci + 1 < count) fetch(ci + 1);
+
+    // U = U0 - W S^T and Q_hat S^T: thread (row i, CPT slice columns)
+    constexpr int CPT = DC * SLICE / NT;
+    const int i = tid / (SLICE / CPT), cc = (tid % (SLICE / CPT)) * CPT;
+    {
+      float ws[CPT] = {}, qs[CPT] = {};
+      for (int d = 0; d < DD; ++d) {
+        const float w = Ws[i * LP + d];
+        const float qv = QHs[i * LP + d];
+#pragma unroll
+        for (int x = 0; x < CPT; ++x) {
+          const float sv = Ss[(cc + x) * LP + d];
+          ws[x] += w * sv;
+          qs[x] += qv * sv;
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < CPT; ++x) {
+        Us[i * OP + cc + x] = U0s[i * OP + cc + x] - ws[x];
+        QSs[i * OP + cc + x] = qs[x];
+      }
+    }
+    __syncthreads();
+    // O = scale (Q_hat S^T + P U) for the chunk's rows inside the document
+    if (i < n) {
+      float acc[CPT];
+#pragma unroll
+      for (int x = 0; x < CPT; ++x) acc[x] = QSs[i * OP + cc + x];
+      for (int j = 0; j <= i; ++j) {
+        const float p = Ps[i * (DC + 1) + j];
+#pragma unroll
+        for (int x = 0; x < CPT; ++x) acc[x] += p * Us[j * OP + cc + x];
+      }
+      bf16* op = out + (size_t)(c0 + i) * rs + (size_t)h * DD + cbase + cc;
+#pragma unroll
+      for (int x = 0; x < CPT; ++x) op[x] = (bf16)(scale * acc[x]);
+    }
+    // S <- S Diag(gamma_C) + U^T K_hat: thread (row c, two groups of 4
+    // columns 64 apart), each thread its own entries of S
+    {
+      static_assert(SLICE * DD / NT == 8 && DD == 128, "8 columns per thread");
+      const int c = tid / 16, l4 = (tid % 16) * 4;
+      float acc[8] = {};
+      for (int j = 0; j < n; ++j) {
+        const float u = Us[j * OP + c];
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+          const float4 kh = *reinterpret_cast<const float4*>(KHs + j * DD + l4 + 64 * y);
+          acc[4 * y] += u * kh.x;
+          acc[4 * y + 1] += u * kh.y;
+          acc[4 * y + 2] += u * kh.z;
+          acc[4 * y + 3] += u * kh.w;
+        }
+      }
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int d = l4 + 64 * y + e;
+          Ss[c * LP + d] = GCs[d] * Ss[c * LP + d] + acc[4 * y + e];
+        }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_delta_fwd(const void* q, const void* k, const void* v, const float* g,
@@ -1132,6 +1465,27 @@ hipError_t launch_delta_fwd(const void* q, const void* k, const void* v, const f
                      dim3(SCAN_THREADS), 0, stream, qb, kb, cu_seqlens, num_seqs, total_tokens,
                      num_heads, scale, seg_off, records, static_cast<bf16*>(out),
                      save ? reinterpret_cast<float*>(ws + w.states) : nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_kda_fwd(const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, const int32_t* cu_seqlens, int num_seqs,
+                          int total_tokens, int num_heads, float scale, void* out,
+                          void* workspace, const DeltaLayout& w, hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  int* header = reinterpret_cast<int*>(ws + w.header);
+  int* seg_off = reinterpret_cast<int*>(ws + w.seg_off);
+  float* records = reinterpret_cast<float*>(ws + w.records);
+  hipLaunchKernelGGL(delta_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, cu_seqlens,
+                     num_seqs, total_tokens, (int)w.chunk_cap, num_heads, 0, header, seg_off);
+  hipLaunchKernelGGL(kda_prep_kernel, dim3((unsigned)(w.chunk_cap * (size_t)num_heads)),
+                     dim3(PREP_THREADS), 0, stream, static_cast<const bf16*>(q),
+                     static_cast<const bf16*>(k), static_cast<const bf16*>(v), g, beta,
+                     cu_seqlens, num_seqs, total_tokens, num_heads, header, seg_off, records);
+  hipLaunchKernelGGL(kda_scan_kernel,
+                     dim3((unsigned)((size_t)num_seqs * num_heads * (DD / SLICE))),
+                     dim3(SCAN_THREADS), 0, stream, cu_seqlens, num_seqs, total_tokens,
+                     num_heads, scale, seg_off, records, static_cast<bf16*>(out));
   return hipGetLastError();
 }
 

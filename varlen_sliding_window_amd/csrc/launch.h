@@ -57,11 +57,17 @@ struct DeltaLayout {
   size_t header, seg_off, records, states, dstates, dubuf, dwbuf, total;
   size_t chunk_cap, record_bytes;
 };
+// Kimi Delta record: W, U0, q (x) gamma, k (x) end decay [C][D]; P [C][C];
+// the chunk's total decay [D]
+constexpr size_t kda_record_floats() {
+  return (size_t)4 * DELTA_CHUNK * DELTA_DIM + (size_t)DELTA_CHUNK * DELTA_CHUNK + DELTA_DIM;
+}
 inline DeltaLayout delta_layout(int64_t total_tokens, int64_t num_seqs, int64_t num_heads,
-                                bool backward = false) {
+                                bool backward = false,
+                                size_t record_floats = delta_record_floats()) {
   DeltaLayout w;
   w.chunk_cap = (size_t)((total_tokens + DELTA_CHUNK - 1) / DELTA_CHUNK) + (size_t)num_seqs;
-  w.record_bytes = delta_record_floats() * sizeof(float);
+  w.record_bytes = record_floats * sizeof(float);
   const size_t units = w.chunk_cap * (size_t)num_heads;
   w.header = 0;
   w.seg_off = 256;
@@ -87,6 +93,13 @@ hipError_t launch_delta_fwd(const void* q, const void* k, const void* v, const f
                             int total_tokens, int num_heads, float scale, void* out,
                             void* workspace, const DeltaLayout& w, bool save,
                             hipStream_t stream);
+
+// Kimi Delta Attention forward (delta.hip): the gate g is [T, H, DELTA_DIM],
+// one log decay per key channel; workspace laid out with kda_record_floats().
+hipError_t launch_kda_fwd(const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, const int32_t* cu_seqlens, int num_seqs,
+                          int total_tokens, int num_heads, float scale, void* out,
+                          void* workspace, const DeltaLayout& w, hipStream_t stream);
 
 // Gradients of sum(dout * out) for the gated delta rule: dq, dk, dv bf16
 // [T, H, D]; dg, dbeta fp32 [T, H].  Recomputes the forward's records and
