@@ -259,6 +259,57 @@ def delta_bench(args, device):
     }))
 
 
+def kda_bench(args, device):
+    """Kimi Delta Attention forward on the workload microbatch (one layer,
+    H = 8 heads of 128, the attention workload's documents); one JSON line."""
+    import torch
+    import varlen_sliding_window_amd as attn
+    from synthetic import CONFIGS, make_cu_seqlens, make_kda_inputs
+
+    cu, _ = make_cu_seqlens(CONFIGS["ctx4096_w512"], args.seed)
+    heads, d = 8, 128
+    inp = make_kda_inputs(cu, heads, d, args.seed)
+    t = int(cu[-1])
+
+    def dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+    q, k, v = dev_bf16(inp.q_bits), dev_bf16(inp.k_bits), dev_bf16(inp.v_bits)
+    g = torch.from_numpy(inp.g).to(device)
+    beta = torch.from_numpy(inp.beta).to(device)
+    cu_dev = torch.from_numpy(cu.astype(np.int32)).to(device)
+    ws = torch.empty(attn.kda_workspace_size(t, len(cu) - 1, heads, d), dtype=torch.uint8,
+                     device=device)
+    out = torch.zeros_like(q)
+
+    def step():
+        attn.kda_fwd(q, k, v, g, beta, cu_dev, d ** -0.5, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    attn.profile_start()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kern = attn.profile_stop()
+    print(json.dumps({
+        "metric": "Kimi Delta Attention forward per 16,384-token microbatch, 8 heads of 128",
+        "value": ms, "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": False, "dtype": "bf16 in, fp32 arithmetic",
+        "data": "synthetic (seeded lognormal document packing; unit q, k; N(0,1) v; per-channel gates)",
+        "vs_baseline": None,
+        "config": {"workload": "kda_ctx4096", "total_tokens": t, "num_heads": heads,
+                   "head_dim": d, "num_seqs": len(cu) - 1, "seed": args.seed},
+        "kernels": {kk: {"avg_ms": vv["avg_ms"]} for kk, vv in kern.items()},
+    }))
+
+
 def copy_calibration(device, mib: int = 256, reps: int = 3):
     """Plain device copies of a known size, for scaling the FETCH_SIZE and
     WRITE_SIZE counters (each copy reads and writes exactly mib MiB)."""
@@ -280,7 +331,7 @@ def main():
                     help="untimed steps first (the GPU clock takes a few tens of ms of load to settle)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--workload", default="ctx4096_w512+global",
-                    choices=sorted(WORKLOADS) + ["delta_ctx4096"])
+                    choices=sorted(WORKLOADS) + ["delta_ctx4096", "kda_ctx4096"])
     ap.add_argument("--softcap", type=float, default=0.0,
                     help="logit soft-cap C > 0 (every logit becomes C tanh(logit / C))")
     ap.add_argument("--head-dim", type=int, default=0, choices=[0, 64, 128, 256],
@@ -318,6 +369,9 @@ def main():
         return
     if args.workload == "delta_ctx4096":
         delta_bench(args, device)
+        return
+    if args.workload == "kda_ctx4096":
+        kda_bench(args, device)
         return
     cu, layers = build_layers(args.workload, args.seed, device, args.softcap, args.head_dim,
                               args.band)
