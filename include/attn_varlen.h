@@ -289,11 +289,12 @@ attn_status attn_delta_bwd_ex(const void* q, const void* k, const void* v, const
  *   beta          fp32 [T, H]
  *   workspace     >= attn_kda_workspace_size(T, num_seqs, H, D) bytes,
  *                 256-byte aligned: per (64-token chunk, head) an fp32 record
- *                 of about 148 KB
+ *                 of about 181 KB (the backward's layout: its triangular
+ *                 inverse and decayed K K^T are written only by the backward)
  * Enqueues three kernels (chunk plan, per-chunk preparation, per-document
  * scan) on `stream`; conventions as attn_delta_fwd.  The factors it forms
  * are decays over at most one chunk or, in the in-chunk products, over at
- * most three tokens, so any g <= 0 is safe.  No backward yet.
+ * most three tokens, so any g <= 0 is safe.
  */
 size_t attn_kda_workspace_size(int32_t total_tokens, int32_t num_seqs_cap, int32_t num_heads,
                                int32_t head_dim);
@@ -302,6 +303,31 @@ attn_status attn_kda_fwd(const void* q, const void* k, const void* v, const floa
                          const float* beta, const int32_t* cu_seqlens, int32_t num_seqs,
                          int32_t total_tokens, int32_t num_heads, int32_t head_dim, float scale,
                          void* out, void* workspace, size_t workspace_bytes,
+                         attn_stream_t stream);
+
+/*
+ * Kimi Delta Attention backward: the gradients of sum(dout * out) for
+ * attn_kda_fwd with the same inputs and checks.
+ *   dout          bf16 [T, H, D]
+ *   dq, dk, dv    bf16 [T, H, D]; dg fp32 [T, H, D] (16-byte aligned);
+ *                 dbeta fp32 [T, H]; written for tokens inside documents
+ *   workspace     >= attn_kda_bwd_workspace_size(T, num_seqs, H, D) bytes,
+ *                 256-byte aligned: the forward's records (with T and the
+ *                 decayed K K^T), each chunk's start state and end-state
+ *                 gradient, dU and dW, about 378 KB per (64-token chunk, head)
+ * Recomputes the forward's records and chunk states, then runs a reverse
+ * per-document scan and three per-chunk gradient kernels (state products,
+ * triangular solve, decayed pair products): seven kernels on `stream`,
+ * nothing allocated.  Every exponential it forms is a decay (at most 1).
+ */
+size_t attn_kda_bwd_workspace_size(int32_t total_tokens, int32_t num_seqs_cap,
+                                   int32_t num_heads, int32_t head_dim);
+
+attn_status attn_kda_bwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const void* dout, const int32_t* cu_seqlens,
+                         int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                         int32_t head_dim, float scale, void* dq, void* dk, void* dv, float* dg,
+                         float* dbeta, void* workspace, size_t workspace_bytes,
                          attn_stream_t stream);
 
 /* Static description of a status code (never NULL). */
@@ -317,7 +343,7 @@ int32_t attn_varlen_version(void);
  * events recorded on the call's stream.  attn_varlen_profile_stop() turns
  * recording off, waits for the recorded events, and writes up to `cap`
  * per-kernel summaries (kernels in launch-pipeline order: "schedule",
- * "forward", "dq", "dkdv", "delta_fwd", "delta_bwd", "kda_fwd"; only kernels that ran).  It returns the number of
+ * "forward", "dq", "dkdv", "delta_fwd", "delta_bwd", "kda_fwd", "kda_bwd"; only kernels that ran).  It returns the number of
  * kernels that ran (which may exceed cap), or a negative attn_status.  The
  * events add a few microseconds per launch, so time whole calls with
  * recording off.  Not for use while another thread is issuing calls.

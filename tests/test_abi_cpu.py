@@ -31,7 +31,8 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert {"attn_varlen_fwd", "attn_varlen_bwd", "attn_varlen_workspace_size",
             "attn_varlen_strerror", "attn_delta_fwd", "attn_delta_bwd",
-            "attn_delta_bwd_workspace_size", "attn_kda_fwd", "attn_kda_workspace_size"} <= set(names)
+            "attn_delta_bwd_workspace_size", "attn_kda_fwd", "attn_kda_workspace_size", "attn_kda_bwd",
+            "attn_kda_bwd_workspace_size"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
 
@@ -197,3 +198,19 @@ def test_kda_rejects(lib):
     # per (chunk, head) record: four 64 x 128 and one 64 x 64 fp32 matrices and 128 decays
     assert n >= (16384 // 64 + 64) * 8 * (4 * 64 * 128 + 64 * 64 + 128) * 4
     assert lib.attn_kda_workspace_size(16384, 64, 8, 64) == 0
+
+
+def test_kda_bwd_rejects(lib):
+    f = lib.attn_kda_bwd
+    base = [FAKE] * 7 + [1, 64, 2, 128, 0.088] + [FAKE] * 6 + [1 << 31, None]
+    for pos, val, code in ((3, FAKE + 4, EINVAL), (5, None, EINVAL), (15, FAKE + 4, EINVAL),
+                           (16, None, EINVAL), (10, 64, EUNSUPPORTED), (17, None, EWORKSPACE),
+                           (18, 1024, EWORKSPACE)):
+        args = list(base)
+        args[pos] = val
+        assert f(*args) == code, (pos, val)
+    fwd = lib.attn_kda_workspace_size(16384, 64, 8, 128)
+    bwd = lib.attn_kda_bwd_workspace_size(16384, 64, 8, 128)
+    units = (16384 // 64 + 64) * 8
+    # one record layout for both; the backward adds two states, dU and dW per unit
+    assert bwd - fwd == units * (2 * 128 * 128 + 2 * 64 * 128) * 4

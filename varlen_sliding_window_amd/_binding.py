@@ -80,6 +80,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_kda_workspace_size.restype = sz
     lib.attn_kda_fwd.argtypes = [vp] * 6 + [i32, i32, i32, i32, ctypes.c_float, vp, vp, sz, vp]
     lib.attn_kda_fwd.restype = ctypes.c_int
+    lib.attn_kda_bwd_workspace_size.argtypes = [i32] * 4
+    lib.attn_kda_bwd_workspace_size.restype = sz
+    lib.attn_kda_bwd.argtypes = [vp] * 7 + [i32, i32, i32, i32, ctypes.c_float] + [vp] * 6 + [
+        sz, vp]
+    lib.attn_kda_bwd.restype = ctypes.c_int
     lib.attn_delta_fwd_ex.argtypes = [vp] * 6 + [i32, i32, i32, i32, ctypes.c_float,
                                                  ctypes.c_uint32, vp, vp, sz, vp]
     lib.attn_delta_fwd_ex.restype = ctypes.c_int
@@ -300,6 +305,38 @@ def kda_fwd(q, k, v, g, beta, cu_seqlens, scale: float | None = None, out=None, 
     if st != ATTN_OK:
         raise AttnError(st, "attn_kda_fwd")
     return out
+
+
+def kda_bwd(q, k, v, g, beta, dout, cu_seqlens, scale: float | None = None, workspace=None):
+    """attn_kda_bwd: gradients of sum(dout * out) of the Kimi Delta forward.
+    Returns dq, dk, dv (bf16 [T, H, D]), dg (fp32 [T, H, D]) and dbeta (fp32
+    [T, H]), zero-filled first."""
+    for name, t_ in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _check_tensor(name, t_, torch.bfloat16, 3)
+    _check_tensor("g", g, torch.float32, 3)
+    _check_tensor("beta", beta, torch.float32, 2)
+    _check_tensor("cu_seqlens", cu_seqlens, torch.int32, 1)
+    t, h, d = q.shape
+    if (k.shape != q.shape or v.shape != q.shape or dout.shape != q.shape or g.shape != q.shape
+            or beta.shape != (t, h)):
+        raise ValueError("q, k, v, g, dout must be [T, H, D] and beta [T, H]")
+    nseq = cu_seqlens.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
+    dg, dbeta = torch.zeros_like(g), torch.zeros_like(beta)
+    if workspace is None:
+        n = int(load_library().attn_kda_bwd_workspace_size(t, nseq, h, d))
+        if n == 0:
+            raise AttnError(-1, "attn_kda_bwd_workspace_size")
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    st = load_library().attn_kda_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(dout),
+                                     _ptr(cu_seqlens), nseq, t, h, d, float(scale), _ptr(dq),
+                                     _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(workspace),
+                                     workspace.numel(), _stream_handle(q.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_kda_bwd")
+    return dq, dk, dv, dg, dbeta
 
 
 def delta_bwd_workspace_size(total_tokens: int, num_seqs: int, num_heads: int,

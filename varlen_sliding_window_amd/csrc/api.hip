@@ -74,9 +74,11 @@ attn_status check_common(const void* q, const void* k, const void* v, const int3
 }
 
 // ---- optional kernel timing (attn_varlen_profile_start / _stop) ----------
-enum KernelId { K_SCHEDULE = 0, K_FORWARD, K_DQ, K_DKDV, K_DELTA, K_DELTA_BWD, K_KDA, K_COUNT };
-const char* const kKernelNames[K_COUNT] = {"schedule",  "forward",   "dq",     "dkdv",
-                                           "delta_fwd", "delta_bwd", "kda_fwd"};
+enum KernelId {
+  K_SCHEDULE = 0, K_FORWARD, K_DQ, K_DKDV, K_DELTA, K_DELTA_BWD, K_KDA, K_KDA_BWD, K_COUNT
+};
+const char* const kKernelNames[K_COUNT] = {"schedule",  "forward",   "dq",      "dkdv",
+                                           "delta_fwd", "delta_bwd", "kda_fwd", "kda_bwd"};
 
 struct ProfileRecord {
   int kernel;
@@ -364,6 +366,40 @@ attn_status attn_kda_fwd(const void* q, const void* k, const void* v, const floa
   if (timed_launch(K_KDA, st, [&] {
         return attn::launch_kda_fwd(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens,
                                     num_heads, scale, out, workspace, w, st);
+      }) != hipSuccess)
+    return ATTN_ELAUNCH;
+  return ATTN_OK;
+}
+
+size_t attn_kda_bwd_workspace_size(int32_t total_tokens, int32_t num_seqs_cap,
+                                   int32_t num_heads, int32_t head_dim) {
+  if (delta_workspace(total_tokens, num_seqs_cap, num_heads, head_dim, false) == 0) return 0;
+  return attn::delta_layout(total_tokens, num_seqs_cap, num_heads, true, attn::kda_record_floats())
+      .total;
+}
+
+attn_status attn_kda_bwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const void* dout, const int32_t* cu_seqlens,
+                         int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                         int32_t head_dim, float scale, void* dq, void* dk, void* dv, float* dg,
+                         float* dbeta, void* workspace, size_t workspace_bytes,
+                         attn_stream_t stream) {
+  attn_status s = check_delta(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
+                              head_dim, scale);
+  if (s != ATTN_OK) return s;
+  if (!dout || !dq || !dk || !dv || !dg || !dbeta) return ATTN_EINVAL;
+  if (!aligned(g, 16) || !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) ||
+      !aligned(dv, 16) || !aligned(dg, 16) || !aligned(dbeta, 4))
+    return ATTN_EINVAL;
+  const attn::DeltaLayout w = attn::delta_layout(total_tokens, num_seqs, num_heads, true,
+                                                 attn::kda_record_floats());
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < w.total) return ATTN_EWORKSPACE;
+  s = check_device();
+  if (s != ATTN_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (timed_launch(K_KDA_BWD, st, [&] {
+        return attn::launch_kda_bwd(q, k, v, g, beta, dout, cu_seqlens, num_seqs, total_tokens,
+                                    num_heads, scale, dq, dk, dv, dg, dbeta, workspace, w, st);
       }) != hipSuccess)
     return ATTN_ELAUNCH;
   return ATTN_OK;

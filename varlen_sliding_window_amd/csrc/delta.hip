@@ -1,5 +1,5 @@
 // Gated delta-rule linear attention, chunked: Gated DeltaNet (scalar gate)
-// forward and backward, Kimi Delta Attention (per-channel gate) forward.
+// and Kimi Delta Attention (per-channel gate), forward and backward.
 //
 // The kernel benchmarks page (research.dws.rip/llm/kernels, section 03 "What
 // linear attention costs") times Gated DeltaNet as the competing local
@@ -1125,12 +1125,15 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
 
 struct KdaRecord {
   static constexpr size_t W = 0;
-  static constexpr size_t U0 = W + (size_t)DC * DD;
+  static constexpr size_t U0 = W + (size_t)DC * DD;    // U after a saving scan
   static constexpr size_t QH = U0 + (size_t)DC * DD;   // q_i o gamma_i
   static constexpr size_t KH = QH + (size_t)DC * DD;   // k_j o exp(G_C - G_j)
   static constexpr size_t P = KH + (size_t)DC * DD;
-  static constexpr size_t GC = P + (size_t)DC * DC;    // gamma_C, per channel
-  static constexpr size_t FLOATS = GC + DD;
+  static constexpr size_t TI = P + (size_t)DC * DC;    // T = (I + A)^-1 (backward only)
+  static constexpr size_t KK = TI + (size_t)DC * DC;   // decayed K K^T below the diagonal (backward only)
+  static constexpr size_t GC = KK + (size_t)DC * DC;   // gamma_C, per channel
+  static constexpr size_t SIDE = GC + DD;              // gamma_C o d(gamma_C) (backward)
+  static constexpr size_t FLOATS = SIDE + DD;
 };
 static_assert(KdaRecord::FLOATS == kda_record_floats(), "record layout");
 static_assert(KdaRecord::FLOATS % 4 == 0 && KdaRecord::GC % 4 == 0, "16-byte aligned fields");
@@ -1139,7 +1142,7 @@ __global__ __launch_bounds__(PREP_THREADS) void kda_prep_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
     int nseq, int T, int H, const int* __restrict__ header, const int* __restrict__ seg_off,
-    float* __restrict__ records) {
+    float* __restrict__ records, int keep_inverse) {
   constexpr int BP = DD + 8;
   __shared__ __attribute__((aligned(16))) bf16 Ks[DC * BP];
   __shared__ __attribute__((aligned(16))) bf16 Qs[DC * BP];
@@ -1223,6 +1226,7 @@ __global__ __launch_bounds__(PREP_THREADS) void kda_prep_kernel(
         const int i = i0 + x, j = j0 + y;
         As[i * (DC + 1) + j] = j < i ? Bs[i] * kk[x][y] : 0.f;
         rec[KdaRecord::P + i * DC + j] = j <= i ? qk[x][y] : 0.f;
+        if (keep_inverse) rec[KdaRecord::KK + i * DC + j] = j < i ? kk[x][y] : 0.f;
       }
   }
   // the chunk's total decay, q o gamma and k o exp(G_C - G)
@@ -1255,6 +1259,11 @@ __global__ __launch_bounds__(PREP_THREADS) void kda_prep_kernel(
     if (tid < i) As[i * (DC + 1) + tid] = acc;
     __syncthreads();
   }
+  if (keep_inverse)
+    for (int f = tid; f < DC * DC; f += PREP_THREADS) {
+      const int i = f / DC, j = f % DC;
+      rec[KdaRecord::TI + f] = j < i ? As[i * (DC + 1) + j] : (j == i ? 1.f : 0.f);
+    }
   // X = diag(beta) (K o Gamma) over the log decays (each thread its own entries)
   for (int f = tid; f < DC * DD; f += PREP_THREADS) {
     const int i = f / DD, d = f % DD;
@@ -1299,7 +1308,8 @@ __global__ __launch_bounds__(PREP_THREADS) void kda_prep_kernel(
 // U = U0 - W S^T, O = scale (Q_hat S^T + P U), S <- S Diag(gamma_C) + U^T K_hat.
 __global__ __launch_bounds__(SCAN_THREADS) void kda_scan_kernel(
     const int32_t* __restrict__ cu, int nseq, int T, int H, float scale,
-    const int* __restrict__ seg_off, const float* __restrict__ records, bf16* __restrict__ out) {
+    const int* __restrict__ seg_off, float* __restrict__ records, bf16* __restrict__ out,
+    float* __restrict__ states) {
   constexpr int SL = DD / SLICE;
   constexpr int OP = SLICE + 1;
   __shared__ float Ss[SLICE * LP];
@@ -1375,6 +1385,16 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_scan_kernel(
     if (tid < DD / 4) reinterpret_cast<float4*>(GCs)[tid] = gr;
     __syncthreads();
     if (ci + 1 < count) fetch(ci + 1);
+    const size_t unit = (size_t)(first + ci) * H + h;
+    if (states) {   // this slice's rows of the chunk's start state
+      float* st = states + unit * DD * DD + (size_t)cbase * DD;
+#pragma unroll
+      for (int r = 0; r < SLICE * DD / 4 / NT; ++r) {
+        const int e4 = tid + NT * r, row = e4 / (DD / 4), c4 = (e4 % (DD / 4)) * 4;
+        const float* src = Ss + row * LP + c4;
+        *reinterpret_cast<float4*>(st + row * DD + c4) = make_float4(src[0], src[1], src[2], src[3]);
+      }
+    }
 
     // U = U0 - W S^T and Q_hat S^T: thread (row i, CPT slice columns)
     constexpr int CPT = DC * SLICE / NT;
@@ -1396,10 +1416,15 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_scan_kernel(
         Us[i * OP + cc + x] = U0s[i * OP + cc + x] - ws[x];
         QSs[i * OP + cc + x] = qs[x];
       }
+      if (states) {
+        float* urec = records + unit * KdaRecord::FLOATS + KdaRecord::U0 + (size_t)i * DD + cbase + cc;
+#pragma unroll
+        for (int x = 0; x < CPT; ++x) urec[x] = U0s[i * OP + cc + x] - ws[x];
+      }
     }
     __syncthreads();
     // O = scale (Q_hat S^T + P U) for the chunk's rows inside the document
-    if (i < n) {
+    if (out && i < n) {
       float acc[CPT];
 #pragma unroll
       for (int x = 0; x < CPT; ++x) acc[x] = QSs[i * OP + cc + x];
@@ -1436,6 +1461,659 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_scan_kernel(
           const int d = l4 + 64 * y + e;
           Ss[c * LP + d] = GCs[d] * Ss[c * LP + d] + acc[4 * y + e];
         }
+    }
+  }
+}
+
+
+// Kimi Delta backward.  With dS_C the gradient of a chunk's end state,
+//   dU = scale P^T dO + K_hat dS_C^T,
+//   dS_0 = dS_C Diag(gamma_C) + scale dO^T Q_hat - dU^T W,
+// walked backwards per document like the forward's scan; then per chunk the
+// state products (dQ_hat = scale dO S_0, dW = -dU S_0, dK_hat = U dS_C,
+// d(gamma_C) = column sums of dS_C o S_0), the triangular solve's gradients
+// and, for the decayed pair products P and A, with M the pair gradient and
+//   R(M, Y)_id = sum_j M_ij Y_jd exp(G_id - G_jd),
+//   C(M, Z)_jd = sum_i M_ij Z_id exp(G_id - G_jd),
+// dq += R(dP, K), dk += C(dP, Q) + R(B, K) + C(B, K) (B = beta_i dA_ij), and
+// the log-decay gradient q o R(dP, K) - k o C(dP, Q) + k o R(B, K) - k o C(B, K)
+// plus the elementwise terms of Q_hat, K_hat, X and gamma_C, summed back
+// onto g per channel inside the chunk.  Every exponential is of G_i - G_j
+// with i >= j, so at most 1.
+__global__ __launch_bounds__(SCAN_THREADS) void kda_rscan_kernel(
+    const bf16* __restrict__ dout, const int32_t* __restrict__ cu, int nseq, int T, int H,
+    float scale, int chunk_cap, const int* __restrict__ header, const int* __restrict__ seg_off,
+    const float* __restrict__ records, float* __restrict__ dstates, float* __restrict__ dubuf) {
+  constexpr int SL = DD / SLICE;
+  constexpr int OP = SLICE + 1;
+  __shared__ float dSs[SLICE * LP];
+  __shared__ __attribute__((aligned(16))) float Ws[DC * DD];    // read a row at a time
+  __shared__ __attribute__((aligned(16))) float QHs[DC * DD];   // read a row at a time
+  __shared__ float KHs[DC * LP];
+  __shared__ float Ps[DC * (DC + 1)];
+  __shared__ float dOs[DC * OP];
+  __shared__ float dUs[DC * OP];
+  __shared__ __attribute__((aligned(16))) float GCs[DD];
+  const int sl = blockIdx.x % SL;
+  const int h = (blockIdx.x / SL) % H;
+  const int s = blockIdx.x / (SL * H);
+  if (s >= nseq || !delta_saved_for(header, T, H, chunk_cap)) return;
+  const int a = min(max(cu[s], 0), T);
+  const int b = min(max(cu[s + 1], a), T);
+  const int total = seg_off[nseq];
+  const int first = min(seg_off[s], total);
+  const int count = max(0, min(seg_off[s + 1], total) - first);
+  const int tid = threadIdx.x;
+  const int cbase = sl * SLICE;
+  const size_t rs = (size_t)H * DD;
+  for (int e = tid; e < SLICE * LP; e += SCAN_THREADS) dSs[e] = 0.f;
+
+  constexpr int NT = SCAN_THREADS;
+  constexpr int WR = DC * DD / 4 / NT, PR = DC * DC / 4 / NT;
+  constexpr int OR = DC * SLICE / 8;
+  float4 wr[WR], qr[WR], kr[WR], pr[PR];
+  float4 gr = make_float4(0.f, 0.f, 0.f, 0.f);
+  uint4 dor = make_uint4(0, 0, 0, 0);
+  auto fetch = [&](int ci) {
+    const int c0 = a + ci * DC;
+    const int n = min(DC, b - c0);
+    const float4* r4 = reinterpret_cast<const float4*>(
+        records + ((size_t)(first + ci) * H + h) * KdaRecord::FLOATS);
+#pragma unroll
+    for (int r = 0; r < WR; ++r) {
+      wr[r] = r4[KdaRecord::W / 4 + tid + NT * r];
+      qr[r] = r4[KdaRecord::QH / 4 + tid + NT * r];
+      kr[r] = r4[KdaRecord::KH / 4 + tid + NT * r];
+    }
+#pragma unroll
+    for (int r = 0; r < PR; ++r) pr[r] = r4[KdaRecord::P / 4 + tid + NT * r];
+    if (tid < OR) {
+      const int i = tid / (SLICE / 8), ch = tid % (SLICE / 8);
+      const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + cbase + ch * 8;
+      dor = i < n ? *reinterpret_cast<const uint4*>(dout + off) : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < DD / 4) gr = r4[KdaRecord::GC / 4 + tid];
+  };
+  if (count > 0) fetch(count - 1);
+
+  for (int ci = count - 1; ci >= 0; --ci) {
+    const int n = min(DC, b - (a + ci * DC));
+    __syncthreads();   // every read of the previous chunk's LDS data is done
+#pragma unroll
+    for (int r = 0; r < WR; ++r) {
+      const int f = tid + NT * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
+      reinterpret_cast<float4*>(Ws)[f] = wr[r];
+      reinterpret_cast<float4*>(QHs)[f] = qr[r];
+      KHs[i * LP + c4] = kr[r].x; KHs[i * LP + c4 + 1] = kr[r].y;
+      KHs[i * LP + c4 + 2] = kr[r].z; KHs[i * LP + c4 + 3] = kr[r].w;
+    }
+#pragma unroll
+    for (int r = 0; r < PR; ++r) {
+      const int f = tid + NT * r, pi = f / (DC / 4), pj = (f % (DC / 4)) * 4;
+      Ps[pi * (DC + 1) + pj] = pr[r].x;
+      Ps[pi * (DC + 1) + pj + 1] = pr[r].y;
+      Ps[pi * (DC + 1) + pj + 2] = pr[r].z;
+      Ps[pi * (DC + 1) + pj + 3] = pr[r].w;
+    }
+    if (tid < OR) {
+      const int i = tid / (SLICE / 8), ch = tid % (SLICE / 8);
+      bf16x8 ov;
+      __builtin_memcpy(&ov, &dor, sizeof(ov));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dOs[i * OP + ch * 8 + e] = (float)ov[e];
+    }
+    if (tid < DD / 4) reinterpret_cast<float4*>(GCs)[tid] = gr;
+    __syncthreads();
+    if (ci > 0) fetch(ci - 1);
+    const size_t unit = (size_t)(first + ci) * H + h;
+    {   // the end-state gradient of this chunk, this slice's rows
+      float* st = dstates + unit * DD * DD + (size_t)cbase * DD;
+#pragma unroll
+      for (int r = 0; r < SLICE * DD / 4 / NT; ++r) {
+        const int e4 = tid + NT * r, row = e4 / (DD / 4), c4 = (e4 % (DD / 4)) * 4;
+        const float* src = dSs + row * LP + c4;
+        *reinterpret_cast<float4*>(st + row * DD + c4) = make_float4(src[0], src[1], src[2], src[3]);
+      }
+    }
+    // dU = scale P^T dO + K_hat dS^T: thread (row j, CPT columns)
+    constexpr int CPT = DC * SLICE / NT;
+    {
+      const int j = tid / (SLICE / CPT), cc = (tid % (SLICE / CPT)) * CPT;
+      float kd[CPT] = {}, pd[CPT] = {};
+      for (int d = 0; d < DD; ++d) {
+        const float kv = KHs[j * LP + d];
+#pragma unroll
+        for (int x = 0; x < CPT; ++x) kd[x] += kv * dSs[(cc + x) * LP + d];
+      }
+      for (int i = j; i < n; ++i) {
+        const float p = Ps[i * (DC + 1) + j];
+#pragma unroll
+        for (int x = 0; x < CPT; ++x) pd[x] += p * dOs[i * OP + cc + x];
+      }
+      float* du = dubuf + unit * DC * DD + (size_t)j * DD + cbase + cc;
+#pragma unroll
+      for (int x = 0; x < CPT; ++x) {
+        const float val = kd[x] + scale * pd[x];
+        dUs[j * OP + cc + x] = val;
+        du[x] = val;
+      }
+    }
+    __syncthreads();
+    // dS_0 = dS Diag(gamma_C) + sum_i (scale dO_i q_hat_i^T - dU_i w_i^T)
+    {
+      static_assert(SLICE * DD / NT == 8 && DD == 128, "8 columns per thread");
+      const int c = tid / 16, l4 = (tid % 16) * 4;
+      float acc[8] = {};
+      for (int i = 0; i < n; ++i) {
+        const float a1 = scale * dOs[i * OP + c];
+        const float a2 = dUs[i * OP + c];
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+          const float4 w = *reinterpret_cast<const float4*>(Ws + i * DD + l4 + 64 * y);
+          const float4 qh = *reinterpret_cast<const float4*>(QHs + i * DD + l4 + 64 * y);
+          acc[4 * y] += a1 * qh.x - a2 * w.x;
+          acc[4 * y + 1] += a1 * qh.y - a2 * w.y;
+          acc[4 * y + 2] += a1 * qh.z - a2 * w.z;
+          acc[4 * y + 3] += a1 * qh.w - a2 * w.w;
+        }
+      }
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int d = l4 + 64 * y + e;
+          dSs[c * LP + d] = GCs[d] * dSs[c * LP + d] + acc[4 * y + e];
+        }
+    }
+  }
+}
+
+// State products per (chunk, head): dQ_hat = scale dO S_0 and dK_hat = U dS_C
+// over this unit's dS_C once read, dW = -dU S_0 to its buffer, and
+// gamma_C o (column sums of dS_C o S_0) into the record's side values.
+__global__ __launch_bounds__(GRAD_THREADS) void kda_gstate_kernel(
+    const bf16* __restrict__ dout, const int32_t* __restrict__ cu, int nseq, int T, int H,
+    float scale, int chunk_cap, const int* __restrict__ header, const int* __restrict__ seg_off,
+    float* __restrict__ records, const float* __restrict__ states, float* __restrict__ dstates,
+    const float* __restrict__ dubuf, float* __restrict__ dwbuf) {
+  constexpr int BP = DD + 8;
+  constexpr int RB = 16;
+  static_assert(RB * DD / 4 == GRAD_THREADS, "one float4 of each state per thread and step");
+  __shared__ __attribute__((aligned(16))) bf16 dOs[DC * BP];
+  __shared__ float Us[DC * LP];
+  __shared__ float dUs[DC * LP];
+  __shared__ __attribute__((aligned(16))) float S0b[RB * DD];
+  __shared__ __attribute__((aligned(16))) float dSb[RB * DD];
+  __shared__ float dgc[DD];
+  const int chunk = blockIdx.x / H, h = blockIdx.x - chunk * H;
+  if (chunk >= header[0] || !delta_saved_for(header, T, H, chunk_cap)) return;
+  int c0, n;
+  delta_chunk_span(cu, seg_off, nseq, T, chunk, c0, n);
+  const int tid = threadIdx.x;
+  const size_t rs = (size_t)H * DD;
+  const size_t unit = blockIdx.x;
+  float* rec = records + unit * KdaRecord::FLOATS;
+  const float* S0 = states + unit * DD * DD;
+  float* dS = dstates + unit * DD * DD;
+  const float* dU = dubuf + unit * DC * DD;
+#pragma unroll
+  for (int r = 0; r < DC * DD / 8 / GRAD_THREADS; ++r) {
+    const int f = tid + GRAD_THREADS * r, i = f / (DD / 8), ch = f % (DD / 8);
+    const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + ch * 8;
+    *reinterpret_cast<uint4*>(dOs + i * BP + ch * 8) =
+        i < n ? *reinterpret_cast<const uint4*>(dout + off) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < DC * DD / 4 / GRAD_THREADS; ++r) {
+    const int f = tid + GRAD_THREADS * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
+    const float4 u = reinterpret_cast<const float4*>(rec + KdaRecord::U0)[f];
+    const float4 du = reinterpret_cast<const float4*>(dU)[f];
+    Us[i * LP + c4] = u.x; Us[i * LP + c4 + 1] = u.y; Us[i * LP + c4 + 2] = u.z; Us[i * LP + c4 + 3] = u.w;
+    dUs[i * LP + c4] = du.x; dUs[i * LP + c4 + 1] = du.y; dUs[i * LP + c4 + 2] = du.z; dUs[i * LP + c4 + 3] = du.w;
+  }
+  if (tid < DD) dgc[tid] = 0.f;
+  const int i0 = (tid / 16) * GR, d8 = (tid % 16) * 8;
+  const int sc4 = (tid % (DD / 4)) * 4;   // the state columns this thread stages
+  float aq[GR][8] = {}, aw[GR][8] = {}, ak[GR][8] = {};
+  float cs[4] = {};
+  for (int cb = 0; cb < DD; cb += RB) {
+    __syncthreads();
+    {
+      const float4 s4 = reinterpret_cast<const float4*>(S0 + (size_t)cb * DD)[tid];
+      const float4 d4 = reinterpret_cast<const float4*>(dS + (size_t)cb * DD)[tid];
+      reinterpret_cast<float4*>(S0b)[tid] = s4;
+      reinterpret_cast<float4*>(dSb)[tid] = d4;
+      cs[0] += s4.x * d4.x; cs[1] += s4.y * d4.y; cs[2] += s4.z * d4.z; cs[3] += s4.w * d4.w;
+    }
+    __syncthreads();
+    for (int c = 0; c < RB; ++c) {
+      const float4 sa = *reinterpret_cast<const float4*>(S0b + c * DD + d8);
+      const float4 sb = *reinterpret_cast<const float4*>(S0b + c * DD + d8 + 4);
+      const float4 ta = *reinterpret_cast<const float4*>(dSb + c * DD + d8);
+      const float4 tb = *reinterpret_cast<const float4*>(dSb + c * DD + d8 + 4);
+      const float s0[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+      const float ds[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
+#pragma unroll
+      for (int x = 0; x < GR; ++x) {
+        const float o = (float)dOs[(i0 + x) * BP + cb + c];
+        const float du = dUs[(i0 + x) * LP + cb + c];
+        const float u = Us[(i0 + x) * LP + cb + c];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          aq[x][e] += o * s0[e];
+          aw[x][e] += du * s0[e];
+          ak[x][e] += u * ds[e];
+        }
+      }
+    }
+  }
+  __syncthreads();   // every read of this unit's dS_C is done before it is overwritten
+#pragma unroll
+  for (int e = 0; e < 4; ++e) atomicAdd(&dgc[sc4 + e], cs[e]);
+#pragma unroll
+  for (int x = 0; x < GR; ++x) {
+    const int i = i0 + x;
+    float4* pq = reinterpret_cast<float4*>(dS + (size_t)i * DD + d8);
+    float4* pk = reinterpret_cast<float4*>(dS + (size_t)DC * DD + (size_t)i * DD + d8);
+    float4* pw = reinterpret_cast<float4*>(dwbuf + unit * DC * DD + (size_t)i * DD + d8);
+    pq[0] = make_float4(scale * aq[x][0], scale * aq[x][1], scale * aq[x][2], scale * aq[x][3]);
+    pq[1] = make_float4(scale * aq[x][4], scale * aq[x][5], scale * aq[x][6], scale * aq[x][7]);
+    pk[0] = make_float4(ak[x][0], ak[x][1], ak[x][2], ak[x][3]);
+    pk[1] = make_float4(ak[x][4], ak[x][5], ak[x][6], ak[x][7]);
+    pw[0] = make_float4(-aw[x][0], -aw[x][1], -aw[x][2], -aw[x][3]);
+    pw[1] = make_float4(-aw[x][4], -aw[x][5], -aw[x][6], -aw[x][7]);
+  }
+  __syncthreads();
+  if (tid < DD) rec[KdaRecord::SIDE + tid] = rec[KdaRecord::GC + tid] * dgc[tid];
+}
+
+// The triangular solve's gradients per (chunk, head), in LDS: dX = T^T dW
+// (over dW's buffer once read), dY = T^T dU (dV = diag(beta) dY, written),
+// dA = -T^T (dW X^T + dU Y^T) T^T below the diagonal with X = diag(beta)
+// K_tilde, K_tilde = K o Gamma, the beta gradient (written), and the pair
+// gradients dPm = scale dO U^T (on and below the diagonal) and
+// B = diag(beta) dA into this unit's start-state area, whose S_0 is spent.
+__global__ __launch_bounds__(GRAD_THREADS) void kda_gmat_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, const bf16* __restrict__ dout,
+    const int32_t* __restrict__ cu, int nseq, int T, int H, float scale, int chunk_cap,
+    const int* __restrict__ header, const int* __restrict__ seg_off,
+    const float* __restrict__ records, float* __restrict__ states, const float* __restrict__ dubuf,
+    float* __restrict__ dwbuf, bf16* __restrict__ dv, float* __restrict__ dbeta) {
+  constexpr int BP = DD + 8, CP = DC + 1;
+  __shared__ float KT[DC * LP];                                    // K o Gamma
+  __shared__ __attribute__((aligned(16))) float Vr[DC * BP / 2];   // V (bf16), then a C x C matrix
+  __shared__ float F1[DC * LP];                                    // U, then dW
+  __shared__ __attribute__((aligned(16))) float F2[DC * LP];       // log decays, dO (bf16), then dU
+  __shared__ float M1[DC * CP], M2[DC * CP];
+  __shared__ float Bs[DC], dBs[DC];
+  static_assert(DC * CP <= DC * BP / 2, "a C x C matrix fits where V was");
+  const int chunk = blockIdx.x / H, h = blockIdx.x - chunk * H;
+  if (chunk >= header[0] || !delta_saved_for(header, T, H, chunk_cap)) return;
+  int c0, n;
+  delta_chunk_span(cu, seg_off, nseq, T, chunk, c0, n);
+  const int tid = threadIdx.x;
+  const size_t rs = (size_t)H * DD;
+  const size_t unit = blockIdx.x;
+  const float* rec = records + unit * KdaRecord::FLOATS;
+  float* side = states + unit * DD * DD;          // [dPm | B], after S_0 was read
+  bf16* Vb = reinterpret_cast<bf16*>(Vr);
+  bf16* dOb = reinterpret_cast<bf16*>(F2);
+  float* M3 = Vr;
+  // log decays into F2, cumulative per channel
+#pragma unroll
+  for (int r = 0; r < DC * DD / 4 / GRAD_THREADS; ++r) {
+    const int f = tid + GRAD_THREADS * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
+    const float4 gv = i < n ? *reinterpret_cast<const float4*>(g + (size_t)(c0 + i) * rs + (size_t)h * DD + c4)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    F2[i * LP + c4] = gv.x; F2[i * LP + c4 + 1] = gv.y; F2[i * LP + c4 + 2] = gv.z; F2[i * LP + c4 + 3] = gv.w;
+  }
+  if (tid < DC) {
+    Bs[tid] = tid < n ? beta[(size_t)(c0 + tid) * H + h] : 0.f;
+    dBs[tid] = 0.f;
+  }
+  __syncthreads();
+  if (tid < DD) {
+    float acc = 0.f;
+    for (int i = 0; i < DC; ++i) {
+      acc += F2[i * LP + tid];
+      F2[i * LP + tid] = acc;
+    }
+  }
+  __syncthreads();
+  // K o Gamma into KT
+  for (int f = tid; f < DC * DD; f += GRAD_THREADS) {
+    const int i = f / DD, d = f % DD;
+    const float kv = i < n ? (float)k[(size_t)(c0 + i) * rs + (size_t)h * DD + d] : 0.f;
+    KT[i * LP + d] = kv * __expf(F2[i * LP + d]);
+  }
+  __syncthreads();   // F2 is reused below
+#pragma unroll
+  for (int r = 0; r < DC * DD / 8 / GRAD_THREADS; ++r) {
+    const int f = tid + GRAD_THREADS * r, i = f / (DD / 8), ch = f % (DD / 8);
+    const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + ch * 8;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(Vb + i * BP + ch * 8) = i < n ? *reinterpret_cast<const uint4*>(v + off) : z;
+    *reinterpret_cast<uint4*>(dOb + i * BP + ch * 8) = i < n ? *reinterpret_cast<const uint4*>(dout + off) : z;
+  }
+#pragma unroll
+  for (int r = 0; r < DC * DD / 4 / GRAD_THREADS; ++r) {
+    const int f = tid + GRAD_THREADS * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
+    const float4 u = reinterpret_cast<const float4*>(rec + KdaRecord::U0)[f];
+    F1[i * LP + c4] = u.x; F1[i * LP + c4 + 1] = u.y; F1[i * LP + c4 + 2] = u.z; F1[i * LP + c4 + 3] = u.w;
+  }
+  __syncthreads();
+  const int r0 = (tid / 16) * GR, s0 = (tid % 16) * 4;   // C x C tile
+  const int i0 = r0, d8 = (tid % 16) * 8;               // C x D tile
+  // dPm = scale dO U^T on and below the diagonal, to global
+  {
+    float dp[GR][4] = {};
+#pragma unroll 4
+    for (int d = 0; d < DD; ++d) {
+      float o[GR], u[4];
+#pragma unroll
+      for (int x = 0; x < GR; ++x) o[x] = (float)dOb[(r0 + x) * BP + d];
+#pragma unroll
+      for (int y = 0; y < 4; ++y) u[y] = F1[(s0 + y) * LP + d];
+#pragma unroll
+      for (int x = 0; x < GR; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) dp[x][y] += o[x] * u[y];
+    }
+#pragma unroll
+    for (int x = 0; x < GR; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y)
+        side[(r0 + x) * DC + s0 + y] = s0 + y <= r0 + x ? scale * dp[x][y] : 0.f;
+  }
+  __syncthreads();   // U and dO are no longer read
+#pragma unroll
+  for (int r = 0; r < DC * DD / 4 / GRAD_THREADS; ++r) {
+    const int f = tid + GRAD_THREADS * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
+    const float4 w = reinterpret_cast<const float4*>(dwbuf + unit * DC * DD)[f];
+    const float4 du = reinterpret_cast<const float4*>(dubuf + unit * DC * DD)[f];
+    F1[i * LP + c4] = w.x; F1[i * LP + c4 + 1] = w.y; F1[i * LP + c4 + 2] = w.z; F1[i * LP + c4 + 3] = w.w;
+    F2[i * LP + c4] = du.x; F2[i * LP + c4 + 1] = du.y; F2[i * LP + c4 + 2] = du.z; F2[i * LP + c4 + 3] = du.w;
+  }
+  for (int f = tid; f < DC * DC; f += GRAD_THREADS) M1[(f / DC) * CP + f % DC] = rec[KdaRecord::TI + f];
+  __syncthreads();
+  // dX = T^T dW (to dW's buffer), dY = T^T dU; dV = diag(beta) dY; beta
+  // gradient through X and Y
+  {
+    float dx[GR][8] = {}, dy[GR][8] = {};
+#pragma unroll 2
+    for (int j = i0; j < DC; ++j) {
+      float w[8], u[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        w[e] = F1[j * LP + d8 + e];
+        u[e] = F2[j * LP + d8 + e];
+      }
+#pragma unroll
+      for (int x = 0; x < GR; ++x) {
+        const float t = M1[j * CP + i0 + x];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          dx[x][e] += t * w[e];
+          dy[x][e] += t * u[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < GR; ++x) {
+      const int i = i0 + x;
+      const bf16x8 vv = *reinterpret_cast<const bf16x8*>(Vb + i * BP + d8);
+      float part = 0.f;
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float kt = KT[i * LP + d8 + e];
+        part += dx[x][e] * kt + (float)vv[e] * dy[x][e];
+        o[e] = (bf16)(Bs[i] * dy[x][e]);
+      }
+      if (i < n) *reinterpret_cast<bf16x8*>(dv + (size_t)(c0 + i) * rs + (size_t)h * DD + d8) = o;
+      float4* px = reinterpret_cast<float4*>(dwbuf + unit * DC * DD + (size_t)i * DD + d8);
+      px[0] = make_float4(dx[x][0], dx[x][1], dx[x][2], dx[x][3]);
+      px[1] = make_float4(dx[x][4], dx[x][5], dx[x][6], dx[x][7]);
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) part += __shfl_xor(part, off);
+      if ((tid & 15) == 0) atomicAdd(&dBs[i], part);
+    }
+  }
+  // dT = dW X^T + dU Y^T = (dW K_tilde^T + dU V^T) diag(beta) into M2
+  {
+    float t[GR][4] = {};
+#pragma unroll 4
+    for (int d = 0; d < DD; ++d) {
+      float w[GR], u[GR], kx[4], vx[4];
+#pragma unroll
+      for (int x = 0; x < GR; ++x) {
+        w[x] = F1[(r0 + x) * LP + d];
+        u[x] = F2[(r0 + x) * LP + d];
+      }
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        kx[y] = KT[(s0 + y) * LP + d];
+        vx[y] = (float)Vb[(s0 + y) * BP + d];
+      }
+#pragma unroll
+      for (int x = 0; x < GR; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) t[x][y] += w[x] * kx[y] + u[x] * vx[y];
+    }
+#pragma unroll
+    for (int x = 0; x < GR; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) M2[(r0 + x) * CP + s0 + y] = Bs[s0 + y] * t[x][y];
+  }
+  __syncthreads();   // V is no longer read: its space holds dT T^T next
+  {
+    float m[GR][4] = {};
+#pragma unroll 4
+    for (int c = 0; c < DC; ++c) {
+      float a_[GR], t_[4];
+#pragma unroll
+      for (int x = 0; x < GR; ++x) a_[x] = M2[(r0 + x) * CP + c];
+#pragma unroll
+      for (int y = 0; y < 4; ++y) t_[y] = M1[(s0 + y) * CP + c];
+#pragma unroll
+      for (int x = 0; x < GR; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) m[x][y] += a_[x] * t_[y];
+    }
+#pragma unroll
+    for (int x = 0; x < GR; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) M3[(r0 + x) * CP + s0 + y] = m[x][y];
+  }
+  __syncthreads();
+  // dA = -(T^T (dT T^T)) below the diagonal: B = diag(beta) dA to global, and
+  // the beta gradient through A = diag(beta) KK
+  {
+    float da[GR][4] = {};
+#pragma unroll 4
+    for (int c = 0; c < DC; ++c) {
+      float t_[GR], m_[4];
+#pragma unroll
+      for (int x = 0; x < GR; ++x) t_[x] = M1[c * CP + r0 + x];
+#pragma unroll
+      for (int y = 0; y < 4; ++y) m_[y] = M3[c * CP + s0 + y];
+#pragma unroll
+      for (int x = 0; x < GR; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) da[x][y] -= t_[x] * m_[y];
+    }
+#pragma unroll
+    for (int x = 0; x < GR; ++x) {
+      const int i = r0 + x;
+      float db = 0.f;
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        const int j = s0 + y;
+        const float dav = j < i ? da[x][y] : 0.f;
+        db += dav * rec[KdaRecord::KK + i * DC + j];
+        side[DC * DC + i * DC + j] = Bs[i] * dav;
+      }
+      atomicAdd(&dBs[i], db);
+    }
+  }
+  __syncthreads();
+  if (tid < n) dbeta[(size_t)(c0 + tid) * H + h] = dBs[tid];
+}
+
+// The decayed pair products per (chunk, head) and the final dq, dk, dg:
+// R(dPm, K) and R(B, K) over j <= i, C(dPm, Q) and C(B, K) over i >= j,
+// each exp(G_i - G_j) formed exactly; the elementwise terms (dq gets
+// dQ_hat o Gamma, dk gets beta dX o Gamma + dK_hat o E, the log-decay
+// gradient dX o X + dQ_hat o Q_hat - dK_hat o K_hat with E = exp(G_C - G),
+// K_hat = k o E, and on the last row the column sums of dK_hat o K_hat and
+// gamma_C d(gamma_C)); then the reverse cumulative sum of the log-decay
+// gradient per channel inside the chunk.
+__global__ __launch_bounds__(GRAD_THREADS) void kda_gpair_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
+    const float* __restrict__ beta, const int32_t* __restrict__ cu, int nseq, int T, int H,
+    int chunk_cap, const int* __restrict__ header, const int* __restrict__ seg_off,
+    const float* __restrict__ records, const float* __restrict__ states,
+    const float* __restrict__ dstates, const float* __restrict__ dwbuf, bf16* __restrict__ dq,
+    bf16* __restrict__ dk, float* __restrict__ dg) {
+  constexpr int BP = DD + 8, CP = DC + 1;
+  __shared__ __attribute__((aligned(16))) bf16 Qb[DC * BP];
+  __shared__ __attribute__((aligned(16))) bf16 Kb[DC * BP];
+  __shared__ __attribute__((aligned(16))) float Gl[DC * DD];   // cumulative log decays, then dG
+  __shared__ float Mp[DC * CP], Mb[DC * CP];
+  __shared__ float ksum[DD];
+  const int chunk = blockIdx.x / H, h = blockIdx.x - chunk * H;
+  if (chunk >= header[0] || !delta_saved_for(header, T, H, chunk_cap)) return;
+  int c0, n;
+  delta_chunk_span(cu, seg_off, nseq, T, chunk, c0, n);
+  const int tid = threadIdx.x;
+  const size_t rs = (size_t)H * DD;
+  const size_t unit = blockIdx.x;
+  const float* rec = records + unit * KdaRecord::FLOATS;
+  const float* side = states + unit * DD * DD;   // [dPm | B]
+  const float* gst = dstates + unit * DD * DD;   // dQ_hat, dK_hat
+  const float* dxb = dwbuf + unit * DC * DD;     // dX
+#pragma unroll
+  for (int r = 0; r < DC * DD / 8 / GRAD_THREADS; ++r) {
+    const int f = tid + GRAD_THREADS * r, i = f / (DD / 8), ch = f % (DD / 8);
+    const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + ch * 8;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(Qb + i * BP + ch * 8) = i < n ? *reinterpret_cast<const uint4*>(q + off) : z;
+    *reinterpret_cast<uint4*>(Kb + i * BP + ch * 8) = i < n ? *reinterpret_cast<const uint4*>(k + off) : z;
+  }
+#pragma unroll
+  for (int r = 0; r < DC * DD / 4 / GRAD_THREADS; ++r) {
+    const int f = tid + GRAD_THREADS * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
+    reinterpret_cast<float4*>(Gl)[f] =
+        i < n ? *reinterpret_cast<const float4*>(g + (size_t)(c0 + i) * rs + (size_t)h * DD + c4)
+              : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  for (int f = tid; f < DC * DC; f += GRAD_THREADS) {
+    Mp[(f / DC) * CP + f % DC] = side[f];
+    Mb[(f / DC) * CP + f % DC] = side[DC * DC + f];
+  }
+  __syncthreads();
+  if (tid < DD) {
+    float acc = 0.f;
+    for (int i = 0; i < DC; ++i) {
+      acc += Gl[i * DD + tid];
+      Gl[i * DD + tid] = acc;
+    }
+    ksum[tid] = 0.f;
+  }
+  __syncthreads();
+  const int i0 = (tid / 16) * GR, d8 = (tid % 16) * 8;
+  const int last = max(n - 1, 0);
+  float gi[GR][8];
+#pragma unroll
+  for (int x = 0; x < GR; ++x)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gi[x][e] = Gl[(i0 + x) * DD + d8 + e];
+  float rp[GR][8] = {}, rb[GR][8] = {}, cp[GR][8] = {}, cb[GR][8] = {};
+  // rows i = i0 + x: sum over j <= i
+  for (int j = 0; j < i0 + GR; ++j) {
+    const float4 ga = *reinterpret_cast<const float4*>(Gl + j * DD + d8);
+    const float4 gb = *reinterpret_cast<const float4*>(Gl + j * DD + d8 + 4);
+    const float gj[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+    const bf16x8 kj = *reinterpret_cast<const bf16x8*>(Kb + j * BP + d8);
+#pragma unroll
+    for (int x = 0; x < GR; ++x) {
+      if (j > i0 + x) continue;
+      const float mp = Mp[(i0 + x) * CP + j], mb = Mb[(i0 + x) * CP + j];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float t = (float)kj[e] * __expf(gi[x][e] - gj[e]);
+        rp[x][e] += mp * t;
+        rb[x][e] += mb * t;
+      }
+    }
+  }
+  // rows j = i0 + x as the column side: sum over i >= j
+  for (int i = i0; i < DC; ++i) {
+    const float4 ga = *reinterpret_cast<const float4*>(Gl + i * DD + d8);
+    const float4 gb = *reinterpret_cast<const float4*>(Gl + i * DD + d8 + 4);
+    const float gI[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+    const bf16x8 qI = *reinterpret_cast<const bf16x8*>(Qb + i * BP + d8);
+    const bf16x8 kI = *reinterpret_cast<const bf16x8*>(Kb + i * BP + d8);
+#pragma unroll
+    for (int x = 0; x < GR; ++x) {
+      if (i < i0 + x) continue;
+      const float mp = Mp[i * CP + i0 + x], mb = Mb[i * CP + i0 + x];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float ex = __expf(gI[e] - gi[x][e]);
+        cp[x][e] += mp * (float)qI[e] * ex;
+        cb[x][e] += mb * (float)kI[e] * ex;
+      }
+    }
+  }
+  // finish dq, dk and the log-decay gradient (held in rp until written)
+#pragma unroll
+  for (int x = 0; x < GR; ++x) {
+    const int i = i0 + x;
+    const float bi = i < n ? beta[(size_t)(c0 + i) * H + h] : 0.f;
+    const bf16x8 qv = *reinterpret_cast<const bf16x8*>(Qb + i * BP + d8);
+    const bf16x8 kv = *reinterpret_cast<const bf16x8*>(Kb + i * BP + d8);
+    bf16x8 oq, ok;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = d8 + e;
+      const float gam = __expf(gi[x][e]);
+      const float en = i < n ? __expf(Gl[last * DD + d] - gi[x][e]) : 0.f;
+      const float dqh = gst[(size_t)i * DD + d];
+      const float dkh = gst[(size_t)DC * DD + (size_t)i * DD + d];
+      const float dxv = dxb[(size_t)i * DD + d];
+      const float qf = (float)qv[e], kf = (float)kv[e];
+      const float khat = kf * en;
+      oq[e] = (bf16)(dqh * gam + rp[x][e]);
+      ok[e] = (bf16)(bi * dxv * gam + dkh * en + cp[x][e] + rb[x][e] + cb[x][e]);
+      rp[x][e] = qf * rp[x][e] - kf * cp[x][e] + kf * (rb[x][e] - cb[x][e]) +
+                 bi * dxv * kf * gam + dqh * qf * gam - dkh * khat;
+      atomicAdd(&ksum[d], dkh * khat);
+    }
+    if (i < n) {
+      *reinterpret_cast<bf16x8*>(dq + (size_t)(c0 + i) * rs + (size_t)h * DD + d8) = oq;
+      *reinterpret_cast<bf16x8*>(dk + (size_t)(c0 + i) * rs + (size_t)h * DD + d8) = ok;
+    }
+  }
+  __syncthreads();   // every read of the log decays is done and the column sums are complete
+#pragma unroll
+  for (int x = 0; x < GR; ++x) {
+    const int i = i0 + x;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = d8 + e;
+      float dgv = rp[x][e];
+      if (i == last) dgv += ksum[d] + rec[KdaRecord::SIDE + d];
+      Gl[i * DD + d] = dgv;
+    }
+  }
+  __syncthreads();
+  if (tid < DD) {   // dg_t = sum over the chunk's rows i >= t of dG_i, channel tid
+    float run = 0.f;
+    for (int i = n - 1; i >= 0; --i) {
+      run += Gl[i * DD + tid];
+      dg[(size_t)(c0 + i) * rs + (size_t)h * DD + tid] = run;
     }
   }
 }
@@ -1481,11 +2159,54 @@ hipError_t launch_kda_fwd(const void* q, const void* k, const void* v, const flo
   hipLaunchKernelGGL(kda_prep_kernel, dim3((unsigned)(w.chunk_cap * (size_t)num_heads)),
                      dim3(PREP_THREADS), 0, stream, static_cast<const bf16*>(q),
                      static_cast<const bf16*>(k), static_cast<const bf16*>(v), g, beta,
-                     cu_seqlens, num_seqs, total_tokens, num_heads, header, seg_off, records);
+                     cu_seqlens, num_seqs, total_tokens, num_heads, header, seg_off, records, 0);
   hipLaunchKernelGGL(kda_scan_kernel,
                      dim3((unsigned)((size_t)num_seqs * num_heads * (DD / SLICE))),
                      dim3(SCAN_THREADS), 0, stream, cu_seqlens, num_seqs, total_tokens,
-                     num_heads, scale, seg_off, records, static_cast<bf16*>(out));
+                     num_heads, scale, seg_off, records, static_cast<bf16*>(out),
+                     static_cast<float*>(nullptr));
+  return hipGetLastError();
+}
+
+hipError_t launch_kda_bwd(const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, const void* dout, const int32_t* cu_seqlens,
+                          int num_seqs, int total_tokens, int num_heads, float scale, void* dq,
+                          void* dk, void* dv, float* dg, float* dbeta, void* workspace,
+                          const DeltaLayout& w, hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  int* header = reinterpret_cast<int*>(ws + w.header);
+  int* seg_off = reinterpret_cast<int*>(ws + w.seg_off);
+  float* records = reinterpret_cast<float*>(ws + w.records);
+  float* states = reinterpret_cast<float*>(ws + w.states);
+  float* dstates = reinterpret_cast<float*>(ws + w.dstates);
+  float* dubuf = reinterpret_cast<float*>(ws + w.dubuf);
+  float* dwbuf = reinterpret_cast<float*>(ws + w.dwbuf);
+  const bf16* qb = static_cast<const bf16*>(q);
+  const bf16* kb = static_cast<const bf16*>(k);
+  const bf16* vb = static_cast<const bf16*>(v);
+  const bf16* ob = static_cast<const bf16*>(dout);
+  const int cap = (int)w.chunk_cap;
+  const dim3 units((unsigned)(w.chunk_cap * (size_t)num_heads));
+  const dim3 scans((unsigned)((size_t)num_seqs * num_heads * (DD / SLICE)));
+  hipLaunchKernelGGL(delta_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, cu_seqlens,
+                     num_seqs, total_tokens, cap, num_heads, 1, header, seg_off);
+  hipLaunchKernelGGL(kda_prep_kernel, units, dim3(PREP_THREADS), 0, stream, qb, kb, vb, g, beta,
+                     cu_seqlens, num_seqs, total_tokens, num_heads, header, seg_off, records, 1);
+  hipLaunchKernelGGL(kda_scan_kernel, scans, dim3(SCAN_THREADS), 0, stream, cu_seqlens,
+                     num_seqs, total_tokens, num_heads, scale, seg_off, records,
+                     static_cast<bf16*>(nullptr), states);
+  hipLaunchKernelGGL(kda_rscan_kernel, scans, dim3(SCAN_THREADS), 0, stream, ob, cu_seqlens,
+                     num_seqs, total_tokens, num_heads, scale, cap, header, seg_off, records,
+                     dstates, dubuf);
+  hipLaunchKernelGGL(kda_gstate_kernel, units, dim3(GRAD_THREADS), 0, stream, ob, cu_seqlens,
+                     num_seqs, total_tokens, num_heads, scale, cap, header, seg_off, records,
+                     states, dstates, dubuf, dwbuf);
+  hipLaunchKernelGGL(kda_gmat_kernel, units, dim3(GRAD_THREADS), 0, stream, qb, kb, vb, g, beta,
+                     ob, cu_seqlens, num_seqs, total_tokens, num_heads, scale, cap, header,
+                     seg_off, records, states, dubuf, dwbuf, static_cast<bf16*>(dv), dbeta);
+  hipLaunchKernelGGL(kda_gpair_kernel, units, dim3(GRAD_THREADS), 0, stream, qb, kb, g, beta,
+                     cu_seqlens, num_seqs, total_tokens, num_heads, cap, header, seg_off, records,
+                     states, dstates, dwbuf, static_cast<bf16*>(dq), static_cast<bf16*>(dk), dg);
   return hipGetLastError();
 }
 

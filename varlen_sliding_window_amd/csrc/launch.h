@@ -57,10 +57,11 @@ struct DeltaLayout {
   size_t header, seg_off, records, states, dstates, dubuf, dwbuf, total;
   size_t chunk_cap, record_bytes;
 };
-// Kimi Delta record: W, U0, q (x) gamma, k (x) end decay [C][D]; P [C][C];
-// the chunk's total decay [D]
+// Kimi Delta record: W, U0, q (x) gamma, k (x) end decay [C][D]; P, T and the
+// decayed K K^T [C][C]; the chunk's total decay and a backward side value [D]
 constexpr size_t kda_record_floats() {
-  return (size_t)4 * DELTA_CHUNK * DELTA_DIM + (size_t)DELTA_CHUNK * DELTA_CHUNK + DELTA_DIM;
+  return (size_t)4 * DELTA_CHUNK * DELTA_DIM + (size_t)3 * DELTA_CHUNK * DELTA_CHUNK +
+         (size_t)2 * DELTA_DIM;
 }
 inline DeltaLayout delta_layout(int64_t total_tokens, int64_t num_seqs, int64_t num_heads,
                                 bool backward = false,
@@ -100,6 +101,15 @@ hipError_t launch_kda_fwd(const void* q, const void* k, const void* v, const flo
                           const float* beta, const int32_t* cu_seqlens, int num_seqs,
                           int total_tokens, int num_heads, float scale, void* out,
                           void* workspace, const DeltaLayout& w, hipStream_t stream);
+
+// Kimi Delta Attention backward: dq, dk, dv bf16 [T, H, D], dg fp32
+// [T, H, D], dbeta fp32 [T, H]; recomputes the forward's records and states
+// (workspace laid out with backward = true and kda_record_floats()).
+hipError_t launch_kda_bwd(const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, const void* dout, const int32_t* cu_seqlens,
+                          int num_seqs, int total_tokens, int num_heads, float scale, void* dq,
+                          void* dk, void* dv, float* dg, float* dbeta, void* workspace,
+                          const DeltaLayout& w, hipStream_t stream);
 
 // Gradients of sum(dout * out) for the gated delta rule: dq, dk, dv bf16
 // [T, H, D]; dg, dbeta fp32 [T, H].  Recomputes the forward's records and
