@@ -260,11 +260,13 @@ def delta_bench(args, device):
 
 
 def kda_bench(args, device):
-    """Kimi Delta Attention forward on the workload microbatch (one layer,
-    H = 8 heads of 128, the attention workload's documents); one JSON line."""
+    """Kimi Delta Attention layer step on the workload microbatch (one layer,
+    H = 8 heads of 128, the attention workload's documents): the forward,
+    saving its chunk records and states, then the backward reusing them;
+    also times the plain forward alone; one JSON line."""
     import torch
     import varlen_sliding_window_amd as attn
-    from synthetic import CONFIGS, make_cu_seqlens, make_kda_inputs
+    from synthetic import CONFIGS, make_cu_seqlens, make_delta_dout, make_kda_inputs
 
     cu, _ = make_cu_seqlens(CONFIGS["ctx4096_w512"], args.seed)
     heads, d = 8, 128
@@ -278,34 +280,44 @@ def kda_bench(args, device):
     g = torch.from_numpy(inp.g).to(device)
     beta = torch.from_numpy(inp.beta).to(device)
     cu_dev = torch.from_numpy(cu.astype(np.int32)).to(device)
-    ws = torch.empty(attn.kda_workspace_size(t, len(cu) - 1, heads, d), dtype=torch.uint8,
+    dout = dev_bf16(make_delta_dout(t, heads, d, args.seed + 1))
+    ws = torch.empty(attn.kda_bwd_workspace_size(t, len(cu) - 1, heads, d), dtype=torch.uint8,
                      device=device)
     out = torch.zeros_like(q)
 
-    def step():
+    def fwd():
         attn.kda_fwd(q, k, v, g, beta, cu_dev, d ** -0.5, out=out, workspace=ws)
+
+    def step():
+        attn.kda_fwd(q, k, v, g, beta, cu_dev, d ** -0.5, out=out, workspace=ws, save=True)
+        attn.kda_bwd(q, k, v, g, beta, dout, cu_dev, d ** -0.5, workspace=ws, reuse=True)
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = timed(step)
+    ms_fwd = timed(fwd)
     attn.profile_start()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     kern = attn.profile_stop()
     print(json.dumps({
-        "metric": "Kimi Delta Attention forward per 16,384-token microbatch, 8 heads of 128",
+        "metric": "Kimi Delta Attention layer step (forward + backward) per 16,384-token microbatch, 8 heads of 128",
         "value": ms, "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": False, "dtype": "bf16 in, fp32 arithmetic",
-        "data": "synthetic (seeded lognormal document packing; unit q, k; N(0,1) v; per-channel gates)",
+        "data": "synthetic (seeded lognormal document packing; unit q, k; N(0,1) v and dout; per-channel gates)",
         "vs_baseline": None,
         "config": {"workload": "kda_ctx4096", "total_tokens": t, "num_heads": heads,
                    "head_dim": d, "num_seqs": len(cu) - 1, "seed": args.seed},
+        "forward_ms": ms_fwd,
         "kernels": {kk: {"avg_ms": vv["avg_ms"]} for kk, vv in kern.items()},
     }))
 

@@ -314,7 +314,8 @@ attn_status attn_kda_fwd(const void* q, const void* k, const void* v, const floa
  *   workspace     >= attn_kda_bwd_workspace_size(T, num_seqs, H, D) bytes,
  *                 256-byte aligned: the forward's records (with T and the
  *                 decayed K K^T), each chunk's start state and end-state
- *                 gradient, dU and dW, about 378 KB per (64-token chunk, head)
+ *                 gradient, dU, dW and two pair-gradient matrices, about 410 KB per
+ *                 (64-token chunk, head)
  * Recomputes the forward's records and chunk states, then runs a reverse
  * per-document scan and three per-chunk gradient kernels (state products,
  * triangular solve, decayed pair products): seven kernels on `stream`,
@@ -322,6 +323,26 @@ attn_status attn_kda_fwd(const void* q, const void* k, const void* v, const floa
  */
 size_t attn_kda_bwd_workspace_size(int32_t total_tokens, int32_t num_seqs_cap,
                                    int32_t num_heads, int32_t head_dim);
+
+/*
+ * As the Gated DeltaNet _ex pair: attn_kda_fwd_ex(ATTN_DELTA_FWD_SAVE) keeps
+ * the records and chunk states in a workspace of
+ * attn_kda_bwd_workspace_size bytes, and attn_kda_bwd_ex(ATTN_DELTA_BWD_REUSE)
+ * takes them instead of recomputing, under the same contract and device
+ * check; the saved data stays intact, so a reusing backward may repeat.
+ */
+attn_status attn_kda_fwd_ex(const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                            int32_t total_tokens, int32_t num_heads, int32_t head_dim,
+                            float scale, uint32_t flags, void* out, void* workspace,
+                            size_t workspace_bytes, attn_stream_t stream);
+
+attn_status attn_kda_bwd_ex(const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, const void* dout, const int32_t* cu_seqlens,
+                            int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                            int32_t head_dim, float scale, uint32_t flags, void* dq, void* dk,
+                            void* dv, float* dg, float* dbeta, void* workspace,
+                            size_t workspace_bytes, attn_stream_t stream);
 
 attn_status attn_kda_bwd(const void* q, const void* k, const void* v, const float* g,
                          const float* beta, const void* dout, const int32_t* cu_seqlens,

@@ -212,5 +212,11 @@ def test_kda_bwd_rejects(lib):
     fwd = lib.attn_kda_workspace_size(16384, 64, 8, 128)
     bwd = lib.attn_kda_bwd_workspace_size(16384, 64, 8, 128)
     units = (16384 // 64 + 64) * 8
-    # one record layout for both; the backward adds two states, dU and dW per unit
-    assert bwd - fwd == units * (2 * 128 * 128 + 2 * 64 * 128) * 4
+    # one record layout for both; the backward adds two states, dU, dW and two
+    # C x C pair gradients per unit
+    assert bwd - fwd == units * (2 * 128 * 128 + 2 * 64 * 128 + 2 * 64 * 64) * 4
+    args = [FAKE] * 6 + [1, 64, 2, 128, 0.088, 1, FAKE, FAKE,
+                         lib.attn_kda_workspace_size(64, 1, 2, 128), None]
+    assert lib.attn_kda_fwd_ex(*args) == EWORKSPACE      # saving needs the backward's size
+    args[11] = 2
+    assert lib.attn_kda_fwd_ex(*args) == EINVAL          # unknown flag

@@ -113,3 +113,30 @@ def test_kda_bwd_equal_channels_match_the_scalar_gate_kernel():
         print(f"[parity] kda bwd equal channels vs delta_bwd {name}: max-rel {mr:.2e} fro-rel {fr:.2e}",
               flush=True)
         assert mr <= MAX_REL and fr <= FRO_REL, name
+
+
+def test_kda_bwd_reusing_a_saving_forward():
+    cu = np.array([0, 130, 131, 400], dtype=np.int32)
+    inp = make_kda_inputs(cu, 3, 128, seed=50)
+    q, k, v = (bits_to_torch(getattr(inp, n + "_bits")) for n in ("q", "k", "v"))
+    g = torch.from_numpy(inp.g).cuda()
+    beta = torch.from_numpy(inp.beta).cuda()
+    do = bits_to_torch(make_delta_dout(400, 3, 128, seed=51))
+    cu_d = torch.from_numpy(cu).cuda()
+    plain = attn.kda_fwd(q, k, v, g, beta, cu_d)
+    ref = attn.kda_bwd(q, k, v, g, beta, do, cu_d)
+    ws = torch.empty(attn.kda_bwd_workspace_size(400, 3, 3, 128), dtype=torch.uint8, device="cuda")
+    saved = attn.kda_fwd(q, k, v, g, beta, cu_d, workspace=ws, save=True)
+    assert torch.equal(saved, plain), "saving changes the forward's output"
+    for rep in range(2):   # a reusing backward leaves the saved data as it was
+        got = attn.kda_bwd(q, k, v, g, beta, do, cu_d, workspace=ws, reuse=True)
+        torch.cuda.synchronize()
+        for name, x, y in zip(NAMES, got, ref):
+            if name in ("dv",):
+                assert torch.equal(x, y), (rep, name)
+            else:   # LDS float atomics may add in another order
+                torch.testing.assert_close(x.float(), y.float(), rtol=1e-2, atol=1e-5)
+    attn.kda_fwd(q, k, v, g, beta, cu_d, workspace=ws)           # saves nothing
+    got = attn.kda_bwd(q, k, v, g, beta, do, cu_d, workspace=ws, reuse=True)
+    torch.cuda.synchronize()
+    assert all(torch.count_nonzero(x) == 0 for x in got), "ran on a workspace not saved for it"

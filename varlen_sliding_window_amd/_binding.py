@@ -85,6 +85,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_kda_bwd.argtypes = [vp] * 7 + [i32, i32, i32, i32, ctypes.c_float] + [vp] * 6 + [
         sz, vp]
     lib.attn_kda_bwd.restype = ctypes.c_int
+    lib.attn_kda_fwd_ex.argtypes = [vp] * 6 + [i32, i32, i32, i32, ctypes.c_float,
+                                               ctypes.c_uint32, vp, vp, sz, vp]
+    lib.attn_kda_fwd_ex.restype = ctypes.c_int
+    lib.attn_kda_bwd_ex.argtypes = [vp] * 7 + [i32, i32, i32, i32, ctypes.c_float,
+                                               ctypes.c_uint32] + [vp] * 6 + [sz, vp]
+    lib.attn_kda_bwd_ex.restype = ctypes.c_int
     lib.attn_delta_fwd_ex.argtypes = [vp] * 6 + [i32, i32, i32, i32, ctypes.c_float,
                                                  ctypes.c_uint32, vp, vp, sz, vp]
     lib.attn_delta_fwd_ex.restype = ctypes.c_int
@@ -277,10 +283,12 @@ def kda_workspace_size(total_tokens: int, num_seqs: int, num_heads: int, head_di
     return int(load_library().attn_kda_workspace_size(total_tokens, num_seqs, num_heads, head_dim))
 
 
-def kda_fwd(q, k, v, g, beta, cu_seqlens, scale: float | None = None, out=None, workspace=None):
-    """attn_kda_fwd: Kimi Delta Attention forward.  q, k, v bf16 [T, H, D];
-    g fp32 [T, H, D] (per-channel log decay); beta fp32 [T, H]; returns out
-    bf16 [T, H, D]."""
+def kda_fwd(q, k, v, g, beta, cu_seqlens, scale: float | None = None, out=None, workspace=None,
+            save: bool = False):
+    """attn_kda_fwd(_ex): Kimi Delta Attention forward.  q, k, v bf16
+    [T, H, D]; g fp32 [T, H, D] (per-channel log decay); beta fp32 [T, H];
+    returns out bf16 [T, H, D].  save=True keeps, in a workspace of
+    kda_bwd_workspace_size bytes, what kda_bwd(..., reuse=True) needs."""
     for name, t_ in (("q", q), ("k", k), ("v", v)):
         _check_tensor(name, t_, torch.bfloat16, 3)
     _check_tensor("g", g, torch.float32, 3)
@@ -295,22 +303,33 @@ def kda_fwd(q, k, v, g, beta, cu_seqlens, scale: float | None = None, out=None, 
     if out is None:
         out = torch.zeros_like(q)
     if workspace is None:
-        n = kda_workspace_size(t, nseq, h, d)
+        n = (kda_bwd_workspace_size if save else kda_workspace_size)(t, nseq, h, d)
         if n == 0:
             raise AttnError(-1, "attn_kda_workspace_size")
         workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
-    st = load_library().attn_kda_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                     _ptr(cu_seqlens), nseq, t, h, d, float(scale), _ptr(out),
-                                     _ptr(workspace), workspace.numel(), _stream_handle(q.device))
+    st = load_library().attn_kda_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                        _ptr(cu_seqlens), nseq, t, h, d, float(scale),
+                                        1 if save else 0, _ptr(out), _ptr(workspace),
+                                        workspace.numel(), _stream_handle(q.device))
     if st != ATTN_OK:
-        raise AttnError(st, "attn_kda_fwd")
+        raise AttnError(st, "attn_kda_fwd_ex")
     return out
 
 
-def kda_bwd(q, k, v, g, beta, dout, cu_seqlens, scale: float | None = None, workspace=None):
-    """attn_kda_bwd: gradients of sum(dout * out) of the Kimi Delta forward.
-    Returns dq, dk, dv (bf16 [T, H, D]), dg (fp32 [T, H, D]) and dbeta (fp32
-    [T, H]), zero-filled first."""
+def kda_bwd_workspace_size(total_tokens: int, num_seqs: int, num_heads: int,
+                           head_dim: int) -> int:
+    return int(load_library().attn_kda_bwd_workspace_size(total_tokens, num_seqs, num_heads,
+                                                           head_dim))
+
+
+def kda_bwd(q, k, v, g, beta, dout, cu_seqlens, scale: float | None = None, workspace=None,
+            reuse: bool = False):
+    """attn_kda_bwd(_ex): gradients of sum(dout * out) of the Kimi Delta
+    forward.  Returns dq, dk, dv (bf16 [T, H, D]), dg (fp32 [T, H, D]) and
+    dbeta (fp32 [T, H]), zero-filled first.  reuse=True takes the records and
+    states a kda_fwd(..., save=True) with the same inputs left in `workspace`."""
+    if reuse and workspace is None:
+        raise ValueError("reuse needs the workspace of a saving forward")
     for name, t_ in (("q", q), ("k", k), ("v", v), ("dout", dout)):
         _check_tensor(name, t_, torch.bfloat16, 3)
     _check_tensor("g", g, torch.float32, 3)
@@ -326,16 +345,17 @@ def kda_bwd(q, k, v, g, beta, dout, cu_seqlens, scale: float | None = None, work
     dq, dk, dv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
     dg, dbeta = torch.zeros_like(g), torch.zeros_like(beta)
     if workspace is None:
-        n = int(load_library().attn_kda_bwd_workspace_size(t, nseq, h, d))
+        n = kda_bwd_workspace_size(t, nseq, h, d)
         if n == 0:
             raise AttnError(-1, "attn_kda_bwd_workspace_size")
         workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
-    st = load_library().attn_kda_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(dout),
-                                     _ptr(cu_seqlens), nseq, t, h, d, float(scale), _ptr(dq),
-                                     _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(workspace),
-                                     workspace.numel(), _stream_handle(q.device))
+    st = load_library().attn_kda_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                        _ptr(dout), _ptr(cu_seqlens), nseq, t, h, d, float(scale),
+                                        1 if reuse else 0, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+                                        _ptr(dbeta), _ptr(workspace), workspace.numel(),
+                                        _stream_handle(q.device))
     if st != ATTN_OK:
-        raise AttnError(st, "attn_kda_bwd")
+        raise AttnError(st, "attn_kda_bwd_ex")
     return dq, dk, dv, dg, dbeta
 
 

@@ -348,42 +348,55 @@ size_t attn_kda_workspace_size(int32_t total_tokens, int32_t num_seqs_cap, int32
       .total;
 }
 
-attn_status attn_kda_fwd(const void* q, const void* k, const void* v, const float* g,
-                         const float* beta, const int32_t* cu_seqlens, int32_t num_seqs,
-                         int32_t total_tokens, int32_t num_heads, int32_t head_dim, float scale,
-                         void* out, void* workspace, size_t workspace_bytes,
-                         attn_stream_t stream) {
+attn_status attn_kda_fwd_ex(const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                            int32_t total_tokens, int32_t num_heads, int32_t head_dim,
+                            float scale, uint32_t flags, void* out, void* workspace,
+                            size_t workspace_bytes, attn_stream_t stream) {
+  if (flags & ~(uint32_t)ATTN_DELTA_FWD_SAVE) return ATTN_EINVAL;
+  const bool save = flags & ATTN_DELTA_FWD_SAVE;
   attn_status s = check_delta(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
                               head_dim, scale);
   if (s != ATTN_OK) return s;
   if (!out || !aligned(out, 16) || !aligned(g, 16)) return ATTN_EINVAL;
-  const attn::DeltaLayout w = attn::delta_layout(total_tokens, num_seqs, num_heads, false,
-                                                 attn::kda_record_floats());
+  const attn::DeltaLayout w = attn::delta_layout(total_tokens, num_seqs, num_heads, save,
+                                                 attn::kda_record_floats(), save);
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < w.total) return ATTN_EWORKSPACE;
   s = check_device();
   if (s != ATTN_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (timed_launch(K_KDA, st, [&] {
         return attn::launch_kda_fwd(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens,
-                                    num_heads, scale, out, workspace, w, st);
+                                    num_heads, scale, out, workspace, w, save, st);
       }) != hipSuccess)
     return ATTN_ELAUNCH;
   return ATTN_OK;
 }
 
+attn_status attn_kda_fwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                         int32_t total_tokens, int32_t num_heads, int32_t head_dim, float scale,
+                         void* out, void* workspace, size_t workspace_bytes,
+                         attn_stream_t stream) {
+  return attn_kda_fwd_ex(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
+                         head_dim, scale, 0u, out, workspace, workspace_bytes, stream);
+}
+
 size_t attn_kda_bwd_workspace_size(int32_t total_tokens, int32_t num_seqs_cap,
                                    int32_t num_heads, int32_t head_dim) {
   if (delta_workspace(total_tokens, num_seqs_cap, num_heads, head_dim, false) == 0) return 0;
-  return attn::delta_layout(total_tokens, num_seqs_cap, num_heads, true, attn::kda_record_floats())
+  return attn::delta_layout(total_tokens, num_seqs_cap, num_heads, true, attn::kda_record_floats(),
+                           true)
       .total;
 }
 
-attn_status attn_kda_bwd(const void* q, const void* k, const void* v, const float* g,
-                         const float* beta, const void* dout, const int32_t* cu_seqlens,
-                         int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
-                         int32_t head_dim, float scale, void* dq, void* dk, void* dv, float* dg,
-                         float* dbeta, void* workspace, size_t workspace_bytes,
-                         attn_stream_t stream) {
+attn_status attn_kda_bwd_ex(const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, const void* dout, const int32_t* cu_seqlens,
+                            int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                            int32_t head_dim, float scale, uint32_t flags, void* dq, void* dk,
+                            void* dv, float* dg, float* dbeta, void* workspace,
+                            size_t workspace_bytes, attn_stream_t stream) {
+  if (flags & ~(uint32_t)ATTN_DELTA_BWD_REUSE) return ATTN_EINVAL;
   attn_status s = check_delta(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
                               head_dim, scale);
   if (s != ATTN_OK) return s;
@@ -392,17 +405,29 @@ attn_status attn_kda_bwd(const void* q, const void* k, const void* v, const floa
       !aligned(dv, 16) || !aligned(dg, 16) || !aligned(dbeta, 4))
     return ATTN_EINVAL;
   const attn::DeltaLayout w = attn::delta_layout(total_tokens, num_seqs, num_heads, true,
-                                                 attn::kda_record_floats());
+                                                 attn::kda_record_floats(), true);
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < w.total) return ATTN_EWORKSPACE;
   s = check_device();
   if (s != ATTN_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (timed_launch(K_KDA_BWD, st, [&] {
         return attn::launch_kda_bwd(q, k, v, g, beta, dout, cu_seqlens, num_seqs, total_tokens,
-                                    num_heads, scale, dq, dk, dv, dg, dbeta, workspace, w, st);
+                                    num_heads, scale, dq, dk, dv, dg, dbeta, workspace, w,
+                                    flags & ATTN_DELTA_BWD_REUSE, st);
       }) != hipSuccess)
     return ATTN_ELAUNCH;
   return ATTN_OK;
+}
+
+attn_status attn_kda_bwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const void* dout, const int32_t* cu_seqlens,
+                         int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                         int32_t head_dim, float scale, void* dq, void* dk, void* dv, float* dg,
+                         float* dbeta, void* workspace, size_t workspace_bytes,
+                         attn_stream_t stream) {
+  return attn_kda_bwd_ex(q, k, v, g, beta, dout, cu_seqlens, num_seqs, total_tokens, num_heads,
+                         head_dim, scale, 0u, dq, dk, dv, dg, dbeta, workspace, workspace_bytes,
+                         stream);
 }
 
 attn_status attn_delta_bwd_ex(const void* q, const void* k, const void* v, const float* g,

@@ -1732,13 +1732,13 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gstate_kernel(
 // dA = -T^T (dW X^T + dU Y^T) T^T below the diagonal with X = diag(beta)
 // K_tilde, K_tilde = K o Gamma, the beta gradient (written), and the pair
 // gradients dPm = scale dO U^T (on and below the diagonal) and
-// B = diag(beta) dA into this unit's start-state area, whose S_0 is spent.
+// B = diag(beta) dA into the unit's pair area.
 __global__ __launch_bounds__(GRAD_THREADS) void kda_gmat_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const bf16* __restrict__ dout,
     const int32_t* __restrict__ cu, int nseq, int T, int H, float scale, int chunk_cap,
     const int* __restrict__ header, const int* __restrict__ seg_off,
-    const float* __restrict__ records, float* __restrict__ states, const float* __restrict__ dubuf,
+    const float* __restrict__ records, float* __restrict__ pairbuf, const float* __restrict__ dubuf,
     float* __restrict__ dwbuf, bf16* __restrict__ dv, float* __restrict__ dbeta) {
   constexpr int BP = DD + 8, CP = DC + 1;
   __shared__ float KT[DC * LP];                                    // K o Gamma
@@ -1756,7 +1756,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gmat_kernel(
   const size_t rs = (size_t)H * DD;
   const size_t unit = blockIdx.x;
   const float* rec = records + unit * KdaRecord::FLOATS;
-  float* side = states + unit * DD * DD;          // [dPm | B], after S_0 was read
+  float* side = pairbuf + unit * 2 * DC * DC;     // [dPm | B]
   bf16* Vb = reinterpret_cast<bf16*>(Vr);
   bf16* dOb = reinterpret_cast<bf16*>(F2);
   float* M3 = Vr;
@@ -1973,7 +1973,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gpair_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, const int32_t* __restrict__ cu, int nseq, int T, int H,
     int chunk_cap, const int* __restrict__ header, const int* __restrict__ seg_off,
-    const float* __restrict__ records, const float* __restrict__ states,
+    const float* __restrict__ records, const float* __restrict__ pairbuf,
     const float* __restrict__ dstates, const float* __restrict__ dwbuf, bf16* __restrict__ dq,
     bf16* __restrict__ dk, float* __restrict__ dg) {
   constexpr int BP = DD + 8, CP = DC + 1;
@@ -1990,7 +1990,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gpair_kernel(
   const size_t rs = (size_t)H * DD;
   const size_t unit = blockIdx.x;
   const float* rec = records + unit * KdaRecord::FLOATS;
-  const float* side = states + unit * DD * DD;   // [dPm | B]
+  const float* side = pairbuf + unit * 2 * DC * DC;   // [dPm | B]
   const float* gst = dstates + unit * DD * DD;   // dQ_hat, dK_hat
   const float* dxb = dwbuf + unit * DC * DD;     // dX
 #pragma unroll
@@ -2149,22 +2149,24 @@ hipError_t launch_delta_fwd(const void* q, const void* k, const void* v, const f
 hipError_t launch_kda_fwd(const void* q, const void* k, const void* v, const float* g,
                           const float* beta, const int32_t* cu_seqlens, int num_seqs,
                           int total_tokens, int num_heads, float scale, void* out,
-                          void* workspace, const DeltaLayout& w, hipStream_t stream) {
+                          void* workspace, const DeltaLayout& w, bool save, hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
   int* header = reinterpret_cast<int*>(ws + w.header);
   int* seg_off = reinterpret_cast<int*>(ws + w.seg_off);
   float* records = reinterpret_cast<float*>(ws + w.records);
   hipLaunchKernelGGL(delta_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, cu_seqlens,
-                     num_seqs, total_tokens, (int)w.chunk_cap, num_heads, 0, header, seg_off);
+                     num_seqs, total_tokens, (int)w.chunk_cap, num_heads, save ? 1 : 0, header,
+                     seg_off);
   hipLaunchKernelGGL(kda_prep_kernel, dim3((unsigned)(w.chunk_cap * (size_t)num_heads)),
                      dim3(PREP_THREADS), 0, stream, static_cast<const bf16*>(q),
                      static_cast<const bf16*>(k), static_cast<const bf16*>(v), g, beta,
-                     cu_seqlens, num_seqs, total_tokens, num_heads, header, seg_off, records, 0);
+                     cu_seqlens, num_seqs, total_tokens, num_heads, header, seg_off, records,
+                     save ? 1 : 0);
   hipLaunchKernelGGL(kda_scan_kernel,
                      dim3((unsigned)((size_t)num_seqs * num_heads * (DD / SLICE))),
                      dim3(SCAN_THREADS), 0, stream, cu_seqlens, num_seqs, total_tokens,
                      num_heads, scale, seg_off, records, static_cast<bf16*>(out),
-                     static_cast<float*>(nullptr));
+                     save ? reinterpret_cast<float*>(ws + w.states) : nullptr);
   return hipGetLastError();
 }
 
@@ -2172,7 +2174,12 @@ hipError_t launch_kda_bwd(const void* q, const void* k, const void* v, const flo
                           const float* beta, const void* dout, const int32_t* cu_seqlens,
                           int num_seqs, int total_tokens, int num_heads, float scale, void* dq,
                           void* dk, void* dv, float* dg, float* dbeta, void* workspace,
-                          const DeltaLayout& w, hipStream_t stream) {
+                          const DeltaLayout& w, bool reuse, hipStream_t stream) {
+  if (!reuse) {   // the forward's records and states, saved
+    const hipError_t e = launch_kda_fwd(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens,
+                                        num_heads, scale, nullptr, workspace, w, true, stream);
+    if (e != hipSuccess) return e;
+  }
   char* ws = static_cast<char*>(workspace);
   int* header = reinterpret_cast<int*>(ws + w.header);
   int* seg_off = reinterpret_cast<int*>(ws + w.seg_off);
@@ -2181,6 +2188,7 @@ hipError_t launch_kda_bwd(const void* q, const void* k, const void* v, const flo
   float* dstates = reinterpret_cast<float*>(ws + w.dstates);
   float* dubuf = reinterpret_cast<float*>(ws + w.dubuf);
   float* dwbuf = reinterpret_cast<float*>(ws + w.dwbuf);
+  float* pairbuf = reinterpret_cast<float*>(ws + w.pairbuf);
   const bf16* qb = static_cast<const bf16*>(q);
   const bf16* kb = static_cast<const bf16*>(k);
   const bf16* vb = static_cast<const bf16*>(v);
@@ -2188,13 +2196,6 @@ hipError_t launch_kda_bwd(const void* q, const void* k, const void* v, const flo
   const int cap = (int)w.chunk_cap;
   const dim3 units((unsigned)(w.chunk_cap * (size_t)num_heads));
   const dim3 scans((unsigned)((size_t)num_seqs * num_heads * (DD / SLICE)));
-  hipLaunchKernelGGL(delta_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, cu_seqlens,
-                     num_seqs, total_tokens, cap, num_heads, 1, header, seg_off);
-  hipLaunchKernelGGL(kda_prep_kernel, units, dim3(PREP_THREADS), 0, stream, qb, kb, vb, g, beta,
-                     cu_seqlens, num_seqs, total_tokens, num_heads, header, seg_off, records, 1);
-  hipLaunchKernelGGL(kda_scan_kernel, scans, dim3(SCAN_THREADS), 0, stream, cu_seqlens,
-                     num_seqs, total_tokens, num_heads, scale, seg_off, records,
-                     static_cast<bf16*>(nullptr), states);
   hipLaunchKernelGGL(kda_rscan_kernel, scans, dim3(SCAN_THREADS), 0, stream, ob, cu_seqlens,
                      num_seqs, total_tokens, num_heads, scale, cap, header, seg_off, records,
                      dstates, dubuf);
@@ -2203,10 +2204,10 @@ hipError_t launch_kda_bwd(const void* q, const void* k, const void* v, const flo
                      states, dstates, dubuf, dwbuf);
   hipLaunchKernelGGL(kda_gmat_kernel, units, dim3(GRAD_THREADS), 0, stream, qb, kb, vb, g, beta,
                      ob, cu_seqlens, num_seqs, total_tokens, num_heads, scale, cap, header,
-                     seg_off, records, states, dubuf, dwbuf, static_cast<bf16*>(dv), dbeta);
+                     seg_off, records, pairbuf, dubuf, dwbuf, static_cast<bf16*>(dv), dbeta);
   hipLaunchKernelGGL(kda_gpair_kernel, units, dim3(GRAD_THREADS), 0, stream, qb, kb, g, beta,
                      cu_seqlens, num_seqs, total_tokens, num_heads, cap, header, seg_off, records,
-                     states, dstates, dwbuf, static_cast<bf16*>(dq), static_cast<bf16*>(dk), dg);
+                     pairbuf, dstates, dwbuf, static_cast<bf16*>(dq), static_cast<bf16*>(dk), dg);
   return hipGetLastError();
 }
 

@@ -54,7 +54,7 @@ constexpr size_t delta_record_floats() {
          (size_t)6 * DELTA_CHUNK;
 }
 struct DeltaLayout {
-  size_t header, seg_off, records, states, dstates, dubuf, dwbuf, total;
+  size_t header, seg_off, records, states, dstates, dubuf, dwbuf, pairbuf, total;
   size_t chunk_cap, record_bytes;
 };
 // Kimi Delta record: W, U0, q (x) gamma, k (x) end decay [C][D]; P, T and the
@@ -63,9 +63,12 @@ constexpr size_t kda_record_floats() {
   return (size_t)4 * DELTA_CHUNK * DELTA_DIM + (size_t)3 * DELTA_CHUNK * DELTA_CHUNK +
          (size_t)2 * DELTA_DIM;
 }
+// pair_area: the backward also keeps two C x C pair-gradient matrices per
+// (chunk, head) (the per-channel gate's backward)
 inline DeltaLayout delta_layout(int64_t total_tokens, int64_t num_seqs, int64_t num_heads,
                                 bool backward = false,
-                                size_t record_floats = delta_record_floats()) {
+                                size_t record_floats = delta_record_floats(),
+                                bool pair_area = false) {
   DeltaLayout w;
   w.chunk_cap = (size_t)((total_tokens + DELTA_CHUNK - 1) / DELTA_CHUNK) + (size_t)num_seqs;
   w.record_bytes = record_floats * sizeof(float);
@@ -77,6 +80,7 @@ inline DeltaLayout delta_layout(int64_t total_tokens, int64_t num_seqs, int64_t 
   w.dstates = w.states;
   w.dubuf = w.states;
   w.dwbuf = w.states;
+  w.pairbuf = w.states;
   w.total = w.states;
   if (backward) {
     const size_t state_bytes = (size_t)DELTA_DIM * DELTA_DIM * sizeof(float);
@@ -84,7 +88,8 @@ inline DeltaLayout delta_layout(int64_t total_tokens, int64_t num_seqs, int64_t 
     w.dstates = w.states + units * state_bytes;
     w.dubuf = w.dstates + units * state_bytes;
     w.dwbuf = w.dubuf + units * chunk_bytes;
-    w.total = w.dwbuf + units * chunk_bytes;
+    w.pairbuf = w.dwbuf + units * chunk_bytes;
+    w.total = w.pairbuf + (pair_area ? units * (size_t)2 * DELTA_CHUNK * DELTA_CHUNK * sizeof(float) : 0);
   }
   return w;
 }
@@ -100,16 +105,17 @@ hipError_t launch_delta_fwd(const void* q, const void* k, const void* v, const f
 hipError_t launch_kda_fwd(const void* q, const void* k, const void* v, const float* g,
                           const float* beta, const int32_t* cu_seqlens, int num_seqs,
                           int total_tokens, int num_heads, float scale, void* out,
-                          void* workspace, const DeltaLayout& w, hipStream_t stream);
+                          void* workspace, const DeltaLayout& w, bool save, hipStream_t stream);
 
 // Kimi Delta Attention backward: dq, dk, dv bf16 [T, H, D], dg fp32
 // [T, H, D], dbeta fp32 [T, H]; recomputes the forward's records and states
-// (workspace laid out with backward = true and kda_record_floats()).
+// (workspace laid out with backward = true, kda_record_floats() and the pair
+// area), or with `reuse` takes those a saving forward left there.
 hipError_t launch_kda_bwd(const void* q, const void* k, const void* v, const float* g,
                           const float* beta, const void* dout, const int32_t* cu_seqlens,
                           int num_seqs, int total_tokens, int num_heads, float scale, void* dq,
                           void* dk, void* dv, float* dg, float* dbeta, void* workspace,
-                          const DeltaLayout& w, hipStream_t stream);
+                          const DeltaLayout& w, bool reuse, hipStream_t stream);
 
 // Gradients of sum(dout * out) for the gated delta rule: dq, dk, dv bf16
 // [T, H, D]; dg, dbeta fp32 [T, H].  Recomputes the forward's records and
