@@ -1144,12 +1144,16 @@ __global__ __launch_bounds__(PREP_THREADS) void kda_prep_kernel(
     int nseq, int T, int H, const int* __restrict__ header, const int* __restrict__ seg_off,
     float* __restrict__ records, int keep_inverse) {
   constexpr int BP = DD + 8;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[DC * BP];
-  __shared__ __attribute__((aligned(16))) bf16 Qs[DC * BP];
+  constexpr int GP = DC + 4;   // channel-major pitch, rows 16-byte aligned
+  __shared__ __attribute__((aligned(16))) bf16 KQs[2 * DC * BP];   // K and Q tiles, then X (fp32)
   __shared__ __attribute__((aligned(16))) bf16 Vs[DC * BP];
-  __shared__ float Gl[DC * LP];          // cumulative log decays, then X = beta gamma k
+  __shared__ __attribute__((aligned(16))) float GT[DD * GP];       // log decays by channel, GT[d][i]
   __shared__ float As[DC * (DC + 1)];    // A, then T = (I + A)^-1 in place
   __shared__ float Bs[DC];
+  static_assert(DC * LP * sizeof(float) <= 2 * DC * BP * sizeof(bf16), "X fits where K and Q were");
+  bf16* Ks = KQs;
+  bf16* Qs = KQs + DC * BP;
+  float* X = reinterpret_cast<float*>(KQs);
   const int chunk = blockIdx.x / H, h = blockIdx.x - chunk * H;
   if (chunk >= header[0]) return;
   int c0, n;
@@ -1170,15 +1174,18 @@ __global__ __launch_bounds__(PREP_THREADS) void kda_prep_kernel(
     const int f = tid + PREP_THREADS * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
     const float4 gv = i < n ? *reinterpret_cast<const float4*>(g + (size_t)(c0 + i) * rs + (size_t)h * DD + c4)
                             : make_float4(0.f, 0.f, 0.f, 0.f);
-    Gl[i * LP + c4] = gv.x; Gl[i * LP + c4 + 1] = gv.y; Gl[i * LP + c4 + 2] = gv.z; Gl[i * LP + c4 + 3] = gv.w;
+    GT[c4 * GP + i] = gv.x;
+    GT[(c4 + 1) * GP + i] = gv.y;
+    GT[(c4 + 2) * GP + i] = gv.z;
+    GT[(c4 + 3) * GP + i] = gv.w;
   }
   if (tid < DC) Bs[tid] = tid < n ? beta[(size_t)(c0 + tid) * H + h] : 0.f;
   __syncthreads();
   if (tid < DD) {   // in-chunk cumulative log decay of channel tid
     float acc = 0.f;
     for (int i = 0; i < DC; ++i) {
-      acc += Gl[i * LP + tid];
-      Gl[i * LP + tid] = acc;
+      acc += GT[tid * GP + i];
+      GT[tid * GP + i] = acc;
     }
   }
   __syncthreads();
@@ -1200,14 +1207,17 @@ __global__ __launch_bounds__(PREP_THREADS) void kda_prep_kernel(
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float ref = Gl[j0 * LP + d + e];
+          const float4 gI = *reinterpret_cast<const float4*>(GT + (d + e) * GP + i0);
+          const float4 gJ = *reinterpret_cast<const float4*>(GT + (d + e) * GP + j0);
+          const float gi[4] = {gI.x, gI.y, gI.z, gI.w};
+          const float gj[4] = {gJ.x, gJ.y, gJ.z, gJ.w};
           float ka[4], qa[4], kb[4];
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
-            const float a = __expf(Gl[(i0 + x) * LP + d + e] - ref);
+            const float a = __expf(gi[x] - gj[0]);
             ka[x] = (float)ki[x][e] * a;
             qa[x] = (float)qi[x][e] * a;
-            kb[x] = (float)kj[x][e] * __expf(ref - Gl[(j0 + x) * LP + d + e]);
+            kb[x] = (float)kj[x][e] * __expf(gj[0] - gj[x]);
           }
 #pragma unroll
           for (int x = 0; x < 4; ++x)
@@ -1231,15 +1241,29 @@ __global__ __launch_bounds__(PREP_THREADS) void kda_prep_kernel(
   }
   // the chunk's total decay, q o gamma and k o exp(G_C - G)
   const int last = max(n - 1, 0);
-  if (tid < DD) rec[KdaRecord::GC + tid] = __expf(Gl[last * LP + tid]);
+  if (tid < DD) rec[KdaRecord::GC + tid] = __expf(GT[tid * GP + last]);
   for (int f = tid; f < DC * DD; f += PREP_THREADS) {
     const int i = f / DD, d = f % DD;
-    const float G = Gl[i * LP + d];
+    const float G = GT[d * GP + i];
     rec[KdaRecord::QH + f] = (float)Qs[i * BP + d] * __expf(G);
-    rec[KdaRecord::KH + f] = i < n ? (float)Ks[i * BP + d] * __expf(Gl[last * LP + d] - G) : 0.f;
+    rec[KdaRecord::KH + f] = i < n ? (float)Ks[i * BP + d] * __expf(GT[d * GP + last] - G) : 0.f;
+  }
+  // X = diag(beta) (K o Gamma), held in registers until K and Q are spent
+  constexpr int XR = DC * DD / PREP_THREADS;
+  float xr[XR];
+#pragma unroll
+  for (int r = 0; r < XR; ++r) {
+    const int f = tid + PREP_THREADS * r, i = f / DD, d = f % DD;
+    xr[r] = Bs[i] * (float)Ks[i * BP + d] * __expf(GT[d * GP + i]);
   }
   __syncthreads();
-  // T = (I + A)^-1 row by row in place of A, as for the scalar gate
+#pragma unroll
+  for (int r = 0; r < XR; ++r) {
+    const int f = tid + PREP_THREADS * r, i = f / DD, d = f % DD;
+    X[i * LP + d] = xr[r];
+  }
+  // T = (I + A)^-1 row by row in place of A, as for the scalar gate (its
+  // barriers also order the X stores before their reads below)
   for (int i = 1; i < DC; ++i) {
     float acc = 0.f;
     if (tid < i) {
@@ -1264,12 +1288,6 @@ __global__ __launch_bounds__(PREP_THREADS) void kda_prep_kernel(
       const int i = f / DC, j = f % DC;
       rec[KdaRecord::TI + f] = j < i ? As[i * (DC + 1) + j] : (j == i ? 1.f : 0.f);
     }
-  // X = diag(beta) (K o Gamma) over the log decays (each thread its own entries)
-  for (int f = tid; f < DC * DD; f += PREP_THREADS) {
-    const int i = f / DD, d = f % DD;
-    Gl[i * LP + d] = Bs[i] * (float)Ks[i * BP + d] * __expf(Gl[i * LP + d]);
-  }
-  __syncthreads();
   // W = T X, U0 = T diag(beta) V: thread (4 rows, 8 columns)
   {
     const int i0 = (tid / 16) * 4, d8 = (tid % 16) * 8;
@@ -1279,7 +1297,7 @@ __global__ __launch_bounds__(PREP_THREADS) void kda_prep_kernel(
       const bf16x8 vv = *reinterpret_cast<const bf16x8*>(Vs + j * BP + d8);
       float xv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xv[e] = Gl[j * LP + d8 + e];
+      for (int e = 0; e < 8; ++e) xv[e] = X[j * LP + d8 + e];
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const int i = i0 + x;
