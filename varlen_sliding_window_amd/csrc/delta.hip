@@ -90,6 +90,68 @@ __device__ __forceinline__ bool delta_saved_for(const int* header, int T, int H,
   return header[1] == T && header[2] == H && header[3] == chunk_cap;
 }
 
+// T = (I + A)^-1 for the unit lower-triangular DC x DC system whose strict
+// lower part A sits in LDS (pitch DC + 1), in place, by a work-group of
+// PREP_THREADS, in 16 x 16 blocks.  Each wave first inverts one diagonal
+// block row by row (lane c keeps column c; one wave reads a row before any
+// lane writes it, so no barrier).  Then, block diagonal by block diagonal,
+//   T_ij = -T_ii sum_{j <= k < i} A_ik T_kj
+// (block forward substitution), each finished block parked transposed above
+// the diagonal, where A is zero, because later blocks of the same row still
+// read A_ik; a last pass moves them below it.  Ms: 3 x 16 x 16 floats of LDS.
+// The caller orders A's stores before and T's reads after.
+constexpr int TB = 16;                // block of the triangular inverse
+__device__ void unit_lower_inverse_blocked(float* As, float* Ms, int tid) {
+  static_assert(DC == 4 * TB && PREP_THREADS == TB * TB && PREP_THREADS == 4 * 64,
+                "four diagonal blocks, one per wave; one thread per block element");
+  constexpr int CP = DC + 1;
+  {
+    const int base = TB * (tid >> 6), c = tid & 63;
+    if (c < TB)
+      for (int r = 1; r < TB; ++r) {
+        float acc = 0.f;
+        if (c < r) {
+          acc = -As[(base + r) * CP + base + c];
+          for (int m = c + 1; m < r; ++m)
+            acc -= As[(base + r) * CP + base + m] * As[(base + m) * CP + base + c];
+        }
+        if (c < r) As[(base + r) * CP + base + c] = acc;
+      }
+  }
+  __syncthreads();
+  const int r = tid / TB, c = tid % TB;
+  for (int s = 1; s < DC / TB; ++s) {
+    for (int b = 0; b < DC / TB - s; ++b) {   // block (i, j) = (s + b, b): M = sum_k A_ik T_kj
+      const int i = s + b, j = b;
+      float m = 0.f;
+      for (int x = TB * j; x < TB * i; ++x) {
+        float t;
+        if (x < TB * (j + 1)) {                // the diagonal block T_jj, in place
+          const int xl = x - TB * j;
+          t = xl > c ? As[x * CP + TB * j + c] : (xl == c ? 1.f : 0.f);
+        } else {
+          t = As[(TB * j + c) * CP + x];       // T_kj, parked transposed
+        }
+        m += As[(TB * i + r) * CP + x] * t;
+      }
+      Ms[b * TB * TB + r * TB + c] = m;
+    }
+    __syncthreads();
+    for (int b = 0; b < DC / TB - s; ++b) {   // T_ij = -T_ii M
+      const int i = s + b, j = b;
+      float t = Ms[b * TB * TB + r * TB + c];
+      for (int mm = 0; mm < r; ++mm)
+        t += As[(TB * i + r) * CP + TB * i + mm] * Ms[b * TB * TB + mm * TB + c];
+      As[(TB * j + c) * CP + TB * i + r] = -t;
+    }
+    __syncthreads();
+  }
+  for (int f = tid; f < DC * DC; f += PREP_THREADS) {
+    const int i = f / DC, j = f % DC;
+    if (i / TB > j / TB) As[i * CP + j] = As[j * CP + i];
+  }
+}
+
 // One record per (chunk, head), fp32: W [DC][DD], U0 [DC][DD] (U after a
 // saving scan), P [DC][DC], gamma [DC],
 // decay to the chunk end [DC], T = (I + A)^-1 [DC][DC] (backward only), and
@@ -119,6 +181,7 @@ __global__ __launch_bounds__(PREP_THREADS) void delta_prep_kernel(
   __shared__ __attribute__((aligned(16))) bf16 Qs[DC * BP];
   __shared__ __attribute__((aligned(16))) bf16 Vs[DC * BP];
   __shared__ float As[DC * (DC + 1)];   // A, then T = (I + A)^-1 in place
+  __shared__ float Ms[3 * TB * TB];     // the inverse's block products
   __shared__ float Gs[DC], Bs[DC];
   const int chunk = blockIdx.x / H, h = blockIdx.x - chunk * H;
   if (chunk >= header[0]) return;
@@ -199,30 +262,9 @@ __global__ __launch_bounds__(PREP_THREADS) void delta_prep_kernel(
     rec[DeltaRecord::END + tid] = tid < n ? __expf(Gs[last] - Gs[tid]) : 0.f;
   }
   __syncthreads();
-  // T = (I + A)^-1, unit lower triangular, row by row in place of A: for
-  // c < i, T_ic = -A_ic - sum_{c < j < i} A_ij T_jc (thread c).  Row i reads
-  // its own A entries and the finished rows j < i, and is written only after
-  // every thread of the row has read it.
-  for (int i = 1; i < DC; ++i) {
-    float acc = 0.f;
-    if (tid < i) {
-      const int c = tid;
-      // four interleaved partial sums shorten the dependent chain
-      float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
-      int j = c + 1;
-      for (; j + 3 < i; j += 4) {
-        p0 += As[i * (DC + 1) + j] * As[j * (DC + 1) + c];
-        p1 += As[i * (DC + 1) + j + 1] * As[(j + 1) * (DC + 1) + c];
-        p2 += As[i * (DC + 1) + j + 2] * As[(j + 2) * (DC + 1) + c];
-        p3 += As[i * (DC + 1) + j + 3] * As[(j + 3) * (DC + 1) + c];
-      }
-      for (; j < i; ++j) p0 += As[i * (DC + 1) + j] * As[j * (DC + 1) + c];
-      acc = -As[i * (DC + 1) + c] - ((p0 + p1) + (p2 + p3));
-    }
-    __syncthreads();
-    if (tid < i) As[i * (DC + 1) + tid] = acc;
-    __syncthreads();
-  }
+  // T = (I + A)^-1 in place of A (A complete: barrier above)
+  unit_lower_inverse_blocked(As, Ms, tid);
+  __syncthreads();
   if (keep_inverse)   // T with its unit diagonal, zero above it
     for (int f = tid; f < DC * DC; f += PREP_THREADS) {
       const int i = f / DC, j = f % DC;
@@ -1149,6 +1191,7 @@ __global__ __launch_bounds__(PREP_THREADS) void kda_prep_kernel(
   __shared__ __attribute__((aligned(16))) bf16 Vs[DC * BP];
   __shared__ __attribute__((aligned(16))) float GT[DD * GP];       // log decays by channel, GT[d][i]
   __shared__ float As[DC * (DC + 1)];    // A, then T = (I + A)^-1 in place
+  __shared__ float Ms[3 * TB * TB];      // the inverse's block products
   __shared__ float Bs[DC];
   static_assert(DC * LP * sizeof(float) <= 2 * DC * BP * sizeof(bf16), "X fits where K and Q were");
   bf16* Ks = KQs;
@@ -1262,27 +1305,10 @@ __global__ __launch_bounds__(PREP_THREADS) void kda_prep_kernel(
     const int f = tid + PREP_THREADS * r, i = f / DD, d = f % DD;
     X[i * LP + d] = xr[r];
   }
-  // T = (I + A)^-1 row by row in place of A, as for the scalar gate (its
-  // barriers also order the X stores before their reads below)
-  for (int i = 1; i < DC; ++i) {
-    float acc = 0.f;
-    if (tid < i) {
-      const int c = tid;
-      float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
-      int j = c + 1;
-      for (; j + 3 < i; j += 4) {
-        p0 += As[i * (DC + 1) + j] * As[j * (DC + 1) + c];
-        p1 += As[i * (DC + 1) + j + 1] * As[(j + 1) * (DC + 1) + c];
-        p2 += As[i * (DC + 1) + j + 2] * As[(j + 2) * (DC + 1) + c];
-        p3 += As[i * (DC + 1) + j + 3] * As[(j + 3) * (DC + 1) + c];
-      }
-      for (; j < i; ++j) p0 += As[i * (DC + 1) + j] * As[j * (DC + 1) + c];
-      acc = -As[i * (DC + 1) + c] - ((p0 + p1) + (p2 + p3));
-    }
-    __syncthreads();
-    if (tid < i) As[i * (DC + 1) + tid] = acc;
-    __syncthreads();
-  }
+  // T = (I + A)^-1 in place of A; its barriers also order the X stores
+  // before their reads below
+  unit_lower_inverse_blocked(As, Ms, tid);
+  __syncthreads();
   if (keep_inverse)
     for (int f = tid; f < DC * DC; f += PREP_THREADS) {
       const int i = f / DC, j = f % DC;
