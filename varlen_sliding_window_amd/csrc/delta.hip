@@ -28,6 +28,11 @@
 namespace attn {
 namespace {
 
+// Plain vector types for the scans' prefetch registers (HIP's float4 and
+// uint4 are structs whose copies keep arrays of them in memory).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int DC = DELTA_CHUNK;       // tokens per chunk
 constexpr int DD = DELTA_DIM;         // d_k = d_v
 constexpr int PLAN_THREADS = 1024;
@@ -203,10 +208,10 @@ __global__ __launch_bounds__(PREP_THREADS) void delta_prep_kernel(
   for (int r = 0; r < DC * DD / 8 / PREP_THREADS; ++r) {
     const int f = tid + PREP_THREADS * r, i = f / (DD / 8), ch = f % (DD / 8);
     const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + ch * 8;
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(Ks + i * BP + ch * 8) = i < n ? *reinterpret_cast<const uint4*>(k + off) : z;
-    *reinterpret_cast<uint4*>(Qs + i * BP + ch * 8) = i < n ? *reinterpret_cast<const uint4*>(q + off) : z;
-    *reinterpret_cast<uint4*>(Vs + i * BP + ch * 8) = i < n ? *reinterpret_cast<const uint4*>(v + off) : z;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(Ks + i * BP + ch * 8) = i < n ? *reinterpret_cast<const u32x4*>(k + off) : z;
+    *reinterpret_cast<u32x4*>(Qs + i * BP + ch * 8) = i < n ? *reinterpret_cast<const u32x4*>(q + off) : z;
+    *reinterpret_cast<u32x4*>(Vs + i * BP + ch * 8) = i < n ? *reinterpret_cast<const u32x4*>(v + off) : z;
   }
   if (tid < DC) {
     const bool in = tid < n;
@@ -314,14 +319,16 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
     float* __restrict__ records, bf16* __restrict__ out, float* __restrict__ states) {
   constexpr int SL = DD / SLICE;       // slices per head
   constexpr int BP = DD + 8;           // bf16 row pitch (16 bytes of padding)
-  __shared__ float Ss[SLICE * LP];     // S rows c0 .. c0 + SLICE - 1, all d_k
-  __shared__ float Ws[DC * LP];
+  constexpr int SP = DD + 4;           // fp32 row pitch, rows 16-byte aligned
+  constexpr int OP = SLICE + 4;        // pitch of the slice-wide tiles, 16-byte aligned
+  __shared__ __attribute__((aligned(16))) float Ss[SLICE * SP];   // S rows c0 .. c0 + SLICE - 1
+  __shared__ __attribute__((aligned(16))) float Ws[DC * SP];
   __shared__ __attribute__((aligned(16))) bf16 Qs[DC * BP];
   __shared__ __attribute__((aligned(16))) bf16 Ks[DC * BP];
   __shared__ float Ps[DC * (DC + 1)];
-  __shared__ float U0s[DC * (SLICE + 1)];
-  __shared__ float Us[DC * (SLICE + 1)];
-  __shared__ float QSs[DC * (SLICE + 1)];
+  __shared__ __attribute__((aligned(16))) float U0s[DC * OP];
+  __shared__ __attribute__((aligned(16))) float Us[DC * OP];
+  __shared__ __attribute__((aligned(16))) float QSs[DC * OP];
   __shared__ float Gm[DC], En[DC];
   const int sl = blockIdx.x % SL;
   const int h = (blockIdx.x / SL) % H;
@@ -336,20 +343,20 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
   const int tid = threadIdx.x;
   const int cbase = sl * SLICE;
   const size_t rs = (size_t)H * DD;
-  for (int e = tid; e < SLICE * LP; e += SCAN_THREADS) Ss[e] = 0.f;
+  for (int e = tid; e < SLICE * SP; e += SCAN_THREADS) Ss[e] = 0.f;
 
   // register staging of one chunk: W, P, q and k rows, the slice of U0 and
   // gamma / end decay, spread over the work-group's threads
   constexpr int NT = SCAN_THREADS;
   constexpr int WR = DC * DD / 4 / NT, PR = DC * DC / 4 / NT, QR = DC * DD / 8 / NT;
-  float4 wr[WR], pr[PR], ur = make_float4(0.f, 0.f, 0.f, 0.f);
-  uint4 qr[QR], kr[QR];
+  f32x4 wr[WR], pr[PR], ur = {0.f, 0.f, 0.f, 0.f};
+  u32x4 qr[QR], kr[QR];
   float gr = 0.f;
-  auto fetch = [&](int ci) {
+  auto fetch = [&](int ci) __attribute__((always_inline)) {
     const int c0 = a + ci * DC;
     const int n = min(DC, b - c0);
     const float* rec = records + ((size_t)(first + ci) * H + h) * DeltaRecord::FLOATS;
-    const float4* r4 = reinterpret_cast<const float4*>(rec);
+    const f32x4* r4 = reinterpret_cast<const f32x4*>(rec);
 #pragma unroll
     for (int r = 0; r < WR; ++r) wr[r] = r4[DeltaRecord::W / 4 + tid + NT * r];
 #pragma unroll
@@ -358,8 +365,8 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
     for (int r = 0; r < QR; ++r) {
       const int f = tid + NT * r, i = f / (DD / 8), ch = f % (DD / 8);
       const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + ch * 8;
-      qr[r] = i < n ? *reinterpret_cast<const uint4*>(q + off) : make_uint4(0, 0, 0, 0);
-      kr[r] = i < n ? *reinterpret_cast<const uint4*>(k + off) : make_uint4(0, 0, 0, 0);
+      qr[r] = i < n ? *reinterpret_cast<const u32x4*>(q + off) : u32x4{0u, 0u, 0u, 0u};
+      kr[r] = i < n ? *reinterpret_cast<const u32x4*>(k + off) : u32x4{0u, 0u, 0u, 0u};
     }
     if (tid < DC * SLICE / 4)
       ur = r4[(DeltaRecord::U0 + (size_t)(tid / (SLICE / 4)) * DD + cbase) / 4 + (tid % (SLICE / 4))];
@@ -374,10 +381,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
 #pragma unroll
     for (int r = 0; r < WR; ++r) {
       const int f = tid + NT * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
-      Ws[i * LP + c4] = wr[r].x;
-      Ws[i * LP + c4 + 1] = wr[r].y;
-      Ws[i * LP + c4 + 2] = wr[r].z;
-      Ws[i * LP + c4 + 3] = wr[r].w;
+      *reinterpret_cast<f32x4*>(Ws + i * SP + c4) = wr[r];
     }
 #pragma unroll
     for (int r = 0; r < PR; ++r) {
@@ -390,15 +394,12 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
 #pragma unroll
     for (int r = 0; r < QR; ++r) {
       const int f = tid + NT * r, i = f / (DD / 8), ch = f % (DD / 8);
-      *reinterpret_cast<uint4*>(Qs + i * BP + ch * 8) = qr[r];
-      *reinterpret_cast<uint4*>(Ks + i * BP + ch * 8) = kr[r];
+      *reinterpret_cast<u32x4*>(Qs + i * BP + ch * 8) = qr[r];
+      *reinterpret_cast<u32x4*>(Ks + i * BP + ch * 8) = kr[r];
     }
     if (tid < DC * SLICE / 4) {
       const int i = tid / (SLICE / 4), c4 = (tid % (SLICE / 4)) * 4;
-      U0s[i * (SLICE + 1) + c4] = ur.x;
-      U0s[i * (SLICE + 1) + c4 + 1] = ur.y;
-      U0s[i * (SLICE + 1) + c4 + 2] = ur.z;
-      U0s[i * (SLICE + 1) + c4 + 3] = ur.w;
+      *reinterpret_cast<f32x4*>(U0s + i * OP + c4) = ur;
     }
     if (tid < DC) Gm[tid] = gr;
     else if (tid < 2 * DC) En[tid - DC] = gr;
@@ -410,7 +411,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
 #pragma unroll
       for (int r = 0; r < SLICE * DD / 4 / NT; ++r) {
         const int e4 = tid + NT * r, row = e4 / (DD / 4), c4 = (e4 % (DD / 4)) * 4;
-        const float* src = Ss + row * LP + c4;
+        const float* src = Ss + row * SP + c4;
         *reinterpret_cast<float4*>(st + row * DD + c4) = make_float4(src[0], src[1], src[2], src[3]);
       }
     }
@@ -418,39 +419,40 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
     // U = U0 - W S^T and Q S^T: thread (row i, CPT slice columns)
     constexpr int CPT = DC * SLICE / NT;          // columns per thread
     const int i = tid / (SLICE / CPT), cc = (tid % (SLICE / CPT)) * CPT;
-    {
+    {   // four columns of d per step, read as vectors
+      static_assert(CPT == 4, "a float4 of U per thread");
       float ws[CPT] = {}, qs[CPT] = {};
-      for (int d = 0; d < DD; ++d) {
-        const float w = Ws[i * LP + d];
-        const float qv = (float)Qs[i * BP + d];
+      for (int d = 0; d < DD; d += 4) {
+        const float4 w = *reinterpret_cast<const float4*>(Ws + i * SP + d);
+        const bf16x4 qb = *reinterpret_cast<const bf16x4*>(Qs + i * BP + d);
+        const float q0 = (float)qb[0], q1 = (float)qb[1], q2 = (float)qb[2], q3 = (float)qb[3];
 #pragma unroll
         for (int x = 0; x < CPT; ++x) {
-          const float sv = Ss[(cc + x) * LP + d];
-          ws[x] += w * sv;
-          qs[x] += qv * sv;
+          const float4 sv = *reinterpret_cast<const float4*>(Ss + (cc + x) * SP + d);
+          ws[x] += w.x * sv.x + w.y * sv.y + w.z * sv.z + w.w * sv.w;
+          qs[x] += q0 * sv.x + q1 * sv.y + q2 * sv.z + q3 * sv.w;
         }
       }
-#pragma unroll
-      for (int x = 0; x < CPT; ++x) {
-        Us[i * (SLICE + 1) + cc + x] = U0s[i * (SLICE + 1) + cc + x] - ws[x];
-        QSs[i * (SLICE + 1) + cc + x] = qs[x];
-      }
-      if (states) {
-        float* urec = records + unit * DeltaRecord::FLOATS + DeltaRecord::U0 + (size_t)i * DD + cbase + cc;
-#pragma unroll
-        for (int x = 0; x < CPT; ++x) urec[x] = U0s[i * (SLICE + 1) + cc + x] - ws[x];
-      }
+      const float4 u0 = *reinterpret_cast<const float4*>(U0s + i * OP + cc);
+      const float4 u = make_float4(u0.x - ws[0], u0.y - ws[1], u0.z - ws[2], u0.w - ws[3]);
+      *reinterpret_cast<float4*>(Us + i * OP + cc) = u;
+      *reinterpret_cast<float4*>(QSs + i * OP + cc) = make_float4(qs[0], qs[1], qs[2], qs[3]);
+      if (states)
+        *reinterpret_cast<float4*>(records + unit * DeltaRecord::FLOATS + DeltaRecord::U0 +
+                                   (size_t)i * DD + cbase + cc) = u;
     }
     __syncthreads();
     // O = scale (gamma Q S^T + P U) for the chunk's rows inside the document
     if (out && i < n) {
-      float acc[CPT];
-#pragma unroll
-      for (int x = 0; x < CPT; ++x) acc[x] = Gm[i] * QSs[i * (SLICE + 1) + cc + x];
+      const float4 qs = *reinterpret_cast<const float4*>(QSs + i * OP + cc);
+      float acc[CPT] = {Gm[i] * qs.x, Gm[i] * qs.y, Gm[i] * qs.z, Gm[i] * qs.w};
       for (int j = 0; j <= i; ++j) {
         const float p = Ps[i * (DC + 1) + j];
-#pragma unroll
-        for (int x = 0; x < CPT; ++x) acc[x] += p * Us[j * (SLICE + 1) + cc + x];
+        const float4 u = *reinterpret_cast<const float4*>(Us + j * OP + cc);
+        acc[0] += p * u.x;
+        acc[1] += p * u.y;
+        acc[2] += p * u.z;
+        acc[3] += p * u.w;
       }
       bf16* op = out + (size_t)(c0 + i) * rs + (size_t)h * DD + cbase + cc;
 #pragma unroll
@@ -462,7 +464,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
       const int c = tid / (DD / DPT), d0 = (tid % (DD / DPT)) * DPT;
       float acc[DPT] = {};
       for (int j = 0; j < n; ++j) {
-        const float u = Us[j * (SLICE + 1) + c] * En[j];
+        const float u = Us[j * OP + c] * En[j];
 #pragma unroll
         for (int y = 0; y < DPT; ++y) acc[y] += u * (float)Ks[j * BP + d0 + y];
       }
@@ -470,7 +472,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
       // each thread updates only its own entries of S, and every read of S
       // in this chunk came before the last barrier
 #pragma unroll
-      for (int y = 0; y < DPT; ++y) Ss[c * LP + d0 + y] = gc * Ss[c * LP + d0 + y] + acc[y];
+      for (int y = 0; y < DPT; ++y) Ss[c * SP + d0 + y] = gc * Ss[c * SP + d0 + y] + acc[y];
     }
   }
 }
@@ -513,14 +515,14 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_rscan_kernel(
   constexpr int NT = SCAN_THREADS;
   constexpr int WR = DC * DD / 4 / NT, PR = DC * DC / 4 / NT, QR = DC * DD / 8 / NT;
   constexpr int OR = DC * SLICE / 8;   // threads loading 8 dO values each
-  float4 wr[WR], pr[PR];
-  uint4 qr[QR], kr[QR], dor = make_uint4(0, 0, 0, 0);
+  f32x4 wr[WR], pr[PR];
+  u32x4 qr[QR], kr[QR], dor = {0u, 0u, 0u, 0u};
   float gr = 0.f;
-  auto fetch = [&](int ci) {
+  auto fetch = [&](int ci) __attribute__((always_inline)) {
     const int c0 = a + ci * DC;
     const int n = min(DC, b - c0);
     const float* rec = records + ((size_t)(first + ci) * H + h) * DeltaRecord::FLOATS;
-    const float4* r4 = reinterpret_cast<const float4*>(rec);
+    const f32x4* r4 = reinterpret_cast<const f32x4*>(rec);
 #pragma unroll
     for (int r = 0; r < WR; ++r) wr[r] = r4[DeltaRecord::W / 4 + tid + NT * r];
 #pragma unroll
@@ -529,13 +531,13 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_rscan_kernel(
     for (int r = 0; r < QR; ++r) {
       const int f = tid + NT * r, i = f / (DD / 8), ch = f % (DD / 8);
       const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + ch * 8;
-      qr[r] = i < n ? *reinterpret_cast<const uint4*>(q + off) : make_uint4(0, 0, 0, 0);
-      kr[r] = i < n ? *reinterpret_cast<const uint4*>(k + off) : make_uint4(0, 0, 0, 0);
+      qr[r] = i < n ? *reinterpret_cast<const u32x4*>(q + off) : u32x4{0u, 0u, 0u, 0u};
+      kr[r] = i < n ? *reinterpret_cast<const u32x4*>(k + off) : u32x4{0u, 0u, 0u, 0u};
     }
     if (tid < OR) {
       const int i = tid / (SLICE / 8), ch = tid % (SLICE / 8);
       const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + cbase + ch * 8;
-      dor = i < n ? *reinterpret_cast<const uint4*>(dout + off) : make_uint4(0, 0, 0, 0);
+      dor = i < n ? *reinterpret_cast<const u32x4*>(dout + off) : u32x4{0u, 0u, 0u, 0u};
     }
     gr = tid < DC ? rec[DeltaRecord::GAM + tid] : (tid < 2 * DC ? rec[DeltaRecord::END + tid - DC] : 0.f);
   };
@@ -545,7 +547,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_rscan_kernel(
     const int n = min(DC, b - (a + ci * DC));
     __syncthreads();   // every read of the previous chunk's LDS data is done
 #pragma unroll
-    for (int r = 0; r < WR; ++r) reinterpret_cast<float4*>(Ws)[tid + NT * r] = wr[r];
+    for (int r = 0; r < WR; ++r) reinterpret_cast<f32x4*>(Ws)[tid + NT * r] = wr[r];
 #pragma unroll
     for (int r = 0; r < PR; ++r) {
       const int f = tid + NT * r, pi = f / (DC / 4), pj = (f % (DC / 4)) * 4;
@@ -557,8 +559,8 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_rscan_kernel(
 #pragma unroll
     for (int r = 0; r < QR; ++r) {
       const int f = tid + NT * r, i = f / (DD / 8), ch = f % (DD / 8);
-      *reinterpret_cast<uint4*>(Qs + i * BP + ch * 8) = qr[r];
-      *reinterpret_cast<uint4*>(Ks + i * BP + ch * 8) = kr[r];
+      *reinterpret_cast<u32x4*>(Qs + i * BP + ch * 8) = qr[r];
+      *reinterpret_cast<u32x4*>(Ks + i * BP + ch * 8) = kr[r];
     }
     if (tid < OR) {
       const int i = tid / (SLICE / 8), ch = tid % (SLICE / 8);
@@ -690,8 +692,8 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_gstate_kernel(
   for (int r = 0; r < DC * DD / 8 / GRAD_THREADS; ++r) {
     const int f = tid + GRAD_THREADS * r, i = f / (DD / 8), ch = f % (DD / 8);
     const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + ch * 8;
-    *reinterpret_cast<uint4*>(dOs + i * BP + ch * 8) =
-        i < n ? *reinterpret_cast<const uint4*>(dout + off) : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<u32x4*>(dOs + i * BP + ch * 8) =
+        i < n ? *reinterpret_cast<const u32x4*>(dout + off) : u32x4{0u, 0u, 0u, 0u};
   }
 #pragma unroll
   for (int r = 0; r < DC * DD / 4 / GRAD_THREADS; ++r) {
@@ -832,11 +834,11 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
     const int f = tid + GRAD_THREADS * r, i = f / (DD / 8), ch = f % (DD / 8);
     const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + ch * 8;
     const bool in = i < n;
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(Kb + i * BP + ch * 8) = in ? *reinterpret_cast<const uint4*>(k + off) : z;
-    *reinterpret_cast<uint4*>(Qb + i * BP + ch * 8) = in ? *reinterpret_cast<const uint4*>(q + off) : z;
-    *reinterpret_cast<uint4*>(Vb + i * BP + ch * 8) = in ? *reinterpret_cast<const uint4*>(v + off) : z;
-    *reinterpret_cast<uint4*>(dOb + i * BP + ch * 8) = in ? *reinterpret_cast<const uint4*>(dout + off) : z;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(Kb + i * BP + ch * 8) = in ? *reinterpret_cast<const u32x4*>(k + off) : z;
+    *reinterpret_cast<u32x4*>(Qb + i * BP + ch * 8) = in ? *reinterpret_cast<const u32x4*>(q + off) : z;
+    *reinterpret_cast<u32x4*>(Vb + i * BP + ch * 8) = in ? *reinterpret_cast<const u32x4*>(v + off) : z;
+    *reinterpret_cast<u32x4*>(dOb + i * BP + ch * 8) = in ? *reinterpret_cast<const u32x4*>(dout + off) : z;
   }
 #pragma unroll
   for (int r = 0; r < DC * DD / 4 / GRAD_THREADS; ++r) {
@@ -1207,16 +1209,15 @@ __global__ __launch_bounds__(PREP_THREADS) void kda_prep_kernel(
   for (int r = 0; r < DC * DD / 8 / PREP_THREADS; ++r) {
     const int f = tid + PREP_THREADS * r, i = f / (DD / 8), ch = f % (DD / 8);
     const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + ch * 8;
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(Ks + i * BP + ch * 8) = i < n ? *reinterpret_cast<const uint4*>(k + off) : z;
-    *reinterpret_cast<uint4*>(Qs + i * BP + ch * 8) = i < n ? *reinterpret_cast<const uint4*>(q + off) : z;
-    *reinterpret_cast<uint4*>(Vs + i * BP + ch * 8) = i < n ? *reinterpret_cast<const uint4*>(v + off) : z;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(Ks + i * BP + ch * 8) = i < n ? *reinterpret_cast<const u32x4*>(k + off) : z;
+    *reinterpret_cast<u32x4*>(Qs + i * BP + ch * 8) = i < n ? *reinterpret_cast<const u32x4*>(q + off) : z;
+    *reinterpret_cast<u32x4*>(Vs + i * BP + ch * 8) = i < n ? *reinterpret_cast<const u32x4*>(v + off) : z;
   }
 #pragma unroll
   for (int r = 0; r < DC * DD / 4 / PREP_THREADS; ++r) {
     const int f = tid + PREP_THREADS * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
-    const float4 gv = i < n ? *reinterpret_cast<const float4*>(g + (size_t)(c0 + i) * rs + (size_t)h * DD + c4)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    const f32x4 gv = i < n ? *reinterpret_cast<const f32x4*>(g + (size_t)(c0 + i) * rs + (size_t)h * DD + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
     GT[c4 * GP + i] = gv.x;
     GT[(c4 + 1) * GP + i] = gv.y;
     GT[(c4 + 2) * GP + i] = gv.z;
@@ -1381,10 +1382,10 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_scan_kernel(
 
   constexpr int NT = SCAN_THREADS;
   constexpr int WR = DC * DD / 4 / NT, PR = DC * DC / 4 / NT;
-  float4 wr[WR], qr[WR], kr[WR], pr[PR];
-  float4 ur = make_float4(0.f, 0.f, 0.f, 0.f), gr = make_float4(0.f, 0.f, 0.f, 0.f);
-  auto fetch = [&](int ci) {
-    const float4* r4 = reinterpret_cast<const float4*>(
+  f32x4 wr[WR], qr[WR], kr[WR], pr[PR];
+  f32x4 ur = {0.f, 0.f, 0.f, 0.f}, gr = {0.f, 0.f, 0.f, 0.f};
+  auto fetch = [&](int ci) __attribute__((always_inline)) {
+    const f32x4* r4 = reinterpret_cast<const f32x4*>(
         records + ((size_t)(first + ci) * H + h) * KdaRecord::FLOATS);
 #pragma unroll
     for (int r = 0; r < WR; ++r) {
@@ -1411,7 +1412,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_scan_kernel(
       Ws[i * LP + c4 + 2] = wr[r].z; Ws[i * LP + c4 + 3] = wr[r].w;
       QHs[i * LP + c4] = qr[r].x; QHs[i * LP + c4 + 1] = qr[r].y;
       QHs[i * LP + c4 + 2] = qr[r].z; QHs[i * LP + c4 + 3] = qr[r].w;
-      reinterpret_cast<float4*>(KHs)[f] = kr[r];
+      reinterpret_cast<f32x4*>(KHs)[f] = kr[r];
     }
 #pragma unroll
     for (int r = 0; r < PR; ++r) {
@@ -1426,7 +1427,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_scan_kernel(
       U0s[i * OP + c4] = ur.x; U0s[i * OP + c4 + 1] = ur.y;
       U0s[i * OP + c4 + 2] = ur.z; U0s[i * OP + c4 + 3] = ur.w;
     }
-    if (tid < DD / 4) reinterpret_cast<float4*>(GCs)[tid] = gr;
+    if (tid < DD / 4) reinterpret_cast<f32x4*>(GCs)[tid] = gr;
     __syncthreads();
     if (ci + 1 < count) fetch(ci + 1);
     const size_t unit = (size_t)(first + ci) * H + h;
@@ -1555,13 +1556,13 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_rscan_kernel(
   constexpr int NT = SCAN_THREADS;
   constexpr int WR = DC * DD / 4 / NT, PR = DC * DC / 4 / NT;
   constexpr int OR = DC * SLICE / 8;
-  float4 wr[WR], qr[WR], kr[WR], pr[PR];
-  float4 gr = make_float4(0.f, 0.f, 0.f, 0.f);
-  uint4 dor = make_uint4(0, 0, 0, 0);
-  auto fetch = [&](int ci) {
+  f32x4 wr[WR], qr[WR], kr[WR], pr[PR];
+  f32x4 gr = {0.f, 0.f, 0.f, 0.f};
+  u32x4 dor = {0u, 0u, 0u, 0u};
+  auto fetch = [&](int ci) __attribute__((always_inline)) {
     const int c0 = a + ci * DC;
     const int n = min(DC, b - c0);
-    const float4* r4 = reinterpret_cast<const float4*>(
+    const f32x4* r4 = reinterpret_cast<const f32x4*>(
         records + ((size_t)(first + ci) * H + h) * KdaRecord::FLOATS);
 #pragma unroll
     for (int r = 0; r < WR; ++r) {
@@ -1574,7 +1575,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_rscan_kernel(
     if (tid < OR) {
       const int i = tid / (SLICE / 8), ch = tid % (SLICE / 8);
       const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + cbase + ch * 8;
-      dor = i < n ? *reinterpret_cast<const uint4*>(dout + off) : make_uint4(0, 0, 0, 0);
+      dor = i < n ? *reinterpret_cast<const u32x4*>(dout + off) : u32x4{0u, 0u, 0u, 0u};
     }
     if (tid < DD / 4) gr = r4[KdaRecord::GC / 4 + tid];
   };
@@ -1586,8 +1587,8 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_rscan_kernel(
 #pragma unroll
     for (int r = 0; r < WR; ++r) {
       const int f = tid + NT * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
-      reinterpret_cast<float4*>(Ws)[f] = wr[r];
-      reinterpret_cast<float4*>(QHs)[f] = qr[r];
+      reinterpret_cast<f32x4*>(Ws)[f] = wr[r];
+      reinterpret_cast<f32x4*>(QHs)[f] = qr[r];
       KHs[i * LP + c4] = kr[r].x; KHs[i * LP + c4 + 1] = kr[r].y;
       KHs[i * LP + c4 + 2] = kr[r].z; KHs[i * LP + c4 + 3] = kr[r].w;
     }
@@ -1606,7 +1607,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_rscan_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) dOs[i * OP + ch * 8 + e] = (float)ov[e];
     }
-    if (tid < DD / 4) reinterpret_cast<float4*>(GCs)[tid] = gr;
+    if (tid < DD / 4) reinterpret_cast<f32x4*>(GCs)[tid] = gr;
     __syncthreads();
     if (ci > 0) fetch(ci - 1);
     const size_t unit = (size_t)(first + ci) * H + h;
@@ -1704,8 +1705,8 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gstate_kernel(
   for (int r = 0; r < DC * DD / 8 / GRAD_THREADS; ++r) {
     const int f = tid + GRAD_THREADS * r, i = f / (DD / 8), ch = f % (DD / 8);
     const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + ch * 8;
-    *reinterpret_cast<uint4*>(dOs + i * BP + ch * 8) =
-        i < n ? *reinterpret_cast<const uint4*>(dout + off) : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<u32x4*>(dOs + i * BP + ch * 8) =
+        i < n ? *reinterpret_cast<const u32x4*>(dout + off) : u32x4{0u, 0u, 0u, 0u};
   }
 #pragma unroll
   for (int r = 0; r < DC * DD / 4 / GRAD_THREADS; ++r) {
@@ -1808,8 +1809,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gmat_kernel(
 #pragma unroll
   for (int r = 0; r < DC * DD / 4 / GRAD_THREADS; ++r) {
     const int f = tid + GRAD_THREADS * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
-    const float4 gv = i < n ? *reinterpret_cast<const float4*>(g + (size_t)(c0 + i) * rs + (size_t)h * DD + c4)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    const f32x4 gv = i < n ? *reinterpret_cast<const f32x4*>(g + (size_t)(c0 + i) * rs + (size_t)h * DD + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
     F2[i * LP + c4] = gv.x; F2[i * LP + c4 + 1] = gv.y; F2[i * LP + c4 + 2] = gv.z; F2[i * LP + c4 + 3] = gv.w;
   }
   if (tid < DC) {
@@ -1836,9 +1836,9 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gmat_kernel(
   for (int r = 0; r < DC * DD / 8 / GRAD_THREADS; ++r) {
     const int f = tid + GRAD_THREADS * r, i = f / (DD / 8), ch = f % (DD / 8);
     const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + ch * 8;
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(Vb + i * BP + ch * 8) = i < n ? *reinterpret_cast<const uint4*>(v + off) : z;
-    *reinterpret_cast<uint4*>(dOb + i * BP + ch * 8) = i < n ? *reinterpret_cast<const uint4*>(dout + off) : z;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(Vb + i * BP + ch * 8) = i < n ? *reinterpret_cast<const u32x4*>(v + off) : z;
+    *reinterpret_cast<u32x4*>(dOb + i * BP + ch * 8) = i < n ? *reinterpret_cast<const u32x4*>(dout + off) : z;
   }
 #pragma unroll
   for (int r = 0; r < DC * DD / 4 / GRAD_THREADS; ++r) {
@@ -2041,16 +2041,16 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gpair_kernel(
   for (int r = 0; r < DC * DD / 8 / GRAD_THREADS; ++r) {
     const int f = tid + GRAD_THREADS * r, i = f / (DD / 8), ch = f % (DD / 8);
     const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + ch * 8;
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(Qb + i * BP + ch * 8) = i < n ? *reinterpret_cast<const uint4*>(q + off) : z;
-    *reinterpret_cast<uint4*>(Kb + i * BP + ch * 8) = i < n ? *reinterpret_cast<const uint4*>(k + off) : z;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(Qb + i * BP + ch * 8) = i < n ? *reinterpret_cast<const u32x4*>(q + off) : z;
+    *reinterpret_cast<u32x4*>(Kb + i * BP + ch * 8) = i < n ? *reinterpret_cast<const u32x4*>(k + off) : z;
   }
 #pragma unroll
   for (int r = 0; r < DC * DD / 4 / GRAD_THREADS; ++r) {
     const int f = tid + GRAD_THREADS * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
-    reinterpret_cast<float4*>(Gl)[f] =
-        i < n ? *reinterpret_cast<const float4*>(g + (size_t)(c0 + i) * rs + (size_t)h * DD + c4)
-              : make_float4(0.f, 0.f, 0.f, 0.f);
+    reinterpret_cast<f32x4*>(Gl)[f] =
+        i < n ? *reinterpret_cast<const f32x4*>(g + (size_t)(c0 + i) * rs + (size_t)h * DD + c4)
+              : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   for (int f = tid; f < DC * DC; f += GRAD_THREADS) {
     Mp[(f / DC) * CP + f % DC] = side[f];
