@@ -489,14 +489,15 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_rscan_kernel(
     const float* __restrict__ records, float* __restrict__ dstates, float* __restrict__ dubuf) {
   constexpr int SL = DD / SLICE;
   constexpr int BP = DD + 8;
-  constexpr int OP = SLICE + 1;
-  __shared__ float dSs[SLICE * LP];    // dS rows c0 .. c0 + SLICE - 1, all d_k
+  constexpr int SP = DD + 4;           // fp32 row pitch, rows 16-byte aligned
+  constexpr int OP = SLICE + 4;        // pitch of the slice-wide tiles, 16-byte aligned
+  __shared__ __attribute__((aligned(16))) float dSs[SLICE * SP];   // dS rows c0 .. c0 + SLICE - 1
   __shared__ __attribute__((aligned(16))) float Ws[DC * DD];   // read a row at a time
   __shared__ __attribute__((aligned(16))) bf16 Qs[DC * BP];
   __shared__ __attribute__((aligned(16))) bf16 Ks[DC * BP];
   __shared__ float Ps[DC * (DC + 1)];
-  __shared__ float dOs[DC * OP];
-  __shared__ float dUs[DC * OP];
+  __shared__ __attribute__((aligned(16))) float dOs[DC * OP];
+  __shared__ __attribute__((aligned(16))) float dUs[DC * OP];
   __shared__ float Gm[DC], En[DC];
   const int sl = blockIdx.x % SL;
   const int h = (blockIdx.x / SL) % H;
@@ -510,7 +511,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_rscan_kernel(
   const int tid = threadIdx.x;
   const int cbase = sl * SLICE;
   const size_t rs = (size_t)H * DD;
-  for (int e = tid; e < SLICE * LP; e += SCAN_THREADS) dSs[e] = 0.f;
+  for (int e = tid; e < SLICE * SP; e += SCAN_THREADS) dSs[e] = 0.f;
 
   constexpr int NT = SCAN_THREADS;
   constexpr int WR = DC * DD / 4 / NT, PR = DC * DC / 4 / NT, QR = DC * DD / 8 / NT;
@@ -579,7 +580,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_rscan_kernel(
 #pragma unroll
       for (int r = 0; r < SLICE * DD / 4 / NT; ++r) {
         const int e4 = tid + NT * r, row = e4 / (DD / 4), c4 = (e4 % (DD / 4)) * 4;
-        const float* src = dSs + row * LP + c4;
+        const float* src = dSs + row * SP + c4;
         *reinterpret_cast<float4*>(st + row * DD + c4) = make_float4(src[0], src[1], src[2], src[3]);
       }
     }
@@ -587,24 +588,29 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_rscan_kernel(
     constexpr int CPT = DC * SLICE / NT;
     {
       const int j = tid / (SLICE / CPT), cc = (tid % (SLICE / CPT)) * CPT;
+      static_assert(CPT == 4, "a float4 of dU per thread");
       float kd[CPT] = {}, pd[CPT] = {};
-      for (int d = 0; d < DD; ++d) {
-        const float kv = (float)Ks[j * BP + d];
+      for (int d = 0; d < DD; d += 4) {   // four columns of d per step, read as vectors
+        const bf16x4 kb = *reinterpret_cast<const bf16x4*>(Ks + j * BP + d);
+        const float k0 = (float)kb[0], k1 = (float)kb[1], k2 = (float)kb[2], k3 = (float)kb[3];
 #pragma unroll
-        for (int x = 0; x < CPT; ++x) kd[x] += kv * dSs[(cc + x) * LP + d];
+        for (int x = 0; x < CPT; ++x) {
+          const f32x4 sv = *reinterpret_cast<const f32x4*>(dSs + (cc + x) * SP + d);
+          kd[x] += k0 * sv.x + k1 * sv.y + k2 * sv.z + k3 * sv.w;
+        }
       }
       for (int i = j; i < n; ++i) {
         const float p = Ps[i * (DC + 1) + j];
-#pragma unroll
-        for (int x = 0; x < CPT; ++x) pd[x] += p * dOs[i * OP + cc + x];
+        const f32x4 o = *reinterpret_cast<const f32x4*>(dOs + i * OP + cc);
+        pd[0] += p * o.x;
+        pd[1] += p * o.y;
+        pd[2] += p * o.z;
+        pd[3] += p * o.w;
       }
-      float* du = dubuf + unit * DC * DD + (size_t)j * DD + cbase + cc;
-#pragma unroll
-      for (int x = 0; x < CPT; ++x) {
-        const float v = En[j] * kd[x] + scale * pd[x];
-        dUs[j * OP + cc + x] = v;
-        du[x] = v;
-      }
+      const f32x4 v = {En[j] * kd[0] + scale * pd[0], En[j] * kd[1] + scale * pd[1],
+                       En[j] * kd[2] + scale * pd[2], En[j] * kd[3] + scale * pd[3]};
+      *reinterpret_cast<f32x4*>(dUs + j * OP + cc) = v;
+      *reinterpret_cast<f32x4*>(dubuf + unit * DC * DD + (size_t)j * DD + cbase + cc) = v;
     }
     __syncthreads();
     // dS_0 = gamma_C dS + sum_i (scale gamma_i dO_i q_i^T - dU_i w_i^T):
@@ -631,7 +637,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_rscan_kernel(
       for (int y = 0; y < 2; ++y)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float* p = dSs + c * LP + l4 + 64 * y + e;
+          float* p = dSs + c * SP + l4 + 64 * y + e;
           *p = gc * *p + acc[4 * y + e];
         }
     }
@@ -1356,15 +1362,16 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_scan_kernel(
     const int* __restrict__ seg_off, float* __restrict__ records, bf16* __restrict__ out,
     float* __restrict__ states) {
   constexpr int SL = DD / SLICE;
-  constexpr int OP = SLICE + 1;
-  __shared__ float Ss[SLICE * LP];
-  __shared__ float Ws[DC * LP];
-  __shared__ float QHs[DC * LP];
+  constexpr int SP = DD + 4;           // fp32 row pitch, rows 16-byte aligned
+  constexpr int OP = SLICE + 4;        // pitch of the slice-wide tiles, 16-byte aligned
+  __shared__ __attribute__((aligned(16))) float Ss[SLICE * SP];
+  __shared__ __attribute__((aligned(16))) float Ws[DC * SP];
+  __shared__ __attribute__((aligned(16))) float QHs[DC * SP];
   __shared__ __attribute__((aligned(16))) float KHs[DC * DD];   // read a row at a time
   __shared__ float Ps[DC * (DC + 1)];
-  __shared__ float U0s[DC * OP];
-  __shared__ float Us[DC * OP];
-  __shared__ float QSs[DC * OP];
+  __shared__ __attribute__((aligned(16))) float U0s[DC * OP];
+  __shared__ __attribute__((aligned(16))) float Us[DC * OP];
+  __shared__ __attribute__((aligned(16))) float QSs[DC * OP];
   __shared__ __attribute__((aligned(16))) float GCs[DD];
   const int sl = blockIdx.x % SL;
   const int h = (blockIdx.x / SL) % H;
@@ -1378,7 +1385,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_scan_kernel(
   const int tid = threadIdx.x;
   const int cbase = sl * SLICE;
   const size_t rs = (size_t)H * DD;
-  for (int e = tid; e < SLICE * LP; e += SCAN_THREADS) Ss[e] = 0.f;
+  for (int e = tid; e < SLICE * SP; e += SCAN_THREADS) Ss[e] = 0.f;
 
   constexpr int NT = SCAN_THREADS;
   constexpr int WR = DC * DD / 4 / NT, PR = DC * DC / 4 / NT;
@@ -1408,10 +1415,8 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_scan_kernel(
 #pragma unroll
     for (int r = 0; r < WR; ++r) {
       const int f = tid + NT * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
-      Ws[i * LP + c4] = wr[r].x; Ws[i * LP + c4 + 1] = wr[r].y;
-      Ws[i * LP + c4 + 2] = wr[r].z; Ws[i * LP + c4 + 3] = wr[r].w;
-      QHs[i * LP + c4] = qr[r].x; QHs[i * LP + c4 + 1] = qr[r].y;
-      QHs[i * LP + c4 + 2] = qr[r].z; QHs[i * LP + c4 + 3] = qr[r].w;
+      *reinterpret_cast<f32x4*>(Ws + i * SP + c4) = wr[r];
+      *reinterpret_cast<f32x4*>(QHs + i * SP + c4) = qr[r];
       reinterpret_cast<f32x4*>(KHs)[f] = kr[r];
     }
 #pragma unroll
@@ -1424,8 +1429,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_scan_kernel(
     }
     if (tid < DC * SLICE / 4) {
       const int i = tid / (SLICE / 4), c4 = (tid % (SLICE / 4)) * 4;
-      U0s[i * OP + c4] = ur.x; U0s[i * OP + c4 + 1] = ur.y;
-      U0s[i * OP + c4 + 2] = ur.z; U0s[i * OP + c4 + 3] = ur.w;
+      *reinterpret_cast<f32x4*>(U0s + i * OP + c4) = ur;
     }
     if (tid < DD / 4) reinterpret_cast<f32x4*>(GCs)[tid] = gr;
     __syncthreads();
@@ -1436,7 +1440,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_scan_kernel(
 #pragma unroll
       for (int r = 0; r < SLICE * DD / 4 / NT; ++r) {
         const int e4 = tid + NT * r, row = e4 / (DD / 4), c4 = (e4 % (DD / 4)) * 4;
-        const float* src = Ss + row * LP + c4;
+        const float* src = Ss + row * SP + c4;
         *reinterpret_cast<float4*>(st + row * DD + c4) = make_float4(src[0], src[1], src[2], src[3]);
       }
     }
@@ -1445,15 +1449,16 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_scan_kernel(
     constexpr int CPT = DC * SLICE / NT;
     const int i = tid / (SLICE / CPT), cc = (tid % (SLICE / CPT)) * CPT;
     {
+      static_assert(CPT == 4, "a float4 of U per thread");
       float ws[CPT] = {}, qs[CPT] = {};
-      for (int d = 0; d < DD; ++d) {
-        const float w = Ws[i * LP + d];
-        const float qv = QHs[i * LP + d];
+      for (int d = 0; d < DD; d += 4) {   // four columns of d per step, read as vectors
+        const f32x4 w = *reinterpret_cast<const f32x4*>(Ws + i * SP + d);
+        const f32x4 qv = *reinterpret_cast<const f32x4*>(QHs + i * SP + d);
 #pragma unroll
         for (int x = 0; x < CPT; ++x) {
-          const float sv = Ss[(cc + x) * LP + d];
-          ws[x] += w * sv;
-          qs[x] += qv * sv;
+          const f32x4 sv = *reinterpret_cast<const f32x4*>(Ss + (cc + x) * SP + d);
+          ws[x] += w.x * sv.x + w.y * sv.y + w.z * sv.z + w.w * sv.w;
+          qs[x] += qv.x * sv.x + qv.y * sv.y + qv.z * sv.z + qv.w * sv.w;
         }
       }
 #pragma unroll
@@ -1470,13 +1475,15 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_scan_kernel(
     __syncthreads();
     // O = scale (Q_hat S^T + P U) for the chunk's rows inside the document
     if (out && i < n) {
-      float acc[CPT];
-#pragma unroll
-      for (int x = 0; x < CPT; ++x) acc[x] = QSs[i * OP + cc + x];
+      const f32x4 qs = *reinterpret_cast<const f32x4*>(QSs + i * OP + cc);
+      float acc[CPT] = {qs.x, qs.y, qs.z, qs.w};
       for (int j = 0; j <= i; ++j) {
         const float p = Ps[i * (DC + 1) + j];
-#pragma unroll
-        for (int x = 0; x < CPT; ++x) acc[x] += p * Us[j * OP + cc + x];
+        const f32x4 u = *reinterpret_cast<const f32x4*>(Us + j * OP + cc);
+        acc[0] += p * u.x;
+        acc[1] += p * u.y;
+        acc[2] += p * u.z;
+        acc[3] += p * u.w;
       }
       bf16* op = out + (size_t)(c0 + i) * rs + (size_t)h * DD + cbase + cc;
 #pragma unroll
@@ -1504,7 +1511,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_scan_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int d = l4 + 64 * y + e;
-          Ss[c * LP + d] = GCs[d] * Ss[c * LP + d] + acc[4 * y + e];
+          Ss[c * SP + d] = GCs[d] * Ss[c * SP + d] + acc[4 * y + e];
         }
     }
   }
@@ -1530,14 +1537,15 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_rscan_kernel(
     float scale, int chunk_cap, const int* __restrict__ header, const int* __restrict__ seg_off,
     const float* __restrict__ records, float* __restrict__ dstates, float* __restrict__ dubuf) {
   constexpr int SL = DD / SLICE;
-  constexpr int OP = SLICE + 1;
-  __shared__ float dSs[SLICE * LP];
+  constexpr int SP = DD + 4;           // fp32 row pitch, rows 16-byte aligned
+  constexpr int OP = SLICE + 4;        // pitch of the slice-wide tiles, 16-byte aligned
+  __shared__ __attribute__((aligned(16))) float dSs[SLICE * SP];
   __shared__ __attribute__((aligned(16))) float Ws[DC * DD];    // read a row at a time
   __shared__ __attribute__((aligned(16))) float QHs[DC * DD];   // read a row at a time
-  __shared__ float KHs[DC * LP];
+  __shared__ __attribute__((aligned(16))) float KHs[DC * SP];
   __shared__ float Ps[DC * (DC + 1)];
-  __shared__ float dOs[DC * OP];
-  __shared__ float dUs[DC * OP];
+  __shared__ __attribute__((aligned(16))) float dOs[DC * OP];
+  __shared__ __attribute__((aligned(16))) float dUs[DC * OP];
   __shared__ __attribute__((aligned(16))) float GCs[DD];
   const int sl = blockIdx.x % SL;
   const int h = (blockIdx.x / SL) % H;
@@ -1551,7 +1559,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_rscan_kernel(
   const int tid = threadIdx.x;
   const int cbase = sl * SLICE;
   const size_t rs = (size_t)H * DD;
-  for (int e = tid; e < SLICE * LP; e += SCAN_THREADS) dSs[e] = 0.f;
+  for (int e = tid; e < SLICE * SP; e += SCAN_THREADS) dSs[e] = 0.f;
 
   constexpr int NT = SCAN_THREADS;
   constexpr int WR = DC * DD / 4 / NT, PR = DC * DC / 4 / NT;
@@ -1589,8 +1597,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_rscan_kernel(
       const int f = tid + NT * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
       reinterpret_cast<f32x4*>(Ws)[f] = wr[r];
       reinterpret_cast<f32x4*>(QHs)[f] = qr[r];
-      KHs[i * LP + c4] = kr[r].x; KHs[i * LP + c4 + 1] = kr[r].y;
-      KHs[i * LP + c4 + 2] = kr[r].z; KHs[i * LP + c4 + 3] = kr[r].w;
+      *reinterpret_cast<f32x4*>(KHs + i * SP + c4) = kr[r];
     }
 #pragma unroll
     for (int r = 0; r < PR; ++r) {
@@ -1616,7 +1623,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_rscan_kernel(
 #pragma unroll
       for (int r = 0; r < SLICE * DD / 4 / NT; ++r) {
         const int e4 = tid + NT * r, row = e4 / (DD / 4), c4 = (e4 % (DD / 4)) * 4;
-        const float* src = dSs + row * LP + c4;
+        const float* src = dSs + row * SP + c4;
         *reinterpret_cast<float4*>(st + row * DD + c4) = make_float4(src[0], src[1], src[2], src[3]);
       }
     }
@@ -1624,24 +1631,29 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_rscan_kernel(
     constexpr int CPT = DC * SLICE / NT;
     {
       const int j = tid / (SLICE / CPT), cc = (tid % (SLICE / CPT)) * CPT;
+      static_assert(CPT == 4, "a float4 of dU per thread");
       float kd[CPT] = {}, pd[CPT] = {};
-      for (int d = 0; d < DD; ++d) {
-        const float kv = KHs[j * LP + d];
+#pragma unroll 4
+      for (int d = 0; d < DD; d += 4) {   // four columns of d per step, read as vectors
+        const f32x4 kv = *reinterpret_cast<const f32x4*>(KHs + j * SP + d);
 #pragma unroll
-        for (int x = 0; x < CPT; ++x) kd[x] += kv * dSs[(cc + x) * LP + d];
+        for (int x = 0; x < CPT; ++x) {
+          const f32x4 sv = *reinterpret_cast<const f32x4*>(dSs + (cc + x) * SP + d);
+          kd[x] += kv.x * sv.x + kv.y * sv.y + kv.z * sv.z + kv.w * sv.w;
+        }
       }
       for (int i = j; i < n; ++i) {
         const float p = Ps[i * (DC + 1) + j];
-#pragma unroll
-        for (int x = 0; x < CPT; ++x) pd[x] += p * dOs[i * OP + cc + x];
+        const f32x4 o = *reinterpret_cast<const f32x4*>(dOs + i * OP + cc);
+        pd[0] += p * o.x;
+        pd[1] += p * o.y;
+        pd[2] += p * o.z;
+        pd[3] += p * o.w;
       }
-      float* du = dubuf + unit * DC * DD + (size_t)j * DD + cbase + cc;
-#pragma unroll
-      for (int x = 0; x < CPT; ++x) {
-        const float val = kd[x] + scale * pd[x];
-        dUs[j * OP + cc + x] = val;
-        du[x] = val;
-      }
+      const f32x4 val = {kd[0] + scale * pd[0], kd[1] + scale * pd[1], kd[2] + scale * pd[2],
+                         kd[3] + scale * pd[3]};
+      *reinterpret_cast<f32x4*>(dUs + j * OP + cc) = val;
+      *reinterpret_cast<f32x4*>(dubuf + unit * DC * DD + (size_t)j * DD + cbase + cc) = val;
     }
     __syncthreads();
     // dS_0 = dS Diag(gamma_C) + sum_i (scale dO_i q_hat_i^T - dU_i w_i^T)
@@ -1667,7 +1679,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_rscan_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int d = l4 + 64 * y + e;
-          dSs[c * LP + d] = GCs[d] * dSs[c * LP + d] + acc[4 * y + e];
+          dSs[c * SP + d] = GCs[d] * dSs[c * SP + d] + acc[4 * y + e];
         }
     }
   }
