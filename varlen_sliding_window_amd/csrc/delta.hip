@@ -23,6 +23,7 @@
 #include <hip/hip_runtime.h>
 
 #include "common.h"
+#include "device.h"
 #include "launch.h"
 
 namespace attn {
@@ -322,7 +323,12 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
   constexpr int SP = DD + 4;           // fp32 row pitch, rows 16-byte aligned
   constexpr int OP = SLICE + 4;        // pitch of the slice-wide tiles, 16-byte aligned
   __shared__ __attribute__((aligned(16))) float Ss[SLICE * SP];   // S rows c0 .. c0 + SLICE - 1
-  __shared__ __attribute__((aligned(16))) float Ws[DC * SP];
+  // bf16 high and low parts (x = hi + lo to about 16 bits) of S and W, the
+  // MFMA operands of W S^T and Q S^T
+  __shared__ __attribute__((aligned(16))) bf16 Shi[SLICE * BP];
+  __shared__ __attribute__((aligned(16))) bf16 Slo[SLICE * BP];
+  __shared__ __attribute__((aligned(16))) bf16 Whi[DC * BP];
+  __shared__ __attribute__((aligned(16))) bf16 Wlo[DC * BP];
   __shared__ __attribute__((aligned(16))) bf16 Qs[DC * BP];
   __shared__ __attribute__((aligned(16))) bf16 Ks[DC * BP];
   __shared__ float Ps[DC * (DC + 1)];
@@ -344,6 +350,10 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
   const int cbase = sl * SLICE;
   const size_t rs = (size_t)H * DD;
   for (int e = tid; e < SLICE * SP; e += SCAN_THREADS) Ss[e] = 0.f;
+  for (int e = tid; e < SLICE * BP; e += SCAN_THREADS) {
+    Shi[e] = (bf16)0.f;
+    Slo[e] = (bf16)0.f;
+  }
 
   // register staging of one chunk: W, P, q and k rows, the slice of U0 and
   // gamma / end decay, spread over the work-group's threads
@@ -381,7 +391,14 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
 #pragma unroll
     for (int r = 0; r < WR; ++r) {
       const int f = tid + NT * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
-      *reinterpret_cast<f32x4*>(Ws + i * SP + c4) = wr[r];
+      bf16x4 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hi[e] = (bf16)wr[r][e];
+        lo[e] = (bf16)(wr[r][e] - (float)hi[e]);
+      }
+      *reinterpret_cast<bf16x4*>(Whi + i * BP + c4) = hi;
+      *reinterpret_cast<bf16x4*>(Wlo + i * BP + c4) = lo;
     }
 #pragma unroll
     for (int r = 0; r < PR; ++r) {
@@ -416,30 +433,49 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
       }
     }
 
-    // U = U0 - W S^T and Q S^T: thread (row i, CPT slice columns)
-    constexpr int CPT = DC * SLICE / NT;          // columns per thread
+    constexpr int CPT = DC * SLICE / NT;          // O columns per thread
     const int i = tid / (SLICE / CPT), cc = (tid % (SLICE / CPT)) * CPT;
-    {   // four columns of d per step, read as vectors
-      static_assert(CPT == 4, "a float4 of U per thread");
-      float ws[CPT] = {}, qs[CPT] = {};
-      for (int d = 0; d < DD; d += 4) {
-        const float4 w = *reinterpret_cast<const float4*>(Ws + i * SP + d);
-        const bf16x4 qb = *reinterpret_cast<const bf16x4*>(Qs + i * BP + d);
-        const float q0 = (float)qb[0], q1 = (float)qb[1], q2 = (float)qb[2], q3 = (float)qb[3];
+    // U = U0 - W S^T and Q S^T on MFMA: wave w < 4 forms one 32 x 32 tile
+    // (rows 32 (w % 2) .. of U for w < 2, of Q S^T for w >= 2) over the 128
+    // columns of d, W S^T as Whi Shi + Whi Slo + Wlo Shi and Q S^T as
+    // Q Shi + Q Slo (Q is bf16 already)
+    {
+      const int wave = tid >> 6, lane = tid & 63;
+      if (wave < 4) {
+        const int r = lane & 31, hh = lane >> 5, m0 = 32 * (wave & 1);
+        f32x16 acc = {};
 #pragma unroll
-        for (int x = 0; x < CPT; ++x) {
-          const float4 sv = *reinterpret_cast<const float4*>(Ss + (cc + x) * SP + d);
-          ws[x] += w.x * sv.x + w.y * sv.y + w.z * sv.z + w.w * sv.w;
-          qs[x] += q0 * sv.x + q1 * sv.y + q2 * sv.z + q3 * sv.w;
+        for (int ks = 0; ks < DD / 16; ++ks) {
+          const int col = 16 * ks + 8 * hh;
+          const bf16x8 sh = *reinterpret_cast<const bf16x8*>(Shi + r * BP + col);
+          const bf16x8 sl = *reinterpret_cast<const bf16x8*>(Slo + r * BP + col);
+          if (wave < 2) {
+            const bf16x8 wh = *reinterpret_cast<const bf16x8*>(Whi + (m0 + r) * BP + col);
+            const bf16x8 wl = *reinterpret_cast<const bf16x8*>(Wlo + (m0 + r) * BP + col);
+            acc = mfma32(wh, sh, acc);
+            acc = mfma32(wh, sl, acc);
+            acc = mfma32(wl, sh, acc);
+          } else {
+            const bf16x8 qv = *reinterpret_cast<const bf16x8*>(Qs + (m0 + r) * BP + col);
+            acc = mfma32(qv, sh, acc);
+            acc = mfma32(qv, sl, acc);
+          }
+        }
+        // lane (r, hh), register x: row m0 + 8 (x / 4) + 4 hh + x % 4, column r
+        float* urec = states ? records + unit * DeltaRecord::FLOATS + DeltaRecord::U0 + cbase + r
+                             : nullptr;
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+          const int m = m0 + 8 * (x / 4) + 4 * hh + (x % 4);
+          if (wave < 2) {
+            const float u = U0s[m * OP + r] - acc[x];
+            Us[m * OP + r] = u;
+            if (urec) urec[(size_t)m * DD] = u;
+          } else {
+            QSs[m * OP + r] = acc[x];
+          }
         }
       }
-      const float4 u0 = *reinterpret_cast<const float4*>(U0s + i * OP + cc);
-      const float4 u = make_float4(u0.x - ws[0], u0.y - ws[1], u0.z - ws[2], u0.w - ws[3]);
-      *reinterpret_cast<float4*>(Us + i * OP + cc) = u;
-      *reinterpret_cast<float4*>(QSs + i * OP + cc) = make_float4(qs[0], qs[1], qs[2], qs[3]);
-      if (states)
-        *reinterpret_cast<float4*>(records + unit * DeltaRecord::FLOATS + DeltaRecord::U0 +
-                                   (size_t)i * DD + cbase + cc) = u;
     }
     __syncthreads();
     // O = scale (gamma Q S^T + P U) for the chunk's rows inside the document
@@ -473,6 +509,16 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
       // in this chunk came before the last barrier
 #pragma unroll
       for (int y = 0; y < DPT; ++y) Ss[c * SP + d0 + y] = gc * Ss[c * SP + d0 + y] + acc[y];
+      static_assert(DPT == 8, "one bf16x8 of each part per thread");
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int y = 0; y < DPT; ++y) {
+        const float v = Ss[c * SP + d0 + y];
+        hi[y] = (bf16)v;
+        lo[y] = (bf16)(v - (float)hi[y]);
+      }
+      *reinterpret_cast<bf16x8*>(Shi + c * BP + d0) = hi;
+      *reinterpret_cast<bf16x8*>(Slo + c * BP + d0) = lo;
     }
   }
 }
