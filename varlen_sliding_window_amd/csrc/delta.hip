@@ -329,6 +329,12 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
   __shared__ __attribute__((aligned(16))) bf16 Slo[SLICE * BP];
   __shared__ __attribute__((aligned(16))) bf16 Whi[DC * BP];
   __shared__ __attribute__((aligned(16))) bf16 Wlo[DC * BP];
+  // (U diag(e))^T, high and low parts, the A operand of the state update:
+  // row c holds, at position 16 t + 8 h + i, chunk row 16 t + 8 (i / 4) +
+  // 4 h + i % 4, the row order of the transposing reads of K
+  constexpr int UP = DC + 8;
+  __shared__ __attribute__((aligned(16))) bf16 UThi[SLICE * UP];
+  __shared__ __attribute__((aligned(16))) bf16 UTlo[SLICE * UP];
   __shared__ __attribute__((aligned(16))) bf16 Qs[DC * BP];
   __shared__ __attribute__((aligned(16))) bf16 Ks[DC * BP];
   __shared__ float Ps[DC * (DC + 1)];
@@ -471,6 +477,12 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
             const float u = U0s[m * OP + r] - acc[x];
             Us[m * OP + r] = u;
             if (urec) urec[(size_t)m * DD] = u;
+            const float ue = u * En[m];
+            const int jj = m & 15;
+            const int pos = (m & ~15) + 8 * ((jj >> 2) & 1) + 4 * (jj >> 3) + (jj & 3);
+            const bf16 uh = (bf16)ue;
+            UThi[r * UP + pos] = uh;
+            UTlo[r * UP + pos] = (bf16)(ue - (float)uh);
           } else {
             QSs[m * OP + r] = acc[x];
           }
@@ -494,31 +506,40 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
 #pragma unroll
       for (int x = 0; x < CPT; ++x) op[x] = (bf16)(scale * acc[x]);
     }
-    // S_C = gamma_C S + U^T diag(end decay) K: thread (row c, DPT columns of d)
+    // S_C = gamma_C S + U^T diag(end decay) K on MFMA: wave w < 4 forms the
+    // 32 x 32 tile of columns 32 w .. of d over the chunk's 64 rows, as
+    // (U e)^T_hi K + (U e)^T_lo K (K is bf16 already); each lane then updates
+    // its 16 entries of S and their high and low parts
     {
-      constexpr int DPT = SLICE * DD / NT;
-      const int c = tid / (DD / DPT), d0 = (tid % (DD / DPT)) * DPT;
-      float acc[DPT] = {};
-      for (int j = 0; j < n; ++j) {
-        const float u = Us[j * OP + c] * En[j];
+      const int wave = tid >> 6, lane = tid & 63;
+      if (wave < 4) {
+        const int r = lane & 31, hh = lane >> 5, d0 = 32 * wave;
+        f32x16 acc = {};
 #pragma unroll
-        for (int y = 0; y < DPT; ++y) acc[y] += u * (float)Ks[j * BP + d0 + y];
+        for (int t = 0; t < DC / 16; ++t) {
+          const bf16x8 ah = *reinterpret_cast<const bf16x8*>(UThi + r * UP + 16 * t + 8 * hh);
+          const bf16x8 al = *reinterpret_cast<const bf16x8*>(UTlo + r * UP + 16 * t + 8 * hh);
+          const int r0 = 16 * t + 4 * hh + ((lane & 15) >> 2);
+          const int col = d0 + (lane & 16) + 4 * (lane & 3);
+          const bf16x4 b0 = lds_read_tr(Ks + r0 * BP + col);
+          const bf16x4 b1 = lds_read_tr(Ks + (r0 + 8) * BP + col);
+          const bf16x8 kb = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+          acc = mfma32(ah, kb, acc);
+          acc = mfma32(al, kb, acc);
+        }
+        const float gc = Gm[n - 1];
+        // each lane updates only its own entries of S; every read of S in
+        // this chunk came before the last barrier
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+          const int c = 8 * (x / 4) + 4 * hh + (x % 4), d = d0 + r;
+          const float v = gc * Ss[c * SP + d] + acc[x];
+          Ss[c * SP + d] = v;
+          const bf16 vh = (bf16)v;
+          Shi[c * BP + d] = vh;
+          Slo[c * BP + d] = (bf16)(v - (float)vh);
+        }
       }
-      const float gc = Gm[n - 1];
-      // each thread updates only its own entries of S, and every read of S
-      // in this chunk came before the last barrier
-#pragma unroll
-      for (int y = 0; y < DPT; ++y) Ss[c * SP + d0 + y] = gc * Ss[c * SP + d0 + y] + acc[y];
-      static_assert(DPT == 8, "one bf16x8 of each part per thread");
-      bf16x8 hi, lo;
-#pragma unroll
-      for (int y = 0; y < DPT; ++y) {
-        const float v = Ss[c * SP + d0 + y];
-        hi[y] = (bf16)v;
-        lo[y] = (bf16)(v - (float)hi[y]);
-      }
-      *reinterpret_cast<bf16x8*>(Shi + c * BP + d0) = hi;
-      *reinterpret_cast<bf16x8*>(Slo + c * BP + d0) = lo;
     }
   }
 }
