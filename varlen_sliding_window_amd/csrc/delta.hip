@@ -548,7 +548,10 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_scan_kernel(
 // Reverse of the scan: walks a document's chunks from the last for one head
 // and a slice of SLICE d_v rows of dS (the gradient of the state), starting
 // from zero after the document's last token.  Per chunk it stores dS (the
-// end-state gradient) and dU, then steps dS back to the chunk's start.
+// end-state gradient) and dU, then steps dS back to the chunk's start.  The
+// products with the 128-wide rows run on MFMA with fp32 operands split into
+// bf16 high and low parts (about 16 bits): K dS^T for dU, and
+// (scale gamma dO)^T Q - dU^T W for the step.
 __global__ __launch_bounds__(SCAN_THREADS) void delta_rscan_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ dout,
     const int32_t* __restrict__ cu, int nseq, int T, int H, float scale, int chunk_cap,
@@ -558,13 +561,24 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_rscan_kernel(
   constexpr int BP = DD + 8;
   constexpr int SP = DD + 4;           // fp32 row pitch, rows 16-byte aligned
   constexpr int OP = SLICE + 4;        // pitch of the slice-wide tiles, 16-byte aligned
+  constexpr int UP = DC + 8;           // pitch of the transposed chunk-row operands
   __shared__ __attribute__((aligned(16))) float dSs[SLICE * SP];   // dS rows c0 .. c0 + SLICE - 1
-  __shared__ __attribute__((aligned(16))) float Ws[DC * DD];   // read a row at a time
+  __shared__ __attribute__((aligned(16))) bf16 dShi[SLICE * BP];
+  __shared__ __attribute__((aligned(16))) bf16 dSlo[SLICE * BP];
+  __shared__ __attribute__((aligned(16))) bf16 Whi[DC * BP];
+  __shared__ __attribute__((aligned(16))) bf16 Wlo[DC * BP];
   __shared__ __attribute__((aligned(16))) bf16 Qs[DC * BP];
   __shared__ __attribute__((aligned(16))) bf16 Ks[DC * BP];
   __shared__ float Ps[DC * (DC + 1)];
   __shared__ __attribute__((aligned(16))) float dOs[DC * OP];
-  __shared__ __attribute__((aligned(16))) float dUs[DC * OP];
+  __shared__ __attribute__((aligned(16))) float PDs[DC * OP];      // scale P^T dO
+  // A operands of the step, row c holding at position 16 t + 8 h + i chunk
+  // row 16 t + 8 (i / 4) + 4 h + i % 4 (the row order of transposing reads):
+  // (scale gamma dO)^T and -dU^T, high and low parts
+  __shared__ __attribute__((aligned(16))) bf16 Ahi[SLICE * UP];
+  __shared__ __attribute__((aligned(16))) bf16 Alo[SLICE * UP];
+  __shared__ __attribute__((aligned(16))) bf16 Bhi[SLICE * UP];
+  __shared__ __attribute__((aligned(16))) bf16 Blo[SLICE * UP];
   __shared__ float Gm[DC], En[DC];
   const int sl = blockIdx.x % SL;
   const int h = (blockIdx.x / SL) % H;
@@ -576,9 +590,16 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_rscan_kernel(
   const int first = min(seg_off[s], total);
   const int count = max(0, min(seg_off[s + 1], total) - first);
   const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int cbase = sl * SLICE;
   const size_t rs = (size_t)H * DD;
   for (int e = tid; e < SLICE * SP; e += SCAN_THREADS) dSs[e] = 0.f;
+  for (int e = tid; e < SLICE * BP; e += SCAN_THREADS) {
+    dShi[e] = (bf16)0.f;
+    dSlo[e] = (bf16)0.f;
+  }
+  // position of chunk row j in the permuted order of the transposed operands
+  auto perm = [](int j) { const int jj = j & 15; return (j & ~15) + 8 * ((jj >> 2) & 1) + 4 * (jj >> 3) + (jj & 3); };
 
   constexpr int NT = SCAN_THREADS;
   constexpr int WR = DC * DD / 4 / NT, PR = DC * DC / 4 / NT, QR = DC * DD / 8 / NT;
@@ -615,7 +636,17 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_rscan_kernel(
     const int n = min(DC, b - (a + ci * DC));
     __syncthreads();   // every read of the previous chunk's LDS data is done
 #pragma unroll
-    for (int r = 0; r < WR; ++r) reinterpret_cast<f32x4*>(Ws)[tid + NT * r] = wr[r];
+    for (int r = 0; r < WR; ++r) {
+      const int f = tid + NT * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
+      bf16x4 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hi[e] = (bf16)wr[r][e];
+        lo[e] = (bf16)(wr[r][e] - (float)hi[e]);
+      }
+      *reinterpret_cast<bf16x4*>(Whi + i * BP + c4) = hi;
+      *reinterpret_cast<bf16x4*>(Wlo + i * BP + c4) = lo;
+    }
 #pragma unroll
     for (int r = 0; r < PR; ++r) {
       const int f = tid + NT * r, pi = f / (DC / 4), pj = (f % (DC / 4)) * 4;
@@ -640,6 +671,18 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_rscan_kernel(
     if (tid < DC) Gm[tid] = gr;
     else if (tid < 2 * DC) En[tid - DC] = gr;
     __syncthreads();
+    if (tid < OR) {   // (scale gamma dO)^T, from this thread's own dO values
+      const int i = tid / (SLICE / 8), ch = tid % (SLICE / 8);
+      const float gs = scale * Gm[i];
+      const int pi = perm(i);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = gs * dOs[i * OP + ch * 8 + e];
+        const bf16 vh = (bf16)v;
+        Ahi[(ch * 8 + e) * UP + pi] = vh;
+        Alo[(ch * 8 + e) * UP + pi] = (bf16)(v - (float)vh);
+      }
+    }
     if (ci > 0) fetch(ci - 1);
     const size_t unit = (size_t)(first + ci) * H + h;
     {   // the end-state gradient of this chunk, this slice's rows
@@ -651,21 +694,12 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_rscan_kernel(
         *reinterpret_cast<float4*>(st + row * DD + c4) = make_float4(src[0], src[1], src[2], src[3]);
       }
     }
-    // dU = scale P^T dO + diag(end decay) K dS^T: thread (row j, CPT columns)
+    // scale P^T dO: thread (row j, CPT columns)
     constexpr int CPT = DC * SLICE / NT;
     {
+      static_assert(CPT == 4, "a float4 per thread");
       const int j = tid / (SLICE / CPT), cc = (tid % (SLICE / CPT)) * CPT;
-      static_assert(CPT == 4, "a float4 of dU per thread");
-      float kd[CPT] = {}, pd[CPT] = {};
-      for (int d = 0; d < DD; d += 4) {   // four columns of d per step, read as vectors
-        const bf16x4 kb = *reinterpret_cast<const bf16x4*>(Ks + j * BP + d);
-        const float k0 = (float)kb[0], k1 = (float)kb[1], k2 = (float)kb[2], k3 = (float)kb[3];
-#pragma unroll
-        for (int x = 0; x < CPT; ++x) {
-          const f32x4 sv = *reinterpret_cast<const f32x4*>(dSs + (cc + x) * SP + d);
-          kd[x] += k0 * sv.x + k1 * sv.y + k2 * sv.z + k3 * sv.w;
-        }
-      }
+      float pd[CPT] = {};
       for (int i = j; i < n; ++i) {
         const float p = Ps[i * (DC + 1) + j];
         const f32x4 o = *reinterpret_cast<const f32x4*>(dOs + i * OP + cc);
@@ -674,39 +708,75 @@ __global__ __launch_bounds__(SCAN_THREADS) void delta_rscan_kernel(
         pd[2] += p * o.z;
         pd[3] += p * o.w;
       }
-      const f32x4 v = {En[j] * kd[0] + scale * pd[0], En[j] * kd[1] + scale * pd[1],
-                       En[j] * kd[2] + scale * pd[2], En[j] * kd[3] + scale * pd[3]};
-      *reinterpret_cast<f32x4*>(dUs + j * OP + cc) = v;
-      *reinterpret_cast<f32x4*>(dubuf + unit * DC * DD + (size_t)j * DD + cbase + cc) = v;
+      *reinterpret_cast<f32x4*>(PDs + j * OP + cc) =
+          f32x4{scale * pd[0], scale * pd[1], scale * pd[2], scale * pd[3]};
     }
     __syncthreads();
-    // dS_0 = gamma_C dS + sum_i (scale gamma_i dO_i q_i^T - dU_i w_i^T):
-    // thread (row c, DPT columns of d)
-    {   // thread (row c, two groups of 4 columns 64 apart): a wave's lanes read adjacent 16 bytes
-      static_assert(SLICE * DD / NT == 8 && DD == 128, "8 columns per thread");
-      const int c = tid / 16, l4 = (tid % 16) * 4;
-      float acc[8] = {};
-      for (int i = 0; i < n; ++i) {
-        const float a1 = scale * Gm[i] * dOs[i * OP + c];
-        const float a2 = dUs[i * OP + c];
+    // dU = diag(e) K dS^T + scale P^T dO: wave w < 2 forms rows 32 w .. on MFMA
+    // (K bf16, dS in high and low parts); stores dU and -dU^T
+    if (wave < 2) {
+      const int r = lane & 31, hh = lane >> 5, m0 = 32 * wave;
+      f32x16 acc = {};
 #pragma unroll
-        for (int y = 0; y < 2; ++y) {
-          const float4 w = *reinterpret_cast<const float4*>(Ws + i * DD + l4 + 64 * y);
-          const bf16x4 qv = *reinterpret_cast<const bf16x4*>(Qs + i * BP + l4 + 64 * y);
-          acc[4 * y] += a1 * (float)qv[0] - a2 * w.x;
-          acc[4 * y + 1] += a1 * (float)qv[1] - a2 * w.y;
-          acc[4 * y + 2] += a1 * (float)qv[2] - a2 * w.z;
-          acc[4 * y + 3] += a1 * (float)qv[3] - a2 * w.w;
-        }
+      for (int ks = 0; ks < DD / 16; ++ks) {
+        const int col = 16 * ks + 8 * hh;
+        const bf16x8 kv = *reinterpret_cast<const bf16x8*>(Ks + (m0 + r) * BP + col);
+        const bf16x8 sh = *reinterpret_cast<const bf16x8*>(dShi + r * BP + col);
+        const bf16x8 sl_ = *reinterpret_cast<const bf16x8*>(dSlo + r * BP + col);
+        acc = mfma32(kv, sh, acc);
+        acc = mfma32(kv, sl_, acc);
+      }
+      float* du = dubuf + unit * DC * DD + cbase + r;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int j = m0 + 8 * (x / 4) + 4 * hh + (x % 4);
+        const float v = En[j] * acc[x] + PDs[j * OP + r];
+        du[(size_t)j * DD] = v;
+        const float nv = -v;
+        const bf16 vh = (bf16)nv;
+        Bhi[r * UP + perm(j)] = vh;
+        Blo[r * UP + perm(j)] = (bf16)(nv - (float)vh);
+      }
+    }
+    __syncthreads();
+    // dS_0 = gamma_C dS + (scale gamma dO)^T Q - dU^T W: wave w < 4 forms the
+    // 32 x 32 tile of columns 32 w .. of d on MFMA, then updates its entries
+    if (wave < 4) {
+      const int r = lane & 31, hh = lane >> 5, d0 = 32 * wave;
+      f32x16 acc = {};
+#pragma unroll
+      for (int t = 0; t < DC / 16; ++t) {
+        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(Ahi + r * UP + 16 * t + 8 * hh);
+        const bf16x8 al = *reinterpret_cast<const bf16x8*>(Alo + r * UP + 16 * t + 8 * hh);
+        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(Bhi + r * UP + 16 * t + 8 * hh);
+        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(Blo + r * UP + 16 * t + 8 * hh);
+        const int r0 = 16 * t + 4 * hh + ((lane & 15) >> 2);
+        const int col = d0 + (lane & 16) + 4 * (lane & 3);
+        const bf16x8 qv = __builtin_shufflevector(lds_read_tr(Qs + r0 * BP + col),
+                                                  lds_read_tr(Qs + (r0 + 8) * BP + col),
+                                                  0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 wh = __builtin_shufflevector(lds_read_tr(Whi + r0 * BP + col),
+                                                  lds_read_tr(Whi + (r0 + 8) * BP + col),
+                                                  0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 wl = __builtin_shufflevector(lds_read_tr(Wlo + r0 * BP + col),
+                                                  lds_read_tr(Wlo + (r0 + 8) * BP + col),
+                                                  0, 1, 2, 3, 4, 5, 6, 7);
+        acc = mfma32(ah, qv, acc);
+        acc = mfma32(al, qv, acc);
+        acc = mfma32(bh, wh, acc);
+        acc = mfma32(bh, wl, acc);
+        acc = mfma32(bl, wh, acc);
       }
       const float gc = Gm[n - 1];
 #pragma unroll
-      for (int y = 0; y < 2; ++y)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float* p = dSs + c * SP + l4 + 64 * y + e;
-          *p = gc * *p + acc[4 * y + e];
-        }
+      for (int x = 0; x < 16; ++x) {
+        const int c = 8 * (x / 4) + 4 * hh + (x % 4), d = d0 + r;
+        const float v = gc * dSs[c * SP + d] + acc[x];
+        dSs[c * SP + d] = v;
+        const bf16 vh = (bf16)v;
+        dShi[c * BP + d] = vh;
+        dSlo[c * BP + d] = (bf16)(v - (float)vh);
+      }
     }
   }
 }
