@@ -1494,21 +1494,33 @@ __global__ __launch_bounds__(PREP_THREADS) void kda_prep_kernel(
 // Walks a document's chunks for one head and a slice of SLICE d_v rows of S,
 // as delta_scan_kernel does, with the decays folded into the record:
 // U = U0 - W S^T, O = scale (Q_hat S^T + P U), S <- S Diag(gamma_C) + U^T K_hat.
+// W S^T, Q_hat S^T and U^T K_hat run on MFMA with the fp32 operands in bf16
+// high and low parts (three products each); K_hat is staged where W was once
+// W S^T is done.
 __global__ __launch_bounds__(SCAN_THREADS) void kda_scan_kernel(
     const int32_t* __restrict__ cu, int nseq, int T, int H, float scale,
     const int* __restrict__ seg_off, float* __restrict__ records, bf16* __restrict__ out,
     float* __restrict__ states) {
   constexpr int SL = DD / SLICE;
+  constexpr int BP = DD + 8;           // bf16 row pitch
   constexpr int SP = DD + 4;           // fp32 row pitch, rows 16-byte aligned
   constexpr int OP = SLICE + 4;        // pitch of the slice-wide tiles, 16-byte aligned
+  constexpr int UP = DC + 8;           // pitch of the transposed chunk-row operand
   __shared__ __attribute__((aligned(16))) float Ss[SLICE * SP];
-  __shared__ __attribute__((aligned(16))) float Ws[DC * SP];
-  __shared__ __attribute__((aligned(16))) float QHs[DC * SP];
-  __shared__ __attribute__((aligned(16))) float KHs[DC * DD];   // read a row at a time
+  __shared__ __attribute__((aligned(16))) bf16 Shi[SLICE * BP];
+  __shared__ __attribute__((aligned(16))) bf16 Slo[SLICE * BP];
+  __shared__ __attribute__((aligned(16))) bf16 Xhi[DC * BP];    // W, then K_hat
+  __shared__ __attribute__((aligned(16))) bf16 Xlo[DC * BP];
+  __shared__ __attribute__((aligned(16))) bf16 QHhi[DC * BP];
+  __shared__ __attribute__((aligned(16))) bf16 QHlo[DC * BP];
   __shared__ float Ps[DC * (DC + 1)];
   __shared__ __attribute__((aligned(16))) float U0s[DC * OP];
   __shared__ __attribute__((aligned(16))) float Us[DC * OP];
   __shared__ __attribute__((aligned(16))) float QSs[DC * OP];
+  // U^T, high and low parts, row c holding at position 16 t + 8 h + i chunk
+  // row 16 t + 8 (i / 4) + 4 h + i % 4 (the row order of transposing reads)
+  __shared__ __attribute__((aligned(16))) bf16 UThi[SLICE * UP];
+  __shared__ __attribute__((aligned(16))) bf16 UTlo[SLICE * UP];
   __shared__ __attribute__((aligned(16))) float GCs[DD];
   const int sl = blockIdx.x % SL;
   const int h = (blockIdx.x / SL) % H;
@@ -1520,22 +1532,38 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_scan_kernel(
   const int first = min(seg_off[s], total);
   const int count = max(0, min(seg_off[s + 1], total) - first);
   const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int cbase = sl * SLICE;
   const size_t rs = (size_t)H * DD;
   for (int e = tid; e < SLICE * SP; e += SCAN_THREADS) Ss[e] = 0.f;
+  for (int e = tid; e < SLICE * BP; e += SCAN_THREADS) {
+    Shi[e] = (bf16)0.f;
+    Slo[e] = (bf16)0.f;
+  }
+  auto perm = [](int j) { const int jj = j & 15; return (j & ~15) + 8 * ((jj >> 2) & 1) + 4 * (jj >> 3) + (jj & 3); };
+  // high and low bf16 parts of 4 floats into two tiles
+  auto split4 = [](f32x4 v, bf16* hi, bf16* lo) __attribute__((always_inline)) {
+    bf16x4 h4, l4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      h4[e] = (bf16)v[e];
+      l4[e] = (bf16)(v[e] - (float)h4[e]);
+    }
+    *reinterpret_cast<bf16x4*>(hi) = h4;
+    *reinterpret_cast<bf16x4*>(lo) = l4;
+  };
 
   constexpr int NT = SCAN_THREADS;
   constexpr int WR = DC * DD / 4 / NT, PR = DC * DC / 4 / NT;
   f32x4 wr[WR], qr[WR], kr[WR], pr[PR];
   f32x4 ur = {0.f, 0.f, 0.f, 0.f}, gr = {0.f, 0.f, 0.f, 0.f};
-  auto fetch = [&](int ci) __attribute__((always_inline)) {
-    const f32x4* r4 = reinterpret_cast<const f32x4*>(
-        records + ((size_t)(first + ci) * H + h) * KdaRecord::FLOATS);
+  auto recp = [&](int ci) { return reinterpret_cast<const f32x4*>(records + ((size_t)(first + ci) * H + h) * KdaRecord::FLOATS); };
+  auto fetch_a = [&](int ci) __attribute__((always_inline)) {
+    const f32x4* r4 = recp(ci);
 #pragma unroll
     for (int r = 0; r < WR; ++r) {
       wr[r] = r4[KdaRecord::W / 4 + tid + NT * r];
       qr[r] = r4[KdaRecord::QH / 4 + tid + NT * r];
-      kr[r] = r4[KdaRecord::KH / 4 + tid + NT * r];
     }
 #pragma unroll
     for (int r = 0; r < PR; ++r) pr[r] = r4[KdaRecord::P / 4 + tid + NT * r];
@@ -1543,7 +1571,15 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_scan_kernel(
       ur = r4[(KdaRecord::U0 + (size_t)(tid / (SLICE / 4)) * DD + cbase) / 4 + (tid % (SLICE / 4))];
     if (tid < DD / 4) gr = r4[KdaRecord::GC / 4 + tid];
   };
-  if (count > 0) fetch(0);
+  auto fetch_b = [&](int ci) __attribute__((always_inline)) {
+    const f32x4* r4 = recp(ci);
+#pragma unroll
+    for (int r = 0; r < WR; ++r) kr[r] = r4[KdaRecord::KH / 4 + tid + NT * r];
+  };
+  if (count > 0) {
+    fetch_a(0);
+    fetch_b(0);
+  }
 
   for (int ci = 0; ci < count; ++ci) {
     const int c0 = a + ci * DC;
@@ -1552,9 +1588,8 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_scan_kernel(
 #pragma unroll
     for (int r = 0; r < WR; ++r) {
       const int f = tid + NT * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
-      *reinterpret_cast<f32x4*>(Ws + i * SP + c4) = wr[r];
-      *reinterpret_cast<f32x4*>(QHs + i * SP + c4) = qr[r];
-      reinterpret_cast<f32x4*>(KHs)[f] = kr[r];
+      split4(wr[r], Xhi + i * BP + c4, Xlo + i * BP + c4);
+      split4(qr[r], QHhi + i * BP + c4, QHlo + i * BP + c4);
     }
 #pragma unroll
     for (int r = 0; r < PR; ++r) {
@@ -1570,7 +1605,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_scan_kernel(
     }
     if (tid < DD / 4) reinterpret_cast<f32x4*>(GCs)[tid] = gr;
     __syncthreads();
-    if (ci + 1 < count) fetch(ci + 1);
+    if (ci + 1 < count) fetch_a(ci + 1);
     const size_t unit = (size_t)(first + ci) * H + h;
     if (states) {   // this slice's rows of the chunk's start state
       float* st = states + unit * DD * DD + (size_t)cbase * DD;
@@ -1581,36 +1616,50 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_scan_kernel(
         *reinterpret_cast<float4*>(st + row * DD + c4) = make_float4(src[0], src[1], src[2], src[3]);
       }
     }
-
-    // U = U0 - W S^T and Q_hat S^T: thread (row i, CPT slice columns)
-    constexpr int CPT = DC * SLICE / NT;
-    const int i = tid / (SLICE / CPT), cc = (tid % (SLICE / CPT)) * CPT;
-    {
-      static_assert(CPT == 4, "a float4 of U per thread");
-      float ws[CPT] = {}, qs[CPT] = {};
-      for (int d = 0; d < DD; d += 4) {   // four columns of d per step, read as vectors
-        const f32x4 w = *reinterpret_cast<const f32x4*>(Ws + i * SP + d);
-        const f32x4 qv = *reinterpret_cast<const f32x4*>(QHs + i * SP + d);
+    // U = U0 - W S^T (waves 0, 1) and Q_hat S^T (waves 2, 3), 32 rows each
+    if (wave < 4) {
+      const int r = lane & 31, hh = lane >> 5, m0 = 32 * (wave & 1);
+      const bf16* Ah = wave < 2 ? Xhi : QHhi;
+      const bf16* Al = wave < 2 ? Xlo : QHlo;
+      f32x16 acc = {};
 #pragma unroll
-        for (int x = 0; x < CPT; ++x) {
-          const f32x4 sv = *reinterpret_cast<const f32x4*>(Ss + (cc + x) * SP + d);
-          ws[x] += w.x * sv.x + w.y * sv.y + w.z * sv.z + w.w * sv.w;
-          qs[x] += qv.x * sv.x + qv.y * sv.y + qv.z * sv.z + qv.w * sv.w;
+      for (int ks = 0; ks < DD / 16; ++ks) {
+        const int col = 16 * ks + 8 * hh;
+        const bf16x8 sh = *reinterpret_cast<const bf16x8*>(Shi + r * BP + col);
+        const bf16x8 sl_ = *reinterpret_cast<const bf16x8*>(Slo + r * BP + col);
+        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(Ah + (m0 + r) * BP + col);
+        const bf16x8 al = *reinterpret_cast<const bf16x8*>(Al + (m0 + r) * BP + col);
+        acc = mfma32(ah, sh, acc);
+        acc = mfma32(ah, sl_, acc);
+        acc = mfma32(al, sh, acc);
+      }
+      float* urec = states ? records + unit * KdaRecord::FLOATS + KdaRecord::U0 + cbase + r : nullptr;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int m = m0 + 8 * (x / 4) + 4 * hh + (x % 4);
+        if (wave < 2) {
+          const float u = U0s[m * OP + r] - acc[x];
+          Us[m * OP + r] = u;
+          if (urec) urec[(size_t)m * DD] = u;
+          const bf16 uh = (bf16)u;
+          UThi[r * UP + perm(m)] = uh;
+          UTlo[r * UP + perm(m)] = (bf16)(u - (float)uh);
+        } else {
+          QSs[m * OP + r] = acc[x];
         }
       }
-#pragma unroll
-      for (int x = 0; x < CPT; ++x) {
-        Us[i * OP + cc + x] = U0s[i * OP + cc + x] - ws[x];
-        QSs[i * OP + cc + x] = qs[x];
-      }
-      if (states) {
-        float* urec = records + unit * KdaRecord::FLOATS + KdaRecord::U0 + (size_t)i * DD + cbase + cc;
-#pragma unroll
-        for (int x = 0; x < CPT; ++x) urec[x] = U0s[i * OP + cc + x] - ws[x];
-      }
     }
+    __syncthreads();   // W is no longer read: K_hat goes where it was
+#pragma unroll
+    for (int r = 0; r < WR; ++r) {
+      const int f = tid + NT * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
+      split4(kr[r], Xhi + i * BP + c4, Xlo + i * BP + c4);
+    }
+    if (ci + 1 < count) fetch_b(ci + 1);
     __syncthreads();
     // O = scale (Q_hat S^T + P U) for the chunk's rows inside the document
+    constexpr int CPT = DC * SLICE / NT;
+    const int i = tid / (SLICE / CPT), cc = (tid % (SLICE / CPT)) * CPT;
     if (out && i < n) {
       const f32x4 qs = *reinterpret_cast<const f32x4*>(QSs + i * OP + cc);
       float acc[CPT] = {qs.x, qs.y, qs.z, qs.w};
@@ -1626,30 +1675,35 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_scan_kernel(
 #pragma unroll
       for (int x = 0; x < CPT; ++x) op[x] = (bf16)(scale * acc[x]);
     }
-    // S <- S Diag(gamma_C) + U^T K_hat: thread (row c, two groups of 4
-    // columns 64 apart), each thread its own entries of S
-    {
-      static_assert(SLICE * DD / NT == 8 && DD == 128, "8 columns per thread");
-      const int c = tid / 16, l4 = (tid % 16) * 4;
-      float acc[8] = {};
-      for (int j = 0; j < n; ++j) {
-        const float u = Us[j * OP + c];
+    // S <- S Diag(gamma_C) + U^T K_hat: wave w < 4 forms columns 32 w .. of d
+    if (wave < 4) {
+      const int r = lane & 31, hh = lane >> 5, d0 = 32 * wave;
+      f32x16 acc = {};
 #pragma unroll
-        for (int y = 0; y < 2; ++y) {
-          const float4 kh = *reinterpret_cast<const float4*>(KHs + j * DD + l4 + 64 * y);
-          acc[4 * y] += u * kh.x;
-          acc[4 * y + 1] += u * kh.y;
-          acc[4 * y + 2] += u * kh.z;
-          acc[4 * y + 3] += u * kh.w;
-        }
+      for (int t = 0; t < DC / 16; ++t) {
+        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(UThi + r * UP + 16 * t + 8 * hh);
+        const bf16x8 al = *reinterpret_cast<const bf16x8*>(UTlo + r * UP + 16 * t + 8 * hh);
+        const int r0 = 16 * t + 4 * hh + ((lane & 15) >> 2);
+        const int col = d0 + (lane & 16) + 4 * (lane & 3);
+        const bf16x8 kh = __builtin_shufflevector(lds_read_tr(Xhi + r0 * BP + col),
+                                                  lds_read_tr(Xhi + (r0 + 8) * BP + col),
+                                                  0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 kl = __builtin_shufflevector(lds_read_tr(Xlo + r0 * BP + col),
+                                                  lds_read_tr(Xlo + (r0 + 8) * BP + col),
+                                                  0, 1, 2, 3, 4, 5, 6, 7);
+        acc = mfma32(ah, kh, acc);
+        acc = mfma32(ah, kl, acc);
+        acc = mfma32(al, kh, acc);
       }
 #pragma unroll
-      for (int y = 0; y < 2; ++y)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int d = l4 + 64 * y + e;
-          Ss[c * SP + d] = GCs[d] * Ss[c * SP + d] + acc[4 * y + e];
-        }
+      for (int x = 0; x < 16; ++x) {
+        const int c = 8 * (x / 4) + 4 * hh + (x % 4), d = d0 + r;
+        const float v = GCs[d] * Ss[c * SP + d] + acc[x];
+        Ss[c * SP + d] = v;
+        const bf16 vh = (bf16)v;
+        Shi[c * BP + d] = vh;
+        Slo[c * BP + d] = (bf16)(v - (float)vh);
+      }
     }
   }
 }
