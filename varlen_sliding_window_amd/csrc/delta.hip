@@ -1728,15 +1728,26 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_rscan_kernel(
     float scale, int chunk_cap, const int* __restrict__ header, const int* __restrict__ seg_off,
     const float* __restrict__ records, float* __restrict__ dstates, float* __restrict__ dubuf) {
   constexpr int SL = DD / SLICE;
+  constexpr int BP = DD + 8;           // bf16 row pitch
   constexpr int SP = DD + 4;           // fp32 row pitch, rows 16-byte aligned
   constexpr int OP = SLICE + 4;        // pitch of the slice-wide tiles, 16-byte aligned
+  constexpr int UP = DC + 8;           // pitch of the transposed chunk-row operands
   __shared__ __attribute__((aligned(16))) float dSs[SLICE * SP];
-  __shared__ __attribute__((aligned(16))) float Ws[DC * DD];    // read a row at a time
-  __shared__ __attribute__((aligned(16))) float QHs[DC * DD];   // read a row at a time
-  __shared__ __attribute__((aligned(16))) float KHs[DC * SP];
+  __shared__ __attribute__((aligned(16))) bf16 dShi[SLICE * BP];
+  __shared__ __attribute__((aligned(16))) bf16 dSlo[SLICE * BP];
+  __shared__ __attribute__((aligned(16))) bf16 Xhi[DC * BP];    // K_hat, then W
+  __shared__ __attribute__((aligned(16))) bf16 Xlo[DC * BP];
+  __shared__ __attribute__((aligned(16))) bf16 QHhi[DC * BP];
+  __shared__ __attribute__((aligned(16))) bf16 QHlo[DC * BP];
   __shared__ float Ps[DC * (DC + 1)];
   __shared__ __attribute__((aligned(16))) float dOs[DC * OP];
-  __shared__ __attribute__((aligned(16))) float dUs[DC * OP];
+  __shared__ __attribute__((aligned(16))) float PDs[DC * OP];   // scale P^T dO
+  // A operands of the step, row c holding at position 16 t + 8 h + i chunk
+  // row 16 t + 8 (i / 4) + 4 h + i % 4: dO^T (bf16 already) and -dU^T
+  // (high and low parts)
+  __shared__ __attribute__((aligned(16))) bf16 OT[SLICE * UP];
+  __shared__ __attribute__((aligned(16))) bf16 Bhi[SLICE * UP];
+  __shared__ __attribute__((aligned(16))) bf16 Blo[SLICE * UP];
   __shared__ __attribute__((aligned(16))) float GCs[DD];
   const int sl = blockIdx.x % SL;
   const int h = (blockIdx.x / SL) % H;
@@ -1748,9 +1759,25 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_rscan_kernel(
   const int first = min(seg_off[s], total);
   const int count = max(0, min(seg_off[s + 1], total) - first);
   const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int cbase = sl * SLICE;
   const size_t rs = (size_t)H * DD;
   for (int e = tid; e < SLICE * SP; e += SCAN_THREADS) dSs[e] = 0.f;
+  for (int e = tid; e < SLICE * BP; e += SCAN_THREADS) {
+    dShi[e] = (bf16)0.f;
+    dSlo[e] = (bf16)0.f;
+  }
+  auto perm = [](int j) { const int jj = j & 15; return (j & ~15) + 8 * ((jj >> 2) & 1) + 4 * (jj >> 3) + (jj & 3); };
+  auto split4 = [](f32x4 v, bf16* hi, bf16* lo) __attribute__((always_inline)) {
+    bf16x4 h4, l4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      h4[e] = (bf16)v[e];
+      l4[e] = (bf16)(v[e] - (float)h4[e]);
+    }
+    *reinterpret_cast<bf16x4*>(hi) = h4;
+    *reinterpret_cast<bf16x4*>(lo) = l4;
+  };
 
   constexpr int NT = SCAN_THREADS;
   constexpr int WR = DC * DD / 4 / NT, PR = DC * DC / 4 / NT;
@@ -1758,14 +1785,13 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_rscan_kernel(
   f32x4 wr[WR], qr[WR], kr[WR], pr[PR];
   f32x4 gr = {0.f, 0.f, 0.f, 0.f};
   u32x4 dor = {0u, 0u, 0u, 0u};
-  auto fetch = [&](int ci) __attribute__((always_inline)) {
+  auto recp = [&](int ci) { return reinterpret_cast<const f32x4*>(records + ((size_t)(first + ci) * H + h) * KdaRecord::FLOATS); };
+  auto fetch_a = [&](int ci) __attribute__((always_inline)) {   // all but W
     const int c0 = a + ci * DC;
     const int n = min(DC, b - c0);
-    const f32x4* r4 = reinterpret_cast<const f32x4*>(
-        records + ((size_t)(first + ci) * H + h) * KdaRecord::FLOATS);
+    const f32x4* r4 = recp(ci);
 #pragma unroll
     for (int r = 0; r < WR; ++r) {
-      wr[r] = r4[KdaRecord::W / 4 + tid + NT * r];
       qr[r] = r4[KdaRecord::QH / 4 + tid + NT * r];
       kr[r] = r4[KdaRecord::KH / 4 + tid + NT * r];
     }
@@ -1778,7 +1804,15 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_rscan_kernel(
     }
     if (tid < DD / 4) gr = r4[KdaRecord::GC / 4 + tid];
   };
-  if (count > 0) fetch(count - 1);
+  auto fetch_b = [&](int ci) __attribute__((always_inline)) {   // W
+    const f32x4* r4 = recp(ci);
+#pragma unroll
+    for (int r = 0; r < WR; ++r) wr[r] = r4[KdaRecord::W / 4 + tid + NT * r];
+  };
+  if (count > 0) {
+    fetch_a(count - 1);
+    fetch_b(count - 1);
+  }
 
   for (int ci = count - 1; ci >= 0; --ci) {
     const int n = min(DC, b - (a + ci * DC));
@@ -1786,9 +1820,8 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_rscan_kernel(
 #pragma unroll
     for (int r = 0; r < WR; ++r) {
       const int f = tid + NT * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
-      reinterpret_cast<f32x4*>(Ws)[f] = wr[r];
-      reinterpret_cast<f32x4*>(QHs)[f] = qr[r];
-      *reinterpret_cast<f32x4*>(KHs + i * SP + c4) = kr[r];
+      split4(kr[r], Xhi + i * BP + c4, Xlo + i * BP + c4);
+      split4(qr[r], QHhi + i * BP + c4, QHlo + i * BP + c4);
     }
 #pragma unroll
     for (int r = 0; r < PR; ++r) {
@@ -1802,12 +1835,16 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_rscan_kernel(
       const int i = tid / (SLICE / 8), ch = tid % (SLICE / 8);
       bf16x8 ov;
       __builtin_memcpy(&ov, &dor, sizeof(ov));
+      const int pi = perm(i);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dOs[i * OP + ch * 8 + e] = (float)ov[e];
+      for (int e = 0; e < 8; ++e) {
+        dOs[i * OP + ch * 8 + e] = (float)ov[e];
+        OT[(ch * 8 + e) * UP + pi] = ov[e];
+      }
     }
     if (tid < DD / 4) reinterpret_cast<f32x4*>(GCs)[tid] = gr;
     __syncthreads();
-    if (ci > 0) fetch(ci - 1);
+    if (ci > 0) fetch_a(ci - 1);
     const size_t unit = (size_t)(first + ci) * H + h;
     {   // the end-state gradient of this chunk, this slice's rows
       float* st = dstates + unit * DD * DD + (size_t)cbase * DD;
@@ -1818,21 +1855,12 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_rscan_kernel(
         *reinterpret_cast<float4*>(st + row * DD + c4) = make_float4(src[0], src[1], src[2], src[3]);
       }
     }
-    // dU = scale P^T dO + K_hat dS^T: thread (row j, CPT columns)
+    // scale P^T dO: thread (row j, CPT columns)
     constexpr int CPT = DC * SLICE / NT;
     {
+      static_assert(CPT == 4, "a float4 per thread");
       const int j = tid / (SLICE / CPT), cc = (tid % (SLICE / CPT)) * CPT;
-      static_assert(CPT == 4, "a float4 of dU per thread");
-      float kd[CPT] = {}, pd[CPT] = {};
-#pragma unroll 4
-      for (int d = 0; d < DD; d += 4) {   // four columns of d per step, read as vectors
-        const f32x4 kv = *reinterpret_cast<const f32x4*>(KHs + j * SP + d);
-#pragma unroll
-        for (int x = 0; x < CPT; ++x) {
-          const f32x4 sv = *reinterpret_cast<const f32x4*>(dSs + (cc + x) * SP + d);
-          kd[x] += kv.x * sv.x + kv.y * sv.y + kv.z * sv.z + kv.w * sv.w;
-        }
-      }
+      float pd[CPT] = {};
       for (int i = j; i < n; ++i) {
         const float p = Ps[i * (DC + 1) + j];
         const f32x4 o = *reinterpret_cast<const f32x4*>(dOs + i * OP + cc);
@@ -1841,37 +1869,85 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_rscan_kernel(
         pd[2] += p * o.z;
         pd[3] += p * o.w;
       }
-      const f32x4 val = {kd[0] + scale * pd[0], kd[1] + scale * pd[1], kd[2] + scale * pd[2],
-                         kd[3] + scale * pd[3]};
-      *reinterpret_cast<f32x4*>(dUs + j * OP + cc) = val;
-      *reinterpret_cast<f32x4*>(dubuf + unit * DC * DD + (size_t)j * DD + cbase + cc) = val;
+      *reinterpret_cast<f32x4*>(PDs + j * OP + cc) =
+          f32x4{scale * pd[0], scale * pd[1], scale * pd[2], scale * pd[3]};
     }
     __syncthreads();
-    // dS_0 = dS Diag(gamma_C) + sum_i (scale dO_i q_hat_i^T - dU_i w_i^T)
-    {
-      static_assert(SLICE * DD / NT == 8 && DD == 128, "8 columns per thread");
-      const int c = tid / 16, l4 = (tid % 16) * 4;
-      float acc[8] = {};
-      for (int i = 0; i < n; ++i) {
-        const float a1 = scale * dOs[i * OP + c];
-        const float a2 = dUs[i * OP + c];
+    // dU = K_hat dS^T + scale P^T dO: wave w < 2 forms rows 32 w .. on MFMA;
+    // stores dU and -dU^T
+    if (wave < 2) {
+      const int r = lane & 31, hh = lane >> 5, m0 = 32 * wave;
+      f32x16 acc = {};
 #pragma unroll
-        for (int y = 0; y < 2; ++y) {
-          const float4 w = *reinterpret_cast<const float4*>(Ws + i * DD + l4 + 64 * y);
-          const float4 qh = *reinterpret_cast<const float4*>(QHs + i * DD + l4 + 64 * y);
-          acc[4 * y] += a1 * qh.x - a2 * w.x;
-          acc[4 * y + 1] += a1 * qh.y - a2 * w.y;
-          acc[4 * y + 2] += a1 * qh.z - a2 * w.z;
-          acc[4 * y + 3] += a1 * qh.w - a2 * w.w;
-        }
+      for (int ks = 0; ks < DD / 16; ++ks) {
+        const int col = 16 * ks + 8 * hh;
+        const bf16x8 kh = *reinterpret_cast<const bf16x8*>(Xhi + (m0 + r) * BP + col);
+        const bf16x8 kl = *reinterpret_cast<const bf16x8*>(Xlo + (m0 + r) * BP + col);
+        const bf16x8 sh = *reinterpret_cast<const bf16x8*>(dShi + r * BP + col);
+        const bf16x8 sl_ = *reinterpret_cast<const bf16x8*>(dSlo + r * BP + col);
+        acc = mfma32(kh, sh, acc);
+        acc = mfma32(kh, sl_, acc);
+        acc = mfma32(kl, sh, acc);
+      }
+      float* du = dubuf + unit * DC * DD + cbase + r;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int j = m0 + 8 * (x / 4) + 4 * hh + (x % 4);
+        const float v = acc[x] + PDs[j * OP + r];
+        du[(size_t)j * DD] = v;
+        const float nv = -v;
+        const bf16 vh = (bf16)nv;
+        Bhi[r * UP + perm(j)] = vh;
+        Blo[r * UP + perm(j)] = (bf16)(nv - (float)vh);
+      }
+    }
+    __syncthreads();   // K_hat is no longer read: W goes where it was
+#pragma unroll
+    for (int r = 0; r < WR; ++r) {
+      const int f = tid + NT * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
+      split4(wr[r], Xhi + i * BP + c4, Xlo + i * BP + c4);
+    }
+    if (ci > 0) fetch_b(ci - 1);
+    __syncthreads();
+    // dS_0 = dS Diag(gamma_C) + scale dO^T Q_hat - dU^T W: wave w < 4 forms
+    // the 32 x 32 tile of columns 32 w .. of d on MFMA, then updates its entries
+    if (wave < 4) {
+      const int r = lane & 31, hh = lane >> 5, d0 = 32 * wave;
+      f32x16 aq = {}, aw = {};
+#pragma unroll
+      for (int t = 0; t < DC / 16; ++t) {
+        const bf16x8 ot = *reinterpret_cast<const bf16x8*>(OT + r * UP + 16 * t + 8 * hh);
+        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(Bhi + r * UP + 16 * t + 8 * hh);
+        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(Blo + r * UP + 16 * t + 8 * hh);
+        const int r0 = 16 * t + 4 * hh + ((lane & 15) >> 2);
+        const int col = d0 + (lane & 16) + 4 * (lane & 3);
+        const bf16x8 qh = __builtin_shufflevector(lds_read_tr(QHhi + r0 * BP + col),
+                                                  lds_read_tr(QHhi + (r0 + 8) * BP + col),
+                                                  0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 ql = __builtin_shufflevector(lds_read_tr(QHlo + r0 * BP + col),
+                                                  lds_read_tr(QHlo + (r0 + 8) * BP + col),
+                                                  0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 wh = __builtin_shufflevector(lds_read_tr(Xhi + r0 * BP + col),
+                                                  lds_read_tr(Xhi + (r0 + 8) * BP + col),
+                                                  0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 wl = __builtin_shufflevector(lds_read_tr(Xlo + r0 * BP + col),
+                                                  lds_read_tr(Xlo + (r0 + 8) * BP + col),
+                                                  0, 1, 2, 3, 4, 5, 6, 7);
+        aq = mfma32(ot, qh, aq);
+        aq = mfma32(ot, ql, aq);
+        aw = mfma32(bh, wh, aw);
+        aw = mfma32(bh, wl, aw);
+        aw = mfma32(bl, wh, aw);
       }
 #pragma unroll
-      for (int y = 0; y < 2; ++y)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int d = l4 + 64 * y + e;
-          dSs[c * SP + d] = GCs[d] * dSs[c * SP + d] + acc[4 * y + e];
-        }
+      for (int x = 0; x < 16; ++x) {
+        const int c = 8 * (x / 4) + 4 * hh + (x % 4), d = d0 + r;
+        const float v = GCs[d] * dSs[c * SP + d] + scale * aq[x] + aw[x];
+        dSs[c * SP + d] = v;
+        const bf16 vh = (bf16)v;
+        dShi[c * BP + d] = vh;
+        dSlo[c * BP + d] = (bf16)(v - (float)vh);
+      }
     }
   }
 }
