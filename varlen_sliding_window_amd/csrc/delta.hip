@@ -800,26 +800,126 @@ __device__ __forceinline__ void delta_chunk_span(const int32_t* __restrict__ cu,
 constexpr int GRAD_THREADS = 512;
 constexpr int GR = DC / (GRAD_THREADS / 16);   // rows per thread of the per-chunk tiles (16 threads a row group)
 
+// The three state products of one (chunk, head) on MFMA, shared by both
+// gates: wave w of GRAD_THREADS forms rows 32 (w / 4) .., columns 32 (w % 4) ..
+// of aq = dO S_0, aw = dU S_0 and ak = U dS_C ([DC][DD] each, summed over the
+// DD rows of the states).  dO (bf16) and the high and low parts of dU and U
+// are staged once with the columns of every 16-block permuted into the row
+// order of transposing reads; S_0 and dS_C stream through LDS 16 rows at a
+// time as high and low parts.  colsum(c4, ss) receives, per staging step,
+// the products of this thread's four state entries (columns c4 .. c4 + 3).
+struct StateProductsLds {
+  static constexpr int AP = DD + 8, RB = 16;
+  bf16 dO[DC * AP], dUh[DC * AP], dUl[DC * AP], Uh[DC * AP], Ul[DC * AP];
+  bf16 Sh[RB * AP], Sl[RB * AP], Dh[RB * AP], Dl[RB * AP];
+};
+
+__device__ __forceinline__ int delta_perm16(int j) {
+  const int jj = j & 15;
+  return (j & ~15) + 8 * ((jj >> 2) & 1) + 4 * (jj >> 3) + (jj & 3);
+}
+
+template <class ColSum>
+__device__ __forceinline__ void delta_state_products(
+    StateProductsLds& L, const bf16* __restrict__ dout, size_t dout_off, size_t rs, int n,
+    const float* __restrict__ U, const float* __restrict__ dU, const float* __restrict__ S0,
+    const float* __restrict__ dS, int tid, f32x16& aq, f32x16& aw, f32x16& ak, ColSum&& colsum) {
+  constexpr int AP = StateProductsLds::AP, RB = StateProductsLds::RB;
+  static_assert(GRAD_THREADS == 8 * 64 && RB * DD / 4 == GRAD_THREADS, "eight waves, one float4 per step");
+  // dO rows (16 bytes = 8 columns per thread and pass), columns permuted
+#pragma unroll
+  for (int r = 0; r < DC * DD / 8 / GRAD_THREADS; ++r) {
+    const int f = tid + GRAD_THREADS * r, i = f / (DD / 8), c8 = (f % (DD / 8)) * 8;
+    bf16x8 v = {};
+    if (i < n) v = *reinterpret_cast<const bf16x8*>(dout + dout_off + (size_t)i * rs + c8);
+    const int p0 = delta_perm16(c8);   // columns c8 .. c8 + 3 -> p0 .., c8 + 4 .. -> p0 + 8 ..
+    *reinterpret_cast<bf16x4*>(L.dO + i * AP + p0) = __builtin_shufflevector(v, v, 0, 1, 2, 3);
+    *reinterpret_cast<bf16x4*>(L.dO + i * AP + p0 + 8) = __builtin_shufflevector(v, v, 4, 5, 6, 7);
+  }
+  // U and dU rows (4 columns per thread and pass), high and low parts, permuted
+#pragma unroll
+  for (int r = 0; r < DC * DD / 4 / GRAD_THREADS; ++r) {
+    const int f = tid + GRAD_THREADS * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
+    const f32x4 u = reinterpret_cast<const f32x4*>(U)[f];
+    const f32x4 du = reinterpret_cast<const f32x4*>(dU)[f];
+    const int p = delta_perm16(c4);
+    bf16x4 uh, ul, dh, dl;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uh[e] = (bf16)u[e];
+      ul[e] = (bf16)(u[e] - (float)uh[e]);
+      dh[e] = (bf16)du[e];
+      dl[e] = (bf16)(du[e] - (float)dh[e]);
+    }
+    *reinterpret_cast<bf16x4*>(L.Uh + i * AP + p) = uh;
+    *reinterpret_cast<bf16x4*>(L.Ul + i * AP + p) = ul;
+    *reinterpret_cast<bf16x4*>(L.dUh + i * AP + p) = dh;
+    *reinterpret_cast<bf16x4*>(L.dUl + i * AP + p) = dl;
+  }
+  const int wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 31, hh = lane >> 5, m0 = 32 * (wave >> 2), d0 = 32 * (wave & 3);
+  const int srow = tid / (DD / 4), sc4 = (tid % (DD / 4)) * 4;
+  aq = f32x16{};
+  aw = f32x16{};
+  ak = f32x16{};
+  for (int kb = 0; kb < DD / RB; ++kb) {
+    __syncthreads();
+    {
+      const f32x4 sv = reinterpret_cast<const f32x4*>(S0 + (size_t)kb * RB * DD)[tid];
+      const f32x4 dv = reinterpret_cast<const f32x4*>(dS + (size_t)kb * RB * DD)[tid];
+      bf16x4 sh, sl, dh, dl;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sh[e] = (bf16)sv[e];
+        sl[e] = (bf16)(sv[e] - (float)sh[e]);
+        dh[e] = (bf16)dv[e];
+        dl[e] = (bf16)(dv[e] - (float)dh[e]);
+      }
+      *reinterpret_cast<bf16x4*>(L.Sh + srow * AP + sc4) = sh;
+      *reinterpret_cast<bf16x4*>(L.Sl + srow * AP + sc4) = sl;
+      *reinterpret_cast<bf16x4*>(L.Dh + srow * AP + sc4) = dh;
+      *reinterpret_cast<bf16x4*>(L.Dl + srow * AP + sc4) = dl;
+      colsum(sc4, f32x4{sv[0] * dv[0], sv[1] * dv[1], sv[2] * dv[2], sv[3] * dv[3]});
+    }
+    __syncthreads();
+    const int col = 16 * kb + 8 * hh;
+    const bf16x8 ao = *reinterpret_cast<const bf16x8*>(L.dO + (m0 + r) * AP + col);
+    const bf16x8 adh = *reinterpret_cast<const bf16x8*>(L.dUh + (m0 + r) * AP + col);
+    const bf16x8 adl = *reinterpret_cast<const bf16x8*>(L.dUl + (m0 + r) * AP + col);
+    const bf16x8 auh = *reinterpret_cast<const bf16x8*>(L.Uh + (m0 + r) * AP + col);
+    const bf16x8 aul = *reinterpret_cast<const bf16x8*>(L.Ul + (m0 + r) * AP + col);
+    const int r0 = 4 * hh + ((lane & 15) >> 2);
+    const int bc = d0 + (lane & 16) + 4 * (lane & 3);
+    auto trb = [&](const bf16* t) {
+      return __builtin_shufflevector(lds_read_tr(t + r0 * AP + bc), lds_read_tr(t + (r0 + 8) * AP + bc),
+                                     0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    const bf16x8 bsh = trb(L.Sh), bsl = trb(L.Sl), bdh = trb(L.Dh), bdl = trb(L.Dl);
+    aq = mfma32(ao, bsh, aq);
+    aq = mfma32(ao, bsl, aq);
+    aw = mfma32(adh, bsh, aw);
+    aw = mfma32(adh, bsl, aw);
+    aw = mfma32(adl, bsh, aw);
+    ak = mfma32(auh, bdh, ak);
+    ak = mfma32(auh, bdl, ak);
+    ak = mfma32(aul, bdh, ak);
+  }
+}
+
 // Products with the chunk's start state S_0 and end-state gradient dS_C, per
-// (chunk, head): dQ_state = scale diag(gamma) dO S_0, dW = -dU S_0,
-// dK_state = diag(e) U dS_C, and the decay gradients they imply.  S_0 and
-// dS_C stream through LDS 16 rows at a time; thread (4 rows, 8 columns).
-// dQ_state and dK_state go over this unit's dS_C once it has been read, dW
-// to its own buffer (the saved records stay as the forward left them).
+// (chunk, head), on MFMA (delta_state_products): dQ_state = scale diag(gamma)
+// dO S_0, dW = -dU S_0, dK_state = diag(e) U dS_C, and the decay gradients
+// they imply (q_i . (dO S_0)_i, k_i . (U dS_C)_i, <dS_C, S_0>).  dQ_state and
+// dK_state go over this unit's dS_C once it has been read, dW to its own
+// buffer (the saved records stay as the forward left them).
 __global__ __launch_bounds__(GRAD_THREADS) void delta_gstate_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ dout,
     const int32_t* __restrict__ cu, int nseq, int T, int H, float scale, int chunk_cap,
     const int* __restrict__ header, const int* __restrict__ seg_off, float* __restrict__ records,
     const float* __restrict__ states, float* __restrict__ dstates,
     const float* __restrict__ dubuf, float* __restrict__ dwbuf) {
-  constexpr int BP = DD + 8;
-  constexpr int RB = 16;   // state rows per staging step
-  __shared__ __attribute__((aligned(16))) bf16 dOs[DC * BP];
-  __shared__ float Us[DC * LP];
-  __shared__ float dUs[DC * LP];
-  __shared__ __attribute__((aligned(16))) float S0b[RB * DD];
-  __shared__ __attribute__((aligned(16))) float dSb[RB * DD];
-  __shared__ float red[GRAD_THREADS / 64];
+  __shared__ __attribute__((aligned(16))) StateProductsLds L;
+  __shared__ float qsd[DC], kdv[DC], red[GRAD_THREADS / 64];
   const int chunk = blockIdx.x / H, h = blockIdx.x - chunk * H;
   if (chunk >= header[0] || !delta_saved_for(header, T, H, chunk_cap)) return;
   int c0, n;
@@ -828,107 +928,51 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_gstate_kernel(
   const size_t rs = (size_t)H * DD;
   const size_t unit = blockIdx.x;
   float* rec = records + unit * DeltaRecord::FLOATS;
-  const float* S0 = states + unit * DD * DD;
   float* dS = dstates + unit * DD * DD;
-  const float* dU = dubuf + unit * DC * DD;
-#pragma unroll
-  for (int r = 0; r < DC * DD / 8 / GRAD_THREADS; ++r) {
-    const int f = tid + GRAD_THREADS * r, i = f / (DD / 8), ch = f % (DD / 8);
-    const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + ch * 8;
-    *reinterpret_cast<u32x4*>(dOs + i * BP + ch * 8) =
-        i < n ? *reinterpret_cast<const u32x4*>(dout + off) : u32x4{0u, 0u, 0u, 0u};
+  if (tid < DC) {
+    qsd[tid] = 0.f;
+    kdv[tid] = 0.f;
   }
-#pragma unroll
-  for (int r = 0; r < DC * DD / 4 / GRAD_THREADS; ++r) {
-    const int f = tid + GRAD_THREADS * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
-    const float4 u = reinterpret_cast<const float4*>(rec + DeltaRecord::U0)[f];
-    const float4 du = reinterpret_cast<const float4*>(dU)[f];
-    Us[i * LP + c4] = u.x; Us[i * LP + c4 + 1] = u.y; Us[i * LP + c4 + 2] = u.z; Us[i * LP + c4 + 3] = u.w;
-    dUs[i * LP + c4] = du.x; dUs[i * LP + c4 + 1] = du.y; dUs[i * LP + c4 + 2] = du.z; dUs[i * LP + c4 + 3] = du.w;
-  }
-  const int i0 = (tid / 16) * GR, d8 = (tid % 16) * 8;
-  float aq[GR][8] = {}, aw[GR][8] = {}, ak[GR][8] = {};
   float dgc = 0.f;   // <dS_C, S_0>, this thread's share
-  for (int cb = 0; cb < DD; cb += RB) {
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < RB * DD / 4 / GRAD_THREADS; ++r) {
-      const int f = tid + GRAD_THREADS * r;
-      const float4 s4 = reinterpret_cast<const float4*>(S0 + (size_t)cb * DD)[f];
-      const float4 d4 = reinterpret_cast<const float4*>(dS + (size_t)cb * DD)[f];
-      reinterpret_cast<float4*>(S0b)[f] = s4;
-      reinterpret_cast<float4*>(dSb)[f] = d4;
-      dgc += s4.x * d4.x + s4.y * d4.y + s4.z * d4.z + s4.w * d4.w;
-    }
-    __syncthreads();
-    for (int c = 0; c < RB; ++c) {
-      const float4 sa = *reinterpret_cast<const float4*>(S0b + c * DD + d8);
-      const float4 sb = *reinterpret_cast<const float4*>(S0b + c * DD + d8 + 4);
-      const float4 ta = *reinterpret_cast<const float4*>(dSb + c * DD + d8);
-      const float4 tb = *reinterpret_cast<const float4*>(dSb + c * DD + d8 + 4);
-      const float s0[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
-      const float ds[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
-#pragma unroll
-      for (int x = 0; x < GR; ++x) {
-        const float o = (float)dOs[(i0 + x) * BP + cb + c];
-        const float du = dUs[(i0 + x) * LP + cb + c];
-        const float u = Us[(i0 + x) * LP + cb + c];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          aq[x][e] += o * s0[e];
-          aw[x][e] += du * s0[e];
-          ak[x][e] += u * ds[e];
-        }
-      }
-    }
-  }
+  f32x16 aq, aw, ak;
+  delta_state_products(L, dout, (size_t)c0 * rs + (size_t)h * DD, rs, n,
+                       rec + DeltaRecord::U0, dubuf + unit * DC * DD, states + unit * DD * DD, dS,
+                       tid, aq, aw, ak,
+                       [&](int, f32x4 p) { dgc += (p[0] + p[1]) + (p[2] + p[3]); });
   __syncthreads();   // every read of this unit's dS_C is done before it is overwritten
-  // row dots q_i . (dO S_0)_i and k_i . (U dS_C)_i, summed over the 16 lanes of a row group
-  float qsd[GR], kd[GR];
-#pragma unroll
-  for (int x = 0; x < GR; ++x) {
-    const int i = i0 + x;
-    qsd[x] = 0.f;
-    kd[x] = 0.f;
-    if (i < n) {
-      const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + d8;
-      const bf16x8 qv = *reinterpret_cast<const bf16x8*>(q + off);
-      const bf16x8 kv = *reinterpret_cast<const bf16x8*>(k + off);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        qsd[x] += (float)qv[e] * aq[x][e];
-        kd[x] += (float)kv[e] * ak[x][e];
-      }
-    }
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-      qsd[x] += __shfl_xor(qsd[x], off);
-      kd[x] += __shfl_xor(kd[x], off);
-    }
-  }
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) dgc += __shfl_xor(dgc, off);
-  if ((tid & 63) == 0) red[tid >> 6] = dgc;
-  __syncthreads();
+  const int wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 31, hh = lane >> 5, m0 = 32 * (wave >> 2), d = 32 * (wave & 3) + r;
   const float* gam = rec + DeltaRecord::GAM;
   const float* en = rec + DeltaRecord::END;
 #pragma unroll
-  for (int x = 0; x < GR; ++x) {
-    const int i = i0 + x;
-    const float gq = scale * gam[i], ek = en[i];
-    float4* pq = reinterpret_cast<float4*>(dS + (size_t)i * DD + d8);
-    float4* pk = reinterpret_cast<float4*>(dS + (size_t)DC * DD + (size_t)i * DD + d8);
-    float4* pw = reinterpret_cast<float4*>(dwbuf + unit * DC * DD + (size_t)i * DD + d8);
-    pq[0] = make_float4(gq * aq[x][0], gq * aq[x][1], gq * aq[x][2], gq * aq[x][3]);
-    pq[1] = make_float4(gq * aq[x][4], gq * aq[x][5], gq * aq[x][6], gq * aq[x][7]);
-    pk[0] = make_float4(ek * ak[x][0], ek * ak[x][1], ek * ak[x][2], ek * ak[x][3]);
-    pk[1] = make_float4(ek * ak[x][4], ek * ak[x][5], ek * ak[x][6], ek * ak[x][7]);
-    pw[0] = make_float4(-aw[x][0], -aw[x][1], -aw[x][2], -aw[x][3]);
-    pw[1] = make_float4(-aw[x][4], -aw[x][5], -aw[x][6], -aw[x][7]);
-    if ((tid & 15) == 0) {
-      rec[DeltaRecord::SIDE + i] = gq * qsd[x];          // gamma_i d(gamma_i), output term
-      rec[DeltaRecord::SIDE + DC + i] = ek * kd[x];      // e_i d(e_i)
+  for (int x = 0; x < 16; ++x) {
+    const int i = m0 + 8 * (x / 4) + 4 * hh + (x % 4);
+    dS[(size_t)i * DD + d] = scale * gam[i] * aq[x];
+    dS[(size_t)DC * DD + (size_t)i * DD + d] = en[i] * ak[x];
+    dwbuf[unit * DC * DD + (size_t)i * DD + d] = -aw[x];
+    float pq = 0.f, pk = 0.f;
+    if (i < n) {
+      const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + d;
+      pq = (float)q[off] * aq[x];
+      pk = (float)k[off] * ak[x];
     }
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {   // over the 32 columns of this lane half
+      pq += __shfl_xor(pq, o);
+      pk += __shfl_xor(pk, o);
+    }
+    if (r == 0) {
+      atomicAdd(&qsd[i], pq);
+      atomicAdd(&kdv[i], pk);
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) dgc += __shfl_xor(dgc, o);
+  if (lane == 0) red[wave] = dgc;
+  __syncthreads();
+  if (tid < DC) {
+    rec[DeltaRecord::SIDE + tid] = scale * gam[tid] * qsd[tid];   // gamma_i d(gamma_i), output term
+    rec[DeltaRecord::SIDE + DC + tid] = en[tid] * kdv[tid];        // e_i d(e_i)
   }
   if (tid == 0) {   // gamma_C d(gamma_C) of the end state
     float tot = 0.f;
@@ -1952,22 +1996,16 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_rscan_kernel(
   }
 }
 
-// State products per (chunk, head): dQ_hat = scale dO S_0 and dK_hat = U dS_C
-// over this unit's dS_C once read, dW = -dU S_0 to its buffer, and
-// gamma_C o (column sums of dS_C o S_0) into the record's side values.
+// State products per (chunk, head) on MFMA (delta_state_products):
+// dQ_hat = scale dO S_0 and dK_hat = U dS_C over this unit's dS_C once read,
+// dW = -dU S_0 to its buffer, and gamma_C o (column sums of dS_C o S_0) into
+// the record's side values.
 __global__ __launch_bounds__(GRAD_THREADS) void kda_gstate_kernel(
     const bf16* __restrict__ dout, const int32_t* __restrict__ cu, int nseq, int T, int H,
     float scale, int chunk_cap, const int* __restrict__ header, const int* __restrict__ seg_off,
     float* __restrict__ records, const float* __restrict__ states, float* __restrict__ dstates,
     const float* __restrict__ dubuf, float* __restrict__ dwbuf) {
-  constexpr int BP = DD + 8;
-  constexpr int RB = 16;
-  static_assert(RB * DD / 4 == GRAD_THREADS, "one float4 of each state per thread and step");
-  __shared__ __attribute__((aligned(16))) bf16 dOs[DC * BP];
-  __shared__ float Us[DC * LP];
-  __shared__ float dUs[DC * LP];
-  __shared__ __attribute__((aligned(16))) float S0b[RB * DD];
-  __shared__ __attribute__((aligned(16))) float dSb[RB * DD];
+  __shared__ __attribute__((aligned(16))) StateProductsLds L;
   __shared__ float dgc[DD];
   const int chunk = blockIdx.x / H, h = blockIdx.x - chunk * H;
   if (chunk >= header[0] || !delta_saved_for(header, T, H, chunk_cap)) return;
@@ -1977,75 +2015,28 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gstate_kernel(
   const size_t rs = (size_t)H * DD;
   const size_t unit = blockIdx.x;
   float* rec = records + unit * KdaRecord::FLOATS;
-  const float* S0 = states + unit * DD * DD;
   float* dS = dstates + unit * DD * DD;
-  const float* dU = dubuf + unit * DC * DD;
-#pragma unroll
-  for (int r = 0; r < DC * DD / 8 / GRAD_THREADS; ++r) {
-    const int f = tid + GRAD_THREADS * r, i = f / (DD / 8), ch = f % (DD / 8);
-    const size_t off = (size_t)(c0 + i) * rs + (size_t)h * DD + ch * 8;
-    *reinterpret_cast<u32x4*>(dOs + i * BP + ch * 8) =
-        i < n ? *reinterpret_cast<const u32x4*>(dout + off) : u32x4{0u, 0u, 0u, 0u};
-  }
-#pragma unroll
-  for (int r = 0; r < DC * DD / 4 / GRAD_THREADS; ++r) {
-    const int f = tid + GRAD_THREADS * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
-    const float4 u = reinterpret_cast<const float4*>(rec + KdaRecord::U0)[f];
-    const float4 du = reinterpret_cast<const float4*>(dU)[f];
-    Us[i * LP + c4] = u.x; Us[i * LP + c4 + 1] = u.y; Us[i * LP + c4 + 2] = u.z; Us[i * LP + c4 + 3] = u.w;
-    dUs[i * LP + c4] = du.x; dUs[i * LP + c4 + 1] = du.y; dUs[i * LP + c4 + 2] = du.z; dUs[i * LP + c4 + 3] = du.w;
-  }
   if (tid < DD) dgc[tid] = 0.f;
-  const int i0 = (tid / 16) * GR, d8 = (tid % 16) * 8;
-  const int sc4 = (tid % (DD / 4)) * 4;   // the state columns this thread stages
-  float aq[GR][8] = {}, aw[GR][8] = {}, ak[GR][8] = {};
-  float cs[4] = {};
-  for (int cb = 0; cb < DD; cb += RB) {
-    __syncthreads();
-    {
-      const float4 s4 = reinterpret_cast<const float4*>(S0 + (size_t)cb * DD)[tid];
-      const float4 d4 = reinterpret_cast<const float4*>(dS + (size_t)cb * DD)[tid];
-      reinterpret_cast<float4*>(S0b)[tid] = s4;
-      reinterpret_cast<float4*>(dSb)[tid] = d4;
-      cs[0] += s4.x * d4.x; cs[1] += s4.y * d4.y; cs[2] += s4.z * d4.z; cs[3] += s4.w * d4.w;
-    }
-    __syncthreads();
-    for (int c = 0; c < RB; ++c) {
-      const float4 sa = *reinterpret_cast<const float4*>(S0b + c * DD + d8);
-      const float4 sb = *reinterpret_cast<const float4*>(S0b + c * DD + d8 + 4);
-      const float4 ta = *reinterpret_cast<const float4*>(dSb + c * DD + d8);
-      const float4 tb = *reinterpret_cast<const float4*>(dSb + c * DD + d8 + 4);
-      const float s0[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
-      const float ds[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
-#pragma unroll
-      for (int x = 0; x < GR; ++x) {
-        const float o = (float)dOs[(i0 + x) * BP + cb + c];
-        const float du = dUs[(i0 + x) * LP + cb + c];
-        const float u = Us[(i0 + x) * LP + cb + c];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          aq[x][e] += o * s0[e];
-          aw[x][e] += du * s0[e];
-          ak[x][e] += u * ds[e];
-        }
-      }
-    }
-  }
+  f32x4 cs = {0.f, 0.f, 0.f, 0.f};   // column sums of dS_C o S_0, this thread's four columns
+  int csc = 0;
+  f32x16 aq, aw, ak;
+  delta_state_products(L, dout, (size_t)c0 * rs + (size_t)h * DD, rs, n,
+                       rec + KdaRecord::U0, dubuf + unit * DC * DD, states + unit * DD * DD, dS,
+                       tid, aq, aw, ak, [&](int c4, f32x4 p) {
+                         cs += p;
+                         csc = c4;
+                       });
   __syncthreads();   // every read of this unit's dS_C is done before it is overwritten
 #pragma unroll
-  for (int e = 0; e < 4; ++e) atomicAdd(&dgc[sc4 + e], cs[e]);
+  for (int e = 0; e < 4; ++e) atomicAdd(&dgc[csc + e], cs[e]);
+  const int wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 31, hh = lane >> 5, m0 = 32 * (wave >> 2), d = 32 * (wave & 3) + r;
 #pragma unroll
-  for (int x = 0; x < GR; ++x) {
-    const int i = i0 + x;
-    float4* pq = reinterpret_cast<float4*>(dS + (size_t)i * DD + d8);
-    float4* pk = reinterpret_cast<float4*>(dS + (size_t)DC * DD + (size_t)i * DD + d8);
-    float4* pw = reinterpret_cast<float4*>(dwbuf + unit * DC * DD + (size_t)i * DD + d8);
-    pq[0] = make_float4(scale * aq[x][0], scale * aq[x][1], scale * aq[x][2], scale * aq[x][3]);
-    pq[1] = make_float4(scale * aq[x][4], scale * aq[x][5], scale * aq[x][6], scale * aq[x][7]);
-    pk[0] = make_float4(ak[x][0], ak[x][1], ak[x][2], ak[x][3]);
-    pk[1] = make_float4(ak[x][4], ak[x][5], ak[x][6], ak[x][7]);
-    pw[0] = make_float4(-aw[x][0], -aw[x][1], -aw[x][2], -aw[x][3]);
-    pw[1] = make_float4(-aw[x][4], -aw[x][5], -aw[x][6], -aw[x][7]);
+  for (int x = 0; x < 16; ++x) {
+    const int i = m0 + 8 * (x / 4) + 4 * hh + (x % 4);
+    dS[(size_t)i * DD + d] = scale * aq[x];
+    dS[(size_t)DC * DD + (size_t)i * DD + d] = ak[x];
+    dwbuf[unit * DC * DD + (size_t)i * DD + d] = -aw[x];
   }
   __syncthreads();
   if (tid < DD) rec[KdaRecord::SIDE + tid] = rec[KdaRecord::GC + tid] * dgc[tid];
