@@ -986,7 +986,10 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_gstate_kernel(
 // masked scores (dP = scale dO U^T), the triangular solve (dX = T^T dW,
 // dY = T^T dU, dT = dW X^T + dU Y^T, dA = -T^T dT T^T below the diagonal,
 // X = diag(beta gamma) K, Y = diag(beta) V) and the log-decay gradients,
-// summed back onto g inside the chunk.
+// summed back onto g inside the chunk.  Every product runs on MFMA, 32 x 32
+// tiles per wave, with fp32 operands split into bf16 high and low parts as
+// their fragments are read (fragment element e of lane half h is index
+// 16 s + 8 h + e of the summed dimension).
 __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const bf16* __restrict__ dout,
@@ -1005,6 +1008,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
   __shared__ float M1[DC * CP], M2[DC * CP];
   __shared__ float Gs[DC], Bs[DC], gm[DC], dGs[DC], dBs[DC];
   static_assert(DC * CP <= DC * BP / 2, "a C x C matrix fits where V was");
+  static_assert(GRAD_THREADS == 512 && DC == 64 && DD == 128, "eight waves of 32 x 32 tiles");
   const int chunk = blockIdx.x / H, h = blockIdx.x - chunk * H;
   if (chunk >= header[0] || !delta_saved_for(header, T, H, chunk_cap)) return;
   int c0, n;
@@ -1050,83 +1054,88 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
     }
   }
   __syncthreads();
-  const int r0 = (tid / 16) * GR, s0 = (tid % 16) * 4;  // C x C tile: rows r0.., columns s0..
-  const int i0 = r0, d8 = (tid % 16) * 8;               // C x D tile: rows i0.., columns d8..
-
-  // dP = scale dO U^T; the decay gradient of the scores P (x) dP; the masked
-  // decayed dP into M1
-  {
-    float dp[GR][4] = {};
-    for (int d = 0; d < DD; ++d) {
-      float o[GR], u[4];
+  const int wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
+  // 8 fp32 values p[e * stride] as bf16 high and low parts
+  auto ld32 = [](const float* p, int stride, bf16x8& hi, bf16x8& lo) __attribute__((always_inline)) {
 #pragma unroll
-      for (int x = 0; x < GR; ++x) o[x] = (float)dOb[(r0 + x) * BP + d];
-#pragma unroll
-      for (int y = 0; y < 4; ++y) u[y] = F1[(s0 + y) * LP + d];
-#pragma unroll
-      for (int x = 0; x < GR; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) dp[x][y] += o[x] * u[y];
+    for (int e = 0; e < 8; ++e) {
+      const float x = p[e * stride];
+      hi[e] = (bf16)x;
+      lo[e] = (bf16)(x - (float)hi[e]);
     }
-    float row[GR] = {}, col[4] = {};
+  };
+  auto ldb = [](const bf16* p, int stride) __attribute__((always_inline)) {
+    bf16x8 o;
 #pragma unroll
-    for (int x = 0; x < GR; ++x)
+    for (int e = 0; e < 8; ++e) o[e] = p[e * stride];
+    return o;
+  };
+  // D layout: register x of lane (r, hh) is row 8 (x / 4) + 4 hh + x % 4, column r
+  auto drow = [hh](int x) { return 8 * (x / 4) + 4 * hh + (x % 4); };
+  // C x C tiles: waves 0..3, rows 32 (w / 2) .., columns 32 (w % 2) ..
+  const int cm0 = 32 * (wave >> 1), cn0 = 32 * (wave & 1);
+  // C x D tiles: all eight waves, rows 32 (w / 4) .., columns 32 (w % 4) ..
+  const int dm0 = 32 * (wave >> 2), dd0 = 32 * (wave & 3);
+
+  // dP = scale dO U^T; the decay gradient of the scores P o dP; the masked
+  // decayed dP into M1
+  if (wave < 4) {
+    f32x16 acc = {};
 #pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        const int i = r0 + x, j = s0 + y;
-        const float dpv = scale * dp[x][y];
-        const float pd = rec[DeltaRecord::P + i * DC + j] * dpv;
-        row[x] += pd;
-        col[y] += pd;
-        M1[i * CP + j] = j <= i ? __expf(Gs[i] - Gs[j]) * dpv : 0.f;
-      }
+    for (int ks = 0; ks < DD / 16; ++ks) {
+      const int kk = 16 * ks + 8 * hh;
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(dOb + (cm0 + r) * BP + kk);
+      bf16x8 bh, bl;
+      ld32(F1 + (cn0 + r) * LP + kk, 1, bh, bl);
+      acc = mfma32(a, bh, acc);
+      acc = mfma32(a, bl, acc);
+    }
+    const int j = cn0 + r;
+    float colsum = 0.f;
 #pragma unroll
-    for (int x = 0; x < GR; ++x) atomicAdd(&dGs[r0 + x], row[x]);
+    for (int x = 0; x < 16; ++x) {
+      const int i = cm0 + drow(x);
+      const float dpv = scale * acc[x];
+      const float pd = rec[DeltaRecord::P + i * DC + j] * dpv;
+      colsum += pd;
+      M1[i * CP + j] = j <= i ? __expf(Gs[i] - Gs[j]) * dpv : 0.f;
+      float rsum = pd;
 #pragma unroll
-    for (int y = 0; y < 4; ++y) atomicAdd(&dGs[s0 + y], -col[y]);
+      for (int o = 1; o < 32; o <<= 1) rsum += __shfl_xor(rsum, o);
+      if (r == 0) atomicAdd(&dGs[i], rsum);
+    }
+    atomicAdd(&dGs[j], -colsum);
   }
   __syncthreads();
-  // dQ = dQ_state + dPm K (written); dK = dK_state + dPm^T Q (kept)
+  // dQ = dQ_state + dPm K (written); dK = dK_state + dPm^T Q (kept in akk)
   const float* gst = dstates + unit * DD * DD;   // dQ_state [C][D], then dK_state [C][D]
-  float dkr[GR][8];
+  f32x16 akk = {};
   {
-    float dqr[GR][8];
+    f32x16 aq = {};
 #pragma unroll
-    for (int x = 0; x < GR; ++x) {
-      const float4* pq = reinterpret_cast<const float4*>(gst + (size_t)(i0 + x) * DD + d8);
-      const float4* pk = reinterpret_cast<const float4*>(gst + (size_t)DC * DD + (size_t)(i0 + x) * DD + d8);
-      const float4 qa = pq[0], qb = pq[1], ka = pk[0], kb = pk[1];
-      dqr[x][0] = qa.x; dqr[x][1] = qa.y; dqr[x][2] = qa.z; dqr[x][3] = qa.w;
-      dqr[x][4] = qb.x; dqr[x][5] = qb.y; dqr[x][6] = qb.z; dqr[x][7] = qb.w;
-      dkr[x][0] = ka.x; dkr[x][1] = ka.y; dkr[x][2] = ka.z; dkr[x][3] = ka.w;
-      dkr[x][4] = kb.x; dkr[x][5] = kb.y; dkr[x][6] = kb.z; dkr[x][7] = kb.w;
+    for (int t = 0; t < DC / 16; ++t) {
+      const int kk = 16 * t + 8 * hh;
+      bf16x8 ah, al, th, tl;
+      ld32(M1 + (dm0 + r) * CP + kk, 1, ah, al);          // dPm[i][j]
+      ld32(M1 + kk * CP + dm0 + r, CP, th, tl);           // dPm[j][i] (transposed)
+      const bf16x8 kb = ldb(Kb + kk * BP + dd0 + r, BP);
+      const bf16x8 qb = ldb(Qb + kk * BP + dd0 + r, BP);
+      aq = mfma32(ah, kb, aq);
+      aq = mfma32(al, kb, aq);
+      akk = mfma32(th, qb, akk);
+      akk = mfma32(tl, qb, akk);
     }
-    for (int j = 0; j < DC; ++j) {
-      const bf16x8 kv = *reinterpret_cast<const bf16x8*>(Kb + j * BP + d8);
-      const bf16x8 qv = *reinterpret_cast<const bf16x8*>(Qb + j * BP + d8);
+    const int d = dd0 + r;
 #pragma unroll
-      for (int x = 0; x < GR; ++x) {
-        const float pa = M1[(i0 + x) * CP + j], pb = M1[j * CP + i0 + x];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          dqr[x][e] += pa * (float)kv[e];
-          dkr[x][e] += pb * (float)qv[e];
-        }
-      }
+    for (int x = 0; x < 16; ++x) {
+      const int i = dm0 + drow(x);
+      if (i < n) dq[(size_t)(c0 + i) * rs + (size_t)h * DD + d] = (bf16)(gst[(size_t)i * DD + d] + aq[x]);
     }
-#pragma unroll
-    for (int x = 0; x < GR; ++x)
-      if (i0 + x < n) {
-        bf16x8 o;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = (bf16)dqr[x][e];
-        *reinterpret_cast<bf16x8*>(dq + (size_t)(c0 + i0 + x) * rs + (size_t)h * DD + d8) = o;
-      }
   }
   __syncthreads();   // U, dO and dPm are no longer read
 #pragma unroll
-  for (int r = 0; r < DC * DD / 4 / GRAD_THREADS; ++r) {
-    const int f = tid + GRAD_THREADS * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
+  for (int rr = 0; rr < DC * DD / 4 / GRAD_THREADS; ++rr) {
+    const int f = tid + GRAD_THREADS * rr, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
     const float4 w = reinterpret_cast<const float4*>(dwbuf + unit * DC * DD)[f];
     const float4 du = reinterpret_cast<const float4*>(dubuf + unit * DC * DD)[f];
     F1[i * LP + c4] = w.x; F1[i * LP + c4 + 1] = w.y; F1[i * LP + c4 + 2] = w.z; F1[i * LP + c4 + 3] = w.w;
@@ -1134,191 +1143,157 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
   }
   for (int f = tid; f < DC * DC; f += GRAD_THREADS) M1[(f / DC) * CP + f % DC] = rec[DeltaRecord::TI + f];
   __syncthreads();
-  // dX = T^T dW, dY = T^T dU (T_ji = 0 for j < i); dV = diag(beta) dY;
-  // dK += diag(beta gamma) dX; the beta and decay gradients through X and Y
+  // dX = T^T dW, dY = T^T dU; dV = diag(beta) dY; dK += diag(beta gamma) dX;
+  // the beta and decay gradients through X and Y
   {
-    float dx[GR][8] = {}, dy[GR][8] = {};
-    for (int j = i0; j < DC; ++j) {
-      float w[8], u[8];
+    f32x16 ax = {}, ay = {};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        w[e] = F1[j * LP + d8 + e];
-        u[e] = F2[j * LP + d8 + e];
+    for (int t = 0; t < DC / 16; ++t) {
+      const int kk = 16 * t + 8 * hh;
+      bf16x8 ah, al, wh, wl, uh, ul;
+      ld32(M1 + kk * CP + dm0 + r, CP, ah, al);           // T[j][i]
+      ld32(F1 + kk * LP + dd0 + r, LP, wh, wl);           // dW[j][d]
+      ld32(F2 + kk * LP + dd0 + r, LP, uh, ul);           // dU[j][d]
+      ax = mfma32(ah, wh, ax);
+      ax = mfma32(ah, wl, ax);
+      ax = mfma32(al, wh, ax);
+      ay = mfma32(ah, uh, ay);
+      ay = mfma32(ah, ul, ay);
+      ay = mfma32(al, uh, ay);
+    }
+    const int d = dd0 + r;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      const int i = dm0 + drow(x);
+      akk[x] += Bs[i] * gm[i] * ax[x];
+      if (i < n) dv[(size_t)(c0 + i) * rs + (size_t)h * DD + d] = (bf16)(Bs[i] * ay[x]);
+      float kdx = (float)Kb[i * BP + d] * ax[x];
+      float vdy = (float)Vb[i * BP + d] * ay[x];
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) {
+        kdx += __shfl_xor(kdx, o);
+        vdy += __shfl_xor(vdy, o);
       }
-#pragma unroll
-      for (int x = 0; x < GR; ++x) {
-        const float t = M1[j * CP + i0 + x];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          dx[x][e] += t * w[e];
-          dy[x][e] += t * u[e];
-        }
+      if (r == 0) {
+        atomicAdd(&dBs[i], gm[i] * kdx + vdy);
+        atomicAdd(&dGs[i], gm[i] * Bs[i] * kdx);
       }
     }
-    float kdx[GR], vdy[GR];
-#pragma unroll
-    for (int x = 0; x < GR; ++x) {
-      const int i = i0 + x;
-      const bf16x8 kv = *reinterpret_cast<const bf16x8*>(Kb + i * BP + d8);
-      const bf16x8 vv = *reinterpret_cast<const bf16x8*>(Vb + i * BP + d8);
-      const float bgi = Bs[i] * gm[i];
-      kdx[x] = 0.f;
-      vdy[x] = 0.f;
-      bf16x8 o;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        kdx[x] += (float)kv[e] * dx[x][e];
-        vdy[x] += (float)vv[e] * dy[x][e];
-        dkr[x][e] += bgi * dx[x][e];
-        o[e] = (bf16)(Bs[i] * dy[x][e]);
-      }
-      if (i < n) *reinterpret_cast<bf16x8*>(dv + (size_t)(c0 + i) * rs + (size_t)h * DD + d8) = o;
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) {
-        kdx[x] += __shfl_xor(kdx[x], off);
-        vdy[x] += __shfl_xor(vdy[x], off);
-      }
-    }
-    if ((tid & 15) == 0)
-#pragma unroll
-      for (int x = 0; x < GR; ++x) {
-        const int i = i0 + x;
-        atomicAdd(&dBs[i], gm[i] * kdx[x] + vdy[x]);
-        atomicAdd(&dGs[i], gm[i] * Bs[i] * kdx[x]);
-      }
   }
   // dT = dW diag(beta gamma) K^T + dU diag(beta) V^T into M2
-  {
-    float tk[GR][4] = {}, tv[GR][4] = {};
-    for (int d = 0; d < DD; d += 8) {
-      bf16x8 kj[4], vj[4];
+  if (wave < 4) {
+    f32x16 a1 = {}, a2 = {};
 #pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        kj[y] = *reinterpret_cast<const bf16x8*>(Kb + (s0 + y) * BP + d);
-        vj[y] = *reinterpret_cast<const bf16x8*>(Vb + (s0 + y) * BP + d);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float w[GR], u[GR];
-#pragma unroll
-        for (int x = 0; x < GR; ++x) {
-          w[x] = F1[(r0 + x) * LP + d + e];
-          u[x] = F2[(r0 + x) * LP + d + e];
-        }
-#pragma unroll
-        for (int x = 0; x < GR; ++x)
-#pragma unroll
-          for (int y = 0; y < 4; ++y) {
-            tk[x][y] += w[x] * (float)kj[y][e];
-            tv[x][y] += u[x] * (float)vj[y][e];
-          }
-      }
+    for (int ks = 0; ks < DD / 16; ++ks) {
+      const int kk = 16 * ks + 8 * hh;
+      bf16x8 wh, wl, uh, ul;
+      ld32(F1 + (cm0 + r) * LP + kk, 1, wh, wl);          // dW[i][d]
+      ld32(F2 + (cm0 + r) * LP + kk, 1, uh, ul);          // dU[i][d]
+      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Kb + (cn0 + r) * BP + kk);
+      const bf16x8 vb = *reinterpret_cast<const bf16x8*>(Vb + (cn0 + r) * BP + kk);
+      a1 = mfma32(wh, kb, a1);
+      a1 = mfma32(wl, kb, a1);
+      a2 = mfma32(uh, vb, a2);
+      a2 = mfma32(ul, vb, a2);
     }
+    const int j = cn0 + r;
 #pragma unroll
-    for (int x = 0; x < GR; ++x)
-#pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        const int j = s0 + y;
-        M2[(r0 + x) * CP + j] = Bs[j] * (gm[j] * tk[x][y] + tv[x][y]);
-      }
+    for (int x = 0; x < 16; ++x) M2[(cm0 + drow(x)) * CP + j] = Bs[j] * (gm[j] * a1[x] + a2[x]);
   }
   __syncthreads();   // V is no longer read: its space holds dT T^T next
-  {
-    float m[GR][4] = {};
-    for (int c = 0; c < DC; ++c) {
-      float a_[GR], t_[4];
+  if (wave < 4) {   // Mx = dT T^T
+    f32x16 acc = {};
 #pragma unroll
-      for (int x = 0; x < GR; ++x) a_[x] = M2[(r0 + x) * CP + c];
-#pragma unroll
-      for (int y = 0; y < 4; ++y) t_[y] = M1[(s0 + y) * CP + c];
-#pragma unroll
-      for (int x = 0; x < GR; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) m[x][y] += a_[x] * t_[y];
+    for (int t = 0; t < DC / 16; ++t) {
+      const int kk = 16 * t + 8 * hh;
+      bf16x8 ah, al, bh, bl;
+      ld32(M2 + (cm0 + r) * CP + kk, 1, ah, al);          // dT[a][b]
+      ld32(M1 + (cn0 + r) * CP + kk, 1, bh, bl);          // T[j][b]
+      acc = mfma32(ah, bh, acc);
+      acc = mfma32(ah, bl, acc);
+      acc = mfma32(al, bh, acc);
     }
 #pragma unroll
-    for (int x = 0; x < GR; ++x)
-#pragma unroll
-      for (int y = 0; y < 4; ++y) M3[(r0 + x) * CP + s0 + y] = m[x][y];
+    for (int x = 0; x < 16; ++x) M3[(cm0 + drow(x)) * CP + cn0 + r] = acc[x];
   }
   __syncthreads();
   // dA = -(T^T (dT T^T)) below the diagonal; with KK = K K^T and
   // A_ij = beta_i exp(G_i - G_j) KK_ij, the beta and decay gradients through
-  // A, and Bm = dA (x) beta_i exp(G_i - G_j) into M2 (dT is no longer read)
-  {
-    float da[GR][4] = {}, kk[GR][4] = {};
-    for (int c = 0; c < DC; ++c) {
-      float t_[GR], m_[4];
+  // A; Bm = dA o beta_i exp(G_i - G_j) into M2 (dT is no longer read)
+  if (wave < 4) {
+    f32x16 aa = {}, ak = {};
 #pragma unroll
-      for (int x = 0; x < GR; ++x) t_[x] = M1[c * CP + r0 + x];
-#pragma unroll
-      for (int y = 0; y < 4; ++y) m_[y] = M3[c * CP + s0 + y];
-#pragma unroll
-      for (int x = 0; x < GR; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) da[x][y] -= t_[x] * m_[y];
+    for (int t = 0; t < DC / 16; ++t) {
+      const int kk = 16 * t + 8 * hh;
+      bf16x8 th, tl, mh, ml;
+      ld32(M1 + kk * CP + cm0 + r, CP, th, tl);           // T[c][i]
+      ld32(M3 + kk * CP + cn0 + r, CP, mh, ml);           // Mx[c][j]
+      aa = mfma32(th, mh, aa);
+      aa = mfma32(th, ml, aa);
+      aa = mfma32(tl, mh, aa);
     }
-    for (int d = 0; d < DD; d += 8) {
-      bf16x8 ki[GR], kj[4];
 #pragma unroll
-      for (int x = 0; x < GR; ++x) ki[x] = *reinterpret_cast<const bf16x8*>(Kb + (r0 + x) * BP + d);
-#pragma unroll
-      for (int y = 0; y < 4; ++y) kj[y] = *reinterpret_cast<const bf16x8*>(Kb + (s0 + y) * BP + d);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int x = 0; x < GR; ++x)
-#pragma unroll
-          for (int y = 0; y < 4; ++y) kk[x][y] += (float)ki[x][e] * (float)kj[y][e];
+    for (int ks = 0; ks < DD / 16; ++ks) {
+      const int kk = 16 * ks + 8 * hh;
+      const bf16x8 ki = *reinterpret_cast<const bf16x8*>(Kb + (cm0 + r) * BP + kk);
+      const bf16x8 kj = *reinterpret_cast<const bf16x8*>(Kb + (cn0 + r) * BP + kk);
+      ak = mfma32(ki, kj, ak);
     }
-    float row[GR] = {}, col[4] = {}, db[GR] = {};
-    float bm[GR][4];
+    const int j = cn0 + r;
+    float colsum = 0.f;
+    float bm[16];
 #pragma unroll
-    for (int x = 0; x < GR; ++x)
-#pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        const int i = r0 + x, j = s0 + y;
-        bm[x][y] = 0.f;
-        if (j < i) {
-          const float dec = __expf(Gs[i] - Gs[j]);
-          const float dkk = da[x][y] * dec * kk[x][y];
-          db[x] += dkk;
-          const float ada = Bs[i] * dkk;   // A_ij dA_ij
-          row[x] += ada;
-          col[y] += ada;
-          bm[x][y] = da[x][y] * Bs[i] * dec;
-        }
+    for (int x = 0; x < 16; ++x) {
+      const int i = cm0 + drow(x);
+      float dkk = 0.f, ada = 0.f;
+      bm[x] = 0.f;
+      if (j < i) {
+        const float dec = __expf(Gs[i] - Gs[j]);
+        const float da = -aa[x];
+        dkk = da * dec * ak[x];
+        ada = Bs[i] * dkk;   // A_ij dA_ij
+        bm[x] = da * Bs[i] * dec;
       }
-    __syncthreads();   // every read of dT is done before Bm replaces it
+      colsum += ada;
+      float rd = dkk, ra = ada;
 #pragma unroll
-    for (int x = 0; x < GR; ++x) {
-#pragma unroll
-      for (int y = 0; y < 4; ++y) M2[(r0 + x) * CP + s0 + y] = bm[x][y];
-      atomicAdd(&dBs[r0 + x], db[x]);
-      atomicAdd(&dGs[r0 + x], row[x]);
+      for (int o = 1; o < 32; o <<= 1) {
+        rd += __shfl_xor(rd, o);
+        ra += __shfl_xor(ra, o);
+      }
+      if (r == 0) {
+        atomicAdd(&dBs[i], rd);
+        atomicAdd(&dGs[i], ra);
+      }
     }
+    atomicAdd(&dGs[j], -colsum);
 #pragma unroll
-    for (int y = 0; y < 4; ++y) atomicAdd(&dGs[s0 + y], -col[y]);
+    for (int x = 0; x < 16; ++x) M2[(cm0 + drow(x)) * CP + j] = bm[x];
   }
   __syncthreads();
-  // dK += Bm K + Bm^T K (written)
-  for (int j = 0; j < DC; ++j) {
-    const bf16x8 kv = *reinterpret_cast<const bf16x8*>(Kb + j * BP + d8);
+  // dK += Bm K + Bm^T K, then written with dK_state
+  {
 #pragma unroll
-    for (int x = 0; x < GR; ++x) {
-      const float w = M2[(i0 + x) * CP + j] + M2[j * CP + i0 + x];
+    for (int t = 0; t < DC / 16; ++t) {
+      const int kk = 16 * t + 8 * hh;
+      bf16x8 ah, al, th, tl;
+      ld32(M2 + (dm0 + r) * CP + kk, 1, ah, al);          // Bm[i][j]
+      ld32(M2 + kk * CP + dm0 + r, CP, th, tl);           // Bm[j][i]
+      const bf16x8 kb = ldb(Kb + kk * BP + dd0 + r, BP);
+      akk = mfma32(ah, kb, akk);
+      akk = mfma32(al, kb, akk);
+      akk = mfma32(th, kb, akk);
+      akk = mfma32(tl, kb, akk);
+    }
+    const int d = dd0 + r;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dkr[x][e] += w * (float)kv[e];
+    for (int x = 0; x < 16; ++x) {
+      const int i = dm0 + drow(x);
+      if (i < n)
+        dk[(size_t)(c0 + i) * rs + (size_t)h * DD + d] =
+            (bf16)(gst[(size_t)DC * DD + (size_t)i * DD + d] + akk[x]);
     }
   }
-#pragma unroll
-  for (int x = 0; x < GR; ++x)
-    if (i0 + x < n) {
-      bf16x8 o;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = (bf16)dkr[x][e];
-      *reinterpret_cast<bf16x8*>(dk + (size_t)(c0 + i0 + x) * rs + (size_t)h * DD + d8) = o;
-    }
   // the log-decay gradient of every token: the side values of the state
   // products (output term; end decays, whose sum lands on the last token, as
   // does the end-state term), then the reverse cumulative sum inside the chunk
@@ -1328,7 +1303,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
     for (int j = 0; j < n; ++j) sde += side[DC + j];
     float add = side[tid] - side[DC + tid];
     if (tid == n - 1) add += side[2 * DC] + sde;
-    dGs[tid] += add;
+    atomicAdd(&dGs[tid], add);
   }
   __syncthreads();
   if (tid < n) {
