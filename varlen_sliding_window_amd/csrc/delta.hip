@@ -229,38 +229,30 @@ __global__ __launch_bounds__(PREP_THREADS) void delta_prep_kernel(
   }
   __syncthreads();
   float* rec = records + (size_t)blockIdx.x * DeltaRecord::FLOATS;
-  // Gram products, a 4 x 4 block of (row, column) pairs per thread: A from
-  // K K^T (strictly below the diagonal), P from Q K^T (on and below it).
+  // Gram products on MFMA (bf16 operands, exact): wave w forms the 32 x 32
+  // tile (rows 32 (w / 2) .., columns 32 (w % 2) ..) of K K^T and of Q K^T;
+  // A from K K^T (strictly below the diagonal), P from Q K^T (on and below it)
+  const int wave = tid >> 6, lane = tid & 63, lr = lane & 31, lh = lane >> 5;
+  const int tm0 = 32 * (wave >> 1), tn0 = 32 * (wave & 1);
   {
-    const int i0 = (tid / 16) * 4, j0 = (tid % 16) * 4;
-    float kk[4][4] = {}, qk[4][4] = {};
-    for (int d = 0; d < DD; d += 8) {
-      bf16x8 ki[4], qi[4], kj[4];
+    f32x16 kk = {}, qk = {};
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        ki[x] = *reinterpret_cast<const bf16x8*>(Ks + (i0 + x) * BP + d);
-        qi[x] = *reinterpret_cast<const bf16x8*>(Qs + (i0 + x) * BP + d);
-        kj[x] = *reinterpret_cast<const bf16x8*>(Ks + (j0 + x) * BP + d);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-          for (int y = 0; y < 4; ++y) {
-            kk[x][y] += (float)ki[x][e] * (float)kj[y][e];
-            qk[x][y] += (float)qi[x][e] * (float)kj[y][e];
-          }
+    for (int ks = 0; ks < DD / 16; ++ks) {
+      const int col = 16 * ks + 8 * lh;
+      const bf16x8 ki = *reinterpret_cast<const bf16x8*>(Ks + (tm0 + lr) * BP + col);
+      const bf16x8 qi = *reinterpret_cast<const bf16x8*>(Qs + (tm0 + lr) * BP + col);
+      const bf16x8 kj = *reinterpret_cast<const bf16x8*>(Ks + (tn0 + lr) * BP + col);
+      kk = mfma32(ki, kj, kk);
+      qk = mfma32(qi, kj, qk);
     }
+    const int j = tn0 + lr;
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        const int i = i0 + x, j = j0 + y;
-        const float dec = j <= i ? __expf(Gs[i] - Gs[j]) : 0.f;
-        As[i * (DC + 1) + j] = j < i ? Bs[i] * dec * kk[x][y] : 0.f;
-        rec[DeltaRecord::P + i * DC + j] = j <= i ? dec * qk[x][y] : 0.f;
-      }
+    for (int x = 0; x < 16; ++x) {
+      const int i = tm0 + 8 * (x / 4) + 4 * lh + (x % 4);
+      const float dec = j <= i ? __expf(Gs[i] - Gs[j]) : 0.f;
+      As[i * (DC + 1) + j] = j < i ? Bs[i] * dec * kk[x] : 0.f;
+      rec[DeltaRecord::P + i * DC + j] = j <= i ? dec * qk[x] : 0.f;
+    }
   }
   if (tid < DC) {
     rec[DeltaRecord::GAM + tid] = __expf(Gs[tid]);
@@ -276,36 +268,53 @@ __global__ __launch_bounds__(PREP_THREADS) void delta_prep_kernel(
       const int i = f / DC, j = f % DC;
       rec[DeltaRecord::TI + f] = j < i ? As[i * (DC + 1) + j] : (j == i ? 1.f : 0.f);
     }
-  // W = T diag(beta gamma) K and U0 = T diag(beta) V: thread (4 rows, 8
-  // columns) of each, T's diagonal being 1.
+  // W = (T diag(beta gamma)) K and U0 = (T diag(beta)) V on MFMA: the fp32
+  // left factors in bf16 high and low parts, K and V exact; wave w forms rows
+  // 32 (w / 2) .., columns 64 (w % 2) .. (two 32 x 32 tiles of each)
   {
-    const int i0 = (tid / 16) * 4, d8 = (tid % 16) * 8;
-    float w[4][8] = {}, u[4][8] = {};
-    for (int j = 0; j < DC; ++j) {
-      const float sw = Bs[j] * __expf(Gs[j]), su = Bs[j];
-      const bf16x8 kv = *reinterpret_cast<const bf16x8*>(Ks + j * BP + d8);
-      const bf16x8 vv = *reinterpret_cast<const bf16x8*>(Vs + j * BP + d8);
+    const int dn0 = 64 * (wave & 1);
+    f32x16 aw0 = {}, aw1 = {}, au0 = {}, au1 = {};
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int i = i0 + x;
-        const float t = j < i ? As[i * (DC + 1) + j] : (j == i ? 1.f : 0.f);
+    for (int t = 0; t < DC / 16; ++t) {
+      const int kk0 = 16 * t + 8 * lh;
+      const int i = tm0 + lr;
+      bf16x8 wh, wl, uh, ul, k0, k1, v0, v1;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          w[x][e] += t * sw * (float)kv[e];
-          u[x][e] += t * su * (float)vv[e];
-        }
+      for (int e = 0; e < 8; ++e) {
+        const int j = kk0 + e;
+        const float tij = j < i ? As[i * (DC + 1) + j] : (j == i ? 1.f : 0.f);
+        const float xw = tij * Bs[j] * __expf(Gs[j]);
+        const float xu = tij * Bs[j];
+        wh[e] = (bf16)xw;
+        wl[e] = (bf16)(xw - (float)wh[e]);
+        uh[e] = (bf16)xu;
+        ul[e] = (bf16)(xu - (float)uh[e]);
+        k0[e] = Ks[j * BP + dn0 + lr];
+        k1[e] = Ks[j * BP + dn0 + 32 + lr];
+        v0[e] = Vs[j * BP + dn0 + lr];
+        v1[e] = Vs[j * BP + dn0 + 32 + lr];
       }
+      aw0 = mfma32(wh, k0, aw0);
+      aw0 = mfma32(wl, k0, aw0);
+      aw1 = mfma32(wh, k1, aw1);
+      aw1 = mfma32(wl, k1, aw1);
+      au0 = mfma32(uh, v0, au0);
+      au0 = mfma32(ul, v0, au0);
+      au1 = mfma32(uh, v1, au1);
+      au1 = mfma32(ul, v1, au1);
     }
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      float4* dw = reinterpret_cast<float4*>(rec + DeltaRecord::W + (i0 + x) * DD + d8);
-      float4* du = reinterpret_cast<float4*>(rec + DeltaRecord::U0 + (i0 + x) * DD + d8);
-      dw[0] = make_float4(w[x][0], w[x][1], w[x][2], w[x][3]);
-      dw[1] = make_float4(w[x][4], w[x][5], w[x][6], w[x][7]);
-      du[0] = make_float4(u[x][0], u[x][1], u[x][2], u[x][3]);
-      du[1] = make_float4(u[x][4], u[x][5], u[x][6], u[x][7]);
+    for (int x = 0; x < 16; ++x) {
+      const int i = tm0 + 8 * (x / 4) + 4 * lh + (x % 4);
+      float* w = rec + DeltaRecord::W + (size_t)i * DD + dn0 + lr;
+      float* u = rec + DeltaRecord::U0 + (size_t)i * DD + dn0 + lr;
+      w[0] = aw0[x];
+      w[32] = aw1[x];
+      u[0] = au0[x];
+      u[32] = au1[x];
     }
   }
+
 }
 
 // Walks a document's chunks in order for one head and a slice of SLICE d_v
