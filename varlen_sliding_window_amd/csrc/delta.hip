@@ -2101,33 +2101,42 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gmat_kernel(
     F1[i * LP + c4] = u.x; F1[i * LP + c4 + 1] = u.y; F1[i * LP + c4 + 2] = u.z; F1[i * LP + c4 + 3] = u.w;
   }
   __syncthreads();
-  const int r0 = (tid / 16) * GR, s0 = (tid % 16) * 4;   // C x C tile
-  const int i0 = r0, d8 = (tid % 16) * 8;               // C x D tile
-  // dPm = scale dO U^T on and below the diagonal, to global
-  {
-    float dp[GR][4] = {};
-#pragma unroll 4
-    for (int d = 0; d < DD; ++d) {
-      float o[GR], u[4];
+  const int wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
+  auto ld32 = [](const float* p, int stride, bf16x8& hi, bf16x8& lo) __attribute__((always_inline)) {
 #pragma unroll
-      for (int x = 0; x < GR; ++x) o[x] = (float)dOb[(r0 + x) * BP + d];
-#pragma unroll
-      for (int y = 0; y < 4; ++y) u[y] = F1[(s0 + y) * LP + d];
-#pragma unroll
-      for (int x = 0; x < GR; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) dp[x][y] += o[x] * u[y];
+    for (int e = 0; e < 8; ++e) {
+      const float x = p[e * stride];
+      hi[e] = (bf16)x;
+      lo[e] = (bf16)(x - (float)hi[e]);
     }
+  };
+  auto drow = [hh](int x) { return 8 * (x / 4) + 4 * hh + (x % 4); };
+  const int cm0 = 32 * (wave >> 1), cn0 = 32 * (wave & 1);   // C x C tiles (waves 0..3)
+  const int dm0 = 32 * (wave >> 2), dd0 = 32 * (wave & 3);   // C x D tiles (all waves)
+  // dPm = scale dO U^T on and below the diagonal, to global (MFMA: dO exact,
+  // U in high and low parts)
+  if (wave < 4) {
+    f32x16 acc = {};
 #pragma unroll
-    for (int x = 0; x < GR; ++x)
+    for (int ks = 0; ks < DD / 16; ++ks) {
+      const int kk = 16 * ks + 8 * hh;
+      const bf16x8 ao = *reinterpret_cast<const bf16x8*>(dOb + (cm0 + r) * BP + kk);
+      bf16x8 uh, ul;
+      ld32(F1 + (cn0 + r) * LP + kk, 1, uh, ul);
+      acc = mfma32(ao, uh, acc);
+      acc = mfma32(ao, ul, acc);
+    }
+    const int j = cn0 + r;
 #pragma unroll
-      for (int y = 0; y < 4; ++y)
-        side[(r0 + x) * DC + s0 + y] = s0 + y <= r0 + x ? scale * dp[x][y] : 0.f;
+    for (int x = 0; x < 16; ++x) {
+      const int i = cm0 + drow(x);
+      side[i * DC + j] = j <= i ? scale * acc[x] : 0.f;
+    }
   }
   __syncthreads();   // U and dO are no longer read
 #pragma unroll
-  for (int r = 0; r < DC * DD / 4 / GRAD_THREADS; ++r) {
-    const int f = tid + GRAD_THREADS * r, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
+  for (int rr = 0; rr < DC * DD / 4 / GRAD_THREADS; ++rr) {
+    const int f = tid + GRAD_THREADS * rr, i = f / (DD / 4), c4 = (f % (DD / 4)) * 4;
     const float4 w = reinterpret_cast<const float4*>(dwbuf + unit * DC * DD)[f];
     const float4 du = reinterpret_cast<const float4*>(dubuf + unit * DC * DD)[f];
     F1[i * LP + c4] = w.x; F1[i * LP + c4 + 1] = w.y; F1[i * LP + c4 + 2] = w.z; F1[i * LP + c4 + 3] = w.w;
@@ -2135,128 +2144,103 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gmat_kernel(
   }
   for (int f = tid; f < DC * DC; f += GRAD_THREADS) M1[(f / DC) * CP + f % DC] = rec[KdaRecord::TI + f];
   __syncthreads();
-  // dX = T^T dW (to dW's buffer), dY = T^T dU; dV = diag(beta) dY; beta
-  // gradient through X and Y
+  // dX = T^T dW (over dW's buffer, read by now), dY = T^T dU; dV = diag(beta)
+  // dY; beta gradient through X = diag(beta) K_tilde and Y
   {
-    float dx[GR][8] = {}, dy[GR][8] = {};
-#pragma unroll 2
-    for (int j = i0; j < DC; ++j) {
-      float w[8], u[8];
+    f32x16 ax = {}, ay = {};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        w[e] = F1[j * LP + d8 + e];
-        u[e] = F2[j * LP + d8 + e];
-      }
-#pragma unroll
-      for (int x = 0; x < GR; ++x) {
-        const float t = M1[j * CP + i0 + x];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          dx[x][e] += t * w[e];
-          dy[x][e] += t * u[e];
-        }
-      }
+    for (int t = 0; t < DC / 16; ++t) {
+      const int kk = 16 * t + 8 * hh;
+      bf16x8 th, tl, wh, wl, uh, ul;
+      ld32(M1 + kk * CP + dm0 + r, CP, th, tl);           // T[j][i]
+      ld32(F1 + kk * LP + dd0 + r, LP, wh, wl);           // dW[j][d]
+      ld32(F2 + kk * LP + dd0 + r, LP, uh, ul);           // dU[j][d]
+      ax = mfma32(th, wh, ax);
+      ax = mfma32(th, wl, ax);
+      ax = mfma32(tl, wh, ax);
+      ay = mfma32(th, uh, ay);
+      ay = mfma32(th, ul, ay);
+      ay = mfma32(tl, uh, ay);
     }
+    const int d = dd0 + r;
 #pragma unroll
-    for (int x = 0; x < GR; ++x) {
-      const int i = i0 + x;
-      const bf16x8 vv = *reinterpret_cast<const bf16x8*>(Vb + i * BP + d8);
-      float part = 0.f;
-      bf16x8 o;
+    for (int x = 0; x < 16; ++x) {
+      const int i = dm0 + drow(x);
+      if (i < n) dv[(size_t)(c0 + i) * rs + (size_t)h * DD + d] = (bf16)(Bs[i] * ay[x]);
+      dwbuf[unit * DC * DD + (size_t)i * DD + d] = ax[x];
+      float part = ax[x] * KT[i * LP + d] + (float)Vb[i * BP + d] * ay[x];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float kt = KT[i * LP + d8 + e];
-        part += dx[x][e] * kt + (float)vv[e] * dy[x][e];
-        o[e] = (bf16)(Bs[i] * dy[x][e]);
-      }
-      if (i < n) *reinterpret_cast<bf16x8*>(dv + (size_t)(c0 + i) * rs + (size_t)h * DD + d8) = o;
-      float4* px = reinterpret_cast<float4*>(dwbuf + unit * DC * DD + (size_t)i * DD + d8);
-      px[0] = make_float4(dx[x][0], dx[x][1], dx[x][2], dx[x][3]);
-      px[1] = make_float4(dx[x][4], dx[x][5], dx[x][6], dx[x][7]);
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) part += __shfl_xor(part, off);
-      if ((tid & 15) == 0) atomicAdd(&dBs[i], part);
+      for (int o = 1; o < 32; o <<= 1) part += __shfl_xor(part, o);
+      if (r == 0) atomicAdd(&dBs[i], part);
     }
   }
   // dT = dW X^T + dU Y^T = (dW K_tilde^T + dU V^T) diag(beta) into M2
-  {
-    float t[GR][4] = {};
-#pragma unroll 4
-    for (int d = 0; d < DD; ++d) {
-      float w[GR], u[GR], kx[4], vx[4];
+  if (wave < 4) {
+    f32x16 acc = {};
 #pragma unroll
-      for (int x = 0; x < GR; ++x) {
-        w[x] = F1[(r0 + x) * LP + d];
-        u[x] = F2[(r0 + x) * LP + d];
-      }
-#pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        kx[y] = KT[(s0 + y) * LP + d];
-        vx[y] = (float)Vb[(s0 + y) * BP + d];
-      }
-#pragma unroll
-      for (int x = 0; x < GR; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) t[x][y] += w[x] * kx[y] + u[x] * vx[y];
+    for (int ks = 0; ks < DD / 16; ++ks) {
+      const int kk = 16 * ks + 8 * hh;
+      bf16x8 wh, wl, uh, ul, kh, kl;
+      ld32(F1 + (cm0 + r) * LP + kk, 1, wh, wl);          // dW[i][d]
+      ld32(F2 + (cm0 + r) * LP + kk, 1, uh, ul);          // dU[i][d]
+      ld32(KT + (cn0 + r) * LP + kk, 1, kh, kl);          // K_tilde[j][d]
+      const bf16x8 vb = *reinterpret_cast<const bf16x8*>(Vb + (cn0 + r) * BP + kk);
+      acc = mfma32(wh, kh, acc);
+      acc = mfma32(wh, kl, acc);
+      acc = mfma32(wl, kh, acc);
+      acc = mfma32(uh, vb, acc);
+      acc = mfma32(ul, vb, acc);
     }
+    const int j = cn0 + r;
 #pragma unroll
-    for (int x = 0; x < GR; ++x)
-#pragma unroll
-      for (int y = 0; y < 4; ++y) M2[(r0 + x) * CP + s0 + y] = Bs[s0 + y] * t[x][y];
+    for (int x = 0; x < 16; ++x) M2[(cm0 + drow(x)) * CP + j] = Bs[j] * acc[x];
   }
   __syncthreads();   // V is no longer read: its space holds dT T^T next
-  {
-    float m[GR][4] = {};
-#pragma unroll 4
-    for (int c = 0; c < DC; ++c) {
-      float a_[GR], t_[4];
+  if (wave < 4) {   // Mx = dT T^T
+    f32x16 acc = {};
 #pragma unroll
-      for (int x = 0; x < GR; ++x) a_[x] = M2[(r0 + x) * CP + c];
-#pragma unroll
-      for (int y = 0; y < 4; ++y) t_[y] = M1[(s0 + y) * CP + c];
-#pragma unroll
-      for (int x = 0; x < GR; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) m[x][y] += a_[x] * t_[y];
+    for (int t = 0; t < DC / 16; ++t) {
+      const int kk = 16 * t + 8 * hh;
+      bf16x8 ah, al, bh, bl;
+      ld32(M2 + (cm0 + r) * CP + kk, 1, ah, al);
+      ld32(M1 + (cn0 + r) * CP + kk, 1, bh, bl);
+      acc = mfma32(ah, bh, acc);
+      acc = mfma32(ah, bl, acc);
+      acc = mfma32(al, bh, acc);
     }
 #pragma unroll
-    for (int x = 0; x < GR; ++x)
-#pragma unroll
-      for (int y = 0; y < 4; ++y) M3[(r0 + x) * CP + s0 + y] = m[x][y];
+    for (int x = 0; x < 16; ++x) M3[(cm0 + drow(x)) * CP + cn0 + r] = acc[x];
   }
   __syncthreads();
   // dA = -(T^T (dT T^T)) below the diagonal: B = diag(beta) dA to global, and
   // the beta gradient through A = diag(beta) KK
-  {
-    float da[GR][4] = {};
-#pragma unroll 4
-    for (int c = 0; c < DC; ++c) {
-      float t_[GR], m_[4];
+  if (wave < 4) {
+    f32x16 acc = {};
 #pragma unroll
-      for (int x = 0; x < GR; ++x) t_[x] = M1[c * CP + r0 + x];
-#pragma unroll
-      for (int y = 0; y < 4; ++y) m_[y] = M3[c * CP + s0 + y];
-#pragma unroll
-      for (int x = 0; x < GR; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) da[x][y] -= t_[x] * m_[y];
+    for (int t = 0; t < DC / 16; ++t) {
+      const int kk = 16 * t + 8 * hh;
+      bf16x8 th, tl, mh, ml;
+      ld32(M1 + kk * CP + cm0 + r, CP, th, tl);           // T[c][i]
+      ld32(M3 + kk * CP + cn0 + r, CP, mh, ml);           // Mx[c][j]
+      acc = mfma32(th, mh, acc);
+      acc = mfma32(th, ml, acc);
+      acc = mfma32(tl, mh, acc);
     }
+    const int j = cn0 + r;
 #pragma unroll
-    for (int x = 0; x < GR; ++x) {
-      const int i = r0 + x;
-      float db = 0.f;
+    for (int x = 0; x < 16; ++x) {
+      const int i = cm0 + drow(x);
+      const float dav = j < i ? -acc[x] : 0.f;
+      side[DC * DC + i * DC + j] = Bs[i] * dav;
+      float db = dav * rec[KdaRecord::KK + i * DC + j];
 #pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        const int j = s0 + y;
-        const float dav = j < i ? da[x][y] : 0.f;
-        db += dav * rec[KdaRecord::KK + i * DC + j];
-        side[DC * DC + i * DC + j] = Bs[i] * dav;
-      }
-      atomicAdd(&dBs[i], db);
+      for (int o = 1; o < 32; o <<= 1) db += __shfl_xor(db, o);
+      if (r == 0) atomicAdd(&dBs[i], db);
     }
   }
   __syncthreads();
   if (tid < n) dbeta[(size_t)(c0 + tid) * H + h] = dBs[tid];
+
 }
 
 // The decayed pair products per (chunk, head) and the final dq, dk, dg:
