@@ -1486,37 +1486,57 @@ __global__ __launch_bounds__(PREP_THREADS) void kda_prep_kernel(
       const int i = f / DC, j = f % DC;
       rec[KdaRecord::TI + f] = j < i ? As[i * (DC + 1) + j] : (j == i ? 1.f : 0.f);
     }
-  // W = T X, U0 = T diag(beta) V: thread (4 rows, 8 columns)
+  // W = T X and U0 = (T diag(beta)) V on MFMA (T and X in bf16 high and low
+  // parts, V exact): wave w forms rows 32 (w / 2) .., columns 64 (w % 2) ..
   {
-    const int i0 = (tid / 16) * 4, d8 = (tid % 16) * 8;
-    float w[4][8] = {}, u[4][8] = {};
-    for (int j = 0; j < DC; ++j) {
-      const float su = Bs[j];
-      const bf16x8 vv = *reinterpret_cast<const bf16x8*>(Vs + j * BP + d8);
-      float xv[8];
+    const int wave = tid >> 6, lane = tid & 63, lr = lane & 31, lh = lane >> 5;
+    const int tm0 = 32 * (wave >> 1), dn0 = 64 * (wave & 1);
+    f32x16 aw0 = {}, aw1 = {}, au0 = {}, au1 = {};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xv[e] = X[j * LP + d8 + e];
+    for (int t = 0; t < DC / 16; ++t) {
+      const int kk0 = 16 * t + 8 * lh;
+      const int i = tm0 + lr;
+      bf16x8 th, tl, bh, bl, x0h, x0l, x1h, x1l, v0, v1;
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int i = i0 + x;
-        const float t = j < i ? As[i * (DC + 1) + j] : (j == i ? 1.f : 0.f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          w[x][e] += t * xv[e];
-          u[x][e] += t * su * (float)vv[e];
-        }
+      for (int e = 0; e < 8; ++e) {
+        const int j = kk0 + e;
+        const float tij = j < i ? As[i * (DC + 1) + j] : (j == i ? 1.f : 0.f);
+        const float tb = tij * Bs[j];
+        const float x0 = X[j * LP + dn0 + lr], x1 = X[j * LP + dn0 + 32 + lr];
+        th[e] = (bf16)tij;
+        tl[e] = (bf16)(tij - (float)th[e]);
+        bh[e] = (bf16)tb;
+        bl[e] = (bf16)(tb - (float)bh[e]);
+        x0h[e] = (bf16)x0;
+        x0l[e] = (bf16)(x0 - (float)x0h[e]);
+        x1h[e] = (bf16)x1;
+        x1l[e] = (bf16)(x1 - (float)x1h[e]);
+        v0[e] = Vs[j * BP + dn0 + lr];
+        v1[e] = Vs[j * BP + dn0 + 32 + lr];
       }
+      aw0 = mfma32(th, x0h, aw0);
+      aw0 = mfma32(th, x0l, aw0);
+      aw0 = mfma32(tl, x0h, aw0);
+      aw1 = mfma32(th, x1h, aw1);
+      aw1 = mfma32(th, x1l, aw1);
+      aw1 = mfma32(tl, x1h, aw1);
+      au0 = mfma32(bh, v0, au0);
+      au0 = mfma32(bl, v0, au0);
+      au1 = mfma32(bh, v1, au1);
+      au1 = mfma32(bl, v1, au1);
     }
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      float4* dw = reinterpret_cast<float4*>(rec + KdaRecord::W + (i0 + x) * DD + d8);
-      float4* du = reinterpret_cast<float4*>(rec + KdaRecord::U0 + (i0 + x) * DD + d8);
-      dw[0] = make_float4(w[x][0], w[x][1], w[x][2], w[x][3]);
-      dw[1] = make_float4(w[x][4], w[x][5], w[x][6], w[x][7]);
-      du[0] = make_float4(u[x][0], u[x][1], u[x][2], u[x][3]);
-      du[1] = make_float4(u[x][4], u[x][5], u[x][6], u[x][7]);
+    for (int x = 0; x < 16; ++x) {
+      const int i = tm0 + 8 * (x / 4) + 4 * lh + (x % 4);
+      float* w = rec + KdaRecord::W + (size_t)i * DD + dn0 + lr;
+      float* u = rec + KdaRecord::U0 + (size_t)i * DD + dn0 + lr;
+      w[0] = aw0[x];
+      w[32] = aw1[x];
+      u[0] = au0[x];
+      u[32] = au1[x];
     }
   }
+
 }
 
 // Walks a document's chunks for one head and a slice of SLICE d_v rows of S,
