@@ -928,7 +928,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_gstate_kernel(
     const float* __restrict__ states, float* __restrict__ dstates,
     const float* __restrict__ dubuf, float* __restrict__ dwbuf) {
   __shared__ __attribute__((aligned(16))) StateProductsLds L;
-  __shared__ float qsd[DC], kdv[DC], red[GRAD_THREADS / 64];
+  __shared__ float red[GRAD_THREADS / 64];
   const int chunk = blockIdx.x / H, h = blockIdx.x - chunk * H;
   if (chunk >= header[0] || !delta_saved_for(header, T, H, chunk_cap)) return;
   int c0, n;
@@ -938,21 +938,24 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_gstate_kernel(
   const size_t unit = blockIdx.x;
   float* rec = records + unit * DeltaRecord::FLOATS;
   float* dS = dstates + unit * DD * DD;
-  if (tid < DC) {
-    qsd[tid] = 0.f;
-    kdv[tid] = 0.f;
-  }
   float dgc = 0.f;   // <dS_C, S_0>, this thread's share
   f32x16 aq, aw, ak;
   delta_state_products(L, dout, (size_t)c0 * rs + (size_t)h * DD, rs, n,
                        rec + DeltaRecord::U0, dubuf + unit * DC * DD, states + unit * DD * DD, dS,
                        tid, aq, aw, ak,
                        [&](int, f32x4 p) { dgc += (p[0] + p[1]) + (p[2] + p[3]); });
-  __syncthreads();   // every read of this unit's dS_C is done before it is overwritten
+  __syncthreads();   // every read of this unit's dS_C and of the staged operands is done
   const int wave = tid >> 6, lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5, m0 = 32 * (wave >> 2), d = 32 * (wave & 3) + r;
   const float* gam = rec + DeltaRecord::GAM;
   const float* en = rec + DeltaRecord::END;
+  // the terms of the row dots q_i . (dO S_0)_i and k_i . (U dS_C)_i go to LDS
+  // where the operands were, then 8 threads sum each row
+  constexpr int TP = DD + 1;
+  float* tq = reinterpret_cast<float*>(L.dO);
+  float* tk = tq + DC * TP;
+  static_assert(2 * DC * TP * sizeof(float) <= 5 * DC * StateProductsLds::AP * sizeof(bf16),
+                "the row-dot terms fit where the operands were");
 #pragma unroll
   for (int x = 0; x < 16; ++x) {
     const int i = m0 + 8 * (x / 4) + 4 * hh + (x % 4);
@@ -965,23 +968,30 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_gstate_kernel(
       pq = (float)q[off] * aq[x];
       pk = (float)k[off] * ak[x];
     }
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) {   // over the 32 columns of this lane half
-      pq += __shfl_xor(pq, o);
-      pk += __shfl_xor(pk, o);
-    }
-    if (r == 0) {
-      atomicAdd(&qsd[i], pq);
-      atomicAdd(&kdv[i], pk);
-    }
+    tq[i * TP + d] = pq;
+    tk[i * TP + d] = pk;
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) dgc += __shfl_xor(dgc, o);
   if (lane == 0) red[wave] = dgc;
   __syncthreads();
-  if (tid < DC) {
-    rec[DeltaRecord::SIDE + tid] = scale * gam[tid] * qsd[tid];   // gamma_i d(gamma_i), output term
-    rec[DeltaRecord::SIDE + DC + tid] = en[tid] * kdv[tid];        // e_i d(e_i)
+  {   // row tid / 8, columns 16 (tid % 8) .. + 15, then over the 8 threads
+    const int i = tid >> 3, c16 = (tid & 7) * 16;
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      sq += tq[i * TP + c16 + c];
+      sk += tk[i * TP + c16 + c];
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      sq += __shfl_xor(sq, o);
+      sk += __shfl_xor(sk, o);
+    }
+    if ((tid & 7) == 0) {
+      rec[DeltaRecord::SIDE + i] = scale * gam[i] * sq;   // gamma_i d(gamma_i), output term
+      rec[DeltaRecord::SIDE + DC + i] = en[i] * sk;       // e_i d(e_i)
+    }
   }
   if (tid == 0) {   // gamma_C d(gamma_C) of the end state
     float tot = 0.f;
