@@ -1415,54 +1415,63 @@ __global__ __launch_bounds__(PREP_THREADS) void kda_prep_kernel(
   }
   __syncthreads();
   float* rec = records + (size_t)blockIdx.x * KdaRecord::FLOATS;
-  // Gram products with the per-channel decays, a 4 x 4 block of (row, column)
-  // pairs per thread; exp(G_i - G_j) = exp(G_i - G_j0) exp(G_j0 - G_j) about
-  // the block's first column j0, both factors bounded (rows i >= j0)
+  // Gram products on MFMA (16 x 16 x 32): for 16-row blocks bi >= bj, with
+  // rho = 16 bi the block's first row,
+  //   KK_ij = sum_d (k_id e^{G_id - G_rho,d}) (k_jd e^{G_rho,d - G_jd}),
+  // and Q K^T likewise with q: the first factor is at most 1 (i >= rho), the
+  // second too for j < rho and spans at most 15 tokens inside the block.  The
+  // operands are formed as their fragments are read, in bf16 high and low
+  // parts (three MFMAs each); the ten block pairs go round-robin to the waves.
   {
-    const int i0 = (tid / 16) * 4, j0 = (tid % 16) * 4;
-    float kk[4][4] = {}, qk[4][4] = {};
-    if (j0 <= i0) {   // blocks above the diagonal stay zero
-      for (int d = 0; d < DD; d += 8) {
-        bf16x8 ki[4], qi[4], kj[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          ki[x] = *reinterpret_cast<const bf16x8*>(Ks + (i0 + x) * BP + d);
-          qi[x] = *reinterpret_cast<const bf16x8*>(Qs + (i0 + x) * BP + d);
-          kj[x] = *reinterpret_cast<const bf16x8*>(Ks + (j0 + x) * BP + d);
-        }
+    const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    for (int pr = wave; pr < 10; pr += PREP_THREADS / 64) {
+      int bi = 0;
+      while ((bi + 1) * (bi + 2) / 2 <= pr) ++bi;   // pr = bi (bi + 1) / 2 + bj
+      const int bj = pr - bi * (bi + 1) / 2;
+      const int rho = 16 * bi, i = 16 * bi + lr, j = 16 * bj + lr;
+      f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < DD / 32; ++ks) {
+        const int d0 = 32 * ks + 8 * lg;
+        bf16x8 kah, kal, qah, qal, kbh, kbl;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float4 gI = *reinterpret_cast<const float4*>(GT + (d + e) * GP + i0);
-          const float4 gJ = *reinterpret_cast<const float4*>(GT + (d + e) * GP + j0);
-          const float gi[4] = {gI.x, gI.y, gI.z, gI.w};
-          const float gj[4] = {gJ.x, gJ.y, gJ.z, gJ.w};
-          float ka[4], qa[4], kb[4];
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            const float a = __expf(gi[x] - gj[0]);
-            ka[x] = (float)ki[x][e] * a;
-            qa[x] = (float)qi[x][e] * a;
-            kb[x] = (float)kj[x][e] * __expf(gj[0] - gj[x]);
-          }
-#pragma unroll
-          for (int x = 0; x < 4; ++x)
-#pragma unroll
-            for (int y = 0; y < 4; ++y) {
-              kk[x][y] += ka[x] * kb[y];
-              qk[x][y] += qa[x] * kb[y];
-            }
+          const int d = d0 + e;
+          const float gr = GT[d * GP + rho];
+          const float ea = __expf(GT[d * GP + i] - gr);
+          const float eb = __expf(gr - GT[d * GP + j]);
+          const float ka = (float)Ks[i * BP + d] * ea, qa = (float)Qs[i * BP + d] * ea;
+          const float kb = (float)Ks[j * BP + d] * eb;
+          kah[e] = (bf16)ka;
+          kal[e] = (bf16)(ka - (float)kah[e]);
+          qah[e] = (bf16)qa;
+          qal[e] = (bf16)(qa - (float)qah[e]);
+          kbh[e] = (bf16)kb;
+          kbl[e] = (bf16)(kb - (float)kbh[e]);
         }
+        kk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kah, kbh, kk, 0, 0, 0);
+        kk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kah, kbl, kk, 0, 0, 0);
+        kk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kal, kbh, kk, 0, 0, 0);
+        qk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qah, kbh, qk, 0, 0, 0);
+        qk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qah, kbl, qk, 0, 0, 0);
+        qk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qal, kbh, qk, 0, 0, 0);
+      }
+      // lane (lr, lg), register x: row 16 bi + 4 lg + x, column 16 bj + lr
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int ii = 16 * bi + 4 * lg + x, jj = 16 * bj + lr;
+        As[ii * (DC + 1) + jj] = jj < ii ? Bs[ii] * kk[x] : 0.f;
+        rec[KdaRecord::P + ii * DC + jj] = jj <= ii ? qk[x] : 0.f;
+        if (keep_inverse) rec[KdaRecord::KK + ii * DC + jj] = jj < ii ? kk[x] : 0.f;
       }
     }
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        const int i = i0 + x, j = j0 + y;
-        As[i * (DC + 1) + j] = j < i ? Bs[i] * kk[x][y] : 0.f;
-        rec[KdaRecord::P + i * DC + j] = j <= i ? qk[x][y] : 0.f;
-        if (keep_inverse) rec[KdaRecord::KK + i * DC + j] = j < i ? kk[x][y] : 0.f;
+    for (int f = tid; f < DC * DC; f += PREP_THREADS) {   // blocks above the diagonal
+      const int ii = f / DC, jj = f % DC;
+      if ((jj >> 4) > (ii >> 4)) {
+        As[ii * (DC + 1) + jj] = 0.f;
+        rec[KdaRecord::P + f] = 0.f;
+        if (keep_inverse) rec[KdaRecord::KK + f] = 0.f;
       }
+    }
   }
   // the chunk's total decay, q o gamma and k o exp(G_C - G)
   const int last = max(n - 1, 0);
