@@ -2283,13 +2283,19 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gmat_kernel(
 }
 
 // The decayed pair products per (chunk, head) and the final dq, dk, dg:
-// R(dPm, K) and R(B, K) over j <= i, C(dPm, Q) and C(B, K) over i >= j,
-// each exp(G_i - G_j) formed exactly; the elementwise terms (dq gets
-// dQ_hat o Gamma, dk gets beta dX o Gamma + dK_hat o E, the log-decay
-// gradient dX o X + dQ_hat o Q_hat - dK_hat o K_hat with E = exp(G_C - G),
-// K_hat = k o E, and on the last row the column sums of dK_hat o K_hat and
-// gamma_C d(gamma_C)); then the reverse cumulative sum of the log-decay
-// gradient per channel inside the chunk.
+// R(dPm, K) and R(B, K) over j <= i, C(dPm, Q) and C(B, K) over i >= j, on
+// MFMA (16 x 16 x 32) with the decay factored about the first row rho of each
+// 16-row block b:
+//   R(M, K)_id = e^{G_id - G_rho,d} sum_j M_ij (K_jd e^{G_rho,d - G_jd})   (i in b)
+//   C(M, Z)_jd = e^{G_rho,d - G_jd} sum_i M_ij (Z_id e^{G_id - G_rho,d})   (j in b)
+// where every factor is at most 1 or spans at most the 15 tokens of the
+// block (operand rows past the block's reach are zero, never evaluated).
+// M and the decayed operands go in bf16 high and low parts.  Then the
+// elementwise terms (dq gets dQ_hat o Gamma, dk gets beta dX o Gamma +
+// dK_hat o E, the log-decay gradient dX o X + dQ_hat o Q_hat - dK_hat o K_hat
+// with E = exp(G_C - G), K_hat = k o E, and on the last row the column sums
+// of dK_hat o K_hat and gamma_C d(gamma_C)), and the reverse cumulative sum
+// of the log-decay gradient per channel inside the chunk.
 __global__ __launch_bounds__(GRAD_THREADS) void kda_gpair_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, const int32_t* __restrict__ cu, int nseq, int T, int H,
@@ -2302,7 +2308,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gpair_kernel(
   __shared__ __attribute__((aligned(16))) bf16 Kb[DC * BP];
   __shared__ __attribute__((aligned(16))) float Gl[DC * DD];   // cumulative log decays, then dG
   __shared__ float Mp[DC * CP], Mb[DC * CP];
-  __shared__ float ksum[DD];
+  __shared__ float ksum[DD], Bsh[DC];
   const int chunk = blockIdx.x / H, h = blockIdx.x - chunk * H;
   if (chunk >= header[0] || !delta_saved_for(header, T, H, chunk_cap)) return;
   int c0, n;
@@ -2333,6 +2339,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gpair_kernel(
     Mp[(f / DC) * CP + f % DC] = side[f];
     Mb[(f / DC) * CP + f % DC] = side[DC * DC + f];
   }
+  if (tid < DC) Bsh[tid] = tid < n ? beta[(size_t)(c0 + tid) * H + h] : 0.f;
   __syncthreads();
   if (tid < DD) {
     float acc = 0.f;
@@ -2343,90 +2350,92 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gpair_kernel(
     ksum[tid] = 0.f;
   }
   __syncthreads();
-  const int i0 = (tid / 16) * GR, d8 = (tid % 16) * 8;
+  const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int last = max(n - 1, 0);
-  float gi[GR][8];
+  auto split = [](float x, bf16x8& hi, bf16x8& lo, int e) __attribute__((always_inline)) {
+    hi[e] = (bf16)x;
+    lo[e] = (bf16)(x - (float)hi[e]);
+  };
+  float dgr[4][4];   // this wave's log-decay gradients, held until the column sums are in
 #pragma unroll
-  for (int x = 0; x < GR; ++x)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) gi[x][e] = Gl[(i0 + x) * DD + d8 + e];
-  float rp[GR][8] = {}, rb[GR][8] = {}, cp[GR][8] = {}, cb[GR][8] = {};
-  // rows i = i0 + x: sum over j <= i
-  for (int j = 0; j < i0 + GR; ++j) {
-    const float4 ga = *reinterpret_cast<const float4*>(Gl + j * DD + d8);
-    const float4 gb = *reinterpret_cast<const float4*>(Gl + j * DD + d8 + 4);
-    const float gj[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
-    const bf16x8 kj = *reinterpret_cast<const bf16x8*>(Kb + j * BP + d8);
-#pragma unroll
-    for (int x = 0; x < GR; ++x) {
-      if (j > i0 + x) continue;
-      const float mp = Mp[(i0 + x) * CP + j], mb = Mb[(i0 + x) * CP + j];
+  for (int tt = 0; tt < 4; ++tt) {
+    const int t = wave + 8 * tt, bb = t / 8, d = 16 * (t % 8) + lr;   // block bb, column d
+    const int rho = 16 * bb;
+    f32x4 rp = {0.f, 0.f, 0.f, 0.f}, rb = rp, cp = rp, cb = rp;
+    // R side: rows i = rho + lr, summed over j < rho + 16
+    for (int j0 = 0; j0 < rho + 16; j0 += 32) {
+      bf16x8 aph, apl, abh, abl, bh, bl;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float t = (float)kj[e] * __expf(gi[x][e] - gj[e]);
-        rp[x][e] += mp * t;
-        rb[x][e] += mb * t;
+        const int j = j0 + 8 * lg + e;
+        const bool in = j < rho + 16;
+        split(in ? Mp[(rho + lr) * CP + j] : 0.f, aph, apl, e);
+        split(in ? Mb[(rho + lr) * CP + j] : 0.f, abh, abl, e);
+        const float y = in ? (float)Kb[j * BP + d] * __expf(Gl[rho * DD + d] - Gl[j * DD + d]) : 0.f;
+        split(y, bh, bl, e);
       }
+      rp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aph, bh, rp, 0, 0, 0);
+      rp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aph, bl, rp, 0, 0, 0);
+      rp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(apl, bh, rp, 0, 0, 0);
+      rb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abh, bh, rb, 0, 0, 0);
+      rb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abh, bl, rb, 0, 0, 0);
+      rb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abl, bh, rb, 0, 0, 0);
     }
-  }
-  // rows j = i0 + x as the column side: sum over i >= j
-  for (int i = i0; i < DC; ++i) {
-    const float4 ga = *reinterpret_cast<const float4*>(Gl + i * DD + d8);
-    const float4 gb = *reinterpret_cast<const float4*>(Gl + i * DD + d8 + 4);
-    const float gI[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
-    const bf16x8 qI = *reinterpret_cast<const bf16x8*>(Qb + i * BP + d8);
-    const bf16x8 kI = *reinterpret_cast<const bf16x8*>(Kb + i * BP + d8);
-#pragma unroll
-    for (int x = 0; x < GR; ++x) {
-      if (i < i0 + x) continue;
-      const float mp = Mp[i * CP + i0 + x], mb = Mb[i * CP + i0 + x];
+    // C side: rows j = rho + lr, summed over i >= rho
+    for (int i0 = rho; i0 < DC; i0 += 32) {
+      bf16x8 aph, apl, abh, abl, qh, ql, kh, kl;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float ex = __expf(gI[e] - gi[x][e]);
-        cp[x][e] += mp * (float)qI[e] * ex;
-        cb[x][e] += mb * (float)kI[e] * ex;
+        const int i = i0 + 8 * lg + e;
+        const bool in = i < DC;
+        const int ic = in ? i : DC - 1;   // every load stays inside the tiles
+        split(in ? Mp[ic * CP + rho + lr] : 0.f, aph, apl, e);
+        split(in ? Mb[ic * CP + rho + lr] : 0.f, abh, abl, e);
+        const float ex = in ? __expf(Gl[ic * DD + d] - Gl[rho * DD + d]) : 0.f;
+        split(in ? (float)Qb[ic * BP + d] * ex : 0.f, qh, ql, e);
+        split(in ? (float)Kb[ic * BP + d] * ex : 0.f, kh, kl, e);
       }
+      cp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aph, qh, cp, 0, 0, 0);
+      cp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aph, ql, cp, 0, 0, 0);
+      cp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(apl, qh, cp, 0, 0, 0);
+      cb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abh, kh, cb, 0, 0, 0);
+      cb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abh, kl, cb, 0, 0, 0);
+      cb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abl, kh, cb, 0, 0, 0);
     }
-  }
-  // finish dq, dk and the log-decay gradient (held in rp until written)
+    // lane (lr, lg), register x: row rho + 4 lg + x, column d
 #pragma unroll
-  for (int x = 0; x < GR; ++x) {
-    const int i = i0 + x;
-    const float bi = i < n ? beta[(size_t)(c0 + i) * H + h] : 0.f;
-    const bf16x8 qv = *reinterpret_cast<const bf16x8*>(Qb + i * BP + d8);
-    const bf16x8 kv = *reinterpret_cast<const bf16x8*>(Kb + i * BP + d8);
-    bf16x8 oq, ok;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = d8 + e;
-      const float gam = __expf(gi[x][e]);
-      const float en = i < n ? __expf(Gl[last * DD + d] - gi[x][e]) : 0.f;
+    for (int x = 0; x < 4; ++x) {
+      const int i = rho + 4 * lg + x;
+      const float gi = Gl[i * DD + d], gr = Gl[rho * DD + d];
+      const float eR = __expf(gi - gr), eC = __expf(gr - gi);
+      const float RP = eR * rp[x], RB = eR * rb[x], CPv = eC * cp[x], CB = eC * cb[x];
+      const float gam = __expf(gi);
+      const float en = i < n ? __expf(Gl[last * DD + d] - gi) : 0.f;
       const float dqh = gst[(size_t)i * DD + d];
       const float dkh = gst[(size_t)DC * DD + (size_t)i * DD + d];
       const float dxv = dxb[(size_t)i * DD + d];
-      const float qf = (float)qv[e], kf = (float)kv[e];
-      const float khat = kf * en;
-      oq[e] = (bf16)(dqh * gam + rp[x][e]);
-      ok[e] = (bf16)(bi * dxv * gam + dkh * en + cp[x][e] + rb[x][e] + cb[x][e]);
-      rp[x][e] = qf * rp[x][e] - kf * cp[x][e] + kf * (rb[x][e] - cb[x][e]) +
-                 bi * dxv * kf * gam + dqh * qf * gam - dkh * khat;
+      const float qf = (float)Qb[i * BP + d], kf = (float)Kb[i * BP + d];
+      const float khat = kf * en, bi = Bsh[i];
+      if (i < n) {
+        dq[(size_t)(c0 + i) * rs + (size_t)h * DD + d] = (bf16)(dqh * gam + RP);
+        dk[(size_t)(c0 + i) * rs + (size_t)h * DD + d] =
+            (bf16)(bi * dxv * gam + dkh * en + CPv + RB + CB);
+      }
+      dgr[tt][x] = qf * RP - kf * CPv + kf * (RB - CB) + bi * dxv * kf * gam + dqh * qf * gam -
+                   dkh * khat;
       atomicAdd(&ksum[d], dkh * khat);
-    }
-    if (i < n) {
-      *reinterpret_cast<bf16x8*>(dq + (size_t)(c0 + i) * rs + (size_t)h * DD + d8) = oq;
-      *reinterpret_cast<bf16x8*>(dk + (size_t)(c0 + i) * rs + (size_t)h * DD + d8) = ok;
     }
   }
   __syncthreads();   // every read of the log decays is done and the column sums are complete
 #pragma unroll
-  for (int x = 0; x < GR; ++x) {
-    const int i = i0 + x;
+  for (int tt = 0; tt < 4; ++tt) {
+    const int t = wave + 8 * tt, bb = t / 8, d = 16 * (t % 8) + lr;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = d8 + e;
-      float dgv = rp[x][e];
-      if (i == last) dgv += ksum[d] + rec[KdaRecord::SIDE + d];
-      Gl[i * DD + d] = dgv;
+    for (int x = 0; x < 4; ++x) {
+      const int i = 16 * bb + 4 * lg + x;
+      float v = dgr[tt][x];
+      if (i == last) v += ksum[d] + rec[KdaRecord::SIDE + d];
+      Gl[i * DD + d] = v;
     }
   }
   __syncthreads();
