@@ -159,10 +159,15 @@ def cpu_baseline(layers, seed, min_seconds=10.0, max_reps=4):
 
 
 def sources_sha256() -> str:
+    """Hash of the sources the attention kernels are compiled from: every file
+    under csrc/ except delta.hip, the translation unit that holds only the
+    delta-rule kernels (it changes none of the attention kernels' code)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "varlen_sliding_window_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if name == "delta.hip":
+            continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
