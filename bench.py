@@ -15,7 +15,14 @@ forward and 10*d backward, pairs counted exactly from cu_seqlens and the
 window.  Prints one JSON line.
 
     python bench.py [--steps 20] [--warmup 50] [--workload ctx4096_w512+global]
-                    [--softcap C] [--head-dim D] [--band]
+                    [--softcap C] [--head-dim D] [--band] [--seeds 8] [--settle-ms 300]
+
+Before the W warm-up steps the step runs untimed for --settle-ms of wall time
+(the GPU clock needs a few tens of ms of load to leave its idle state); the
+timed region is exactly K steps.  The line also carries the per-layer and
+per-kernel times, the dominant kernel's roofline, a graph-replay timing,
+the same step on seeds 0..7 (K steps each, with their aggregate), the CPU
+oracle's rate, and the timed outputs' errors against the oracle ("parity").
 
 --softcap C times the same step with every logit soft-capped to
 C tanh(logit / C) (attn_varlen_fwd_ex / attn_varlen_bwd_ex); the counted
@@ -90,6 +97,10 @@ def build_layers(workload: str, seed: int, device, softcap: float = 0.0, head_di
     spec = WORKLOADS[workload]
     cu, _ = make_cu_seqlens(CONFIGS[spec[0][1]], seed)
     layers = []
+    # Layers that share the microbatch's cu_seqlens and a window share one
+    # workspace: the first of them builds the tile schedule, the others reuse
+    # it (ATTN_FWD_REUSE_SCHEDULE), as a training step over a layer stack can.
+    shared_ws = {}
     for idx, (label, cname) in enumerate(spec):
         cfg = CONFIGS[cname]
         if head_dim:
@@ -102,6 +113,11 @@ def build_layers(workload: str, seed: int, device, softcap: float = 0.0, head_di
 
         q, k, v, do = dev(mb.q_bits), dev(mb.k_bits), dev(mb.v_bits), dev(mb.dout_bits)
         t, hq, d = q.shape
+        key = (cfg.window, hq)
+        reuse_fwd = key in shared_ws and not band
+        if key not in shared_ws:
+            shared_ws[key] = attn.new_workspace(t, len(cu) - 1, hq, k.shape[1], d,
+                                                mb.max_seqlen, cfg.window, device)
         lay = {
             "label": label, "cfg": cfg, "mb": mb, "q": q, "k": k, "v": v, "do": do,
             "cu": torch.from_numpy(cu.astype(np.int32)).to(device),
@@ -109,8 +125,8 @@ def build_layers(workload: str, seed: int, device, softcap: float = 0.0, head_di
             "out": torch.empty_like(q), "lse": torch.empty((hq, t), dtype=torch.float32,
                                                            device=device),
             "dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
-            "ws": attn.new_workspace(t, len(cu) - 1, hq, k.shape[1], d, mb.max_seqlen,
-                                     cfg.window, device),
+            "reuse_fwd": reuse_fwd,
+            "ws": shared_ws[key],
             "flops": attention_flops(cu, cfg.window, hq, d),
             "softcap": softcap,
             "band": band and cfg.window > 0,
@@ -121,7 +137,8 @@ def build_layers(workload: str, seed: int, device, softcap: float = 0.0, head_di
 
 def run_layer(attn, L):
     attn.fwd(L["q"], L["k"], L["v"], L["cu"], L["max_seqlen"], L["window"], L["scale"],
-             out=L["out"], lse=L["lse"], workspace=L["ws"], softcap=L["softcap"], band=L["band"])
+             out=L["out"], lse=L["lse"], workspace=L["ws"], softcap=L["softcap"], band=L["band"],
+             reuse_schedule=L["reuse_fwd"])
     # the backward of a layer reuses the tile schedule its forward just built
     # (the band-block backward always rebuilds its own)
     attn.bwd(L["q"], L["k"], L["v"], L["out"], L["lse"], L["do"], L["cu"], L["max_seqlen"],
@@ -131,21 +148,25 @@ def run_layer(attn, L):
 
 def cpu_baseline(layers, seed, min_seconds=10.0, max_reps=4):
     """The CPU oracle, as it stands, on the step's layers (fwd+bwd each),
-    repeated until at least min_seconds of CPU work (bounded by max_reps)."""
+    repeated until at least min_seconds of CPU work (bounded by max_reps).
+    Also returns the oracle's results of the first repetition, per layer."""
     from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import attention_backward
 
     cores = len(os.sched_getaffinity(0))
     reps = 0
     flops = 0
+    results = []
     t0 = time.perf_counter()
     with threadpool_limits(limits=cores):
         used = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
         while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < min_seconds):
             for L in layers:
                 mb = L["mb"]
-                attention_backward(mb.f32("q"), mb.f32("k"), mb.f32("v"), mb.f32("dout"),
-                                   mb.cu_seqlens, L["window"], L["scale"], L["softcap"])
+                r = attention_backward(mb.f32("q"), mb.f32("k"), mb.f32("v"), mb.f32("dout"),
+                                       mb.cu_seqlens, L["window"], L["scale"], L["softcap"])
+                if reps == 0:
+                    results.append(r)
                 flops += L["flops"]["fwd_bwd"]
             reps += 1
     secs = time.perf_counter() - t0
@@ -155,7 +176,30 @@ def cpu_baseline(layers, seed, min_seconds=10.0, max_reps=4):
             "seconds": secs, "cpu": cpu_info(),
             "sample": (f"{reps} x one step ({labels}, forward+backward) of the seed-{seed} "
                        f"microbatch, {mb.num_seqs} segments, all {mb.cfg.num_q_heads} query heads; "
-                       f"fp64 NumPy oracle; counted flops / wall seconds")}
+                       f"fp64 NumPy oracle; counted flops / wall seconds")}, results
+
+
+def parity_report(layers, oracle_results):
+    """The timed step's outputs (every layer's out, lse, dq, dk, dv as the last
+    timed step left them) against the oracle's: norm-wise max-rel and
+    Frobenius-rel per tensor, worst over the layers of each label, and
+    whether every one meets the bar (max-rel <= 1e-2, Fro-rel <= 5e-3)."""
+    report = {}
+    ok = True
+    for L, (dq, dk, dv, out, lse, _) in zip(layers, oracle_results):
+        rep = report.setdefault(L["label"], {})
+        for name, ref in (("out", out), ("dq", dq), ("dk", dk), ("dv", dv)):
+            x = L[name].float().cpu().numpy().astype(np.float64)
+            d = x - ref
+            mr = float(np.max(np.abs(d)) / np.max(np.abs(ref)))
+            fr = float(np.linalg.norm(d) / np.linalg.norm(ref))
+            prev = rep.get(name, {"max_rel": 0.0, "fro_rel": 0.0})
+            rep[name] = {"max_rel": max(prev["max_rel"], mr), "fro_rel": max(prev["fro_rel"], fr)}
+            ok = ok and mr <= 1e-2 and fr <= 5e-3 and bool(np.all(np.isfinite(x)))
+        le = float(np.max(np.abs(L["lse"].cpu().numpy().astype(np.float64) - lse)))
+        rep["lse_max_abs"] = max(rep.get("lse_max_abs", 0.0), le)
+    return {"bar": {"max_rel": 1e-2, "fro_rel": 5e-3}, "pass": ok, "layers": report,
+            "reference": "CPU oracle (fp64) on the same seeded inputs"}
 
 
 def sources_sha256() -> str:
@@ -363,6 +407,13 @@ def main():
                     help="skip the graph-replay timing (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain copies of a known size (counter calibration)")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed steps before the warm-up until this much wall time has "
+                         "passed: the GPU clock leaves its idle state only after a few tens "
+                         "of ms of load (0: none)")
+    ap.add_argument("--seeds", type=int, default=8,
+                    help="also time seeds 0 .. N-1 of the workload (K steps each) and report "
+                         "each and their aggregate (0 or 1: the headline seed only)")
     args = ap.parse_args()
     if args.print_sources_sha:
         print(sources_sha256())
@@ -403,6 +454,14 @@ def main():
             if events is not None:
                 events[i][1].record()
 
+    # The clock settles first (untimed, reported), then the W warm-up steps.
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        step()
+        torch.cuda.synchronize()
+        settle_steps += 1
+    settle_s = time.perf_counter() - t_settle
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -512,6 +571,40 @@ def main():
                         "speedup_vs_eager": ms_per_step / graph_ms, "steps": args.steps}
         del graph
 
+    # Other seeds of the same workload (other document mixes), K timed steps
+    # each after a few warm-up steps; the headline seed's figure is the one
+    # measured above.  The aggregate is total flops over total time.
+    seeds_report = None
+    if args.seeds > 1:
+        per_seed = {str(args.seed): {"ms_per_step": ms_per_step, "gflop": step_flops / 1e9,
+                                     "tflops": value, "num_seqs": len(cu) - 1}}
+        for sd in range(args.seeds):
+            if sd == args.seed:
+                continue
+            print(f"[bench] seed {sd}", file=sys.stderr, flush=True)
+            cu_s, lay_s = build_layers(args.workload, sd, device, args.softcap, args.head_dim,
+                                       args.band)
+            for _ in range(max(args.warmup, 3)):
+                for L in lay_s:
+                    run_layer(attn, L)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                for L in lay_s:
+                    run_layer(attn, L)
+            torch.cuda.synchronize()
+            ms_s = (time.perf_counter() - t0) * 1e3 / args.steps
+            fl = sum(L["flops"]["fwd_bwd"] for L in lay_s)
+            per_seed[str(sd)] = {"ms_per_step": ms_s, "gflop": fl / 1e9,
+                                 "tflops": fl / (ms_s * 1e-3) / 1e12, "num_seqs": len(cu_s) - 1}
+            del lay_s
+        tot_fl = sum(v["gflop"] for v in per_seed.values()) * 1e9
+        tot_ms = sum(v["ms_per_step"] for v in per_seed.values())
+        seeds_report = {"per_seed": per_seed, "steps_each": args.steps,
+                        "aggregate_tflops": tot_fl / (tot_ms * 1e-3) / 1e12,
+                        "aggregate_frac_of_peak": tot_fl / (tot_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                        "mean_ms_per_step": tot_ms / len(per_seed)}
+
     result = {
         "metric": "fwd+bwd TFLOPS per 16,384-token microbatch (window-512 and global layers, "
                   "context 4,096)",
@@ -541,15 +634,21 @@ def main():
             "softcap": args.softcap if args.softcap > 0 else None,
             "band": True if args.band else None,
         },
+        "frac_of_peak": value / PEAK_BF16_TFLOPS,
+        "clock_settle": {"steps": settle_steps, "seconds": settle_s,
+                         "note": "untimed steps before the W warm-up steps"},
         "layers": layer_report,
         "kernels": kernels,
         "roofline": roofline,
         "graph_replay": graph_report,
+        "seeds": seeds_report,
         "gpu": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(layers, args.seed)
+        result["cpu_baseline"], oracle_results = cpu_baseline(layers, args.seed)
+        # the outputs the timed steps produced, against the oracle's
+        result["parity"] = parity_report(layers, oracle_results)
     print(json.dumps(result), flush=True)
 
 

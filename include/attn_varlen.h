@@ -6,9 +6,8 @@
  * What the library computes
  * -------------------------
  * A packed microbatch of T tokens is split into segments [cu[s], cu[s+1]).
- * No token attends across its own segment boundary and attention is causal
- * inside a segment (research.dws.rip/llm/kernels, section 01 "How it was
- * measured").  Local layers add a sliding window, global layers use full
+ * Attention is confined to each segment and causal inside it
+ * (research.dws.rip/llm/kernels, section 01 "How it was measured").  Local layers add a sliding window, global layers use full
  * causal context; query heads share key-value heads in groups (same page,
  * Fig. 2 "Benchmark setup": 8 query / 2 key-value heads of width 128,
  * 512-token window; section 02: the call is a varlen attention with sliding
@@ -41,15 +40,20 @@
  *                      (research.dws.rip/llm/kernels, section 06 "CUDA
  *                      graphs work, with padding")
  *   max_seqlen       : >= the longest segment (used to bound the schedule)
- *   supported shapes : D in {64, 128, 256}, Hq % Hkv == 0, (Hq / Hkv) % 4 == 0,
- *                      and k (T x Hkv x D bf16) under 4 GiB
+ *   supported shapes : D in {64, 128, 256}, any Hq % Hkv == 0 (grouped,
+ *                      multi-query or multi-head), and k (T x Hkv x D bf16)
+ *                      under 4 GiB
  *
  * Execution
  *   Every call enqueues its kernels on `stream` and returns without waiting
  *   and without reading device memory on the host, so calls can be captured
- *   in a HIP graph.  The contents of cu_seqlens are not validated on the
- *   host (that would need a device read).  Calls are deterministic: the same
- *   inputs give bit-identical outputs (no floating-point atomics).
+ *   in a HIP graph.  The contents of cu_seqlens are checked on the device
+ *   by the schedule kernel (cu[0] = 0, non-decreasing, cu[num_seqs] = T):
+ *   malformed boundaries make every output of the call NaN (the kernels stay
+ *   inside their buffers either way); the host cannot see them without a
+ *   device read, so the call still returns ATTN_OK.  Calls are
+ *   deterministic: the same inputs give bit-identical outputs (no
+ *   floating-point atomics).
  *
  * Errors
  *   Host-checkable problems return a negative attn_status before anything is
@@ -69,7 +73,7 @@ extern "C" {
 typedef enum {
   ATTN_OK = 0,
   ATTN_EINVAL = -1,       /* null/misaligned pointer, bad size, bad scale, ... */
-  ATTN_EUNSUPPORTED = -2, /* valid arguments this build does not implement (D, group % 4, k >= 4 GiB) */
+  ATTN_EUNSUPPORTED = -2, /* valid arguments this build does not implement (D, k >= 4 GiB) */
   ATTN_EWORKSPACE = -3,   /* workspace null or smaller than attn_varlen_workspace_size() */
   ATTN_EDEVICE = -4,      /* no usable gfx950 device / HIP runtime error before launch */
   ATTN_ELAUNCH = -5       /* a kernel launch failed */
@@ -134,25 +138,29 @@ attn_status attn_varlen_bwd(const void* q, const void* k, const void* v,
  * arguments as there; the backward must get the same softcap as the forward
  * that produced out and lse.
  *   softcap   finite and >= 0; negative, NaN or infinite -> ATTN_EINVAL
- *   flags     (backward) 0 or ATTN_BWD_REUSE_SCHEDULE; other bits -> ATTN_EINVAL
+ *   flags     forward: 0 or ATTN_FWD_REUSE_SCHEDULE; backward: 0 or
+ *             ATTN_BWD_REUSE_SCHEDULE; other bits -> ATTN_EINVAL
  *
- * ATTN_BWD_REUSE_SCHEDULE: every forward call leaves in its workspace the
- * tile schedule of both passes (it depends only on cu_seqlens, the sizes and
- * the window).  A backward call that passes this flag with the same
- * workspace, after a forward call on the same stream with the same
- * cu_seqlens contents, num_seqs, total_tokens, num_q_heads and window (the
- * pair of calls of one layer in a training step), skips rebuilding it.  The
- * caller vouches for the cu_seqlens contents; the kernels check the rest on
- * the device and do nothing (outputs unwritten) if the schedule in the
- * workspace was built for another total_tokens, num_seqs or window.
+ * Schedule reuse: every forward call that builds a schedule leaves in its
+ * workspace the tile lists of both passes (they depend only on cu_seqlens,
+ * total_tokens, num_seqs and the window).  A later call on the same stream
+ * with the same workspace and the same cu_seqlens contents, num_seqs,
+ * total_tokens and window may skip rebuilding them: the backward of the same
+ * layer (ATTN_BWD_REUSE_SCHEDULE), or the forward (ATTN_FWD_REUSE_SCHEDULE)
+ * and backward of another layer of a stack that shares the boundaries and
+ * the window.  The caller vouches for the cu_seqlens contents; the kernels
+ * compare total_tokens, num_seqs and the window with the schedule's record
+ * on the device and, if they differ (or the schedule's boundaries were
+ * malformed), write NaN to every output of the call instead of computing
+ * it.  Calls that share a workspace must not overlap in time (one stream).
  */
-enum { ATTN_BWD_REUSE_SCHEDULE = 1 };
+enum { ATTN_BWD_REUSE_SCHEDULE = 1, ATTN_FWD_REUSE_SCHEDULE = 1 };
 
 attn_status attn_varlen_fwd_ex(const void* q, const void* k, const void* v,
                                const int32_t* cu_seqlens, int32_t num_seqs,
                                int32_t total_tokens, int32_t num_q_heads, int32_t num_kv_heads,
                                int32_t head_dim, int32_t max_seqlen, int32_t window, float scale,
-                               float softcap, void* out, float* lse,
+                               float softcap, uint32_t flags, void* out, float* lse,
                                void* workspace, size_t workspace_bytes, attn_stream_t stream);
 
 attn_status attn_varlen_bwd_ex(const void* q, const void* k, const void* v,

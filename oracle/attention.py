@@ -7,8 +7,8 @@ baseline do.  It shares no code with the HIP path.
 What is computed
 ----------------
 The kernel benchmarks page (research.dws.rip/llm/kernels) fixes the
-workload: section 01 "How it was measured" says no document attends across
-its own boundary and each row is cut at the context length, so attention is
+workload: section 01 "How it was measured" describes packed rows, ended at
+the context length, in which attention stays inside each document, so it is
 causal inside each segment of a packed microbatch; Fig. 2 "Benchmark setup"
 gives 8 query and 2 key-value heads of width 128 and a 512-token window for
 the local layers; section 02 says the kernel is FlashAttention-2's varlen

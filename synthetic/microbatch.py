@@ -8,8 +8,8 @@ What it stands in for
 ---------------------
 The kernel benchmarks page (research.dws.rip/llm/kernels, section 01 "How it
 was measured", and Fig. 2 "Benchmark setup") times attention on 16,384-token
-microbatches cut from real token shards: documents never attend across their
-own boundary, each row is cut at the context length (512 to 4,096), the
+microbatches cut from real token shards: attention is confined to each
+document, rows end every 512 to 4,096 tokens (the context length), the
 median document is 457 tokens and almost half of the tokens sit in long
 documents. Those shards are not available, so this generator draws document
 lengths from a lognormal with median 457 and sigma 1.6 instead, lays the

@@ -80,8 +80,8 @@ def call_fwd(lib, **over):
     ({"ms": 65}, EINVAL), ({"scale": 0.0}, EINVAL), ({"scale": -1.0}, EINVAL),
     ({"scale": float("nan")}, EINVAL), ({"scale": float("inf")}, EINVAL),
     ({"d": 96}, EUNSUPPORTED), ({"d": 32}, EUNSUPPORTED), ({"d": 512}, EUNSUPPORTED),
-    ({"d": 0}, EUNSUPPORTED), ({"hq": 2, "hkv": 1}, EUNSUPPORTED),
-    ({"hq": 8, "hkv": 8}, EUNSUPPORTED), ({"ws": None}, EWORKSPACE), ({"wsb": 16}, EWORKSPACE),
+    ({"d": 0}, EUNSUPPORTED), ({"hq": 2, "hkv": 4}, EINVAL), ({"hq": 6, "hkv": 4}, EINVAL),
+    ({"hkv": 0}, EINVAL), ({"ws": None}, EWORKSPACE), ({"wsb": 16}, EWORKSPACE),
     ({"ws": FAKE + 16}, EWORKSPACE),
 ])
 def test_fwd_rejects(lib, over, code):
@@ -90,11 +90,18 @@ def test_fwd_rejects(lib, over, code):
 
 @pytest.mark.parametrize("cap", [-1.0, -1e-30, float("nan"), float("inf"), float("-inf")])
 def test_softcap_rejects(lib, cap):
-    args = [FAKE] * 4 + [1, 64, 8, 2, 128, 64, 0, 0.088, cap, FAKE, FAKE, FAKE, 1 << 30, None]
+    args = [FAKE] * 4 + [1, 64, 8, 2, 128, 64, 0, 0.088, cap, 0, FAKE, FAKE, FAKE, 1 << 30, None]
     assert lib.attn_varlen_fwd_ex(*args) == EINVAL
     bargs = [FAKE] * 7 + [1, 64, 8, 2, 128, 64, 0, 0.088, cap, 0, FAKE, FAKE, FAKE, FAKE,
                           1 << 30, None]
     assert lib.attn_varlen_bwd_ex(*bargs) == EINVAL
+
+
+@pytest.mark.parametrize("flags", [2, 4, 0x80000000, 3])
+def test_fwd_ex_rejects_unknown_flags(lib, flags):
+    args = [FAKE] * 4 + [1, 64, 8, 2, 128, 64, 0, 0.088, 0.0, flags, FAKE, FAKE, FAKE, 1 << 30,
+                         None]
+    assert lib.attn_varlen_fwd_ex(*args) == EINVAL
 
 
 @pytest.mark.parametrize("flags", [2, 4, 0x80000000, 3])

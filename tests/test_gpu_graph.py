@@ -9,7 +9,8 @@ whole fwd + bwd call sequence can be captured once and replayed while the
 caller rewrites the boundary list in place between replays.  Each replay
 must equal an eager run on the same boundaries bit for bit.  Replays are
 interleaved with eager work and host synchronisations, and every replay is
-checked, as graphs of this kind are known to go wrong only on later replays.
+checked, as graphs of this kind are known to go wrong only on later replays;
+one later replay is also held to the oracle.
 """
 from __future__ import annotations
 
@@ -20,7 +21,8 @@ import torch
 import varlen_sliding_window_amd as attn
 from synthetic import CONFIGS, make_cu_seqlens, make_custom
 
-from gpu_common import bits_to_torch
+from gpu_common import assert_parity, bits_to_torch
+from oracle import attention_backward
 
 pytestmark = pytest.mark.gpu
 
@@ -96,3 +98,12 @@ def test_graph_replay_matches_eager(window, reuse):
             assert torch.equal(got.view(torch.int16) if got.dtype == torch.bfloat16 else got,
                                want.view(torch.int16) if want.dtype == torch.bfloat16 else want), \
                 f"replay {rep} (boundaries {i}, window {window}): {name} differs from eager"
+        if rep == 4:
+            # a later replay (boundary set 0, the workload's ctx-4,096 packing)
+            # against the oracle, whole arrays
+            got = {n: t.float().cpu().numpy().astype(np.float64)
+                   for n, t in zip(("out", "lse", "dq", "dk", "dv"), outs)}
+            dq_r, dk_r, dv_r, out_r, lse_r, _ = attention_backward(
+                mb.f32("q"), mb.f32("k"), mb.f32("v"), mb.f32("dout"), bounds[i], window, scale)
+            assert_parity(got, {"dq": dq_r, "dk": dk_r, "dv": dv_r, "out": out_r, "lse": lse_r},
+                          f"graph replay {rep}, window {window}")

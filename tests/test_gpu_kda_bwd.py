@@ -89,6 +89,31 @@ def test_kda_bwd_workload_microbatch_sampled():
                 f"T=16,384 H=8, document {s} ({hi - lo} tokens)")
 
 
+def test_kda_bwd_workload_longest_document():
+    """The longest document of the workload microbatch (3,678 tokens at seed
+    0), all 8 heads, against the oracle run on that document alone."""
+    cu, _ = make_cu_seqlens(CONFIGS["ctx4096_w512"], 0)
+    t = int(cu[-1])
+    inp = make_kda_inputs(cu, 8, 128, seed=0)
+    dout = make_delta_dout(t, 8, 128, seed=1)
+    got = run(inp, dout, 128 ** -0.5)
+    s = int(np.argmax(np.diff(cu)))
+    lo, hi = int(cu[s]), int(cu[s + 1])
+    print(f"[case] kda bwd longest document {s}: {hi - lo} tokens", flush=True)
+    compare([x[lo:hi] for x in got], reference(inp, dout, 128 ** -0.5, lo, hi),
+            f"T=16,384 H=8, longest document {s} ({hi - lo} tokens)")
+
+
+def test_kda_bwd_repeatable():
+    cu = np.array([0, 70, 200], dtype=np.int32)
+    inp = make_kda_inputs(cu, 2, 128, seed=52)
+    dout = make_delta_dout(200, 2, 128, seed=53)
+    a = run(inp, dout, 0.3)
+    b = run(inp, dout, 0.3)
+    for name, x, y in zip(NAMES, a, b):   # fixed-order sums everywhere: bit for bit
+        assert np.array_equal(x, y), name
+
+
 def test_kda_bwd_strong_decay():
     inp = make_kda_inputs(np.array([0, 150, 300], dtype=np.int32), 2, 128, seed=45)
     g = np.log(np.random.default_rng(46).uniform(0.05, 1.0, size=inp.g.shape)).astype(np.float32)
@@ -132,11 +157,10 @@ def test_kda_bwd_reusing_a_saving_forward():
         got = attn.kda_bwd(q, k, v, g, beta, do, cu_d, workspace=ws, reuse=True)
         torch.cuda.synchronize()
         for name, x, y in zip(NAMES, got, ref):
-            if name in ("dv",):
-                assert torch.equal(x, y), (rep, name)
-            else:   # LDS float atomics may add in another order
-                torch.testing.assert_close(x.float(), y.float(), rtol=1e-2, atol=1e-5)
+            assert torch.equal(x, y), (rep, name)
     attn.kda_fwd(q, k, v, g, beta, cu_d, workspace=ws)           # saves nothing
-    got = attn.kda_bwd(q, k, v, g, beta, do, cu_d, workspace=ws, reuse=True)
+    with pytest.raises(ValueError):                              # the binding's own record
+        attn.kda_bwd(q, k, v, g, beta, do, cu_d, workspace=ws, reuse=True)
+    got = attn.kda_bwd(q, k, v, g, beta, do, cu_d, workspace=ws, reuse=True, check_reuse=False)
     torch.cuda.synchronize()
-    assert all(torch.count_nonzero(x) == 0 for x in got), "ran on a workspace not saved for it"
+    assert all(torch.isnan(x.float()).all() for x in got), "ran on a workspace not saved for it"

@@ -32,7 +32,7 @@ def _need_gpu():
 
 @pytest.mark.parametrize("name", ["tiny_ctx512_w512", "ctx512_w512", "ctx4096_w512",
                                   "ctx4096_global", "ctx1024_global", "ctx2048_global",
-                                  "ctx4096_w512_h16"])
+                                  "ctx4096_w512_h16", "ctx4096_global_h16"])
 def test_parity_config(name):
     cfg = CONFIGS[name]
     mb = make_microbatch(cfg, 0)

@@ -1,7 +1,9 @@
-"""A backward call that reuses the forward call's tile schedule
-(ATTN_BWD_REUSE_SCHEDULE) gives the same results, bit for bit, as one that
-rebuilds it; with a schedule built for another window the kernels leave the
-outputs untouched (the device-side check of the workspace header)."""
+"""Schedule reuse and boundary checks: a backward call that reuses the
+forward call's tile schedule (ATTN_BWD_REUSE_SCHEDULE), and the layers of a
+stack that share one schedule (ATTN_FWD_REUSE_SCHEDULE), give the same
+results, bit for bit, as calls that rebuild it; a schedule built for another
+window is refused by the binding and, on the device, turns every output into
+NaN; malformed boundaries do the same."""
 from __future__ import annotations
 
 import numpy as np
@@ -10,7 +12,7 @@ import pytest
 torch = pytest.importorskip("torch")
 
 import varlen_sliding_window_amd as attn  # noqa: E402
-from synthetic import make_microbatch  # noqa: E402
+from synthetic import CONFIGS, make_cu_seqlens, make_layer, make_microbatch  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -46,7 +48,7 @@ def test_reused_schedule_is_bitwise_equal(name, softcap):
         assert torch.equal(_views(a), _views(b)), f"{name_} differs with a reused schedule"
 
 
-def test_schedule_for_another_window_is_refused_on_device():
+def test_schedule_for_another_window_is_refused():
     mb = make_microbatch("tiny_ctx512_w512", 3)
     q, k, v, do, cu = device_inputs(mb)
     t, hq, d = q.shape
@@ -54,14 +56,74 @@ def test_schedule_for_another_window_is_refused_on_device():
     ws = attn.new_workspace(t, mb.num_seqs, hq, k.shape[1], d, ms, 512, q.device)
     out, lse = attn.fwd(q, k, v, cu, ms, 0, sc)              # outputs for window 0
     attn.fwd(q, k, v, cu, ms, 64, sc, workspace=ws)          # schedule for window 64
-    dq, dk, dv = (torch.full_like(x, float("nan")) for x in (q, k, v))
+    # the binding's record of the workspace refuses the call on the host
+    with pytest.raises(ValueError):
+        attn.bwd(q, k, v, out, lse, do, cu, ms, 0, sc, workspace=ws, reuse_schedule=True)
+    with pytest.raises(ValueError):
+        attn.fwd(q, k, v, cu, ms, 0, sc, workspace=ws, reuse_schedule=True)
+    # the device-side check: every output of the call becomes NaN
+    dq, dk, dv = (torch.zeros_like(x) for x in (q, k, v))
     attn.bwd(q, k, v, out, lse, do, cu, ms, 0, sc, dq=dq, dk=dk, dv=dv, workspace=ws,
-             reuse_schedule=True)
+             reuse_schedule=True, check_reuse=False)
+    o2, l2 = torch.zeros_like(out), torch.zeros_like(lse)
+    attn.fwd(q, k, v, cu, ms, 0, sc, out=o2, lse=l2, workspace=ws, reuse_schedule=True,
+             check_reuse=False)
     torch.cuda.synchronize()
-    for x in (dq, dk, dv):
+    for x in (dq, dk, dv, o2, l2):
         assert torch.isnan(x.float()).all(), "kernels ran on a schedule built for another window"
-    # the same call without the flag rebuilds the schedule and fills them
+    # the same calls without the flag rebuild the schedule and fill them
     attn.bwd(q, k, v, out, lse, do, cu, ms, 0, sc, dq=dq, dk=dk, dv=dv, workspace=ws)
+    attn.fwd(q, k, v, cu, ms, 0, sc, out=o2, lse=l2, workspace=ws)
     torch.cuda.synchronize()
-    for x in (dq, dk, dv):
+    for x in (dq, dk, dv, o2, l2):
         assert torch.isfinite(x.float()).all()
+
+
+@pytest.mark.parametrize("window", [512, 0])
+def test_one_schedule_serves_a_stack_of_layers(window):
+    """Layers that share cu_seqlens and the window (the per-microbatch stack of
+    15 local + 5 global layers) may build the schedule once: every later
+    forward and backward reuses it, with results equal bit for bit to calls
+    that rebuild it."""
+    name = "ctx4096_w512" if window else "ctx4096_global"
+    cfg = CONFIGS[name]
+    cu_np, _ = make_cu_seqlens(cfg, 4)
+    ws = None
+    for layer in range(3):
+        mb = make_layer(cfg, 4, layer, cu_np)
+        q, k, v, do, cu = device_inputs(mb)
+        t, hq, d = q.shape
+        sc, ms = cfg.scale, mb.max_seqlen
+        if ws is None:
+            ws = attn.new_workspace(t, mb.num_seqs, hq, k.shape[1], d, ms, window, q.device)
+        out, lse = attn.fwd(q, k, v, cu, ms, window, sc, workspace=ws,
+                            reuse_schedule=layer > 0)
+        got = attn.bwd(q, k, v, out, lse, do, cu, ms, window, sc, workspace=ws,
+                       reuse_schedule=True)
+        ref_out, ref_lse = attn.fwd(q, k, v, cu, ms, window, sc)
+        ref = attn.bwd(q, k, v, ref_out, ref_lse, do, cu, ms, window, sc)
+        torch.cuda.synchronize()
+        for name_, a, b in zip(("out", "lse", "dq", "dk", "dv"), (out, lse) + got,
+                               (ref_out, ref_lse) + ref):
+            assert torch.equal(_views(a), _views(b)), f"layer {layer}: {name_} differs"
+
+
+@pytest.mark.parametrize("case", ["first_not_zero", "decreasing", "last_not_T"])
+def test_malformed_boundaries_give_nan_outputs(case):
+    """Boundaries that break cu[0] = 0, non-decreasing or cu[n] = T are caught
+    by the schedule kernel on the device: every output of the call is NaN (the
+    kernels stay inside their buffers, and nothing waits for the host)."""
+    mb = make_microbatch("tiny_ctx512_w512", 9)
+    q, k, v, do, cu = device_inputs(mb)
+    t = q.shape[0]
+    bad = {"first_not_zero": [5, 300, 700, t], "decreasing": [0, 300, 200, t],
+           "last_not_T": [0, 300, 700, t - 3]}[case]
+    bad = np.asarray(bad, dtype=np.int32)
+    cu_bad = torch.from_numpy(bad).cuda()
+    print(f"[case] malformed cu_seqlens ({case}): {bad.tolist()}", flush=True)
+    out, lse = attn.fwd(q, k, v, cu_bad, t, 512, mb.cfg.scale)
+    good_out, good_lse = attn.fwd(q, k, v, cu, mb.max_seqlen, 512, mb.cfg.scale)
+    dq, dk, dv = attn.bwd(q, k, v, good_out, good_lse, do, cu_bad, t, 512, mb.cfg.scale)
+    torch.cuda.synchronize()
+    for name_, x in (("out", out), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
+        assert torch.isnan(x.float()).all(), f"{case}: {name_} not NaN"

@@ -42,6 +42,7 @@ def _need_gpu():
     ("ctx4096_w512", 2.0, 1.0),
     ("ctx4096_global", 30.0, 8.0),
     ("ctx4096_w512_h16", 50.0, 4.0),
+    ("ctx4096_global_h16", 20.0, 4.0),
 ])
 def test_softcap_parity_config(name, cap, scale_mul):
     cfg = CONFIGS[name]

@@ -18,10 +18,33 @@ LIBRARY_PATH = os.path.join(_HERE, "libattn_varlen.so")
 
 ATTN_OK = 0
 ATTN_BWD_REUSE_SCHEDULE = 1
+ATTN_FWD_REUSE_SCHEDULE = 1
+ATTN_DELTA_FWD_SAVE = 1
+ATTN_DELTA_BWD_REUSE = 1
 STATUS_NAMES = {0: "ATTN_OK", -1: "ATTN_EINVAL", -2: "ATTN_EUNSUPPORTED",
                 -3: "ATTN_EWORKSPACE", -4: "ATTN_EDEVICE", -5: "ATTN_ELAUNCH"}
 
 _lib = None
+
+# What the last call that built a schedule (or saved delta-rule state) left in
+# each workspace, keyed by the workspace's device address and size: a reuse
+# that does not match is refused here, before the device-side check (which
+# would turn the outputs into NaN).
+_WS_RECORD: dict = {}
+
+
+def _ws_key(ws) -> tuple:
+    return (ws.device.index, ws.data_ptr(), ws.numel())
+
+
+def _effective_window(window: int, total_tokens: int) -> int:
+    return 0 if window <= 0 or window >= total_tokens else int(window)
+
+
+def _check_reuse(ws, want: tuple, what: str) -> None:
+    have = _WS_RECORD.get(_ws_key(ws))
+    if have != want:
+        raise ValueError(f"{what}: the workspace holds {have}, this call needs {want}")
 
 
 class KernelStats(ctypes.Structure):
@@ -56,7 +79,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                     i32, ctypes.c_float, vp, vp, vp, vp, sz, vp]
     lib.attn_varlen_bwd.restype = ctypes.c_int
     lib.attn_varlen_fwd_ex.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
-                                       ctypes.c_float, ctypes.c_float, vp, vp, vp, sz, vp]
+                                       ctypes.c_float, ctypes.c_float, ctypes.c_uint32, vp, vp,
+                                       vp, sz, vp]
     lib.attn_varlen_fwd_ex.restype = ctypes.c_int
     lib.attn_varlen_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                        i32, i32, ctypes.c_float, ctypes.c_float, ctypes.c_uint32,
@@ -151,12 +175,18 @@ def new_workspace(total_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, m
 
 
 def fwd(q, k, v, cu_seqlens, max_seqlen: int, window: int, scale: float | None = None,
-        out=None, lse=None, workspace=None, softcap: float = 0.0, band: bool = False):
-    """attn_varlen_fwd (attn_varlen_fwd_ex when softcap > 0, attn_varlen_band_fwd
-    when band): returns (out [T,Hq,D] bf16, lse [Hq,T] fp32).
+        out=None, lse=None, workspace=None, softcap: float = 0.0, band: bool = False,
+        reuse_schedule: bool = False, check_reuse: bool = True):
+    """attn_varlen_fwd (attn_varlen_fwd_ex with a soft-cap or reuse_schedule,
+    attn_varlen_band_fwd when band): returns (out [T,Hq,D] bf16, lse [Hq,T] fp32).
 
     softcap > 0 caps every logit to softcap * tanh(logit / softcap); band runs
-    the band-block formulation (window >= 1, no soft-cap)."""
+    the band-block formulation (window >= 1, no soft-cap).  reuse_schedule:
+    `workspace` already holds the tile schedule of an earlier call with the
+    same cu_seqlens, window and sizes (another layer of a stack), which this
+    call uses instead of building it.  check_reuse=False skips the binding's
+    own record of what the workspace holds and leaves the refusal of a
+    mismatched reuse to the device (NaN outputs)."""
     _check_tensor("q", q, torch.bfloat16, 3)
     _check_tensor("k", k, torch.bfloat16, 3)
     _check_tensor("v", v, torch.bfloat16, 3)
@@ -172,28 +202,37 @@ def fwd(q, k, v, cu_seqlens, max_seqlen: int, window: int, scale: float | None =
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((hq, t), dtype=torch.float32, device=q.device)
+    if reuse_schedule and workspace is None:
+        raise ValueError("reuse_schedule needs a workspace that holds a schedule")
     if workspace is None:
         workspace = new_workspace(t, nseq, hq, hkv, d, max_seqlen, window, q.device)
+    sched = ("schedule", t, nseq, _effective_window(int(window), t))
+    if reuse_schedule and check_reuse:
+        _check_reuse(workspace, sched, "attn_varlen_fwd_ex(ATTN_FWD_REUSE_SCHEDULE)")
     lib = load_library()
     head = (_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), nseq, t, hq, hkv, d, int(max_seqlen),
             int(window), float(scale))
     tail = (_ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream_handle(q.device))
     if band:
-        if softcap:
-            raise ValueError("the band-block calls take no soft-cap")
+        if softcap or reuse_schedule:
+            raise ValueError("the band-block calls take no soft-cap and no flags")
         st, where = lib.attn_varlen_band_fwd(*head, *tail), "attn_varlen_band_fwd"
-    elif softcap:
-        st, where = lib.attn_varlen_fwd_ex(*head, float(softcap), *tail), "attn_varlen_fwd_ex"
+    elif softcap or reuse_schedule:
+        flags = ATTN_FWD_REUSE_SCHEDULE if reuse_schedule else 0
+        st, where = (lib.attn_varlen_fwd_ex(*head, float(softcap), flags, *tail),
+                     "attn_varlen_fwd_ex")
     else:
         st, where = lib.attn_varlen_fwd(*head, *tail), "attn_varlen_fwd"
     if st != ATTN_OK:
         raise AttnError(st, where)
+    _WS_RECORD[_ws_key(workspace)] = sched
     return out, lse
 
 
 def bwd(q, k, v, out, lse, dout, cu_seqlens, max_seqlen: int, window: int,
         scale: float | None = None, dq=None, dk=None, dv=None, workspace=None,
-        softcap: float = 0.0, reuse_schedule: bool = False, band: bool = False):
+        softcap: float = 0.0, reuse_schedule: bool = False, band: bool = False,
+        check_reuse: bool = True):
     """attn_varlen_bwd (attn_varlen_bwd_ex with a soft-cap or reuse_schedule,
     attn_varlen_band_bwd when band): returns (dq, dk, dv), bf16, shaped like
     q, k, v.  softcap must be the forward's.  reuse_schedule: `workspace` was
@@ -227,6 +266,9 @@ def bwd(q, k, v, out, lse, dout, cu_seqlens, max_seqlen: int, window: int,
             _stream_handle(q.device))
     if reuse_schedule and workspace_arg_missing:
         raise ValueError("reuse_schedule needs the forward call's workspace")
+    sched = ("schedule", t, nseq, _effective_window(int(window), t))
+    if reuse_schedule and check_reuse:
+        _check_reuse(workspace, sched, "attn_varlen_bwd_ex(ATTN_BWD_REUSE_SCHEDULE)")
     if band:
         if softcap or reuse_schedule:
             raise ValueError("the band-block calls take no soft-cap and no flags")
@@ -239,7 +281,24 @@ def bwd(q, k, v, out, lse, dout, cu_seqlens, max_seqlen: int, window: int,
         st, where = lib.attn_varlen_bwd(*head, *tail), "attn_varlen_bwd"
     if st != ATTN_OK:
         raise AttnError(st, where)
+    if not reuse_schedule:
+        _WS_RECORD[_ws_key(workspace)] = sched
     return dq, dk, dv
+
+
+def _grad_buffers(grads, q, k, v, g, beta):
+    """The delta-rule backward's outputs: the caller's (dq, dk, dv, dg, dbeta),
+    checked, or new zero-filled ones."""
+    if grads is None:
+        return (torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v),
+                torch.zeros_like(g), torch.zeros_like(beta))
+    dq, dk, dv, dg, dbeta = grads
+    for name, x, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v), ("dg", dg, g),
+                          ("dbeta", dbeta, beta)):
+        _check_tensor(name, x, like.dtype, like.dim())
+        if x.shape != like.shape:
+            raise ValueError(f"{name} must be shaped like its input")
+    return dq, dk, dv, dg, dbeta
 
 
 def delta_workspace_size(total_tokens: int, num_seqs: int, num_heads: int, head_dim: int) -> int:
@@ -276,6 +335,7 @@ def delta_fwd(q, k, v, g, beta, cu_seqlens, scale: float | None = None, out=None
                                           workspace.numel(), _stream_handle(q.device))
     if st != ATTN_OK:
         raise AttnError(st, "attn_delta_fwd_ex")
+    _WS_RECORD[_ws_key(workspace)] = ("delta", t, nseq, h) if save else None
     return out
 
 
@@ -313,6 +373,7 @@ def kda_fwd(q, k, v, g, beta, cu_seqlens, scale: float | None = None, out=None, 
                                         workspace.numel(), _stream_handle(q.device))
     if st != ATTN_OK:
         raise AttnError(st, "attn_kda_fwd_ex")
+    _WS_RECORD[_ws_key(workspace)] = ("kda", t, nseq, h) if save else None
     return out
 
 
@@ -323,7 +384,7 @@ def kda_bwd_workspace_size(total_tokens: int, num_seqs: int, num_heads: int,
 
 
 def kda_bwd(q, k, v, g, beta, dout, cu_seqlens, scale: float | None = None, workspace=None,
-            reuse: bool = False):
+            reuse: bool = False, check_reuse: bool = True, grads=None):
     """attn_kda_bwd(_ex): gradients of sum(dout * out) of the Kimi Delta
     forward.  Returns dq, dk, dv (bf16 [T, H, D]), dg (fp32 [T, H, D]) and
     dbeta (fp32 [T, H]), zero-filled first.  reuse=True takes the records and
@@ -342,13 +403,14 @@ def kda_bwd(q, k, v, g, beta, dout, cu_seqlens, scale: float | None = None, work
     nseq = cu_seqlens.numel() - 1
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    dq, dk, dv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
-    dg, dbeta = torch.zeros_like(g), torch.zeros_like(beta)
+    dq, dk, dv, dg, dbeta = _grad_buffers(grads, q, k, v, g, beta)
     if workspace is None:
         n = kda_bwd_workspace_size(t, nseq, h, d)
         if n == 0:
             raise AttnError(-1, "attn_kda_bwd_workspace_size")
         workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    if reuse and check_reuse:
+        _check_reuse(workspace, ("kda", t, nseq, h), "attn_kda_bwd_ex(ATTN_DELTA_BWD_REUSE)")
     st = load_library().attn_kda_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                         _ptr(dout), _ptr(cu_seqlens), nseq, t, h, d, float(scale),
                                         1 if reuse else 0, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
@@ -356,6 +418,8 @@ def kda_bwd(q, k, v, g, beta, dout, cu_seqlens, scale: float | None = None, work
                                         _stream_handle(q.device))
     if st != ATTN_OK:
         raise AttnError(st, "attn_kda_bwd_ex")
+    if not reuse:   # the recomputing backward saves into its workspace
+        _WS_RECORD[_ws_key(workspace)] = ("kda", t, nseq, h)
     return dq, dk, dv, dg, dbeta
 
 
@@ -366,7 +430,7 @@ def delta_bwd_workspace_size(total_tokens: int, num_seqs: int, num_heads: int,
 
 
 def delta_bwd(q, k, v, g, beta, dout, cu_seqlens, scale: float | None = None, workspace=None,
-              reuse: bool = False):
+              reuse: bool = False, check_reuse: bool = True, grads=None):
     """attn_delta_bwd(_ex): gradients of sum(dout * out) of the gated
     delta-rule forward.  Returns dq, dk, dv (bf16 [T, H, D]) and dg, dbeta
     (fp32 [T, H]), zero-filled first.  reuse=True takes the records and states
@@ -385,13 +449,14 @@ def delta_bwd(q, k, v, g, beta, dout, cu_seqlens, scale: float | None = None, wo
     nseq = cu_seqlens.numel() - 1
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    dq, dk, dv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
-    dg, dbeta = torch.zeros_like(g), torch.zeros_like(beta)
+    dq, dk, dv, dg, dbeta = _grad_buffers(grads, q, k, v, g, beta)
     if workspace is None:
         n = delta_bwd_workspace_size(t, nseq, h, d)
         if n == 0:
             raise AttnError(-1, "attn_delta_bwd_workspace_size")
         workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    if reuse and check_reuse:
+        _check_reuse(workspace, ("delta", t, nseq, h), "attn_delta_bwd_ex(ATTN_DELTA_BWD_REUSE)")
     st = load_library().attn_delta_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                           _ptr(dout), _ptr(cu_seqlens), nseq, t, h, d,
                                           float(scale), 1 if reuse else 0, _ptr(dq), _ptr(dk),
@@ -399,6 +464,8 @@ def delta_bwd(q, k, v, g, beta, dout, cu_seqlens, scale: float | None = None, wo
                                           workspace.numel(), _stream_handle(q.device))
     if st != ATTN_OK:
         raise AttnError(st, "attn_delta_bwd_ex")
+    if not reuse:   # the recomputing backward saves into its workspace
+        _WS_RECORD[_ws_key(workspace)] = ("delta", t, nseq, h)
     return dq, dk, dv, dg, dbeta
 
 

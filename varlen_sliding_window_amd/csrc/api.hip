@@ -46,7 +46,6 @@ attn_status check_shape(int32_t total_tokens, int32_t num_seqs, int32_t num_q_he
   if (num_q_heads % num_kv_heads != 0) return ATTN_EINVAL;
   if (max_seqlen <= 0 || max_seqlen > total_tokens) return ATTN_EINVAL;
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return ATTN_EUNSUPPORTED;
-  if ((num_q_heads / num_kv_heads) % 4 != 0) return ATTN_EUNSUPPORTED;
   // grid sizes must fit in 32 bits
   const size_t cap = attn::tile_capacity(total_tokens, num_seqs);
   if (cap * (size_t)num_q_heads >= (size_t)1 << 31) return ATTN_EUNSUPPORTED;
@@ -119,7 +118,7 @@ namespace {
 attn_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
                      int32_t num_seqs, int32_t total_tokens, int32_t num_q_heads,
                      int32_t num_kv_heads, int32_t head_dim, int32_t max_seqlen, int32_t window,
-                     float scale, float softcap, bool band, void* out, float* lse,
+                     float scale, float softcap, uint32_t flags, bool band, void* out, float* lse,
                      void* workspace, size_t workspace_bytes, attn_stream_t stream) {
   WorkspaceLayout w;
   attn_status s = check_common(q, k, v, cu_seqlens, total_tokens, num_seqs, num_q_heads,
@@ -128,6 +127,7 @@ attn_status fwd_impl(const void* q, const void* k, const void* v, const int32_t*
   if (s != ATTN_OK) return s;
   if (!out || !lse || !aligned(out, 16) || !aligned(lse, 4)) return ATTN_EINVAL;
   if (!std::isfinite(softcap) || softcap < 0.f) return ATTN_EINVAL;
+  if (flags & ~(uint32_t)ATTN_FWD_REUSE_SCHEDULE) return ATTN_EINVAL;
   if (band && window <= 0) return ATTN_EINVAL;
   s = check_device();
   if (s != ATTN_OK) return s;
@@ -135,8 +135,9 @@ attn_status fwd_impl(const void* q, const void* k, const void* v, const int32_t*
   const Problem p{total_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, wnd, scale,
                   softcap, band && wnd > 0 ? 1 : 0};
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // both lists, so that the matching backward call may reuse them
-  if (timed_launch(K_SCHEDULE, st, [&] {
+  // both lists, so that the matching backward call (and later layers) may
+  // reuse them
+  if (!(flags & ATTN_FWD_REUSE_SCHEDULE) && timed_launch(K_SCHEDULE, st, [&] {
         return attn::launch_schedule(cu_seqlens, p, true, workspace, w, st);
       }) != hipSuccess)
     return ATTN_ELAUNCH;
@@ -205,10 +206,10 @@ attn_status attn_varlen_fwd_ex(const void* q, const void* k, const void* v,
                                const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                int32_t max_seqlen, int32_t window, float scale, float softcap,
-                               void* out, float* lse, void* workspace, size_t workspace_bytes,
-                               attn_stream_t stream) {
+                               uint32_t flags, void* out, float* lse, void* workspace,
+                               size_t workspace_bytes, attn_stream_t stream) {
   return fwd_impl(q, k, v, cu_seqlens, num_seqs, total_tokens, num_q_heads, num_kv_heads,
-                  head_dim, max_seqlen, window, scale, softcap, false, out, lse, workspace,
+                  head_dim, max_seqlen, window, scale, softcap, flags, false, out, lse, workspace,
                   workspace_bytes, stream);
 }
 
@@ -219,7 +220,7 @@ attn_status attn_varlen_fwd(const void* q, const void* k, const void* v,
                             float* lse, void* workspace, size_t workspace_bytes,
                             attn_stream_t stream) {
   return attn_varlen_fwd_ex(q, k, v, cu_seqlens, num_seqs, total_tokens, num_q_heads,
-                            num_kv_heads, head_dim, max_seqlen, window, scale, 0.f, out, lse,
+                            num_kv_heads, head_dim, max_seqlen, window, scale, 0.f, 0u, out, lse,
                             workspace, workspace_bytes, stream);
 }
 
@@ -253,7 +254,7 @@ attn_status attn_varlen_band_fwd(const void* q, const void* k, const void* v,
                                  float scale, void* out, float* lse, void* workspace,
                                  size_t workspace_bytes, attn_stream_t stream) {
   return fwd_impl(q, k, v, cu_seqlens, num_seqs, total_tokens, num_q_heads, num_kv_heads,
-                  head_dim, max_seqlen, window, scale, 0.f, true, out, lse, workspace,
+                  head_dim, max_seqlen, window, scale, 0.f, 0u, true, out, lse, workspace,
                   workspace_bytes, stream);
 }
 
@@ -473,7 +474,7 @@ const char* attn_varlen_strerror(attn_status s) {
   switch (s) {
     case ATTN_OK: return "success";
     case ATTN_EINVAL: return "invalid argument (null or misaligned pointer, bad size or scale)";
-    case ATTN_EUNSUPPORTED: return "unsupported shape (head_dim must be 64, 128 or 256 and Hq/Hkv a multiple of 4)";
+    case ATTN_EUNSUPPORTED: return "unsupported shape (head_dim must be 64, 128 or 256, k under 4 GiB)";
     case ATTN_EWORKSPACE: return "workspace missing, misaligned (256 B) or too small";
     case ATTN_EDEVICE: return "no usable gfx950 device";
     case ATTN_ELAUNCH: return "kernel launch failed";
@@ -481,7 +482,7 @@ const char* attn_varlen_strerror(attn_status s) {
   return "unknown status";
 }
 
-int32_t attn_varlen_version(void) { return 220; }
+int32_t attn_varlen_version(void) { return 30000; }
 
 attn_status attn_varlen_profile_start(void) {
   std::lock_guard<std::mutex> lock(g_prof_mu);

@@ -53,17 +53,28 @@ __global__ __launch_bounds__(BWD_THREADS, BlockGeom<D>::MIN_WG) void dq_kernel(
   constexpr int KB = Geo::KB, H2 = Geo::H2, KS = Geo::KS, DB = Geo::DB;
   __shared__ __attribute__((aligned(16))) char smem[2 * Geo::BUF_BYTES];
 
-  const int chunks = Hq >> 2;
+  if (!schedule_ok(header, T, tile_cap, window)) {
+    poison_words(dq, (size_t)T * Hq * (D / 2), NAN_BF16X2);
+    return;
+  }
+  // work-group -> (tile, key-value head g, chunk of 4 of its G query heads),
+  // as in the forward
+  const int G = Hq / Hkv;
+  const int cpg = (G + HEADS_PER_WG - 1) / HEADS_PER_WG;
+  const int chunks = Hkv * cpg;
   const int item = blockIdx.x / chunks;
   const int hc = blockIdx.x - item * chunks;
-  if (item >= header[0] || !schedule_matches(header, T, tile_cap, window)) return;
+  if (item >= header[0]) return;
   const Tile tl = tiles[item];
+  if (tl.t1 <= tl.t0) return;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lh = lane >> 5, lq = lane & 31;
-  const int head = hc * 4 + wave;
-  const int g = (hc * 4) / (Hq / Hkv);
+  const int g = hc / cpg;
+  const int hrel = (hc - g * cpg) * HEADS_PER_WG + wave;
+  const bool active = hrel < G;   // else: stages K/V only
+  const int head = g * G + min(hrel, G - 1);
   const int q0 = tl.t0, q1 = tl.t1, a = tl.seg_a;
   const int klo = tile_key_lo(q0, a, window, band);
   const int nblk = (q1 - klo + KB - 1) / KB;
@@ -154,7 +165,7 @@ __global__ __launch_bounds__(BWD_THREADS, BlockGeom<D>::MIN_WG) void dq_kernel(
   const float Dv = dpart + __shfl_xor(dpart, 32);
   const float lsev = qrow < T ? lse[(size_t)head * T + qrow] : 0.f;
   const float lse2 = lsev * LOG2E;
-  if (lh == 0) {
+  if (active && lh == 0) {
     // Rows past the tile get seeds that make them vanish (P = 0, dP - D = 0),
     // so every value the dK/dV kernel reads is finite.
     TileStats* ts = stats + (size_t)head * tile_cap + tl.idx;
@@ -177,6 +188,7 @@ __global__ __launch_bounds__(BWD_THREADS, BlockGeom<D>::MIN_WG) void dq_kernel(
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (n + 1 < nblk) issue(n + 1, buf ^ 1);
+    if (!active) continue;
     const bf16* Ks = reinterpret_cast<const bf16*>(smem + buf * Geo::BUF_BYTES);
     const bf16* Vs = Ks + KB * D;
 
@@ -224,9 +236,13 @@ __global__ __launch_bounds__(BWD_THREADS, BlockGeom<D>::MIN_WG) void dq_kernel(
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         if constexpr (CAP) {
+          // An invisible element has dP - D = 0 exactly; its P may overflow
+          // (exp2(-lse log2 e) for a very negative lse), so it is zeroed by
+          // a select rather than a product.
           const float t = s[r + e];
           const float p = exp2_fast(cap_c2 * t - lse2);
-          v[e] = p * (dp[r + e] - Dv) * (1.f - t * t);
+          const float dd = dp[r + e] - Dv;
+          v[e] = dd == 0.f ? 0.f : p * dd * (1.f - t * t);
         } else {
           const float p = exp2_fast(s[r + e] * scale_log2 - lse2);
           v[e] = p * (dp[r + e] - Dv);
@@ -261,6 +277,7 @@ __global__ __launch_bounds__(BWD_THREADS, BlockGeom<D>::MIN_WG) void dq_kernel(
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (!active) return;
 
   if constexpr (STAGE) {
     // Through the K/V buffer the last block did not use (idle since the
@@ -327,8 +344,14 @@ __global__ __launch_bounds__(BWD_THREADS, (D == 64 && !CAP) ? 2 : 1) void dkdv_k
   const int run = pos / (run_len * Hkv), within = pos - run * run_len * Hkv;
   const int g = within / run_len;
   const int item = run * run_len + (within - g * run_len);
-  if (item >= header[0] || !schedule_matches(header, T, tile_cap, window)) return;
+  if (!schedule_ok(header, T, tile_cap, window)) {
+    poison_words(dk, (size_t)T * Hkv * (D / 2), NAN_BF16X2);
+    poison_words(dv, (size_t)T * Hkv * (D / 2), NAN_BF16X2);
+    return;
+  }
+  if (item >= header[0]) return;
   const Tile tl = tiles[item];
+  if (tl.t1 <= tl.t0) return;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -337,7 +360,9 @@ __global__ __launch_bounds__(BWD_THREADS, (D == 64 && !CAP) ? 2 : 1) void dkdv_k
   const int k0 = tl.t0, k1 = tl.t1, b = tl.seg_b;
   const int qhi = tile_query_hi(k1, b, window, band);
   const int nqb = (qhi - k0 + QBLK - 1) / QBLK;
-  const int steps = (G / DKDV_WAVES) * nqb;   // (head, q-block) pairs of this wave
+  // (head, q-block) pairs of this wave: heads wave, wave + 4, ... of the group
+  const int nheads = wave < G ? (G - wave + DKDV_WAVES - 1) / DKDV_WAVES : 0;
+  const int steps = nheads * nqb;
   const size_t qstride = (size_t)Hq * D;
   const size_t kstride = (size_t)Hkv * D;
 
@@ -632,8 +657,14 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_split_kernel(
   const int run = pos / (run_len * Hkv), within = pos - run * run_len * Hkv;
   const int g = within / run_len;
   const int item = run * run_len + (within - g * run_len);
-  if (item >= header[0] || !schedule_matches(header, T, tile_cap, window)) return;
+  if (!schedule_ok(header, T, tile_cap, window)) {
+    poison_words(dk, (size_t)T * Hkv * (D / 2), NAN_BF16X2);
+    poison_words(dv, (size_t)T * Hkv * (D / 2), NAN_BF16X2);
+    return;
+  }
+  if (item >= header[0]) return;
   const Tile tl = tiles[item];
+  if (tl.t1 <= tl.t0) return;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -643,7 +674,12 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_split_kernel(
   const int k0 = tl.t0, k1 = tl.t1, b = tl.seg_b;
   const int qhi = tile_query_hi(k1, b, window, band);
   const int nqb = (qhi - k0 + QBLK - 1) / QBLK;
-  const int steps = (G / 2) * nqb;   // (head, q-block) pairs of this wave
+  // (head, q-block) pairs: pair p takes heads p, p + 2, ... of the group.
+  // Both pairs run the same number of steps (the loop's barriers are shared);
+  // when G is odd, pair 1's last head's steps are dummies that re-read a
+  // valid head and add nothing.
+  const int steps = ((G + 1) / 2) * nqb;
+  const int live_steps = pair < G ? ((G - pair + 1) / 2) * nqb : 0;
   const size_t qstride = (size_t)Hq * D;
   const size_t kstride = (size_t)Hkv * D;
 
@@ -680,7 +716,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_split_kernel(
   };
   int ld_head = g * G + pair, ld_i = 0;
   auto issue_next = [&](int buf) {
-    issue(ld_head, ld_i, buf);
+    issue(min(ld_head, g * G + G - 1), ld_i, buf);
     if (++ld_i == nqb) {
       ld_i = 0;
       ld_head += 2;
@@ -778,9 +814,10 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_split_kernel(
     }
 
     // P and dS (rows = this lane's key, k = the step's queries), then this
-    // wave's 128 columns of dV += P^T dO and dK += dS^T Q.
+    // wave's 128 columns of dV += P^T dO and dK += dS^T Q.  A dummy step
+    // (it >= live_steps) sees nothing.
     if constexpr (CAP) tanh_fragments<1>(&s, cap_a, TANH_NARROW / cap_a);
-    const int x0 = qb + mbias;
+    const int x0 = it < live_steps ? qb + mbias : -(1 << 30);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       bf16x8 pf, dsf;
@@ -880,8 +917,14 @@ __global__ __launch_bounds__(OCC_THREADS, 1) void dkdv_occ_kernel(
   const int run = pos / (run_len * Hkv), within = pos - run * run_len * Hkv;
   const int g = within / run_len;
   const int item = run * run_len + (within - g * run_len);
-  if (item >= header[0] || !schedule_matches(header, T, tile_cap, window)) return;
+  if (!schedule_ok(header, T, tile_cap, window)) {
+    poison_words(dk, (size_t)T * Hkv * (D / 2), NAN_BF16X2);
+    poison_words(dv, (size_t)T * Hkv * (D / 2), NAN_BF16X2);
+    return;
+  }
+  if (item >= header[0]) return;
   const Tile tl = tiles[item];
+  if (tl.t1 <= tl.t0) return;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -892,7 +935,8 @@ __global__ __launch_bounds__(OCC_THREADS, 1) void dkdv_occ_kernel(
   const int qhi = tile_query_hi(k1, b, window, band);
   const int nqb = (qhi - k0 + QBLK - 1) / QBLK;
   const int nmine = (nqb - par + 1) / 2;       // q-blocks of this parity
-  const int steps = (G / 4) * nmine;
+  const int nheads = hs < G ? (G - hs + 3) / 4 : 0;   // heads hs, hs + 4, ... of the group
+  const int steps = nheads * nmine;
   const size_t qstride = (size_t)Hq * D;
   const size_t kstride = (size_t)Hkv * D;
 
@@ -1089,7 +1133,7 @@ template <int D, bool CAP>
 void launch_dq_kernel(const void* q, const void* k, const void* v, const void* out,
                       const float* lse, const void* dout, const Problem& p, void* dq, char* ws,
                       const WorkspaceLayout& w, hipStream_t stream) {
-  const unsigned grid = (unsigned)(w.tile_cap * (size_t)(p.num_q_heads / 4));
+  const unsigned grid = (unsigned)(w.tile_cap * (size_t)head_chunks(p.num_q_heads, p.num_kv_heads));
   const CapConstants cc = cap_constants(p);
   hipLaunchKernelGGL((dq_kernel<D, CAP>), dim3(grid), dim3(BWD_THREADS), 0, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),

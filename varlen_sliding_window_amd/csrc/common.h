@@ -74,13 +74,26 @@ inline WorkspaceLayout workspace_layout(int64_t total_tokens, int64_t num_seqs,
   return w;
 }
 
-// Workspace header: [0] number of tiles, then the total tokens, tile capacity
-// and window the schedule was built for.  A backward call that reuses the
-// forward's schedule runs only if they match its own, so a stale schedule
-// can give wrong results but never addresses outside the call's buffers.
-__device__ __forceinline__ bool schedule_matches(const int* header, int T, int tile_cap,
-                                                 int window) {
-  return header[1] == T && header[2] == tile_cap && header[3] == window;
+// Workspace header: [0] number of tiles, [1] the total tokens, [2] tile
+// capacity and [3] window the schedule was built for, [4] 1 if cu_seqlens
+// was well formed (cu[0] = 0, non-decreasing, cu[num_seqs] = T), else 0.  A
+// call whose schedule does not match its own arguments (a reused schedule
+// built for another call) or whose boundaries were malformed writes NaN to
+// all of its outputs instead of computing them, so that misuse cannot pass
+// unnoticed; the schedule's clamping keeps every kernel inside its buffers
+// either way.
+constexpr int HEADER_WORDS = 5;
+__device__ __forceinline__ bool schedule_ok(const int* header, int T, int tile_cap, int window) {
+  return header[1] == T && header[2] == tile_cap && header[3] == window && header[4] == 1;
+}
+
+// Query heads per work-group of the forward and dQ kernels: 4 heads of one
+// key-value group, one per wave.  A group of G query heads takes
+// ceil(G / 4) work-groups per q-tile; waves past the group's last head
+// stage the shared key/value blocks but compute nothing.
+constexpr int HEADS_PER_WG = 4;
+__host__ __device__ __forceinline__ int head_chunks(int Hq, int Hkv) {
+  return Hkv * ((Hq / Hkv + HEADS_PER_WG - 1) / HEADS_PER_WG);
 }
 
 // Visible key range of query i in segment starting at a (inclusive bounds).

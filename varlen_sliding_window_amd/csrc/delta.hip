@@ -19,7 +19,10 @@
 // of every (chunk, head) in parallel; delta_scan_kernel then walks each
 // document's chunks in order carrying S, one work-group per (document, head,
 // slice of d_v): the rows of S, the columns of U and of O of different d_v
-// indices never mix.  Everything is fp32 arithmetic on the vector ALU.
+// indices never mix.  The state, the records and all sums are fp32; the
+// products run on bf16 MFMA with each fp32 operand split into a high and a
+// low bf16 part (x = hi + lo, three products per fp32 x fp32 product, the
+// dropped lo * lo term below 2^-16 relative), bf16 inputs exactly.
 #include <hip/hip_runtime.h>
 
 #include "common.h"
@@ -1025,11 +1028,25 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
   __shared__ __attribute__((aligned(16))) float F1[DC * LP];       // U, then dW
   __shared__ __attribute__((aligned(16))) float F2[DC * LP];       // dO (bf16), then dU
   __shared__ float M1[DC * CP], M2[DC * CP];
-  __shared__ float Gs[DC], Bs[DC], gm[DC], dGs[DC], dBs[DC];
+  __shared__ float Gs[DC], Bs[DC], gm[DC], dGs[DC];
+  // Per-wave partial sums of the log-decay and beta gradients: each wave adds
+  // only into its own row (one lane per element and instruction), and the
+  // rows are summed in a fixed order at the end, so dg and dbeta are bitwise
+  // reproducible (no float atomics).
+  __shared__ float wG[GRAD_THREADS / 64][DC], wB[GRAD_THREADS / 64][DC];
   static_assert(DC * CP <= DC * BP / 2, "a C x C matrix fits where V was");
   static_assert(GRAD_THREADS == 512 && DC == 64 && DD == 128, "eight waves of 32 x 32 tiles");
   const int chunk = blockIdx.x / H, h = blockIdx.x - chunk * H;
-  if (chunk >= header[0] || !delta_saved_for(header, T, H, chunk_cap)) return;
+  if (!delta_saved_for(header, T, H, chunk_cap)) {   // no matching saved forward: NaN outputs
+    const size_t nv = (size_t)T * H * (DD / 2);
+    poison_words(dq, nv, NAN_BF16X2);
+    poison_words(dk, nv, NAN_BF16X2);
+    poison_words(dv, nv, NAN_BF16X2);
+    poison_words(dg, (size_t)T * H, NAN_F32);
+    poison_words(dbeta, (size_t)T * H, NAN_F32);
+    return;
+  }
+  if (chunk >= header[0]) return;
   int c0, n;
   delta_chunk_span(cu, seg_off, nseq, T, chunk, c0, n);
   const int tid = threadIdx.x;
@@ -1061,8 +1078,10 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
     Gs[tid] = in ? g[(size_t)(c0 + tid) * H + h] : 0.f;
     Bs[tid] = in ? beta[(size_t)(c0 + tid) * H + h] : 0.f;
     gm[tid] = rec[DeltaRecord::GAM + tid];
-    dGs[tid] = 0.f;
-    dBs[tid] = 0.f;
+  }
+  for (int f = tid; f < (GRAD_THREADS / 64) * DC; f += GRAD_THREADS) {
+    (&wG[0][0])[f] = 0.f;
+    (&wB[0][0])[f] = 0.f;
   }
   __syncthreads();
   if (tid == 0) {   // in-chunk cumulative log decay, summed as the preparation does
@@ -1121,9 +1140,10 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
       float rsum = pd;
 #pragma unroll
       for (int o = 1; o < 32; o <<= 1) rsum += __shfl_xor(rsum, o);
-      if (r == 0) atomicAdd(&dGs[i], rsum);
+      if (r == 0) wG[wave][i] += rsum;
     }
-    atomicAdd(&dGs[j], -colsum);
+    colsum += __shfl_xor(colsum, 32);
+    if (hh == 0) wG[wave][j] -= colsum;
   }
   __syncthreads();
   // dQ = dQ_state + dPm K (written); dK = dK_state + dPm^T Q (kept in akk)
@@ -1194,8 +1214,8 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
         vdy += __shfl_xor(vdy, o);
       }
       if (r == 0) {
-        atomicAdd(&dBs[i], gm[i] * kdx + vdy);
-        atomicAdd(&dGs[i], gm[i] * Bs[i] * kdx);
+        wB[wave][i] += gm[i] * kdx + vdy;
+        wG[wave][i] += gm[i] * Bs[i] * kdx;
       }
     }
   }
@@ -1281,11 +1301,12 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
         ra += __shfl_xor(ra, o);
       }
       if (r == 0) {
-        atomicAdd(&dBs[i], rd);
-        atomicAdd(&dGs[i], ra);
+        wB[wave][i] += rd;
+        wG[wave][i] += ra;
       }
     }
-    atomicAdd(&dGs[j], -colsum);
+    colsum += __shfl_xor(colsum, 32);
+    if (hh == 0) wG[wave][j] -= colsum;
 #pragma unroll
     for (int x = 0; x < 16; ++x) M2[(cm0 + drow(x)) * CP + j] = bm[x];
   }
@@ -1322,14 +1343,20 @@ __global__ __launch_bounds__(GRAD_THREADS) void delta_glocal_kernel(
     for (int j = 0; j < n; ++j) sde += side[DC + j];
     float add = side[tid] - side[DC + tid];
     if (tid == n - 1) add += side[2 * DC] + sde;
-    atomicAdd(&dGs[tid], add);
+    float sg = add, sb = 0.f;
+#pragma unroll
+    for (int w = 0; w < GRAD_THREADS / 64; ++w) {
+      sg += wG[w][tid];
+      sb += wB[w][tid];
+    }
+    dGs[tid] = sg;
+    if (tid < n) dbeta[(size_t)(c0 + tid) * H + h] = sb;
   }
   __syncthreads();
   if (tid < n) {
     float run = 0.f;
     for (int i = n - 1; i >= tid; --i) run += dGs[i];
     dg[(size_t)(c0 + tid) * H + h] = run;
-    dbeta[(size_t)(c0 + tid) * H + h] = dBs[tid];
   }
 }
 
@@ -2029,7 +2056,10 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gstate_kernel(
     float* __restrict__ records, const float* __restrict__ states, float* __restrict__ dstates,
     const float* __restrict__ dubuf, float* __restrict__ dwbuf) {
   __shared__ __attribute__((aligned(16))) StateProductsLds L;
-  __shared__ float dgc[DD];
+  // Column sums of dS_C o S_0: each thread's partial over its rows, summed
+  // per column in a fixed order (bitwise reproducible, no float atomics).
+  constexpr int CS_ROWS = GRAD_THREADS / (DD / 4);
+  __shared__ __attribute__((aligned(16))) float cpart[CS_ROWS][DD];
   const int chunk = blockIdx.x / H, h = blockIdx.x - chunk * H;
   if (chunk >= header[0] || !delta_saved_for(header, T, H, chunk_cap)) return;
   int c0, n;
@@ -2039,7 +2069,6 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gstate_kernel(
   const size_t unit = blockIdx.x;
   float* rec = records + unit * KdaRecord::FLOATS;
   float* dS = dstates + unit * DD * DD;
-  if (tid < DD) dgc[tid] = 0.f;
   f32x4 cs = {0.f, 0.f, 0.f, 0.f};   // column sums of dS_C o S_0, this thread's four columns
   int csc = 0;
   f32x16 aq, aw, ak;
@@ -2050,8 +2079,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gstate_kernel(
                          csc = c4;
                        });
   __syncthreads();   // every read of this unit's dS_C is done before it is overwritten
-#pragma unroll
-  for (int e = 0; e < 4; ++e) atomicAdd(&dgc[csc + e], cs[e]);
+  *reinterpret_cast<f32x4*>(&cpart[tid / (DD / 4)][csc]) = cs;
   const int wave = tid >> 6, lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5, m0 = 32 * (wave >> 2), d = 32 * (wave & 3) + r;
 #pragma unroll
@@ -2062,7 +2090,12 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gstate_kernel(
     dwbuf[unit * DC * DD + (size_t)i * DD + d] = -aw[x];
   }
   __syncthreads();
-  if (tid < DD) rec[KdaRecord::SIDE + tid] = rec[KdaRecord::GC + tid] * dgc[tid];
+  if (tid < DD) {
+    float dgc = 0.f;
+#pragma unroll
+    for (int i = 0; i < CS_ROWS; ++i) dgc += cpart[i][tid];
+    rec[KdaRecord::SIDE + tid] = rec[KdaRecord::GC + tid] * dgc;
+  }
 }
 
 // The triangular solve's gradients per (chunk, head), in LDS: dX = T^T dW
@@ -2084,10 +2117,18 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gmat_kernel(
   __shared__ float F1[DC * LP];                                    // U, then dW
   __shared__ __attribute__((aligned(16))) float F2[DC * LP];       // log decays, dO (bf16), then dU
   __shared__ float M1[DC * CP], M2[DC * CP];
-  __shared__ float Bs[DC], dBs[DC];
+  __shared__ float Bs[DC];
+  // per-wave partial sums of the beta gradient, added in a fixed order at the
+  // end (bitwise reproducible, no float atomics)
+  __shared__ float wB[GRAD_THREADS / 64][DC];
   static_assert(DC * CP <= DC * BP / 2, "a C x C matrix fits where V was");
   const int chunk = blockIdx.x / H, h = blockIdx.x - chunk * H;
-  if (chunk >= header[0] || !delta_saved_for(header, T, H, chunk_cap)) return;
+  if (!delta_saved_for(header, T, H, chunk_cap)) {   // no matching saved forward: NaN outputs
+    poison_words(dv, (size_t)T * H * (DD / 2), NAN_BF16X2);
+    poison_words(dbeta, (size_t)T * H, NAN_F32);
+    return;
+  }
+  if (chunk >= header[0]) return;
   int c0, n;
   delta_chunk_span(cu, seg_off, nseq, T, chunk, c0, n);
   const int tid = threadIdx.x;
@@ -2107,8 +2148,8 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gmat_kernel(
   }
   if (tid < DC) {
     Bs[tid] = tid < n ? beta[(size_t)(c0 + tid) * H + h] : 0.f;
-    dBs[tid] = 0.f;
   }
+  for (int f = tid; f < (GRAD_THREADS / 64) * DC; f += GRAD_THREADS) (&wB[0][0])[f] = 0.f;
   __syncthreads();
   if (tid < DD) {
     float acc = 0.f;
@@ -2210,7 +2251,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gmat_kernel(
       float part = ax[x] * KT[i * LP + d] + (float)Vb[i * BP + d] * ay[x];
 #pragma unroll
       for (int o = 1; o < 32; o <<= 1) part += __shfl_xor(part, o);
-      if (r == 0) atomicAdd(&dBs[i], part);
+      if (r == 0) wB[wave][i] += part;
     }
   }
   // dT = dW X^T + dU Y^T = (dW K_tilde^T + dU V^T) diag(beta) into M2
@@ -2274,12 +2315,16 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gmat_kernel(
       float db = dav * rec[KdaRecord::KK + i * DC + j];
 #pragma unroll
       for (int o = 1; o < 32; o <<= 1) db += __shfl_xor(db, o);
-      if (r == 0) atomicAdd(&dBs[i], db);
+      if (r == 0) wB[wave][i] += db;
     }
   }
   __syncthreads();
-  if (tid < n) dbeta[(size_t)(c0 + tid) * H + h] = dBs[tid];
-
+  if (tid < n) {
+    float sb = 0.f;
+#pragma unroll
+    for (int w = 0; w < GRAD_THREADS / 64; ++w) sb += wB[w][tid];
+    dbeta[(size_t)(c0 + tid) * H + h] = sb;
+  }
 }
 
 // The decayed pair products per (chunk, head) and the final dq, dk, dg:
@@ -2310,7 +2355,13 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gpair_kernel(
   __shared__ float Mp[DC * CP], Mb[DC * CP];
   __shared__ float ksum[DD], Bsh[DC];
   const int chunk = blockIdx.x / H, h = blockIdx.x - chunk * H;
-  if (chunk >= header[0] || !delta_saved_for(header, T, H, chunk_cap)) return;
+  if (!delta_saved_for(header, T, H, chunk_cap)) {   // no matching saved forward: NaN outputs
+    poison_words(dq, (size_t)T * H * (DD / 2), NAN_BF16X2);
+    poison_words(dk, (size_t)T * H * (DD / 2), NAN_BF16X2);
+    poison_words(dg, (size_t)T * H * DD, NAN_F32);
+    return;
+  }
+  if (chunk >= header[0]) return;
   int c0, n;
   delta_chunk_span(cu, seg_off, nseq, T, chunk, c0, n);
   const int tid = threadIdx.x;
@@ -2347,7 +2398,6 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gpair_kernel(
       acc += Gl[i * DD + tid];
       Gl[i * DD + tid] = acc;
     }
-    ksum[tid] = 0.f;
   }
   __syncthreads();
   const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
@@ -2357,6 +2407,10 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gpair_kernel(
     lo[e] = (bf16)(x - (float)hi[e]);
   };
   float dgr[4][4];   // this wave's log-decay gradients, held until the column sums are in
+  // Column d = 16 wave + lr belongs to this wave alone: its sum of dK_hat o
+  // K_hat is kept per lane over the 16 rows the lane meets, then added over
+  // the 4 lane groups in a fixed order (no float atomics).
+  float kacc = 0.f;
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
     const int t = wave + 8 * tt, bb = t / 8, d = 16 * (t % 8) + lr;   // block bb, column d
@@ -2423,9 +2477,12 @@ __global__ __launch_bounds__(GRAD_THREADS) void kda_gpair_kernel(
       }
       dgr[tt][x] = qf * RP - kf * CPv + kf * (RB - CB) + bi * dxv * kf * gam + dqh * qf * gam -
                    dkh * khat;
-      atomicAdd(&ksum[d], dkh * khat);
+      kacc += dkh * khat;
     }
   }
+  kacc += __shfl_xor(kacc, 16);
+  kacc += __shfl_xor(kacc, 32);
+  if (lg == 0) ksum[16 * wave + lr] = kacc;
   __syncthreads();   // every read of the log decays is done and the column sums are complete
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {

@@ -216,6 +216,18 @@ __device__ __forceinline__ void store_tile_rows(bf16* base, size_t stride, int n
   }
 }
 
+// Writes `word` to every 4-byte word of [p, p + nwords), spread over all
+// work-groups of the launch: the outputs of a call whose schedule does not
+// belong to it, or whose boundaries are malformed, become NaN.
+constexpr uint32_t NAN_BF16X2 = 0x7FC07FC0u;   // two bf16 quiet NaNs
+constexpr uint32_t NAN_F32 = 0x7FC00000u;
+__device__ __forceinline__ void poison_words(void* p, size_t nwords, uint32_t word) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  uint32_t* w = static_cast<uint32_t*>(p);
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nwords; i += stride)
+    w[i] = word;
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 

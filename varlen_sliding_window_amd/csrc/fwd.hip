@@ -1,9 +1,10 @@
 // Forward kernel: out and lse of document-masked causal GQA attention.
 //
-// One work-group (4 waves) takes one q-tile of TILE = 32 rows and the 4
-// query heads of one key-value head group (research.dws.rip/llm/kernels,
-// Fig. 2 "Benchmark setup": 8 query heads share 2 key-value heads, so 4 query
-// heads read the same K/V).  Each wave owns one head: its 32 q rows stay in
+// One work-group (4 waves) takes one q-tile of TILE = 32 rows and 4 query
+// heads of one key-value head group (research.dws.rip/llm/kernels, Fig. 2
+// "Benchmark setup": 8 query heads share 2 key-value heads, so 4 query heads
+// read the same K/V; a group of G heads takes ceil(G / 4) work-groups, and
+// waves past its last head only help stage K/V).  Each wave owns one head: its 32 q rows stay in
 // registers as MFMA operands, while the work-group streams the visible keys
 // through LDS in blocks shared by the 4 heads (64 keys for head dims 64 and
 // 128, 32 for 256, so that two double-buffered K/V blocks stay at 64 KB).  The blocks
@@ -39,24 +40,37 @@ constexpr float RESCALE_LOG2 = 8.f;
 template <int D, bool CAP>
 __global__ __launch_bounds__(FWD_THREADS, BlockGeom<D>::MIN_WG) void fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
-    int window, int band, float scale_log2, float cap_a, float cap_c2, bf16* __restrict__ out,
-    float* __restrict__ lse) {
+    const int* __restrict__ header, const Tile* __restrict__ tiles, int tile_cap, int T, int Hq,
+    int Hkv, int window, int band, float scale_log2, float cap_a, float cap_c2,
+    bf16* __restrict__ out, float* __restrict__ lse) {
   using Geo = BlockGeom<D>;
   constexpr int KB = Geo::KB, H2 = Geo::H2, KS = Geo::KS, DB = Geo::DB;
   __shared__ __attribute__((aligned(16))) char smem[2 * Geo::BUF_BYTES];
 
-  const int chunks = Hq >> 2;
+  if (!schedule_ok(header, T, tile_cap, window)) {
+    poison_words(out, (size_t)T * Hq * (D / 2), NAN_BF16X2);
+    poison_words(lse, (size_t)Hq * T, NAN_F32);
+    return;
+  }
+  // work-group -> (tile, key-value head g, chunk of 4 of its G query heads)
+  const int G = Hq / Hkv;
+  const int cpg = (G + HEADS_PER_WG - 1) / HEADS_PER_WG;
+  const int chunks = Hkv * cpg;
   const int item = blockIdx.x / chunks;
   const int hc = blockIdx.x - item * chunks;
   if (item >= header[0]) return;
   const Tile tl = tiles[item];
+  if (tl.t1 <= tl.t0) return;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lh = lane >> 5, lq = lane & 31;
-  const int head = hc * 4 + wave;
-  const int g = (hc * 4) / (Hq / Hkv);
+  const int g = hc / cpg;
+  const int hrel = (hc - g * cpg) * HEADS_PER_WG + wave;   // head within the group
+  // A wave past the group's last head (G not a multiple of 4) still stages
+  // its share of every key/value block but computes and stores nothing.
+  const bool active = hrel < G;
+  const int head = g * G + min(hrel, G - 1);
   const int q0 = tl.t0, q1 = tl.t1, a = tl.seg_a;
   const int klo = tile_key_lo(q0, a, window, band);
   const int nblk = (q1 - klo + KB - 1) / KB;
@@ -132,6 +146,7 @@ __global__ __launch_bounds__(FWD_THREADS, BlockGeom<D>::MIN_WG) void fwd_kernel(
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (n + 1 < nblk) issue(n + 1, buf ^ 1);
+    if (!active) continue;
     const bf16* Ks = reinterpret_cast<const bf16*>(smem + buf * Geo::BUF_BYTES);
     const bf16* Vs = Ks + KB * D;
 
@@ -215,6 +230,7 @@ __global__ __launch_bounds__(FWD_THREADS, BlockGeom<D>::MIN_WG) void fwd_kernel(
         o[db] = mfma32(swz_frag_rows<D>(Vs, db * 32, t, lane), pf[t], o[db]);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (!active) return;
 
   const float lt = lsum + __shfl_xor(lsum, 32);
   const float inv = 1.f / lt;
@@ -245,8 +261,9 @@ void launch_fwd_kernel(unsigned grid, hipStream_t stream, const void* q, const v
   hipLaunchKernelGGL((fwd_kernel<D, CAP>), dim3(grid), dim3(FWD_THREADS), 0, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                      static_cast<const bf16*>(v), reinterpret_cast<const int*>(ws + w.header),
-                     reinterpret_cast<const Tile*>(ws + w.tiles_fwd), p.total_tokens,
-                     p.num_q_heads, p.num_kv_heads, p.window, p.band, CAP ? 1.f : p.scale * LOG2E,
+                     reinterpret_cast<const Tile*>(ws + w.tiles_fwd), (int)w.tile_cap,
+                     p.total_tokens, p.num_q_heads, p.num_kv_heads, p.window, p.band,
+                     CAP ? 1.f : p.scale * LOG2E,
                      cc.cap_a, cc.cap_c2, static_cast<bf16*>(out), lse);
 }
 
@@ -266,7 +283,7 @@ hipError_t launch_forward(const void* q, const void* k, const void* v, const Pro
                           void* out, float* lse, void* workspace, const WorkspaceLayout& w,
                           hipStream_t stream) {
   const char* ws = static_cast<const char*>(workspace);
-  const unsigned grid = (unsigned)(w.tile_cap * (size_t)(p.num_q_heads / 4));
+  const unsigned grid = (unsigned)(w.tile_cap * (size_t)head_chunks(p.num_q_heads, p.num_kv_heads));
   switch (p.head_dim) {
     case 64: launch_fwd_dim<64>(grid, stream, q, k, v, ws, w, p, out, lse); break;
     case 128: launch_fwd_dim<128>(grid, stream, q, k, v, ws, w, p, out, lse); break;

@@ -1,9 +1,9 @@
 // Tile scheduler: turns cu_seqlens into the two work lists of one call.
 //
 // Segments are cut into tiles of TILE tokens starting at each segment start
-// (the last tile of a segment may be short).  Because no token attends
-// across its own document boundary (research.dws.rip/llm/kernels, section
-// 01 "How it was measured"), a tile only ever meets keys (forward, dQ) or
+// (the last tile of a segment may be short).  Because attention is confined
+// to each document (research.dws.rip/llm/kernels, section 01 "How it was
+// measured"), a tile only ever meets keys (forward, dQ) or
 // queries (dK/dV) of its own segment, so fully masked tiles are never
 // emitted.  The same tiles are sorted twice, longest first:
 //   forward / dQ order : by the number of KBLK-key steps over the visible
@@ -15,7 +15,10 @@
 //
 // Everything runs on the device (one work-group), so nothing waits for the
 // host and a call can be captured in a graph; the work lists live in the
-// caller's workspace.  Segment bounds are clamped into [0, T] so that even
+// caller's workspace.  The kernel also checks the boundaries (cu[0] = 0,
+// non-decreasing, cu[num_seqs] = T) and records the verdict in the
+// workspace header: the attention kernels turn a malformed list into NaN
+// outputs.  Segment bounds are clamped into [0, T] all the same, so that
 // malformed cu_seqlens cannot send a kernel outside its buffers.
 #include "common.h"
 #include "launch.h"
@@ -66,7 +69,8 @@ __device__ __forceinline__ Tile tile_at(int i, const int* __restrict__ seg_off,
   const int a = clampi(cu[lo], 0, T);
   const int b = clampi(cu[lo + 1], a, T);
   // With valid boundaries t0 lies in [a, b).  Malformed ones (offsets that
-  // overflowed) give an empty tile at b, which every kernel skips safely.
+  // overflowed) give an empty tile at b, which every kernel skips (and the
+  // header marks the call's boundaries as malformed).
   long long t0 = (long long)a + ((long long)i - seg_off[lo]) * TILE;
   if (t0 < a || t0 > b) t0 = b;
   Tile t;
@@ -124,15 +128,17 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
   __shared__ int hist_b[SORT_BINS];
   __shared__ int lds_cu[SCHED_LDS_SEGS + 1];
   __shared__ int lds_off[SCHED_LDS_SEGS + 1];
+  __shared__ int malformed;
   const int tid = threadIdx.x;
+  if (tid == 0) malformed = (cu_g[0] != 0 || cu_g[nseq] != T) ? 1 : 0;
   const int32_t* cu = cu_g;
   int* seg_off = seg_off_g;
   if (nseq <= SCHED_LDS_SEGS) {
     for (int i = tid; i <= nseq; i += SCHED_THREADS) lds_cu[i] = cu_g[i];
     cu = lds_cu;
     seg_off = lds_off;
-    __syncthreads();
   }
+  __syncthreads();
 
   // 1. tiles per segment -> exclusive offsets
   int carry = 0;
@@ -140,6 +146,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
     const int s = base + tid;
     int n = 0;
     if (s < nseq) {
+      if (cu[s + 1] < cu[s]) malformed = 1;
       const int a = clampi(cu[s], 0, T);
       const int b = clampi(cu[s + 1], a, T);
       n = (b - a + TILE - 1) / TILE;
@@ -238,6 +245,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
     header[1] = T;
     header[2] = tile_cap;
     header[3] = window;
+    header[4] = malformed ? 0 : 1;
   }
 }
 
