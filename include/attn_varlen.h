@@ -76,7 +76,8 @@ typedef enum {
   ATTN_EUNSUPPORTED = -2, /* valid arguments this build does not implement (D, k >= 4 GiB) */
   ATTN_EWORKSPACE = -3,   /* workspace null or smaller than attn_varlen_workspace_size() */
   ATTN_EDEVICE = -4,      /* no usable gfx950 device / HIP runtime error before launch */
-  ATTN_ELAUNCH = -5       /* a kernel launch failed */
+  ATTN_ELAUNCH = -5,      /* a kernel launch failed */
+  ATTN_ESCRATCH = -6      /* attn_varlen_bwd_static: the problem needs more than its static scratch */
 } attn_status;
 
 /* opaque stream handle: a hipStream_t (0 = the legacy default stream) */
@@ -358,6 +359,38 @@ attn_status attn_kda_bwd(const void* q, const void* k, const void* v, const floa
                          int32_t head_dim, float scale, void* dq, void* dk, void* dv, float* dg,
                          float* dbeta, void* workspace, size_t workspace_bytes,
                          attn_stream_t stream);
+
+/*
+ * Backward pass that allocates nothing, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation): attn_varlen_bwd with the same arguments minus
+ * the workspace.  The schedule and the per-row statistics the kernels pass
+ * between them live in a static device array of
+ * ATTN_STATIC_SCRATCH_BYTES (16 MiB) that the library holds on every GPU it
+ * runs on until the process ends; the call itself calls no allocator.
+ *   - The problem's workspace (attn_varlen_workspace_size) must fit in it:
+ *     otherwise ATTN_ESCRATCH, before anything is enqueued.  About 256 B per
+ *     (32-token tile, query head) plus the tile lists: e.g. T = 16,384 with
+ *     Hq = 8 needs 1.2 MB, and T = 65,536 with Hq = 16 about 8.6 MB.
+ *   - Every call on a GPU shares that GPU's one scratch array and leaves its
+ *     contents behind; the kernels rewrite everything they read, so nothing
+ *     needs clearing, but calls that overlap in time on one GPU (other
+ *     streams, other threads) race and give wrong results: serialise them.
+ *   - No soft-cap and no schedule reuse; results equal attn_varlen_bwd's bit
+ *     for bit (same kernels, same schedule).
+ * attn_varlen_static_scratch_bytes() returns the array's size.
+ */
+#define ATTN_STATIC_SCRATCH_BYTES (16u << 20)
+
+size_t attn_varlen_static_scratch_bytes(void);
+
+attn_status attn_varlen_bwd_static(const void* q, const void* k, const void* v,
+                                   const void* out, const float* lse, const void* dout,
+                                   const int32_t* cu_seqlens, int32_t num_seqs,
+                                   int32_t total_tokens, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t max_seqlen,
+                                   int32_t window, float scale, void* dq, void* dk, void* dv,
+                                   attn_stream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char* attn_varlen_strerror(attn_status s);

@@ -227,3 +227,21 @@ def test_kda_bwd_rejects(lib):
     assert lib.attn_kda_fwd_ex(*args) == EWORKSPACE      # saving needs the backward's size
     args[11] = 2
     assert lib.attn_kda_fwd_ex(*args) == EINVAL          # unknown flag
+
+
+def test_static_backward_refuses_beyond_its_scratch_before_the_device(lib):
+    """attn_varlen_bwd_static checks the problem against its static scratch
+    (and the usual shape rules) on the host, before looking at the device."""
+    cap = lib.attn_varlen_static_scratch_bytes()
+    assert cap == 16 << 20
+    t = 1 << 20
+    assert attn.workspace_size(t, 1, 64, 8, 128, t, 0) > cap
+    args = [FAKE] * 7 + [1, t, 64, 8, 128, t, 0, 0.088, FAKE, FAKE, FAKE, None]
+    assert lib.attn_varlen_bwd_static(*args) == -6          # ATTN_ESCRATCH
+    bad = list(args)
+    bad[11] = 96                                             # head dim
+    assert lib.attn_varlen_bwd_static(*bad) == EUNSUPPORTED
+    bad = list(args)
+    bad[10] = 3                                              # Hq % Hkv != 0
+    assert lib.attn_varlen_bwd_static(*bad) == EINVAL
+

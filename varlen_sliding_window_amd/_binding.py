@@ -22,7 +22,8 @@ ATTN_FWD_REUSE_SCHEDULE = 1
 ATTN_DELTA_FWD_SAVE = 1
 ATTN_DELTA_BWD_REUSE = 1
 STATUS_NAMES = {0: "ATTN_OK", -1: "ATTN_EINVAL", -2: "ATTN_EUNSUPPORTED",
-                -3: "ATTN_EWORKSPACE", -4: "ATTN_EDEVICE", -5: "ATTN_ELAUNCH"}
+                -3: "ATTN_EWORKSPACE", -4: "ATTN_EDEVICE", -5: "ATTN_ELAUNCH",
+                -6: "ATTN_ESCRATCH"}
 
 _lib = None
 
@@ -121,6 +122,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_delta_bwd_ex.argtypes = [vp] * 7 + [i32, i32, i32, i32, ctypes.c_float,
                                                  ctypes.c_uint32] + [vp] * 6 + [sz, vp]
     lib.attn_delta_bwd_ex.restype = ctypes.c_int
+    lib.attn_varlen_bwd_static.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                           i32, i32, ctypes.c_float, vp, vp, vp, vp]
+    lib.attn_varlen_bwd_static.restype = ctypes.c_int
+    lib.attn_varlen_static_scratch_bytes.argtypes = []
+    lib.attn_varlen_static_scratch_bytes.restype = sz
     lib.attn_varlen_strerror.argtypes = [ctypes.c_int]
     lib.attn_varlen_strerror.restype = ctypes.c_char_p
     lib.attn_varlen_version.argtypes = []
@@ -299,6 +305,35 @@ def _grad_buffers(grads, q, k, v, g, beta):
         if x.shape != like.shape:
             raise ValueError(f"{name} must be shaped like its input")
     return dq, dk, dv, dg, dbeta
+
+
+def bwd_static(q, k, v, out, lse, dout, cu_seqlens, max_seqlen: int, window: int,
+               scale: float | None = None, dq=None, dk=None, dv=None):
+    """attn_varlen_bwd_static: the backward without a workspace (the library's
+    static device scratch instead; nothing is allocated by the call when dq,
+    dk, dv are given).  Calls that overlap in time on one GPU race."""
+    for name, t_ in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _check_tensor(name, t_, torch.bfloat16, 3)
+    _check_tensor("lse", lse, torch.float32, 2)
+    _check_tensor("cu_seqlens", cu_seqlens, torch.int32, 1)
+    t, hq, d = q.shape
+    hkv = k.shape[1]
+    if out.shape != q.shape or dout.shape != q.shape or lse.shape != (hq, t):
+        raise ValueError("out/dout must match q and lse must be [Hq, T]")
+    if k.shape != (t, hkv, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [T, Hkv, D] with q's T and D")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    st = load_library().attn_varlen_bwd_static(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(cu_seqlens),
+        cu_seqlens.numel() - 1, t, hq, hkv, d, int(max_seqlen), int(window), float(scale),
+        _ptr(dq), _ptr(dk), _ptr(dv), _stream_handle(q.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_varlen_bwd_static")
+    return dq, dk, dv
 
 
 def delta_workspace_size(total_tokens: int, num_seqs: int, num_heads: int, head_dim: int) -> int:

@@ -470,6 +470,70 @@ attn_status attn_delta_bwd(const void* q, const void* k, const void* v, const fl
                            stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Device memory of attn_varlen_bwd_static: a file-scope array that every GPU
+// the library runs on holds from module load until the process ends.  Host
+// code never uses the array's name as an address (on the host it is only a
+// stand-in symbol): the device address of each GPU's copy is looked up once
+// per device with hipGetSymbolAddress and kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = (size_t)ATTN_STATIC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch` (looked up on the first call on
+// that device, with the device current).
+attn_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_EDEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ATTN_EDEVICE;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_varlen_static_scratch_bytes(void) { return kScratchBytes; }
+
+attn_status attn_varlen_bwd_static(const void* q, const void* k, const void* v, const void* out,
+                                   const float* lse, const void* dout,
+                                   const int32_t* cu_seqlens, int32_t num_seqs,
+                                   int32_t total_tokens, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t max_seqlen,
+                                   int32_t window, float scale, void* dq, void* dk, void* dv,
+                                   attn_stream_t stream) {
+  // The sizes are checked before the scratch is looked up, so a problem too
+  // large for it is refused without touching the device.
+  attn_status s = check_shape(total_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                              max_seqlen);
+  if (s != ATTN_OK) return s;
+  if (attn::workspace_layout(total_tokens, num_seqs, num_q_heads).total > kScratchBytes)
+    return ATTN_ESCRATCH;
+  s = check_device();
+  if (s != ATTN_OK) return s;
+  void* ws = nullptr;
+  s = scratch_address(&ws);
+  if (s != ATTN_OK) return s;
+  // Same kernels as attn_varlen_bwd, with the static scratch as workspace:
+  // the schedule kernel rewrites the header and lists, and the dQ kernel
+  // every row statistic the dK/dV kernel then reads, so nothing in the
+  // scratch has to start at zero.
+  return bwd_impl(q, k, v, out, lse, dout, cu_seqlens, num_seqs, total_tokens, num_q_heads,
+                  num_kv_heads, head_dim, max_seqlen, window, scale, 0.f, 0u, false, dq, dk, dv,
+                  ws, kScratchBytes, stream);
+}
+
 const char* attn_varlen_strerror(attn_status s) {
   switch (s) {
     case ATTN_OK: return "success";
@@ -478,6 +542,7 @@ const char* attn_varlen_strerror(attn_status s) {
     case ATTN_EWORKSPACE: return "workspace missing, misaligned (256 B) or too small";
     case ATTN_EDEVICE: return "no usable gfx950 device";
     case ATTN_ELAUNCH: return "kernel launch failed";
+    case ATTN_ESCRATCH: return "problem needs more workspace than the static scratch of attn_varlen_bwd_static";
   }
   return "unknown status";
 }
