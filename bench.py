@@ -237,6 +237,26 @@ def load_traffic(kernel: str):
     return None
 
 
+def load_counters():
+    """Per-kernel counter summary (MFMA utilisation, executed/counted MFMA
+    flops) from the committed rocprofv3 summary (a 'summary-json:' line),
+    provided it was taken on the current kernel sources; else None."""
+    pdir = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(pdir):
+        return None
+    sha = sources_sha256()
+    for name in sorted(os.listdir(pdir)):
+        if not name.endswith(".md"):
+            continue
+        with open(os.path.join(pdir, name)) as f:
+            for line in f:
+                if line.startswith("summary-json:"):
+                    data = json.loads(line.split(":", 1)[1])
+                    if data.get("sources_sha256") == sha:
+                        return data.get("kernels")
+    return None
+
+
 def delta_bench(args, device):
     """Gated delta-rule layer step on the workload microbatch (one layer, H = 8
     heads of 128, the documents of the attention workload's cu_seqlens): the
@@ -538,12 +558,14 @@ def main():
     dom = by_kernel[dom_name]
     achieved = dom["flops"] / (dom["ms"] * 1e-3) / 1e12 if dom["ms"] > 0 else 0.0
     traffic = load_traffic(dom_name)
+    counters = load_counters() if args.workload == "ctx4096_w512+global" else None
     roofline = {"bound": "mfma", "kernel": dom_name, "achieved": achieved,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                 "traffic": traffic,
                 "avg_ms": dom["ms"] / dom["launches"], "launches_per_step": dom["launches"],
                 "flops_per_launch": dom["flops"] / dom["launches"],
-                "share_of_step": dom["ms"] / ms_per_step}
+                "share_of_step": dom["ms"] / ms_per_step,
+                "counters": counters}
 
     # The same step captured once as a HIP graph and replayed (the library
     # allocates nothing and never waits on the host, so the whole step is
