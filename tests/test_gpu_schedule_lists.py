@@ -10,7 +10,10 @@ cu_seqlens):
   tile's key range (forward) or query range (backward) is non-empty;
 - both lists are sorted by cost, longest first (the forward list by 64-key
   blocks over the visible keys, the backward list by 32-query blocks over
-  the queries that see the tile);
+  the queries that see the tile); without a window the backward list's sort
+  key is the cost of the tile's chunk of 16 neighbouring tiles from the
+  segment start (that of its first tile), so that runs of the list stay
+  within a document;
 - the header records the tile count, T, the tile capacity and the window,
   and marks the boundaries as well formed.
 
@@ -33,6 +36,7 @@ if torch.cuda.is_available():
     from gpu_common import device_inputs  # noqa: E402
 
 TILE, KBLK, QBLK = 32, 64, 32
+CHUNK = 16      # tiles per sort chunk without a window
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -72,6 +76,19 @@ def bwd_cost(t0, t1, b, window):
     return (qhi - t0 + QBLK - 1) // QBLK
 
 
+def fwd_key(x, window):
+    t0, t1, a, b, _ = x
+    return fwd_cost(t0, t1, a, window)
+
+
+def bwd_key(x, window):
+    t0, t1, a, b, _ = x
+    if window > 0:
+        return bwd_cost(t0, t1, b, window)
+    c0 = a + ((t0 - a) // (TILE * CHUNK)) * TILE * CHUNK
+    return bwd_cost(c0, min(c0 + TILE, b), b, window)
+
+
 def check_lists(cu: np.ndarray, window: int, hq: int = 8, hkv: int = 2):
     cu = np.asarray(cu, dtype=np.int32)
     t = int(cu[-1])
@@ -88,14 +105,16 @@ def check_lists(cu: np.ndarray, window: int, hq: int = 8, hkv: int = 2):
     eff_window = 0 if window <= 0 or window >= t else window
     assert header.tolist() == [n, t, cap, eff_window, 1], header
     want_set = set(want)
-    for name, lst, cost in (("forward", fwd, lambda x: fwd_cost(x[0], x[1], x[2], eff_window)),
-                            ("backward", bwd, lambda x: bwd_cost(x[0], x[1], x[3], eff_window))):
+    for name, lst, cost in (("forward", fwd, lambda x: fwd_key(x, eff_window)),
+                            ("backward", bwd, lambda x: bwd_key(x, eff_window))):
         got = [tuple(int(v) for v in row[:5]) for row in lst[:n]]
         assert len(set(got)) == n, f"{name}: a tile appears twice"
         assert set(got) == want_set, f"{name}: tiles differ from the segments' tiles"
         assert all(x[1] > x[0] for x in got), f"{name}: empty tile"
+        work = [fwd_cost(x[0], x[1], x[2], eff_window) if name == "forward"
+                else bwd_cost(x[0], x[1], x[3], eff_window) for x in got]
+        assert all(c >= 1 for c in work), f"{name}: a tile with nothing to do"
         costs = [cost(x) for x in got]
-        assert all(c >= 1 for c in costs), f"{name}: a tile with nothing to do"
         assert all(c0 >= c1 for c0, c1 in zip(costs, costs[1:])), f"{name}: not longest first"
     covered = np.zeros(t, dtype=np.int32)
     for t0, t1, *_ in want:

@@ -46,9 +46,10 @@ attn_status check_shape(int32_t total_tokens, int32_t num_seqs, int32_t num_q_he
   if (num_q_heads % num_kv_heads != 0) return ATTN_EINVAL;
   if (max_seqlen <= 0 || max_seqlen > total_tokens) return ATTN_EINVAL;
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return ATTN_EUNSUPPORTED;
-  // grid sizes must fit in 32 bits
+  // grid sizes must fit in 32 bits (a grid covers up to num_q_heads entries
+  // per tile, in runs padded to 8 * LOCAL_RUN)
   const size_t cap = attn::tile_capacity(total_tokens, num_seqs);
-  if (cap * (size_t)num_q_heads >= (size_t)1 << 31) return ATTN_EUNSUPPORTED;
+  if ((cap + 8 * attn::LOCAL_RUN) * (size_t)num_q_heads >= (size_t)1 << 31) return ATTN_EUNSUPPORTED;
   // the kernels address k and v rows with 32-bit byte offsets from a
   // key-value head's first row
   if ((size_t)total_tokens * (size_t)num_kv_heads * (size_t)head_dim * 2 > (size_t)UINT32_MAX)

@@ -58,12 +58,13 @@ __global__ __launch_bounds__(BWD_THREADS, BlockGeom<D>::MIN_WG) void dq_kernel(
     return;
   }
   // work-group -> (tile, key-value head g, chunk of 4 of its G query heads),
-  // as in the forward
+  // in runs of neighbouring tiles per XCD, whose key/value blocks meet in
+  // that XCD's L2 (xcd_run_item)
   const int G = Hq / Hkv;
   const int cpg = (G + HEADS_PER_WG - 1) / HEADS_PER_WG;
   const int chunks = Hkv * cpg;
-  const int item = blockIdx.x / chunks;
-  const int hc = blockIdx.x - item * chunks;
+  int hc;
+  const int item = xcd_run_item(blockIdx.x, run_length(window), chunks, &hc);
   if (item >= header[0]) return;
   const Tile tl = tiles[item];
   if (tl.t1 <= tl.t0) return;
@@ -331,19 +332,10 @@ __global__ __launch_bounds__(BWD_THREADS, (D == 64 && !CAP) ? 2 : 1) void dkdv_k
   constexpr int DKDV_TILE_BYTES = Geo::TILE_BYTES, DKDV_BUF_BYTES = Geo::BUF_BYTES;
   __shared__ __attribute__((aligned(16))) char smem[Geo::LDS_BYTES];
 
-  // Work-groups go to the 8 XCDs round-robin (work-group b to XCD b % 8).
-  // XCD x takes runs of R consecutive entries of the sorted list with one
-  // key-value head, so that the work-groups running together on an XCD are
-  // mostly neighbouring key tiles whose Q/dO rows meet in that XCD's L2.
-  // Rounds of 8 runs go to the XCDs in alternating directions, so that no
-  // XCD always gets the most expensive run of a round.
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int round = slot / run_len;
-  const int rx = (round & 1) ? 7 - xcd : xcd;
-  const int pos = (round * 8 + rx) * run_len + (slot - round * run_len);
-  const int run = pos / (run_len * Hkv), within = pos - run * run_len * Hkv;
-  const int g = within / run_len;
-  const int item = run * run_len + (within - g * run_len);
+  // work-group -> (key tile, key-value head), in runs of neighbouring key
+  // tiles per XCD, whose Q/dO rows meet in that XCD's L2 (xcd_run_item)
+  int g;
+  const int item = xcd_run_item(blockIdx.x, run_len, Hkv, &g);
   if (!schedule_ok(header, T, tile_cap, window)) {
     poison_words(dk, (size_t)T * Hkv * (D / 2), NAN_BF16X2);
     poison_words(dv, (size_t)T * Hkv * (D / 2), NAN_BF16X2);
@@ -650,13 +642,8 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_split_kernel(
   __shared__ __attribute__((aligned(16))) char smem[Geo::LDS_BYTES];
 
   // work-group -> (key tile, key-value head): as in dkdv_kernel
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int round = slot / run_len;
-  const int rx = (round & 1) ? 7 - xcd : xcd;
-  const int pos = (round * 8 + rx) * run_len + (slot - round * run_len);
-  const int run = pos / (run_len * Hkv), within = pos - run * run_len * Hkv;
-  const int g = within / run_len;
-  const int item = run * run_len + (within - g * run_len);
+  int g;
+  const int item = xcd_run_item(blockIdx.x, run_len, Hkv, &g);
   if (!schedule_ok(header, T, tile_cap, window)) {
     poison_words(dk, (size_t)T * Hkv * (D / 2), NAN_BF16X2);
     poison_words(dv, (size_t)T * Hkv * (D / 2), NAN_BF16X2);
@@ -910,13 +897,8 @@ __global__ __launch_bounds__(OCC_THREADS, 1) void dkdv_occ_kernel(
                 "reduction buffer must fit in the staging buffers");
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
 
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int round = slot / run_len;
-  const int rx = (round & 1) ? 7 - xcd : xcd;
-  const int pos = (round * 8 + rx) * run_len + (slot - round * run_len);
-  const int run = pos / (run_len * Hkv), within = pos - run * run_len * Hkv;
-  const int g = within / run_len;
-  const int item = run * run_len + (within - g * run_len);
+  int g;
+  const int item = xcd_run_item(blockIdx.x, run_len, Hkv, &g);
   if (!schedule_ok(header, T, tile_cap, window)) {
     poison_words(dk, (size_t)T * Hkv * (D / 2), NAN_BF16X2);
     poison_words(dv, (size_t)T * Hkv * (D / 2), NAN_BF16X2);
@@ -1133,7 +1115,8 @@ template <int D, bool CAP>
 void launch_dq_kernel(const void* q, const void* k, const void* v, const void* out,
                       const float* lse, const void* dout, const Problem& p, void* dq, char* ws,
                       const WorkspaceLayout& w, hipStream_t stream) {
-  const unsigned grid = (unsigned)(w.tile_cap * (size_t)head_chunks(p.num_q_heads, p.num_kv_heads));
+  const unsigned grid = run_grid(head_chunks(p.num_q_heads, p.num_kv_heads), w.tile_cap,
+                                 run_length(p.window));
   const CapConstants cc = cap_constants(p);
   hipLaunchKernelGGL((dq_kernel<D, CAP>), dim3(grid), dim3(BWD_THREADS), 0, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),
@@ -1150,16 +1133,10 @@ template <int D, bool CAP>
 void launch_dkdv_kernel(const void* q, const void* k, const void* v, const void* dout,
                         const Problem& p, void* dk, void* dv, const char* ws,
                         const WorkspaceLayout& w, hipStream_t stream) {
-  // Runs of R list entries per key-value head, dealt to the XCDs in rounds
-  // of 8 runs (see the kernel); the grid covers every (tile, head) pair.
-  // Local layers, where most tiles cost the same, take long runs (more L2
-  // reuse); global layers, where costs fall along each document, take
-  // shorter ones (balance against reuse: over four document mixes at
-  // context 4,096, 16 beat 8 by 0.9% on average and 32 lost balance).
-  const int run_len = p.window > 0 ? 32 : 16;
-  const size_t items = (size_t)p.num_kv_heads * (w.tile_cap + run_len - 1);
-  const size_t round = 8 * (size_t)run_len;
-  const unsigned grid = (unsigned)((items + round - 1) / round * round);
+  // Runs of run_length(window) list entries per key-value head, dealt to the
+  // XCDs in rounds of 8 runs; the grid covers every (tile, head) pair.
+  const int run_len = run_length(p.window);
+  const unsigned grid = run_grid(p.num_kv_heads, w.tile_cap, run_len);
   const CapConstants cc = cap_constants(p);
   // head dim 256: pairs of waves split the head dim; 128: two waves per
   // SIMD; 64: the software-pipelined kernel

@@ -96,6 +96,45 @@ __host__ __device__ __forceinline__ int head_chunks(int Hq, int Hkv) {
   return Hkv * ((Hq / Hkv + HEADS_PER_WG - 1) / HEADS_PER_WG);
 }
 
+// Work-groups in runs per XCD.  Work-groups are dealt to the 8 XCDs
+// round-robin, and each XCD has its own L2, so a kernel maps its blocks so
+// that runs of run_len consecutive list entries, all with one head index
+// (nh of them per entry), land on one XCD: neighbouring tiles of a document
+// read mostly the same rows, which that XCD's L2 then serves.  Rounds of 8
+// runs go to the XCDs in alternating directions, so that no XCD always gets
+// a round's most expensive run.  Returns the list entry; *h the head index.
+// The grid is run_grid(nh, tile_cap, run_len) blocks; entries at or past the
+// list length are idle.
+__device__ __forceinline__ int xcd_run_item(int bid, int run_len, int nh, int* h) {
+  const int xcd = bid & 7, slot = bid >> 3;
+  const int round = slot / run_len;
+  const int rx = (round & 1) ? 7 - xcd : xcd;
+  const int pos = (round * 8 + rx) * run_len + (slot - round * run_len);
+  const int run = pos / (run_len * nh), within = pos - run * run_len * nh;
+  *h = within / run_len;
+  return run * run_len + (within - *h * run_len);
+}
+inline unsigned run_grid(int nh, size_t tile_cap, int run_len) {
+  const size_t items = (size_t)nh * (tile_cap + run_len - 1);
+  const size_t round = 8 * (size_t)run_len;
+  return (unsigned)((items + round - 1) / round * round);
+}
+
+// Run lengths and sort chunks.  Local layers: most tiles cost the same, the
+// sorted lists keep equal-cost neighbours in token order, and long runs give
+// the most L2 reuse.  Global layers: costs change along each document, so a
+// plain longest-first sort interleaves documents.  The backward list (whose
+// work-groups each stream a long run of Q/dO rows) is instead sorted by the
+// cost of each tile's chunk (GLOBAL_RUN consecutive tiles of one document,
+// ranked by its most expensive tile), so that a run is mostly one chunk, at
+// some cost in balance; the forward list keeps the plain order, which
+// balanced better there.
+constexpr int LOCAL_RUN = 32;
+constexpr int GLOBAL_RUN = 16;
+__host__ __device__ __forceinline__ int run_length(int window) {
+  return window > 0 ? LOCAL_RUN : GLOBAL_RUN;
+}
+
 // Visible key range of query i in segment starting at a (inclusive bounds).
 __device__ __forceinline__ int first_visible_key(int i, int a, int window) {
   return window > 0 ? max(a, i - window + 1) : a;

@@ -52,12 +52,14 @@ __global__ __launch_bounds__(FWD_THREADS, BlockGeom<D>::MIN_WG) void fwd_kernel(
     poison_words(lse, (size_t)Hq * T, NAN_F32);
     return;
   }
-  // work-group -> (tile, key-value head g, chunk of 4 of its G query heads)
+  // work-group -> (tile, key-value head g, chunk of 4 of its G query heads),
+  // in runs of neighbouring tiles per XCD, whose key/value blocks meet in
+  // that XCD's L2 (xcd_run_item)
   const int G = Hq / Hkv;
   const int cpg = (G + HEADS_PER_WG - 1) / HEADS_PER_WG;
   const int chunks = Hkv * cpg;
-  const int item = blockIdx.x / chunks;
-  const int hc = blockIdx.x - item * chunks;
+  int hc;
+  const int item = xcd_run_item(blockIdx.x, run_length(window), chunks, &hc);
   if (item >= header[0]) return;
   const Tile tl = tiles[item];
   if (tl.t1 <= tl.t0) return;
@@ -283,7 +285,8 @@ hipError_t launch_forward(const void* q, const void* k, const void* v, const Pro
                           void* out, float* lse, void* workspace, const WorkspaceLayout& w,
                           hipStream_t stream) {
   const char* ws = static_cast<const char*>(workspace);
-  const unsigned grid = (unsigned)(w.tile_cap * (size_t)head_chunks(p.num_q_heads, p.num_kv_heads));
+  const unsigned grid = run_grid(head_chunks(p.num_q_heads, p.num_kv_heads), w.tile_cap,
+                                 run_length(p.window));
   switch (p.head_dim) {
     case 64: launch_fwd_dim<64>(grid, stream, q, k, v, ws, w, p, out, lse); break;
     case 128: launch_fwd_dim<128>(grid, stream, q, k, v, ws, w, p, out, lse); break;

@@ -10,8 +10,10 @@
 //                        keys [max(a, t0 - W + 1), t1)
 //   dK / dV order      : by the number of QBLK-query steps over the queries
 //                        that see the tile, [t0, min(b, t1 - 1 + W))
-// Work-groups are dispatched in list order, so the hardware's in-order
-// dispatch gives a greedy longest-processing-time-first assignment.
+// Without a window, the backward order sorts tiles by the cost of their
+// chunk of GLOBAL_RUN neighbouring tiles instead (see run_length).  Work-groups are
+// dispatched in list order, so the hardware's in-order dispatch gives a
+// greedy longest-processing-time-first assignment.
 //
 // Everything runs on the device (one work-group), so nothing waits for the
 // host and a call can be captured in a graph; the work lists live in the
@@ -83,14 +85,31 @@ __device__ __forceinline__ Tile tile_at(int i, const int* __restrict__ seg_off,
   return t;
 }
 
+__device__ __forceinline__ int fwd_cost(int t0, int t1, int a, int window, int band) {
+  const int klo = tile_key_lo(t0, a, window, band);
+  return (t1 - klo + KBLK - 1) / KBLK;
+}
+
+__device__ __forceinline__ int bwd_cost(int t0, int t1, int b, int window, int band) {
+  const int qhi = tile_query_hi(t1, b, window, band);
+  return (qhi - t0 + QBLK - 1) / QBLK;
+}
+
+// Sort keys: the tile's own cost, except in the backward order without a
+// window, where it is the cost of the tile's chunk of GLOBAL_RUN tiles (that
+// of its first tile: costs fall along a document).
 __device__ __forceinline__ int fwd_bin(const Tile& t, int window, int band) {
-  const int klo = tile_key_lo(t.t0, t.seg_a, window, band);
-  return min((t.t1 - klo + KBLK - 1) / KBLK, SORT_BINS - 1);
+  return min(fwd_cost(t.t0, t.t1, t.seg_a, window, band), SORT_BINS - 1);
 }
 
 __device__ __forceinline__ int bwd_bin(const Tile& t, int window, int band) {
-  const int qhi = tile_query_hi(t.t1, t.seg_b, window, band);
-  return min((qhi - t.t0 + QBLK - 1) / QBLK, SORT_BINS - 1);
+  int c = bwd_cost(t.t0, t.t1, t.seg_b, window, band);
+  if (window <= 0) {
+    const int span = TILE * GLOBAL_RUN;
+    const int c0 = t.seg_a + ((t.t0 - t.seg_a) / span) * span;
+    c = bwd_cost(c0, min(c0 + TILE, t.seg_b), t.seg_b, window, band);
+  }
+  return min(c, SORT_BINS - 1);
 }
 
 // Slot of this lane's tile in bucket `bin` (hist holds the next free slot of
