@@ -134,7 +134,7 @@ attn_status fwd_impl(const void* q, const void* k, const void* v, const int32_t*
   if (s != ATTN_OK) return s;
   const int32_t wnd = effective_window(window, total_tokens);
   const Problem p{total_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, wnd, scale,
-                  softcap, band && wnd > 0 ? 1 : 0};
+                  softcap, band && wnd > 0 ? 1 : 0, max_seqlen};
   hipStream_t st = static_cast<hipStream_t>(stream);
   // both lists, so that the matching backward call (and later layers) may
   // reuse them
@@ -171,7 +171,7 @@ attn_status bwd_impl(const void* q, const void* k, const void* v, const void* ou
   if (s != ATTN_OK) return s;
   const int32_t wnd = effective_window(window, total_tokens);
   const Problem p{total_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, wnd, scale,
-                  softcap, band && wnd > 0 ? 1 : 0};
+                  softcap, band && wnd > 0 ? 1 : 0, max_seqlen};
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (!(flags & ATTN_BWD_REUSE_SCHEDULE) &&
       timed_launch(K_SCHEDULE, st, [&] {

@@ -46,17 +46,13 @@ template <int D, bool CAP>
 __global__ __launch_bounds__(BWD_THREADS, BlockGeom<D>::MIN_WG) void dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ out, const bf16* __restrict__ dout, const float* __restrict__ lse,
-    const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
+    const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
     int window, int band, float scale_log2, float scale, float cap_a, float cap_c2, int tile_cap,
     bf16* __restrict__ dq, TileStats* __restrict__ stats) {
   using Geo = BlockGeom<D>;
   constexpr int KB = Geo::KB, H2 = Geo::H2, KS = Geo::KS, DB = Geo::DB;
   __shared__ __attribute__((aligned(16))) char smem[2 * Geo::BUF_BYTES];
 
-  if (!schedule_ok(header, T, tile_cap, window)) {
-    poison_words(dq, (size_t)T * Hq * (D / 2), NAN_BF16X2);
-    return;
-  }
   // work-group -> (tile, key-value head g, chunk of 4 of its G query heads),
   // in runs of neighbouring tiles per XCD, whose key/value blocks meet in
   // that XCD's L2 (xcd_run_item)
@@ -65,9 +61,13 @@ __global__ __launch_bounds__(BWD_THREADS, BlockGeom<D>::MIN_WG) void dq_kernel(
   const int chunks = Hkv * cpg;
   int hc;
   const int item = xcd_run_item(blockIdx.x, run_length(window), chunks, &hc);
-  if (item >= header[0]) return;
-  const Tile tl = tiles[item];
-  if (tl.t1 <= tl.t0) return;
+  const ScheduleView sv = read_schedule(tiles, item, tile_cap, T, window);
+  const Tile tl = sv.tile;
+  if (!sv.ok) {
+    poison_words(dq, (size_t)T * Hq * (D / 2), NAN_BF16X2);
+    return;
+  }
+  if (!sv.valid) return;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -324,7 +324,7 @@ template <int D, bool CAP>
 __global__ __launch_bounds__(BWD_THREADS, (D == 64 && !CAP) ? 2 : 1) void dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const TileStats* __restrict__ stats, int tile_cap,
-    const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
+    const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
     int window, int band, float scale_log2, float scale, float cap_a, float cap_c2, int run_len,
     bf16* __restrict__ dk, bf16* __restrict__ dv) {
   using Geo = DkdvGeom<D>;
@@ -336,14 +336,14 @@ __global__ __launch_bounds__(BWD_THREADS, (D == 64 && !CAP) ? 2 : 1) void dkdv_k
   // tiles per XCD, whose Q/dO rows meet in that XCD's L2 (xcd_run_item)
   int g;
   const int item = xcd_run_item(blockIdx.x, run_len, Hkv, &g);
-  if (!schedule_ok(header, T, tile_cap, window)) {
+  const ScheduleView sv = read_schedule(tiles, item, tile_cap, T, window);
+  const Tile tl = sv.tile;
+  if (!sv.ok) {
     poison_words(dk, (size_t)T * Hkv * (D / 2), NAN_BF16X2);
     poison_words(dv, (size_t)T * Hkv * (D / 2), NAN_BF16X2);
     return;
   }
-  if (item >= header[0]) return;
-  const Tile tl = tiles[item];
-  if (tl.t1 <= tl.t0) return;
+  if (!sv.valid) return;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -632,7 +632,7 @@ template <bool CAP>
 __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_split_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const TileStats* __restrict__ stats, int tile_cap,
-    const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
+    const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
     int window, int band, float scale_log2, float scale, float cap_a, float cap_c2, int run_len,
     bf16* __restrict__ dk, bf16* __restrict__ dv) {
   constexpr int D = 256, DH = 128;      // head dim, columns per wave
@@ -644,14 +644,14 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_split_kernel(
   // work-group -> (key tile, key-value head): as in dkdv_kernel
   int g;
   const int item = xcd_run_item(blockIdx.x, run_len, Hkv, &g);
-  if (!schedule_ok(header, T, tile_cap, window)) {
+  const ScheduleView sv = read_schedule(tiles, item, tile_cap, T, window);
+  const Tile tl = sv.tile;
+  if (!sv.ok) {
     poison_words(dk, (size_t)T * Hkv * (D / 2), NAN_BF16X2);
     poison_words(dv, (size_t)T * Hkv * (D / 2), NAN_BF16X2);
     return;
   }
-  if (item >= header[0]) return;
-  const Tile tl = tiles[item];
-  if (tl.t1 <= tl.t0) return;
+  if (!sv.valid) return;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -883,7 +883,7 @@ template <bool CAP>
 __global__ __launch_bounds__(OCC_THREADS, 1) void dkdv_occ_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const TileStats* __restrict__ stats, int tile_cap,
-    const int* __restrict__ header, const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
+    const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
     int window, int band, float scale_log2, float scale, float cap_a, float cap_c2, int run_len,
     bf16* __restrict__ dk, bf16* __restrict__ dv) {
   constexpr int D = 128;
@@ -899,14 +899,14 @@ __global__ __launch_bounds__(OCC_THREADS, 1) void dkdv_occ_kernel(
 
   int g;
   const int item = xcd_run_item(blockIdx.x, run_len, Hkv, &g);
-  if (!schedule_ok(header, T, tile_cap, window)) {
+  const ScheduleView sv = read_schedule(tiles, item, tile_cap, T, window);
+  const Tile tl = sv.tile;
+  if (!sv.ok) {
     poison_words(dk, (size_t)T * Hkv * (D / 2), NAN_BF16X2);
     poison_words(dv, (size_t)T * Hkv * (D / 2), NAN_BF16X2);
     return;
   }
-  if (item >= header[0]) return;
-  const Tile tl = tiles[item];
-  if (tl.t1 <= tl.t0) return;
+  if (!sv.valid) return;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1111,6 +1111,238 @@ __global__ __launch_bounds__(OCC_THREADS, 1) void dkdv_occ_kernel(
   }
 }
 
+// dK/dV at head dim 128 without a cap, two work-groups per CU: 4 waves per
+// work-group (wave w takes query heads w, w + 4, ... of the group and all of
+// their q-blocks), one work-group per (32-key tile, kv head).  LDS holds the
+// tile's K and V rows (16 KB) and one Q/dO buffer per wave (16 KB): 80 KB, so
+// that two work-groups share a CU and each one's start (boundaries, tile
+// record, K/V rows, first block) and end (the reduction over its waves and
+// the stores) overlap the other's products.  The TileStats seeds of a step
+// go straight from global memory into the registers that become its S and
+// dP accumulators; they are loaded during the previous step's dV/dK
+// products, when those registers are free.  Otherwise each step is that of
+// dkdv_occ_kernel; the 4 partial sums are added in a fixed order at the end.
+constexpr int TWIN_WAVES = 4;
+constexpr int TWIN_MAX_SPAN = 1024;   // queries per key tile, see launch_dkdv_kernel
+constexpr int TWIN_THREADS = 64 * TWIN_WAVES;
+
+__global__ __launch_bounds__(TWIN_THREADS, 2) void dkdv_twin_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const TileStats* __restrict__ stats, int tile_cap,
+    const Tile* __restrict__ tiles, int T, int Hq, int Hkv,
+    int window, int band, float scale_log2, float scale, int run_len, bf16* __restrict__ dk,
+    bf16* __restrict__ dv) {
+  constexpr int D = 128;
+  using Geo = DkdvGeom<D>;
+  constexpr int KS = Geo::KS, DB = Geo::DB, RED_PITCH = Geo::RED_PITCH;
+  constexpr int TILE_BYTES = Geo::TILE_BYTES;                  // 32 x 128 bf16
+  constexpr int KV_BYTES = 2 * TILE_BYTES;                     // K and V tiles
+  constexpr int WBUF_BYTES = 2 * TILE_BYTES;                   // a wave's Q and dO
+  constexpr size_t LDS_BYTES = (size_t)KV_BYTES + (size_t)TWIN_WAVES * WBUF_BYTES;
+  static_assert(2 * LDS_BYTES <= 160 * 1024, "two work-groups per CU");
+  static_assert((size_t)TWIN_WAVES * TILE * RED_PITCH * sizeof(float) <= LDS_BYTES,
+                "reduction buffer must fit in the staging buffers");
+  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+
+  // work-group -> (key tile, key-value head), in runs of neighbouring key
+  // tiles per XCD (xcd_run_item)
+  int g;
+  const int item = xcd_run_item(blockIdx.x, run_len, Hkv, &g);
+  const ScheduleView sv = read_schedule(tiles, item, tile_cap, T, window);
+  const Tile tl = sv.tile;
+  if (!sv.ok) {
+    poison_words(dk, (size_t)T * Hkv * (D / 2), NAN_BF16X2);
+    poison_words(dv, (size_t)T * Hkv * (D / 2), NAN_BF16X2);
+    return;
+  }
+  if (!sv.valid) return;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lh = lane >> 5, lq = lane & 31;
+  const int G = Hq / Hkv;
+  const int k0 = tl.t0, k1 = tl.t1, b = tl.seg_b;
+  const int qhi = tile_query_hi(k1, b, window, band);
+  const int nqb = (qhi - k0 + QBLK - 1) / QBLK;
+  const int nheads = wave < G ? (G - wave + 3) / 4 : 0;   // heads wave, wave + 4, ...
+  const int steps = nheads * nqb;
+  const size_t qstride = (size_t)Hq * D;
+  const size_t kstride = (size_t)Hkv * D;
+
+  const bf16* Kt = reinterpret_cast<const bf16*>(smem);
+  const bf16* Vt = Kt + TILE * D;
+  char* wb = smem + KV_BYTES + (size_t)wave * WBUF_BYTES;
+  const bf16* Qs = reinterpret_cast<const bf16*>(wb);
+  const bf16* Ds = reinterpret_cast<const bf16*>(wb + TILE_BYTES);
+  const uint32_t lds_wb = lds_address(wb);
+
+  // K and V rows of the key tile: wave w loads rows 8w .. 8w + 7 (rows past
+  // T re-read row T - 1; they are masked)
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 8 * wave + TileLoad<D>::RPD * j + lane / TileLoad<D>::CPR;
+    const uint32_t off = (uint32_t)min(k0 + r, T - 1) * (uint32_t)(kstride * sizeof(bf16)) +
+                         TileLoad<D>::chunk_offset(lane, r);
+    dma16(k + (size_t)g * D, off, lds_address(smem) + (uint32_t)(wave * 2048 + j * 1024));
+    dma16(v + (size_t)g * D, off, lds_address(smem) + (uint32_t)(TILE_BYTES + wave * 2048 + j * 1024));
+  }
+
+  // Step s: head g G + wave + 4 (s / nqb), q-block s % nqb.  Rows past T
+  // re-read row T - 1 (masked later).
+  const uint32_t rstride = (uint32_t)(qstride * sizeof(bf16));
+  auto issue = [&](int s) {
+    const int j = s / nqb, i = s - j * nqb;
+    const int qb = k0 + i * QBLK;
+    const size_t hoff = (size_t)qb * qstride + (size_t)(g * G + wave + 4 * j) * D;
+    const int rmax = T - 1 - qb;
+#pragma unroll
+    for (int x = 0; x < Geo::LOADS; ++x) {
+      const int r = TileLoad<D>::RPD * x + lane / TileLoad<D>::CPR;
+      const uint32_t off = (uint32_t)min(r, rmax) * rstride + TileLoad<D>::chunk_offset(lane, r);
+      dma16(q + hoff, off, lds_wb + x * 1024);
+      dma16(dout + hoff, off, lds_wb + TILE_BYTES + x * 1024);
+    }
+  };
+  // Seeds of step s (-lse / scale and -D of its rows, in accumulator order)
+  auto seeds = [&](int s, f32x16& s0, f32x16& d0) {
+    const int j = s / nqb, i = s - j * nqb;
+    const TileStats* st = stats + (size_t)(g * G + wave + 4 * j) * tile_cap + tl.idx + i;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const float4 a4 = *reinterpret_cast<const float4*>(st->s0 + 8 * x + 4 * lh);
+      const float4 b4 = *reinterpret_cast<const float4*>(st->dp0 + 8 * x + 4 * lh);
+      s0[4 * x + 0] = a4.x; s0[4 * x + 1] = a4.y; s0[4 * x + 2] = a4.z; s0[4 * x + 3] = a4.w;
+      d0[4 * x + 0] = b4.x; d0[4 * x + 1] = b4.y; d0[4 * x + 2] = b4.z; d0[4 * x + 3] = b4.w;
+    }
+  };
+
+  f32x16 dka[DB], dva[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dka[db] = zero_f32x16();
+    dva[db] = zero_f32x16();
+  }
+  const int krow = k0 + lq;
+  const bool kvalid = krow < k1;
+  const int vis_hi = window > 0 ? min(b - 1, krow + window - 1) : b - 1;
+  const int mbias = (kvalid ? 0 : -(1 << 30)) + 4 * lh - krow;
+  const uint32_t mspan = kvalid ? (uint32_t)(vis_hi - krow) : 0u;
+
+  f32x16 seed_s = zero_f32x16(), seed_d = zero_f32x16();
+  if (steps > 0) {
+    seeds(0, seed_s, seed_d);
+    issue(0);
+  }
+  // the K and V tiles (every wave's rows) are in LDS after the barrier
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  for (int s = 0; s < steps; ++s) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int i = s % nqb;
+    f32x16 sacc = seed_s, dpacc = seed_d;
+    {
+      // operand reads run two k-steps ahead of the products (ring of 3)
+      bf16x8 ring[3][4];
+      auto load = [&](int ks, bf16x8* r) {
+        r[0] = swz_frag_cols<D>(Qs, ks, lane);
+        r[1] = swz_frag_cols<D>(Kt, ks, lane);
+        r[2] = swz_frag_cols<D>(Ds, ks, lane);
+        r[3] = swz_frag_cols<D>(Vt, ks, lane);
+      };
+      load(0, ring[0]);
+      load(1, ring[1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 2 < KS) load(ks + 2, ring[(ks + 2) % 3]);
+        sacc = mfma32(ring[ks % 3][0], ring[ks % 3][1], sacc);
+        dpacc = mfma32(ring[ks % 3][2], ring[ks % 3][3], dpacc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    const int x0 = k0 + i * QBLK + mbias;
+    bf16x8 pf[2], dsf[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * t + e;
+        const bool vis = (uint32_t)(x0 + 8 * (r >> 2) + (r & 3)) <= mspan;
+        float p = exp2_fast(sacc[r] * scale_log2);
+        p = vis ? p : 0.f;
+        pf[t][e] = (bf16)p;
+        dsf[t][e] = (bf16)(p * dpacc[r]);
+      }
+    // the next step's seeds (this step's again after the last, so that the
+    // seed registers are rewritten on every path and free during S/dP)
+    seeds(s + 1 < steps ? s + 1 : s, seed_s, seed_d);
+    {
+      // the 16 dV/dK products, their transposing reads four products ahead
+      constexpr int NP = 4 * DB;
+      constexpr int AHEAD = 4;
+      bf16x8 ring[AHEAD + 1];
+      auto load = [&](int m) {
+        const int t = m / (2 * DB), db = (m >> 1) % DB;
+        return swz_frag_rows<D>((m & 1) ? Qs : Ds, db * 32, t, lane);
+      };
+#pragma unroll
+      for (int m = 0; m < AHEAD; ++m) ring[m] = load(m);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int m = 0; m < NP; ++m) {
+        if (m + AHEAD < NP) ring[(m + AHEAD) % (AHEAD + 1)] = load(m + AHEAD);
+        const int t = m / (2 * DB), db = (m >> 1) % DB;
+        if (m & 1)
+          dka[db] = mfma32(dsf[t], ring[m % (AHEAD + 1)], dka[db]);
+        else
+          dva[db] = mfma32(pf[t], ring[m % (AHEAD + 1)], dva[db]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // every read of this wave's buffer has returned (the products above
+    // consumed them), so the next step's loads may overwrite it
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (s + 1 < steps) issue(s + 1);
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+
+  // Reduction over the 4 waves in a fixed order, then store: thread t sums
+  // 16 columns of key t / 8.
+  float* red = reinterpret_cast<float*>(smem);
+  constexpr int OCOLS = D / 8;
+  const int okey = tid >> 3, od = (tid & 7) * OCOLS;
+  for (int pass = 0; pass < 2; ++pass) {
+    __syncthreads();
+    float* mine = red + (size_t)wave * TILE * RED_PITCH;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = (r >> 2) * 8 + lh * 4 + (r & 3);
+        mine[key * RED_PITCH + db * 32 + lq] = pass == 0 ? dka[db][r] : dva[db][r];
+      }
+    __syncthreads();
+    if (k0 + okey < k1) {
+      const float mul = pass == 0 ? scale : 1.f;
+      bf16* dst = (pass == 0 ? dk : dv) + (size_t)(k0 + okey) * kstride + (size_t)g * D + od;
+#pragma unroll
+      for (int e = 0; e < OCOLS; e += 4) {
+        float acc4[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          float sum = 0.f;
+#pragma unroll
+          for (int w = 0; w < TWIN_WAVES; ++w)
+            sum += red[(size_t)w * TILE * RED_PITCH + okey * RED_PITCH + od + e + x];
+          acc4[x] = sum * mul;
+        }
+        store_bf16x4(dst + e, acc4[0], acc4[1], acc4[2], acc4[3]);
+      }
+    }
+  }
+}
+
 template <int D, bool CAP>
 void launch_dq_kernel(const void* q, const void* k, const void* v, const void* out,
                       const float* lse, const void* dout, const Problem& p, void* dq, char* ws,
@@ -1122,7 +1354,6 @@ void launch_dq_kernel(const void* q, const void* k, const void* v, const void* o
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                      static_cast<const bf16*>(v), static_cast<const bf16*>(out),
                      static_cast<const bf16*>(dout), lse,
-                     reinterpret_cast<const int*>(ws + w.header),
                      reinterpret_cast<const Tile*>(ws + w.tiles_fwd), p.total_tokens,
                      p.num_q_heads, p.num_kv_heads, p.window, p.band, p.scale * LOG2E, p.scale,
                      cc.cap_a, cc.cap_c2, (int)w.tile_cap, static_cast<bf16*>(dq),
@@ -1138,12 +1369,32 @@ void launch_dkdv_kernel(const void* q, const void* k, const void* v, const void*
   const int run_len = run_length(p.window);
   const unsigned grid = run_grid(p.num_kv_heads, w.tile_cap, run_len);
   const CapConstants cc = cap_constants(p);
+  // When no tile meets more than TWIN_MAX_SPAN queries (a window, or short
+  // documents) the two-work-groups-per-CU kernel runs; otherwise the 8-wave
+  // one: a twin work-group streams all of a tile's q-blocks through each
+  // wave, twice as long as an 8-wave one, and a long document's first tiles
+  // then outlast the average work per CU (A/B at context 4,096: window-512
+  // dK/dV 83.0 -> 79.7 us, global 180 -> 204 us).  The choice depends only on
+  // the call's window and max_seqlen (not the band formulation), so a window
+  // at least as long as every segment still gives the same bits as no
+  // window, and a band call the same bits as a plain one.
+  const int reach = p.window > 0 ? p.window : p.max_seqlen;
+  if (D == 128 && !CAP && std::min(reach, p.max_seqlen) <= TWIN_MAX_SPAN) {
+    hipLaunchKernelGGL(dkdv_twin_kernel, dim3(grid), dim3(TWIN_THREADS), 0, stream,
+                       static_cast<const bf16*>(q), static_cast<const bf16*>(k),
+                       static_cast<const bf16*>(v), static_cast<const bf16*>(dout),
+                       reinterpret_cast<const TileStats*>(ws + w.rowstats), (int)w.tile_cap,
+                       reinterpret_cast<const Tile*>(ws + w.tiles_bwd), p.total_tokens,
+                       p.num_q_heads, p.num_kv_heads, p.window, p.band, p.scale * LOG2E,
+                       p.scale, run_len, static_cast<bf16*>(dk), static_cast<bf16*>(dv));
+    return;
+  }
   // head dim 256: pairs of waves split the head dim; 128: two waves per
   // SIMD; 64: the software-pipelined kernel
   constexpr bool occ = D == 128;
   void (*kernel)(const bf16*, const bf16*, const bf16*, const bf16*, const TileStats*, int,
-                 const int*, const Tile*, int, int, int, int, int, float, float, float, float,
-                 int, bf16*, bf16*);
+                 const Tile*, int, int, int, int, int, float, float, float, float, int, bf16*,
+                 bf16*);
   if constexpr (D == 256)
     kernel = dkdv_split_kernel<CAP>;
   else if constexpr (D == 128)
@@ -1154,7 +1405,6 @@ void launch_dkdv_kernel(const void* q, const void* k, const void* v, const void*
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                      static_cast<const bf16*>(v), static_cast<const bf16*>(dout),
                      reinterpret_cast<const TileStats*>(ws + w.rowstats), (int)w.tile_cap,
-                     reinterpret_cast<const int*>(ws + w.header),
                      reinterpret_cast<const Tile*>(ws + w.tiles_bwd), p.total_tokens,
                      p.num_q_heads, p.num_kv_heads, p.window, p.band, p.scale * LOG2E, p.scale,
                      cc.cap_a, cc.cap_c2, run_len, static_cast<bf16*>(dk),

@@ -30,10 +30,14 @@ constexpr float LN2 = 0.6931471805599453f;
 
 // One tile of one segment: tokens [t0, t1) of segment [seg_a, seg_b).
 // idx numbers the tiles in token order; the tiles of one segment have
-// consecutive indices, so tile idx + i starts TILE * i tokens later.
+// consecutive indices, so tile idx + i starts TILE * i tokens later.  Every
+// record also carries the call it was built for: the total tokens, the
+// window and a stamp (the tile capacity, or -1 when the boundaries were
+// malformed), so that a kernel checks its schedule with the one load that
+// brings its tile.  Entries past the last tile are written empty (t0 = t1).
 struct __attribute__((aligned(16))) Tile {
   int t0, t1, seg_a, seg_b;
-  int idx, pad0, pad1, pad2;
+  int idx, total, window, stamp;
 };
 
 // Per-row values the backward passes from the dQ kernel to the dK/dV kernel,
@@ -76,15 +80,33 @@ inline WorkspaceLayout workspace_layout(int64_t total_tokens, int64_t num_seqs,
 
 // Workspace header: [0] number of tiles, [1] the total tokens, [2] tile
 // capacity and [3] window the schedule was built for, [4] 1 if cu_seqlens
-// was well formed (cu[0] = 0, non-decreasing, cu[num_seqs] = T), else 0.  A
-// call whose schedule does not match its own arguments (a reused schedule
-// built for another call) or whose boundaries were malformed writes NaN to
-// all of its outputs instead of computing them, so that misuse cannot pass
-// unnoticed; the schedule's clamping keeps every kernel inside its buffers
-// either way.
+// was well formed (cu[0] = 0, non-decreasing, cu[num_seqs] = T), else 0.
+// (The kernels check the same facts in their tile records.)  A call whose
+// schedule does not match its own arguments (a reused schedule built for
+// another call) or whose boundaries were malformed writes NaN to all of its
+// outputs instead of computing them, so that misuse cannot pass unnoticed;
+// the schedule's clamping keeps every kernel inside its buffers either way.
 constexpr int HEADER_WORDS = 5;
-__device__ __forceinline__ bool schedule_ok(const int* header, int T, int tile_cap, int window) {
-  return header[1] == T && header[2] == tile_cap && header[3] == window && header[4] == 1;
+
+// A work-group's tile record and the check of its schedule, in one load.
+// item may lie past the list (an idle work-group): the record then read
+// (clamped to the list's capacity) is not used.  ok is false when the
+// schedule was built for another call or from malformed boundaries.
+struct ScheduleView {
+  Tile tile;
+  bool ok, valid;   // valid: a tile to compute
+};
+__device__ __forceinline__ ScheduleView read_schedule(const Tile* __restrict__ tiles, int item,
+                                                      int tile_cap, int T, int window) {
+  ScheduleView v;
+  v.tile = tiles[min(item, tile_cap - 1)];
+  // all fields at once (else the compiler loads the check's fields first and
+  // the tile's after the check, a second round trip)
+  asm volatile("" ::"s"(v.tile.t0), "s"(v.tile.t1), "s"(v.tile.seg_a), "s"(v.tile.seg_b),
+               "s"(v.tile.idx), "s"(v.tile.total), "s"(v.tile.window), "s"(v.tile.stamp));
+  v.ok = (v.tile.total == T) & (v.tile.window == window) & (v.tile.stamp == tile_cap);
+  v.valid = item < tile_cap && v.tile.t0 < v.tile.t1;
+  return v;
 }
 
 // Query heads per work-group of the forward and dQ kernels: 4 heads of one

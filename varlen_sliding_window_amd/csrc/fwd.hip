@@ -40,18 +40,13 @@ constexpr float RESCALE_LOG2 = 8.f;
 template <int D, bool CAP>
 __global__ __launch_bounds__(FWD_THREADS, BlockGeom<D>::MIN_WG) void fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const int* __restrict__ header, const Tile* __restrict__ tiles, int tile_cap, int T, int Hq,
+    const Tile* __restrict__ tiles, int tile_cap, int T, int Hq,
     int Hkv, int window, int band, float scale_log2, float cap_a, float cap_c2,
     bf16* __restrict__ out, float* __restrict__ lse) {
   using Geo = BlockGeom<D>;
   constexpr int KB = Geo::KB, H2 = Geo::H2, KS = Geo::KS, DB = Geo::DB;
   __shared__ __attribute__((aligned(16))) char smem[2 * Geo::BUF_BYTES];
 
-  if (!schedule_ok(header, T, tile_cap, window)) {
-    poison_words(out, (size_t)T * Hq * (D / 2), NAN_BF16X2);
-    poison_words(lse, (size_t)Hq * T, NAN_F32);
-    return;
-  }
   // work-group -> (tile, key-value head g, chunk of 4 of its G query heads),
   // in runs of neighbouring tiles per XCD, whose key/value blocks meet in
   // that XCD's L2 (xcd_run_item)
@@ -60,9 +55,14 @@ __global__ __launch_bounds__(FWD_THREADS, BlockGeom<D>::MIN_WG) void fwd_kernel(
   const int chunks = Hkv * cpg;
   int hc;
   const int item = xcd_run_item(blockIdx.x, run_length(window), chunks, &hc);
-  if (item >= header[0]) return;
-  const Tile tl = tiles[item];
-  if (tl.t1 <= tl.t0) return;
+  const ScheduleView sv = read_schedule(tiles, item, tile_cap, T, window);
+  const Tile tl = sv.tile;
+  if (!sv.ok) {
+    poison_words(out, (size_t)T * Hq * (D / 2), NAN_BF16X2);
+    poison_words(lse, (size_t)Hq * T, NAN_F32);
+    return;
+  }
+  if (!sv.valid) return;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -262,8 +262,7 @@ void launch_fwd_kernel(unsigned grid, hipStream_t stream, const void* q, const v
   // capped scores arrive in log2 units already: unit scale
   hipLaunchKernelGGL((fwd_kernel<D, CAP>), dim3(grid), dim3(FWD_THREADS), 0, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),
-                     static_cast<const bf16*>(v), reinterpret_cast<const int*>(ws + w.header),
-                     reinterpret_cast<const Tile*>(ws + w.tiles_fwd), (int)w.tile_cap,
+                     static_cast<const bf16*>(v), reinterpret_cast<const Tile*>(ws + w.tiles_fwd), (int)w.tile_cap,
                      p.total_tokens, p.num_q_heads, p.num_kv_heads, p.window, p.band,
                      CAP ? 1.f : p.scale * LOG2E,
                      cc.cap_a, cc.cap_c2, static_cast<bf16*>(out), lse);

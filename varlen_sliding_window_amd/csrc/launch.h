@@ -10,6 +10,7 @@ struct Problem {
   float scale;
   float softcap;   // > 0: logits become softcap * tanh(logit / softcap); 0: no cap
   int band;        // 1: band-block key/query ranges (window > 0 only); 0: tight ranges
+  int max_seqlen;  // the caller's bound on segment lengths (picks kernel variants only)
 };
 
 // Constants of the capped logit in the exp2 domain:

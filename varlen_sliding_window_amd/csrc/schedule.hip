@@ -81,7 +81,14 @@ __device__ __forceinline__ Tile tile_at(int i, const int* __restrict__ seg_off,
   t.seg_a = a;
   t.seg_b = b;
   t.idx = i;
-  t.pad0 = t.pad1 = t.pad2 = 0;
+  t.total = t.window = t.stamp = 0;   // stamped when written
+  return t;
+}
+
+__device__ __forceinline__ Tile stamped(Tile t, int T, int window, int stamp) {
+  t.total = T;
+  t.window = window;
+  t.stamp = stamp;
   return t;
 }
 
@@ -229,6 +236,19 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
   }
   __syncthreads();
 
+  // Every record carries this call's stamp; entries past the last tile are
+  // written empty, so that no kernel takes a stale record for a tile.
+  const int stamp = malformed ? -1 : tile_cap;
+  {
+    Tile e;
+    e.t0 = e.t1 = e.seg_a = e.seg_b = e.idx = 0;
+    e = stamped(e, T, window, stamp);
+    for (int i = ntiles + tid; i < tile_cap; i += SCHED_THREADS) {
+      fwd_list[i] = e;
+      if (need_bwd) bwd_list[i] = e;
+    }
+  }
+
   // 4. scatter (results do not depend on the order inside a bucket).  In the
   // backward list each wave places its 64 consecutive tiles so that tiles of
   // one bucket from one wave keep their token order (a few ballot rounds,
@@ -236,10 +256,10 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
   // neighbouring tiles, which the dK/dV kernel maps onto one XCD, whose L2
   // then serves the rows that neighbouring tiles share.
   if (one_pass) {
-    if (my_valid) fwd_list[atomicAdd(&hist_f[my_bf], 1)] = mine;
+    if (my_valid) fwd_list[atomicAdd(&hist_f[my_bf], 1)] = stamped(mine, T, window, stamp);
     if (need_bwd) {
       const int pb = ordered_slot(hist_b, my_bb, my_valid);
-      if (my_valid) bwd_list[pb] = mine;
+      if (my_valid) bwd_list[pb] = stamped(mine, T, window, stamp);
     }
   } else {
     for (int i0 = 0; i0 < ntiles; i0 += SCHED_THREADS) {
@@ -252,10 +272,10 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
         bf = fwd_bin(t, window, band);
         bb = bwd_bin(t, window, band);
       }
-      if (valid) fwd_list[atomicAdd(&hist_f[bf], 1)] = t;
+      if (valid) fwd_list[atomicAdd(&hist_f[bf], 1)] = stamped(t, T, window, stamp);
       if (need_bwd) {
         const int pb = ordered_slot(hist_b, bb, valid);
-        if (valid) bwd_list[pb] = t;
+        if (valid) bwd_list[pb] = stamped(t, T, window, stamp);
       }
     }
   }
