@@ -157,6 +157,23 @@ attn_status attn_varlen_bwd(const void* q, const void* k, const void* v,
  */
 enum { ATTN_BWD_REUSE_SCHEDULE = 1, ATTN_FWD_REUSE_SCHEDULE = 1 };
 
+/*
+ * Builds only the tile schedule (the lists of both passes and their record,
+ * as a forward call without ATTN_FWD_REUSE_SCHEDULE would) in workspace, so
+ * that it can be made ahead of the calls that use it with the REUSE flags:
+ * for instance on a second stream while the previous layer's kernels run,
+ * the caller ordering the two streams (events) so that the schedule is done
+ * before its first use and no call still using the workspace's previous
+ * schedule overlaps it.  Arguments as for attn_varlen_fwd (the head counts
+ * and head dim only size and validate the workspace).  Same error
+ * behaviour; nothing but the workspace is written.
+ */
+attn_status attn_varlen_schedule(const int32_t* cu_seqlens, int32_t num_seqs,
+                                 int32_t total_tokens, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t max_seqlen,
+                                 int32_t window, void* workspace, size_t workspace_bytes,
+                                 attn_stream_t stream);
+
 attn_status attn_varlen_fwd_ex(const void* q, const void* k, const void* v,
                                const int32_t* cu_seqlens, int32_t num_seqs,
                                int32_t total_tokens, int32_t num_q_heads, int32_t num_kv_heads,

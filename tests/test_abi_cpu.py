@@ -245,3 +245,25 @@ def test_static_backward_refuses_beyond_its_scratch_before_the_device(lib):
     bad[10] = 3                                              # Hq % Hkv != 0
     assert lib.attn_varlen_bwd_static(*bad) == EINVAL
 
+
+
+def test_schedule_call_checks_its_arguments_before_the_device(lib):
+    """attn_varlen_schedule validates shapes, the boundaries pointer and the
+    workspace on the host, before it looks for a device."""
+    n = attn.workspace_size(4096, 2, 8, 2, 128, 2048, 512)
+    args = [FAKE, 2, 4096, 8, 2, 128, 2048, 512, FAKE, n, None]
+    bad = list(args)
+    bad[0] = None                                            # no cu_seqlens
+    assert lib.attn_varlen_schedule(*bad) == EINVAL
+    bad = list(args)
+    bad[4] = 3                                               # Hq % Hkv != 0
+    assert lib.attn_varlen_schedule(*bad) == EINVAL
+    bad = list(args)
+    bad[5] = 96                                              # head dim
+    assert lib.attn_varlen_schedule(*bad) == EUNSUPPORTED
+    bad = list(args)
+    bad[9] = n - 1                                           # workspace too small
+    assert lib.attn_varlen_schedule(*bad) == EWORKSPACE
+    bad = list(args)
+    bad[8] = None
+    assert lib.attn_varlen_schedule(*bad) == EWORKSPACE

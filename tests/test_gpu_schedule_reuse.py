@@ -127,3 +127,41 @@ def test_malformed_boundaries_give_nan_outputs(case):
     torch.cuda.synchronize()
     for name_, x in (("out", out), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
         assert torch.isnan(x.float()).all(), f"{case}: {name_} not NaN"
+
+
+@pytest.mark.parametrize("name", ["ctx4096_w512", "ctx4096_global"])
+def test_schedule_built_ahead_on_another_stream(name):
+    """attn_varlen_schedule on a second stream, ordered by an event before a
+    forward and backward that reuse it: bit for bit the calls that build
+    their own; rebuilt while the first stream still runs an earlier pair of
+    calls on another workspace."""
+    mb = make_microbatch(name, 4)
+    q, k, v, do, cu = device_inputs(mb)
+    t, hq, d = q.shape
+    w, sc, ms = mb.cfg.window, mb.cfg.scale, mb.max_seqlen
+    print(f"[case] schedule ahead {name}", flush=True)
+    out0, lse0 = attn.fwd(q, k, v, cu, ms, w, sc)
+    ref = attn.bwd(q, k, v, out0, lse0, do, cu, ms, w, sc)
+    ws = attn.new_workspace(t, mb.num_seqs, hq, k.shape[1], d, ms, w, q.device)
+    ws.fill_(0x5A)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(main)
+    for rep in range(2):
+        other = attn.fwd(q, k, v, cu, ms, w, sc)             # busy work on the first stream
+        with torch.cuda.stream(side):
+            attn.schedule(cu, t, ms, w, ws, hq, k.shape[1], d)
+            ready = torch.cuda.Event()
+            ready.record(side)
+        main.wait_event(ready)
+        out, lse = attn.fwd(q, k, v, cu, ms, w, sc, workspace=ws, reuse_schedule=True)
+        got = attn.bwd(q, k, v, out, lse, do, cu, ms, w, sc, workspace=ws, reuse_schedule=True)
+        done = torch.cuda.Event()
+        done.record(main)
+        side.wait_event(done)                                # before the next rebuild
+        torch.cuda.synchronize()
+        assert torch.equal(_views(out), _views(out0)), f"out differs (rep {rep})"
+        assert torch.equal(_views(lse), _views(lse0)), f"lse differs (rep {rep})"
+        for name_, a, b in zip(("dq", "dk", "dv"), got, ref):
+            assert torch.equal(_views(a), _views(b)), f"{name_} differs (rep {rep})"
+        del other

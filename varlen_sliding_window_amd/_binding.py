@@ -79,6 +79,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_varlen_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                     i32, ctypes.c_float, vp, vp, vp, vp, sz, vp]
     lib.attn_varlen_bwd.restype = ctypes.c_int
+    lib.attn_varlen_schedule.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+    lib.attn_varlen_schedule.restype = ctypes.c_int
     lib.attn_varlen_fwd_ex.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                        ctypes.c_float, ctypes.c_float, ctypes.c_uint32, vp, vp,
                                        vp, sz, vp]
@@ -178,6 +180,23 @@ def new_workspace(total_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, m
     if n == 0:
         raise AttnError(-1, "attn_varlen_workspace_size")
     return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def schedule(cu_seqlens, total_tokens: int, max_seqlen: int, window: int, workspace,
+             num_q_heads: int, num_kv_heads: int, head_dim: int):
+    """attn_varlen_schedule: build the tile schedule of (cu_seqlens, window)
+    into `workspace` on the current stream, for later fwd/bwd calls with
+    reuse_schedule=True (ordered after it by the caller when they run on
+    another stream)."""
+    _check_tensor("cu_seqlens", cu_seqlens, torch.int32, 1)
+    t, nseq = int(total_tokens), cu_seqlens.numel() - 1
+    lib = load_library()
+    st = lib.attn_varlen_schedule(_ptr(cu_seqlens), nseq, t, int(num_q_heads), int(num_kv_heads),
+                                  int(head_dim), int(max_seqlen), int(window), _ptr(workspace),
+                                  workspace.numel(), _stream_handle(cu_seqlens.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_varlen_schedule")
+    _WS_RECORD[_ws_key(workspace)] = ("schedule", t, nseq, _effective_window(int(window), t))
 
 
 def fwd(q, k, v, cu_seqlens, max_seqlen: int, window: int, scale: float | None = None,

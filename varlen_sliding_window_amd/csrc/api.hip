@@ -214,6 +214,30 @@ attn_status attn_varlen_fwd_ex(const void* q, const void* k, const void* v,
                   workspace_bytes, stream);
 }
 
+attn_status attn_varlen_schedule(const int32_t* cu_seqlens, int32_t num_seqs,
+                                 int32_t total_tokens, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t max_seqlen,
+                                 int32_t window, void* workspace, size_t workspace_bytes,
+                                 attn_stream_t stream) {
+  attn_status s = check_shape(total_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                              max_seqlen);
+  if (s != ATTN_OK) return s;
+  if (!cu_seqlens || !aligned(cu_seqlens, 4)) return ATTN_EINVAL;
+  const WorkspaceLayout w = attn::workspace_layout(total_tokens, num_seqs, num_q_heads);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < w.total) return ATTN_EWORKSPACE;
+  s = check_device();
+  if (s != ATTN_OK) return s;
+  const int32_t wnd = effective_window(window, total_tokens);
+  const Problem p{total_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, wnd, 1.f,
+                  0.f, 0, max_seqlen};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (timed_launch(K_SCHEDULE, st, [&] {
+        return attn::launch_schedule(cu_seqlens, p, true, workspace, w, st);
+      }) != hipSuccess)
+    return ATTN_ELAUNCH;
+  return ATTN_OK;
+}
+
 attn_status attn_varlen_fwd(const void* q, const void* k, const void* v,
                             const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
