@@ -120,15 +120,22 @@ __global__ __launch_bounds__(BWD_THREADS, BlockGeom<D>::MIN_WG) void dq_kernel(
   const size_t tile_off = (size_t)q0 * qstride + (size_t)head * D;
   const uint32_t row_bytes = (uint32_t)(qstride * sizeof(bf16));
   const int rows = min(TILE, T - q0);
+  // The row's lse, in the first round trip (rows past T read row T - 1, as
+  // the staged tiles do; their results are never stored)
+  const int qrow_c = min(qrow, T - 1);
+  const float lse_row = lse[(size_t)head * T + qrow_c];
   if constexpr (STAGE) dma_tile_rows<D>(q + tile_off, row_bytes, rows, lds_address(wave_tile(1)), lane);
   issue(0, 0);
   bf16x8 qf[KS], df[KS];
   float dpart = 0.f;
   const size_t off = (size_t)qrow * qstride + (size_t)head * D + lh * 8;
   if constexpr (STAGE) {
+    // O with the row clamped like the staged Q and dO rows: unconditional
+    // loads, all in flight together
+    const size_t off_c = (size_t)qrow_c * qstride + (size_t)head * D + lh * 8;
     bf16x8 ov[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) ov[ks] = qrow < T ? as_bf16x8(ldg16(out + off + ks * 16)) : zero_bf16x8();
+    for (int ks = 0; ks < KS; ++ks) ov[ks] = as_bf16x8(ldg16(out + off_c + ks * 16));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = swz_frag_cols<D>(wave_tile(1), ks, lane);
@@ -164,7 +171,7 @@ __global__ __launch_bounds__(BWD_THREADS, BlockGeom<D>::MIN_WG) void dq_kernel(
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]), "v"(df[ks]));
   const float Dv = dpart + __shfl_xor(dpart, 32);
-  const float lsev = qrow < T ? lse[(size_t)head * T + qrow] : 0.f;
+  const float lsev = qrow < T ? lse_row : 0.f;
   const float lse2 = lsev * LOG2E;
   if (active && lh == 0) {
     // Rows past the tile get seeds that make them vanish (P = 0, dP - D = 0),

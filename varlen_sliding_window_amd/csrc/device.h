@@ -229,6 +229,15 @@ __device__ __forceinline__ void poison_words(void* p, size_t nwords, uint32_t wo
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max(x of lane l, x of lane l ^ 32): the two lanes that hold one query row's
+// halves of a 32 x 32 accumulator.  v_permlane32_swap hands each lane both
+// x[l % 32] and x[l % 32 + 32] in registers, without the LDS round trip of a
+// shuffle.
+__device__ __forceinline__ float row_halves_max(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
 // tanh in fp32 with a relative error of about 2e-7 everywhere.

@@ -200,7 +200,7 @@ __global__ __launch_bounds__(FWD_THREADS, BlockGeom<D>::MIN_WG) void fwd_kernel(
     for (int h2 = 0; h2 < H2; ++h2)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[h2][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+    mx = row_halves_max(mx) * scale_log2;
     if (__builtin_amdgcn_ballot_w64(mx > m + RESCALE_LOG2)) {
       const float mnew = fmaxf(m, mx);
       const float alpha = mnew == -INFINITY ? 1.f : exp2_fast(m - mnew);
