@@ -62,6 +62,8 @@ WORKLOADS = {
     "ctx4096_global": [("global", "ctx4096_global")],
     "ctx1024_global": [("global", "ctx1024_global")],
     "ctx2048_global": [("global", "ctx2048_global")],
+    "ctx1024_w512": [("window512", "ctx1024_w512")],
+    "ctx2048_w512": [("window512", "ctx2048_w512")],
     "stack_ctx4096": [("window512", "ctx4096_w512")] * 15 + [("global", "ctx4096_global")] * 5,
     "stack_ctx4096_h16": [("window512", "ctx4096_w512_h16")] * 15
     + [("global", "ctx4096_global_h16")] * 5,
